@@ -1,0 +1,40 @@
+"""CPU oracle for one tensor-parallel rank's share of the Megatron MLP block.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
+execute this package: only the tests, the smoke check and the benchmark's CPU
+baseline leg use it.  It shares no code with the GPU path; the only thing the
+two sides share is the bit patterns of the seeded inputs.
+
+What it computes, and where the pages define it:
+
+* Shard map ("Megatron architecture and 6D parallel guide", §3.1, TP=2
+  example; "Megatron-LM deep architecture", column/row-parallel section):
+  rank i holds A_i = A[:, i·F:(i+1)·F] and B_i = B[i·F:(i+1)·F, :], F = 4d/N.
+* Column-parallel GEMM + elementwise GeLU (same sections; "Megatron-LM"
+  glossary, tensor-parallel FFN table): Z_i = GeLU(X·A_i), no exchange.
+* Row-parallel GEMM ("Megatron-LM deep architecture", column/row-parallel
+  section): Y_i = Z_i·B_i.
+* Closed form of the output (same section, eq. for Output):
+  Y = Z·B = Σ_i Z_i·B_i = Σ_i Y_i.
+* fp8 e4m3 forward GEMMs with amax-derived per-tensor scales
+  ("Megatron-LM deep architecture", FP8 hybrid precision section).
+
+Everything is float64, on bfloat16 (or e4m3) inputs decoded exactly.  Z is
+rounded to bfloat16 once, after GeLU, which models the GPU's stored Z.
+
+Pins (tests marked "not gpu"): an exact rational brute force on tiny shapes,
+the closed form Σ_i Y_i = Y, N=1 = unsharded, structured inputs that reduce
+the path to an elementwise GeLU, textbook values of the normal CDF, and
+exhaustive codec checks against torch's CPU conversions.
+"""
+from .codecs import (bf16_decode, bf16_encode, e4m3_decode, e4m3_encode, E4M3_MAX)
+from .mlp import (shard_columns, gelu, col_gelu, row_partial, mlp_shard, partial_sum,
+                  mlp_unsharded, amax, quant_scale, quant_e4m3, col_gelu_e4m3,
+                  requant_z, row_partial_e4m3, mlp_shard_e4m3, quantize_inputs_e4m3)
+
+__all__ = [
+    "bf16_decode", "bf16_encode", "e4m3_decode", "e4m3_encode", "E4M3_MAX",
+    "shard_columns", "gelu", "col_gelu", "row_partial", "mlp_shard", "partial_sum",
+    "mlp_unsharded", "amax", "quant_scale", "quant_e4m3", "col_gelu_e4m3", "requant_z",
+    "row_partial_e4m3", "mlp_shard_e4m3", "quantize_inputs_e4m3",
+]

@@ -1,0 +1,167 @@
+"""The tensor-parallel MLP shard, step by step, in float64.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+Inputs are bfloat16 bit arrays (uint16) or e4m3 code arrays (uint8) plus
+float32 scales; outputs are float64 arrays, except Z, which is returned as
+bfloat16 bits because the path stores it in bfloat16.
+
+Notation (as on the pages): X [M, d]; A [d, 4d]; B [4d, d]; N ranks;
+F = 4d/N; A_i = A[:, i·F:(i+1)·F]; B_i = B[i·F:(i+1)·F, :];
+Z_i = GeLU(X·A_i) [M, F]; Y_i = Z_i·B_i [M, d]; Y = Σ_i Y_i.
+"""
+from __future__ import annotations
+
+import numpy as np
+from scipy.special import erfc
+
+from .codecs import bf16_decode, bf16_encode, e4m3_decode, e4m3_encode, E4M3_MAX
+
+_INV_SQRT2 = 0.7071067811865476  # 1/√2 rounded to float64
+
+
+def shard_columns(H: int, N: int, rank: int) -> tuple[int, int]:
+    """Column range [lo, hi) of A (and row range of B) held by `rank`.
+
+    The first weight is split by columns and the second by rows into N equal
+    contiguous blocks ("Megatron architecture and 6D parallel guide", §3.1:
+    at TP=2, GPU 0 holds A[:, :2d] and B[:2d, :], GPU 1 the rest).  A width
+    that N does not divide is an error here rather than a silent truncation.
+    """
+    if N < 1 or not (0 <= rank < N):
+        raise ValueError(f"rank {rank} not in [0, {N})")
+    if H % N:
+        raise ValueError(f"width {H} not divisible by N={N}")
+    F = H // N
+    return rank * F, (rank + 1) * F
+
+
+def gelu(s: np.ndarray) -> np.ndarray:
+    """GeLU(s) = s·Φ(s), Φ the standard normal CDF, Φ(s) = ½·erfc(−s/√2).
+
+    The pages apply GeLU elementwise between the two GEMMs but never define
+    it; this is the exact (Gaussian-CDF) form.  erfc keeps Φ accurate in the
+    far negative tail, where 1 + erf(s/√2) would cancel.
+    """
+    s = np.asarray(s, dtype=np.float64)
+    return s * (0.5 * erfc(-s * _INV_SQRT2))
+
+
+def col_gelu(X_bits: np.ndarray, A_i_bits: np.ndarray) -> np.ndarray:
+    """Column-parallel step: Z_i = bf16(GeLU(X·A_i)), as bfloat16 bits.
+
+    "Megatron-LM deep architecture", column-parallel linear: each rank takes
+    the same X and its own column block of the first weight, and applies
+    GeLU to its own columns with no exchange.
+    """
+    S = bf16_decode(X_bits) @ bf16_decode(A_i_bits)
+    return bf16_encode(gelu(S))
+
+
+def row_partial(Z_bits: np.ndarray, B_i_bits: np.ndarray) -> np.ndarray:
+    """Row-parallel step: the partial output Y_i = Z_i·B_i (float64).
+
+    "Megatron-LM deep architecture", row-parallel linear: each rank multiplies
+    its local activation by its row block of the second weight.
+    """
+    return bf16_decode(Z_bits) @ bf16_decode(B_i_bits)
+
+
+def mlp_shard(X_bits, A_bits, B_bits, N: int, rank: int, return_z: bool = False):
+    """Rank `rank`'s partial output Y_i = GeLU(X·A_i)·B_i of an N-way split.
+
+    A is [d, H] and B is [H, d]; the rank's blocks are taken by
+    `shard_columns` ("Megatron architecture and 6D parallel guide", §3.1
+    forward pass: Y_i = GeLU(X·A_i)·B_i on each GPU).
+    """
+    H = A_bits.shape[1]
+    if B_bits.shape[0] != H or X_bits.shape[1] != A_bits.shape[0] or B_bits.shape[1] != A_bits.shape[0]:
+        raise ValueError("shape mismatch")
+    lo, hi = shard_columns(H, N, rank)
+    Z = col_gelu(X_bits, A_bits[:, lo:hi])
+    Y = row_partial(Z, B_bits[lo:hi, :])
+    return (Y, Z) if return_z else Y
+
+
+def partial_sum(parts) -> np.ndarray:
+    """Y = Σ_i Y_i, added in rank order 0..N−1 (float64).
+
+    This is the arithmetic of the AllReduce(sum) that ends the block
+    ("Megatron-LM deep architecture", eq. for Output).
+    """
+    parts = list(parts)
+    if not parts:
+        raise ValueError("no partials")
+    acc = np.array(parts[0], dtype=np.float64, copy=True)
+    for p in parts[1:]:
+        acc += np.asarray(p, dtype=np.float64)
+    return acc
+
+
+def mlp_unsharded(X_bits, A_bits, B_bits) -> np.ndarray:
+    """The unsharded block Y = bf16(GeLU(X·A))·B (Z rounded as in a shard)."""
+    return row_partial(col_gelu(X_bits, A_bits), B_bits)
+
+
+# ----------------------------------------------------------------------------
+# fp8 e4m3 variant ("Megatron-LM deep architecture", FP8 hybrid precision):
+# every tensor is multiplied by a scale S derived from its amax before it is
+# cast to E4M3; the GEMM result is divided by the product of the two scales.
+# Current scaling is used: each tensor's own amax.
+# ----------------------------------------------------------------------------
+
+def amax(T_bits: np.ndarray) -> float:
+    """max |T| of a bfloat16 tensor (exact)."""
+    if T_bits.size == 0:
+        return 0.0
+    return float(np.max(np.abs(bf16_decode(T_bits))))
+
+
+def quant_scale(a: float) -> np.float32:
+    """Per-tensor quantisation scale s = 448/amax, an fp32 division (1 if amax = 0)."""
+    if a == 0.0:
+        return np.float32(1.0)
+    return np.float32(np.float32(E4M3_MAX) / np.float32(a))
+
+
+def quant_e4m3(T_bits: np.ndarray, s: np.float32) -> np.ndarray:
+    """e4m3 codes of T·s: the product is taken in fp32 (RNE), clamped to ±448,
+    then rounded once to e4m3 (RNE)."""
+    t32 = bf16_decode(T_bits).astype(np.float32)
+    v = (t32 * np.float32(s)).astype(np.float32)
+    v = np.clip(v, -E4M3_MAX, E4M3_MAX)
+    return e4m3_encode(v.astype(np.float64))
+
+
+def quantize_inputs_e4m3(T_bits: np.ndarray):
+    """(codes, s) of a bfloat16 tensor under its own amax scale."""
+    s = quant_scale(amax(T_bits))
+    return quant_e4m3(T_bits, s), s
+
+
+def col_gelu_e4m3(Xq, sX, Aq_i, sA) -> np.ndarray:
+    """Z_i = bf16(GeLU((Xq·Aq_i)/(sX·sA))) as bfloat16 bits."""
+    S = (e4m3_decode(Xq) @ e4m3_decode(Aq_i)) / (float(sX) * float(sA))
+    return bf16_encode(gelu(S))
+
+
+def requant_z(Z_bits: np.ndarray):
+    """Z_q = e4m3(Z·s_Z) with s_Z = 448/amax(Z); returns (codes, s_Z)."""
+    return quantize_inputs_e4m3(Z_bits)
+
+
+def row_partial_e4m3(Zq, sZ, Bq_i, sB) -> np.ndarray:
+    """Y_i = (Zq·Bq_i)/(sZ·sB) in float64 (the GPU stores it as bfloat16)."""
+    return (e4m3_decode(Zq) @ e4m3_decode(Bq_i)) / (float(sZ) * float(sB))
+
+
+def mlp_shard_e4m3(Xq, sX, Aq, sA, Bq, sB, N: int = 1, rank: int = 0, return_all=False):
+    """fp8 partial output of rank `rank` from quantised X, A, B (codes + scales)."""
+    H = Aq.shape[1]
+    lo, hi = shard_columns(H, N, rank)
+    Z = col_gelu_e4m3(Xq, sX, Aq[:, lo:hi], sA)
+    Zq, sZ = requant_z(Z)
+    Y = row_partial_e4m3(Zq, sZ, Bq[lo:hi, :], sB)
+    if return_all:
+        return Y, Z, Zq, sZ
+    return Y

@@ -1,0 +1,114 @@
+"""Exact rational brute force of the MLP shard, for tiny shapes.
+
+Independent of the oracle: it decodes bfloat16/e4m3 with its own code, forms
+every dot product as an exact `fractions.Fraction`, evaluates GeLU with
+Python's `math.erfc`, and rounds with its own integer round-half-even.
+"""
+from __future__ import annotations
+
+import math
+import struct
+from fractions import Fraction
+
+HALF = Fraction(1, 2)
+
+
+def bf16_value(bits: int) -> Fraction:
+    """Exact value of a bfloat16 bit pattern."""
+    f = struct.unpack("<f", struct.pack("<I", (int(bits) & 0xFFFF) << 16))[0]
+    return Fraction(f)
+
+
+def e4m3_value(code: int) -> Fraction:
+    """Exact value of an OCP e4m3 code (NaN codes are rejected)."""
+    code = int(code) & 0xFF
+    sign = -1 if code & 0x80 else 1
+    E = (code >> 3) & 0xF
+    m = code & 7
+    if E == 15 and m == 7:
+        raise ValueError("NaN code")
+    if E == 0:
+        return sign * Fraction(m, 2 ** 9)
+    return sign * (1 + Fraction(m, 8)) * Fraction(2) ** (E - 7)
+
+
+def round_half_even(v: Fraction, frac_bits: int, emin: int) -> Fraction:
+    """Round v to the binary grid with `frac_bits` fraction bits, subnormal
+    spacing 2^(emin - frac_bits), ties to even (no overflow handling)."""
+    if v == 0:
+        return Fraction(0)
+    sign = -1 if v < 0 else 1
+    a = abs(v)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    e = max(e, emin)
+    q = Fraction(2) ** (e - frac_bits)
+    n = a / q
+    fl = n.numerator // n.denominator
+    rem = n - fl
+    if rem > HALF or (rem == HALF and fl % 2 == 1):
+        fl += 1
+    return sign * fl * q
+
+
+def bf16_round(v: Fraction) -> Fraction:
+    return round_half_even(v, 7, -126)
+
+
+def gelu_float(x: float) -> float:
+    """x·Φ(x) with Φ(x) = erfc(−x/√2)/2, in Python floats."""
+    return x * 0.5 * math.erfc(-x / math.sqrt(2.0))
+
+
+def matmul_exact(P, Q):
+    """Exact product of two nested lists of Fractions."""
+    n_in = len(Q)
+    cols = len(Q[0])
+    return [[sum((row[k] * Q[k][j] for k in range(n_in)), Fraction(0)) for j in range(cols)]
+            for row in P]
+
+
+def shard_exact(X_bits, A_bits, B_bits, N, rank):
+    """(Z_i, Y_i) of rank `rank`: Z as exact Fractions on the bf16 grid, Y exact."""
+    X = [[bf16_value(b) for b in row] for row in X_bits.tolist()]
+    A = [[bf16_value(b) for b in row] for row in A_bits.tolist()]
+    B = [[bf16_value(b) for b in row] for row in B_bits.tolist()]
+    H = len(A[0])
+    F = H // N
+    lo, hi = rank * F, (rank + 1) * F
+    A_i = [row[lo:hi] for row in A]
+    B_i = B[lo:hi]
+    S = matmul_exact(X, A_i)
+    Z = [[bf16_round(Fraction(gelu_float(float(s)))) for s in row] for row in S]
+    Y = matmul_exact(Z, B_i)
+    return Z, Y
+
+
+def fp8_shard_exact(Xq, sX, Aq, sA, Bq, sB):
+    """Exact fp8 path on codes: returns (Z on the bf16 grid, Z codes, sZ, Y)."""
+    X = [[e4m3_value(c) for c in row] for row in Xq.tolist()]
+    A = [[e4m3_value(c) for c in row] for row in Aq.tolist()]
+    B = [[e4m3_value(c) for c in row] for row in Bq.tolist()]
+    S = matmul_exact(X, A)
+    den = Fraction(float(sX)) * Fraction(float(sA))
+    Z = [[bf16_round(Fraction(gelu_float(float(s / den)))) for s in row] for row in S]
+    zmax = max(abs(z) for row in Z for z in row)
+    import numpy as np
+    sZ = np.float32(1.0) if zmax == 0 else np.float32(np.float32(448.0) / np.float32(float(zmax)))
+    codes = []
+    Zq = []
+    for row in Z:
+        qrow = []
+        for z in row:
+            # product in fp32 (RNE), clamp, then one e4m3 rounding
+            p = Fraction(float(np.float32(np.float32(float(z)) * sZ)))
+            p = max(min(p, Fraction(448)), Fraction(-448))
+            qrow.append(round_half_even(p, 3, -6))
+        Zq.append(qrow)
+    Y = matmul_exact(Zq, B)
+    den2 = Fraction(float(sZ)) * Fraction(float(sB))
+    Y = [[y / den2 for y in row] for row in Y]
+    return Z, Zq, sZ, Y

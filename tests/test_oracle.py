@@ -1,0 +1,247 @@
+"""Pins for the oracle (CPU only): it is checked against things other than
+itself - an exact rational brute force, the pages' closed form, textbook
+values of the normal CDF, structured inputs that reduce the path to a known
+function, and the pages' printed TP=2 shard map.
+"""
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import brute
+import oracle
+from oracle import mlp as omlp
+from workloads import WORKLOADS, make_inputs, make_random, bf16_bits_from_f32
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _table(name):
+    out = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                out.append(line.split())
+    return out
+
+
+def _rel_maxdiff(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300))
+
+
+# ---------------------------------------------------------------- GeLU ----
+
+def test_gelu_matches_normal_table():
+    for x, phi, tol in _table("normal_cdf.txt"):
+        x, phi, tol = float(x), float(phi), float(tol)
+        g = float(oracle.gelu(np.array([x]))[0])
+        if x == 0:
+            assert g == 0.0
+        else:
+            assert abs(g / x - phi) <= tol, (x, g / x, phi)
+
+
+def test_gelu_identities():
+    x = np.linspace(-12, 12, 20001)
+    g = oracle.gelu(x)
+    # Φ(−x) = 1 − Φ(x)  =>  GeLU(x) − GeLU(−x) = x
+    assert np.max(np.abs(g - oracle.gelu(-x) - x)) <= 4e-15 * 12
+    assert oracle.gelu(np.array([0.0]))[0] == 0.0
+    big = x[x >= 10]
+    assert np.all(np.abs(oracle.gelu(big) / big - 1) < 1e-22 + 1e-15)
+    neg = x[x <= -10]
+    gn = oracle.gelu(neg)
+    assert np.all(gn <= 0) and np.all(np.abs(gn) < 1e-20)
+    # far tail is accurate (no cancellation): x·Φ(x) with Φ(−10) ≈ 7.62e-24
+    assert abs(oracle.gelu(np.array([-10.0]))[0] / (-10 * 7.619853024160527e-24) - 1) < 1e-12
+
+
+def test_gelu_matches_math_erf_dense_grid():
+    x = np.linspace(-10, 10, 4001)
+    ref = np.array([v * 0.5 * (1 + math.erf(v / math.sqrt(2))) for v in x])
+    assert np.max(np.abs(oracle.gelu(x) - ref)) < 1e-14
+
+
+# ----------------------------------------------------------- shard map ----
+
+def test_shard_map_matches_tp2_example():
+    for d, N, rank, lo, hi in _table("tp2_shard_map.txt"):
+        d, N, rank, lo, hi = map(int, (d, N, rank, lo, hi))
+        assert oracle.shard_columns(4 * d, N, rank) == (lo, hi)
+
+
+def test_shard_map_partitions_and_errors():
+    for H, N in [(256, 1), (256, 2), (256, 8), (16384, 8), (3072, 3)]:
+        blocks = [oracle.shard_columns(H, N, r) for r in range(N)]
+        assert blocks[0][0] == 0 and blocks[-1][1] == H
+        assert all(blocks[r][1] == blocks[r + 1][0] for r in range(N - 1))
+        assert len({hi - lo for lo, hi in blocks}) == 1
+    with pytest.raises(ValueError):
+        oracle.shard_columns(256, 3, 0)       # 4d not divisible by N
+    with pytest.raises(ValueError):
+        oracle.shard_columns(256, 2, 2)       # rank out of range
+    with pytest.raises(ValueError):
+        oracle.shard_columns(256, 0, 0)
+
+
+# --------------------------------------------------------- brute force ----
+
+def _check_against_brute(X, A, B, N):
+    for rank in range(N):
+        Y, Z = oracle.mlp_shard(X, A, B, N, rank, return_z=True)
+        Zb, Yb = brute.shard_exact(X, A, B, N, rank)
+        Zb_f = np.array([[float(z) for z in row] for row in Zb])
+        Yb_f = np.array([[float(y) for y in row] for row in Yb])
+        assert np.array_equal(oracle.bf16_decode(Z), Zb_f), f"Z mismatch at rank {rank}"
+        assert _rel_maxdiff(Y, Yb_f) <= 1e-13, f"Y mismatch at rank {rank}"
+
+
+def test_tiny_tp2_matches_brute_force():
+    X, A, B = make_inputs("tiny_tp2")
+    _check_against_brute(X, A, B, 2)
+
+
+@pytest.mark.parametrize("M,d,H,N,seed", [
+    (3, 4, 16, 1, 10), (5, 8, 16, 2, 11), (7, 16, 16, 4, 12), (16, 12, 8, 2, 13),
+    (1, 16, 16, 4, 14), (9, 5, 12, 3, 15),
+])
+def test_random_tiny_matches_brute_force(M, d, H, N, seed):
+    # wider spread of A so GeLU sees large positive and negative arguments
+    X, A, B = make_random(M, d, H, seed, sigma=0.5)
+    _check_against_brute(X, A, B, N)
+
+
+# --------------------------------------------------------- closed form ----
+
+@pytest.mark.parametrize("M,d,N,seed", [(32, 64, 2, 0), (40, 48, 4, 21), (17, 32, 8, 22),
+                                        (64, 128, 8, 23), (5, 24, 3, 24)])
+def test_sum_of_shards_equals_unsharded(M, d, N, seed):
+    """Output = Z·W2 = Σ_i Z_i·W2_i = Σ_i Y_i ("Megatron-LM deep architecture",
+    eq. for Output)."""
+    X, A, B = make_random(M, d, 4 * d, seed)
+    parts = [oracle.mlp_shard(X, A, B, N, r) for r in range(N)]
+    Ysum = oracle.partial_sum(parts)
+    Yfull = oracle.mlp_unsharded(X, A, B)
+    assert _rel_maxdiff(Ysum, Yfull) <= 1e-12
+
+
+def test_tiny_tp2_closed_form():
+    X, A, B = make_inputs("tiny_tp2")
+    Y0 = oracle.mlp_shard(X, A, B, 2, 0)
+    Y1 = oracle.mlp_shard(X, A, B, 2, 1)
+    assert _rel_maxdiff(Y0 + Y1, oracle.mlp_unsharded(X, A, B)) <= 1e-12
+
+
+def test_n1_is_unsharded():
+    X, A, B = make_random(24, 32, 128, 5)
+    assert np.array_equal(oracle.mlp_shard(X, A, B, 1, 0), oracle.mlp_unsharded(X, A, B))
+
+
+def test_partial_sum_rank_order_and_errors():
+    parts = [np.full((2, 2), 1e16), np.ones((2, 2)), np.full((2, 2), -1e16)]
+    # (1e16 + 1) - 1e16 in float64 loses the 1: rank order is what is summed
+    assert np.all(oracle.partial_sum(parts) == 0.0)
+    with pytest.raises(ValueError):
+        oracle.partial_sum([])
+
+
+# ---------------------------------------------------- structured inputs ----
+
+def test_zero_input_gives_zero():
+    _, A, B = make_random(8, 16, 64, 3)
+    X = np.zeros((8, 16), np.uint16)
+    for r in range(4):
+        Y = oracle.mlp_shard(X, A, B, 4, r)
+        assert np.all(Y == 0.0)
+
+
+def test_identity_weights_reduce_to_elementwise_gelu():
+    d, M = 16, 10
+    rng = np.random.default_rng(4)
+    X = bf16_bits_from_f32(rng.standard_normal((M, d)).astype(np.float32) * 3)
+    eye = np.zeros((d, 4 * d), np.float32)
+    eye[:, :d] = np.eye(d)
+    A = bf16_bits_from_f32(eye)
+    B = bf16_bits_from_f32(eye.T.copy())
+    Y, Z = oracle.mlp_shard(X, A, B, 1, 0, return_z=True)
+    xv = oracle.bf16_decode(X)
+    expect = np.array([[float(brute.bf16_round(Fraction(brute.gelu_float(v)))) for v in row]
+                       for row in xv])
+    assert np.array_equal(Y, expect)
+    assert np.all(oracle.bf16_decode(Z)[:, d:] == 0)
+    # with N=4 only rank 0 holds the identity block
+    assert np.array_equal(oracle.mlp_shard(X, A, B, 4, 0), expect)
+    for r in (1, 2, 3):
+        assert np.all(oracle.mlp_shard(X, A, B, 4, r) == 0)
+
+
+def test_permuted_columns_permute_z():
+    """A column permutation of A_i permutes Z_i's columns (GeLU is elementwise)."""
+    X, A, B = make_random(12, 16, 32, 8, sigma=0.3)
+    perm = np.random.default_rng(0).permutation(32)
+    Z = oracle.col_gelu(X, A)
+    Zp = oracle.col_gelu(X, A[:, perm])
+    assert np.array_equal(Z[:, perm], Zp)
+
+
+# --------------------------------------------------------------- fp8 -----
+
+def test_quant_scale_and_codes():
+    T = bf16_bits_from_f32(np.array([[0.5, -2.0, 0.001, 1.75]], np.float32))
+    a = oracle.amax(T)
+    assert a == 2.0
+    s = oracle.quant_scale(a)
+    assert s == np.float32(224.0)
+    q = oracle.quant_e4m3(T, s)
+    # 0.5·224 = 112, −2·224 = −448, 0.001·224 ≈ 0.224 → 0.21875 (RNE), 1.75·224 = 392 → 384
+    assert oracle.e4m3_decode(q).tolist() == [[112.0, -448.0, 0.21875, 384.0]]
+    assert oracle.quant_scale(0.0) == 1.0
+
+
+def test_quant_matches_torch_float8():
+    import torch
+    X, _, _ = make_random(64, 256, 16, 9)
+    q, s = oracle.quantize_inputs_e4m3(X)
+    prod = torch.from_numpy(oracle.bf16_decode(X).astype(np.float32)) * float(s)
+    ref = prod.clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(q, ref)
+    # the amax element maps exactly to ±448
+    assert np.max(np.abs(oracle.e4m3_decode(q))) == 448.0
+
+
+@pytest.mark.parametrize("M,d,F,seed", [(4, 16, 8, 30), (6, 32, 16, 31), (3, 16, 32, 32)])
+def test_fp8_path_matches_brute_force(M, d, F, seed):
+    X, A, B = make_random(M, d, F, seed, sigma=0.3)
+    Xq, sX = oracle.quantize_inputs_e4m3(X)
+    Aq, sA = oracle.quantize_inputs_e4m3(A)
+    Bq, sB = oracle.quantize_inputs_e4m3(B)
+    Y, Z, Zq, sZ = oracle.mlp_shard_e4m3(Xq, sX, Aq, sA, Bq, sB, return_all=True)
+    Zb, Zqb, sZb, Yb = brute.fp8_shard_exact(Xq, sX, Aq, sA, Bq, sB)
+    assert np.array_equal(oracle.bf16_decode(Z), np.array([[float(z) for z in r] for r in Zb]))
+    assert sZ == sZb
+    assert np.array_equal(oracle.e4m3_decode(Zq), np.array([[float(z) for z in r] for r in Zqb]))
+    assert _rel_maxdiff(Y, np.array([[float(y) for y in r] for r in Yb])) <= 1e-13
+
+
+def test_fp8_close_to_bf16_on_small_175b_like_shapes():
+    """Quantisation error of the e4m3 path is a few per cent of max|Y|."""
+    X, A, B = make_random(64, 384, 192, 3, sigma=0.006)
+    Yb = oracle.mlp_shard(X, A, B, 1, 0)
+    Xq, sX = oracle.quantize_inputs_e4m3(X)
+    Aq, sA = oracle.quantize_inputs_e4m3(A)
+    Bq, sB = oracle.quantize_inputs_e4m3(B)
+    Yq = oracle.mlp_shard_e4m3(Xq, sX, Aq, sA, Bq, sB)
+    assert _rel_maxdiff(Yq, Yb) < 0.06
+
+
+def test_workload_table_shapes():
+    wl = WORKLOADS["7b_tp8"]
+    assert (wl.M, wl.d, wl.F) == (8192, 4096, 2048) and wl.H == 4 * wl.d
+    wl = WORKLOADS["175b_tp8"]
+    assert (wl.M, wl.d, wl.F) == (2048, 12288, 6144)
+    assert WORKLOADS["tiny_tp2"].flops_per_shard() == 4 * 32 * 64 * 128

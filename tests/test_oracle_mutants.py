@@ -1,0 +1,117 @@
+"""The pins catch plausible mistakes: each test plants one mistake in the
+oracle (on the CPU, by monkeypatching) and checks that at least one pin in
+test_oracle.py then fails."""
+import numpy as np
+import pytest
+from scipy.special import erfc
+
+import oracle
+from oracle import mlp as omlp
+from oracle import codecs as ocodecs
+import test_oracle as pins
+
+
+def _pins_fail(fns):
+    for fn in fns:
+        try:
+            fn()
+        except (AssertionError, ValueError, IndexError):
+            return True
+    return False
+
+
+BF16_PINS = [
+    pins.test_gelu_matches_normal_table,
+    pins.test_gelu_identities,
+    pins.test_tiny_tp2_matches_brute_force,
+    lambda: pins.test_random_tiny_matches_brute_force(7, 16, 16, 4, 12),
+    lambda: pins.test_random_tiny_matches_brute_force(16, 12, 8, 2, 13),
+    pins.test_tiny_tp2_closed_form,
+    pins.test_identity_weights_reduce_to_elementwise_gelu,
+    pins.test_shard_map_matches_tp2_example,
+]
+
+
+def _gelu_tanh(s):
+    s = np.asarray(s, np.float64)
+    return 0.5 * s * (1 + np.tanh(np.sqrt(2 / np.pi) * (s + 0.044715 * s ** 3)))
+
+
+MUTANTS = {
+    "gelu_tanh_form": ("gelu", _gelu_tanh),
+    "gelu_dropped_half": ("gelu", lambda s: np.asarray(s) * erfc(-np.asarray(s) * omlp._INV_SQRT2)),
+    "gelu_sign_flip": ("gelu", lambda s: np.asarray(s) * 0.5 * erfc(np.asarray(s) * omlp._INV_SQRT2)),
+    "gelu_identity": ("gelu", lambda s: np.asarray(s, np.float64)),
+    "shard_off_by_one": ("shard_columns",
+                         lambda H, N, r: ((r + 1) % N * (H // N), ((r + 1) % N + 1) * (H // N))),
+    "shard_stride_wrong": ("shard_columns", lambda H, N, r: (r, r + H // N)),
+    "row_partial_reversed_rows": ("row_partial",
+                                  lambda Z, B: ocodecs.bf16_decode(Z) @ ocodecs.bf16_decode(B)[::-1]),
+    "col_gelu_transposed_x": ("col_gelu", lambda X, A: ocodecs.bf16_encode(omlp.gelu(
+        (ocodecs.bf16_decode(X)[:, ::-1]) @ ocodecs.bf16_decode(A)))),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_bf16_mutant_is_caught(name, monkeypatch):
+    attr, fn = MUTANTS[name]
+    monkeypatch.setattr(omlp, attr, fn)
+    monkeypatch.setattr(oracle, attr, fn, raising=False)
+    assert _pins_fail(BF16_PINS), f"mutant {name} passed every pin"
+
+
+def _truncating_bf16_encode(x):
+    x = np.asarray(x, np.float64)
+    return (x.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def test_truncating_rounding_is_caught(monkeypatch):
+    monkeypatch.setattr(omlp, "bf16_encode", _truncating_bf16_encode)
+    assert _pins_fail(BF16_PINS)
+
+
+def test_unrounded_z_is_caught(monkeypatch):
+    # keep S·GeLU in float64 all the way: Z is not rounded to bf16 before GEMM2
+    def col_gelu(X, A):
+        return omlp.gelu(ocodecs.bf16_decode(X) @ ocodecs.bf16_decode(A))
+
+    def row_partial(Z, B):
+        Zf = Z if Z.dtype == np.float64 else ocodecs.bf16_decode(Z)
+        return Zf @ ocodecs.bf16_decode(B)
+    monkeypatch.setattr(omlp, "col_gelu", col_gelu)
+    monkeypatch.setattr(omlp, "row_partial", row_partial)
+    assert _pins_fail([pins.test_tiny_tp2_matches_brute_force,
+                       lambda: pins.test_random_tiny_matches_brute_force(7, 16, 16, 4, 12)])
+
+
+def test_partial_sum_dropping_a_rank_is_caught(monkeypatch):
+    monkeypatch.setattr(omlp, "partial_sum", lambda parts: sum(list(parts)[:-1]))
+    monkeypatch.setattr(oracle, "partial_sum", omlp.partial_sum)
+    assert _pins_fail([pins.test_tiny_tp2_closed_form,
+                       lambda: pins.test_sum_of_shards_equals_unsharded(40, 48, 4, 21)])
+
+
+FP8_PINS = [
+    lambda: pins.test_fp8_path_matches_brute_force(4, 16, 8, 30),
+    lambda: pins.test_fp8_path_matches_brute_force(6, 32, 16, 31),
+    pins.test_quant_scale_and_codes,
+    pins.test_quant_matches_torch_float8,
+]
+
+
+def test_fp8_scale_inverted_is_caught(monkeypatch):
+    monkeypatch.setattr(omlp, "row_partial_e4m3",
+                        lambda Zq, sZ, Bq, sB: (ocodecs.e4m3_decode(Zq) @ ocodecs.e4m3_decode(Bq))
+                        * (float(sZ) * float(sB)))
+    assert _pins_fail(FP8_PINS)
+
+
+def test_fp8_no_clamp_rounding_mode_is_caught(monkeypatch):
+    # quantising by truncation toward zero instead of RNE
+    def quant(T, s):
+        v = (ocodecs.bf16_decode(T).astype(np.float32) * np.float32(s)).astype(np.float64)
+        pos = ocodecs.e4m3_decode(np.arange(0x7F, dtype=np.uint8))
+        idx = np.searchsorted(pos, np.abs(v), side="right") - 1
+        return (idx.astype(np.uint8) | np.where(v < 0, 0x80, 0).astype(np.uint8))
+    monkeypatch.setattr(omlp, "quant_e4m3", quant)
+    assert _pins_fail(FP8_PINS)

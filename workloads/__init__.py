@@ -1,0 +1,134 @@
+"""Seeded synthetic inputs for the tensor-parallel MLP shard.
+
+This module only draws random numbers and stores them as bfloat16 bit
+patterns.  It holds none of the MLP's arithmetic, and both the CPU oracle and
+the GPU path consume exactly the bits it returns.
+
+The MLP block is Y = GeLU(X·A)·B with A of shape [d, 4d] and B of shape
+[4d, d] ("Megatron architecture and 6D parallel guide", §3.1 tensor-parallel
+principle).  Rank i of an N-way tensor-parallel group holds the column block
+A_i and the matching row block B_i.
+
+Recipe (the same for every workload):
+  rng = numpy.random.default_rng(seed)          (PCG64)
+  X = rng.standard_normal((M, d))                drawn first, float64
+  A = sigma * rng.standard_normal((d, H))        drawn second
+  B = sigma * rng.standard_normal((H, d))        drawn third
+each then rounded float64 -> float32 (IEEE, round to nearest even) and
+float32 -> bfloat16 (round to nearest even).  H is 4d for a full weight, or
+the shard width F when a workload draws one rank's shard directly.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+__all__ = ["Workload", "WORKLOADS", "make_inputs", "make_random", "bf16_bits_from_f32",
+           "bf16_bits_to_f32"]
+
+
+@dataclass(frozen=True)
+class Workload:
+    """One MLP shape.  H is the column count of the drawn A (4d, or F)."""
+    name: str
+    M: int            # tokens (rows of X)
+    d: int            # model width
+    H: int            # columns of the drawn A / rows of the drawn B
+    N: int            # tensor-parallel degree the drawn A/B are split over
+    sigma: float      # std-dev of A and B entries
+    seed: int
+    description: str = ""
+    fp8: bool = False  # the workload runs the e4m3 variant of the path
+    tags: tuple = field(default_factory=tuple)
+
+    @property
+    def F(self) -> int:
+        return self.H // self.N
+
+    def flops_per_shard(self) -> int:
+        """Two GEMMs of 2·M·d·F flops each."""
+        return 4 * self.M * self.d * self.F
+
+
+WORKLOADS = {
+    # Tiny MLP at TP=2, both ranks run.
+    "tiny_tp2": Workload("tiny_tp2", M=32, d=64, H=256, N=2, sigma=0.02, seed=0,
+                         description="X[32x64], A[64x256], B[256x64], TP N=2, both ranks"),
+    # GPT-2-small width, unsharded (N=1): 8 sequences x 1024 tokens.
+    "gpt2s_n1": Workload("gpt2s_n1", M=8192, d=768, H=3072, N=1, sigma=0.02, seed=1,
+                         description="X[8192x768], A[768x3072], B[3072x768], N=1"),
+    # 7B-class width d=4096 at TP=8: 4 sequences x 2048 tokens; full A, B drawn
+    # and sliced into 8 shards A_i[4096x2048], B_i[2048x4096].
+    "7b_tp8": Workload("7b_tp8", M=8192, d=4096, H=16384, N=8, sigma=0.02, seed=2,
+                       description="X[8192x4096], A[4096x16384] -> A_i[4096x2048], "
+                                   "B[16384x4096] -> B_i[2048x4096], TP N=8, all ranks"),
+    # 175B-class width d=12288 at TP=8: one 2048-token micro-batch; one rank's
+    # shard drawn directly at its shape (every rank is statistically alike).
+    "175b_tp8": Workload("175b_tp8", M=2048, d=12288, H=6144, N=1, sigma=0.006, seed=3,
+                         description="X[2048x12288], A_i[12288x6144], B_i[6144x12288], "
+                                     "one TP=8 rank's shard"),
+    # The same shard in fp8 e4m3 with per-tensor amax scales.
+    "175b_tp8_e4m3": Workload("175b_tp8_e4m3", M=2048, d=12288, H=6144, N=1, sigma=0.006,
+                              seed=3, fp8=True,
+                              description="175b_tp8 shard quantised to e4m3, per-tensor "
+                                          "scale 448/amax, bf16 output"),
+}
+
+
+def bf16_bits_from_f32(x32: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns, round to nearest even (finite inputs)."""
+    u = np.ascontiguousarray(x32, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return u.astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns -> float32 (exact)."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def _draw_bf16(rng: np.random.Generator, shape, sigma: float) -> np.ndarray:
+    x = rng.standard_normal(shape)
+    if sigma != 1.0:
+        x *= sigma
+    return bf16_bits_from_f32(x.astype(np.float32))
+
+
+def make_random(M: int, d: int, H: int, seed: int, sigma: float = 0.02,
+                x_sigma: float = 1.0):
+    """(X, A, B) as uint16 bfloat16 bit arrays of shapes [M,d], [d,H], [H,d]."""
+    rng = np.random.default_rng(seed)
+    X = _draw_bf16(rng, (M, d), x_sigma)
+    A = _draw_bf16(rng, (d, H), sigma)
+    B = _draw_bf16(rng, (H, d), sigma)
+    return X, A, B
+
+
+def make_inputs(name_or_wl) -> tuple:
+    """Inputs of a named workload: (X, A, B) bfloat16 bit arrays (uint16)."""
+    wl = WORKLOADS[name_or_wl] if isinstance(name_or_wl, str) else name_or_wl
+    return make_random(wl.M, wl.d, wl.H, wl.seed, wl.sigma)
+
+
+def make_integer_valued(M: int, d: int, H: int, seed: int, lo: int = -4, hi: int = 4):
+    """Small-integer-valued bfloat16 inputs (every value exact in bf16).
+
+    With |x| <= 4 and sums far below 2**24 every fp32 dot product is exact, so
+    integer GEMM results can be compared bit for bit.
+    """
+    rng = np.random.default_rng(seed)
+    X = rng.integers(lo, hi + 1, size=(M, d)).astype(np.float32)
+    A = rng.integers(lo, hi + 1, size=(d, H)).astype(np.float32)
+    B = rng.integers(lo, hi + 1, size=(H, d)).astype(np.float32)
+    return bf16_bits_from_f32(X), bf16_bits_from_f32(A), bf16_bits_from_f32(B)
+
+
+def sample_rows(M: int, count: int, seed: int = 1234) -> np.ndarray:
+    """Sorted distinct row indices in [0, M), always including 0 and M-1."""
+    rng = np.random.default_rng(seed)
+    count = min(count, M)
+    rows = set([0, M - 1])
+    if count > len(rows):
+        rows.update(rng.choice(M, size=count, replace=False).tolist())
+    return np.array(sorted(rows), dtype=np.int64)
