@@ -1,0 +1,293 @@
+#!/usr/bin/env python3
+"""Throughput of the tensor-parallel MLP shard path on one MI355X.
+
+One step is one pass of the whole path over one batch: for every rank i of the
+N-way split, the column-parallel GEMM with fused GeLU (Z_i = bf16(GeLU(X·A_i)))
+and the row-parallel GEMM (Y_i = Z_i·B_i, fp32), then the on-device sum of the
+N partials (Y = Σ_i Y_i). These are the same two launches tp_mlp_shard makes
+per rank; the bench calls them separately so each kernel can be timed with HIP
+events on the stream it runs on.
+
+Default workload: 7b_tp8 - d = 4096, TP N = 8, X[8192x4096] (4 x 2048 tokens),
+A_i[4096x2048], B_i[2048x4096]; all 8 ranks then the sum. Other workloads:
+gpt2s_n1, 175b_tp8, 175b_tp8_e4m3 (fp8: col GEMM + GeLU + amax, requantise Z,
+row GEMM; inputs quantised once, outside the timed region).
+
+Prints one JSON line. `value` is TFLOP/s over the whole step (FLOPs =
+4·M·d·F per rank shard; GeLU, scaling and the sum are not counted).
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+
+def _host_cores() -> int:
+    n = len(os.sched_getaffinity(0))
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and int(omp) > 0:
+        n = min(n, int(omp))
+    return max(1, n)
+
+
+HOST_CORES = _host_cores()
+# the oracle's BLAS thread count is fixed when numpy loads
+os.environ.setdefault("OPENBLAS_NUM_THREADS", str(HOST_CORES))
+
+import numpy as np  # noqa: E402
+
+METRIC = "TFLOP/s and % of MFMA peak per TP-rank MLP shard (GeLU(X·A_i)·B_i), 1 GPU"
+PEAK_TFLOPS = {"bf16": 2516.6, "e4m3": 5033.2}   # MI355X dense MFMA (256 CU x 2.4 GHz)
+HBM_PEAK_GBS = 8000.0
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="7b_tp8")
+    p.add_argument("--no-cpu-baseline", action="store_true", help="skip the timed oracle leg")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="stop adding oracle row chunks once this much CPU time is spent")
+    p.add_argument("--partial-dtype", choices=["f32", "bf16"], default="f32")
+    return p.parse_args()
+
+
+def dev_bf16(bits):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+class KernelTimer:
+    """HIP events recorded on the current stream around each launch."""
+
+    def __init__(self):
+        self.marks = {}
+
+    def around(self, name, fn):
+        import torch
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        self.marks.setdefault(name, []).append((a, b))
+
+    def summary(self):
+        out = {}
+        for name, pairs in self.marks.items():
+            ms = [a.elapsed_time(b) for a, b in pairs]
+            out[name] = {"launches": len(ms), "avg_us": 1e3 * float(np.mean(ms)),
+                         "min_us": 1e3 * float(np.min(ms)), "total_ms": float(np.sum(ms))}
+        return out
+
+
+def build_bf16_step(tpm, wl, partial_dtype):
+    import torch
+    X, A, B = __import__("workloads").make_inputs(wl)
+    Xd, Ad, Bd = dev_bf16(X), dev_bf16(A), dev_bf16(B)
+    M, d, H, N, F = wl.M, wl.d, wl.H, wl.N, wl.F
+    pdt = torch.float32 if partial_dtype == "f32" else torch.bfloat16
+    Z = torch.empty((M, F), dtype=torch.bfloat16, device="cuda")
+    parts = [torch.empty((M, d), dtype=pdt, device="cuda") for _ in range(N)]
+    Y = torch.empty((M, d), dtype=torch.float32, device="cuda")
+    views = [(Ad[:, r * F:(r + 1) * F], Bd[r * F:(r + 1) * F, :]) for r in range(N)]
+
+    def step(timer=None):
+        for r in range(N):
+            A_i, B_i = views[r]
+            if timer is None:
+                tpm.tp_mlp_col_gelu(Xd, A_i, Z)
+                tpm.tp_mlp_row_partial(Z, B_i, parts[r])
+            else:
+                timer.around("col_gelu", lambda: tpm.tp_mlp_col_gelu(Xd, A_i, Z))
+                timer.around("row_partial", lambda: tpm.tp_mlp_row_partial(Z, B_i, parts[r]))
+        if N > 1:
+            if timer is None:
+                tpm.tp_partial_sum(parts, Y=Y)
+            else:
+                timer.around("partial_sum", lambda: tpm.tp_partial_sum(parts, Y=Y))
+
+    kern_flops = {"col_gelu": 2 * M * d * F, "row_partial": 2 * M * d * F}
+    psum_bytes = (N * parts[0].element_size() + Y.element_size()) * M * d
+    out = Y if N > 1 else parts[0]
+    return step, kern_flops, psum_bytes, (X, A, B), out
+
+
+def build_e4m3_step(tpm, wl):
+    import torch
+    X, A, B = __import__("workloads").make_inputs(wl)
+    M, d, F = wl.M, wl.d, wl.F
+
+    def quant(bits):
+        T = dev_bf16(bits)
+        amax = tpm.tp_amax_bf16(T)
+        return tpm.tp_quant_e4m3(T, amax)
+    (Xq, sX), (Aq, sA), (Bq, sB) = quant(X), quant(A), quant(B)
+    torch.cuda.synchronize()
+    Z = torch.empty((M, F), dtype=torch.bfloat16, device="cuda")
+    Zq = torch.empty((M, F), dtype=torch.uint8, device="cuda")
+    za = torch.empty(1, dtype=torch.float32, device="cuda")
+    sZ = torch.empty(1, dtype=torch.float32, device="cuda")
+    Y = torch.empty((M, d), dtype=torch.bfloat16, device="cuda")
+
+    def step(timer=None):
+        calls = [("col_gelu_e4m3", lambda: tpm.tp_mlp_col_gelu_e4m3(Xq, sX, Aq, sA, Z, za)),
+                 ("quant_z", lambda: tpm.tp_quant_e4m3(Z, za, Zq, sZ)),
+                 ("row_partial_e4m3", lambda: tpm.tp_mlp_row_partial_e4m3(Zq, sZ, Bq, sB, Y))]
+        for name, fn in calls:
+            if timer is None:
+                fn()
+            else:
+                timer.around(name, fn)
+
+    kern_flops = {"col_gelu_e4m3": 2 * M * d * F, "row_partial_e4m3": 2 * M * d * F}
+    return step, kern_flops, 0, (X, A, B), Y
+
+
+def cpu_baseline(wl, inputs, budget_s):
+    """Time the oracle as it stands on row chunks of the same step until the budget is spent."""
+    import oracle
+    X, A, B = inputs
+    chunk = max(1, min(wl.M, 1024))
+    if wl.fp8:   # input quantisation is preparation (outside the GPU's timed step too)
+        Xq, sX = oracle.quantize_inputs_e4m3(X)
+        Aq, sA = oracle.quantize_inputs_e4m3(A)
+        Bq, sB = oracle.quantize_inputs_e4m3(B)
+    done = 0
+    t_total = 0.0
+    while done < wl.M and t_total < budget_s:
+        rows = slice(done, min(wl.M, done + chunk))
+        t0 = time.perf_counter()
+        if wl.fp8:
+            oracle.mlp_shard_e4m3(Xq[rows], sX, Aq, sA, Bq, sB)
+        else:
+            parts = [oracle.mlp_shard(X[rows], A, B, wl.N, r) for r in range(wl.N)]
+            if wl.N > 1:
+                oracle.partial_sum(parts)
+        t_total += time.perf_counter() - t0
+        done = rows.stop
+    flops = wl.N * 4 * done * wl.d * wl.F
+    what = (f"rows [0, {done}) of {wl.M} of the {wl.name} step"
+            + (f" (all {wl.N} ranks + partial sum)" if wl.N > 1 else "")
+            + f", float64 numpy/OpenBLAS oracle, {t_total:.2f} s")
+    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": HOST_CORES,
+            "kind": "oracle", "sample": what, "seconds": t_total}
+
+
+def sampled_check(wl, inputs, out, nrows=8):
+    import torch
+    import oracle
+    from workloads import sample_rows
+    X, A, B = inputs
+    rows = sample_rows(wl.M, nrows)
+    got = out[torch.from_numpy(rows).cuda()].double().cpu().numpy()
+    if wl.fp8:
+        return None
+    if wl.N > 1:
+        ref = oracle.mlp_unsharded(X[rows], A, B)
+    else:
+        ref = oracle.mlp_shard(X[rows], A, B, 1, 0)
+    return float(np.max(np.abs(got - ref)) / np.max(np.abs(ref)))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU's share of the path; --gpus {args.gpus} is not "
+              "supported (the N tensor-parallel ranks run one after another on one GPU).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import megatron_tensor_transformer_shard_amd as tpm
+    from workloads import WORKLOADS
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    wl = WORKLOADS[args.workload]
+    dtype = "e4m3" if wl.fp8 else "bf16"
+    log(f"bench: workload {wl.name}: {wl.description}")
+    if wl.fp8:
+        step, kern_flops, psum_bytes, inputs, out = build_e4m3_step(tpm, wl)
+    else:
+        step, kern_flops, psum_bytes, inputs, out = build_bf16_step(tpm, wl, args.partial_dtype)
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"bench: warmup {args.warmup} steps done")
+
+    # whole-step timing: exactly K steps between two synchronisations
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t0
+    ms_per_step = 1e3 * wall_s / max(1, args.steps)
+    flops_step = wl.N * wl.flops_per_shard()
+    value = flops_step / (ms_per_step * 1e-3) / 1e12
+    log(f"bench: {args.steps} steps, {ms_per_step:.3f} ms/step, {value:.1f} TFLOP/s")
+
+    # per-kernel timing with events on the launch stream (separate pass)
+    timer = KernelTimer()
+    for _ in range(args.steps):
+        step(timer)
+    torch.cuda.synchronize()
+    kstats = timer.summary()
+    peak = PEAK_TFLOPS[dtype]
+    for name, fl in kern_flops.items():
+        kstats[name]["tflops"] = fl / (kstats[name]["avg_us"] * 1e-6) / 1e12
+        kstats[name]["frac_of_peak"] = kstats[name]["tflops"] / peak
+    if "partial_sum" in kstats:
+        kstats["partial_sum"]["GBps"] = psum_bytes / (kstats["partial_sum"]["avg_us"] * 1e-6) / 1e9
+    dom = max(kern_flops, key=lambda k: kstats[k]["total_ms"])
+    ach = kstats[dom]["tflops"]
+    roofline = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": None,
+                "flops_per_launch": kern_flops[dom], "avg_launch_us": round(kstats[dom]["avg_us"], 2)}
+
+    check = sampled_check(wl, inputs, out)
+    props = torch.cuda.get_device_properties(0)
+    device = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
+              "cus": props.multi_processor_count}
+    clk = getattr(props, "clock_rate", None)
+    if clk:
+        device["clock_khz"] = clk
+        device["peak_from_props_tflops"] = props.multi_processor_count * clk * 1e3 * (
+            4096 if dtype == "bf16" else 8192) / 1e12
+
+    result = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
+        "data": "synthetic: seeded X~N(0,1), weights~N(0,sigma^2), bf16 (no trained weights)",
+        "config": {"workload": wl.name, "M": wl.M, "d": wl.d, "F": wl.F, "tp_ranks": wl.N,
+                   "partial_dtype": "bf16" if wl.fp8 else args.partial_dtype,
+                   "parallelism": f"tp{wl.N} ranks sequentially on 1 GPU" if wl.N > 1 else "none"},
+        "pct_of_peak": round(100 * value / peak, 2),
+        "roofline": roofline,
+        "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                    for k, v in kstats.items()},
+        "check_max_err_ratio_8rows": check,
+        "device": device,
+    }
+    if not args.no_cpu_baseline:
+        log("bench: timing the CPU oracle")
+        result["cpu_baseline"] = cpu_baseline(wl, inputs, args.cpu_seconds)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,204 @@
+/*
+ * tpmlp.h - one tensor-parallel rank's share of the Megatron MLP block on an
+ * AMD Instinct MI355X (gfx950), as a C ABI.
+ *
+ * The block is Y = GeLU(X·A)·B with A [d, 4d] and B [4d, d]. With N-way tensor
+ * parallelism the first weight is split by columns and the second by rows;
+ * rank i holds A_i = A[:, i·F:(i+1)·F] and B_i = B[i·F:(i+1)·F, :], F = 4d/N
+ * ("Megatron architecture and 6D parallel guide", §3.1 tensor-parallel
+ * principle, TP=2 example). Each rank computes Z_i = GeLU(X·A_i) with no
+ * exchange, because GeLU is elementwise, and its partial output
+ * Y_i = Z_i·B_i; the block's output is the sum of the partials,
+ * Y = Σ_i Y_i ("Megatron-LM deep architecture", column/row-parallel section,
+ * eq. for Output). On the pages that sum is one AllReduce(sum); here it is a
+ * plain on-device sum of partials computed one after another on one GPU.
+ *
+ * Conventions shared by every call:
+ *  - Matrices are row-major. X is [M, d], Z_i is [M, F], Y_i and Y are [M, d];
+ *    these are dense (row stride = column count). Weights use the math layout
+ *    of the pages' formula (A: [d, H], B: [H, d]), not nn.Linear's [out, in].
+ *  - Pointers named as device pointers must be device memory of the current
+ *    HIP device; host pointers are named as such. All data pointers must be
+ *    16-byte aligned and every row stride in bytes a multiple of 16, so d and
+ *    F must be multiples of 8 for bf16 and of 16 for e4m3. M is any value
+ *    >= 1 (partial tiles are handled); M = 0 is a no-op that returns TPM_OK.
+ *  - The caller owns every buffer and keeps it alive until the work on
+ *    `stream` has finished. The library allocates nothing, keeps no pointers
+ *    and has no global mutable state. Outputs are overwritten, never
+ *    accumulated, and must not overlap any input (TPM_ERR_ALIAS).
+ *  - `stream` is a hipStream_t passed as void*; NULL means the default
+ *    stream. Every call only enqueues work and returns; device faults surface
+ *    at the caller's next synchronisation.
+ *  - Arguments are validated on the host before anything is enqueued; a
+ *    non-zero status means no work was enqueued, except TPM_ERR_HIP, which
+ *    reports a failed launch (work of earlier launches of the same call may
+ *    have been enqueued).
+ *  - bfloat16 rounding is round-to-nearest-even. GeLU is the exact form
+ *    x·Φ(x) = ½·x·(1 + erf(x/√2)) (the pages name GeLU without defining it).
+ */
+#ifndef TPMLP_H
+#define TPMLP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TPM_ABI_VERSION 1
+
+/* Element types. */
+typedef enum {
+  TPM_BF16 = 0, /* bfloat16 */
+  TPM_F32 = 1,  /* IEEE binary32 */
+  TPM_E4M3 = 2  /* OCP 8-bit float E4M3 ("E4M3FN": max 448, no inf) */
+} tpm_dtype;
+
+/* Status codes (all calls return int). */
+typedef enum {
+  TPM_OK = 0,
+  TPM_ERR_NULL = -1,      /* a required pointer is NULL */
+  TPM_ERR_ARG = -2,       /* N < 1, N > TPM_MAX_PARTS, rank not in [0, N) */
+  TPM_ERR_SHAPE = -3,     /* negative or inconsistent sizes, H not divisible by N,
+                             a width that is not a multiple of 8 (16 for e4m3) */
+  TPM_ERR_DTYPE = -4,     /* unsupported element type for this call */
+  TPM_ERR_ALIGN = -5,     /* pointer not 16-byte aligned, row stride not 16-byte multiple */
+  TPM_ERR_WORKSPACE = -6, /* workspace NULL or smaller than the size query returns */
+  TPM_ERR_ALIAS = -7,     /* an output overlaps an input */
+  TPM_ERR_HIP = -8        /* a HIP launch failed */
+} tpm_status;
+
+/* Largest number of partials tp_partial_sum accepts in one call. */
+#define TPM_MAX_PARTS 64
+
+int tp_abi_version(void);
+/* Static string naming a status code; never NULL. */
+const char* tp_status_string(int status);
+
+/*
+ * Column-parallel step ("Megatron-LM deep architecture", column-parallel
+ * linear: every rank takes the same X and computes GeLU(X·W_1,i) locally).
+ *   Z_i = bf16(GeLU(X · A_i)), accumulated in fp32, GeLU in fp32, one
+ *   rounding to bf16 per element.
+ * X   : device, bf16 [M, d], dense.
+ * A_i : device, bf16 [d, F] with row stride lda >= F elements (lda = H when
+ *       A_i is a column block of a full A [d, H]).
+ * Z_i : device, bf16 [M, F], dense; written.
+ */
+int tp_mlp_col_gelu(const void* X, const void* A_i, int64_t lda, void* Z_i,
+                    int64_t M, int64_t d, int64_t F, void* stream);
+
+/*
+ * Row-parallel step ("Megatron-LM deep architecture", row-parallel linear:
+ * the local activation times the local row block of W_2 gives the partial).
+ *   Y_i = Z_i · B_i, accumulated in fp32.
+ * Z_i : device, bf16 [M, F], dense.
+ * B_i : device, bf16 [F, d], dense (a row block of a full B is dense).
+ * Y_i : device, [M, d], dense, y_dtype TPM_F32 (default) or TPM_BF16.
+ */
+int tp_mlp_row_partial(const void* Z_i, const void* B_i, void* Y_i, int y_dtype,
+                       int64_t M, int64_t F, int64_t d, void* stream);
+
+/*
+ * Bytes of device workspace tp_mlp_shard needs (Z_i, bf16 [M, F], 256-byte
+ * aligned). Returns 0 for invalid sizes.
+ */
+size_t tp_mlp_shard_workspace_size(int64_t M, int64_t d, int64_t H, int N);
+
+/*
+ * One rank's partial output of the N-way split MLP
+ * ("Megatron architecture and 6D parallel guide", §3.1 forward pass:
+ * Y_i = GeLU(X·A_i)·B_i on each GPU):
+ *   F = H / N, A_i = A[:, rank·F : (rank+1)·F], B_i = B[rank·F : (rank+1)·F, :],
+ *   Z_i = bf16(GeLU(X·A_i)) into the workspace, then Y_i = Z_i·B_i.
+ * X : device, bf16 [M, d]. A : device, bf16 [d, H]. B : device, bf16 [H, d].
+ * Pass N = 1, rank = 0 with A = A_i [d, F] and B = B_i [F, d] to run a shard
+ * that is stored on its own.
+ * Y_i : device, [M, d], y_dtype TPM_F32 or TPM_BF16.
+ * workspace : device, at least tp_mlp_shard_workspace_size(M, d, H, N) bytes,
+ *   16-byte aligned; its contents on return are Z_i.
+ */
+int tp_mlp_shard(const void* X, const void* A, const void* B, void* Y_i, int y_dtype,
+                 int64_t M, int64_t d, int64_t H, int N, int rank,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Sum of the partial outputs, the arithmetic of the AllReduce(sum) that ends
+ * the block ("Megatron-LM deep architecture", eq. for Output:
+ * Output = Σ_i Y_i):
+ *   Y = Σ_{i=0}^{N-1} parts[i], added in rank order in fp32.
+ * parts : HOST array of N device pointers, each [numel] of part_dtype
+ *   (TPM_F32 or TPM_BF16). 1 <= N <= TPM_MAX_PARTS.
+ * Y : device, [numel] of y_dtype (TPM_F32 or TPM_BF16). Y may be exactly
+ *   parts[0] (in-place) when the dtypes match; any other overlap is an error.
+ */
+int tp_partial_sum(const void* const* parts, int N, int part_dtype, void* Y, int y_dtype,
+                   int64_t numel, void* stream);
+
+/* ------------------------------------------------------------------------
+ * fp8 e4m3 variant ("Megatron-LM deep architecture", FP8 hybrid precision:
+ * E4M3 for forward activation×weight GEMMs, each tensor scaled by a factor
+ * derived from its amax). Current scaling: a tensor's scale is
+ * s = 448 / amax(tensor), an fp32 division (s = 1 when amax = 0); a value t is
+ * stored as e4m3(clamp(fp32(t·s), ±448)), rounded to nearest even; a GEMM of
+ * two quantised operands is divided by the product of their scales.
+ * Scales live in device memory as fp32 s (not 1/s).
+ * ------------------------------------------------------------------------ */
+
+/*
+ * amax[0] = max |T| over numel bf16 values (device T, device amax).
+ * amax is overwritten (the call clears it itself on the stream).
+ */
+int tp_amax_bf16(const void* T, int64_t numel, float* amax, void* stream);
+
+/*
+ * Quantise a bf16 tensor with the scale derived from a device amax:
+ * scale[0] = s = 448/amax[0] (1 if amax[0] == 0); Tq[j] = e4m3(T[j]·s).
+ * T : device bf16 [numel]; amax : device fp32 [1]; Tq : device e4m3 [numel];
+ * scale : device fp32 [1], written. numel must be a multiple of 16.
+ */
+int tp_quant_e4m3(const void* T, int64_t numel, const float* amax, void* Tq, float* scale,
+                  void* stream);
+
+/*
+ * fp8 column-parallel step: Z_i = bf16(GeLU((Xq·Aq_i) / (sX·sA))) and, when
+ * z_amax is not NULL, z_amax[0] = max |Z_i| (the call clears it first).
+ * Xq : device e4m3 [M, d]; Aq_i : device e4m3 [d, F], row stride lda;
+ * sX, sA : device fp32 [1] scales; Z_i : device bf16 [M, F].
+ */
+int tp_mlp_col_gelu_e4m3(const void* Xq, const float* sX, const void* Aq_i, int64_t lda,
+                         const float* sA, void* Z_i, float* z_amax,
+                         int64_t M, int64_t d, int64_t F, void* stream);
+
+/*
+ * fp8 row-parallel step: Y_i = bf16((Zq·Bq_i) / (sZ·sB)).
+ * Zq : device e4m3 [M, F]; Bq_i : device e4m3 [F, d]; sZ, sB : device fp32 [1];
+ * Y_i : device bf16 [M, d].
+ */
+int tp_mlp_row_partial_e4m3(const void* Zq, const float* sZ, const void* Bq_i,
+                            const float* sB, void* Y_i, int64_t M, int64_t F, int64_t d,
+                            void* stream);
+
+/* Bytes of workspace tp_mlp_shard_e4m3 needs: Z (bf16), Zq (e4m3), amax and
+ * scale of Z. Returns 0 for invalid sizes. */
+size_t tp_mlp_shard_e4m3_workspace_size(int64_t M, int64_t d, int64_t H, int N);
+
+/*
+ * fp8 partial output of one rank: with F = H/N and the rank's blocks of the
+ * quantised A [d, H] and B [H, d] (one scale per whole tensor):
+ *   Z = bf16(GeLU((Xq·Aq_i)/(sX·sA))), amax_Z = max|Z|, sZ = 448/amax_Z,
+ *   Zq = e4m3(Z·sZ), Y_i = bf16((Zq·Bq_i)/(sZ·sB)).
+ * Y_i : device bf16 [M, d]. Workspace as for tp_mlp_shard, sized by
+ * tp_mlp_shard_e4m3_workspace_size; on return it holds Z, Zq, amax_Z, sZ.
+ */
+int tp_mlp_shard_e4m3(const void* Xq, const float* sX, const void* Aq, const float* sA,
+                      const void* Bq, const float* sB, void* Y_i,
+                      int64_t M, int64_t d, int64_t H, int N, int rank,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TPMLP_H */

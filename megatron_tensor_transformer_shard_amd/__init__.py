@@ -1,0 +1,307 @@
+"""One tensor-parallel rank's share of the Megatron MLP block on MI355X.
+
+Y_i = GeLU(X·A_i)·B_i, with A_i the column block and B_i the matching row
+block of the MLP weights ("Megatron architecture and 6D parallel guide",
+§3.1; "Megatron-LM deep architecture", column/row-parallel section), and
+Y = Σ_i Y_i.
+
+This module is a thin ctypes binding over libtpmlp.so (C ABI in
+include/tpmlp.h): it checks tensor dtypes/devices/contiguity, passes raw
+device pointers, sizes and torch's current HIP stream, and raises on a
+non-zero status. Every step of the computation runs in the library's HIP
+kernels; there is no fallback. Importing fails loudly when the library has
+not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # loads the HIP runtime that libtpmlp.so then binds to
+
+__all__ = [
+    "LIB_PATH", "TpmError", "abi_version", "status_string",
+    "tp_mlp_col_gelu", "tp_mlp_row_partial", "tp_mlp_shard", "tp_mlp_shard_workspace_size",
+    "tp_partial_sum", "tp_amax_bf16", "tp_quant_e4m3", "tp_mlp_col_gelu_e4m3",
+    "tp_mlp_row_partial_e4m3", "tp_mlp_shard_e4m3", "tp_mlp_shard_e4m3_workspace_size",
+    "TPM_BF16", "TPM_F32", "TPM_E4M3", "EXPORTED_SYMBOLS",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtpmlp.so")
+
+TPM_BF16, TPM_F32, TPM_E4M3 = 0, 1, 2
+TPM_MAX_PARTS = 64
+
+_i64, _int, _vp, _sz = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+_fp = ctypes.c_void_p  # float* (device)
+
+# name -> (restype, argtypes); mirrors include/tpmlp.h
+_SIGNATURES = {
+    "tp_abi_version": (_int, []),
+    "tp_status_string": (ctypes.c_char_p, [_int]),
+    "tp_mlp_col_gelu": (_int, [_vp, _vp, _i64, _vp, _i64, _i64, _i64, _vp]),
+    "tp_mlp_row_partial": (_int, [_vp, _vp, _vp, _int, _i64, _i64, _i64, _vp]),
+    "tp_mlp_shard_workspace_size": (_sz, [_i64, _i64, _i64, _int]),
+    "tp_mlp_shard": (_int, [_vp, _vp, _vp, _vp, _int, _i64, _i64, _i64, _int, _int, _vp, _sz, _vp]),
+    "tp_partial_sum": (_int, [ctypes.POINTER(_vp), _int, _int, _vp, _int, _i64, _vp]),
+    "tp_amax_bf16": (_int, [_vp, _i64, _fp, _vp]),
+    "tp_quant_e4m3": (_int, [_vp, _i64, _fp, _vp, _fp, _vp]),
+    "tp_mlp_col_gelu_e4m3": (_int, [_vp, _fp, _vp, _i64, _fp, _vp, _fp, _i64, _i64, _i64, _vp]),
+    "tp_mlp_row_partial_e4m3": (_int, [_vp, _fp, _vp, _fp, _vp, _i64, _i64, _i64, _vp]),
+    "tp_mlp_shard_e4m3_workspace_size": (_sz, [_i64, _i64, _i64, _int]),
+    "tp_mlp_shard_e4m3": (_int, [_vp, _fp, _vp, _fp, _vp, _fp, _vp, _i64, _i64, _i64, _int, _int,
+                                 _vp, _sz, _vp]),
+}
+EXPORTED_SYMBOLS = tuple(_SIGNATURES)
+
+
+def _load_library():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -m megatron_tensor_transformer_shard_amd.build_lib` "
+            "(there is no CPU fallback)")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load_library()
+
+
+class TpmError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+def abi_version() -> int:
+    return lib.tp_abi_version()
+
+
+def status_string(status: int) -> str:
+    return lib.tp_status_string(status).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise TpmError(status, where)
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype, ndim=None, contiguous=True):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU (got {t.device})")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must be {ndim}-D (got shape {tuple(t.shape)})")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _dtype_code(dt) -> int:
+    if dt == torch.float32:
+        return TPM_F32
+    if dt == torch.bfloat16:
+        return TPM_BF16
+    raise TypeError(f"unsupported dtype {dt}")
+
+
+def _fptr(t: torch.Tensor) -> int:
+    _need(t, "scale/amax", torch.float32, contiguous=False)
+    return t.data_ptr()
+
+
+# --------------------------------------------------------------- bf16 path
+
+def tp_mlp_col_gelu(X: torch.Tensor, A_i: torch.Tensor, Z_i: torch.Tensor | None = None,
+                    stream=None) -> torch.Tensor:
+    """Z_i = bf16(GeLU(X·A_i)). X [M, d] bf16; A_i [d, F] bf16 (may be a column
+    slice of a full A: unit column stride, any row stride)."""
+    _need(X, "X", torch.bfloat16, 2)
+    _need(A_i, "A_i", torch.bfloat16, 2, contiguous=False)
+    if A_i.stride(1) != 1:
+        raise ValueError("A_i must have unit column stride")
+    M, d = X.shape
+    d2, F = A_i.shape
+    if d2 != d:
+        raise ValueError(f"inner dimensions differ: X {tuple(X.shape)}, A_i {tuple(A_i.shape)}")
+    if Z_i is None:
+        Z_i = torch.empty((M, F), dtype=torch.bfloat16, device=X.device)
+    _need(Z_i, "Z_i", torch.bfloat16, 2)
+    if tuple(Z_i.shape) != (M, F):
+        raise ValueError("Z_i has the wrong shape")
+    _check(lib.tp_mlp_col_gelu(X.data_ptr(), A_i.data_ptr(), A_i.stride(0), Z_i.data_ptr(),
+                               M, d, F, _stream(stream)), "tp_mlp_col_gelu")
+    return Z_i
+
+
+def tp_mlp_row_partial(Z_i: torch.Tensor, B_i: torch.Tensor, Y_i: torch.Tensor | None = None,
+                       out_dtype=torch.float32, stream=None) -> torch.Tensor:
+    """Y_i = Z_i·B_i (fp32 or bf16). Z_i [M, F] bf16; B_i [F, d] bf16."""
+    _need(Z_i, "Z_i", torch.bfloat16, 2)
+    _need(B_i, "B_i", torch.bfloat16, 2)
+    M, F = Z_i.shape
+    F2, d = B_i.shape
+    if F2 != F:
+        raise ValueError(f"inner dimensions differ: Z_i {tuple(Z_i.shape)}, B_i {tuple(B_i.shape)}")
+    if Y_i is None:
+        Y_i = torch.empty((M, d), dtype=out_dtype, device=Z_i.device)
+    _need(Y_i, "Y_i", None, 2)
+    if tuple(Y_i.shape) != (M, d):
+        raise ValueError("Y_i has the wrong shape")
+    _check(lib.tp_mlp_row_partial(Z_i.data_ptr(), B_i.data_ptr(), Y_i.data_ptr(),
+                                  _dtype_code(Y_i.dtype), M, F, d, _stream(stream)),
+           "tp_mlp_row_partial")
+    return Y_i
+
+
+def tp_mlp_shard_workspace_size(M: int, d: int, H: int, N: int) -> int:
+    return int(lib.tp_mlp_shard_workspace_size(M, d, H, N))
+
+
+def tp_mlp_shard(X: torch.Tensor, A: torch.Tensor, B: torch.Tensor, N: int, rank: int,
+                 Y_i: torch.Tensor | None = None, out_dtype=torch.float32,
+                 workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Rank `rank`'s partial output GeLU(X·A_i)·B_i of the N-way split of A [d, H], B [H, d]."""
+    _need(X, "X", torch.bfloat16, 2)
+    _need(A, "A", torch.bfloat16, 2)
+    _need(B, "B", torch.bfloat16, 2)
+    M, d = X.shape
+    dA, H = A.shape
+    if dA != d or tuple(B.shape) != (H, d):
+        raise ValueError(f"shape mismatch: X {tuple(X.shape)}, A {tuple(A.shape)}, B {tuple(B.shape)}")
+    if Y_i is None:
+        Y_i = torch.empty((M, d), dtype=out_dtype, device=X.device)
+    _need(Y_i, "Y_i", None, 2)
+    if tuple(Y_i.shape) != (M, d):
+        raise ValueError("Y_i has the wrong shape")
+    need = tp_mlp_shard_workspace_size(M, d, H, N) if N >= 1 else 0
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=X.device)
+    _need(workspace, "workspace", None)
+    _check(lib.tp_mlp_shard(X.data_ptr(), A.data_ptr(), B.data_ptr(), Y_i.data_ptr(),
+                            _dtype_code(Y_i.dtype), M, d, H, N, rank, workspace.data_ptr(),
+                            workspace.numel() * workspace.element_size(), _stream(stream)),
+           "tp_mlp_shard")
+    return Y_i
+
+
+def tp_partial_sum(parts, Y: torch.Tensor | None = None, out_dtype=None,
+                   stream=None) -> torch.Tensor:
+    """Y = Σ_i parts[i], in rank order, fp32 accumulation."""
+    parts = list(parts)
+    if not parts:
+        raise ValueError("no partials")
+    dt = parts[0].dtype
+    for i, p in enumerate(parts):
+        _need(p, f"parts[{i}]", dt)
+        if p.shape != parts[0].shape:
+            raise ValueError("partials differ in shape")
+    if Y is None:
+        Y = torch.empty(parts[0].shape, dtype=out_dtype or dt, device=parts[0].device)
+    _need(Y, "Y", None)
+    if Y.numel() != parts[0].numel():
+        raise ValueError("Y has the wrong size")
+    arr = (_vp * len(parts))(*[p.data_ptr() for p in parts])
+    _check(lib.tp_partial_sum(arr, len(parts), _dtype_code(dt), Y.data_ptr(),
+                              _dtype_code(Y.dtype), parts[0].numel(), _stream(stream)),
+           "tp_partial_sum")
+    return Y
+
+
+# ---------------------------------------------------------------- fp8 path
+# e4m3 tensors are carried as torch.uint8 tensors of codes.
+
+def tp_amax_bf16(T: torch.Tensor, amax: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    _need(T, "T", torch.bfloat16)
+    if amax is None:
+        amax = torch.empty(1, dtype=torch.float32, device=T.device)
+    _check(lib.tp_amax_bf16(T.data_ptr(), T.numel(), _fptr(amax), _stream(stream)), "tp_amax_bf16")
+    return amax
+
+
+def tp_quant_e4m3(T: torch.Tensor, amax: torch.Tensor, Tq: torch.Tensor | None = None,
+                  scale: torch.Tensor | None = None, stream=None):
+    """(Tq, scale): e4m3 codes (uint8) of T·s, s = 448/amax (device fp32)."""
+    _need(T, "T", torch.bfloat16)
+    if Tq is None:
+        Tq = torch.empty(T.shape, dtype=torch.uint8, device=T.device)
+    if scale is None:
+        scale = torch.empty(1, dtype=torch.float32, device=T.device)
+    _need(Tq, "Tq", torch.uint8)
+    _check(lib.tp_quant_e4m3(T.data_ptr(), T.numel(), _fptr(amax), Tq.data_ptr(), _fptr(scale),
+                             _stream(stream)), "tp_quant_e4m3")
+    return Tq, scale
+
+
+def tp_mlp_col_gelu_e4m3(Xq, sX, Aq_i, sA, Z_i=None, z_amax=None, stream=None):
+    _need(Xq, "Xq", torch.uint8, 2)
+    _need(Aq_i, "Aq_i", torch.uint8, 2, contiguous=False)
+    if Aq_i.stride(1) != 1:
+        raise ValueError("Aq_i must have unit column stride")
+    M, d = Xq.shape
+    d2, F = Aq_i.shape
+    if d2 != d:
+        raise ValueError("inner dimensions differ")
+    if Z_i is None:
+        Z_i = torch.empty((M, F), dtype=torch.bfloat16, device=Xq.device)
+    _need(Z_i, "Z_i", torch.bfloat16, 2)
+    za = _fptr(z_amax) if z_amax is not None else None
+    _check(lib.tp_mlp_col_gelu_e4m3(Xq.data_ptr(), _fptr(sX), Aq_i.data_ptr(), Aq_i.stride(0),
+                                    _fptr(sA), Z_i.data_ptr(), za, M, d, F, _stream(stream)),
+           "tp_mlp_col_gelu_e4m3")
+    return Z_i
+
+
+def tp_mlp_row_partial_e4m3(Zq, sZ, Bq_i, sB, Y_i=None, stream=None):
+    _need(Zq, "Zq", torch.uint8, 2)
+    _need(Bq_i, "Bq_i", torch.uint8, 2)
+    M, F = Zq.shape
+    F2, d = Bq_i.shape
+    if F2 != F:
+        raise ValueError("inner dimensions differ")
+    if Y_i is None:
+        Y_i = torch.empty((M, d), dtype=torch.bfloat16, device=Zq.device)
+    _need(Y_i, "Y_i", torch.bfloat16, 2)
+    _check(lib.tp_mlp_row_partial_e4m3(Zq.data_ptr(), _fptr(sZ), Bq_i.data_ptr(), _fptr(sB),
+                                       Y_i.data_ptr(), M, F, d, _stream(stream)),
+           "tp_mlp_row_partial_e4m3")
+    return Y_i
+
+
+def tp_mlp_shard_e4m3_workspace_size(M: int, d: int, H: int, N: int) -> int:
+    return int(lib.tp_mlp_shard_e4m3_workspace_size(M, d, H, N))
+
+
+def tp_mlp_shard_e4m3(Xq, sX, Aq, sA, Bq, sB, N: int = 1, rank: int = 0, Y_i=None,
+                      workspace=None, stream=None):
+    """fp8 partial output of one rank (bf16 [M, d]); see include/tpmlp.h."""
+    _need(Xq, "Xq", torch.uint8, 2)
+    _need(Aq, "Aq", torch.uint8, 2)
+    _need(Bq, "Bq", torch.uint8, 2)
+    M, d = Xq.shape
+    dA, H = Aq.shape
+    if dA != d or tuple(Bq.shape) != (H, d):
+        raise ValueError("shape mismatch")
+    if Y_i is None:
+        Y_i = torch.empty((M, d), dtype=torch.bfloat16, device=Xq.device)
+    _need(Y_i, "Y_i", torch.bfloat16, 2)
+    need = tp_mlp_shard_e4m3_workspace_size(M, d, H, N) if N >= 1 else 0
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=Xq.device)
+    _check(lib.tp_mlp_shard_e4m3(Xq.data_ptr(), _fptr(sX), Aq.data_ptr(), _fptr(sA), Bq.data_ptr(),
+                                 _fptr(sB), Y_i.data_ptr(), M, d, H, N, rank, workspace.data_ptr(),
+                                 workspace.numel() * workspace.element_size(), _stream(stream)),
+           "tp_mlp_shard_e4m3")
+    return Y_i

@@ -1,0 +1,302 @@
+// C ABI of the tensor-parallel MLP shard library (declared in include/tpmlp.h).
+//
+// Every entry point validates its arguments on the host before anything is
+// enqueued (so an error status means no work was done), derives the rank's
+// shard views, and enqueues the kernels on the caller's stream.
+#include "../../include/tpmlp.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "kernels.hpp"
+
+namespace {
+
+using tpmlp::OutKind;
+
+constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct Span {
+  uintptr_t lo, hi;  // byte range [lo, hi)
+};
+
+// Bytes touched by a rows x cols matrix with row stride ld (elements of `esize` bytes).
+Span mat_span(const void* p, int64_t rows, int64_t cols, int64_t ld, int64_t esize) {
+  const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+  if (rows <= 0 || cols <= 0) return {lo, lo};
+  return {lo, lo + (uintptr_t)(((rows - 1) * ld + cols) * esize)};
+}
+
+bool overlap(Span a, Span b) { return a.lo < b.hi && b.lo < a.hi && a.lo < a.hi && b.lo < b.hi; }
+
+int status_of(hipError_t e) { return e == hipSuccess ? TPM_OK : TPM_ERR_HIP; }
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+// Shared size checks for a GEMM step with inputs [M, K] and [K, N].
+int check_dims(int64_t M, int64_t K, int64_t N, int64_t mult) {
+  if (M < 0 || K <= 0 || N <= 0) return TPM_ERR_SHAPE;
+  if (M > kMaxDim || K > kMaxDim || N > kMaxDim) return TPM_ERR_SHAPE;
+  if (K % mult != 0 || N % mult != 0) return TPM_ERR_SHAPE;
+  if (M * K > (int64_t(1) << 46) || M * N > (int64_t(1) << 46) || K * N > (int64_t(1) << 46))
+    return TPM_ERR_SHAPE;
+  return TPM_OK;
+}
+
+size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
+
+}  // namespace
+
+extern "C" {
+
+int tp_abi_version(void) { return TPM_ABI_VERSION; }
+
+const char* tp_status_string(int status) {
+  switch (status) {
+    case TPM_OK: return "TPM_OK: success";
+    case TPM_ERR_NULL: return "TPM_ERR_NULL: a required pointer is NULL";
+    case TPM_ERR_ARG: return "TPM_ERR_ARG: invalid N or rank";
+    case TPM_ERR_SHAPE: return "TPM_ERR_SHAPE: invalid or inconsistent sizes";
+    case TPM_ERR_DTYPE: return "TPM_ERR_DTYPE: unsupported element type";
+    case TPM_ERR_ALIGN: return "TPM_ERR_ALIGN: pointer or row stride not 16-byte aligned";
+    case TPM_ERR_WORKSPACE: return "TPM_ERR_WORKSPACE: workspace missing or too small";
+    case TPM_ERR_ALIAS: return "TPM_ERR_ALIAS: an output overlaps an input";
+    case TPM_ERR_HIP: return "TPM_ERR_HIP: a HIP launch failed";
+    default: return "unknown tpmlp status";
+  }
+}
+
+int tp_mlp_col_gelu(const void* X, const void* A_i, int64_t lda, void* Z_i, int64_t M,
+                    int64_t d, int64_t F, void* stream) {
+  int st = check_dims(M, d, F, 8);
+  if (st != TPM_OK) return st;
+  if (lda < F || lda > kMaxDim) return TPM_ERR_SHAPE;
+  if (M == 0) return TPM_OK;
+  if (!X || !A_i || !Z_i) return TPM_ERR_NULL;
+  if (!aligned16(X) || !aligned16(A_i) || !aligned16(Z_i) || lda % 8 != 0) return TPM_ERR_ALIGN;
+  const Span z = mat_span(Z_i, M, F, F, 2);
+  if (overlap(z, mat_span(X, M, d, d, 2)) || overlap(z, mat_span(A_i, d, F, lda, 2)))
+    return TPM_ERR_ALIAS;
+  return status_of(tpmlp::launch_gemm_bf16(static_cast<const uint16_t*>(X), d,
+                                           static_cast<const uint16_t*>(A_i), lda, Z_i, F,
+                                           (int)M, (int)F, (int)d, OutKind::GeluBf16,
+                                           as_stream(stream)));
+}
+
+int tp_mlp_row_partial(const void* Z_i, const void* B_i, void* Y_i, int y_dtype, int64_t M,
+                       int64_t F, int64_t d, void* stream) {
+  if (y_dtype != TPM_F32 && y_dtype != TPM_BF16) return TPM_ERR_DTYPE;
+  int st = check_dims(M, F, d, 8);
+  if (st != TPM_OK) return st;
+  if (M == 0) return TPM_OK;
+  if (!Z_i || !B_i || !Y_i) return TPM_ERR_NULL;
+  if (!aligned16(Z_i) || !aligned16(B_i) || !aligned16(Y_i)) return TPM_ERR_ALIGN;
+  const Span y = mat_span(Y_i, M, d, d, y_dtype == TPM_F32 ? 4 : 2);
+  if (overlap(y, mat_span(Z_i, M, F, F, 2)) || overlap(y, mat_span(B_i, F, d, d, 2)))
+    return TPM_ERR_ALIAS;
+  return status_of(tpmlp::launch_gemm_bf16(
+      static_cast<const uint16_t*>(Z_i), F, static_cast<const uint16_t*>(B_i), d, Y_i, d,
+      (int)M, (int)d, (int)F, y_dtype == TPM_F32 ? OutKind::F32 : OutKind::Bf16,
+      as_stream(stream)));
+}
+
+size_t tp_mlp_shard_workspace_size(int64_t M, int64_t d, int64_t H, int N) {
+  if (M < 0 || d <= 0 || H <= 0 || N < 1 || H % N != 0) return 0;
+  if (M > kMaxDim || H > kMaxDim) return 0;
+  const int64_t F = H / N;
+  return round256((size_t)M * (size_t)F * 2);
+}
+
+int tp_mlp_shard(const void* X, const void* A, const void* B, void* Y_i, int y_dtype, int64_t M,
+                 int64_t d, int64_t H, int N, int rank, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  if (y_dtype != TPM_F32 && y_dtype != TPM_BF16) return TPM_ERR_DTYPE;
+  if (N < 1 || rank < 0 || rank >= N) return TPM_ERR_ARG;
+  if (H <= 0 || H % N != 0) return TPM_ERR_SHAPE;
+  const int64_t F = H / N;
+  int st = check_dims(M, d, F, 8);
+  if (st != TPM_OK) return st;
+  if (H > kMaxDim || H * d > (int64_t(1) << 46)) return TPM_ERR_SHAPE;
+  if (M == 0) return TPM_OK;
+  if (!X || !A || !B || !Y_i) return TPM_ERR_NULL;
+  if (!workspace || workspace_bytes < tp_mlp_shard_workspace_size(M, d, H, N))
+    return TPM_ERR_WORKSPACE;
+  if (!aligned16(X) || !aligned16(A) || !aligned16(B) || !aligned16(Y_i) || !aligned16(workspace))
+    return TPM_ERR_ALIGN;
+  const Span sx = mat_span(X, M, d, d, 2), sa = mat_span(A, d, H, H, 2);
+  const Span sb = mat_span(B, H, d, d, 2);
+  const Span sy = mat_span(Y_i, M, d, d, y_dtype == TPM_F32 ? 4 : 2);
+  const Span sw = {reinterpret_cast<uintptr_t>(workspace),
+                   reinterpret_cast<uintptr_t>(workspace) + (uintptr_t)(M * F * 2)};
+  if (overlap(sy, sx) || overlap(sy, sa) || overlap(sy, sb) || overlap(sy, sw) ||
+      overlap(sw, sx) || overlap(sw, sa) || overlap(sw, sb))
+    return TPM_ERR_ALIAS;
+
+  // Shard views ("Megatron architecture and 6D parallel guide", §3.1):
+  // A_i = A[:, rank·F : (rank+1)·F] (row stride H), B_i = B[rank·F : (rank+1)·F, :].
+  const uint16_t* A_i = static_cast<const uint16_t*>(A) + (int64_t)rank * F;
+  const uint16_t* B_i = static_cast<const uint16_t*>(B) + (int64_t)rank * F * d;
+  uint16_t* Z = static_cast<uint16_t*>(workspace);
+  hipStream_t s = as_stream(stream);
+  hipError_t e = tpmlp::launch_gemm_bf16(static_cast<const uint16_t*>(X), d, A_i, H, Z, F,
+                                         (int)M, (int)F, (int)d, OutKind::GeluBf16, s);
+  if (e != hipSuccess) return TPM_ERR_HIP;
+  e = tpmlp::launch_gemm_bf16(Z, F, B_i, d, Y_i, d, (int)M, (int)d, (int)F,
+                              y_dtype == TPM_F32 ? OutKind::F32 : OutKind::Bf16, s);
+  return status_of(e);
+}
+
+int tp_partial_sum(const void* const* parts, int N, int part_dtype, void* Y, int y_dtype,
+                   int64_t numel, void* stream) {
+  if ((part_dtype != TPM_F32 && part_dtype != TPM_BF16) ||
+      (y_dtype != TPM_F32 && y_dtype != TPM_BF16))
+    return TPM_ERR_DTYPE;
+  if (N < 1 || N > TPM_MAX_PARTS) return TPM_ERR_ARG;
+  if (numel < 0 || numel > (int64_t(1) << 40)) return TPM_ERR_SHAPE;
+  if (numel == 0) return TPM_OK;
+  if (!parts || !Y) return TPM_ERR_NULL;
+  for (int i = 0; i < N; ++i)
+    if (!parts[i]) return TPM_ERR_NULL;
+  if (!aligned16(Y)) return TPM_ERR_ALIGN;
+  for (int i = 0; i < N; ++i)
+    if (!aligned16(parts[i])) return TPM_ERR_ALIGN;
+  const int64_t pe = part_dtype == TPM_F32 ? 4 : 2, ye = y_dtype == TPM_F32 ? 4 : 2;
+  const Span sy = mat_span(Y, 1, numel, numel, ye);
+  for (int i = 0; i < N; ++i) {
+    const Span sp = mat_span(parts[i], 1, numel, numel, pe);
+    const bool in_place = (i == 0 && parts[0] == Y && pe == ye);
+    if (!in_place && overlap(sy, sp)) return TPM_ERR_ALIAS;
+  }
+  return status_of(tpmlp::launch_partial_sum(parts, N, part_dtype == TPM_BF16, Y,
+                                             y_dtype == TPM_BF16, numel, as_stream(stream)));
+}
+
+// ------------------------------------------------------------------ fp8 --
+
+int tp_amax_bf16(const void* T, int64_t numel, float* amax, void* stream) {
+  if (numel < 0 || numel > (int64_t(1) << 40)) return TPM_ERR_SHAPE;
+  if (!amax || (!T && numel > 0)) return TPM_ERR_NULL;
+  if ((T && !aligned16(T)) || (reinterpret_cast<uintptr_t>(amax) & 3u)) return TPM_ERR_ALIGN;
+  if (numel > 0 && overlap(mat_span(amax, 1, 1, 1, 4), mat_span(T, 1, numel, numel, 2)))
+    return TPM_ERR_ALIAS;
+  return status_of(tpmlp::launch_amax_bf16(static_cast<const uint16_t*>(T), numel, amax,
+                                           as_stream(stream)));
+}
+
+int tp_quant_e4m3(const void* T, int64_t numel, const float* amax, void* Tq, float* scale,
+                  void* stream) {
+  if (numel < 0 || numel % 16 != 0 || numel > (int64_t(1) << 40)) return TPM_ERR_SHAPE;
+  if (!amax || !scale || ((!T || !Tq) && numel > 0)) return TPM_ERR_NULL;
+  if ((T && !aligned16(T)) || (Tq && !aligned16(Tq)) ||
+      (reinterpret_cast<uintptr_t>(amax) & 3u) || (reinterpret_cast<uintptr_t>(scale) & 3u))
+    return TPM_ERR_ALIGN;
+  const Span st = mat_span(T, 1, numel, numel, 2), sq = mat_span(Tq, 1, numel, numel, 1);
+  const Span ss = mat_span(scale, 1, 1, 1, 4), sa = mat_span(amax, 1, 1, 1, 4);
+  if (overlap(sq, st) || overlap(sq, sa) || overlap(ss, st) || overlap(ss, sq) || overlap(ss, sa))
+    return TPM_ERR_ALIAS;
+  return status_of(tpmlp::launch_quant_e4m3(static_cast<const uint16_t*>(T), numel, amax,
+                                            static_cast<uint8_t*>(Tq), scale, as_stream(stream)));
+}
+
+int tp_mlp_col_gelu_e4m3(const void* Xq, const float* sX, const void* Aq_i, int64_t lda,
+                         const float* sA, void* Z_i, float* z_amax, int64_t M, int64_t d,
+                         int64_t F, void* stream) {
+  int st = check_dims(M, d, F, 16);
+  if (st != TPM_OK) return st;
+  if (lda < F || lda > kMaxDim) return TPM_ERR_SHAPE;
+  if (M == 0) {
+    if (z_amax) return status_of(tpmlp::launch_fill_f32(z_amax, 0.0f, as_stream(stream)));
+    return TPM_OK;
+  }
+  if (!Xq || !sX || !Aq_i || !sA || !Z_i) return TPM_ERR_NULL;
+  if (!aligned16(Xq) || !aligned16(Aq_i) || !aligned16(Z_i) || lda % 16 != 0 ||
+      (reinterpret_cast<uintptr_t>(z_amax) & 3u))
+    return TPM_ERR_ALIGN;
+  const Span z = mat_span(Z_i, M, F, F, 2);
+  if (overlap(z, mat_span(Xq, M, d, d, 1)) || overlap(z, mat_span(Aq_i, d, F, lda, 1)) ||
+      overlap(z, mat_span(sX, 1, 1, 1, 4)) || overlap(z, mat_span(sA, 1, 1, 1, 4)))
+    return TPM_ERR_ALIAS;
+  if (z_amax && (overlap(mat_span(z_amax, 1, 1, 1, 4), z) ||
+                 overlap(mat_span(z_amax, 1, 1, 1, 4), mat_span(Xq, M, d, d, 1)) ||
+                 overlap(mat_span(z_amax, 1, 1, 1, 4), mat_span(Aq_i, d, F, lda, 1))))
+    return TPM_ERR_ALIAS;
+  return status_of(tpmlp::launch_gemm_e4m3(
+      static_cast<const uint8_t*>(Xq), d, sX, static_cast<const uint8_t*>(Aq_i), lda, sA,
+      static_cast<uint16_t*>(Z_i), F, z_amax, (int)M, (int)F, (int)d, OutKind::GeluBf16,
+      as_stream(stream)));
+}
+
+int tp_mlp_row_partial_e4m3(const void* Zq, const float* sZ, const void* Bq_i, const float* sB,
+                            void* Y_i, int64_t M, int64_t F, int64_t d, void* stream) {
+  int st = check_dims(M, F, d, 16);
+  if (st != TPM_OK) return st;
+  if (M == 0) return TPM_OK;
+  if (!Zq || !sZ || !Bq_i || !sB || !Y_i) return TPM_ERR_NULL;
+  if (!aligned16(Zq) || !aligned16(Bq_i) || !aligned16(Y_i)) return TPM_ERR_ALIGN;
+  const Span y = mat_span(Y_i, M, d, d, 2);
+  if (overlap(y, mat_span(Zq, M, F, F, 1)) || overlap(y, mat_span(Bq_i, F, d, d, 1)) ||
+      overlap(y, mat_span(sZ, 1, 1, 1, 4)) || overlap(y, mat_span(sB, 1, 1, 1, 4)))
+    return TPM_ERR_ALIAS;
+  return status_of(tpmlp::launch_gemm_e4m3(
+      static_cast<const uint8_t*>(Zq), F, sZ, static_cast<const uint8_t*>(Bq_i), d, sB,
+      static_cast<uint16_t*>(Y_i), d, nullptr, (int)M, (int)d, (int)F, OutKind::Bf16,
+      as_stream(stream)));
+}
+
+size_t tp_mlp_shard_e4m3_workspace_size(int64_t M, int64_t d, int64_t H, int N) {
+  if (M < 0 || d <= 0 || H <= 0 || N < 1 || H % N != 0) return 0;
+  if (M > kMaxDim || H > kMaxDim) return 0;
+  const size_t MF = (size_t)M * (size_t)(H / N);
+  return round256(MF * 2) + round256(MF) + 256;
+}
+
+int tp_mlp_shard_e4m3(const void* Xq, const float* sX, const void* Aq, const float* sA,
+                      const void* Bq, const float* sB, void* Y_i, int64_t M, int64_t d, int64_t H,
+                      int N, int rank, void* workspace, size_t workspace_bytes, void* stream) {
+  if (N < 1 || rank < 0 || rank >= N) return TPM_ERR_ARG;
+  if (H <= 0 || H % N != 0) return TPM_ERR_SHAPE;
+  const int64_t F = H / N;
+  int st = check_dims(M, d, F, 16);
+  if (st != TPM_OK) return st;
+  if (H > kMaxDim || H * d > (int64_t(1) << 46)) return TPM_ERR_SHAPE;
+  if (M == 0) return TPM_OK;
+  if (!Xq || !sX || !Aq || !sA || !Bq || !sB || !Y_i) return TPM_ERR_NULL;
+  if (!workspace || workspace_bytes < tp_mlp_shard_e4m3_workspace_size(M, d, H, N))
+    return TPM_ERR_WORKSPACE;
+  if (!aligned16(Xq) || !aligned16(Aq) || !aligned16(Bq) || !aligned16(Y_i) ||
+      !aligned16(workspace))
+    return TPM_ERR_ALIGN;
+  const size_t MF = (size_t)M * (size_t)F;
+  const Span sx = mat_span(Xq, M, d, d, 1), sa = mat_span(Aq, d, H, H, 1);
+  const Span sb = mat_span(Bq, H, d, d, 1), sy = mat_span(Y_i, M, d, d, 2);
+  const Span sw = {reinterpret_cast<uintptr_t>(workspace),
+                   reinterpret_cast<uintptr_t>(workspace) +
+                       tp_mlp_shard_e4m3_workspace_size(M, d, H, N)};
+  const Span ssx = mat_span(sX, 1, 1, 1, 4), ssa = mat_span(sA, 1, 1, 1, 4);
+  const Span ssb = mat_span(sB, 1, 1, 1, 4);
+  for (Span in : {sx, sa, sb, ssx, ssa, ssb})
+    if (overlap(sy, in) || overlap(sw, in)) return TPM_ERR_ALIAS;
+  if (overlap(sy, sw)) return TPM_ERR_ALIAS;
+
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  uint16_t* Z = reinterpret_cast<uint16_t*>(ws);
+  uint8_t* Zq = ws + round256(MF * 2);
+  float* z_amax = reinterpret_cast<float*>(Zq + round256(MF));
+  float* sZ = z_amax + 1;
+  const uint8_t* Aq_i = static_cast<const uint8_t*>(Aq) + (int64_t)rank * F;
+  const uint8_t* Bq_i = static_cast<const uint8_t*>(Bq) + (int64_t)rank * F * d;
+  hipStream_t s = as_stream(stream);
+  hipError_t e = tpmlp::launch_gemm_e4m3(static_cast<const uint8_t*>(Xq), d, sX, Aq_i, H, sA, Z,
+                                         F, z_amax, (int)M, (int)F, (int)d, OutKind::GeluBf16, s);
+  if (e != hipSuccess) return TPM_ERR_HIP;
+  e = tpmlp::launch_quant_e4m3(Z, (int64_t)MF, z_amax, Zq, sZ, s);
+  if (e != hipSuccess) return TPM_ERR_HIP;
+  e = tpmlp::launch_gemm_e4m3(Zq, F, sZ, Bq_i, d, sB, static_cast<uint16_t*>(Y_i), d, nullptr,
+                              (int)M, (int)d, (int)F, OutKind::Bf16, s);
+  return status_of(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,35 @@
+// Internal launch interface between the C ABI (abi.cpp) and the gfx950
+// kernels. Every launcher enqueues on `stream` and returns the launch status;
+// argument validation has already happened in the ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace tpmlp {
+
+enum class OutKind : int { GeluBf16 = 0, F32 = 1, Bf16 = 2 };
+
+// C[M, N] = epilogue(P[M, K] · Q[K, N]); P rows K-contiguous (stride ldp),
+// Q rows N-contiguous (stride ldq), C dense with stride ldc, all bf16 inputs.
+hipError_t launch_gemm_bf16(const uint16_t* P, int64_t ldp, const uint16_t* Q, int64_t ldq,
+                            void* C, int64_t ldc, int M, int N, int K, OutKind out,
+                            hipStream_t stream);
+
+// Y = Σ_i parts[i] in rank order, fp32 accumulation.
+hipError_t launch_partial_sum(const void* const* parts, int nparts, bool parts_bf16, void* Y,
+                              bool y_bf16, int64_t numel, hipStream_t stream);
+
+// fp8 (OCP e4m3) path.
+hipError_t launch_fill_f32(float* p, float v, hipStream_t stream);
+hipError_t launch_amax_bf16(const uint16_t* T, int64_t numel, float* amax, hipStream_t stream);
+hipError_t launch_quant_e4m3(const uint16_t* T, int64_t numel, const float* amax, uint8_t* Tq,
+                             float* scale, hipStream_t stream);
+// C = epilogue((P·Q) / (sP·sQ)); GeluBf16 also folds max|Z| into z_amax when
+// z_amax is not NULL; Bf16 stores bf16.
+hipError_t launch_gemm_e4m3(const uint8_t* P, int64_t ldp, const float* sP, const uint8_t* Q,
+                            int64_t ldq, const float* sQ, uint16_t* C, int64_t ldc, float* z_amax,
+                            int M, int N, int K, OutKind out, hipStream_t stream);
+
+}  // namespace tpmlp

@@ -1,0 +1,117 @@
+// Sum of the tensor-parallel partial outputs, Y = Σ_i Y_i, on one GPU.
+//
+// This is the arithmetic of the AllReduce(sum) that ends the MLP block
+// ("Megatron-LM deep architecture", eq. for Output: Output = Σ_i Y_i). It is
+// HBM-bound: N reads and one write per element. Each thread owns 8
+// consecutive elements per step (one 16-byte load per bf16 part, two per fp32
+// part), issues the loads of up to 8 parts before adding, and adds strictly in
+// rank order in fp32, so the result does not depend on the launch shape.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace tpmlp {
+namespace {
+
+constexpr int kMaxParts = 64;
+constexpr int kThreads = 256;
+
+struct PartPtrs {
+  const void* p[kMaxParts];
+};
+
+template <bool IN_BF16>
+__device__ __forceinline__ void load8(const void* base, int64_t v, float (&x)[8]) {
+  if constexpr (IN_BF16) {
+    const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base) + v);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[2 * j] = bf16_bits_to_f32(w[j] & 0xFFFFu);
+      x[2 * j + 1] = bf16_bits_to_f32(w[j] >> 16);
+    }
+  } else {
+    const f32x4* p = reinterpret_cast<const f32x4*>(base) + 2 * v;
+    const f32x4 a = __builtin_nontemporal_load(p), b = __builtin_nontemporal_load(p + 1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[j] = a[j];
+      x[4 + j] = b[j];
+    }
+  }
+}
+
+template <bool IN_BF16, bool OUT_BF16>
+__global__ __launch_bounds__(kThreads) void partial_sum_kernel(PartPtrs parts, int nparts,
+                                                               void* __restrict__ Y, int64_t nvec,
+                                                               int64_t numel) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t v = (int64_t)blockIdx.x * kThreads + threadIdx.x; v < nvec; v += stride) {
+    float acc[8];
+    load8<IN_BF16>(parts.p[0], v, acc);
+    int i = 1;
+    for (; i + 8 <= nparts; i += 8) {
+      float x[8][8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) load8<IN_BF16>(parts.p[i + j], v, x[j]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] += x[j][e];
+    }
+    for (; i < nparts; ++i) {
+      float x[8];
+      load8<IN_BF16>(parts.p[i], v, x);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += x[e];
+    }
+    if constexpr (OUT_BF16) {
+      u32x4 o = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                 pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
+      reinterpret_cast<u32x4*>(Y)[v] = o;
+    } else {
+      f32x4* q = reinterpret_cast<f32x4*>(Y) + 2 * v;
+      q[0] = f32x4{acc[0], acc[1], acc[2], acc[3]};
+      q[1] = f32x4{acc[4], acc[5], acc[6], acc[7]};
+    }
+  }
+  // Scalar tail (numel not a multiple of 8), handled by the first block.
+  if (blockIdx.x == 0) {
+    for (int64_t e = nvec * 8 + threadIdx.x; e < numel; e += kThreads) {
+      float a = 0.0f;
+      for (int i = 0; i < nparts; ++i) {
+        const float x = IN_BF16 ? bf16_bits_to_f32(static_cast<const uint16_t*>(parts.p[i])[e])
+                                : static_cast<const float*>(parts.p[i])[e];
+        a = (i == 0) ? x : a + x;
+      }
+      if constexpr (OUT_BF16)
+        static_cast<uint16_t*>(Y)[e] = (uint16_t)f32_to_bf16_rne(a);
+      else
+        static_cast<float*>(Y)[e] = a;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_partial_sum(const void* const* parts, int nparts, bool parts_bf16, void* Y,
+                              bool y_bf16, int64_t numel, hipStream_t stream) {
+  if (numel == 0) return hipSuccess;
+  PartPtrs pp{};
+  for (int i = 0; i < nparts; ++i) pp.p[i] = parts[i];
+  const int64_t nvec = numel / 8;
+  int64_t blocks = (nvec + kThreads - 1) / kThreads;
+  const int64_t max_blocks = 256 * 8;  // 8 workgroups per CU, grid-stride beyond that
+  if (blocks > max_blocks) blocks = max_blocks;
+  if (blocks < 1) blocks = 1;
+  const dim3 grid((unsigned)blocks), block(kThreads);
+  if (parts_bf16 && y_bf16)
+    hipLaunchKernelGGL((partial_sum_kernel<true, true>), grid, block, 0, stream, pp, nparts, Y, nvec, numel);
+  else if (parts_bf16)
+    hipLaunchKernelGGL((partial_sum_kernel<true, false>), grid, block, 0, stream, pp, nparts, Y, nvec, numel);
+  else if (y_bf16)
+    hipLaunchKernelGGL((partial_sum_kernel<false, true>), grid, block, 0, stream, pp, nparts, Y, nvec, numel);
+  else
+    hipLaunchKernelGGL((partial_sum_kernel<false, false>), grid, block, 0, stream, pp, nparts, Y, nvec, numel);
+  return hipGetLastError();
+}
+
+}  // namespace tpmlp

@@ -1,0 +1,168 @@
+"""The C-ABI library loads, exports every symbol include/tpmlp.h declares, and
+rejects invalid arguments on the host before any HIP call (CPU only: every call
+here returns from validation; none reaches a kernel launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import megatron_tensor_transformer_shard_amd as tpm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tpmlp.h")
+
+OK, ENULL, EARG, ESHAPE, EDTYPE, EALIGN, EWS, EALIAS, EHIP = 0, -1, -2, -3, -4, -5, -6, -7, -8
+BF16, F32, E4M3 = 0, 1, 2
+
+# Fake, never-dereferenced "device" addresses; validation only inspects them.
+BASE = 1 << 40
+GB = 1 << 30
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(tp_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_and_binding_agree():
+    declared = _declared_functions()
+    assert len(declared) >= 13
+    assert sorted(tpm.EXPORTED_SYMBOLS) == declared
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(tpm.LIB_PATH)
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings():
+    assert tpm.abi_version() == 1
+    for code in (OK, ENULL, EARG, ESHAPE, EDTYPE, EALIGN, EWS, EALIAS, EHIP):
+        s = tpm.status_string(code)
+        assert s.startswith("TPM_")
+    assert "unknown" in tpm.status_string(12345)
+
+
+L = tpm.lib
+
+
+def col_gelu(X=BASE, A=BASE + GB, lda=256, Z=BASE + 2 * GB, M=32, d=64, F=256):
+    return L.tp_mlp_col_gelu(X, A, lda, Z, M, d, F, None)
+
+
+def test_col_gelu_validation():
+    assert col_gelu(M=0) == OK                       # empty: no-op, nothing launched
+    assert col_gelu(X=None) == ENULL
+    assert col_gelu(Z=None) == ENULL
+    assert col_gelu(M=-1) == ESHAPE
+    assert col_gelu(d=0) == ESHAPE
+    assert col_gelu(d=60) == ESHAPE                   # not a multiple of 8
+    assert col_gelu(F=12) == ESHAPE
+    assert col_gelu(lda=128) == ESHAPE                # lda < F
+    assert col_gelu(lda=260) == EALIGN                # row stride not 16-byte multiple
+    assert col_gelu(X=BASE + 2) == EALIGN
+    assert col_gelu(Z=BASE + 96) == EALIAS            # Z overlaps X
+    assert col_gelu(Z=BASE + GB + 512) == EALIAS      # Z overlaps A_i
+    assert col_gelu(M=1 << 31) == ESHAPE
+
+
+def row_partial(Z=BASE, B=BASE + GB, Y=BASE + 2 * GB, yd=F32, M=32, F=128, d=64):
+    return L.tp_mlp_row_partial(Z, B, Y, yd, M, F, d, None)
+
+
+def test_row_partial_validation():
+    assert row_partial(M=0) == OK
+    assert row_partial(yd=E4M3) == EDTYPE
+    assert row_partial(yd=7) == EDTYPE
+    assert row_partial(B=None) == ENULL
+    assert row_partial(d=12) == ESHAPE
+    assert row_partial(Y=BASE + 8) == EALIGN
+    assert row_partial(Y=BASE + 16) == EALIAS
+
+
+def shard(X=BASE, A=BASE + GB, B=BASE + 2 * GB, Y=BASE + 3 * GB, yd=F32, M=32, d=64, H=256,
+          N=2, rank=0, ws=BASE + 4 * GB, wsb=None):
+    if wsb is None:
+        wsb = L.tp_mlp_shard_workspace_size(M, d, H, N)
+    return L.tp_mlp_shard(X, A, B, Y, yd, M, d, H, N, rank, ws, wsb, None)
+
+
+def test_shard_validation():
+    assert L.tp_mlp_shard_workspace_size(32, 64, 256, 2) == 32 * 128 * 2
+    assert L.tp_mlp_shard_workspace_size(32, 64, 256, 3) == 0
+    assert shard(M=0) == OK
+    assert shard(N=0) == EARG
+    assert shard(rank=2) == EARG
+    assert shard(rank=-1) == EARG
+    assert shard(N=3) == ESHAPE                        # 4d not divisible by N
+    assert shard(N=64, H=256) == ESHAPE                # F = 4 not a multiple of 8
+    assert shard(yd=E4M3) == EDTYPE
+    assert shard(ws=None) == EWS
+    assert shard(wsb=100) == EWS
+    assert shard(ws=BASE + 4 * GB + 4) == EALIGN
+    assert shard(Y=BASE + 64) == EALIAS               # Y overlaps X
+    assert shard(ws=BASE + GB) == EALIAS               # workspace overlaps A
+    assert shard(Y=BASE + 4 * GB) == EALIAS            # Y overlaps workspace
+
+
+def psum(parts, N=None, pd=F32, Y=BASE + 10 * GB, yd=F32, numel=4096):
+    arr = (ctypes.c_void_p * max(1, len(parts)))(*parts)
+    return L.tp_partial_sum(arr, len(parts) if N is None else N, pd, Y, yd, numel, None)
+
+
+def test_partial_sum_validation():
+    parts = [BASE + i * GB for i in range(4)]
+    assert psum(parts, numel=0) == OK
+    assert psum(parts, N=0) == EARG
+    assert psum([BASE + i * GB for i in range(65)]) == EARG
+    assert psum(parts, pd=E4M3) == EDTYPE
+    assert psum(parts, yd=9) == EDTYPE
+    assert psum(parts, numel=-1) == ESHAPE
+    assert psum(parts[:1] + [None] + parts[2:]) == ENULL
+    assert psum(parts, Y=None) == ENULL
+    assert psum(parts, Y=BASE + 10 * GB + 8) == EALIGN
+    assert psum([parts[0] + 4] + parts[1:]) == EALIGN
+    assert psum(parts, Y=parts[1]) == EALIAS           # only parts[0] may be Y
+    assert psum(parts, Y=parts[0] + 16) == EALIAS
+    assert psum(parts, Y=parts[0], pd=BF16, yd=F32) == EALIAS  # in place needs equal dtypes
+
+
+def test_fp8_validation():
+    sc = BASE + 20 * GB
+    assert L.tp_quant_e4m3(BASE, 100, sc, BASE + GB, sc + 64, None) == ESHAPE   # not /16
+    assert L.tp_quant_e4m3(BASE, 4096, None, BASE + GB, sc, None) == ENULL
+    assert L.tp_quant_e4m3(BASE, 4096, sc, BASE + 16, sc + 64, None) == EALIAS
+    assert L.tp_quant_e4m3(BASE, 4096, sc, BASE + GB, sc, None) == EALIAS      # scale == amax
+    assert L.tp_amax_bf16(BASE, -1, sc, None) == ESHAPE
+    assert L.tp_amax_bf16(BASE, 64, None, None) == ENULL
+    assert L.tp_amax_bf16(BASE, 64, BASE + 16, None) == EALIAS
+    args = dict(Xq=BASE, sX=sc, Aq=BASE + GB, lda=256, sA=sc + 4, Z=BASE + 2 * GB, za=sc + 8,
+                M=32, d=64, F=256)
+
+    def cg(**kw):
+        a = dict(args, **kw)
+        return L.tp_mlp_col_gelu_e4m3(a["Xq"], a["sX"], a["Aq"], a["lda"], a["sA"], a["Z"],
+                                      a["za"], a["M"], a["d"], a["F"], None)
+    assert cg(d=40) == ESHAPE                         # e4m3 widths must be multiples of 16
+    assert cg(sX=None) == ENULL
+    assert cg(lda=264) == EALIGN
+    assert cg(Z=BASE + 32) == EALIAS
+    assert L.tp_mlp_row_partial_e4m3(BASE, sc, BASE + GB, sc, BASE + 2 * GB, 32, 24, 64, None) == ESHAPE
+    ws = L.tp_mlp_shard_e4m3_workspace_size(32, 64, 256, 2)
+    assert ws >= 32 * 128 * 3
+    assert L.tp_mlp_shard_e4m3(BASE, sc, BASE + GB, sc, BASE + 2 * GB, sc, BASE + 3 * GB,
+                               32, 64, 256, 2, 2, BASE + 4 * GB, ws, None) == EARG
+    assert L.tp_mlp_shard_e4m3(BASE, sc, BASE + GB, sc, BASE + 2 * GB, sc, BASE + 3 * GB,
+                               32, 64, 256, 2, 0, BASE + 4 * GB, ws - 1, None) == EWS
+    assert L.tp_mlp_shard_e4m3(BASE, sc, BASE + GB, sc, BASE + 2 * GB, sc, BASE + 3 * GB,
+                               32, 64, 256, 2, 0, BASE + 3 * GB, ws, None) == EALIAS
+
+
+def test_python_wrapper_rejects_cpu_tensors():
+    import torch
+    X = torch.zeros(4, 8, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        tpm.tp_mlp_col_gelu(X, torch.zeros(8, 8, dtype=torch.bfloat16))

@@ -1,0 +1,382 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Bar: max|Y − Y_ref| <= 1e-2·max|Y_ref| for bf16 and 6e-2·max|Y_ref| for e4m3;
+bit-exact for integer-valued GEMMs, partial sums and quantised codes; Z within
+one bf16 ulp (plus the fp32-accumulation slack) of the oracle's Z.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from helpers import (bf16_ulp, dev_bf16, dev_f32, dev_u8, host_bf16_bits, host_f64, log,
+                     max_err_ratio)
+from workloads import WORKLOADS, make_inputs, make_integer_valued, make_random, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+TOL_BF16 = 1e-2
+TOL_E4M3 = 6e-2
+
+
+@pytest.fixture(scope="module")
+def tpm():
+    import torch
+    import megatron_tensor_transformer_shard_amd as m
+    assert torch.cuda.is_available()
+    return m
+
+
+def _sync():
+    import torch
+    torch.cuda.synchronize()
+
+
+def _check_z(z_gpu_bits, z_ref_bits, what):
+    zg = oracle.bf16_decode(z_gpu_bits)
+    zr = oracle.bf16_decode(z_ref_bits)
+    slack = 1e-5 * max(float(np.max(np.abs(zr))), 1e-30)
+    bad = np.abs(zg - zr) > bf16_ulp(zr) + slack
+    assert not np.any(bad), f"{what}: {int(bad.sum())} Z elements beyond 1 ulp"
+    frac_exact = float(np.mean(zg == zr))
+    log(f"{what}: Z bit-identical fraction {frac_exact:.6f}")
+    return frac_exact
+
+
+# ------------------------------------------------------------ tiny config --
+
+def test_tiny_tp2_both_ranks(tpm):
+    import torch
+    wl = WORKLOADS["tiny_tp2"]
+    log("case tiny_tp2", wl.description)
+    X, A, B = make_inputs(wl)
+    Xd, Ad, Bd = dev_bf16(X), dev_bf16(A), dev_bf16(B)
+    parts = []
+    for rank in range(wl.N):
+        lo, hi = oracle.shard_columns(wl.H, wl.N, rank)
+        ws = torch.empty(tpm.tp_mlp_shard_workspace_size(wl.M, wl.d, wl.H, wl.N),
+                         dtype=torch.uint8, device="cuda")
+        Y = tpm.tp_mlp_shard(Xd, Ad, Bd, wl.N, rank, workspace=ws)
+        _sync()
+        Yref, Zref = oracle.mlp_shard(X, A, B, wl.N, rank, return_z=True)
+        Zgpu = host_bf16_bits(ws[: wl.M * wl.F * 2].view(torch.bfloat16).view(wl.M, wl.F))
+        _check_z(Zgpu, Zref, f"tiny rank {rank}")
+        r = max_err_ratio(host_f64(Y), Yref)
+        log(f"tiny rank {rank}: err ratio {r:.3e}")
+        assert r <= TOL_BF16
+        parts.append(Y)
+    Ysum = tpm.tp_partial_sum(parts)
+    _sync()
+    r = max_err_ratio(host_f64(Ysum), oracle.mlp_unsharded(X, A, B))
+    log(f"tiny sum vs unsharded: err ratio {r:.3e}")
+    assert r <= TOL_BF16
+
+
+# ------------------------------------------------- ragged, several tiles --
+
+RAGGED = [
+    # M, d, H, N, out dtype
+    (300, 136, 528, 2, "f32"),
+    (513, 264, 1056, 4, "f32"),
+    (700, 1032, 2064, 1, "bf16"),
+    (1, 64, 256, 1, "f32"),
+    (257, 8, 64, 8, "f32"),
+    (1030, 520, 4160, 8, "bf16"),
+]
+
+
+@pytest.mark.parametrize("M,d,H,N,odt", RAGGED)
+def test_ragged_shapes_all_ranks(tpm, M, d, H, N, odt):
+    import torch
+    log(f"case ragged M={M} d={d} H={H} N={N} out={odt}")
+    X, A, B = make_random(M, d, H, seed=M + d + H + N, sigma=0.05)
+    Xd, Ad, Bd = dev_bf16(X), dev_bf16(A), dev_bf16(B)
+    out_dtype = torch.float32 if odt == "f32" else torch.bfloat16
+    parts = []
+    for rank in range(N):
+        F = H // N
+        ws = torch.empty(tpm.tp_mlp_shard_workspace_size(M, d, H, N), dtype=torch.uint8,
+                         device="cuda")
+        Y = torch.full((M, d), float("nan"), dtype=out_dtype, device="cuda")
+        tpm.tp_mlp_shard(Xd, Ad, Bd, N, rank, Y_i=Y, workspace=ws)
+        _sync()
+        Yref, Zref = oracle.mlp_shard(X, A, B, N, rank, return_z=True)
+        _check_z(host_bf16_bits(ws[: M * F * 2].view(torch.bfloat16).view(M, F)), Zref,
+                 f"rank {rank}")
+        Yg = host_f64(Y)
+        assert not np.isnan(Yg).any(), "unwritten output elements"
+        r = max_err_ratio(Yg, Yref)
+        log(f"rank {rank}: err ratio {r:.3e}")
+        assert r <= TOL_BF16
+        parts.append(Y)
+    Ysum = tpm.tp_partial_sum(parts, out_dtype=torch.float32)
+    _sync()
+    r = max_err_ratio(host_f64(Ysum), oracle.mlp_unsharded(X, A, B))
+    log(f"sum vs unsharded: err ratio {r:.3e}")
+    assert r <= TOL_BF16
+
+
+def test_col_gelu_on_strided_column_view(tpm):
+    import torch
+    M, d, H, N = 200, 96, 768, 3
+    X, A, B = make_random(M, d, H, seed=5, sigma=0.1)
+    Xd, Ad = dev_bf16(X), dev_bf16(A)
+    for rank in range(N):
+        lo, hi = oracle.shard_columns(H, N, rank)
+        Z = tpm.tp_mlp_col_gelu(Xd, Ad[:, lo:hi])
+        _sync()
+        _check_z(host_bf16_bits(Z), oracle.col_gelu(X, A[:, lo:hi]), f"view rank {rank}")
+
+
+def test_row_partial_integer_inputs_bit_exact(tpm):
+    import torch
+    M, F, d = 333, 520, 264
+    Zi, Bi, _ = make_integer_valued(M, F, d, seed=3)     # Zi [M, F], Bi [F, d]
+    Zd, Bd = dev_bf16(Zi), dev_bf16(Bi)
+    Y = tpm.tp_mlp_row_partial(Zd, Bd)
+    _sync()
+    ref = oracle.bf16_decode(Zi) @ oracle.bf16_decode(Bi)
+    assert np.array_equal(host_f64(Y), ref)
+    Yb = tpm.tp_mlp_row_partial(Zd, Bd, out_dtype=torch.bfloat16)
+    _sync()
+    assert np.array_equal(host_bf16_bits(Yb), oracle.bf16_encode(ref))
+
+
+def test_identity_weights_give_elementwise_gelu(tpm):
+    import torch
+    from workloads import bf16_bits_from_f32
+    M, d = 130, 64
+    rng = np.random.default_rng(9)
+    X = bf16_bits_from_f32((rng.standard_normal((M, d)) * 3).astype(np.float32))
+    eye = np.zeros((d, 4 * d), np.float32)
+    eye[:, :d] = np.eye(d)
+    A = bf16_bits_from_f32(eye)
+    B = bf16_bits_from_f32(eye.T.copy())
+    ws = torch.empty(tpm.tp_mlp_shard_workspace_size(M, d, 4 * d, 1), dtype=torch.uint8,
+                     device="cuda")
+    Y = tpm.tp_mlp_shard(dev_bf16(X), dev_bf16(A), dev_bf16(B), 1, 0, workspace=ws)
+    _sync()
+    Z = host_bf16_bits(ws[: M * 4 * d * 2].view(torch.bfloat16).view(M, 4 * d))
+    assert np.all(oracle.bf16_decode(Z[:, d:]) == 0)
+    _check_z(Z[:, :d], oracle.bf16_encode(oracle.gelu(oracle.bf16_decode(X))), "identity")
+    # B = [I; 0] makes Y the first d columns of Z exactly
+    assert np.array_equal(host_f64(Y), oracle.bf16_decode(Z[:, :d]))
+
+
+def test_zero_rows_and_empty(tpm):
+    import torch
+    X = torch.zeros((0, 64), dtype=torch.bfloat16, device="cuda")
+    A = torch.zeros((64, 256), dtype=torch.bfloat16, device="cuda")
+    B = torch.zeros((256, 64), dtype=torch.bfloat16, device="cuda")
+    Y = tpm.tp_mlp_shard(X, A, B, 2, 1)
+    assert Y.shape == (0, 64)
+    Xz = torch.zeros((50, 64), dtype=torch.bfloat16, device="cuda")
+    _, A1, B1 = make_random(50, 64, 256, seed=2)
+    Y = tpm.tp_mlp_shard(Xz, dev_bf16(A1), dev_bf16(B1), 2, 0)
+    _sync()
+    assert torch.all(Y == 0).item()
+
+
+def test_deterministic_reruns(tpm):
+    import torch
+    M, d, H = 777, 512, 2048
+    X, A, B = make_random(M, d, H, seed=17)
+    Xd, Ad, Bd = dev_bf16(X), dev_bf16(A), dev_bf16(B)
+    outs = [tpm.tp_mlp_shard(Xd, Ad, Bd, 2, 1).cpu() for _ in range(3)]
+    assert all(torch.equal(outs[0], o) for o in outs[1:])
+
+
+# ----------------------------------------------------------- partial sum --
+
+@pytest.mark.parametrize("nparts,numel", [(1, 4096), (2, 1000003), (3, 77), (8, 1 << 20),
+                                          (9, 12345), (64, 40000)])
+def test_partial_sum_integer_exact(tpm, nparts, numel):
+    import torch
+    rng = np.random.default_rng(nparts * 7 + numel)
+    parts = rng.integers(-1000, 1000, size=(nparts, numel)).astype(np.float32)
+    dparts = [torch.from_numpy(p).cuda() for p in parts]
+    Y = tpm.tp_partial_sum(dparts)
+    _sync()
+    assert np.array_equal(Y.cpu().numpy(), parts.sum(axis=0, dtype=np.float64).astype(np.float32))
+    # bf16 partials (small integers are exact in bf16) -> fp32 and bf16 sums
+    from workloads import bf16_bits_from_f32
+    small = rng.integers(-100, 100, size=(nparts, numel)).astype(np.float32)
+    bparts = [dev_bf16(bf16_bits_from_f32(p)) for p in small]
+    Yf = tpm.tp_partial_sum(bparts, out_dtype=torch.float32)
+    Yb = tpm.tp_partial_sum(bparts, out_dtype=torch.bfloat16)
+    _sync()
+    exact = small.sum(axis=0, dtype=np.float64)
+    assert np.array_equal(host_f64(Yf), exact)
+    assert np.array_equal(host_bf16_bits(Yb), oracle.bf16_encode(exact))
+
+
+def test_partial_sum_rank_order_and_in_place(tpm):
+    import torch
+    # (1e8 + 1) − 1e8 in fp32 is 0; any other association gives 1
+    p = [torch.full((1000,), v, dtype=torch.float32, device="cuda") for v in (1e8, 1.0, -1e8)]
+    Y = tpm.tp_partial_sum(p)
+    _sync()
+    assert torch.all(Y == 0).item()
+    q = [torch.full((4099,), float(i + 1), device="cuda") for i in range(5)]
+    out = tpm.tp_partial_sum(q, Y=q[0])
+    _sync()
+    assert out.data_ptr() == q[0].data_ptr() and torch.all(q[0] == 15.0).item()
+
+
+# ------------------------------------------------------------ fp8 path ---
+
+def _quant_on_gpu(tpm, bits):
+    T = dev_bf16(bits)
+    amax = tpm.tp_amax_bf16(T)
+    Tq, s = tpm.tp_quant_e4m3(T, amax)
+    return amax, Tq, s
+
+
+@pytest.mark.parametrize("shape,sigma", [((300, 272), 1.0), ((64, 4096), 0.006), ((17, 16), 3.0)])
+def test_amax_and_quant_codes_bit_exact(tpm, shape, sigma):
+    X, _, _ = make_random(shape[0], shape[1], 16, seed=shape[0], x_sigma=sigma)
+    amax, Tq, s = _quant_on_gpu(tpm, X)
+    _sync()
+    a_ref = oracle.amax(X)
+    q_ref, s_ref = oracle.quantize_inputs_e4m3(X)
+    assert float(amax.item()) == a_ref
+    assert np.float32(s.item()) == s_ref
+    assert np.array_equal(Tq.cpu().numpy(), q_ref)
+
+
+def test_quant_zero_tensor_scale_one(tpm):
+    import torch
+    T = torch.zeros(64, dtype=torch.bfloat16, device="cuda")
+    amax = tpm.tp_amax_bf16(T)
+    Tq, s = tpm.tp_quant_e4m3(T, amax)
+    _sync()
+    assert amax.item() == 0.0 and s.item() == 1.0 and torch.all(Tq == 0).item()
+
+
+@pytest.mark.parametrize("M,d,H,N", [(300, 272, 800, 1), (257, 512, 2048, 4), (1, 64, 64, 1)])
+def test_fp8_shard_vs_oracle(tpm, M, d, H, N):
+    import torch
+    log(f"case fp8 M={M} d={d} H={H} N={N}")
+    X, A, B = make_random(M, d, H, seed=M + H, sigma=0.05)
+    _, Xq, sX = _quant_on_gpu(tpm, X)
+    _, Aq, sA = _quant_on_gpu(tpm, A)
+    _, Bq, sB = _quant_on_gpu(tpm, B)
+    Xq_ref, sX_ref = oracle.quantize_inputs_e4m3(X)
+    Aq_ref, sA_ref = oracle.quantize_inputs_e4m3(A)
+    Bq_ref, sB_ref = oracle.quantize_inputs_e4m3(B)
+    for rank in range(N):
+        F = H // N
+        ws = torch.empty(tpm.tp_mlp_shard_e4m3_workspace_size(M, d, H, N), dtype=torch.uint8,
+                         device="cuda")
+        Y = tpm.tp_mlp_shard_e4m3(Xq, sX, Aq, sA, Bq, sB, N, rank, workspace=ws)
+        _sync()
+        lo, hi = oracle.shard_columns(H, N, rank)
+        Yref, Zref, Zq_ref, sZ_ref = oracle.mlp_shard_e4m3(Xq_ref, sX_ref, Aq_ref, sA_ref,
+                                                           Bq_ref, sB_ref, N, rank,
+                                                           return_all=True)
+        Zg = host_bf16_bits(ws[: M * F * 2].view(torch.bfloat16).view(M, F))
+        _check_z(Zg, Zref, f"fp8 rank {rank}")
+        r = max_err_ratio(host_f64(Y), Yref)
+        log(f"fp8 rank {rank}: err ratio {r:.3e}")
+        assert r <= TOL_E4M3
+
+
+def test_fp8_steps_individually(tpm):
+    import torch
+    M, d, F = 130, 96, 208
+    X, A, B = make_random(M, d, F, seed=44, sigma=0.1)
+    Xq_ref, sX_ref = oracle.quantize_inputs_e4m3(X)
+    Aq_ref, sA_ref = oracle.quantize_inputs_e4m3(A)
+    Bq_ref, sB_ref = oracle.quantize_inputs_e4m3(B)
+    sX, sA, sB = dev_f32([sX_ref]), dev_f32([sA_ref]), dev_f32([sB_ref])
+    za = torch.empty(1, dtype=torch.float32, device="cuda")
+    Z = tpm.tp_mlp_col_gelu_e4m3(dev_u8(Xq_ref), sX, dev_u8(Aq_ref), sA, z_amax=za)
+    _sync()
+    Zref = oracle.col_gelu_e4m3(Xq_ref, sX_ref, Aq_ref, sA_ref)
+    Zg = host_bf16_bits(Z)
+    _check_z(Zg, Zref, "fp8 col_gelu")
+    assert za.item() == oracle.amax(Zg)
+    # requantise the GPU's own Z and check the codes bit for bit
+    Zq, sZ = tpm.tp_quant_e4m3(Z, za)
+    _sync()
+    Zq_ref, sZ_ref = oracle.requant_z(Zg)
+    assert np.float32(sZ.item()) == sZ_ref
+    assert np.array_equal(Zq.cpu().numpy(), Zq_ref)
+    Y = tpm.tp_mlp_row_partial_e4m3(Zq, sZ, dev_u8(Bq_ref), sB)
+    _sync()
+    r = max_err_ratio(host_f64(Y), oracle.row_partial_e4m3(Zq_ref, sZ_ref, Bq_ref, sB_ref))
+    log(f"fp8 row_partial: err ratio {r:.3e}")
+    assert r <= 1e-2   # same codes on both sides: only fp32 accumulation and bf16 output
+
+
+# ------------------------------------------------ full-size workloads ----
+
+def _full_size_bf16(tpm, name, nsample):
+    import torch
+    wl = WORKLOADS[name]
+    log(f"case {name}: {wl.description}")
+    X, A, B = make_inputs(wl)
+    Xd, Ad, Bd = dev_bf16(X), dev_bf16(A), dev_bf16(B)
+    rows = sample_rows(wl.M, nsample)
+    ws = torch.empty(tpm.tp_mlp_shard_workspace_size(wl.M, wl.d, wl.H, wl.N), dtype=torch.uint8,
+                     device="cuda")
+    parts = []
+    for rank in range(wl.N):
+        Y = torch.empty((wl.M, wl.d), dtype=torch.float32, device="cuda")
+        tpm.tp_mlp_shard(Xd, Ad, Bd, wl.N, rank, Y_i=Y, workspace=ws)
+        parts.append(Y)
+    Ysum = tpm.tp_partial_sum(parts) if wl.N > 1 else parts[0]
+    _sync()
+    Xs = X[rows]
+    worst = 0.0
+    for rank in range(wl.N):
+        r = max_err_ratio(host_f64(parts[rank][torch.from_numpy(rows).cuda()]),
+                          oracle.mlp_shard(Xs, A, B, wl.N, rank))
+        worst = max(worst, r)
+    log(f"{name}: sampled {len(rows)} rows, worst per-rank err ratio {worst:.3e}")
+    assert worst <= TOL_BF16
+    if wl.N > 1:
+        r = max_err_ratio(host_f64(Ysum[torch.from_numpy(rows).cuda()]),
+                          oracle.mlp_unsharded(Xs, A, B))
+        log(f"{name}: sum of {wl.N} ranks vs unsharded err ratio {r:.3e}")
+        assert r <= TOL_BF16
+
+
+def test_full_gpt2s_n1(tpm):
+    _full_size_bf16(tpm, "gpt2s_n1", 96)
+
+
+def test_full_7b_tp8_all_ranks_and_sum(tpm):
+    _full_size_bf16(tpm, "7b_tp8", 48)
+
+
+def test_full_175b_tp8(tpm):
+    _full_size_bf16(tpm, "175b_tp8", 48)
+
+
+def test_full_175b_tp8_e4m3(tpm):
+    import torch
+    wl = WORKLOADS["175b_tp8_e4m3"]
+    log(f"case {wl.name}: {wl.description}")
+    X, A, B = make_inputs(wl)
+    _, Xq, sX = _quant_on_gpu(tpm, X)
+    _, Aq, sA = _quant_on_gpu(tpm, A)
+    _, Bq, sB = _quant_on_gpu(tpm, B)
+    Y = tpm.tp_mlp_shard_e4m3(Xq, sX, Aq, sA, Bq, sB)
+    _sync()
+    Xq_ref, sX_ref = oracle.quantize_inputs_e4m3(X)
+    Aq_ref, sA_ref = oracle.quantize_inputs_e4m3(A)
+    Bq_ref, sB_ref = oracle.quantize_inputs_e4m3(B)
+    assert np.array_equal(Xq.cpu().numpy(), Xq_ref) and np.array_equal(Aq.cpu().numpy(), Aq_ref)
+    assert np.array_equal(Bq.cpu().numpy(), Bq_ref)
+    # Z's scale depends on all of Z, so the oracle computes Z in full, then Y on sampled rows
+    Zref = oracle.col_gelu_e4m3(Xq_ref, sX_ref, Aq_ref, sA_ref)
+    Zq_ref, sZ_ref = oracle.requant_z(Zref)
+    rows = sample_rows(wl.M, 64)
+    Yref = oracle.row_partial_e4m3(Zq_ref[rows], sZ_ref, Bq_ref, sB_ref)
+    r = max_err_ratio(host_f64(Y[torch.from_numpy(rows).cuda()]), Yref)
+    log(f"{wl.name}: sampled {len(rows)} rows, err ratio {r:.3e}")
+    assert r <= TOL_E4M3
+    # informational: quantisation error against the bf16 oracle
+    rb = max_err_ratio(host_f64(Y[torch.from_numpy(rows).cuda()]),
+                       oracle.mlp_shard(X[rows], A, B, 1, 0))
+    log(f"{wl.name}: vs bf16 oracle (quantisation error) {rb:.3e}")
