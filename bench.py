@@ -54,7 +54,10 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="7b_tp8")
+    p.add_argument("--workload", default="7b_tp8",
+                   help="7b_tp8 (default), gpt2s_n1, 175b_tp8, 175b_tp8_e4m3, or copy (a "
+                        "1-part tp_partial_sum over 256 MiB of fp32: the known-size copy that "
+                        "calibrates rocprofv3's FETCH_SIZE / WRITE_SIZE)")
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the timed oracle leg")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="stop adding oracle row chunks once this much CPU time is spent")
@@ -200,6 +203,26 @@ def sampled_check(wl, inputs, out, nrows=8):
     return float(np.max(np.abs(got - ref)) / np.max(np.abs(ref)))
 
 
+def copy_calibration(tpm, args):
+    """Y = parts[0] over 64 Mi fp32 elements: 256 MiB read, 256 MiB written per launch."""
+    import torch
+    n = 64 << 20
+    src = torch.arange(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        tpm.tp_partial_sum([src], Y=dst)
+    torch.cuda.synchronize()
+    timer = KernelTimer()
+    for _ in range(args.steps):
+        timer.around("copy", lambda: tpm.tp_partial_sum([src], Y=dst))
+    torch.cuda.synchronize()
+    st = timer.summary()["copy"]
+    nbytes = 2 * n * 4
+    print(json.dumps({"workload": "copy", "bytes_read": n * 4, "bytes_written": n * 4,
+                      "avg_us": st["avg_us"], "GBps": nbytes / (st["avg_us"] * 1e-6) / 1e9}),
+          flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -213,6 +236,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.workload == "copy":
+        copy_calibration(tpm, args)
+        return
     wl = WORKLOADS[args.workload]
     dtype = "e4m3" if wl.fp8 else "bf16"
     log(f"bench: workload {wl.name}: {wl.description}")

@@ -20,8 +20,9 @@
  *  - Pointers named as device pointers must be device memory of the current
  *    HIP device; host pointers are named as such. All data pointers must be
  *    16-byte aligned and every row stride in bytes a multiple of 16, so d and
- *    F must be multiples of 8 for bf16 and of 16 for e4m3. M is any value
- *    >= 1 (partial tiles are handled); M = 0 is a no-op that returns TPM_OK.
+ *    F must be multiples of 8 for bf16 and of 16 for e4m3. Row strides (d, F,
+ *    H, lda) are at most 2^23 elements. M is any value >= 1 (partial tiles
+ *    are handled); M = 0 is a no-op that returns TPM_OK.
  *  - The caller owns every buffer and keeps it alive until the work on
  *    `stream` has finished. The library allocates nothing, keeps no pointers
  *    and has no global mutable state. Outputs are overwritten, never

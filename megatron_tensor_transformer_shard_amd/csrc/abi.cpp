@@ -16,6 +16,9 @@ namespace {
 using tpmlp::OutKind;
 
 constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+// Row strides (and so d, F, lda) are limited so that the kernels' per-lane
+// byte offsets within a tile fit in 32 bits.
+constexpr int64_t kMaxLd = int64_t(1) << 23;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -39,7 +42,7 @@ hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 // Shared size checks for a GEMM step with inputs [M, K] and [K, N].
 int check_dims(int64_t M, int64_t K, int64_t N, int64_t mult) {
   if (M < 0 || K <= 0 || N <= 0) return TPM_ERR_SHAPE;
-  if (M > kMaxDim || K > kMaxDim || N > kMaxDim) return TPM_ERR_SHAPE;
+  if (M > kMaxDim || K > kMaxLd || N > kMaxLd) return TPM_ERR_SHAPE;
   if (K % mult != 0 || N % mult != 0) return TPM_ERR_SHAPE;
   if (M * K > (int64_t(1) << 46) || M * N > (int64_t(1) << 46) || K * N > (int64_t(1) << 46))
     return TPM_ERR_SHAPE;
@@ -73,7 +76,7 @@ int tp_mlp_col_gelu(const void* X, const void* A_i, int64_t lda, void* Z_i, int6
                     int64_t d, int64_t F, void* stream) {
   int st = check_dims(M, d, F, 8);
   if (st != TPM_OK) return st;
-  if (lda < F || lda > kMaxDim) return TPM_ERR_SHAPE;
+  if (lda < F || lda > kMaxLd) return TPM_ERR_SHAPE;
   if (M == 0) return TPM_OK;
   if (!X || !A_i || !Z_i) return TPM_ERR_NULL;
   if (!aligned16(X) || !aligned16(A_i) || !aligned16(Z_i) || lda % 8 != 0) return TPM_ERR_ALIGN;
@@ -119,7 +122,7 @@ int tp_mlp_shard(const void* X, const void* A, const void* B, void* Y_i, int y_d
   const int64_t F = H / N;
   int st = check_dims(M, d, F, 8);
   if (st != TPM_OK) return st;
-  if (H > kMaxDim || H * d > (int64_t(1) << 46)) return TPM_ERR_SHAPE;
+  if (H > kMaxLd || H * d > (int64_t(1) << 46)) return TPM_ERR_SHAPE;
   if (M == 0) return TPM_OK;
   if (!X || !A || !B || !Y_i) return TPM_ERR_NULL;
   if (!workspace || workspace_bytes < tp_mlp_shard_workspace_size(M, d, H, N))
@@ -206,7 +209,7 @@ int tp_mlp_col_gelu_e4m3(const void* Xq, const float* sX, const void* Aq_i, int6
                          int64_t F, void* stream) {
   int st = check_dims(M, d, F, 16);
   if (st != TPM_OK) return st;
-  if (lda < F || lda > kMaxDim) return TPM_ERR_SHAPE;
+  if (lda < F || lda > kMaxLd) return TPM_ERR_SHAPE;
   if (M == 0) {
     if (z_amax) return status_of(tpmlp::launch_fill_f32(z_amax, 0.0f, as_stream(stream)));
     return TPM_OK;
@@ -261,7 +264,7 @@ int tp_mlp_shard_e4m3(const void* Xq, const float* sX, const void* Aq, const flo
   const int64_t F = H / N;
   int st = check_dims(M, d, F, 16);
   if (st != TPM_OK) return st;
-  if (H > kMaxDim || H * d > (int64_t(1) << 46)) return TPM_ERR_SHAPE;
+  if (H > kMaxLd || H * d > (int64_t(1) << 46)) return TPM_ERR_SHAPE;
   if (M == 0) return TPM_OK;
   if (!Xq || !sX || !Aq || !sA || !Bq || !sB || !Y_i) return TPM_ERR_NULL;
   if (!workspace || workspace_bytes < tp_mlp_shard_e4m3_workspace_size(M, d, H, N))

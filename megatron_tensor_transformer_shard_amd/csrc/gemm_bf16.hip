@@ -7,21 +7,32 @@
 // C = P·Q with P [M, K] K-contiguous (X or Z_i) and Q [K, N] N-contiguous
 // (A_i or B_i in the pages' math layout), so one tile engine serves both.
 //
-// Tile engine (one workgroup = 4 waves = 256 threads, one tile BM x BN):
-//  - k advances in slices of BK = 64 (128 bytes of bf16 per LDS row).
-//  - P slices are copied HBM -> registers -> LDS with 128-bit loads/stores,
-//    stored K-contiguous. Q slices are loaded as 8x8 (k x n) blocks with
-//    128-bit loads, transposed in registers, and stored K-contiguous, so every
-//    MFMA operand is one 128-bit LDS read.
-//  - LDS rows are 128 bytes; the 16-byte chunk index is XOR-swizzled with the
-//    row so that the 8 (or 16) lanes served per LDS cycle hit distinct banks
-//    both when MFMA fragments are read and when tiles are written.
-//  - Two LDS stages: slice k+1 is fetched into registers before the MFMAs of
-//    slice k are issued, and written to the other stage after them; one
-//    barrier per slice.
-//  - v_mfma_f32_32x32x16_bf16 with the Q fragment as the A operand and the P
-//    fragment as the B operand, so each lane ends with 4 consecutive output
-//    columns per 32x32 tile (8- or 16-byte stores in the epilogue).
+// Tile engine (one workgroup = 4 waves = 256 threads, tile BM x BN, waves 2 x 2):
+//  - k advances in slices of BK = 64. Both operand slices go HBM -> LDS with
+//    global_load_lds_dwordx4 (no staging registers): each wave instruction
+//    fills 1 KB of LDS contiguously, and each lane picks the 16-byte granule
+//    of HBM that belongs at its LDS position, which is how the LDS swizzles
+//    below are realised.
+//  - The P slice is stored K-contiguous, 128-byte rows, 16-byte chunk c of row
+//    r at c ^ ((r & 7) ^ ((r >> 3) & 1)), so the 8 or 16 lanes served per LDS
+//    cycle by a ds_read_b128 of 32 consecutive rows hit distinct banks.
+//  - The Q slice stays N-contiguous as in HBM (rows of 2·BN bytes); granule g
+//    of row r is stored at (g + 4·(r & 3)) mod (BN/8), a rotation by 64 bytes
+//    per row, so the 4 rows read together by a transposing read land in
+//    distinct 64-byte bank groups.
+//  - MFMA v_mfma_f32_32x32x16_bf16. The Q fragment is the A operand and is read
+//    with ds_read_b64_tr_b16: in each 16-lane group, lane L addresses row
+//    L>>2, columns 4·(L&3)..+3 of a 4 x 16 block, and lane j receives column j
+//    of the 4 rows. Two such reads give the 8 k-values of one output column.
+//    The P fragment (B operand) is one ds_read_b128. Each lane ends with 4
+//    consecutive output columns per 32x32 tile (8- or 16-byte stores).
+//  - Two LDS stages, one barrier per slice: the next slice's data is awaited
+//    and the barrier taken before the last k-step's MFMAs, the DMA for the
+//    slice after next is issued right after the barrier, and the first
+//    fragments of the next slice are read while those MFMAs run.
+//  - Rows of P beyond M and columns of Q beyond N are loaded from clamped
+//    addresses (their outputs are discarded). In a last partial slice, the
+//    k >= K part of both LDS tiles is cleared after the DMA lands.
 //  - Workgroup ids are remapped so the tiles of one XCD share P and Q panels
 //    in that XCD's L2.
 #include "common.hpp"
@@ -31,28 +42,107 @@ namespace tpmlp {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int BK = 64;
 
-// Position of 16-byte chunk `chunk` in LDS row `row`: rows r and r+8 get
-// different XOR patterns so 16 consecutive rows also spread over 64 banks.
-__device__ __forceinline__ int swz(int row, int chunk) {
-  return chunk ^ ((row & 7) ^ ((row >> 3) & 1));
+// Keeps the interleaved order of one k-step slot (MFMA, its fragment read,
+// its DMA instruction) from being rearranged by the scheduler.
+#ifndef SCHED_PIN
+#define SCHED_PIN() __builtin_amdgcn_sched_barrier(0)
+#endif
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// Position of 16-byte chunk c in P row r (CH chunks per row). 8 chunks
+// (128-byte rows): c ^ ((r & 7) ^ ((r >> 3) & 1)). 4 chunks (64-byte rows):
+// c ^ (((r >> 1) ^ (r >> 3)) & 3). Either way a ds_read_b128 of 32
+// consecutive rows at one chunk spreads each 8 (or 16) consecutive lanes over
+// distinct 16-byte bank groups of a 32-bank (or 64-bank) LDS.
+template <int CH>
+__device__ __forceinline__ int swz_p(int r, int c) {
+  if constexpr (CH == 8) return c ^ ((r & 7) ^ ((r >> 3) & 1));
+  else return c ^ (((r >> 1) ^ (r >> 3)) & 3);
 }
 
-template <int BM, int BN, int OUT>
+template <int GR>  // granules per Q row
+__device__ __forceinline__ int rot_q(int row, int g) {
+  return (g + 4 * (row & 3)) % GR;
+}
+
+// LDS byte address of a __shared__ pointer.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) void*)p);
+}
+
+// 16 bytes from base + off (per lane) into LDS at lds + 16·lane, where `lds`
+// and `base` are wave-uniform. Issued through asm so that the only waits on
+// it are the explicit s_waitcnt below (the compiler cannot tell which LDS
+// stage a DMA writes and would otherwise wait for it before every ds_read).
+// M0 is used by nothing else in these kernels.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(lds), "v"(off), "s"(base)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// s_waitcnt vmcnt(VM) expcnt(7) lgkmcnt(LGKM), gfx9 encoding (vmcnt in bits 3:0 and 15:14).
+template <int VM, int LGKM>
+__device__ __forceinline__ void waitcnt() {
+  static_assert(VM >= 0 && VM < 64 && LGKM >= 0 && LGKM < 16, "waitcnt range");
+  __builtin_amdgcn_s_waitcnt((VM & 0xF) | ((VM >> 4) << 14) | (0x7 << 4) | (LGKM << 8));
+}
+
+// Wait until at most `slices` DMA slices of R instructions each are in flight
+// (and every LDS read has returned).
+template <int R, int MAXS>
+__device__ __forceinline__ void wait_dma(int slices) {
+  static_assert(MAXS <= 3, "extend wait_dma");
+  if (MAXS >= 3 && slices >= 3) waitcnt<(MAXS >= 3 ? 3 * R : 0), 0>();
+  else if (MAXS >= 2 && slices == 2) waitcnt<(MAXS >= 2 ? 2 * R : 0), 0>();
+  else if (MAXS >= 1 && slices == 1) waitcnt<R, 0>();
+  else waitcnt<0, 0>();
+}
+
+// Workgroup barrier that the compiler may not move memory operations across;
+// the hardware waits are issued explicitly by the caller.
+__device__ __forceinline__ void barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ bf16x8 read_tr_pair(const uint8_t* lds_a, const uint8_t* lds_b) {
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds_a));
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds_b));
+  const s16x4 v[2] = {lo, hi};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+template <int BM, int BN, int BK, int NS, int OUT>
 __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
     const uint16_t* __restrict__ P, int64_t ldp, const uint16_t* __restrict__ Q, int64_t ldq,
     void* __restrict__ C, int64_t ldc, int M, int N, int K, int group_m) {
   constexpr int TM = BM / 2, TN = BN / 2;      // wave tile (2 x 2 waves)
   constexpr int MT = TM / 32, NT = TN / 32;    // 32x32 MFMA tiles per wave
-  constexpr int P_CHUNKS = BM * (BK / 8);      // 16-byte chunks in a P slice
-  constexpr int P_PER_THREAD = (P_CHUNKS + kThreads - 1) / kThreads;
-  constexpr int Q_BLOCKS = (BK / 8) * (BN / 8);  // 8x8 blocks in a Q slice
-  constexpr int Q_PER_THREAD = (Q_BLOCKS + kThreads - 1) / kThreads;
-  constexpr int STAGE = (BM + BN) * BK;          // uint16 elements per LDS stage
-  static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32");
+  constexpr int CH = BK / 8;                   // 16-byte chunks per P row
+  constexpr int PROW = BK * 2;                 // bytes per P row
+  constexpr int PG = BM * CH;                  // granules in a P slice
+  constexpr int QGR = BN / 8;                  // granules per Q row
+  constexpr int QG = BK * QGR;                 // granules in a Q slice
+  constexpr int P_ROUNDS = PG / kThreads, Q_ROUNDS = QG / kThreads;
+  constexpr int ROUNDS = P_ROUNDS + Q_ROUNDS;  // DMA instructions per wave per slice
+  constexpr int P_BYTES = PG * 16, STAGE = (PG + QG) * 16;
+  constexpr int KS = BK / 16;                  // MFMA k-steps per slice
+  static_assert(CH == 4 || CH == 8, "BK must be 32 or 64");
+  static_assert(PG % kThreads == 0 && QG % kThreads == 0, "slices must split over 256 lanes");
+  static_assert(QGR % 4 == 0, "Q rows must hold a multiple of 4 granules");
+  static_assert(NS >= 2 && NS <= 5 && NS * STAGE <= 163840, "LDS stages");
 
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE];
 
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   int tm, tn;
@@ -60,71 +150,134 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
   const int m0 = tm * BM, n0 = tn * BN;
 
   const int t = threadIdx.x;
-  const int lane = t & 63, wave = t >> 6;
+  const int lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 
-  u32x4 preg[P_PER_THREAD];
-  u32x4 qreg[Q_PER_THREAD][8];
-
-  auto load_global = [&](int k0) {
+  // Per-lane byte offsets (from the tile's wave-uniform base) of the granules
+  // this lane copies; rows of P beyond M and columns of Q beyond N are clamped.
+  const uint16_t* p_base = P + (int64_t)m0 * ldp;
+  const uint16_t* q_base = Q + n0;
+  uint32_t p_off[P_ROUNDS], q_off[Q_ROUNDS];
+  int p_chunk[P_ROUNDS], q_row[Q_ROUNDS];
 #pragma unroll
-    for (int j = 0; j < P_PER_THREAD; ++j) {
-      const int i = t + j * kThreads;
-      const int r = i >> 3, c = i & 7;
-      const int gm = m0 + r, gk = k0 + c * 8;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if ((P_CHUNKS % kThreads == 0 || i < P_CHUNKS) && gm < M && gk < K)
-        v = *reinterpret_cast<const u32x4*>(P + (int64_t)gm * ldp + gk);
-      preg[j] = v;
+  for (int j = 0; j < P_ROUNDS; ++j) {
+    const int pos = (j * 4 + wave) * 64 + lane;
+    const int r = pos / CH, c = swz_p<CH>(r, pos % CH);
+    p_chunk[j] = c;
+    p_off[j] = (uint32_t)(((int64_t)(min(m0 + r, M - 1) - m0) * ldp + c * 8) * 2);
+  }
+#pragma unroll
+  for (int j = 0; j < Q_ROUNDS; ++j) {
+    const int pos = (j * 4 + wave) * 64 + lane;
+    const int r = pos / QGR, gp = pos % QGR;
+    const int g = (gp + QGR - 4 * (r & 3)) % QGR;
+    q_row[j] = r;
+    q_off[j] = (uint32_t)(((int64_t)r * ldq + min(n0 + g * 8, N - 8) - n0) * 2);
+  }
+
+  const int ktiles = (K + BK - 1) / BK;
+  const bool k_tail = (K % BK) != 0;
+  const uint32_t lds0 = lds_addr(smem) + wave * 1024;
+
+  // DMA of slice kt into stage kt % NS: the wave-uniform HBM bases and LDS
+  // address of the slice, and the j-th of its ROUNDS instructions.
+  struct SliceDma {
+    const uint16_t* pb;
+    const uint16_t* qb;
+    uint32_t lp;
+  };
+  auto slice_dma = [&](int kt) {
+    SliceDma d;
+    d.pb = p_base + kt * BK;
+    d.qb = q_base + (int64_t)(kt * BK) * ldq;
+    d.lp = lds0 + (kt % NS) * STAGE;
+    return d;
+  };
+  auto issue_one = [&](const SliceDma& d, int j) {
+    if (j < P_ROUNDS) dma16(d.pb, p_off[j], d.lp + j * 4096);
+    else dma16(d.qb, q_off[j - P_ROUNDS], d.lp + P_BYTES + (j - P_ROUNDS) * 4096);
+  };
+  // Whole slice at once; the last, partial slice clamps k into [k0, K) (the
+  // excess is cleared after it lands) and offsets only move down.
+  auto issue_slice = [&](int kt) {
+    const SliceDma d = slice_dma(kt);
+    if (!(k_tail && kt + 1 == ktiles)) {
+#pragma unroll
+      for (int j = 0; j < ROUNDS; ++j) issue_one(d, j);
+      return;
+    }
+    const int k0 = kt * BK;
+#pragma unroll
+    for (int j = 0; j < P_ROUNDS; ++j) {
+      const int cc = p_chunk[j] * 8, keep = min(cc, K - 8 - k0);
+      dma16(d.pb, p_off[j] - 2u * (uint32_t)(cc - keep), d.lp + j * 4096);
     }
 #pragma unroll
-    for (int j = 0; j < Q_PER_THREAD; ++j) {
-      const int i = t + j * kThreads;
-      const int kb = i & 7, nb = i >> 3;
-      const int gn = n0 + nb * 8;
-      const bool ok = (Q_BLOCKS % kThreads == 0 || i < Q_BLOCKS) && gn < N;
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const int gk = k0 + kb * 8 + r;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (ok && gk < K) v = *reinterpret_cast<const u32x4*>(Q + (int64_t)gk * ldq + gn);
-        qreg[j][r] = v;
-      }
+    for (int j = 0; j < Q_ROUNDS; ++j) {
+      const int r = q_row[j], keep = min(r, K - 1 - k0);
+      dma16(d.qb, q_off[j] - 2u * (uint32_t)(r - keep) * (uint32_t)ldq,
+            d.lp + P_BYTES + j * 4096);
     }
   };
 
-  auto store_lds = [&](int buf) {
-    uint16_t* sP = smem + buf * STAGE;
-    uint16_t* sQ = sP + BM * BK;
-#pragma unroll
-    for (int j = 0; j < P_PER_THREAD; ++j) {
-      const int i = t + j * kThreads;
-      if (P_CHUNKS % kThreads == 0 || i < P_CHUNKS) {
-        const int r = i >> 3, c = i & 7;
-        *reinterpret_cast<u32x4*>(sP + r * BK + swz(r, c) * 8) = preg[j];
-      }
+  // Clear the k >= K part of the last, partial slice (after its DMA landed).
+  auto clear_tail = [&](int kt) {
+    uint8_t* sp = smem + (kt % NS) * STAGE;
+    uint8_t* sq = sp + P_BYTES;
+    const int kvalid = K - kt * BK;  // multiple of 8, in (0, BK)
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    for (int i = t; i < PG; i += kThreads) {
+      const int r = i / CH, c = i % CH;
+      if (c * 8 >= kvalid) *reinterpret_cast<u32x4*>(sp + r * PROW + swz_p<CH>(r, c) * 16) = z;
     }
+    for (int i = t; i < QG; i += kThreads) {
+      if (i / QGR >= kvalid) *reinterpret_cast<u32x4*>(sq + i * 16) = z;
+    }
+  };
+
+  // Fragment addressing (byte offsets within a stage).
+  // P (B operand): row m, 16-byte chunk 2s + (lane >> 5).
+  int p_frag[MT];
 #pragma unroll
-    for (int j = 0; j < Q_PER_THREAD; ++j) {
-      const int i = t + j * kThreads;
-      if (Q_BLOCKS % kThreads == 0 || i < Q_BLOCKS) {
-        const int kb = i & 7, nb = i >> 3;
-        // qreg[j][r] holds row k = kb*8 + r, columns nb*8 .. nb*8+7; dword p
-        // holds columns 2p (low half) and 2p+1 (high half). Column jn of the
-        // block becomes one K-contiguous 16-byte chunk.
+  for (int mi = 0; mi < MT; ++mi) p_frag[mi] = wm * TM + mi * 32 + (lane & 31);
+  // Q (A operand): rows k = 16s + 8(lane>>5) + 4h + ((lane&15)>>2),
+  // columns n = wn*TN + ni*32 + 16((lane>>4)&1) + 4(lane&3); the row & 3 of
+  // every row a lane reads is (lane&15)>>2, so its rotated granule is fixed.
+  const int q_rsub = 8 * (lane >> 5) + ((lane & 15) >> 2);
+  const int q_byte = 8 * (lane & 1);
+  int q_pos[NT];
 #pragma unroll
-        for (int jn = 0; jn < 8; ++jn) {
-          const int p = jn >> 1;
-          u32x4 o;
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const uint32_t x = qreg[j][2 * q][p], y = qreg[j][2 * q + 1][p];
-            o[q] = (jn & 1) ? ((x >> 16) | (y & 0xFFFF0000u)) : ((x & 0xFFFFu) | (y << 16));
-          }
-          const int n = nb * 8 + jn;
-          *reinterpret_cast<u32x4*>(sQ + n * BK + swz(n, kb) * 8) = o;
-        }
-      }
+  for (int ni = 0; ni < NT; ++ni)
+    q_pos[ni] = rot_q<QGR>(q_rsub,
+                           (wn * TN + ni * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3)) >> 3) *
+                    16 + q_byte;
+
+  // Fragment registers, double-buffered across k-steps. A fragments are two
+  // 8-byte halves (one transposing read each).
+  s16x8 afr[2][NT];
+  bf16x8 bfr[2][MT];
+  constexpr int NREADS = MT + 2 * NT;
+  // idx-th fragment read of k-step s of slice kt into buffer buf; ordered so
+  // that the next k-step's first MFMAs (A fragment 0 with every B fragment)
+  // find their operands first.
+  auto read_one = [&](int kt, int s, int buf, int idx) {
+    const uint8_t* sp = smem + (kt % NS) * STAGE;
+    const uint8_t* sq = sp + P_BYTES;
+    const int r0 = 16 * s + q_rsub;
+    if (idx < 2) {
+      const uint8_t* a = sq + (r0 + 4 * idx) * (2 * BN) + q_pos[0];
+      const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)a);
+      if (idx == 0) afr[buf][0].lo = v; else afr[buf][0].hi = v;
+    } else if (idx < 2 + MT) {
+      const int mi = idx - 2, r = p_frag[mi];
+      bfr[buf][mi] = *reinterpret_cast<const bf16x8*>(
+          sp + r * PROW + swz_p<CH>(r, 2 * s + (lane >> 5)) * 16);
+    } else {
+      const int ni = 1 + (idx - 2 - MT) / 2, h = (idx - 2 - MT) % 2;
+      const uint8_t* a = sq + (r0 + 4 * h) * (2 * BN) + q_pos[ni];
+      const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)a);
+      if (h == 0) afr[buf][ni].lo = v; else afr[buf][ni].hi = v;
     }
   };
 
@@ -136,40 +289,84 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[ni][mi][v] = 0.0f;
 
-  const int ktiles = (K + BK - 1) / BK;
-  load_global(0);
-  store_lds(0);
-  __syncthreads();
-
-  for (int kt = 0; kt < ktiles; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < ktiles) load_global((kt + 1) * BK);
-
-    const uint16_t* sP = smem + buf * STAGE;
-    const uint16_t* sQ = sP + BM * BK;
+  // One k-step: the NT x MT MFMAs on buffer `cur`; after MFMA i the i-th
+  // fragment read for the next k-step (into cur ^ 1) and, when `dma`, the
+  // i-th DMA instruction of slice dkt are issued, so that neither LDS nor
+  // global-load issue ever stalls the MFMA pipe for long.
+  // (With fewer MFMAs than reads or DMA instructions, slot i takes every
+  // j with j·NMFMA/count == i.)
+  constexpr int NMFMA = NT * MT;
+  auto kstep = [&](int cur, bool reads, int rkt, int rs, bool dma, const SliceDma& dd) {
 #pragma unroll
-    for (int s = 0; s < BK / 16; ++s) {
-      const int chunk = 2 * s + (lane >> 5);
-      bf16x8 a[NT], b[MT];
+    for (int i = 0; i < NMFMA; ++i) {
+      const int ni = i / MT, mi = i % MT;
+      acc[ni][mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          __builtin_bit_cast(bf16x8, afr[cur][ni]), bfr[cur][mi], acc[ni][mi], 0, 0, 0);
+      if (reads) {
 #pragma unroll
-      for (int ni = 0; ni < NT; ++ni) {
-        const int n = wn * TN + ni * 32 + (lane & 31);
-        a[ni] = *reinterpret_cast<const bf16x8*>(sQ + n * BK + swz(n, chunk) * 8);
+        for (int j = 0; j < NREADS; ++j)
+          if ((NREADS <= NMFMA ? j : j * NMFMA / NREADS) == i) read_one(rkt, rs, cur ^ 1, j);
       }
+      if (dma) {
 #pragma unroll
-      for (int mi = 0; mi < MT; ++mi) {
-        const int m = wm * TM + mi * 32 + (lane & 31);
-        b[mi] = *reinterpret_cast<const bf16x8*>(sP + m * BK + swz(m, chunk) * 8);
+        for (int j = 0; j < ROUNDS; ++j)
+          if ((ROUNDS <= NMFMA ? j : j * NMFMA / ROUNDS) == i) issue_one(dd, j);
       }
-#pragma unroll
-      for (int ni = 0; ni < NT; ++ni)
-#pragma unroll
-        for (int mi = 0; mi < MT; ++mi)
-          acc[ni][mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ni], b[mi], acc[ni][mi], 0, 0, 0);
+      SCHED_PIN();
     }
+  };
 
-    if (kt + 1 < ktiles) store_lds(buf ^ 1);
-    __syncthreads();
+  // Prologue: the first NS slices in flight; wait for slice 0.
+  const int pre = min(NS, ktiles);
+  for (int kt = 0; kt < pre; ++kt) issue_slice(kt);
+  wait_dma<ROUNDS, NS - 1 < 3 ? NS - 1 : 3>(pre - 1);
+  barrier();
+  if (k_tail && ktiles == 1) {
+    clear_tail(0);
+    waitcnt<0, 0>();
+    barrier();
+  }
+#pragma unroll
+  for (int i = 0; i < NREADS; ++i) read_one(0, 0, 0, i);
+
+  // Slice kt is read from stage kt % NS. Before its last k-step: wait until
+  // slice kt+1 has landed (slices kt+2 .. kt+NS-1 may still be in flight),
+  // barrier (every wave has finished reading stage kt % NS), then, during
+  // the last k-step, issue slice kt+NS into that stage and read the first
+  // fragments of slice kt+1.
+  auto sync_next = [&](int kt) {
+    wait_dma<ROUNDS, NS - 2 < 3 ? NS - 2 : 3>(min(kt + NS, ktiles) - (kt + 2));
+    barrier();
+    if (k_tail && kt + 2 == ktiles) {
+      clear_tail(kt + 1);
+      waitcnt<0, 0>();
+      barrier();
+    }
+  };
+  const SliceDma none{};
+
+  // Steady state: every slice issues a full slice kt+NS, interleaved with its
+  // last k-step's MFMAs. (One MFMA sequence per call site keeps the
+  // accumulators in place.)
+  const int steady_end = ktiles - NS - (k_tail ? 1 : 0);
+  int kt = 0;
+  for (; kt < steady_end; ++kt) {
+#pragma unroll
+    for (int s = 0; s + 1 < KS; ++s) kstep(s & 1, true, kt, s + 1, false, none);
+    sync_next(kt);
+    kstep((KS - 1) & 1, true, kt + 1, 0, true, slice_dma(kt + NS));
+  }
+  // Drain: the remaining slices; a DMA still due (possibly the partial last
+  // slice) is issued whole.
+  for (; kt < ktiles; ++kt) {
+#pragma unroll
+    for (int s = 0; s + 1 < KS; ++s) kstep(s & 1, true, kt, s + 1, false, none);
+    const bool more = kt + 1 < ktiles;
+    if (more) {
+      sync_next(kt);
+      if (kt + NS < ktiles) issue_slice(kt + NS);
+    }
+    kstep((KS - 1) & 1, more, kt + 1, 0, false, none);
   }
 
   // Epilogue. Lane holds, for 32x32 tile (ni, mi) and group g = 0..3,
@@ -202,6 +399,8 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
   }
 }
 
+constexpr int kBK = 64, kStages = 2;
+
 template <int BM, int BN>
 hipError_t launch_cfg(const uint16_t* P, int64_t ldp, const uint16_t* Q, int64_t ldq, void* C,
                       int64_t ldc, int M, int N, int K, OutKind out, hipStream_t stream) {
@@ -209,15 +408,15 @@ hipError_t launch_cfg(const uint16_t* P, int64_t ldp, const uint16_t* Q, int64_t
   const int group_m = 4;
   switch (out) {
     case OutKind::GeluBf16:
-      hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, (int)OutKind::GeluBf16>), dim3(tiles),
+      hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, kBK, kStages, (int)OutKind::GeluBf16>), dim3(tiles),
                          dim3(kThreads), 0, stream, P, ldp, Q, ldq, C, ldc, M, N, K, group_m);
       break;
     case OutKind::F32:
-      hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, (int)OutKind::F32>), dim3(tiles),
+      hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, kBK, kStages, (int)OutKind::F32>), dim3(tiles),
                          dim3(kThreads), 0, stream, P, ldp, Q, ldq, C, ldc, M, N, K, group_m);
       break;
     case OutKind::Bf16:
-      hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, (int)OutKind::Bf16>), dim3(tiles),
+      hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, kBK, kStages, (int)OutKind::Bf16>), dim3(tiles),
                          dim3(kThreads), 0, stream, P, ldp, Q, ldq, C, ldc, M, N, K, group_m);
       break;
   }

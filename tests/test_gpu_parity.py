@@ -31,15 +31,36 @@ def _sync():
     torch.cuda.synchronize()
 
 
-def _check_z(z_gpu_bits, z_ref_bits, what):
+# The GPU evaluates GeLU with the Abramowitz & Stegun 7.1.26 approximation of
+# erf (|error| <= 1.5e-7); with fp32 evaluation |ΔGeLU(s)| <= 3e-7·|s|.
+GELU_APPROX_REL = 3e-7
+
+
+def _check_z(z_gpu_bits, z_ref_bits, what, absdot=None, K=None):
+    """Z within one bf16 ulp of the oracle's Z, plus the worst-case fp32
+    accumulation error of the GPU's S = Σ_k x_k·a_k (recursive summation:
+    |ΔS| <= K·2^-24·Σ_k|x_k·a_k|) carried through GeLU (|GeLU'| <= 1.13), plus
+    the GeLU approximation's bound (|s| <= Σ_k|x_k·a_k|).
+    At least 95% of the elements must be bit-identical."""
     zg = oracle.bf16_decode(z_gpu_bits)
     zr = oracle.bf16_decode(z_ref_bits)
-    slack = 1e-5 * max(float(np.max(np.abs(zr))), 1e-30)
-    bad = np.abs(zg - zr) > bf16_ulp(zr) + slack
-    assert not np.any(bad), f"{what}: {int(bad.sum())} Z elements beyond 1 ulp"
+    tol = bf16_ulp(zr)
+    if absdot is not None:
+        tol = tol + (1.13 * K * 2.0 ** -24 + GELU_APPROX_REL) * absdot
+    bad = np.abs(zg - zr) > tol
     frac_exact = float(np.mean(zg == zr))
     log(f"{what}: Z bit-identical fraction {frac_exact:.6f}")
+    assert not np.any(bad), f"{what}: {int(bad.sum())} Z elements beyond the bound"
+    assert frac_exact >= 0.95, f"{what}: only {frac_exact:.4f} of Z bit-identical"
     return frac_exact
+
+
+def _absdot_bf16(X, A_i):
+    return np.abs(oracle.bf16_decode(X)) @ np.abs(oracle.bf16_decode(A_i))
+
+
+def _absdot_e4m3(Xq, sX, Aq_i, sA):
+    return (np.abs(oracle.e4m3_decode(Xq)) @ np.abs(oracle.e4m3_decode(Aq_i))) / (float(sX) * float(sA))
 
 
 # ------------------------------------------------------------ tiny config --
@@ -59,7 +80,7 @@ def test_tiny_tp2_both_ranks(tpm):
         _sync()
         Yref, Zref = oracle.mlp_shard(X, A, B, wl.N, rank, return_z=True)
         Zgpu = host_bf16_bits(ws[: wl.M * wl.F * 2].view(torch.bfloat16).view(wl.M, wl.F))
-        _check_z(Zgpu, Zref, f"tiny rank {rank}")
+        _check_z(Zgpu, Zref, f"tiny rank {rank}", _absdot_bf16(X, A[:, lo:hi]), wl.d)
         r = max_err_ratio(host_f64(Y), Yref)
         log(f"tiny rank {rank}: err ratio {r:.3e}")
         assert r <= TOL_BF16
@@ -100,8 +121,9 @@ def test_ragged_shapes_all_ranks(tpm, M, d, H, N, odt):
         tpm.tp_mlp_shard(Xd, Ad, Bd, N, rank, Y_i=Y, workspace=ws)
         _sync()
         Yref, Zref = oracle.mlp_shard(X, A, B, N, rank, return_z=True)
+        lo, hi = oracle.shard_columns(H, N, rank)
         _check_z(host_bf16_bits(ws[: M * F * 2].view(torch.bfloat16).view(M, F)), Zref,
-                 f"rank {rank}")
+                 f"rank {rank}", _absdot_bf16(X, A[:, lo:hi]), d)
         Yg = host_f64(Y)
         assert not np.isnan(Yg).any(), "unwritten output elements"
         r = max_err_ratio(Yg, Yref)
@@ -124,7 +146,8 @@ def test_col_gelu_on_strided_column_view(tpm):
         lo, hi = oracle.shard_columns(H, N, rank)
         Z = tpm.tp_mlp_col_gelu(Xd, Ad[:, lo:hi])
         _sync()
-        _check_z(host_bf16_bits(Z), oracle.col_gelu(X, A[:, lo:hi]), f"view rank {rank}")
+        _check_z(host_bf16_bits(Z), oracle.col_gelu(X, A[:, lo:hi]), f"view rank {rank}",
+                 _absdot_bf16(X, A[:, lo:hi]), d)
 
 
 def test_row_partial_integer_inputs_bit_exact(tpm):
@@ -157,7 +180,8 @@ def test_identity_weights_give_elementwise_gelu(tpm):
     _sync()
     Z = host_bf16_bits(ws[: M * 4 * d * 2].view(torch.bfloat16).view(M, 4 * d))
     assert np.all(oracle.bf16_decode(Z[:, d:]) == 0)
-    _check_z(Z[:, :d], oracle.bf16_encode(oracle.gelu(oracle.bf16_decode(X))), "identity")
+    _check_z(Z[:, :d], oracle.bf16_encode(oracle.gelu(oracle.bf16_decode(X))), "identity",
+             np.abs(oracle.bf16_decode(X)), 1)
     # B = [I; 0] makes Y the first d columns of Z exactly
     assert np.array_equal(host_f64(Y), oracle.bf16_decode(Z[:, :d]))
 
@@ -274,7 +298,7 @@ def test_fp8_shard_vs_oracle(tpm, M, d, H, N):
                                                            Bq_ref, sB_ref, N, rank,
                                                            return_all=True)
         Zg = host_bf16_bits(ws[: M * F * 2].view(torch.bfloat16).view(M, F))
-        _check_z(Zg, Zref, f"fp8 rank {rank}")
+        _check_z(Zg, Zref, f"fp8 rank {rank}", _absdot_e4m3(Xq_ref, sX_ref, Aq_ref[:, lo:hi], sA_ref), d)
         r = max_err_ratio(host_f64(Y), Yref)
         log(f"fp8 rank {rank}: err ratio {r:.3e}")
         assert r <= TOL_E4M3
@@ -293,7 +317,7 @@ def test_fp8_steps_individually(tpm):
     _sync()
     Zref = oracle.col_gelu_e4m3(Xq_ref, sX_ref, Aq_ref, sA_ref)
     Zg = host_bf16_bits(Z)
-    _check_z(Zg, Zref, "fp8 col_gelu")
+    _check_z(Zg, Zref, "fp8 col_gelu", _absdot_e4m3(Xq_ref, sX_ref, Aq_ref, sA_ref), d)
     assert za.item() == oracle.amax(Zg)
     # requantise the GPU's own Z and check the codes bit for bit
     Zq, sZ = tpm.tp_quant_e4m3(Z, za)
