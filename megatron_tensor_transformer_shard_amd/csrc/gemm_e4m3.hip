@@ -16,6 +16,7 @@
 //                bf16 + amax(|Z|) epilogue or a plain bf16 store.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "tile_engine.hpp"
 
 namespace tpmlp {
 namespace {
@@ -97,18 +98,37 @@ __global__ __launch_bounds__(kThreads) void quant_e4m3_kernel(const uint16_t* __
 }
 
 // ---------------------------------------------------------------------------
-// e4m3 GEMM tile engine. LDS rows are 128 bytes (BK = 128 e4m3 values), with
-// the same 16-byte chunk swizzle as the bf16 engine.
+// e4m3 GEMM on the same tile engine as the bf16 GEMMs (see gemm_bf16.hip): a
+// k-slice is 128 e4m3 values (BK bytes = 128, the same 128-byte P rows), two
+// LDS stages filled by global_load_lds_dwordx4, one barrier per slice, and one
+// fragment read and one DMA instruction interleaved after each MFMA.
+//  - MFMA v_mfma_scale_f32_32x32x64_f8f6f4 (both operands e4m3, unit block
+//    scales): each lane holds 32 k-values of one row (A) or column (B); lane
+//    half h = lane >> 5 holds k = 64s + 32h .. +31 of k-step s.
+//  - P fragment (B operand): two ds_read_b128 (16-byte chunks 4s+2h, 4s+2h+1).
+//  - Q fragment (A operand) from the N-contiguous e4m3 Q tile: four
+//    ds_read_b64_tr_b8. In each 16-lane group, lane L addresses row L>>1,
+//    bytes 8·(L&1)..+7 of an 8-row x 16-byte block, and lane j receives byte
+//    column j of the 8 rows: 8 k-values of one output column per read.
+//  - Q rows are BN bytes; granule g of row r is rotated so that the 8 rows x 2
+//    granules one read instruction touches per lane half fall in distinct
+//    16-byte bank groups (rotations found by exhaustive search over
+//    f(r) = a·(r&1) + b·((r>>1)&1) + c·((r>>2)&1)).
 // ---------------------------------------------------------------------------
-constexpr int BK = 128;
+namespace e4 {
 
-__device__ __forceinline__ int swz(int row, int chunk) {
-  return chunk ^ ((row & 7) ^ ((row >> 3) & 1));
-}
+using namespace engine;
 
-// byte lanes: perm(hi, lo, sel) picks result byte i from {lo[0..3], hi[0..3]} by sel byte i.
-__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
-  return __builtin_amdgcn_perm(hi, lo, sel);
+constexpr int BK = 128, NS = 2, KS = BK / 64;
+
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+
+template <int GR>
+__device__ __forceinline__ int rot_q8(int r, int g) {
+  if constexpr (GR == 16) return (g + 2 * (r & 7)) & 15;
+  else if constexpr (GR == 12) return (g + 2 * ((r >> 2) & 1)) % 12;
+  else return (g + 2 * ((r >> 1) & 1) + 4 * ((r >> 2) & 1)) % GR;
 }
 
 template <int BM, int BN, int OUT>
@@ -119,96 +139,139 @@ __global__ __launch_bounds__(kThreads) void gemm_e4m3_kernel(
     int group_m) {
   constexpr int TM = BM / 2, TN = BN / 2;
   constexpr int MT = TM / 32, NT = TN / 32;
-  constexpr int P_CHUNKS = BM * (BK / 16);          // 16-byte chunks in a P slice
-  constexpr int P_PER_THREAD = (P_CHUNKS + kThreads - 1) / kThreads;
-  constexpr int Q_BLOCKS = (BK / 8) * (BN / 16);    // 8(k) x 16(n) byte blocks
-  constexpr int Q_PER_THREAD = (Q_BLOCKS + kThreads - 1) / kThreads;
-  constexpr int STAGE = (BM + BN) * BK;             // bytes per LDS stage
+  constexpr int CH = 8, PROW = BK;            // 16-byte chunks / bytes per P row
+  constexpr int PG = BM * CH;
+  constexpr int QGR = BN / 16;                // granules per Q row
+  constexpr int QG = BK * QGR;
+  constexpr int P_ROUNDS = PG / kThreads, Q_ROUNDS = QG / kThreads;
+  constexpr int ROUNDS = P_ROUNDS + Q_ROUNDS;
+  constexpr int P_BYTES = PG * 16, STAGE = (PG + QG) * 16;
+  static_assert(PG % kThreads == 0 && QG % kThreads == 0, "slices must split over 256 lanes");
+  static_assert(NS * STAGE <= 163840, "LDS stages");
 
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE];
 
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   int tm, tn;
   grouped_tile(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n, group_m, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
-
   const int t = threadIdx.x;
-  const int lane = t & 63, wave = t >> 6;
+  const int lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 
-  u32x4 preg[P_PER_THREAD];
-  u32x4 qreg[Q_PER_THREAD][8];
-
-  auto load_global = [&](int k0) {
+  const uint8_t* p_base = P + (int64_t)m0 * ldp;
+  const uint8_t* q_base = Q + n0;
+  uint32_t p_off[P_ROUNDS], q_off[Q_ROUNDS];
+  int p_chunk[P_ROUNDS], q_row[Q_ROUNDS];
 #pragma unroll
-    for (int j = 0; j < P_PER_THREAD; ++j) {
-      const int i = t + j * kThreads;
-      const int r = i >> 3, c = i & 7;
-      const int gm = m0 + r, gk = k0 + c * 16;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if ((P_CHUNKS % kThreads == 0 || i < P_CHUNKS) && gm < M && gk < K)
-        v = *reinterpret_cast<const u32x4*>(P + (int64_t)gm * ldp + gk);
-      preg[j] = v;
+  for (int j = 0; j < P_ROUNDS; ++j) {
+    const int pos = (j * 4 + wave) * 64 + lane;
+    const int r = pos / CH, c = swz_p<CH>(r, pos % CH);
+    p_chunk[j] = c;
+    p_off[j] = (uint32_t)((int64_t)(min(m0 + r, M - 1) - m0) * ldp + c * 16);
+  }
+#pragma unroll
+  for (int j = 0; j < Q_ROUNDS; ++j) {
+    const int pos = (j * 4 + wave) * 64 + lane;
+    const int r = pos / QGR, gp = pos % QGR;
+    int g = 0;  // the granule stored at position gp of row r
+#pragma unroll
+    for (int c = 0; c < QGR; ++c)
+      if (rot_q8<QGR>(r, c) == gp) g = c;
+    q_row[j] = r;
+    q_off[j] = (uint32_t)((int64_t)r * ldq + min(n0 + g * 16, N - 16) - n0);
+  }
+
+  const int ktiles = (K + BK - 1) / BK;
+  const bool k_tail = (K % BK) != 0;
+  const uint32_t lds0 = lds_addr(smem) + wave * 1024;
+
+  struct SliceDma {
+    const uint8_t* pb;
+    const uint8_t* qb;
+    uint32_t lp;
+  };
+  auto slice_dma = [&](int kt) {
+    SliceDma d;
+    d.pb = p_base + kt * BK;
+    d.qb = q_base + (int64_t)(kt * BK) * ldq;
+    d.lp = lds0 + (kt % NS) * STAGE;
+    return d;
+  };
+  auto issue_one = [&](const SliceDma& d, int j) {
+    if (j < P_ROUNDS) dma16(d.pb, p_off[j], d.lp + j * 4096);
+    else dma16(d.qb, q_off[j - P_ROUNDS], d.lp + P_BYTES + (j - P_ROUNDS) * 4096);
+  };
+  auto issue_slice = [&](int kt) {
+    const SliceDma d = slice_dma(kt);
+    if (!(k_tail && kt + 1 == ktiles)) {
+#pragma unroll
+      for (int j = 0; j < ROUNDS; ++j) issue_one(d, j);
+      return;
+    }
+    const int k0 = kt * BK;
+#pragma unroll
+    for (int j = 0; j < P_ROUNDS; ++j) {
+      const int cc = p_chunk[j] * 16, keep = min(cc, K - 16 - k0);
+      dma16(d.pb, p_off[j] - (uint32_t)(cc - keep), d.lp + j * 4096);
     }
 #pragma unroll
-    for (int j = 0; j < Q_PER_THREAD; ++j) {
-      const int i = t + j * kThreads;
-      const int kb = i & 15, nb = i >> 4;   // 16 k-blocks of 8 rows; n-chunks of 16 bytes
-      const int gn = n0 + nb * 16;
-      const bool ok = (Q_BLOCKS % kThreads == 0 || i < Q_BLOCKS) && gn < N;
-#pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        const int gk = k0 + kb * 8 + r;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (ok && gk < K) v = *reinterpret_cast<const u32x4*>(Q + (int64_t)gk * ldq + gn);
-        qreg[j][r] = v;
-      }
+    for (int j = 0; j < Q_ROUNDS; ++j) {
+      const int r = q_row[j], keep = min(r, K - 1 - k0);
+      dma16(d.qb, q_off[j] - (uint32_t)(r - keep) * (uint32_t)ldq, d.lp + P_BYTES + j * 4096);
     }
   };
-
-  auto store_lds = [&](int buf) {
-    uint8_t* sPl = smem + buf * STAGE;
-    uint8_t* sQl = sPl + BM * BK;
-#pragma unroll
-    for (int j = 0; j < P_PER_THREAD; ++j) {
-      const int i = t + j * kThreads;
-      if (P_CHUNKS % kThreads == 0 || i < P_CHUNKS) {
-        const int r = i >> 3, c = i & 7;
-        *reinterpret_cast<u32x4*>(sPl + r * BK + swz(r, c) * 16) = preg[j];
-      }
+  auto clear_tail = [&](int kt) {
+    uint8_t* sp = smem + (kt % NS) * STAGE;
+    uint8_t* sq = sp + P_BYTES;
+    const int kvalid = K - kt * BK;  // multiple of 16, in (0, BK)
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    for (int i = t; i < PG; i += kThreads) {
+      const int r = i / CH, c = i % CH;
+      if (c * 16 >= kvalid) *reinterpret_cast<u32x4*>(sp + r * PROW + swz_p<CH>(r, c) * 16) = z;
     }
+    for (int i = t; i < QG; i += kThreads)
+      if (i / QGR >= kvalid) *reinterpret_cast<u32x4*>(sq + i * 16) = z;
+  };
+
+  // Fragment addressing.
+  int p_frag[MT];
 #pragma unroll
-    for (int j = 0; j < Q_PER_THREAD; ++j) {
-      const int i = t + j * kThreads;
-      if (Q_BLOCKS % kThreads == 0 || i < Q_BLOCKS) {
-        const int kb = i & 15, nb = i >> 4;
-        // qreg[j][r] = row k = kb*8 + r, bytes n = nb*16 .. +15 (dword c holds n = 4c..4c+3).
-        // Output for column n: 8 bytes, k = kb*8 .. +7 (two dwords).
+  for (int mi = 0; mi < MT; ++mi) p_frag[mi] = wm * TM + mi * 32 + (lane & 31);
+  const int q_rsub = 32 * (lane >> 5) + ((lane & 15) >> 1);   // + 64s + 8q
+  const int q_byte = 8 * (lane & 1);
+  int q_gran[NT];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          uint32_t out[2][4];   // [k half][n within the dword]
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const uint32_t a = qreg[j][4 * h + 0][c], b = qreg[j][4 * h + 1][c];
-            const uint32_t cc = qreg[j][4 * h + 2][c], d = qreg[j][4 * h + 3][c];
-            const uint32_t t0 = perm(b, a, 0x05010400u);   // a0 b0 a1 b1
-            const uint32_t t1 = perm(b, a, 0x07030602u);   // a2 b2 a3 b3
-            const uint32_t t2 = perm(d, cc, 0x05010400u);  // c0 d0 c1 d1
-            const uint32_t t3 = perm(d, cc, 0x07030602u);  // c2 d2 c3 d3
-            out[h][0] = perm(t2, t0, 0x05040100u);         // a0 b0 c0 d0
-            out[h][1] = perm(t2, t0, 0x07060302u);         // a1 b1 c1 d1
-            out[h][2] = perm(t3, t1, 0x05040100u);         // a2 b2 c2 d2
-            out[h][3] = perm(t3, t1, 0x07060302u);         // a3 b3 c3 d3
-          }
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int n = nb * 16 + 4 * c + e;
-            const int c16 = kb >> 1, half = kb & 1;
-            u32x2 o = {out[0][e], out[1][e]};
-            *reinterpret_cast<u32x2*>(sQl + n * BK + swz(n, c16) * 16 + half * 8) = o;
-          }
-        }
-      }
+  for (int ni = 0; ni < NT; ++ni) q_gran[ni] = (wn * TN + ni * 32 + 16 * ((lane >> 4) & 1)) >> 4;
+
+  i32x8 afr[2][NT], bfr[2][MT];
+  constexpr int NREADS = 2 * MT + 4 * NT;
+  // idx-th fragment read of k-step s of slice kt: first the 4 reads of A
+  // fragment 0, then the B fragments, then the other A fragments.
+  auto read_one = [&](int kt, int s, int buf, int idx) {
+    const uint8_t* sp = smem + (kt % NS) * STAGE;
+    const uint8_t* sq = sp + P_BYTES;
+    auto read_a = [&](int ni, int q) {
+      const int r = 64 * s + q_rsub + 8 * q;
+      const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+          (lds_i32x2*)(sq + r * BN + rot_q8<QGR>(r, q_gran[ni]) * 16 + q_byte));
+      if (q == 0) afr[buf][ni].s01 = v;
+      else if (q == 1) afr[buf][ni].s23 = v;
+      else if (q == 2) afr[buf][ni].s45 = v;
+      else afr[buf][ni].s67 = v;
+    };
+    if (idx < 4) {
+      read_a(0, idx);
+    } else if (idx < 4 + 2 * MT) {
+      const int mi = (idx - 4) / 2, half = (idx - 4) % 2, r = p_frag[mi];
+      const int chunk = 4 * s + 2 * (lane >> 5) + half;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(sp + r * PROW + swz_p<CH>(r, chunk) * 16);
+      const i32x4 vi = __builtin_bit_cast(i32x4, v);
+      if (half == 0) bfr[buf][mi].lo = vi; else bfr[buf][mi].hi = vi;
+    } else {
+      const int j = idx - 4 - 2 * MT;
+      read_a(1 + j / 4, j % 4);
     }
   };
 
@@ -220,48 +283,69 @@ __global__ __launch_bounds__(kThreads) void gemm_e4m3_kernel(
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[ni][mi][v] = 0.0f;
 
-  const int ktiles = (K + BK - 1) / BK;
-  load_global(0);
-  store_lds(0);
-  __syncthreads();
-
-  for (int kt = 0; kt < ktiles; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < ktiles) load_global((kt + 1) * BK);
-    const uint8_t* sPl = smem + buf * STAGE;
-    const uint8_t* sQl = sPl + BM * BK;
+  constexpr int NMFMA = NT * MT;
+  auto kstep = [&](int cur, bool reads, int rkt, int rs, bool dma, const SliceDma& dd) {
 #pragma unroll
-    for (int s = 0; s < BK / 64; ++s) {
-      // lane half h holds k = s*64 + h*32 .. +31: 16-byte chunks 4s+2h, 4s+2h+1
-      const int c0 = 4 * s + 2 * (lane >> 5);
-      i32x8 a[NT], b[MT];
+    for (int i = 0; i < NMFMA; ++i) {
+      const int ni = i / MT, mi = i % MT;
+      acc[ni][mi] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+          afr[cur][ni], bfr[cur][mi], acc[ni][mi], 0, 0, 0, 127, 0, 127);
+      if (reads) {
 #pragma unroll
-      for (int ni = 0; ni < NT; ++ni) {
-        const int n = wn * TN + ni * 32 + (lane & 31);
-        const u32x4 lo = *reinterpret_cast<const u32x4*>(sQl + n * BK + swz(n, c0) * 16);
-        const u32x4 hi = *reinterpret_cast<const u32x4*>(sQl + n * BK + swz(n, c0 + 1) * 16);
-        a[ni] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                      (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        for (int j = 0; j < NREADS; ++j)
+          if ((NREADS <= NMFMA ? j : j * NMFMA / NREADS) == i) read_one(rkt, rs, cur ^ 1, j);
       }
+      if (dma) {
 #pragma unroll
-      for (int mi = 0; mi < MT; ++mi) {
-        const int m = wm * TM + mi * 32 + (lane & 31);
-        const u32x4 lo = *reinterpret_cast<const u32x4*>(sPl + m * BK + swz(m, c0) * 16);
-        const u32x4 hi = *reinterpret_cast<const u32x4*>(sPl + m * BK + swz(m, c0 + 1) * 16);
-        b[mi] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
-                      (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        for (int j = 0; j < ROUNDS; ++j)
+          if ((ROUNDS <= NMFMA ? j : j * NMFMA / ROUNDS) == i) issue_one(dd, j);
       }
-#pragma unroll
-      for (int ni = 0; ni < NT; ++ni)
-#pragma unroll
-        for (int mi = 0; mi < MT; ++mi)
-          acc[ni][mi] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              a[ni], b[mi], acc[ni][mi], 0, 0, 0, 127, 0, 127);
+      SCHED_PIN();
     }
-    if (kt + 1 < ktiles) store_lds(buf ^ 1);
-    __syncthreads();
+  };
+
+  const int pre = min(NS, ktiles);
+  for (int kt = 0; kt < pre; ++kt) issue_slice(kt);
+  wait_dma<ROUNDS, NS - 1>(pre - 1);
+  barrier();
+  if (k_tail && ktiles == 1) {
+    clear_tail(0);
+    waitcnt<0, 0>();
+    barrier();
+  }
+#pragma unroll
+  for (int i = 0; i < NREADS; ++i) read_one(0, 0, 0, i);
+
+  auto sync_next = [&](int kt) {
+    wait_dma<ROUNDS, NS - 2>(min(kt + NS, ktiles) - (kt + 2));
+    barrier();
+    if (k_tail && kt + 2 == ktiles) {
+      clear_tail(kt + 1);
+      waitcnt<0, 0>();
+      barrier();
+    }
+  };
+  const SliceDma none{};
+  const int steady_end = ktiles - NS - (k_tail ? 1 : 0);
+  int kt = 0;
+  for (; kt < steady_end; ++kt) {
+#pragma unroll
+    for (int s = 0; s + 1 < KS; ++s) kstep(s & 1, true, kt, s + 1, false, none);
+    sync_next(kt);
+    kstep((KS - 1) & 1, true, kt + 1, 0, true, slice_dma(kt + NS));
+  }
+  for (; kt < ktiles; ++kt) {
+#pragma unroll
+    for (int s = 0; s + 1 < KS; ++s) kstep(s & 1, true, kt, s + 1, false, none);
+    const bool more = kt + 1 < ktiles;
+    if (more) {
+      sync_next(kt);
+      if (kt + NS < ktiles) issue_slice(kt + NS);
+    }
+    kstep((KS - 1) & 1, more, kt + 1, 0, false, none);
   }
 
+  // Epilogue: dequantise by 1/(sP·sQ); GeLU + bf16 + max|Z|, or bf16.
   const float dq = 1.0f / (sP[0] * sQ[0]);
   float zmax = 0.0f;
 #pragma unroll
@@ -274,13 +358,11 @@ __global__ __launch_bounds__(kThreads) void gemm_e4m3_kernel(
       for (int g = 0; g < 4; ++g) {
         const int n = n0 + wn * TN + ni * 32 + 8 * g + 4 * (lane >> 5);
         if (n >= N) continue;
-        float v[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = acc[ni][mi][4 * g + e] * dq;
         uint32_t bits[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float z = (OUT == (int)OutKind::GeluBf16) ? gelu_exact(v[e]) : v[e];
+          const float v = acc[ni][mi][4 * g + e] * dq;
+          const float z = (OUT == (int)OutKind::GeluBf16) ? gelu_exact(v) : v;
           bits[e] = f32_to_bf16_rne(z);
           if (OUT == (int)OutKind::GeluBf16) zmax = fmaxf(zmax, fabsf(bf16_bits_to_f32(bits[e])));
         }
@@ -295,6 +377,8 @@ __global__ __launch_bounds__(kThreads) void gemm_e4m3_kernel(
   }
 }
 
+}  // namespace e4
+
 template <int BM, int BN>
 hipError_t launch_cfg(const uint8_t* P, int64_t ldp, const float* sP, const uint8_t* Q,
                       int64_t ldq, const float* sQ, uint16_t* C, int64_t ldc, float* z_amax,
@@ -302,11 +386,11 @@ hipError_t launch_cfg(const uint8_t* P, int64_t ldp, const float* sP, const uint
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   const int group_m = 4;
   if (out == OutKind::GeluBf16)
-    hipLaunchKernelGGL((gemm_e4m3_kernel<BM, BN, (int)OutKind::GeluBf16>), dim3(tiles),
+    hipLaunchKernelGGL((e4::gemm_e4m3_kernel<BM, BN, (int)OutKind::GeluBf16>), dim3(tiles),
                        dim3(kThreads), 0, stream, P, ldp, sP, Q, ldq, sQ, C, ldc, z_amax, M, N,
                        K, group_m);
   else
-    hipLaunchKernelGGL((gemm_e4m3_kernel<BM, BN, (int)OutKind::Bf16>), dim3(tiles),
+    hipLaunchKernelGGL((e4::gemm_e4m3_kernel<BM, BN, (int)OutKind::Bf16>), dim3(tiles),
                        dim3(kThreads), 0, stream, P, ldp, sP, Q, ldq, sQ, C, ldc, z_amax, M, N,
                        K, group_m);
   return hipGetLastError();
@@ -348,15 +432,20 @@ hipError_t launch_gemm_e4m3(const uint8_t* P, int64_t ldp, const float* sP, cons
     if (e != hipSuccess) return e;
   }
   if (M == 0 || N == 0) return hipSuccess;
-  // 256x256 e4m3 tiles exceed the register budget (the byte transpose needs
-  // more live registers than the bf16 one), so the widest tile is 256x192.
-  const long tiles192 = (long)((M + 255) / 256) * ((N + 191) / 192);
-  const long tiles128 = (long)((M + 127) / 128) * ((N + 127) / 128);
-  const double w192 = (double)((tiles192 + 255) / 256);
-  const double w128 = (double)((tiles128 + 255) / 256) * 0.40;
-  if (w128 < w192 - 1e-9)
-    return launch_cfg<128, 128>(P, ldp, sP, Q, ldq, sQ, C, ldc, z_amax, M, N, K, out, stream);
-  return launch_cfg<256, 192>(P, ldp, sP, Q, ldq, sQ, C, ldc, z_amax, M, N, K, out, stream);
+  // Tile shape with the best estimated time: waves of 256 CUs times a
+  // per-tile cost that grows for smaller tiles. (A 256x256 e4m3 tile would
+  // need more than the 512 registers a lane has.)
+  static const struct { int bm, bn; double cost; } cands[] = {{256, 192, 1.00}, {128, 128, 0.38}};
+  double best = 1e300;
+  int pick = 0;
+  for (int i = 0; i < 2; ++i) {
+    const long tiles = (long)((M + cands[i].bm - 1) / cands[i].bm) * ((N + cands[i].bn - 1) / cands[i].bn);
+    const double est = (double)((tiles + 255) / 256) * cands[i].cost;
+    if (est < best - 1e-9) { best = est; pick = i; }
+  }
+  if (pick == 0)
+    return launch_cfg<256, 192>(P, ldp, sP, Q, ldq, sQ, C, ldc, z_amax, M, N, K, out, stream);
+  return launch_cfg<128, 128>(P, ldp, sP, Q, ldq, sQ, C, ldc, z_amax, M, N, K, out, stream);
 }
 
 }  // namespace tpmlp

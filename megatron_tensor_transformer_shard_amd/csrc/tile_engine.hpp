@@ -1,0 +1,83 @@
+// Device helpers of the gfx950 GEMM tile engine shared by the bf16 and e4m3
+// kernels: LDS swizzles, direct-to-LDS loads, explicit waits and barriers.
+#pragma once
+
+#include "common.hpp"
+
+namespace tpmlp {
+namespace engine {
+
+// Keeps the interleaved order of one k-step slot (MFMA, its fragment read,
+// its DMA instruction) from being rearranged by the scheduler.
+#ifndef SCHED_PIN
+#define SCHED_PIN() __builtin_amdgcn_sched_barrier(0)
+#endif
+
+// Position of 16-byte chunk c in P row r (CH chunks per row). 8 chunks
+// (128-byte rows): c ^ ((r & 7) ^ ((r >> 3) & 1)). 4 chunks (64-byte rows):
+// c ^ (((r >> 1) ^ (r >> 3)) & 3). Either way a ds_read_b128 of 32
+// consecutive rows at one chunk spreads each 8 (or 16) consecutive lanes over
+// distinct 16-byte bank groups of a 32-bank (or 64-bank) LDS.
+template <int CH>
+__device__ __forceinline__ int swz_p(int r, int c) {
+  if constexpr (CH == 8) return c ^ ((r & 7) ^ ((r >> 3) & 1));
+  else return c ^ (((r >> 1) ^ (r >> 3)) & 3);
+}
+
+// Position of granule g in row `row` of an N-contiguous bf16 Q tile with GR
+// granules per row: a rotation by 64 bytes per row, so that the 4 rows a
+// ds_read_b64_tr_b16 lane group reads at one column land in distinct 64-byte
+// bank groups.
+template <int GR>
+__device__ __forceinline__ int rot_q(int row, int g) {
+  return (g + 4 * (row & 3)) % GR;
+}
+
+// LDS byte address of a __shared__ pointer.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) void*)p);
+}
+
+// 16 bytes from base + off (per lane) into LDS at lds + 16·lane, where `lds`
+// and `base` are wave-uniform. Issued through asm so that the only waits on
+// it are the explicit s_waitcnt below (the compiler cannot tell which LDS
+// stage a DMA writes and would otherwise wait for it before every ds_read).
+// M0 is used by nothing else in these kernels.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(lds), "v"(off), "s"(base)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// s_waitcnt vmcnt(VM) expcnt(7) lgkmcnt(LGKM), gfx9 encoding (vmcnt in bits 3:0 and 15:14).
+template <int VM, int LGKM>
+__device__ __forceinline__ void waitcnt() {
+  static_assert(VM >= 0 && VM < 64 && LGKM >= 0 && LGKM < 16, "waitcnt range");
+  __builtin_amdgcn_s_waitcnt((VM & 0xF) | ((VM >> 4) << 14) | (0x7 << 4) | (LGKM << 8));
+}
+
+// Wait until at most `slices` DMA slices of R instructions each are in flight
+// (and every LDS read has returned).
+template <int R, int MAXS>
+__device__ __forceinline__ void wait_dma(int slices) {
+  static_assert(MAXS <= 3, "extend wait_dma");
+  if (MAXS >= 3 && slices >= 3) waitcnt<(MAXS >= 3 ? 3 * R : 0), 0>();
+  else if (MAXS >= 2 && slices == 2) waitcnt<(MAXS >= 2 ? 2 * R : 0), 0>();
+  else if (MAXS >= 1 && slices == 1) waitcnt<R, 0>();
+  else waitcnt<0, 0>();
+}
+
+// Workgroup barrier that the compiler may not move memory operations across;
+// the hardware waits are issued explicitly by the caller.
+__device__ __forceinline__ void barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+}  // namespace engine
+}  // namespace tpmlp
