@@ -2,10 +2,13 @@
 //
 // This is the arithmetic of the AllReduce(sum) that ends the MLP block
 // ("Megatron-LM deep architecture", eq. for Output: Output = Σ_i Y_i). It is
-// HBM-bound: N reads and one write per element. Each thread owns 8
-// consecutive elements per step (one 16-byte load per bf16 part, two per fp32
-// part), issues the loads of up to 8 parts before adding, and adds strictly in
-// rank order in fp32, so the result does not depend on the launch shape.
+// HBM-bound: N reads and one write per element, each touched once, so loads
+// and stores are non-temporal (they bypass the caches' normal retention; a
+// sweep on MI355X gave ~5.8-6.1 TB/s this way against ~5.0 with temporal
+// stores). Each thread owns one 16-byte chunk of a partial per step (4 fp32
+// or 8 bf16 elements), issues the loads of up to 8 partials before adding,
+// and adds strictly in rank order in fp32, so the result does not depend on
+// the launch shape.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -19,8 +22,12 @@ struct PartPtrs {
   const void* p[kMaxParts];
 };
 
+// Elements per 16-byte chunk of a partial.
 template <bool IN_BF16>
-__device__ __forceinline__ void load8(const void* base, int64_t v, float (&x)[8]) {
+constexpr int kVec = IN_BF16 ? 8 : 4;
+
+template <bool IN_BF16>
+__device__ __forceinline__ void load_chunk(const void* base, int64_t v, float (&x)[kVec<IN_BF16>]) {
   if constexpr (IN_BF16) {
     const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base) + v);
 #pragma unroll
@@ -29,13 +36,9 @@ __device__ __forceinline__ void load8(const void* base, int64_t v, float (&x)[8]
       x[2 * j + 1] = bf16_bits_to_f32(w[j] >> 16);
     }
   } else {
-    const f32x4* p = reinterpret_cast<const f32x4*>(base) + 2 * v;
-    const f32x4 a = __builtin_nontemporal_load(p), b = __builtin_nontemporal_load(p + 1);
+    const f32x4 w = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(base) + v);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      x[j] = a[j];
-      x[4 + j] = b[j];
-    }
+    for (int j = 0; j < 4; ++j) x[j] = w[j];
   }
 }
 
@@ -43,39 +46,45 @@ template <bool IN_BF16, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads) void partial_sum_kernel(PartPtrs parts, int nparts,
                                                                void* __restrict__ Y, int64_t nvec,
                                                                int64_t numel) {
+  constexpr int V = kVec<IN_BF16>;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
   for (int64_t v = (int64_t)blockIdx.x * kThreads + threadIdx.x; v < nvec; v += stride) {
-    float acc[8];
-    load8<IN_BF16>(parts.p[0], v, acc);
+    float acc[V];
+    load_chunk<IN_BF16>(parts.p[0], v, acc);
     int i = 1;
     for (; i + 8 <= nparts; i += 8) {
-      float x[8][8];
+      float x[8][V];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) load8<IN_BF16>(parts.p[i + j], v, x[j]);
+      for (int j = 0; j < 8; ++j) load_chunk<IN_BF16>(parts.p[i + j], v, x[j]);
 #pragma unroll
       for (int j = 0; j < 8; ++j)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] += x[j][e];
+        for (int e = 0; e < V; ++e) acc[e] += x[j][e];
     }
     for (; i < nparts; ++i) {
-      float x[8];
-      load8<IN_BF16>(parts.p[i], v, x);
+      float x[V];
+      load_chunk<IN_BF16>(parts.p[i], v, x);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] += x[e];
+      for (int e = 0; e < V; ++e) acc[e] += x[e];
     }
     if constexpr (OUT_BF16) {
-      u32x4 o = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
-                 pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
-      reinterpret_cast<u32x4*>(Y)[v] = o;
+      if constexpr (V == 8) {
+        const u32x4 o = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                         pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
+        __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(Y) + v);
+      } else {
+        const u32x2 o = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+        __builtin_nontemporal_store(o, reinterpret_cast<u32x2*>(Y) + v);
+      }
     } else {
-      f32x4* q = reinterpret_cast<f32x4*>(Y) + 2 * v;
-      q[0] = f32x4{acc[0], acc[1], acc[2], acc[3]};
-      q[1] = f32x4{acc[4], acc[5], acc[6], acc[7]};
+      f32x4* q = reinterpret_cast<f32x4*>(Y) + (V / 4) * v;
+      __builtin_nontemporal_store(f32x4{acc[0], acc[1], acc[2], acc[3]}, q);
+      if constexpr (V == 8) __builtin_nontemporal_store(f32x4{acc[4], acc[5], acc[6], acc[7]}, q + 1);
     }
   }
-  // Scalar tail (numel not a multiple of 8), handled by the first block.
+  // Scalar tail (numel not a multiple of the chunk), handled by the first block.
   if (blockIdx.x == 0) {
-    for (int64_t e = nvec * 8 + threadIdx.x; e < numel; e += kThreads) {
+    for (int64_t e = nvec * V + threadIdx.x; e < numel; e += kThreads) {
       float a = 0.0f;
       for (int i = 0; i < nparts; ++i) {
         const float x = IN_BF16 ? bf16_bits_to_f32(static_cast<const uint16_t*>(parts.p[i])[e])
@@ -97,9 +106,9 @@ hipError_t launch_partial_sum(const void* const* parts, int nparts, bool parts_b
   if (numel == 0) return hipSuccess;
   PartPtrs pp{};
   for (int i = 0; i < nparts; ++i) pp.p[i] = parts[i];
-  const int64_t nvec = numel / 8;
+  const int64_t nvec = numel / (parts_bf16 ? 8 : 4);
   int64_t blocks = (nvec + kThreads - 1) / kThreads;
-  const int64_t max_blocks = 256 * 8;  // 8 workgroups per CU, grid-stride beyond that
+  const int64_t max_blocks = 256 * 64;  // 64 workgroups per CU, grid-stride beyond that
   if (blocks > max_blocks) blocks = max_blocks;
   if (blocks < 1) blocks = 1;
   const dim3 grid((unsigned)blocks), block(kThreads);
