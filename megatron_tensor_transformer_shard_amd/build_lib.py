@@ -22,11 +22,15 @@ SOURCES = ["gemm_bf16.hip", "gemm_e4m3.hip", "partial_sum.hip", "abi.cpp"]
 ARCH = "gfx950"
 
 # Packed-fp32 VALU instructions are disabled for the device code; hipcc's host
-# pass warns that it does not know the feature, which is harmless.
+# pass warns that it does not know the feature, which is harmless. The GEMM
+# k-steps are fully unrolled loops of up to 64 MFMAs with their interleaved
+# loads; clang's default size limit for `#pragma unroll` would leave them
+# rolled, and the accumulator arrays would then live in scratch memory.
 CFLAGS = [
     "-O3", "-std=c++17", f"--offload-arch={ARCH}", "-mcode-object-version=5", "-fPIC",
     "-Wall", "-Wno-unused-function",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-pragma-unroll-threshold=1000000",
 ]
 
 

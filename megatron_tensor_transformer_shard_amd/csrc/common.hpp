@@ -16,49 +16,48 @@ typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 typedef __attribute__((ext_vector_type(8))) int i32x8;
 typedef __attribute__((ext_vector_type(4))) int i32x4;
 
-// float -> bfloat16 bits, round to nearest even (finite inputs).
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+
+// Two floats -> two bfloat16 (low half = lo), round to nearest even; a single
+// v_cvt_pk_bf16_f32 on gfx950.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+// float -> bfloat16 bits, round to nearest even.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  return pack_bf16x2(f, 0.0f) & 0xFFFFu;
 }
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
   return __builtin_bit_cast(float, b << 16);
 }
 
-// GeLU(x) = x·Φ(x), the exact (Gaussian CDF) form, Φ(x) = ½·erfc(−x/√2).
+// GeLU(x) = x·Φ(x), the exact (Gaussian CDF) form.
 //
-// erfc(z), z = |x|/√2 >= 0, is evaluated with the rational approximation of
+// With h = Φ(−|x|) = ½·erfc(|x|/√2): GeLU(x) = x − |x|·h for x >= 0 and
+// x·h = −|x|·h for x < 0, i.e. GeLU(x) = max(x, 0) − |x|·h in both cases.
+// erfc(z), z = |x|/√2, is evaluated with the rational approximation of
 // Abramowitz & Stegun, Handbook of Mathematical Functions, formula 7.1.26
 // (C. Hastings): erfc(z) ≈ (a1·t + a2·t² + a3·t³ + a4·t⁴ + a5·t⁵)·e^(−z²),
-// t = 1/(1 + p·z), with |error| ≤ 1.5e-7 on erf. In fp32 (hardware reciprocal
-// and 2^x, each within about 1 ulp) the GeLU error is below |x|·3e-7, far
-// under half a bf16 ulp of GeLU(x) except where GeLU(x) itself is below
-// about 1e-4, i.e. in the far negative tail. About 15 VALU operations.
-__device__ __forceinline__ float gelu_as(float x) {
-  const float z = fabsf(x) * 0.70710678118654752f;
-  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, z, 1.0f));
-  float p = fmaf(t, 1.061405429f, -1.453152027f);
-  p = fmaf(t, p, 1.421413741f);
-  p = fmaf(t, p, -0.284496736f);
-  p = fmaf(t, p, 0.254829592f);
-  const float e = __builtin_amdgcn_exp2f(-1.4426950408889634f * z * z);  // e^(−z²)
-  const float half_erfc = 0.5f * t * p * e;
-  return x * (x >= 0.0f ? 1.0f - half_erfc : half_erfc);
+// t = 1/(1 + p·z), |error| ≤ 1.5e-7 on erf. Here p/√2 and the ½ are folded
+// into the constants and e^(−z²) = 2^(−x²·log2(e)/2). In fp32 (hardware
+// reciprocal and 2^x, each within about 1 ulp) the GeLU error is below
+// |x|·3e-7, far under half a bf16 ulp of GeLU(x) except where GeLU(x) itself
+// is below about 1e-4, i.e. in the far negative tail. 11 VALU operations and
+// 2 transcendentals.
+__device__ __forceinline__ float gelu_exact(float x) {
+  const float ax = fabsf(x);
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f * 0.70710678118654752f, ax, 1.0f));
+  float p = fmaf(t, 0.5f * 1.061405429f, 0.5f * -1.453152027f);
+  p = fmaf(t, p, 0.5f * 1.421413741f);
+  p = fmaf(t, p, 0.5f * -0.284496736f);
+  p = fmaf(t, p, 0.5f * 0.254829592f);
+  const float e = __builtin_amdgcn_exp2f((x * -0.72134752044448170f) * x);  // e^(−x²/2)
+  const float h = (t * p) * e;                                              // Φ(−|x|)
+  return fmaf(-ax, h, fmaxf(x, 0.0f));
 }
-
-// Reference evaluation with the device library's erfcf (used where cost does
-// not matter).
-__device__ __forceinline__ float gelu_erfc(float x) {
-  return 0.5f * x * erfcf(-0.70710678118654752f * x);
-}
-
-__device__ __forceinline__ float gelu_exact(float x) { return gelu_as(x); }
 
 // Consecutive workgroup ids are dispatched round-robin over the 8 XCDs of
 // an MI355X, each of which has its own L2. Renumber so that a run of

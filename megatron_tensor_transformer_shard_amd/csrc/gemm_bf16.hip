@@ -7,32 +7,39 @@
 // C = P·Q with P [M, K] K-contiguous (X or Z_i) and Q [K, N] N-contiguous
 // (A_i or B_i in the pages' math layout), so one tile engine serves both.
 //
-// Tile engine (one workgroup = 4 waves = 256 threads, tile BM x BN, waves 2 x 2):
-//  - k advances in slices of BK = 64. Both operand slices go HBM -> LDS with
-//    global_load_lds_dwordx4 (no staging registers): each wave instruction
-//    fills 1 KB of LDS contiguously, and each lane picks the 16-byte granule
-//    of HBM that belongs at its LDS position, which is how the LDS swizzles
-//    below are realised.
-//  - The P slice is stored K-contiguous, 128-byte rows, 16-byte chunk c of row
-//    r at c ^ ((r & 7) ^ ((r >> 3) & 1)), so the 8 or 16 lanes served per LDS
-//    cycle by a ds_read_b128 of 32 consecutive rows hit distinct banks.
-//  - The Q slice stays N-contiguous as in HBM (rows of 2·BN bytes); granule g
-//    of row r is stored at (g + 4·(r & 3)) mod (BN/8), a rotation by 64 bytes
-//    per row, so the 4 rows read together by a transposing read land in
-//    distinct 64-byte bank groups.
-//  - MFMA v_mfma_f32_32x32x16_bf16. The Q fragment is the A operand and is read
-//    with ds_read_b64_tr_b16: in each 16-lane group, lane L addresses row
-//    L>>2, columns 4·(L&3)..+3 of a 4 x 16 block, and lane j receives column j
-//    of the 4 rows. Two such reads give the 8 k-values of one output column.
-//    The P fragment (B operand) is one ds_read_b128. Each lane ends with 4
-//    consecutive output columns per 32x32 tile (8- or 16-byte stores).
-//  - Two LDS stages, one barrier per slice: the next slice's data is awaited
-//    and the barrier taken before the last k-step's MFMAs, the DMA for the
-//    slice after next is issued right after the barrier, and the first
-//    fragments of the next slice are read while those MFMAs run.
+// Tile engine (one workgroup = 4 waves = 256 threads, tile BM x BN, waves 2 x 2,
+// wave tile up to 128 x 128):
+//  - MFMA v_mfma_f32_16x16x32_bf16. With random operands the chip's power
+//    limit holds a 16x16x32 stream at a markedly higher clock than the
+//    32x32x16 one (fewer accumulator reads and writes per flop), which is
+//    what bounds a dense bf16 GEMM on MI355X.
+//  - k advances in slices of BK = 64 (two MFMA k-steps of 32). Both operand
+//    slices go HBM -> LDS with global_load_lds_dwordx4 (no staging
+//    registers): each wave instruction fills 1 KB of LDS contiguously, and
+//    each lane picks the 16-byte granule of HBM that belongs at its LDS
+//    position, which is how the LDS layouts below are realised.
+//  - P slice: K-contiguous 128-byte rows, 16-byte chunk c of row r stored at
+//    c ^ ((r & 7) ^ ((r >> 3) & 1)). B-operand fragment (16 rows x 32 k):
+//    one ds_read_b128 per lane (row = lane & 15, chunk 4s + lane >> 4).
+//  - Q slice: N-contiguous rows as in HBM; granule g of row r stored at
+//    (g + rot(r)) mod (BN/8), a row-dependent rotation that spreads the 8
+//    rows a 32-lane half of a transposing read touches over distinct banks.
+//    A-operand fragment (16 columns x 32 k): two ds_read_b64_tr_b16 per lane;
+//    in each 16-lane group lane L addresses k-row 8g + 4h + (L >> 2) at
+//    columns 4(L & 3) .. +3 and receives column L of the 4 rows.
+//  - Two LDS stages, one barrier per slice. Slice kt: k-step 0 (reads the
+//    fragments of k-step 1); wait for slice kt+1 and barrier; k-step 1 (reads
+//    the first fragments of slice kt+1 and issues the DMA of slice kt+2 into
+//    the stage just released). Fragment reads and DMA instructions are
+//    interleaved one by one with the MFMAs.
+//  - The main loop is uniform: past the last slice the DMA reloads the last
+//    slice into the stage just released, whose contents are not read again,
+//    so every MFMA has exactly one call site and the accumulators stay in
+//    AGPRs without copies.
 //  - Rows of P beyond M and columns of Q beyond N are loaded from clamped
-//    addresses (their outputs are discarded). In a last partial slice, the
-//    k >= K part of both LDS tiles is cleared after the DMA lands.
+//    addresses (their outputs are discarded). When K is not a multiple of 64
+//    (KTAIL), the last slice loads k clamped into [k_last, K) and the k >= K
+//    part of its LDS stage is cleared after it lands.
 //  - Workgroup ids are remapped so the tiles of one XCD share P and Q panels
 //    in that XCD's L2.
 #include "common.hpp"
@@ -43,6 +50,8 @@ namespace tpmlp {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kBK = 64;  // k per LDS slice
+constexpr int kNS = 2;   // LDS stages
 
 using namespace engine;
 
@@ -50,12 +59,25 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
-template <int BM, int BN, int BK, int NS, int OUT>
+// Granule rotation of Q row `row` (GR granules of 16 bytes per row). A
+// 32-lane half of a ds_read_b64_tr_b16 reads 2 adjacent granules of rows
+// {0,1,2,3, 8,9,10,11} (+ a multiple of 4); with 512- or 256-byte rows
+// (GR = 32, 16) every row starts at bank 0, so those rows are spread by
+// 32 bytes each; with 384-byte rows (GR = 24) odd rows already start half a
+// bank row later, so rows are only spread by 32 bytes per row pair.
+template <int GR>
+__device__ __forceinline__ int q_rot(int row) {
+  if constexpr (GR % 16 == 0) return 2 * (row & 3) + 8 * ((row >> 3) & 1);
+  else return 2 * ((row >> 1) & 1) + 4 * ((row >> 3) & 1);
+}
+
+template <int BM, int BN, int OUT, bool KTAIL>
 __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
     const uint16_t* __restrict__ P, int64_t ldp, const uint16_t* __restrict__ Q, int64_t ldq,
     void* __restrict__ C, int64_t ldc, int M, int N, int K, int group_m) {
+  constexpr int BK = kBK, NS = kNS;
   constexpr int TM = BM / 2, TN = BN / 2;      // wave tile (2 x 2 waves)
-  constexpr int MT = TM / 32, NT = TN / 32;    // 32x32 MFMA tiles per wave
+  constexpr int MT = TM / 16, NT = TN / 16;    // 16x16 MFMA tiles per wave
   constexpr int CH = BK / 8;                   // 16-byte chunks per P row
   constexpr int PROW = BK * 2;                 // bytes per P row
   constexpr int PG = BM * CH;                  // granules in a P slice
@@ -64,11 +86,10 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
   constexpr int P_ROUNDS = PG / kThreads, Q_ROUNDS = QG / kThreads;
   constexpr int ROUNDS = P_ROUNDS + Q_ROUNDS;  // DMA instructions per wave per slice
   constexpr int P_BYTES = PG * 16, STAGE = (PG + QG) * 16;
-  constexpr int KS = BK / 16;                  // MFMA k-steps per slice
-  static_assert(CH == 4 || CH == 8, "BK must be 32 or 64");
+  static_assert(CH == 8, "P rows are 128 bytes");
   static_assert(PG % kThreads == 0 && QG % kThreads == 0, "slices must split over 256 lanes");
-  static_assert(QGR % 4 == 0, "Q rows must hold a multiple of 4 granules");
-  static_assert(NS >= 2 && NS <= 5 && NS * STAGE <= 163840, "LDS stages");
+  static_assert(QGR % 8 == 0, "Q rows must hold a multiple of 8 granules");
+  static_assert(NS * STAGE <= 163840, "LDS stages");
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE];
 
@@ -82,78 +103,61 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 
-  // Per-lane byte offsets (from the tile's wave-uniform base) of the granules
-  // this lane copies; rows of P beyond M and columns of Q beyond N are clamped.
+  const int ktiles = (K + BK - 1) / BK;
+  const int last = ktiles - 1;
+  const int k_last = last * BK;  // first k of the last slice
+
+  // Per-lane byte offsets (from the slice's wave-uniform base) of the
+  // granules this lane copies; rows of P beyond M and columns of Q beyond N
+  // are clamped. With KTAIL the last slice uses offsets clamped into
+  // [k_last, K); they only ever move down, so they stay non-negative.
   const uint16_t* p_base = P + (int64_t)m0 * ldp;
   const uint16_t* q_base = Q + n0;
   uint32_t p_off[P_ROUNDS], q_off[Q_ROUNDS];
-  int p_chunk[P_ROUNDS], q_row[Q_ROUNDS];
+  uint32_t p_off_t[KTAIL ? P_ROUNDS : 1], q_off_t[KTAIL ? Q_ROUNDS : 1];
 #pragma unroll
   for (int j = 0; j < P_ROUNDS; ++j) {
     const int pos = (j * 4 + wave) * 64 + lane;
     const int r = pos / CH, c = swz_p<CH>(r, pos % CH);
-    p_chunk[j] = c;
     p_off[j] = (uint32_t)(((int64_t)(min(m0 + r, M - 1) - m0) * ldp + c * 8) * 2);
+    if constexpr (KTAIL) {
+      const int keep = min(c * 8, K - 8 - k_last);
+      p_off_t[j] = p_off[j] - 2u * (uint32_t)(c * 8 - keep);
+    }
   }
 #pragma unroll
   for (int j = 0; j < Q_ROUNDS; ++j) {
     const int pos = (j * 4 + wave) * 64 + lane;
     const int r = pos / QGR, gp = pos % QGR;
-    const int g = (gp + QGR - 4 * (r & 3)) % QGR;
-    q_row[j] = r;
+    const int g = (gp + QGR - q_rot<QGR>(r)) % QGR;  // granule stored at position gp
     q_off[j] = (uint32_t)(((int64_t)r * ldq + min(n0 + g * 8, N - 8) - n0) * 2);
+    if constexpr (KTAIL) {
+      const int keep = min(r, K - 1 - k_last);
+      q_off_t[j] = q_off[j] - 2u * (uint32_t)(r - keep) * (uint32_t)ldq;
+    }
   }
-
-  const int ktiles = (K + BK - 1) / BK;
-  const bool k_tail = (K % BK) != 0;
   const uint32_t lds0 = lds_addr(smem) + wave * 1024;
 
-  // DMA of slice kt into stage kt % NS: the wave-uniform HBM bases and LDS
-  // address of the slice, and the j-th of its ROUNDS instructions.
-  struct SliceDma {
-    const uint16_t* pb;
-    const uint16_t* qb;
-    uint32_t lp;
-  };
-  auto slice_dma = [&](int kt) {
-    SliceDma d;
-    d.pb = p_base + kt * BK;
-    d.qb = q_base + (int64_t)(kt * BK) * ldq;
-    d.lp = lds0 + (kt % NS) * STAGE;
-    return d;
-  };
-  auto issue_one = [&](const SliceDma& d, int j) {
-    if (j < P_ROUNDS) dma16(d.pb, p_off[j], d.lp + j * 4096);
-    else dma16(d.qb, q_off[j - P_ROUNDS], d.lp + P_BYTES + (j - P_ROUNDS) * 4096);
-  };
-  // Whole slice at once; the last, partial slice clamps k into [k0, K) (the
-  // excess is cleared after it lands) and offsets only move down.
-  auto issue_slice = [&](int kt) {
-    const SliceDma d = slice_dma(kt);
-    if (!(k_tail && kt + 1 == ktiles)) {
-#pragma unroll
-      for (int j = 0; j < ROUNDS; ++j) issue_one(d, j);
-      return;
-    }
-    const int k0 = kt * BK;
-#pragma unroll
-    for (int j = 0; j < P_ROUNDS; ++j) {
-      const int cc = p_chunk[j] * 8, keep = min(cc, K - 8 - k0);
-      dma16(d.pb, p_off[j] - 2u * (uint32_t)(cc - keep), d.lp + j * 4096);
-    }
-#pragma unroll
-    for (int j = 0; j < Q_ROUNDS; ++j) {
-      const int r = q_row[j], keep = min(r, K - 1 - k0);
-      dma16(d.qb, q_off[j] - 2u * (uint32_t)(r - keep) * (uint32_t)ldq,
-            d.lp + P_BYTES + j * 4096);
+  // DMA instruction j of slice kt into LDS stage `stage`.
+  auto issue_one = [&](int kt, int stage, int j) __attribute__((always_inline)) {
+    const uint32_t lp = lds0 + stage * STAGE;
+    if (j < P_ROUNDS) {
+      uint32_t off = p_off[j];
+      if constexpr (KTAIL) off = kt == last ? p_off_t[j] : off;
+      dma16(p_base + kt * BK, off, lp + j * 4096);
+    } else {
+      const int jq = j - P_ROUNDS;
+      uint32_t off = q_off[jq];
+      if constexpr (KTAIL) off = kt == last ? q_off_t[jq] : off;
+      dma16(q_base + (int64_t)(kt * BK) * ldq, off, lp + P_BYTES + jq * 4096);
     }
   };
 
-  // Clear the k >= K part of the last, partial slice (after its DMA landed).
-  auto clear_tail = [&](int kt) {
-    uint8_t* sp = smem + (kt % NS) * STAGE;
+  // Clear the k >= K part of the last slice's stage (after its DMA landed).
+  auto clear_tail = [&]() {
+    uint8_t* sp = smem + (last % NS) * STAGE;
     uint8_t* sq = sp + P_BYTES;
-    const int kvalid = K - kt * BK;  // multiple of 8, in (0, BK)
+    const int kvalid = K - k_last;  // multiple of 8, in (0, BK)
     const u32x4 z = {0u, 0u, 0u, 0u};
     for (int i = t; i < PG; i += kThreads) {
       const int r = i / CH, c = i % CH;
@@ -164,35 +168,30 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
     }
   };
 
-  // Fragment addressing (byte offsets within a stage).
-  // P (B operand): row m, 16-byte chunk 2s + (lane >> 5).
+  // Fragment addressing (k-step s covers k 32s .. 32s+31 of the slice; lane
+  // group g = lane >> 4 holds k 8g .. 8g+7 of its row or column).
   int p_frag[MT];
 #pragma unroll
-  for (int mi = 0; mi < MT; ++mi) p_frag[mi] = wm * TM + mi * 32 + (lane & 31);
-  // Q (A operand): rows k = 16s + 8(lane>>5) + 4h + ((lane&15)>>2),
-  // columns n = wn*TN + ni*32 + 16((lane>>4)&1) + 4(lane&3); the row & 3 of
-  // every row a lane reads is (lane&15)>>2, so its rotated granule is fixed.
-  const int q_rsub = 8 * (lane >> 5) + ((lane & 15) >> 2);
-  const int q_byte = 8 * (lane & 1);
+  for (int mi = 0; mi < MT; ++mi) p_frag[mi] = wm * TM + mi * 16 + (lane & 15);
+  // Every k-row a lane reads is 32s + 4h + q_rsub, whose rotation (bits 0,
+  // 1 and 3 of the row) equals that of q_rsub.
+  const int q_rsub = 8 * (lane >> 4) + ((lane & 15) >> 2);
   int q_pos[NT];
 #pragma unroll
   for (int ni = 0; ni < NT; ++ni)
-    q_pos[ni] = rot_q<QGR>(q_rsub,
-                           (wn * TN + ni * 32 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3)) >> 3) *
-                    16 + q_byte;
+    q_pos[ni] = ((((wn * TN + ni * 16 + 4 * (lane & 3)) >> 3) + q_rot<QGR>(q_rsub)) % QGR) * 16 +
+                8 * (lane & 1);
 
-  // Fragment registers, double-buffered across k-steps. A fragments are two
-  // 8-byte halves (one transposing read each).
   s16x8 afr[2][NT];
   bf16x8 bfr[2][MT];
   constexpr int NREADS = MT + 2 * NT;
-  // idx-th fragment read of k-step s of slice kt into buffer buf; ordered so
-  // that the next k-step's first MFMAs (A fragment 0 with every B fragment)
-  // find their operands first.
-  auto read_one = [&](int kt, int s, int buf, int idx) {
-    const uint8_t* sp = smem + (kt % NS) * STAGE;
+  // idx-th fragment read of k-step s of the slice in `stage` into buffer
+  // buf; ordered so that the next k-step's first MFMAs (A fragment 0 with
+  // every B fragment) find their operands first.
+  auto read_one = [&](int stage, int s, int buf, int idx) __attribute__((always_inline)) {
+    const uint8_t* sp = smem + stage * STAGE;
     const uint8_t* sq = sp + P_BYTES;
-    const int r0 = 16 * s + q_rsub;
+    const int r0 = 32 * s + q_rsub;
     if (idx < 2) {
       const uint8_t* a = sq + (r0 + 4 * idx) * (2 * BN) + q_pos[0];
       const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)a);
@@ -200,7 +199,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
     } else if (idx < 2 + MT) {
       const int mi = idx - 2, r = p_frag[mi];
       bfr[buf][mi] = *reinterpret_cast<const bf16x8*>(
-          sp + r * PROW + swz_p<CH>(r, 2 * s + (lane >> 5)) * 16);
+          sp + r * PROW + swz_p<CH>(r, 4 * s + (lane >> 4)) * 16);
     } else {
       const int ni = 1 + (idx - 2 - MT) / 2, h = (idx - 2 - MT) % 2;
       const uint8_t* a = sq + (r0 + 4 * h) * (2 * BN) + q_pos[ni];
@@ -209,146 +208,122 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
     }
   };
 
-  f32x16 acc[NT][MT];
+  f32x4 acc[NT][MT];
 #pragma unroll
   for (int ni = 0; ni < NT; ++ni)
 #pragma unroll
-    for (int mi = 0; mi < MT; ++mi)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[ni][mi][v] = 0.0f;
+    for (int mi = 0; mi < MT; ++mi) acc[ni][mi] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // One k-step: the NT x MT MFMAs on buffer `cur`; after MFMA i the i-th
-  // fragment read for the next k-step (into cur ^ 1) and, when `dma`, the
-  // i-th DMA instruction of slice dkt are issued, so that neither LDS nor
-  // global-load issue ever stalls the MFMA pipe for long.
-  // (With fewer MFMAs than reads or DMA instructions, slot i takes every
-  // j with j·NMFMA/count == i.)
+  // One k-step: the NT x MT MFMAs on buffer `cur`, each followed by its
+  // share of the fragment reads for the next k-step (stage rstage, k-step
+  // rs, into cur ^ 1) and, when `dma`, of the DMA instructions of slice dkt
+  // into stage dstage.
   constexpr int NMFMA = NT * MT;
-  auto kstep = [&](int cur, bool reads, int rkt, int rs, bool dma, const SliceDma& dd) {
+  static_assert(NREADS <= NMFMA && ROUNDS <= NMFMA, "one MFMA slot per read and DMA");
+  auto kstep = [&](int cur, int rstage, int rs, bool dma, int dkt, int dstage)
+                   __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < NMFMA; ++i) {
       const int ni = i / MT, mi = i % MT;
-      acc[ni][mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+      acc[ni][mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
           __builtin_bit_cast(bf16x8, afr[cur][ni]), bfr[cur][mi], acc[ni][mi], 0, 0, 0);
-      if (reads) {
 #pragma unroll
-        for (int j = 0; j < NREADS; ++j)
-          if ((NREADS <= NMFMA ? j : j * NMFMA / NREADS) == i) read_one(rkt, rs, cur ^ 1, j);
-      }
+      for (int j = 0; j < NREADS; ++j)
+        if (j * NMFMA / NREADS == i) read_one(rstage, rs, cur ^ 1, j);
       if (dma) {
 #pragma unroll
         for (int j = 0; j < ROUNDS; ++j)
-          if ((ROUNDS <= NMFMA ? j : j * NMFMA / ROUNDS) == i) issue_one(dd, j);
+          if (j * NMFMA / ROUNDS == i) issue_one(dkt, dstage, j);
       }
       SCHED_PIN();
     }
   };
 
-  // Prologue: the first NS slices in flight; wait for slice 0.
-  const int pre = min(NS, ktiles);
-  for (int kt = 0; kt < pre; ++kt) issue_slice(kt);
-  wait_dma<ROUNDS, NS - 1 < 3 ? NS - 1 : 3>(pre - 1);
+  // Prologue: slices 0 and 1 into stages 0 and 1 (slice indices past the
+  // end are clamped to the last slice: a reload into a stage whose contents
+  // are never used); wait for slice 0.
+#pragma unroll
+  for (int j = 0; j < ROUNDS; ++j) issue_one(0, 0, j);
+#pragma unroll
+  for (int j = 0; j < ROUNDS; ++j) issue_one(min(1, last), 1, j);
+  waitcnt<ROUNDS, 0>();
   barrier();
-  if (k_tail && ktiles == 1) {
-    clear_tail(0);
-    waitcnt<0, 0>();
+  if (KTAIL && ktiles == 1) {
+    clear_tail();
+    waitcnt<63, 0>();
     barrier();
   }
 #pragma unroll
   for (int i = 0; i < NREADS; ++i) read_one(0, 0, 0, i);
 
-  // Slice kt is read from stage kt % NS. Before its last k-step: wait until
-  // slice kt+1 has landed (slices kt+2 .. kt+NS-1 may still be in flight),
-  // barrier (every wave has finished reading stage kt % NS), then, during
-  // the last k-step, issue slice kt+NS into that stage and read the first
-  // fragments of slice kt+1.
-  auto sync_next = [&](int kt) {
-    wait_dma<ROUNDS, NS - 2 < 3 ? NS - 2 : 3>(min(kt + NS, ktiles) - (kt + 2));
-    barrier();
-    if (k_tail && kt + 2 == ktiles) {
-      clear_tail(kt + 1);
-      waitcnt<0, 0>();
+  // Slice kt lives in stage kt % 2. The DMA issued during its second k-step
+  // always targets that stage, just released by the barrier; near the end
+  // it reloads the last slice there, which is never read again.
+  for (int kt = 0; kt < ktiles; ++kt) {
+    const int st = kt & 1;
+    kstep(0, st, 1, false, 0, 0);
+    waitcnt<0, 0>();  // slice kt+1 has landed (nothing later is in flight)
+    barrier();        // every wave is done reading stage kt % 2
+    if (KTAIL && kt + 2 == ktiles) {
+      clear_tail();
+      waitcnt<63, 0>();
       barrier();
     }
-  };
-  const SliceDma none{};
-
-  // Steady state: every slice issues a full slice kt+NS, interleaved with its
-  // last k-step's MFMAs. (One MFMA sequence per call site keeps the
-  // accumulators in place.)
-  const int steady_end = ktiles - NS - (k_tail ? 1 : 0);
-  int kt = 0;
-  for (; kt < steady_end; ++kt) {
-#pragma unroll
-    for (int s = 0; s + 1 < KS; ++s) kstep(s & 1, true, kt, s + 1, false, none);
-    sync_next(kt);
-    kstep((KS - 1) & 1, true, kt + 1, 0, true, slice_dma(kt + NS));
+    kstep(1, st ^ 1, 0, true, min(kt + 2, last), st);
   }
-  // Drain: the remaining slices; a DMA still due (possibly the partial last
-  // slice) is issued whole.
-  for (; kt < ktiles; ++kt) {
-#pragma unroll
-    for (int s = 0; s + 1 < KS; ++s) kstep(s & 1, true, kt, s + 1, false, none);
-    const bool more = kt + 1 < ktiles;
-    if (more) {
-      sync_next(kt);
-      if (kt + NS < ktiles) issue_slice(kt + NS);
-    }
-    kstep((KS - 1) & 1, more, kt + 1, 0, false, none);
-  }
+  waitcnt<0, 0>();  // no DMA may still write LDS when the workgroup ends
 
-  // Epilogue. Lane holds, for 32x32 tile (ni, mi) and group g = 0..3,
-  // C[m][n .. n+3] with m = (lane & 31), n = 8g + 4·(lane >> 5) (tile-relative).
+  // Epilogue. Lane holds, for 16x16 tile (ni, mi), C[m][n .. n+3] with
+  // m = mi·16 + (lane & 15), n = ni·16 + 4·(lane >> 4) (wave-tile relative).
 #pragma unroll
   for (int ni = 0; ni < NT; ++ni) {
 #pragma unroll
     for (int mi = 0; mi < MT; ++mi) {
-      const int m = m0 + wm * TM + mi * 32 + (lane & 31);
-      if (m >= M) continue;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int n = n0 + wn * TN + ni * 32 + 8 * g + 4 * (lane >> 5);
-        if (n >= N) continue;
-        const float v0 = acc[ni][mi][4 * g + 0], v1 = acc[ni][mi][4 * g + 1];
-        const float v2 = acc[ni][mi][4 * g + 2], v3 = acc[ni][mi][4 * g + 3];
-        if constexpr (OUT == (int)OutKind::F32) {
-          f32x4 o = {v0, v1, v2, v3};
-          *reinterpret_cast<f32x4*>(static_cast<float*>(C) + (int64_t)m * ldc + n) = o;
-        } else if constexpr (OUT == (int)OutKind::GeluBf16) {
-          u32x2 o = {pack_bf16x2(gelu_exact(v0), gelu_exact(v1)),
-                     pack_bf16x2(gelu_exact(v2), gelu_exact(v3))};
-          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(C) + (int64_t)m * ldc + n) = o;
-        } else {
-          u32x2 o = {pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
-          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(C) + (int64_t)m * ldc + n) = o;
-        }
+      const int m = m0 + wm * TM + mi * 16 + (lane & 15);
+      const int n = n0 + wn * TN + ni * 16 + 4 * (lane >> 4);
+      if (m >= M || n >= N) continue;
+      const f32x4 v = acc[ni][mi];
+      if constexpr (OUT == (int)OutKind::F32) {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(C) + (int64_t)m * ldc + n) = v;
+      } else if constexpr (OUT == (int)OutKind::GeluBf16) {
+        const u32x2 o = {pack_bf16x2(gelu_exact(v[0]), gelu_exact(v[1])),
+                         pack_bf16x2(gelu_exact(v[2]), gelu_exact(v[3]))};
+        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(C) + (int64_t)m * ldc + n) = o;
+      } else {
+        const u32x2 o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(C) + (int64_t)m * ldc + n) = o;
       }
     }
   }
 }
 
-constexpr int kBK = 64, kStages = 2;
-
-template <int BM, int BN>
+template <int BM, int BN, bool KTAIL>
 hipError_t launch_cfg(const uint16_t* P, int64_t ldp, const uint16_t* Q, int64_t ldq, void* C,
                       int64_t ldc, int M, int N, int K, OutKind out, hipStream_t stream) {
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   const int group_m = 4;
   switch (out) {
     case OutKind::GeluBf16:
-      hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, kBK, kStages, (int)OutKind::GeluBf16>), dim3(tiles),
+      hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, (int)OutKind::GeluBf16, KTAIL>), dim3(tiles),
                          dim3(kThreads), 0, stream, P, ldp, Q, ldq, C, ldc, M, N, K, group_m);
       break;
     case OutKind::F32:
-      hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, kBK, kStages, (int)OutKind::F32>), dim3(tiles),
+      hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, (int)OutKind::F32, KTAIL>), dim3(tiles),
                          dim3(kThreads), 0, stream, P, ldp, Q, ldq, C, ldc, M, N, K, group_m);
       break;
     case OutKind::Bf16:
-      hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, kBK, kStages, (int)OutKind::Bf16>), dim3(tiles),
+      hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, (int)OutKind::Bf16, KTAIL>), dim3(tiles),
                          dim3(kThreads), 0, stream, P, ldp, Q, ldq, C, ldc, M, N, K, group_m);
       break;
   }
   return hipGetLastError();
+}
+
+template <int BM, int BN>
+hipError_t launch_tile(const uint16_t* P, int64_t ldp, const uint16_t* Q, int64_t ldq, void* C,
+                       int64_t ldc, int M, int N, int K, OutKind out, hipStream_t stream) {
+  if (K % kBK == 0) return launch_cfg<BM, BN, false>(P, ldp, Q, ldq, C, ldc, M, N, K, out, stream);
+  return launch_cfg<BM, BN, true>(P, ldp, Q, ldq, C, ldc, M, N, K, out, stream);
 }
 
 struct TileChoice { int bm, bn; };
@@ -378,10 +353,10 @@ hipError_t launch_gemm_bf16(const uint16_t* P, int64_t ldp, const uint16_t* Q, i
                             hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
   const TileChoice tc = choose_tile(M, N);
-  if (tc.bm == 256 && tc.bn == 256) return launch_cfg<256, 256>(P, ldp, Q, ldq, C, ldc, M, N, K, out, stream);
-  if (tc.bm == 256 && tc.bn == 192) return launch_cfg<256, 192>(P, ldp, Q, ldq, C, ldc, M, N, K, out, stream);
-  if (tc.bm == 256 && tc.bn == 128) return launch_cfg<256, 128>(P, ldp, Q, ldq, C, ldc, M, N, K, out, stream);
-  return launch_cfg<128, 128>(P, ldp, Q, ldq, C, ldc, M, N, K, out, stream);
+  if (tc.bm == 256 && tc.bn == 256) return launch_tile<256, 256>(P, ldp, Q, ldq, C, ldc, M, N, K, out, stream);
+  if (tc.bm == 256 && tc.bn == 192) return launch_tile<256, 192>(P, ldp, Q, ldq, C, ldc, M, N, K, out, stream);
+  if (tc.bm == 256 && tc.bn == 128) return launch_tile<256, 128>(P, ldp, Q, ldq, C, ldc, M, N, K, out, stream);
+  return launch_tile<128, 128>(P, ldp, Q, ldq, C, ldc, M, N, K, out, stream);
 }
 
 }  // namespace tpmlp

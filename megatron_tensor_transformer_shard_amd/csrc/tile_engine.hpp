@@ -24,15 +24,6 @@ __device__ __forceinline__ int swz_p(int r, int c) {
   else return c ^ (((r >> 1) ^ (r >> 3)) & 3);
 }
 
-// Position of granule g in row `row` of an N-contiguous bf16 Q tile with GR
-// granules per row: a rotation by 64 bytes per row, so that the 4 rows a
-// ds_read_b64_tr_b16 lane group reads at one column land in distinct 64-byte
-// bank groups.
-template <int GR>
-__device__ __forceinline__ int rot_q(int row, int g) {
-  return (g + 4 * (row & 3)) % GR;
-}
-
 // LDS byte address of a __shared__ pointer.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) void*)p);
