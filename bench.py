@@ -17,6 +17,7 @@ Prints one JSON line. `value` is TFLOP/s over the whole step (FLOPs =
 4·M·d·F per rank shard; GeLU, scaling and the sum are not counted).
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -43,6 +44,31 @@ import numpy as np  # noqa: E402
 METRIC = "TFLOP/s and % of MFMA peak per TP-rank MLP shard (GeLU(X·A_i)·B_i), 1 GPU"
 PEAK_TFLOPS = {"bf16": 2516.6, "e4m3": 5033.2}   # MI355X dense MFMA (256 CU x 2.4 GHz)
 HBM_PEAK_GBS = 8000.0
+
+
+def kernel_source_sha256() -> str:
+    """Hash of every kernel source file; counter figures are tied to it."""
+    d = os.path.join(ROOT, "megatron_tensor_transformer_shard_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(d)):
+        h.update(f.encode())
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE passes (scaled by the copy calibration), or None when there are
+    none for this workload or the kernels have changed since they were taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        t = json.load(fh)
+    if t.get("source_sha256") != kernel_source_sha256() or kernel not in t.get("kernels", {}):
+        return None
+    return int(round(t["kernels"][kernel]["bytes"]))
 
 
 def log(msg):
@@ -121,9 +147,12 @@ def build_bf16_step(tpm, wl, partial_dtype):
                 timer.around("partial_sum", lambda: tpm.tp_partial_sum(parts, Y=Y))
 
     kern_flops = {"col_gelu": 2 * M * d * F, "row_partial": 2 * M * d * F}
+    # algorithmic bytes: each operand read once, each output written once
+    kern_bytes = {"col_gelu": (M * d + d * F) * 2 + M * F * 2,
+                  "row_partial": (M * F + F * d) * 2 + M * d * parts[0].element_size()}
     psum_bytes = (N * parts[0].element_size() + Y.element_size()) * M * d
     out = Y if N > 1 else parts[0]
-    return step, kern_flops, psum_bytes, (X, A, B), out
+    return step, kern_flops, kern_bytes, psum_bytes, (X, A, B), out
 
 
 def build_e4m3_step(tpm, wl):
@@ -154,7 +183,9 @@ def build_e4m3_step(tpm, wl):
                 timer.around(name, fn)
 
     kern_flops = {"col_gelu_e4m3": 2 * M * d * F, "row_partial_e4m3": 2 * M * d * F}
-    return step, kern_flops, 0, (X, A, B), Y
+    kern_bytes = {"col_gelu_e4m3": M * d + d * F + M * F * 2,
+                  "row_partial_e4m3": M * F + F * d + M * d * 2}
+    return step, kern_flops, kern_bytes, 0, (X, A, B), Y
 
 
 def cpu_baseline(wl, inputs, budget_s):
@@ -243,9 +274,10 @@ def main():
     dtype = "e4m3" if wl.fp8 else "bf16"
     log(f"bench: workload {wl.name}: {wl.description}")
     if wl.fp8:
-        step, kern_flops, psum_bytes, inputs, out = build_e4m3_step(tpm, wl)
+        step, kern_flops, kern_bytes, psum_bytes, inputs, out = build_e4m3_step(tpm, wl)
     else:
-        step, kern_flops, psum_bytes, inputs, out = build_bf16_step(tpm, wl, args.partial_dtype)
+        step, kern_flops, kern_bytes, psum_bytes, inputs, out = build_bf16_step(
+            tpm, wl, args.partial_dtype)
     torch.cuda.synchronize()
 
     for _ in range(args.warmup):
@@ -279,8 +311,10 @@ def main():
     dom = max(kern_flops, key=lambda k: kstats[k]["total_ms"])
     ach = kstats[dom]["tflops"]
     roofline = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2), "peak": peak,
-                "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": None,
-                "flops_per_launch": kern_flops[dom], "avg_launch_us": round(kstats[dom]["avg_us"], 2)}
+                "unit": "TFLOP/s", "frac": round(ach / peak, 4),
+                "traffic": measured_traffic(wl.name, dom),
+                "flops_per_launch": kern_flops[dom], "algorithmic_bytes": kern_bytes[dom],
+                "avg_launch_us": round(kstats[dom]["avg_us"], 2)}
 
     check = sampled_check(wl, inputs, out)
     props = torch.cuda.get_device_properties(0)
