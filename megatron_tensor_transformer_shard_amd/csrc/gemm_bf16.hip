@@ -27,15 +27,18 @@
 //    A-operand fragment (16 columns x 32 k): two ds_read_b64_tr_b16 per lane;
 //    in each 16-lane group lane L addresses k-row 8g + 4h + (L >> 2) at
 //    columns 4(L & 3) .. +3 and receives column L of the 4 rows.
-//  - Two LDS stages, one barrier per slice. Slice kt: k-step 0 (reads the
-//    fragments of k-step 1); wait for slice kt+1 and barrier; k-step 1 (reads
-//    the first fragments of slice kt+1 and issues the DMA of slice kt+2 into
-//    the stage just released). Fragment reads and DMA instructions are
-//    interleaved one by one with the MFMAs.
+//  - Three LDS stages for P and two for Q (3 x 32 + 2 x 32 KB = 160 KB for a
+//    256 x 256 tile), one barrier per slice. Slice kt: k-step 0 (reads the
+//    fragments of k-step 1 and issues the P part of slice kt+2 into the P
+//    stage of slice kt-1); wait for slice kt+1 and barrier; k-step 1 (reads
+//    the first fragments of slice kt+1 and issues the Q part of slice kt+2
+//    into the Q stage just released). Fragment reads and DMA instructions are
+//    interleaved one by one with the MFMAs. A DMA instruction whose address
+//    unit is busy stalls the wave's in-order issue, so splitting a slice's
+//    DMA over both k-steps halves the burst each k-step carries.
 //  - The main loop is uniform: past the last slice the DMA reloads the last
-//    slice into the stage just released, whose contents are not read again,
-//    so every MFMA has exactly one call site and the accumulators stay in
-//    AGPRs without copies.
+//    slice into stages that are not read again, so every MFMA has exactly
+//    one call site and the accumulators stay in AGPRs without copies.
 //  - Rows of P beyond M and columns of Q beyond N are loaded from clamped
 //    addresses (their outputs are discarded). When K is not a multiple of 64
 //    (KTAIL), the last slice loads k clamped into [k_last, K) and the k >= K
@@ -50,8 +53,9 @@ namespace tpmlp {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kBK = 64;  // k per LDS slice
-constexpr int kNS = 2;   // LDS stages
+constexpr int kBK = 64;   // k per LDS slice
+constexpr int kNSP = 3;   // LDS stages of the P operand
+constexpr int kNSQ = 2;   // LDS stages of the Q operand
 
 using namespace engine;
 
@@ -75,7 +79,7 @@ template <int BM, int BN, int OUT, bool KTAIL>
 __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
     const uint16_t* __restrict__ P, int64_t ldp, const uint16_t* __restrict__ Q, int64_t ldq,
     void* __restrict__ C, int64_t ldc, int M, int N, int K, int group_m) {
-  constexpr int BK = kBK, NS = kNS;
+  constexpr int BK = kBK, NSP = kNSP, NSQ = kNSQ;
   constexpr int TM = BM / 2, TN = BN / 2;      // wave tile (2 x 2 waves)
   constexpr int MT = TM / 16, NT = TN / 16;    // 16x16 MFMA tiles per wave
   constexpr int CH = BK / 8;                   // 16-byte chunks per P row
@@ -85,13 +89,14 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
   constexpr int QG = BK * QGR;                 // granules in a Q slice
   constexpr int P_ROUNDS = PG / kThreads, Q_ROUNDS = QG / kThreads;
   constexpr int ROUNDS = P_ROUNDS + Q_ROUNDS;  // DMA instructions per wave per slice
-  constexpr int P_BYTES = PG * 16, STAGE = (PG + QG) * 16;
+  constexpr int P_BYTES = PG * 16, Q_BYTES = QG * 16;  // one stage of each operand
+  constexpr int Q_BASE = NSP * P_BYTES;                // Q stages follow the P stages
   static_assert(CH == 8, "P rows are 128 bytes");
   static_assert(PG % kThreads == 0 && QG % kThreads == 0, "slices must split over 256 lanes");
   static_assert(QGR % 8 == 0, "Q rows must hold a multiple of 8 granules");
-  static_assert(NS * STAGE <= 163840, "LDS stages");
+  static_assert(NSP * P_BYTES + NSQ * Q_BYTES <= 163840, "LDS stages");
 
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NSP * P_BYTES + NSQ * Q_BYTES];
 
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   int tm, tn;
@@ -138,25 +143,22 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
   }
   const uint32_t lds0 = lds_addr(smem) + wave * 1024;
 
-  // DMA instruction j of slice kt into LDS stage `stage`.
-  auto issue_one = [&](int kt, int stage, int j) __attribute__((always_inline)) {
-    const uint32_t lp = lds0 + stage * STAGE;
-    if (j < P_ROUNDS) {
-      uint32_t off = p_off[j];
-      if constexpr (KTAIL) off = kt == last ? p_off_t[j] : off;
-      dma16(p_base + kt * BK, off, lp + j * 4096);
-    } else {
-      const int jq = j - P_ROUNDS;
-      uint32_t off = q_off[jq];
-      if constexpr (KTAIL) off = kt == last ? q_off_t[jq] : off;
-      dma16(q_base + (int64_t)(kt * BK) * ldq, off, lp + P_BYTES + jq * 4096);
-    }
+  // DMA instruction j of the P (Q) part of slice kt into P stage pst (Q stage qst).
+  auto issue_p = [&](int kt, int pst, int j) __attribute__((always_inline)) {
+    uint32_t off = p_off[j];
+    if constexpr (KTAIL) off = kt == last ? p_off_t[j] : off;
+    dma16(p_base + kt * BK, off, lds0 + pst * P_BYTES + j * 4096);
+  };
+  auto issue_q = [&](int kt, int qst, int j) __attribute__((always_inline)) {
+    uint32_t off = q_off[j];
+    if constexpr (KTAIL) off = kt == last ? q_off_t[j] : off;
+    dma16(q_base + (int64_t)(kt * BK) * ldq, off, lds0 + Q_BASE + qst * Q_BYTES + j * 4096);
   };
 
-  // Clear the k >= K part of the last slice's stage (after its DMA landed).
+  // Clear the k >= K part of the last slice's stages (after its DMA landed).
   auto clear_tail = [&]() {
-    uint8_t* sp = smem + (last % NS) * STAGE;
-    uint8_t* sq = sp + P_BYTES;
+    uint8_t* sp = smem + (last % NSP) * P_BYTES;
+    uint8_t* sq = smem + Q_BASE + (last % NSQ) * Q_BYTES;
     const int kvalid = K - k_last;  // multiple of 8, in (0, BK)
     const u32x4 z = {0u, 0u, 0u, 0u};
     for (int i = t; i < PG; i += kThreads) {
@@ -188,9 +190,9 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
   // idx-th fragment read of k-step s of the slice in `stage` into buffer
   // buf; ordered so that the next k-step's first MFMAs (A fragment 0 with
   // every B fragment) find their operands first.
-  auto read_one = [&](int stage, int s, int buf, int idx) __attribute__((always_inline)) {
-    const uint8_t* sp = smem + stage * STAGE;
-    const uint8_t* sq = sp + P_BYTES;
+  auto read_one = [&](int pst, int qst, int s, int buf, int idx) __attribute__((always_inline)) {
+    const uint8_t* sp = smem + pst * P_BYTES;
+    const uint8_t* sq = smem + Q_BASE + qst * Q_BYTES;
     const int r0 = 32 * s + q_rsub;
     if (idx < 2) {
       const uint8_t* a = sq + (r0 + 4 * idx) * (2 * BN) + q_pos[0];
@@ -215,13 +217,16 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
     for (int mi = 0; mi < MT; ++mi) acc[ni][mi] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
   // One k-step: the NT x MT MFMAs on buffer `cur`, each followed by its
-  // share of the fragment reads for the next k-step (stage rstage, k-step
-  // rs, into cur ^ 1) and, when `dma`, of the DMA instructions of slice dkt
-  // into stage dstage.
+  // share of the fragment reads for the next k-step (P stage rp, Q stage rq,
+  // k-step rs, into cur ^ 1) and of the DMA instructions of one operand of
+  // slice dkt (the P part into P stage dst when DQ is false, else the Q
+  // part into Q stage dst).
   constexpr int NMFMA = NT * MT;
-  static_assert(NREADS <= NMFMA && ROUNDS <= NMFMA, "one MFMA slot per read and DMA");
-  auto kstep = [&](int cur, int rstage, int rs, bool dma, int dkt, int dstage)
+  static_assert(NREADS <= NMFMA && P_ROUNDS <= NMFMA && Q_ROUNDS <= NMFMA,
+                "one MFMA slot per read and DMA");
+  auto kstep = [&](int cur, int rp, int rq, int rs, bool dq, int dkt, int dst)
                    __attribute__((always_inline)) {
+    constexpr int NDMA_P = P_ROUNDS, NDMA_Q = Q_ROUNDS;
 #pragma unroll
     for (int i = 0; i < NMFMA; ++i) {
       const int ni = i / MT, mi = i % MT;
@@ -229,23 +234,31 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
           __builtin_bit_cast(bf16x8, afr[cur][ni]), bfr[cur][mi], acc[ni][mi], 0, 0, 0);
 #pragma unroll
       for (int j = 0; j < NREADS; ++j)
-        if (j * NMFMA / NREADS == i) read_one(rstage, rs, cur ^ 1, j);
-      if (dma) {
+        if (j * NMFMA / NREADS == i) read_one(rp, rq, rs, cur ^ 1, j);
+      if (!dq) {
 #pragma unroll
-        for (int j = 0; j < ROUNDS; ++j)
-          if (j * NMFMA / ROUNDS == i) issue_one(dkt, dstage, j);
+        for (int j = 0; j < NDMA_P; ++j)
+          if (j * NMFMA / NDMA_P == i) issue_p(dkt, dst, j);
+      } else {
+#pragma unroll
+        for (int j = 0; j < NDMA_Q; ++j)
+          if (j * NMFMA / NDMA_Q == i) issue_q(dkt, dst, j);
       }
       SCHED_PIN();
     }
   };
 
-  // Prologue: slices 0 and 1 into stages 0 and 1 (slice indices past the
-  // end are clamped to the last slice: a reload into a stage whose contents
-  // are never used); wait for slice 0.
+  // Prologue: slices 0 and 1 into P stages 0, 1 and Q stages 0, 1 (slice
+  // indices past the end are clamped to the last slice: a reload into a
+  // stage whose contents are never used); wait for slice 0.
 #pragma unroll
-  for (int j = 0; j < ROUNDS; ++j) issue_one(0, 0, j);
+  for (int j = 0; j < P_ROUNDS; ++j) issue_p(0, 0, j);
 #pragma unroll
-  for (int j = 0; j < ROUNDS; ++j) issue_one(min(1, last), 1, j);
+  for (int j = 0; j < Q_ROUNDS; ++j) issue_q(0, 0, j);
+#pragma unroll
+  for (int j = 0; j < P_ROUNDS; ++j) issue_p(min(1, last), 1, j);
+#pragma unroll
+  for (int j = 0; j < Q_ROUNDS; ++j) issue_q(min(1, last), 1, j);
   waitcnt<ROUNDS, 0>();
   barrier();
   if (KTAIL && ktiles == 1) {
@@ -254,22 +267,28 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
     barrier();
   }
 #pragma unroll
-  for (int i = 0; i < NREADS; ++i) read_one(0, 0, 0, i);
+  for (int i = 0; i < NREADS; ++i) read_one(0, 0, 0, 0, i);
 
-  // Slice kt lives in stage kt % 2. The DMA issued during its second k-step
-  // always targets that stage, just released by the barrier; near the end
-  // it reloads the last slice there, which is never read again.
+  // Slice kt lives in P stage kt % 3 and Q stage kt % 2. Its fragments are
+  // all read by the end of its first k-step. The P part of slice kt+2 is
+  // copied during the first k-step, into the P stage of slice kt-1 (free
+  // since the previous iteration's barrier); the Q part during the second
+  // k-step, into the Q stage of slice kt (free once this iteration's barrier
+  // has passed). So each k-step carries half of a slice's DMA instructions.
+  // Near the end the DMA reloads the last slice into stages that are never
+  // read again.
   for (int kt = 0; kt < ktiles; ++kt) {
-    const int st = kt & 1;
-    kstep(0, st, 1, false, 0, 0);
-    waitcnt<0, 0>();  // slice kt+1 has landed (nothing later is in flight)
-    barrier();        // every wave is done reading stage kt % 2
+    const int qs = kt & 1;
+    const int ps = kt % 3, ps1 = (kt + 1) % 3, ps2 = (kt + 2) % 3;
+    kstep(0, ps, qs, 1, false, min(kt + 2, last), ps2);
+    waitcnt<P_ROUNDS, 0>();  // slice kt+1 has landed (only the P part of kt+2 may be in flight)
+    barrier();               // every wave is done reading the stages of slice kt
     if (KTAIL && kt + 2 == ktiles) {
       clear_tail();
       waitcnt<63, 0>();
       barrier();
     }
-    kstep(1, st ^ 1, 0, true, min(kt + 2, last), st);
+    kstep(1, ps1, qs ^ 1, 0, true, min(kt + 2, last), qs);
   }
   waitcnt<0, 0>();  // no DMA may still write LDS when the workgroup ends
 

@@ -33,11 +33,12 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // and `base` are wave-uniform. Issued through asm so that the only waits on
 // it are the explicit s_waitcnt below (the compiler cannot tell which LDS
 // stage a DMA writes and would otherwise wait for it before every ds_read).
-// M0 is used by nothing else in these kernels.
+// M0 is used by nothing else in these kernels. GFX9 needs one wait state
+// between an SALU write of M0 and an LDS DMA instruction that reads it.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                :
                : "s"(lds), "v"(off), "s"(base)
                : "memory", "m0");
