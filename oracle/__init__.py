@@ -16,6 +16,10 @@ What it computes, and where the pages define it:
   section): Y_i = Z_i·B_i.
 * Closed form of the output (same section, eq. for Output):
   Y = Z·B = Σ_i Z_i·B_i = Σ_i Y_i.
+* Sequence-parallel share of the sum and the bias ("Megatron-LM deep
+  architecture", sequence-parallel section and the row-parallel code
+  pattern): rank j keeps rows [j·M/N, (j+1)·M/N) of Σ_i Y_i, and the bias
+  is added once, after the reduction.
 * fp8 e4m3 forward GEMMs with amax-derived per-tensor scales
   ("Megatron-LM deep architecture", FP8 hybrid precision section).
 
@@ -29,12 +33,14 @@ exhaustive codec checks against torch's CPU conversions.
 """
 from .codecs import (bf16_decode, bf16_encode, e4m3_decode, e4m3_encode, E4M3_MAX)
 from .mlp import (shard_columns, gelu, col_gelu, row_partial, mlp_shard, partial_sum,
-                  mlp_unsharded, amax, quant_scale, quant_e4m3, col_gelu_e4m3,
-                  requant_z, row_partial_e4m3, mlp_shard_e4m3, quantize_inputs_e4m3)
+                  sp_rows, partial_sum_rows, reduce_scatter_share, mlp_unsharded, amax,
+                  quant_scale, quant_e4m3, col_gelu_e4m3, requant_z, row_partial_e4m3,
+                  mlp_shard_e4m3, quantize_inputs_e4m3)
 
 __all__ = [
     "bf16_decode", "bf16_encode", "e4m3_decode", "e4m3_encode", "E4M3_MAX",
     "shard_columns", "gelu", "col_gelu", "row_partial", "mlp_shard", "partial_sum",
-    "mlp_unsharded", "amax", "quant_scale", "quant_e4m3", "col_gelu_e4m3", "requant_z",
-    "row_partial_e4m3", "mlp_shard_e4m3", "quantize_inputs_e4m3",
+    "sp_rows", "partial_sum_rows", "reduce_scatter_share", "mlp_unsharded", "amax",
+    "quant_scale", "quant_e4m3", "col_gelu_e4m3", "requant_z", "row_partial_e4m3",
+    "mlp_shard_e4m3", "quantize_inputs_e4m3",
 ]

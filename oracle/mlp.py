@@ -98,6 +98,54 @@ def partial_sum(parts) -> np.ndarray:
     return acc
 
 
+def sp_rows(M: int, N: int, rank: int) -> tuple[int, int]:
+    """Row range [lo, hi) of the block output that `rank` keeps under
+    sequence parallelism.
+
+    "Megatron-LM deep architecture", sequence-parallel section: an
+    AllReduce is an AllGather of a ReduceScatter, and after the MLP the
+    ReduceScatter leaves each GPU the summed output for its own 1/N slice of
+    the sequence.  With tokens stored sequence-major ([S, B, H], rows in
+    sequence order) that slice is the contiguous row block
+    [rank·M/N, (rank+1)·M/N).  A row count that N does not divide is an
+    error.
+    """
+    if N < 1 or not (0 <= rank < N):
+        raise ValueError(f"rank {rank} not in [0, {N})")
+    if M % N:
+        raise ValueError(f"{M} rows not divisible by N={N}")
+    R = M // N
+    return rank * R, (rank + 1) * R
+
+
+def partial_sum_rows(parts, lo: int, hi: int, bias=None) -> np.ndarray:
+    """Rows [lo, hi) of Σ_i Y_i (rank order, float64), plus `bias` once.
+
+    The bias of the row-parallel linear is added after the reduction, once
+    ("Megatron-LM deep architecture", code pattern of the row-parallel
+    linear: all-reduce the local output, then add the bias).  `bias` is a
+    float64 vector of the output width, or None.
+    """
+    parts = [np.asarray(p, dtype=np.float64) for p in parts]
+    if not parts:
+        raise ValueError("no partials")
+    M = parts[0].shape[0]
+    if not (0 <= lo <= hi <= M):
+        raise ValueError(f"row range [{lo}, {hi}) outside [0, {M})")
+    acc = partial_sum([p[lo:hi] for p in parts])
+    if bias is not None:
+        acc = acc + np.asarray(bias, dtype=np.float64)[None, :]
+    return acc
+
+
+def reduce_scatter_share(parts, rank: int, bias=None) -> np.ndarray:
+    """Rank `rank`'s share of the ReduceScatter that replaces the AllReduce
+    under sequence parallelism: its row block of Σ_i Y_i, plus the bias."""
+    parts = list(parts)
+    lo, hi = sp_rows(np.asarray(parts[0]).shape[0], len(parts), rank)
+    return partial_sum_rows(parts, lo, hi, bias)
+
+
 def mlp_unsharded(X_bits, A_bits, B_bits) -> np.ndarray:
     """The unsharded block Y = bf16(GeLU(X·A))·B (Z rounded as in a shard)."""
     return row_partial(col_gelu(X_bits, A_bits), B_bits)

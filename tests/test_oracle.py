@@ -150,6 +150,58 @@ def test_partial_sum_rank_order_and_errors():
         oracle.partial_sum([])
 
 
+# ------------------------------------- sequence-parallel share and bias ----
+
+def _tiny_parts(N, M=32, d=64, H=256, seed=40):
+    X, A, B = make_random(M, d, H, seed)
+    return X, A, B, [oracle.mlp_shard(X, A, B, N, r) for r in range(N)]
+
+
+@pytest.mark.parametrize("N", [2, 4, 8])
+def test_all_gather_of_reduce_scatter_is_all_reduce(N):
+    # AllReduce(Y) = AllGather(ReduceScatter(Y)): the N shares, stacked in
+    # rank order, are the full sum, element for element
+    _, _, _, parts = _tiny_parts(N)
+    shares = [oracle.reduce_scatter_share(parts, r) for r in range(N)]
+    assert all(s.shape == (32 // N, 64) for s in shares)
+    assert np.array_equal(np.concatenate(shares, axis=0), oracle.partial_sum(parts))
+
+
+def test_reduce_scatter_shares_sum_to_unsharded_output():
+    X, A, B, parts = _tiny_parts(4)
+    full = np.concatenate([oracle.reduce_scatter_share(parts, r) for r in range(4)])
+    assert _rel_maxdiff(full, oracle.mlp_unsharded(X, A, B)) <= 1e-12
+
+
+def test_bias_added_once_after_the_sum_brute_force():
+    # each element against an exact rational sum of its partials plus one bias
+    rng = np.random.default_rng(41)
+    N, M, d = 3, 6, 16
+    parts = [rng.standard_normal((M, d)) for _ in range(N)]
+    bias = rng.standard_normal(d)
+    for rank in range(N):
+        got = oracle.reduce_scatter_share(parts, rank, bias)
+        lo = rank * (M // N)
+        for r in range(M // N):
+            for c in range(d):
+                exact = sum(Fraction(float(p[lo + r, c])) for p in parts) + Fraction(float(bias[c]))
+                assert abs(Fraction(float(got[r, c])) - exact) <= Fraction(1, 2 ** 48) * max(1, abs(exact))
+
+
+def test_partial_sum_rows_ranges_and_errors():
+    _, _, _, parts = _tiny_parts(2)
+    full = oracle.partial_sum(parts)
+    assert np.array_equal(oracle.partial_sum_rows(parts, 5, 19), full[5:19])
+    assert oracle.partial_sum_rows(parts, 7, 7).shape == (0, 64)
+    with pytest.raises(ValueError):
+        oracle.partial_sum_rows(parts, 10, 40)
+    with pytest.raises(ValueError):
+        oracle.sp_rows(30, 4, 0)           # rows not divisible by N
+    with pytest.raises(ValueError):
+        oracle.sp_rows(32, 4, 4)
+    assert oracle.sp_rows(8192, 8, 7) == (7168, 8192)
+
+
 # ---------------------------------------------------- structured inputs ----
 
 def test_zero_input_gives_zero():

@@ -115,3 +115,37 @@ def test_fp8_no_clamp_rounding_mode_is_caught(monkeypatch):
         return (idx.astype(np.uint8) | np.where(v < 0, 0x80, 0).astype(np.uint8))
     monkeypatch.setattr(omlp, "quant_e4m3", quant)
     assert _pins_fail(FP8_PINS)
+
+
+SP_PINS = [
+    lambda: pins.test_all_gather_of_reduce_scatter_is_all_reduce(4),
+    pins.test_reduce_scatter_shares_sum_to_unsharded_output,
+    pins.test_bias_added_once_after_the_sum_brute_force,
+    pins.test_partial_sum_rows_ranges_and_errors,
+]
+
+
+def test_bias_added_per_partial_is_caught(monkeypatch):
+    def rows(parts, lo, hi, bias=None):
+        parts = [np.asarray(p, np.float64) for p in parts]
+        b = 0.0 if bias is None else np.asarray(bias)[None, :]
+        return omlp.partial_sum([p[lo:hi] + b for p in parts])
+    monkeypatch.setattr(omlp, "partial_sum_rows", rows)
+    monkeypatch.setattr(oracle, "partial_sum_rows", rows)
+    assert _pins_fail(SP_PINS)
+
+
+def test_share_of_the_wrong_rank_is_caught(monkeypatch):
+    monkeypatch.setattr(omlp, "sp_rows", lambda M, N, r: (((r + 1) % N) * (M // N), ((r + 1) % N + 1) * (M // N)))
+    assert _pins_fail(SP_PINS)
+
+
+def test_share_rows_interleaved_instead_of_blocked_is_caught(monkeypatch):
+    # a strided (batch-major) slice instead of the contiguous sequence block
+    def share(parts, rank, bias=None):
+        parts = [np.asarray(p, np.float64) for p in parts]
+        acc = omlp.partial_sum([p[rank::len(parts)] for p in parts])
+        return acc if bias is None else acc + np.asarray(bias)[None, :]
+    monkeypatch.setattr(omlp, "reduce_scatter_share", share)
+    monkeypatch.setattr(oracle, "reduce_scatter_share", share)
+    assert _pins_fail(SP_PINS)
