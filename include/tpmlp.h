@@ -137,6 +137,32 @@ int tp_mlp_shard(const void* X, const void* A, const void* B, void* Y_i, int y_d
 int tp_partial_sum(const void* const* parts, int N, int part_dtype, void* Y, int y_dtype,
                    int64_t numel, void* stream);
 
+/*
+ * A block of rows of the sum of the partial outputs, plus an optional bias
+ * added once, after the sum:
+ *   Y[r - row_begin, c] = (Σ_{i=0}^{N-1} parts[i][r, c]) + bias[c],
+ *   r in [row_begin, row_end), added in rank order in fp32, bias last.
+ * Under sequence parallelism the AllReduce that ends the block becomes a
+ * ReduceScatter that leaves each GPU the sum over its own slice of the
+ * sequence ("Megatron-LM deep architecture", sequence-parallel section:
+ * AllReduce = AllGather(ReduceScatter)); with tokens stored sequence-major
+ * ([S, B, H]), rank j's share is rows [j·M/N, (j+1)·M/N). The bias of the
+ * row-parallel linear is added once, after the reduction (same page, code
+ * pattern of the row-parallel linear), never per partial. row_begin = 0,
+ * row_end = M with a bias is the all-reduce form.
+ * parts : HOST array of N device pointers, each [M, d] dense of part_dtype
+ *   (TPM_F32 or TPM_BF16); 1 <= N <= TPM_MAX_PARTS. d is a multiple of 8.
+ * bias : device [d] of bias_dtype (TPM_F32 or TPM_BF16), or NULL (then
+ *   bias_dtype is ignored).
+ * Y : device [row_end - row_begin, d] dense of y_dtype (TPM_F32 or
+ *   TPM_BF16). Y may be exactly the first row of the block in parts[0]
+ *   (in place) when the dtypes match; any other overlap is an error.
+ * 0 <= row_begin <= row_end <= M; an empty range is a no-op.
+ */
+int tp_partial_sum_rows(const void* const* parts, int N, int part_dtype, int64_t M, int64_t d,
+                        int64_t row_begin, int64_t row_end, const void* bias, int bias_dtype,
+                        void* Y, int y_dtype, void* stream);
+
 /* ------------------------------------------------------------------------
  * fp8 e4m3 variant ("Megatron-LM deep architecture", FP8 hybrid precision:
  * E4M3 for forward activation×weight GEMMs, each tensor scaled by a factor

@@ -22,7 +22,7 @@ import torch  # loads the HIP runtime that libtpmlp.so then binds to
 __all__ = [
     "LIB_PATH", "TpmError", "abi_version", "status_string",
     "tp_mlp_col_gelu", "tp_mlp_row_partial", "tp_mlp_shard", "tp_mlp_shard_workspace_size",
-    "tp_partial_sum", "tp_amax_bf16", "tp_quant_e4m3", "tp_mlp_col_gelu_e4m3",
+    "tp_partial_sum", "tp_partial_sum_rows", "tp_reduce_scatter_share", "tp_amax_bf16", "tp_quant_e4m3", "tp_mlp_col_gelu_e4m3",
     "tp_mlp_row_partial_e4m3", "tp_mlp_shard_e4m3", "tp_mlp_shard_e4m3_workspace_size",
     "TPM_BF16", "TPM_F32", "TPM_E4M3", "EXPORTED_SYMBOLS",
 ]
@@ -44,6 +44,8 @@ _SIGNATURES = {
     "tp_mlp_shard_workspace_size": (_sz, [_i64, _i64, _i64, _int]),
     "tp_mlp_shard": (_int, [_vp, _vp, _vp, _vp, _int, _i64, _i64, _i64, _int, _int, _vp, _sz, _vp]),
     "tp_partial_sum": (_int, [ctypes.POINTER(_vp), _int, _int, _vp, _int, _i64, _vp]),
+    "tp_partial_sum_rows": (_int, [ctypes.POINTER(_vp), _int, _int, _i64, _i64, _i64, _i64, _vp,
+                                   _int, _vp, _int, _vp]),
     "tp_amax_bf16": (_int, [_vp, _i64, _fp, _vp]),
     "tp_quant_e4m3": (_int, [_vp, _i64, _fp, _vp, _fp, _vp]),
     "tp_mlp_col_gelu_e4m3": (_int, [_vp, _fp, _vp, _i64, _fp, _vp, _fp, _i64, _i64, _i64, _vp]),
@@ -218,6 +220,54 @@ def tp_partial_sum(parts, Y: torch.Tensor | None = None, out_dtype=None,
                               _dtype_code(Y.dtype), parts[0].numel(), _stream(stream)),
            "tp_partial_sum")
     return Y
+
+
+def tp_partial_sum_rows(parts, row_begin: int, row_end: int, bias: torch.Tensor | None = None,
+                        Y: torch.Tensor | None = None, out_dtype=None, stream=None) -> torch.Tensor:
+    """Rows [row_begin, row_end) of Σ_i parts[i] (rank order, fp32), plus
+    `bias` once after the sum. parts are [M, d] tensors of one dtype."""
+    parts = list(parts)
+    if not parts:
+        raise ValueError("no partials")
+    dt = parts[0].dtype
+    for i, p in enumerate(parts):
+        _need(p, f"parts[{i}]", dt)
+        if p.dim() != 2 or p.shape != parts[0].shape:
+            raise ValueError("partials must be [M, d] tensors of one shape")
+    M, d = parts[0].shape
+    if Y is None:
+        Y = torch.empty((max(0, row_end - row_begin), d), dtype=out_dtype or dt,
+                        device=parts[0].device)
+    _need(Y, "Y", None)
+    if Y.numel() != max(0, row_end - row_begin) * d:
+        raise ValueError("Y has the wrong size")
+    bptr, bdt = None, TPM_F32
+    if bias is not None:
+        _need(bias, "bias", None)
+        if bias.numel() != d:
+            raise ValueError("bias must have d elements")
+        bptr, bdt = bias.data_ptr(), _dtype_code(bias.dtype)
+    arr = (_vp * len(parts))(*[p.data_ptr() for p in parts])
+    _check(lib.tp_partial_sum_rows(arr, len(parts), _dtype_code(dt), M, d, row_begin, row_end,
+                                   bptr, bdt, Y.data_ptr(), _dtype_code(Y.dtype), _stream(stream)),
+           "tp_partial_sum_rows")
+    return Y
+
+
+def tp_reduce_scatter_share(parts, rank: int, bias: torch.Tensor | None = None,
+                            Y: torch.Tensor | None = None, out_dtype=None,
+                            stream=None) -> torch.Tensor:
+    """Rank `rank`'s share of the sequence-parallel reduce-scatter: rows
+    [rank·M/N, (rank+1)·M/N) of Σ_i parts[i] (N = len(parts)), plus bias."""
+    parts = list(parts)
+    N = len(parts)
+    if N < 1 or not (0 <= rank < N):
+        raise ValueError(f"rank {rank} not in [0, {N})")
+    M = parts[0].shape[0]
+    if M % N:
+        raise ValueError(f"{M} rows not divisible by N={N}")
+    R = M // N
+    return tp_partial_sum_rows(parts, rank * R, (rank + 1) * R, bias, Y, out_dtype, stream)
 
 
 # ---------------------------------------------------------------- fp8 path

@@ -1,6 +1,9 @@
 """Build libtpmlp.so (the C-ABI library and its gfx950 kernels) in-tree with hipcc.
 
-    python -m megatron_tensor_transformer_shard_amd.build_lib [-v]
+    python megatron_tensor_transformer_shard_amd/build_lib.py [-v]
+
+(run as a file: importing the package loads the library, which may not be
+built yet or may be out of date)
 
 Objects go to <package>/_build/, the library to <package>/libtpmlp.so.
 """

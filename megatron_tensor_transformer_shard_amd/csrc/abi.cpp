@@ -174,7 +174,45 @@ int tp_partial_sum(const void* const* parts, int N, int part_dtype, void* Y, int
     if (!in_place && overlap(sy, sp)) return TPM_ERR_ALIAS;
   }
   return status_of(tpmlp::launch_partial_sum(parts, N, part_dtype == TPM_BF16, Y,
-                                             y_dtype == TPM_BF16, numel, as_stream(stream)));
+                                             y_dtype == TPM_BF16, numel, nullptr, 0, 1,
+                                             as_stream(stream)));
+}
+
+int tp_partial_sum_rows(const void* const* parts, int N, int part_dtype, int64_t M, int64_t d,
+                        int64_t row_begin, int64_t row_end, const void* bias, int bias_dtype,
+                        void* Y, int y_dtype, void* stream) {
+  if ((part_dtype != TPM_F32 && part_dtype != TPM_BF16) ||
+      (y_dtype != TPM_F32 && y_dtype != TPM_BF16) ||
+      (bias && bias_dtype != TPM_F32 && bias_dtype != TPM_BF16))
+    return TPM_ERR_DTYPE;
+  if (N < 1 || N > TPM_MAX_PARTS) return TPM_ERR_ARG;
+  if (M < 0 || d <= 0 || d % 8 != 0 || d > kMaxLd || M > kMaxDim ||
+      M * d > (int64_t(1) << 40))
+    return TPM_ERR_SHAPE;
+  if (row_begin < 0 || row_end < row_begin || row_end > M) return TPM_ERR_SHAPE;
+  const int64_t rows = row_end - row_begin;
+  if (rows == 0) return TPM_OK;
+  if (!parts || !Y) return TPM_ERR_NULL;
+  for (int i = 0; i < N; ++i)
+    if (!parts[i]) return TPM_ERR_NULL;
+  if (!aligned16(Y) || (bias && !aligned16(bias))) return TPM_ERR_ALIGN;
+  for (int i = 0; i < N; ++i)
+    if (!aligned16(parts[i])) return TPM_ERR_ALIGN;
+  const int64_t pe = part_dtype == TPM_F32 ? 4 : 2, ye = y_dtype == TPM_F32 ? 4 : 2;
+  const int64_t be = bias_dtype == TPM_F32 ? 4 : 2;
+  const Span sy = mat_span(Y, rows, d, d, ye);
+  const void* first[TPM_MAX_PARTS];
+  for (int i = 0; i < N; ++i) {
+    first[i] = static_cast<const uint8_t*>(parts[i]) + row_begin * d * pe;
+    const Span sp = mat_span(parts[i], M, d, d, pe);
+    // in place: Y is exactly the block's rows of parts[0], same dtype
+    const bool in_place = (i == 0 && first[0] == Y && pe == ye);
+    if (!in_place && overlap(sy, sp)) return TPM_ERR_ALIAS;
+  }
+  if (bias && overlap(sy, mat_span(bias, 1, d, d, be))) return TPM_ERR_ALIAS;
+  return status_of(tpmlp::launch_partial_sum(
+      first, N, part_dtype == TPM_BF16, Y, y_dtype == TPM_BF16, rows * d, bias,
+      bias ? (bias_dtype == TPM_F32 ? 1 : 2) : 0, d, as_stream(stream)));
 }
 
 // ------------------------------------------------------------------ fp8 --

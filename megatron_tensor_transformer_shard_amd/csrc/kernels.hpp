@@ -17,9 +17,11 @@ hipError_t launch_gemm_bf16(const uint16_t* P, int64_t ldp, const uint16_t* Q, i
                             void* C, int64_t ldc, int M, int N, int K, OutKind out,
                             hipStream_t stream);
 
-// Y = Σ_i parts[i] in rank order, fp32 accumulation.
+// Y = Σ_i parts[i] in rank order, fp32 accumulation, then + bias[e % d] when
+// bias_kind is 1 (fp32 bias) or 2 (bf16 bias); bias_kind 0 adds nothing.
 hipError_t launch_partial_sum(const void* const* parts, int nparts, bool parts_bf16, void* Y,
-                              bool y_bf16, int64_t numel, hipStream_t stream);
+                              bool y_bf16, int64_t numel, const void* bias, int bias_kind,
+                              int64_t d, hipStream_t stream);
 
 // fp8 (OCP e4m3) path.
 hipError_t launch_fill_f32(float* p, float v, hipStream_t stream);

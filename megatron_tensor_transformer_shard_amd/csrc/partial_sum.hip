@@ -9,6 +9,15 @@
 // or 8 bf16 elements), issues the loads of up to 8 partials before adding,
 // and adds strictly in rank order in fp32, so the result does not depend on
 // the launch shape.
+//
+// An optional bias (fp32 or bf16, one value per output column) is added once,
+// after the sum, as the row-parallel linear of the pages' code pattern does
+// after its all-reduce. Under sequence parallelism the all-reduce becomes a
+// reduce-scatter and a rank keeps only its block of rows of the sum
+// ("Megatron-LM deep architecture", sequence-parallel section); the host
+// offsets the partial pointers to the first row, so the kernel always sums a
+// contiguous range. Rows are d elements, d a multiple of the chunk, so a
+// chunk never straddles two rows.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -42,10 +51,13 @@ __device__ __forceinline__ void load_chunk(const void* base, int64_t v, float (&
   }
 }
 
+// bias_kind: 0 none, 1 fp32, 2 bf16; d = row length (the bias period).
 template <bool IN_BF16, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads) void partial_sum_kernel(PartPtrs parts, int nparts,
                                                                void* __restrict__ Y, int64_t nvec,
-                                                               int64_t numel) {
+                                                               int64_t numel,
+                                                               const void* __restrict__ bias,
+                                                               int bias_kind, int64_t d) {
   constexpr int V = kVec<IN_BF16>;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
   for (int64_t v = (int64_t)blockIdx.x * kThreads + threadIdx.x; v < nvec; v += stride) {
@@ -66,6 +78,13 @@ __global__ __launch_bounds__(kThreads) void partial_sum_kernel(PartPtrs parts, i
       load_chunk<IN_BF16>(parts.p[i], v, x);
 #pragma unroll
       for (int e = 0; e < V; ++e) acc[e] += x[e];
+    }
+    if (bias_kind != 0) {  // once, after the whole sum
+      const int64_t c0 = (v * V) % d;
+#pragma unroll
+      for (int e = 0; e < V; ++e)
+        acc[e] += bias_kind == 1 ? static_cast<const float*>(bias)[c0 + e]
+                                 : bf16_bits_to_f32(static_cast<const uint16_t*>(bias)[c0 + e]);
     }
     if constexpr (OUT_BF16) {
       if constexpr (V == 8) {
@@ -91,6 +110,9 @@ __global__ __launch_bounds__(kThreads) void partial_sum_kernel(PartPtrs parts, i
                                 : static_cast<const float*>(parts.p[i])[e];
         a = (i == 0) ? x : a + x;
       }
+      if (bias_kind != 0)
+        a += bias_kind == 1 ? static_cast<const float*>(bias)[e % d]
+                            : bf16_bits_to_f32(static_cast<const uint16_t*>(bias)[e % d]);
       if constexpr (OUT_BF16)
         static_cast<uint16_t*>(Y)[e] = (uint16_t)f32_to_bf16_rne(a);
       else
@@ -102,7 +124,8 @@ __global__ __launch_bounds__(kThreads) void partial_sum_kernel(PartPtrs parts, i
 }  // namespace
 
 hipError_t launch_partial_sum(const void* const* parts, int nparts, bool parts_bf16, void* Y,
-                              bool y_bf16, int64_t numel, hipStream_t stream) {
+                              bool y_bf16, int64_t numel, const void* bias, int bias_kind,
+                              int64_t d, hipStream_t stream) {
   if (numel == 0) return hipSuccess;
   PartPtrs pp{};
   for (int i = 0; i < nparts; ++i) pp.p[i] = parts[i];
@@ -113,13 +136,13 @@ hipError_t launch_partial_sum(const void* const* parts, int nparts, bool parts_b
   if (blocks < 1) blocks = 1;
   const dim3 grid((unsigned)blocks), block(kThreads);
   if (parts_bf16 && y_bf16)
-    hipLaunchKernelGGL((partial_sum_kernel<true, true>), grid, block, 0, stream, pp, nparts, Y, nvec, numel);
+    hipLaunchKernelGGL((partial_sum_kernel<true, true>), grid, block, 0, stream, pp, nparts, Y, nvec, numel, bias, bias_kind, d);
   else if (parts_bf16)
-    hipLaunchKernelGGL((partial_sum_kernel<true, false>), grid, block, 0, stream, pp, nparts, Y, nvec, numel);
+    hipLaunchKernelGGL((partial_sum_kernel<true, false>), grid, block, 0, stream, pp, nparts, Y, nvec, numel, bias, bias_kind, d);
   else if (y_bf16)
-    hipLaunchKernelGGL((partial_sum_kernel<false, true>), grid, block, 0, stream, pp, nparts, Y, nvec, numel);
+    hipLaunchKernelGGL((partial_sum_kernel<false, true>), grid, block, 0, stream, pp, nparts, Y, nvec, numel, bias, bias_kind, d);
   else
-    hipLaunchKernelGGL((partial_sum_kernel<false, false>), grid, block, 0, stream, pp, nparts, Y, nvec, numel);
+    hipLaunchKernelGGL((partial_sum_kernel<false, false>), grid, block, 0, stream, pp, nparts, Y, nvec, numel, bias, bias_kind, d);
   return hipGetLastError();
 }
 

@@ -130,6 +130,35 @@ def test_partial_sum_validation():
     assert psum(parts, Y=parts[0], pd=BF16, yd=F32) == EALIAS  # in place needs equal dtypes
 
 
+def psum_rows(parts, N=None, pd=F32, M=64, d=128, rb=0, re=32, bias=None, bd=F32,
+              Y=BASE + 10 * GB, yd=F32):
+    arr = (ctypes.c_void_p * max(1, len(parts)))(*parts)
+    return L.tp_partial_sum_rows(arr, len(parts) if N is None else N, pd, M, d, rb, re, bias, bd,
+                                 Y, yd, None)
+
+
+def test_partial_sum_rows_validation():
+    parts = [BASE + i * GB for i in range(4)]
+    bias = BASE + 20 * GB
+    assert psum_rows(parts, rb=5, re=5) == OK          # empty range: no-op
+    assert psum_rows(parts, N=0) == EARG
+    assert psum_rows(parts, pd=E4M3) == EDTYPE
+    assert psum_rows(parts, yd=E4M3) == EDTYPE
+    assert psum_rows(parts, bias=bias, bd=E4M3) == EDTYPE
+    assert psum_rows(parts, bias=None, bd=E4M3) != EDTYPE   # bias_dtype ignored without a bias
+    assert psum_rows(parts, d=100) == ESHAPE            # d not a multiple of 8
+    assert psum_rows(parts, rb=-1) == ESHAPE
+    assert psum_rows(parts, rb=10, re=9) == ESHAPE
+    assert psum_rows(parts, re=65) == ESHAPE            # beyond M
+    assert psum_rows(parts[:1] + [None] + parts[2:]) == ENULL
+    assert psum_rows(parts, Y=None) == ENULL
+    assert psum_rows(parts, bias=bias + 4) == EALIGN
+    assert psum_rows(parts, Y=BASE + 10 * GB + 8) == EALIGN
+    assert psum_rows(parts, Y=parts[1] + 128 * 4 * 8) == EALIAS   # inside parts[1]
+    assert psum_rows(parts, rb=8, re=16, Y=parts[0]) == EALIAS     # not the block's first row
+    assert psum_rows(parts, bias=BASE + 10 * GB + 64) == EALIAS    # bias overlaps Y
+
+
 def test_fp8_validation():
     sc = BASE + 20 * GB
     assert L.tp_quant_e4m3(BASE, 100, sc, BASE + GB, sc + 64, None) == ESHAPE   # not /16

@@ -246,6 +246,80 @@ def test_partial_sum_rank_order_and_in_place(tpm):
     assert out.data_ptr() == q[0].data_ptr() and torch.all(q[0] == 15.0).item()
 
 
+# ------------------------------------------ sequence-parallel share, bias --
+
+@pytest.mark.parametrize("N,M,d", [(2, 32, 64), (4, 1000, 72), (8, 8192, 4096)])
+def test_reduce_scatter_shares_integer_exact_with_bias(tpm, N, M, d):
+    # integer-valued fp32 partials and bias: every fp32 sum is exact, so each
+    # share must equal the oracle's element for element; the shares stacked in
+    # rank order must equal the all-reduce form (bias added once)
+    import torch
+    rng = np.random.default_rng(N * 1000 + M)
+    parts = rng.integers(-1000, 1000, size=(N, M, d)).astype(np.float32)
+    bias = rng.integers(-50, 50, size=d).astype(np.float32)
+    dparts = [torch.from_numpy(p).cuda() for p in parts]
+    dbias = torch.from_numpy(bias).cuda()
+    log(f"reduce-scatter N={N} M={M} d={d}")
+    shares = [tpm.tp_reduce_scatter_share(dparts, r, bias=dbias) for r in range(N)]
+    full = tpm.tp_partial_sum_rows(dparts, 0, M, bias=dbias)
+    _sync()
+    ref = [oracle.reduce_scatter_share(parts, r, bias) for r in range(N)]
+    for r in range(N):
+        assert np.array_equal(host_f64(shares[r]), ref[r]), f"rank {r}"
+    assert np.array_equal(host_f64(full), oracle.partial_sum_rows(parts, 0, M, bias))
+    assert np.array_equal(np.concatenate([host_f64(x) for x in shares]), host_f64(full))
+
+
+@pytest.mark.parametrize("part_dt,bias_dt,out_dt", [("f32", "f32", "f32"), ("f32", "bf16", "bf16"),
+                                                    ("bf16", "bf16", "f32"), ("bf16", None, "bf16")])
+def test_partial_sum_rows_matches_oracle_on_ragged_range(tpm, part_dt, bias_dt, out_dt):
+    # partial outputs of a real tiny TP=4 shard, an arbitrary row range
+    import torch
+    from workloads import bf16_bits_from_f32
+    X, A, B = make_random(40, 64, 256, 11)
+    parts64 = [oracle.mlp_shard(X, A, B, 4, r) for r in range(4)]
+    rng = np.random.default_rng(12)
+    bias64 = rng.standard_normal(64) * 0.1
+    if part_dt == "f32":
+        parts = [p.astype(np.float32) for p in parts64]
+        dparts = [torch.from_numpy(p).cuda() for p in parts]
+        host_parts = [p.astype(np.float64) for p in parts]
+    else:
+        bits = [bf16_bits_from_f32(p.astype(np.float32)) for p in parts64]
+        dparts = [dev_bf16(b) for b in bits]
+        host_parts = [oracle.bf16_decode(b) for b in bits]
+    dbias, host_bias = None, None
+    if bias_dt == "f32":
+        dbias = torch.from_numpy(bias64.astype(np.float32)).cuda()
+        host_bias = bias64.astype(np.float32).astype(np.float64)
+    elif bias_dt == "bf16":
+        bb = bf16_bits_from_f32(bias64.astype(np.float32))
+        dbias, host_bias = dev_bf16(bb), oracle.bf16_decode(bb)
+    odt = torch.float32 if out_dt == "f32" else torch.bfloat16
+    Y = tpm.tp_partial_sum_rows(dparts, 7, 33, bias=dbias, out_dtype=odt)
+    _sync()
+    ref = oracle.partial_sum_rows(host_parts, 7, 33, host_bias)
+    got = host_f64(Y) if out_dt == "f32" else oracle.bf16_decode(host_bf16_bits(Y))
+    err = max_err_ratio(got, ref)
+    log(f"rows [7,33) parts {part_dt} bias {bias_dt} out {out_dt}: err ratio {err:.3e}")
+    assert err <= (1e-6 if out_dt == "f32" else TOL_BF16)
+    # empty range: no-op
+    E = tpm.tp_partial_sum_rows(dparts, 5, 5)
+    assert E.numel() == 0
+
+
+def test_partial_sum_rows_in_place(tpm):
+    import torch
+    M, d, N = 64, 128, 4
+    q = [torch.full((M, d), float(i + 1), device="cuda") for i in range(N)]
+    before = q[0].clone()
+    out = tpm.tp_partial_sum_rows(q, 16, 32, Y=q[0][16:32])
+    _sync()
+    assert out.data_ptr() == q[0][16:32].data_ptr()
+    assert torch.all(q[0][16:32] == 10.0).item()
+    assert torch.equal(q[0][:16], before[:16]) and torch.equal(q[0][32:], before[32:])
+
+
 # ------------------------------------------------------------ fp8 path ---
 
 def _quant_on_gpu(tpm, bits):
