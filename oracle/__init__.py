@@ -21,7 +21,9 @@ What it computes, and where the pages define it:
   pattern): rank j keeps rows [j·M/N, (j+1)·M/N) of Σ_i Y_i, and the bias
   is added once, after the reduction.
 * fp8 e4m3 forward GEMMs with amax-derived per-tensor scales
-  ("Megatron-LM deep architecture", FP8 hybrid precision section).
+  ("Megatron-LM deep architecture", FP8 hybrid precision section), with the
+  current scale (the tensor's own amax) or the delayed one (448 over the
+  moving average of the amaxes recorded in earlier steps).
 
 Everything is float64, on bfloat16 (or e4m3) inputs decoded exactly.  Z is
 rounded to bfloat16 once, after GeLU, which models the GPU's stored Z.
@@ -35,12 +37,14 @@ from .codecs import (bf16_decode, bf16_encode, e4m3_decode, e4m3_encode, E4M3_MA
 from .mlp import (shard_columns, gelu, col_gelu, row_partial, mlp_shard, partial_sum,
                   sp_rows, partial_sum_rows, reduce_scatter_share, mlp_unsharded, amax,
                   quant_scale, quant_e4m3, col_gelu_e4m3, requant_z, row_partial_e4m3,
-                  mlp_shard_e4m3, quantize_inputs_e4m3)
+                  mlp_shard_e4m3, quantize_inputs_e4m3, delayed_scale, amax_history_push,
+                  col_gelu_e4m3_delayed, mlp_shard_e4m3_delayed)
 
 __all__ = [
     "bf16_decode", "bf16_encode", "e4m3_decode", "e4m3_encode", "E4M3_MAX",
     "shard_columns", "gelu", "col_gelu", "row_partial", "mlp_shard", "partial_sum",
     "sp_rows", "partial_sum_rows", "reduce_scatter_share", "mlp_unsharded", "amax",
     "quant_scale", "quant_e4m3", "col_gelu_e4m3", "requant_z", "row_partial_e4m3",
-    "mlp_shard_e4m3", "quantize_inputs_e4m3",
+    "mlp_shard_e4m3", "quantize_inputs_e4m3", "delayed_scale", "amax_history_push",
+    "col_gelu_e4m3_delayed", "mlp_shard_e4m3_delayed",
 ]

@@ -213,3 +213,54 @@ def mlp_shard_e4m3(Xq, sX, Aq, sA, Bq, sB, N: int = 1, rank: int = 0, return_all
     if return_all:
         return Y, Z, Zq, sZ
     return Y
+
+
+# ----------------------------------------------------------------------------
+# fp8 delayed scaling ("Megatron-LM deep architecture", FP8 hybrid precision
+# and delayed scaling): the scale a step applies is not taken from the
+# tensor's own amax but predicted from the moving average of the amaxes
+# recorded in earlier steps, so no amax has to be known before the tensor is
+# quantised.  Here it is applied to Z, the one tensor quantised inside the
+# path: Z is quantised in the column-parallel GEMM's epilogue with the
+# predicted scale, and its amax is recorded for later steps.
+# ----------------------------------------------------------------------------
+
+def delayed_scale(history) -> np.float32:
+    """Scale from an amax history: s = 448 / mean(history), the mean taken
+    over the recorded values (float64), rounded to fp32, and the division done
+    in fp32 (1 if the history is empty or its mean is 0)."""
+    h = np.asarray(history, dtype=np.float64)
+    if h.size == 0:
+        return np.float32(1.0)
+    mean = np.float32(np.mean(h))
+    if mean == 0.0:
+        return np.float32(1.0)
+    return np.float32(np.float32(E4M3_MAX) / mean)
+
+
+def amax_history_push(history, amax_value, L: int):
+    """Record one step's amax in a window of the last L steps; returns the new
+    window (oldest first) and the scale the next step applies."""
+    if L < 1:
+        raise ValueError("window length must be >= 1")
+    h = list(history)[-(L - 1):] if L > 1 else []
+    h.append(float(np.float32(amax_value)))
+    return h, delayed_scale(h)
+
+
+def col_gelu_e4m3_delayed(Xq, sX, Aq_i, sA, sZ):
+    """Z_q = e4m3(bf16(GeLU((Xq·Aq_i)/(sX·sA)))·sZ) with a given (predicted)
+    scale sZ, and amax(Z) of this step.  Z is rounded to bf16 first, exactly
+    as in the current-scaling path, so the two agree whenever sZ is the same."""
+    Z = col_gelu_e4m3(Xq, sX, Aq_i, sA)
+    return quant_e4m3(Z, np.float32(sZ)), amax(Z)
+
+
+def mlp_shard_e4m3_delayed(Xq, sX, Aq, sA, Bq, sB, sZ, N: int = 1, rank: int = 0):
+    """fp8 partial output of rank `rank` with Z quantised by the predicted
+    scale sZ; returns (Y_i, Z_q, amax(Z))."""
+    H = Aq.shape[1]
+    lo, hi = shard_columns(H, N, rank)
+    Zq, za = col_gelu_e4m3_delayed(Xq, sX, Aq[:, lo:hi], sA, sZ)
+    Y = row_partial_e4m3(Zq, sZ, Bq[lo:hi, :], sB)
+    return Y, Zq, za

@@ -87,8 +87,9 @@ def shard_exact(X_bits, A_bits, B_bits, N, rank):
     return Z, Y
 
 
-def fp8_shard_exact(Xq, sX, Aq, sA, Bq, sB):
-    """Exact fp8 path on codes: returns (Z on the bf16 grid, Z codes, sZ, Y)."""
+def fp8_shard_exact(Xq, sX, Aq, sA, Bq, sB, sZ_given=None):
+    """Exact fp8 path on codes: returns (Z on the bf16 grid, Z codes, sZ, Y).
+    sZ is Z's own amax scale unless sZ_given (a predicted scale) is passed."""
     X = [[e4m3_value(c) for c in row] for row in Xq.tolist()]
     A = [[e4m3_value(c) for c in row] for row in Aq.tolist()]
     B = [[e4m3_value(c) for c in row] for row in Bq.tolist()]
@@ -98,6 +99,8 @@ def fp8_shard_exact(Xq, sX, Aq, sA, Bq, sB):
     zmax = max(abs(z) for row in Z for z in row)
     import numpy as np
     sZ = np.float32(1.0) if zmax == 0 else np.float32(np.float32(448.0) / np.float32(float(zmax)))
+    if sZ_given is not None:
+        sZ = np.float32(sZ_given)
     codes = []
     Zq = []
     for row in Z:

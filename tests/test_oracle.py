@@ -291,6 +291,60 @@ def test_fp8_close_to_bf16_on_small_175b_like_shapes():
     assert _rel_maxdiff(Yq, Yb) < 0.06
 
 
+# ------------------------------------------------- fp8 delayed scaling ----
+
+def test_delayed_scale_moving_average_window():
+    # small integers: every mean below is exact, so each scale is 448/mean
+    # rounded once; the window keeps the last L amaxes
+    h, L = [], 4
+    expect_windows = [[1], [1, 2], [1, 2, 3], [1, 2, 3, 4], [2, 3, 4, 5], [3, 4, 5, 6]]
+    for step, a in enumerate([1, 2, 3, 4, 5, 6]):
+        h, s = oracle.amax_history_push(h, float(a), L)
+        assert h == [float(v) for v in expect_windows[step]]
+        mean = Fraction(sum(expect_windows[step]), len(expect_windows[step]))
+        assert s == np.float32(np.float32(448) / np.float32(float(mean)))
+    assert oracle.amax_history_push([], 7.0, 1)[0] == [7.0]
+    assert oracle.delayed_scale([]) == 1.0
+    assert oracle.delayed_scale([0.0, 0.0]) == 1.0
+    assert oracle.delayed_scale([2.0, 2.0]) == np.float32(224.0)
+    with pytest.raises(ValueError):
+        oracle.amax_history_push([], 1.0, 0)
+
+
+def _fp8_tiny(M, d, F, seed):
+    X, A, B = make_random(M, d, F, seed, sigma=0.3)
+    return (*oracle.quantize_inputs_e4m3(X), *oracle.quantize_inputs_e4m3(A),
+            *oracle.quantize_inputs_e4m3(B))
+
+
+def test_delayed_path_with_the_current_scale_is_the_current_path():
+    Xq, sX, Aq, sA, Bq, sB = _fp8_tiny(6, 32, 16, 31)
+    Y, Z, Zq, sZ = oracle.mlp_shard_e4m3(Xq, sX, Aq, sA, Bq, sB, return_all=True)
+    Yd, Zqd, za = oracle.mlp_shard_e4m3_delayed(Xq, sX, Aq, sA, Bq, sB, sZ)
+    assert np.array_equal(Zq, Zqd) and np.array_equal(Y, Yd)
+    assert za == oracle.amax(Z)
+
+
+@pytest.mark.parametrize("factor", [0.37, 1.0, 3.5])
+def test_delayed_path_matches_brute_force_with_a_predicted_scale(factor):
+    # a predicted scale below, at and above the current one (above: the
+    # largest |Z| saturate at ±448 instead of overflowing)
+    M, d, F = 4, 16, 8
+    Xq, sX, Aq, sA, Bq, sB = _fp8_tiny(M, d, F, 33)
+    Zc = oracle.col_gelu_e4m3(Xq, sX, Aq, sA)
+    sZ = np.float32(oracle.quant_scale(oracle.amax(Zc)) * np.float32(factor))
+    Y, Zq, za = oracle.mlp_shard_e4m3_delayed(Xq, sX, Aq, sA, Bq, sB, sZ)
+    Zb, Zqb, sZb, Yb = brute.fp8_shard_exact(Xq, sX, Aq, sA, Bq, sB, sZ_given=sZ)
+    assert sZb == sZ
+    assert np.array_equal(oracle.e4m3_decode(Zq), np.array([[float(z) for z in r] for r in Zqb]))
+    assert za == max(abs(float(z)) for r in Zb for z in r)
+    assert _rel_maxdiff(Y, np.array([[float(y) for y in r] for r in Yb])) <= 1e-13
+    codes = Zq.astype(np.int64)
+    assert not np.any((codes & 0x7F) == 0x7F)             # never NaN
+    if factor > 1:
+        assert np.max(np.abs(oracle.e4m3_decode(Zq))) == 448.0
+
+
 def test_workload_table_shapes():
     wl = WORKLOADS["7b_tp8"]
     assert (wl.M, wl.d, wl.F) == (8192, 4096, 2048) and wl.H == 4 * wl.d

@@ -149,3 +149,39 @@ def test_share_rows_interleaved_instead_of_blocked_is_caught(monkeypatch):
     monkeypatch.setattr(omlp, "reduce_scatter_share", share)
     monkeypatch.setattr(oracle, "reduce_scatter_share", share)
     assert _pins_fail(SP_PINS)
+
+
+DELAYED_PINS = [
+    pins.test_delayed_scale_moving_average_window,
+    pins.test_delayed_path_with_the_current_scale_is_the_current_path,
+    lambda: pins.test_delayed_path_matches_brute_force_with_a_predicted_scale(3.5),
+    lambda: pins.test_delayed_path_matches_brute_force_with_a_predicted_scale(0.37),
+]
+
+
+def test_delayed_scale_from_the_max_instead_of_the_mean_is_caught(monkeypatch):
+    def scale(history):
+        h = np.asarray(history, np.float64)
+        return np.float32(1.0) if h.size == 0 or h.max() == 0 else np.float32(448.0 / h.max())
+    monkeypatch.setattr(omlp, "delayed_scale", scale)
+    assert _pins_fail(DELAYED_PINS)
+
+
+def test_delayed_window_off_by_one_is_caught(monkeypatch):
+    def push(history, a, L):
+        h = list(history)[-L:] + [float(np.float32(a))]
+        return h, omlp.delayed_scale(h)
+    monkeypatch.setattr(omlp, "amax_history_push", push)
+    monkeypatch.setattr(oracle, "amax_history_push", push)
+    assert _pins_fail(DELAYED_PINS)
+
+
+def test_delayed_quantising_unrounded_z_is_caught(monkeypatch):
+    # quantise GeLU's value before it is rounded to bf16
+    def col(Xq, sX, Aq, sA, sZ):
+        S = (ocodecs.e4m3_decode(Xq) @ ocodecs.e4m3_decode(Aq)) / (float(sX) * float(sA))
+        Zf = omlp.gelu(S)
+        v = np.clip((Zf.astype(np.float32) * np.float32(sZ)), -448, 448)
+        return ocodecs.e4m3_encode(v.astype(np.float64)), float(np.max(np.abs(Zf)))
+    monkeypatch.setattr(omlp, "col_gelu_e4m3_delayed", col)
+    assert _pins_fail(DELAYED_PINS)
