@@ -224,6 +224,62 @@ int tp_mlp_shard_e4m3(const void* Xq, const float* sX, const void* Aq, const flo
                       int64_t M, int64_t d, int64_t H, int N, int rank,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * fp8 delayed scaling ("Megatron-LM deep architecture", FP8 hybrid precision
+ * and delayed scaling: the scale a step applies is predicted from the moving
+ * average of the amaxes measured in earlier steps instead of the tensor's own
+ * amax, so it is known before the tensor is produced). Here it is applied to
+ * Z, the one tensor quantised inside the path: the column-parallel GEMM
+ * quantises Z in its epilogue with the predicted scale and records the step's
+ * amax, which tp_amax_history_push adds to the history.
+ * Z is still rounded to bf16 after GeLU and before the scale is applied, so
+ * with the same scale the codes equal those of the current-scaling path.
+ * ------------------------------------------------------------------------ */
+
+/* Longest amax history a tensor may keep. */
+#define TPM_MAX_HISTORY 65536
+
+/*
+ * Record one step's amax and derive the next step's scale.
+ * history : device fp32 [L], a ring of the recorded amaxes (zero it, with
+ *   count, before the first step).
+ * count : device uint32 [1], the number of steps recorded so far.
+ * The call writes amax[0] into history[count % L], increments count, and sets
+ * next_scale[0] = 448 / mean of the last min(count, L) recorded amaxes (the
+ * mean in fp32; 1 when it is 0). amax, next_scale: device fp32 [1].
+ * 1 <= L <= TPM_MAX_HISTORY. Calls on one history must be ordered on a
+ * stream (each reads what the previous wrote).
+ */
+int tp_amax_history_push(float* history, uint32_t* count, int L, const float* amax,
+                         float* next_scale, void* stream);
+
+/*
+ * fp8 column-parallel step with a given scale for Z:
+ *   Z = bf16(GeLU((Xq·Aq_i)/(sX·sA))), Zq_i = e4m3(clamp(fp32(Z·sZ), ±448)),
+ *   z_amax[0] = max|Z| (the call clears it first; never NULL here).
+ * Xq : device e4m3 [M, d]; Aq_i : device e4m3 [d, F], row stride lda;
+ * sX, sA, sZ : device fp32 [1]; Zq_i : device e4m3 [M, F], dense.
+ */
+int tp_mlp_col_gelu_e4m3_delayed(const void* Xq, const float* sX, const void* Aq_i, int64_t lda,
+                                 const float* sA, const float* sZ, void* Zq_i, float* z_amax,
+                                 int64_t M, int64_t d, int64_t F, void* stream);
+
+/* Bytes of workspace tp_mlp_shard_e4m3_delayed needs (Zq, e4m3 [M, F]).
+ * Returns 0 for invalid sizes. */
+size_t tp_mlp_shard_e4m3_delayed_workspace_size(int64_t M, int64_t d, int64_t H, int N);
+
+/*
+ * fp8 partial output of one rank with Z quantised by the given scale sZ:
+ *   Zq = e4m3(bf16(GeLU((Xq·Aq_i)/(sX·sA)))·sZ), Y_i = bf16((Zq·Bq_i)/(sZ·sB)),
+ *   z_amax[0] = max|Z| (to be recorded with tp_amax_history_push).
+ * Shapes and the shard map as for tp_mlp_shard_e4m3. The workspace holds Zq
+ * on return.
+ */
+int tp_mlp_shard_e4m3_delayed(const void* Xq, const float* sX, const void* Aq, const float* sA,
+                              const void* Bq, const float* sB, const float* sZ, void* Y_i,
+                              float* z_amax, int64_t M, int64_t d, int64_t H, int N, int rank,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

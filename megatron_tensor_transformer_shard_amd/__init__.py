@@ -24,6 +24,8 @@ __all__ = [
     "tp_mlp_col_gelu", "tp_mlp_row_partial", "tp_mlp_shard", "tp_mlp_shard_workspace_size",
     "tp_partial_sum", "tp_partial_sum_rows", "tp_reduce_scatter_share", "tp_amax_bf16", "tp_quant_e4m3", "tp_mlp_col_gelu_e4m3",
     "tp_mlp_row_partial_e4m3", "tp_mlp_shard_e4m3", "tp_mlp_shard_e4m3_workspace_size",
+    "tp_amax_history_push", "tp_mlp_col_gelu_e4m3_delayed", "tp_mlp_shard_e4m3_delayed",
+    "tp_mlp_shard_e4m3_delayed_workspace_size", "AmaxHistory",
     "TPM_BF16", "TPM_F32", "TPM_E4M3", "EXPORTED_SYMBOLS",
 ]
 
@@ -53,6 +55,12 @@ _SIGNATURES = {
     "tp_mlp_shard_e4m3_workspace_size": (_sz, [_i64, _i64, _i64, _int]),
     "tp_mlp_shard_e4m3": (_int, [_vp, _fp, _vp, _fp, _vp, _fp, _vp, _i64, _i64, _i64, _int, _int,
                                  _vp, _sz, _vp]),
+    "tp_amax_history_push": (_int, [_fp, _vp, _int, _fp, _fp, _vp]),
+    "tp_mlp_col_gelu_e4m3_delayed": (_int, [_vp, _fp, _vp, _i64, _fp, _fp, _vp, _fp, _i64, _i64,
+                                            _i64, _vp]),
+    "tp_mlp_shard_e4m3_delayed_workspace_size": (_sz, [_i64, _i64, _i64, _int]),
+    "tp_mlp_shard_e4m3_delayed": (_int, [_vp, _fp, _vp, _fp, _vp, _fp, _fp, _vp, _fp, _i64, _i64,
+                                         _i64, _int, _int, _vp, _sz, _vp]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGNATURES)
 
@@ -355,3 +363,80 @@ def tp_mlp_shard_e4m3(Xq, sX, Aq, sA, Bq, sB, N: int = 1, rank: int = 0, Y_i=Non
                                  workspace.numel() * workspace.element_size(), _stream(stream)),
            "tp_mlp_shard_e4m3")
     return Y_i
+
+
+# ------------------------------------------------------ fp8 delayed scaling
+
+class AmaxHistory:
+    """Device state of one tensor's delayed scale: a ring of the last L
+    recorded amaxes, the count of recorded steps, and the scale the next step
+    applies (`scale`, device fp32 [1]; `initial_scale` until the first push)."""
+
+    def __init__(self, L: int, initial_scale: float = 1.0, device="cuda"):
+        self.L = int(L)
+        self.history = torch.zeros(self.L, dtype=torch.float32, device=device)
+        self.count = torch.zeros(1, dtype=torch.int32, device=device)   # read as uint32
+        self.scale = torch.full((1,), float(initial_scale), dtype=torch.float32, device=device)
+
+    def push(self, amax: torch.Tensor, stream=None) -> torch.Tensor:
+        tp_amax_history_push(self.history, self.count, amax, self.scale, stream)
+        return self.scale
+
+
+def tp_amax_history_push(history: torch.Tensor, count: torch.Tensor, amax: torch.Tensor,
+                         next_scale: torch.Tensor, stream=None) -> torch.Tensor:
+    _need(history, "history", torch.float32)
+    if count.dtype != torch.int32 or count.numel() != 1 or not count.is_cuda:
+        raise ValueError("count must be a one-element int32 device tensor")
+    _check(lib.tp_amax_history_push(_fptr(history), count.data_ptr(), history.numel(), _fptr(amax),
+                                    _fptr(next_scale), _stream(stream)), "tp_amax_history_push")
+    return next_scale
+
+
+def tp_mlp_col_gelu_e4m3_delayed(Xq, sX, Aq_i, sA, sZ, Zq_i=None, z_amax=None, stream=None):
+    """(Zq_i, z_amax): Z quantised to e4m3 in the GEMM's epilogue with the
+    given (predicted) scale sZ, and max|Z| of this call."""
+    _need(Xq, "Xq", torch.uint8, 2)
+    _need(Aq_i, "Aq_i", torch.uint8, 2, contiguous=False)
+    if Aq_i.stride(1) != 1:
+        raise ValueError("Aq_i must have unit column stride")
+    M, d = Xq.shape
+    d2, F = Aq_i.shape
+    if d2 != d:
+        raise ValueError("inner dimensions differ")
+    if Zq_i is None:
+        Zq_i = torch.empty((M, F), dtype=torch.uint8, device=Xq.device)
+    if z_amax is None:
+        z_amax = torch.empty(1, dtype=torch.float32, device=Xq.device)
+    _need(Zq_i, "Zq_i", torch.uint8, 2)
+    _check(lib.tp_mlp_col_gelu_e4m3_delayed(Xq.data_ptr(), _fptr(sX), Aq_i.data_ptr(),
+                                            Aq_i.stride(0), _fptr(sA), _fptr(sZ), Zq_i.data_ptr(),
+                                            _fptr(z_amax), M, d, F, _stream(stream)),
+           "tp_mlp_col_gelu_e4m3_delayed")
+    return Zq_i, z_amax
+
+
+def tp_mlp_shard_e4m3_delayed_workspace_size(M: int, d: int, H: int, N: int) -> int:
+    return int(lib.tp_mlp_shard_e4m3_delayed_workspace_size(M, d, H, N))
+
+
+def tp_mlp_shard_e4m3_delayed(Xq, sX, Aq, sA, Bq, sB, sZ, N: int, rank: int, Y_i=None,
+                              z_amax=None, workspace=None, stream=None):
+    """(Y_i, z_amax): rank `rank`'s fp8 partial output with Z quantised by sZ."""
+    for t, n in ((Xq, "Xq"), (Aq, "Aq"), (Bq, "Bq")):
+        _need(t, n, torch.uint8, 2)
+    M, d = Xq.shape
+    H = Aq.shape[1]
+    if Y_i is None:
+        Y_i = torch.empty((M, d), dtype=torch.bfloat16, device=Xq.device)
+    if z_amax is None:
+        z_amax = torch.empty(1, dtype=torch.float32, device=Xq.device)
+    need = tp_mlp_shard_e4m3_delayed_workspace_size(M, d, H, N)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=Xq.device)
+    _check(lib.tp_mlp_shard_e4m3_delayed(Xq.data_ptr(), _fptr(sX), Aq.data_ptr(), _fptr(sA),
+                                         Bq.data_ptr(), _fptr(sB), _fptr(sZ), Y_i.data_ptr(),
+                                         _fptr(z_amax), M, d, H, N, rank, workspace.data_ptr(),
+                                         workspace.numel() * workspace.element_size(),
+                                         _stream(stream)), "tp_mlp_shard_e4m3_delayed")
+    return Y_i, z_amax

@@ -266,8 +266,8 @@ int tp_mlp_col_gelu_e4m3(const void* Xq, const float* sX, const void* Aq_i, int6
     return TPM_ERR_ALIAS;
   return status_of(tpmlp::launch_gemm_e4m3(
       static_cast<const uint8_t*>(Xq), d, sX, static_cast<const uint8_t*>(Aq_i), lda, sA,
-      static_cast<uint16_t*>(Z_i), F, z_amax, (int)M, (int)F, (int)d, OutKind::GeluBf16,
-      as_stream(stream)));
+      static_cast<uint16_t*>(Z_i), F, z_amax, nullptr, (int)M, (int)F, (int)d,
+      OutKind::GeluBf16, as_stream(stream)));
 }
 
 int tp_mlp_row_partial_e4m3(const void* Zq, const float* sZ, const void* Bq_i, const float* sB,
@@ -283,7 +283,7 @@ int tp_mlp_row_partial_e4m3(const void* Zq, const float* sZ, const void* Bq_i, c
     return TPM_ERR_ALIAS;
   return status_of(tpmlp::launch_gemm_e4m3(
       static_cast<const uint8_t*>(Zq), F, sZ, static_cast<const uint8_t*>(Bq_i), d, sB,
-      static_cast<uint16_t*>(Y_i), d, nullptr, (int)M, (int)d, (int)F, OutKind::Bf16,
+      static_cast<uint16_t*>(Y_i), d, nullptr, nullptr, (int)M, (int)d, (int)F, OutKind::Bf16,
       as_stream(stream)));
 }
 
@@ -331,12 +331,102 @@ int tp_mlp_shard_e4m3(const void* Xq, const float* sX, const void* Aq, const flo
   const uint8_t* Bq_i = static_cast<const uint8_t*>(Bq) + (int64_t)rank * F * d;
   hipStream_t s = as_stream(stream);
   hipError_t e = tpmlp::launch_gemm_e4m3(static_cast<const uint8_t*>(Xq), d, sX, Aq_i, H, sA, Z,
-                                         F, z_amax, (int)M, (int)F, (int)d, OutKind::GeluBf16, s);
+                                         F, z_amax, nullptr, (int)M, (int)F, (int)d,
+                                         OutKind::GeluBf16, s);
   if (e != hipSuccess) return TPM_ERR_HIP;
   e = tpmlp::launch_quant_e4m3(Z, (int64_t)MF, z_amax, Zq, sZ, s);
   if (e != hipSuccess) return TPM_ERR_HIP;
   e = tpmlp::launch_gemm_e4m3(Zq, F, sZ, Bq_i, d, sB, static_cast<uint16_t*>(Y_i), d, nullptr,
-                              (int)M, (int)d, (int)F, OutKind::Bf16, s);
+                              nullptr, (int)M, (int)d, (int)F, OutKind::Bf16, s);
+  return status_of(e);
+}
+
+// ------------------------------------------------- fp8 delayed scaling --
+
+int tp_amax_history_push(float* history, uint32_t* count, int L, const float* amax,
+                         float* next_scale, void* stream) {
+  if (L < 1 || L > TPM_MAX_HISTORY) return TPM_ERR_ARG;
+  if (!history || !count || !amax || !next_scale) return TPM_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(history) & 3u) || (reinterpret_cast<uintptr_t>(count) & 3u) ||
+      (reinterpret_cast<uintptr_t>(amax) & 3u) || (reinterpret_cast<uintptr_t>(next_scale) & 3u))
+    return TPM_ERR_ALIGN;
+  const Span sh = mat_span(history, 1, L, L, 4), sc = mat_span(count, 1, 1, 1, 4);
+  const Span sa = mat_span(amax, 1, 1, 1, 4), ss = mat_span(next_scale, 1, 1, 1, 4);
+  if (overlap(sh, sc) || overlap(sh, sa) || overlap(sh, ss) || overlap(sc, sa) ||
+      overlap(sc, ss) || overlap(sa, ss))
+    return TPM_ERR_ALIAS;
+  return status_of(
+      tpmlp::launch_amax_history_push(history, count, L, amax, next_scale, as_stream(stream)));
+}
+
+int tp_mlp_col_gelu_e4m3_delayed(const void* Xq, const float* sX, const void* Aq_i, int64_t lda,
+                                 const float* sA, const float* sZ, void* Zq_i, float* z_amax,
+                                 int64_t M, int64_t d, int64_t F, void* stream) {
+  int st = check_dims(M, d, F, 16);
+  if (st != TPM_OK) return st;
+  if (lda < F || lda > kMaxLd) return TPM_ERR_SHAPE;
+  if (!z_amax) return TPM_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(z_amax) & 3u) return TPM_ERR_ALIGN;
+  if (M == 0) return status_of(tpmlp::launch_fill_f32(z_amax, 0.0f, as_stream(stream)));
+  if (!Xq || !sX || !Aq_i || !sA || !sZ || !Zq_i) return TPM_ERR_NULL;
+  if (!aligned16(Xq) || !aligned16(Aq_i) || !aligned16(Zq_i) || lda % 16 != 0 ||
+      (reinterpret_cast<uintptr_t>(sZ) & 3u))
+    return TPM_ERR_ALIGN;
+  const Span z = mat_span(Zq_i, M, F, F, 1), za = mat_span(z_amax, 1, 1, 1, 4);
+  for (Span in : {mat_span(Xq, M, d, d, 1), mat_span(Aq_i, d, F, lda, 1), mat_span(sX, 1, 1, 1, 4),
+                  mat_span(sA, 1, 1, 1, 4), mat_span(sZ, 1, 1, 1, 4)})
+    if (overlap(z, in) || overlap(za, in)) return TPM_ERR_ALIAS;
+  if (overlap(z, za)) return TPM_ERR_ALIAS;
+  return status_of(tpmlp::launch_gemm_e4m3(
+      static_cast<const uint8_t*>(Xq), d, sX, static_cast<const uint8_t*>(Aq_i), lda, sA, Zq_i, F,
+      z_amax, sZ, (int)M, (int)F, (int)d, OutKind::GeluE4m3, as_stream(stream)));
+}
+
+size_t tp_mlp_shard_e4m3_delayed_workspace_size(int64_t M, int64_t d, int64_t H, int N) {
+  if (M < 0 || d <= 0 || H <= 0 || N < 1 || H % N != 0) return 0;
+  if (M > kMaxDim || H > kMaxDim) return 0;
+  return round256((size_t)M * (size_t)(H / N)) + 256;
+}
+
+int tp_mlp_shard_e4m3_delayed(const void* Xq, const float* sX, const void* Aq, const float* sA,
+                              const void* Bq, const float* sB, const float* sZ, void* Y_i,
+                              float* z_amax, int64_t M, int64_t d, int64_t H, int N, int rank,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  if (N < 1 || rank < 0 || rank >= N) return TPM_ERR_ARG;
+  if (H <= 0 || H % N != 0) return TPM_ERR_SHAPE;
+  const int64_t F = H / N;
+  int st = check_dims(M, d, F, 16);
+  if (st != TPM_OK) return st;
+  if (H > kMaxLd || H * d > (int64_t(1) << 46)) return TPM_ERR_SHAPE;
+  if (!z_amax) return TPM_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(z_amax) & 3u) return TPM_ERR_ALIGN;
+  if (M == 0) return status_of(tpmlp::launch_fill_f32(z_amax, 0.0f, as_stream(stream)));
+  if (!Xq || !sX || !Aq || !sA || !Bq || !sB || !sZ || !Y_i) return TPM_ERR_NULL;
+  if (!workspace || workspace_bytes < tp_mlp_shard_e4m3_delayed_workspace_size(M, d, H, N))
+    return TPM_ERR_WORKSPACE;
+  if (!aligned16(Xq) || !aligned16(Aq) || !aligned16(Bq) || !aligned16(Y_i) ||
+      !aligned16(workspace) || (reinterpret_cast<uintptr_t>(sZ) & 3u))
+    return TPM_ERR_ALIGN;
+  const Span sy = mat_span(Y_i, M, d, d, 2), sza = mat_span(z_amax, 1, 1, 1, 4);
+  const Span sw = {reinterpret_cast<uintptr_t>(workspace),
+                   reinterpret_cast<uintptr_t>(workspace) +
+                       tp_mlp_shard_e4m3_delayed_workspace_size(M, d, H, N)};
+  for (Span in : {mat_span(Xq, M, d, d, 1), mat_span(Aq, d, H, H, 1), mat_span(Bq, H, d, d, 1),
+                  mat_span(sX, 1, 1, 1, 4), mat_span(sA, 1, 1, 1, 4), mat_span(sB, 1, 1, 1, 4),
+                  mat_span(sZ, 1, 1, 1, 4)})
+    if (overlap(sy, in) || overlap(sw, in) || overlap(sza, in)) return TPM_ERR_ALIAS;
+  if (overlap(sy, sw) || overlap(sy, sza) || overlap(sw, sza)) return TPM_ERR_ALIAS;
+
+  uint8_t* Zq = static_cast<uint8_t*>(workspace);
+  const uint8_t* Aq_i = static_cast<const uint8_t*>(Aq) + (int64_t)rank * F;
+  const uint8_t* Bq_i = static_cast<const uint8_t*>(Bq) + (int64_t)rank * F * d;
+  hipStream_t s = as_stream(stream);
+  hipError_t e = tpmlp::launch_gemm_e4m3(static_cast<const uint8_t*>(Xq), d, sX, Aq_i, H, sA, Zq,
+                                         F, z_amax, sZ, (int)M, (int)F, (int)d,
+                                         OutKind::GeluE4m3, s);
+  if (e != hipSuccess) return TPM_ERR_HIP;
+  e = tpmlp::launch_gemm_e4m3(Zq, F, sZ, Bq_i, d, sB, static_cast<uint16_t*>(Y_i), d, nullptr,
+                              nullptr, (int)M, (int)d, (int)F, OutKind::Bf16, s);
   return status_of(e);
 }
 

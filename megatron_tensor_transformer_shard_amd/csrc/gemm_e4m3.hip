@@ -13,7 +13,14 @@
 //  - gemm_e4m3:  C = epilogue((P·Q)/(sP·sQ)) with v_mfma_scale_f32_32x32x64_f8f6f4
 //                (both operands e4m3, unit block scales), the same tile engine
 //                as the bf16 GEMM with BK = 128 bytes, and either a GeLU +
-//                bf16 + amax(|Z|) epilogue or a plain bf16 store.
+//                bf16 + amax(|Z|) epilogue, the same with Z quantised to e4m3
+//                by a given (delayed) scale, or a plain bf16 store.
+//  - amax_history_push: delayed scaling ("Megatron-LM deep architecture",
+//                FP8 section: the scale a step applies is predicted from the
+//                moving average of the amaxes of earlier steps, so it is known
+//                before the tensor exists and Z can be quantised inside the
+//                GEMM's epilogue). One wave records the step's amax in a ring
+//                of L values and derives the next scale from their mean.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "tile_engine.hpp"
@@ -67,6 +74,30 @@ __device__ __forceinline__ uint32_t cvt_e4m3x2(float a, float b) {
 
 __device__ __forceinline__ float clamp448(float x) {
   return fminf(fmaxf(x, -kE4m3Max), kE4m3Max);
+}
+
+// One wave: lane l sums ring slots l, l+64, ... (the new amax in place of
+// its slot), a butterfly combines the lanes, lane 0 writes the slot, the
+// count and the scale. Reads of the ring all precede lane 0's write.
+__global__ __launch_bounds__(64) void amax_history_push_kernel(float* __restrict__ hist,
+                                                               uint32_t* __restrict__ count, int L,
+                                                               const float* __restrict__ amax,
+                                                               float* __restrict__ next_scale) {
+  const int lane = threadIdx.x;
+  const uint32_t c = count[0];
+  const uint32_t slot = c % (uint32_t)L;
+  const uint32_t n = c < (uint32_t)L ? c + 1u : (uint32_t)L;
+  const float a = amax[0];
+  float sum = 0.0f;
+  for (uint32_t j = lane; j < n; j += 64) sum += (j == slot) ? a : hist[j];
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 64);
+  if (lane == 0) {
+    hist[slot] = a;
+    count[0] = c + 1u;
+    const float mean = sum / (float)n;
+    next_scale[0] = mean > 0.0f ? kE4m3Max / mean : 1.0f;
+  }
 }
 
 // 16 elements per thread per step: 2 x 16-byte bf16 loads, one 16-byte store.
@@ -135,8 +166,8 @@ template <int BM, int BN, int OUT>
 __global__ __launch_bounds__(kThreads) void gemm_e4m3_kernel(
     const uint8_t* __restrict__ P, int64_t ldp, const float* __restrict__ sP,
     const uint8_t* __restrict__ Q, int64_t ldq, const float* __restrict__ sQ,
-    uint16_t* __restrict__ C, int64_t ldc, float* __restrict__ z_amax, int M, int N, int K,
-    int group_m) {
+    void* __restrict__ C, int64_t ldc, float* __restrict__ z_amax, const float* __restrict__ sC,
+    int M, int N, int K, int group_m) {
   constexpr int TM = BM / 2, TN = BN / 2;
   constexpr int MT = TM / 32, NT = TN / 32;
   constexpr int CH = 8, PROW = BK;            // 16-byte chunks / bytes per P row
@@ -345,8 +376,11 @@ __global__ __launch_bounds__(kThreads) void gemm_e4m3_kernel(
     kstep((KS - 1) & 1, more, kt + 1, 0, false, none);
   }
 
-  // Epilogue: dequantise by 1/(sP·sQ); GeLU + bf16 + max|Z|, or bf16.
+  // Epilogue: dequantise by 1/(sP·sQ); GeLU + bf16 + max|Z| (+ e4m3 with the
+  // given scale), or bf16.
+  constexpr bool GELU = OUT == (int)OutKind::GeluBf16 || OUT == (int)OutKind::GeluE4m3;
   const float dq = 1.0f / (sP[0] * sQ[0]);
+  const float sc = OUT == (int)OutKind::GeluE4m3 ? sC[0] : 1.0f;
   float zmax = 0.0f;
 #pragma unroll
   for (int ni = 0; ni < NT; ++ni) {
@@ -362,16 +396,25 @@ __global__ __launch_bounds__(kThreads) void gemm_e4m3_kernel(
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float v = acc[ni][mi][4 * g + e] * dq;
-          const float z = (OUT == (int)OutKind::GeluBf16) ? gelu_exact(v) : v;
+          const float z = GELU ? gelu_exact(v) : v;
           bits[e] = f32_to_bf16_rne(z);
-          if (OUT == (int)OutKind::GeluBf16) zmax = fmaxf(zmax, fabsf(bf16_bits_to_f32(bits[e])));
+          if (GELU) zmax = fmaxf(zmax, fabsf(bf16_bits_to_f32(bits[e])));
         }
-        u32x2 o = {bits[0] | (bits[1] << 16), bits[2] | (bits[3] << 16)};
-        *reinterpret_cast<u32x2*>(C + (int64_t)m * ldc + n) = o;
+        if constexpr (OUT == (int)OutKind::GeluE4m3) {
+          // the bf16 Z times the scale in fp32, clamped to ±448, one RNE rounding
+          float q[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) q[e] = clamp448(bf16_bits_to_f32(bits[e]) * sc);
+          const uint32_t o = cvt_e4m3x2(q[0], q[1]) | (cvt_e4m3x2(q[2], q[3]) << 16);
+          *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(C) + (int64_t)m * ldc + n) = o;
+        } else {
+          u32x2 o = {bits[0] | (bits[1] << 16), bits[2] | (bits[3] << 16)};
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(C) + (int64_t)m * ldc + n) = o;
+        }
       }
     }
   }
-  if (OUT == (int)OutKind::GeluBf16 && z_amax != nullptr) {
+  if (GELU && z_amax != nullptr) {
     zmax = wave_max(zmax);
     if (lane == 0) atomic_max_nonneg(z_amax, zmax);
   }
@@ -381,18 +424,22 @@ __global__ __launch_bounds__(kThreads) void gemm_e4m3_kernel(
 
 template <int BM, int BN>
 hipError_t launch_cfg(const uint8_t* P, int64_t ldp, const float* sP, const uint8_t* Q,
-                      int64_t ldq, const float* sQ, uint16_t* C, int64_t ldc, float* z_amax,
-                      int M, int N, int K, OutKind out, hipStream_t stream) {
+                      int64_t ldq, const float* sQ, void* C, int64_t ldc, float* z_amax,
+                      const float* sC, int M, int N, int K, OutKind out, hipStream_t stream) {
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   const int group_m = 4;
   if (out == OutKind::GeluBf16)
     hipLaunchKernelGGL((e4::gemm_e4m3_kernel<BM, BN, (int)OutKind::GeluBf16>), dim3(tiles),
-                       dim3(kThreads), 0, stream, P, ldp, sP, Q, ldq, sQ, C, ldc, z_amax, M, N,
-                       K, group_m);
+                       dim3(kThreads), 0, stream, P, ldp, sP, Q, ldq, sQ, C, ldc, z_amax, sC, M,
+                       N, K, group_m);
+  else if (out == OutKind::GeluE4m3)
+    hipLaunchKernelGGL((e4::gemm_e4m3_kernel<BM, BN, (int)OutKind::GeluE4m3>), dim3(tiles),
+                       dim3(kThreads), 0, stream, P, ldp, sP, Q, ldq, sQ, C, ldc, z_amax, sC, M,
+                       N, K, group_m);
   else
     hipLaunchKernelGGL((e4::gemm_e4m3_kernel<BM, BN, (int)OutKind::Bf16>), dim3(tiles),
-                       dim3(kThreads), 0, stream, P, ldp, sP, Q, ldq, sQ, C, ldc, z_amax, M, N,
-                       K, group_m);
+                       dim3(kThreads), 0, stream, P, ldp, sP, Q, ldq, sQ, C, ldc, z_amax, sC, M,
+                       N, K, group_m);
   return hipGetLastError();
 }
 
@@ -424,9 +471,17 @@ hipError_t launch_quant_e4m3(const uint16_t* T, int64_t numel, const float* amax
   return hipGetLastError();
 }
 
+hipError_t launch_amax_history_push(float* history, uint32_t* count, int L, const float* amax,
+                                    float* next_scale, hipStream_t stream) {
+  hipLaunchKernelGGL(amax_history_push_kernel, dim3(1), dim3(64), 0, stream, history, count, L,
+                     amax, next_scale);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm_e4m3(const uint8_t* P, int64_t ldp, const float* sP, const uint8_t* Q,
-                            int64_t ldq, const float* sQ, uint16_t* C, int64_t ldc, float* z_amax,
-                            int M, int N, int K, OutKind out, hipStream_t stream) {
+                            int64_t ldq, const float* sQ, void* C, int64_t ldc, float* z_amax,
+                            const float* sC, int M, int N, int K, OutKind out,
+                            hipStream_t stream) {
   if (z_amax != nullptr) {
     hipError_t e = launch_fill_f32(z_amax, 0.0f, stream);
     if (e != hipSuccess) return e;
@@ -444,8 +499,8 @@ hipError_t launch_gemm_e4m3(const uint8_t* P, int64_t ldp, const float* sP, cons
     if (est < best - 1e-9) { best = est; pick = i; }
   }
   if (pick == 0)
-    return launch_cfg<256, 192>(P, ldp, sP, Q, ldq, sQ, C, ldc, z_amax, M, N, K, out, stream);
-  return launch_cfg<128, 128>(P, ldp, sP, Q, ldq, sQ, C, ldc, z_amax, M, N, K, out, stream);
+    return launch_cfg<256, 192>(P, ldp, sP, Q, ldq, sQ, C, ldc, z_amax, sC, M, N, K, out, stream);
+  return launch_cfg<128, 128>(P, ldp, sP, Q, ldq, sQ, C, ldc, z_amax, sC, M, N, K, out, stream);
 }
 
 }  // namespace tpmlp

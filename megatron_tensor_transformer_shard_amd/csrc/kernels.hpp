@@ -9,7 +9,9 @@
 
 namespace tpmlp {
 
-enum class OutKind : int { GeluBf16 = 0, F32 = 1, Bf16 = 2 };
+// GeluE4m3 (e4m3 GEMM only): Z = bf16(GeLU(.)) quantised to e4m3 with a
+// given scale, one byte per element.
+enum class OutKind : int { GeluBf16 = 0, F32 = 1, Bf16 = 2, GeluE4m3 = 3 };
 
 // C[M, N] = epilogue(P[M, K] · Q[K, N]); P rows K-contiguous (stride ldp),
 // Q rows N-contiguous (stride ldq), C dense with stride ldc, all bf16 inputs.
@@ -29,9 +31,16 @@ hipError_t launch_amax_bf16(const uint16_t* T, int64_t numel, float* amax, hipSt
 hipError_t launch_quant_e4m3(const uint16_t* T, int64_t numel, const float* amax, uint8_t* Tq,
                              float* scale, hipStream_t stream);
 // C = epilogue((P·Q) / (sP·sQ)); GeluBf16 also folds max|Z| into z_amax when
-// z_amax is not NULL; Bf16 stores bf16.
+// z_amax is not NULL; Bf16 stores bf16; GeluE4m3 stores e4m3(bf16(GeLU)·sC[0])
+// bytes (ldc in bytes) and folds max|bf16(GeLU)| into z_amax.
 hipError_t launch_gemm_e4m3(const uint8_t* P, int64_t ldp, const float* sP, const uint8_t* Q,
-                            int64_t ldq, const float* sQ, uint16_t* C, int64_t ldc, float* z_amax,
-                            int M, int N, int K, OutKind out, hipStream_t stream);
+                            int64_t ldq, const float* sQ, void* C, int64_t ldc, float* z_amax,
+                            const float* sC, int M, int N, int K, OutKind out,
+                            hipStream_t stream);
+// Delayed scaling: record amax[0] in the ring history[L] at slot count % L,
+// advance count, and write next_scale[0] = 448 / mean of the recorded values
+// (the last min(count, L)), or 1 when that mean is 0.
+hipError_t launch_amax_history_push(float* history, uint32_t* count, int L, const float* amax,
+                                    float* next_scale, hipStream_t stream);
 
 }  // namespace tpmlp

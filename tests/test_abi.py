@@ -190,6 +190,43 @@ def test_fp8_validation():
                                32, 64, 256, 2, 0, BASE + 3 * GB, ws, None) == EALIAS
 
 
+def test_fp8_delayed_validation():
+    sc = BASE + 20 * GB
+    hist, cnt, am, ns = BASE + 21 * GB, BASE + 22 * GB, BASE + 23 * GB, BASE + 24 * GB
+    assert L.tp_amax_history_push(hist, cnt, 0, am, ns, None) == EARG
+    assert L.tp_amax_history_push(hist, cnt, 65537, am, ns, None) == EARG
+    assert L.tp_amax_history_push(None, cnt, 16, am, ns, None) == ENULL
+    assert L.tp_amax_history_push(hist, cnt, 16, am, None, None) == ENULL
+    assert L.tp_amax_history_push(hist + 2, cnt, 16, am, ns, None) == EALIGN
+    assert L.tp_amax_history_push(hist, hist + 32, 16, am, ns, None) == EALIAS   # count inside the ring
+    assert L.tp_amax_history_push(hist, cnt, 16, am, am, None) == EALIAS
+    args = dict(Xq=BASE, sX=sc, Aq=BASE + GB, lda=256, sA=sc + 4, sZ=sc + 8, Zq=BASE + 2 * GB,
+                za=sc + 12, M=32, d=64, F=256)
+
+    def cg(**kw):
+        a = dict(args, **kw)
+        return L.tp_mlp_col_gelu_e4m3_delayed(a["Xq"], a["sX"], a["Aq"], a["lda"], a["sA"], a["sZ"],
+                                              a["Zq"], a["za"], a["M"], a["d"], a["F"], None)
+    assert cg(za=None) == ENULL                      # the step's amax is always recorded
+    assert cg(sZ=None) == ENULL
+    assert cg(d=40) == ESHAPE
+    assert cg(lda=200) == ESHAPE
+    assert cg(Zq=BASE + 16) == EALIAS                # Zq overlaps Xq
+    assert cg(za=sc + 8) == EALIAS                   # amax is the scale
+    ws = L.tp_mlp_shard_e4m3_delayed_workspace_size(32, 64, 256, 2)
+    assert ws >= 32 * 128
+    assert L.tp_mlp_shard_e4m3_delayed_workspace_size(32, 64, 256, 3) == 0
+
+    def sh(rank=0, wsb=ws, wsp=BASE + 4 * GB, za=sc + 12, Y=BASE + 3 * GB):
+        return L.tp_mlp_shard_e4m3_delayed(BASE, sc, BASE + GB, sc, BASE + 2 * GB, sc, sc + 8, Y, za,
+                                           32, 64, 256, 2, rank, wsp, wsb, None)
+    assert sh(rank=2) == EARG
+    assert sh(wsb=ws - 1) == EWS
+    assert sh(za=None) == ENULL
+    assert sh(wsp=BASE + 3 * GB) == EALIAS          # workspace is Y
+    assert sh(Y=BASE + 4 * GB) == EALIAS
+
+
 def test_python_wrapper_rejects_cpu_tensors():
     import torch
     X = torch.zeros(4, 8, dtype=torch.bfloat16)

@@ -329,6 +329,104 @@ def _quant_on_gpu(tpm, bits):
     return amax, Tq, s
 
 
+# ----------------------------------------------- fp8 delayed scaling ------
+
+def test_amax_history_push_ring_and_scale(tpm):
+    import torch
+    L = 5
+    hist = tpm.AmaxHistory(L, initial_scale=1.0)
+    rng = np.random.default_rng(50)
+    window = []
+    pushed = []
+    for step in range(12):
+        # small integers first (every mean exact), then general floats
+        a = float(step + 1) if step < 7 else float(np.float32(rng.uniform(0.1, 9.0)))
+        pushed.append(a)
+        s = hist.push(dev_f32([a]))
+        _sync()
+        window, s_ref = oracle.amax_history_push(window, a, L)
+        got = np.float32(s.item())
+        if step < 7:
+            assert got == s_ref, f"step {step}: {got} vs {s_ref}"
+        else:
+            # the GPU sums the window in fp32: relative error <= (n-1)·2^-24 on
+            # the mean, plus one rounding of the mean and of the division
+            n = len(window)
+            assert abs(float(got) - float(s_ref)) <= ((n + 2) * 2.0 ** -24) * float(s_ref)
+    _sync()
+    assert int(hist.count.item()) == 12
+    ring = hist.history.cpu().numpy()
+    for c, a in enumerate(pushed[-L:], start=12 - L):
+        assert ring[c % L] == np.float32(a)
+
+
+def _fp8_inputs(M, d, F, seed, sigma=0.3):
+    X, A, B = make_random(M, d, F, seed, sigma=sigma)
+    return [oracle.quantize_inputs_e4m3(T) for T in (X, A, B)]
+
+
+@pytest.mark.parametrize("M,d,F", [(300, 272, 800), (257, 512, 2048), (1, 64, 64)])
+def test_col_gelu_e4m3_delayed_equals_current_path_at_the_current_scale(tpm, M, d, F):
+    import torch
+    (Xq, sX), (Aq, sA), _ = _fp8_inputs(M, d, F, M + d)
+    dX, dA, dsX, dsA = dev_u8(Xq), dev_u8(Aq), dev_f32([sX]), dev_f32([sA])
+    za = torch.empty(1, dtype=torch.float32, device="cuda")
+    Z = tpm.tp_mlp_col_gelu_e4m3(dX, dsX, dA, dsA, z_amax=za)
+    Zq, sZ = tpm.tp_quant_e4m3(Z, za)
+    Zq_d, za_d = tpm.tp_mlp_col_gelu_e4m3_delayed(dX, dsX, dA, dsA, sZ)
+    _sync()
+    log(f"delayed at the current scale M={M} d={d} F={F}: sZ={sZ.item()}")
+    assert np.array_equal(Zq_d.cpu().numpy(), Zq.cpu().numpy())
+    assert za_d.item() == za.item()
+
+
+@pytest.mark.parametrize("factor", [0.37, 3.5])
+def test_col_gelu_e4m3_delayed_with_a_predicted_scale(tpm, factor):
+    # codes must be the oracle's quantisation of the GPU's own bf16 Z with the
+    # same scale (same fp32 product, clamp and rounding); a scale above the
+    # current one saturates at ±448, never NaN
+    import torch
+    (Xq, sX), (Aq, sA), _ = _fp8_inputs(257, 512, 2048, 77)
+    dX, dA, dsX, dsA = dev_u8(Xq), dev_u8(Aq), dev_f32([sX]), dev_f32([sA])
+    za = torch.empty(1, dtype=torch.float32, device="cuda")
+    Z = tpm.tp_mlp_col_gelu_e4m3(dX, dsX, dA, dsA, z_amax=za)
+    _sync()
+    sZ = np.float32(np.float32(448.0) / np.float32(za.item()) * np.float32(factor))
+    Zq_d, _ = tpm.tp_mlp_col_gelu_e4m3_delayed(dX, dsX, dA, dsA, dev_f32([sZ]))
+    _sync()
+    ref = oracle.quant_e4m3(host_bf16_bits(Z), sZ)
+    got = Zq_d.cpu().numpy()
+    assert np.array_equal(got, ref)
+    assert not np.any((got & 0x7F) == 0x7F)
+    if factor > 1:
+        assert np.max(np.abs(oracle.e4m3_decode(got))) == 448.0
+
+
+def test_fp8_shard_delayed_steps_vs_oracle(tpm):
+    # three steps of one rank's shard: the first with the initial scale, the
+    # next ones with the scale predicted from the recorded amaxes
+    import torch
+    M, d, H, N, rank = 257, 512, 2048, 2, 1
+    L = 16
+    hist = tpm.AmaxHistory(L, initial_scale=64.0)
+    window = []
+    for step in range(3):
+        (Xq, sX), (Aq, sA), (Bq, sB) = _fp8_inputs(M, d, H, 90 + step)
+        sZ_used = np.float32(hist.scale.item())
+        Y, za = tpm.tp_mlp_shard_e4m3_delayed(dev_u8(Xq), dev_f32([sX]), dev_u8(Aq), dev_f32([sA]),
+                                              dev_u8(Bq), dev_f32([sB]), hist.scale, N, rank)
+        _sync()
+        Y_ref, _, za_ref = oracle.mlp_shard_e4m3_delayed(Xq, sX, Aq, sA, Bq, sB, sZ_used, N, rank)
+        err = max_err_ratio(oracle.bf16_decode(host_bf16_bits(Y)), Y_ref)
+        log(f"delayed step {step}: sZ={sZ_used} amax {za.item():.5f} vs {za_ref:.5f} err {err:.3e}")
+        assert err <= TOL_E4M3
+        assert abs(za.item() - za_ref) <= 2.0 ** -7 * za_ref   # one bf16 ulp of the largest |Z|
+        window, _ = oracle.amax_history_push(window, za.item(), L)
+        hist.push(za)
+    _sync()
+    assert int(hist.count.item()) == 3
+
+
 @pytest.mark.parametrize("shape,sigma", [((300, 272), 1.0), ((64, 4096), 0.006), ((17, 16), 3.0)])
 def test_amax_and_quant_codes_bit_exact(tpm, shape, sigma):
     X, _, _ = make_random(shape[0], shape[1], 16, seed=shape[0], x_sigma=sigma)
