@@ -10,7 +10,7 @@
 //  - amax_bf16:  max |T| of a bf16 tensor -> one float (atomic max on the bits;
 //                non-negative floats order like their unsigned bit patterns).
 //  - quant_e4m3: s = 448/amax; Tq = e4m3(clamp(T·s, ±448)), RNE (v_cvt_pk_fp8_f32).
-//  - gemm_e4m3:  C = epilogue((P·Q)/(sP·sQ)) with v_mfma_scale_f32_32x32x64_f8f6f4
+//  - gemm_e4m3:  C = epilogue((P·Q)/(sP·sQ)) with v_mfma_scale_f32_16x16x128_f8f6f4
 //                (both operands e4m3, unit block scales), the same tile engine
 //                as the bf16 GEMM with BK = 128 bytes, and either a GeLU +
 //                bf16 + amax(|Z|) epilogue, the same with Z quantised to e4m3
@@ -129,134 +129,142 @@ __global__ __launch_bounds__(kThreads) void quant_e4m3_kernel(const uint16_t* __
 }
 
 // ---------------------------------------------------------------------------
-// e4m3 GEMM on the same tile engine as the bf16 GEMMs (see gemm_bf16.hip): a
-// k-slice is 128 e4m3 values (BK bytes = 128, the same 128-byte P rows), two
-// LDS stages filled by global_load_lds_dwordx4, one barrier per slice, and one
-// fragment read and one DMA instruction interleaved after each MFMA.
-//  - MFMA v_mfma_scale_f32_32x32x64_f8f6f4 (both operands e4m3, unit block
-//    scales): each lane holds 32 k-values of one row (A) or column (B); lane
-//    half h = lane >> 5 holds k = 64s + 32h .. +31 of k-step s.
-//  - P fragment (B operand): two ds_read_b128 (16-byte chunks 4s+2h, 4s+2h+1).
+// e4m3 GEMM on the same tile engine as the bf16 GEMMs (see gemm_bf16.hip).
+//  - MFMA v_mfma_scale_f32_16x16x128_f8f6f4 (both operands e4m3, unit block
+//    scales): a k-slice is 128 e4m3 values (128-byte P rows) and one MFMA
+//    k-step. Lane group g = lane >> 4 holds 32 consecutive k-values,
+//    k = 32g .. 32g+31, of one row (B operand, from P) or one column (A
+//    operand, from Q); any k order works as long as both operands agree.
+//  - A workgroup is 4 waves (2 x 2) with a wave tile of up to 128 x 128
+//    (MT x NT fragments of 16). The k-step is split into two halves of MFMAs
+//    (fragment columns ni < NT/2, then ni >= NT/2) around the slice's barrier,
+//    as the bf16 engine splits a slice into its two k-steps.
+//  - P fragment (B operand): two ds_read_b128 (16-byte chunks 2g, 2g+1 of the
+//    swizzled 128-byte row). The second half runs mi-major, so P fragment mi
+//    is reloaded for the next slice right after its last MFMA.
 //  - Q fragment (A operand) from the N-contiguous e4m3 Q tile: four
-//    ds_read_b64_tr_b8. In each 16-lane group, lane L addresses row L>>1,
-//    bytes 8·(L&1)..+7 of an 8-row x 16-byte block, and lane j receives byte
-//    column j of the 8 rows: 8 k-values of one output column per read.
-//  - Q rows are BN bytes; granule g of row r is rotated so that the 8 rows x 2
-//    granules one read instruction touches per lane half fall in distinct
-//    16-byte bank groups (rotations found by exhaustive search over
-//    f(r) = a·(r&1) + b·((r>>1)&1) + c·((r>>2)&1)).
+//    ds_read_b64_tr_b8. In each 16-lane group, lane L addresses k-row
+//    32g + 8q + (L >> 1), bytes 8·(L & 1) .. +7 of the fragment's 16-byte
+//    column granule, and lane j receives byte column j of the 8 rows: 8
+//    k-values of one output column per read. Single-buffered: fragment ni is
+//    reloaded for the next slice once its last MFMA of this slice is issued.
+//  - Granule g of Q row r is stored at (g + f(r)) mod (BN/16); f depends on
+//    bits 0-2 and 5 of r and makes every 32-lane pass of a transposing read
+//    hit 64 distinct banks (found by exhaustive search).
+//  - Three LDS stages for P and two for Q, one barrier per slice: the first
+//    half k-step reads the second-half Q fragments of slice kt and issues the
+//    P part of slice kt+2 into the P stage of slice kt-1; wait for slice kt+1
+//    and barrier; the second half reads the P fragments and first-half Q
+//    fragments of slice kt+1 and issues the Q part of slice kt+2 into the Q
+//    stage of slice kt. The main loop is uniform (the DMA reloads the last
+//    slice into stages never read again near the end).
+//  - When K is not a multiple of 128, the last slice loads k clamped into
+//    [k_last, K) and its k >= K part is cleared in LDS after it lands.
 // ---------------------------------------------------------------------------
 namespace e4 {
 
 using namespace engine;
 
-constexpr int BK = 128, NS = 2, KS = BK / 64;
+constexpr int BK = 128;   // k (bytes) per LDS slice
+constexpr int NSP = 3, NSQ = 2;
 
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 
+// Rotation of the granules of Q row r (GR granules of 16 bytes per row).
 template <int GR>
-__device__ __forceinline__ int rot_q8(int r, int g) {
-  if constexpr (GR == 16) return (g + 2 * (r & 7)) & 15;
-  else if constexpr (GR == 12) return (g + 2 * ((r >> 2) & 1)) % 12;
-  else return (g + 2 * ((r >> 1) & 1) + 4 * ((r >> 2) & 1)) % GR;
+__device__ __forceinline__ int q8_rot(int r) {
+  if constexpr (GR == 16) return (r & 7) + 8 * ((r >> 5) & 1);
+  else if constexpr (GR == 12) return ((r >> 2) & 1) + 2 * ((r >> 5) & 1);
+  else return ((r >> 1) & 1) + 2 * ((r >> 2) & 1) + 4 * ((r >> 5) & 1);
 }
 
-template <int BM, int BN, int OUT>
+template <int BM, int BN, int OUT, bool KTAIL>
 __global__ __launch_bounds__(kThreads) void gemm_e4m3_kernel(
     const uint8_t* __restrict__ P, int64_t ldp, const float* __restrict__ sP,
     const uint8_t* __restrict__ Q, int64_t ldq, const float* __restrict__ sQ,
     void* __restrict__ C, int64_t ldc, float* __restrict__ z_amax, const float* __restrict__ sC,
     int M, int N, int K, int group_m) {
-  constexpr int TM = BM / 2, TN = BN / 2;
-  constexpr int MT = TM / 32, NT = TN / 32;
-  constexpr int CH = 8, PROW = BK;            // 16-byte chunks / bytes per P row
-  constexpr int PG = BM * CH;
-  constexpr int QGR = BN / 16;                // granules per Q row
-  constexpr int QG = BK * QGR;
+  constexpr int TM = BM / 2, TN = BN / 2;      // wave tile (2 x 2 waves)
+  constexpr int MT = TM / 16, NT = TN / 16;    // 16x16 MFMA tiles per wave
+  constexpr int NH = NT / 2;                   // fragment columns of the first half k-step
+  constexpr int CH = 8;                        // 16-byte chunks per P row
+  constexpr int PROW = BK;                     // bytes per P row
+  constexpr int PG = BM * CH;                  // granules in a P slice
+  constexpr int QGR = BN / 16;                 // granules per Q row
+  constexpr int QG = BK * QGR;                 // granules in a Q slice
   constexpr int P_ROUNDS = PG / kThreads, Q_ROUNDS = QG / kThreads;
   constexpr int ROUNDS = P_ROUNDS + Q_ROUNDS;
-  constexpr int P_BYTES = PG * 16, STAGE = (PG + QG) * 16;
+  constexpr int P_BYTES = PG * 16, Q_BYTES = QG * 16;
+  constexpr int Q_BASE = NSP * P_BYTES;
   static_assert(PG % kThreads == 0 && QG % kThreads == 0, "slices must split over 256 lanes");
-  static_assert(NS * STAGE <= 163840, "LDS stages");
+  static_assert(NT % 2 == 0, "two half k-steps");
+  static_assert(NSP * P_BYTES + NSQ * Q_BYTES <= 163840, "LDS stages");
+  constexpr bool GELU = OUT == (int)OutKind::GeluBf16 || OUT == (int)OutKind::GeluE4m3;
 
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NSP * P_BYTES + NSQ * Q_BYTES];
 
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   int tm, tn;
   grouped_tile(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n, group_m, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
+
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 
+  const int ktiles = (K + BK - 1) / BK;
+  const int last = ktiles - 1;
+  const int k_last = last * BK;
+
+  // Per-lane byte offsets (from the slice's wave-uniform base) of the
+  // granules this lane copies; rows of P beyond M and columns of Q beyond N
+  // are clamped; with KTAIL the last slice's offsets are clamped into
+  // [k_last, K) (they only move down, so they stay non-negative).
   const uint8_t* p_base = P + (int64_t)m0 * ldp;
   const uint8_t* q_base = Q + n0;
   uint32_t p_off[P_ROUNDS], q_off[Q_ROUNDS];
-  int p_chunk[P_ROUNDS], q_row[Q_ROUNDS];
+  uint32_t p_off_t[KTAIL ? P_ROUNDS : 1], q_off_t[KTAIL ? Q_ROUNDS : 1];
 #pragma unroll
   for (int j = 0; j < P_ROUNDS; ++j) {
     const int pos = (j * 4 + wave) * 64 + lane;
     const int r = pos / CH, c = swz_p<CH>(r, pos % CH);
-    p_chunk[j] = c;
     p_off[j] = (uint32_t)((int64_t)(min(m0 + r, M - 1) - m0) * ldp + c * 16);
+    if constexpr (KTAIL) {
+      const int keep = min(c * 16, K - 16 - k_last);
+      p_off_t[j] = p_off[j] - (uint32_t)(c * 16 - keep);
+    }
   }
 #pragma unroll
   for (int j = 0; j < Q_ROUNDS; ++j) {
     const int pos = (j * 4 + wave) * 64 + lane;
     const int r = pos / QGR, gp = pos % QGR;
-    int g = 0;  // the granule stored at position gp of row r
-#pragma unroll
-    for (int c = 0; c < QGR; ++c)
-      if (rot_q8<QGR>(r, c) == gp) g = c;
-    q_row[j] = r;
+    const int g = (gp + QGR - q8_rot<QGR>(r)) % QGR;  // granule stored at position gp
     q_off[j] = (uint32_t)((int64_t)r * ldq + min(n0 + g * 16, N - 16) - n0);
+    if constexpr (KTAIL) {
+      const int keep = min(r, K - 1 - k_last);
+      q_off_t[j] = q_off[j] - (uint32_t)(r - keep) * (uint32_t)ldq;
+    }
   }
-
-  const int ktiles = (K + BK - 1) / BK;
-  const bool k_tail = (K % BK) != 0;
   const uint32_t lds0 = lds_addr(smem) + wave * 1024;
 
-  struct SliceDma {
-    const uint8_t* pb;
-    const uint8_t* qb;
-    uint32_t lp;
+  auto issue_p = [&](int kt, int pst, int j) __attribute__((always_inline)) {
+    uint32_t off = p_off[j];
+    if constexpr (KTAIL) off = kt == last ? p_off_t[j] : off;
+    dma16(p_base + (int64_t)kt * BK, off, lds0 + pst * P_BYTES + j * 4096);
   };
-  auto slice_dma = [&](int kt) {
-    SliceDma d;
-    d.pb = p_base + kt * BK;
-    d.qb = q_base + (int64_t)(kt * BK) * ldq;
-    d.lp = lds0 + (kt % NS) * STAGE;
-    return d;
+  auto issue_q = [&](int kt, int qst, int j) __attribute__((always_inline)) {
+    uint32_t off = q_off[j];
+    if constexpr (KTAIL) off = kt == last ? q_off_t[j] : off;
+    dma16(q_base + (int64_t)kt * BK * ldq, off, lds0 + Q_BASE + qst * Q_BYTES + j * 4096);
   };
-  auto issue_one = [&](const SliceDma& d, int j) {
-    if (j < P_ROUNDS) dma16(d.pb, p_off[j], d.lp + j * 4096);
-    else dma16(d.qb, q_off[j - P_ROUNDS], d.lp + P_BYTES + (j - P_ROUNDS) * 4096);
-  };
-  auto issue_slice = [&](int kt) {
-    const SliceDma d = slice_dma(kt);
-    if (!(k_tail && kt + 1 == ktiles)) {
-#pragma unroll
-      for (int j = 0; j < ROUNDS; ++j) issue_one(d, j);
-      return;
-    }
-    const int k0 = kt * BK;
-#pragma unroll
-    for (int j = 0; j < P_ROUNDS; ++j) {
-      const int cc = p_chunk[j] * 16, keep = min(cc, K - 16 - k0);
-      dma16(d.pb, p_off[j] - (uint32_t)(cc - keep), d.lp + j * 4096);
-    }
-#pragma unroll
-    for (int j = 0; j < Q_ROUNDS; ++j) {
-      const int r = q_row[j], keep = min(r, K - 1 - k0);
-      dma16(d.qb, q_off[j] - (uint32_t)(r - keep) * (uint32_t)ldq, d.lp + P_BYTES + j * 4096);
-    }
-  };
-  auto clear_tail = [&](int kt) {
-    uint8_t* sp = smem + (kt % NS) * STAGE;
-    uint8_t* sq = sp + P_BYTES;
-    const int kvalid = K - kt * BK;  // multiple of 16, in (0, BK)
+
+  // Clear the k >= K part of the last slice's stages (after its DMA landed).
+  auto clear_tail = [&]() {
+    uint8_t* sp = smem + (last % NSP) * P_BYTES;
+    uint8_t* sq = smem + Q_BASE + (last % NSQ) * Q_BYTES;
+    const int kvalid = K - k_last;  // multiple of 16, in (0, BK)
     const u32x4 z = {0u, 0u, 0u, 0u};
     for (int i = t; i < PG; i += kThreads) {
       const int r = i / CH, c = i % CH;
@@ -269,116 +277,136 @@ __global__ __launch_bounds__(kThreads) void gemm_e4m3_kernel(
   // Fragment addressing.
   int p_frag[MT];
 #pragma unroll
-  for (int mi = 0; mi < MT; ++mi) p_frag[mi] = wm * TM + mi * 32 + (lane & 31);
-  const int q_rsub = 32 * (lane >> 5) + ((lane & 15) >> 1);   // + 64s + 8q
-  const int q_byte = 8 * (lane & 1);
-  int q_gran[NT];
+  for (int mi = 0; mi < MT; ++mi) p_frag[mi] = wm * TM + mi * 16 + (lane & 15);
+  // Q fragment ni, read q: byte q_addr[ni] + 8q·BN of the Q stage. The row's
+  // rotation only depends on the lane (bits 0-2 and 5 of the row).
+  const int q_row0 = 32 * (lane >> 4) + ((lane & 15) >> 1);
+  int q_addr[NT];
 #pragma unroll
-  for (int ni = 0; ni < NT; ++ni) q_gran[ni] = (wn * TN + ni * 32 + 16 * ((lane >> 4) & 1)) >> 4;
+  for (int ni = 0; ni < NT; ++ni) {
+    const int gq = (wn * TN + ni * 16) >> 4;
+    q_addr[ni] = q_row0 * BN + ((gq + q8_rot<QGR>(q_row0)) % QGR) * 16 + 8 * (lane & 1);
+  }
 
-  i32x8 afr[2][NT], bfr[2][MT];
-  constexpr int NREADS = 2 * MT + 4 * NT;
-  // idx-th fragment read of k-step s of slice kt: first the 4 reads of A
-  // fragment 0, then the B fragments, then the other A fragments.
-  auto read_one = [&](int kt, int s, int buf, int idx) {
-    const uint8_t* sp = smem + (kt % NS) * STAGE;
-    const uint8_t* sq = sp + P_BYTES;
-    auto read_a = [&](int ni, int q) {
-      const int r = 64 * s + q_rsub + 8 * q;
-      const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-          (lds_i32x2*)(sq + r * BN + rot_q8<QGR>(r, q_gran[ni]) * 16 + q_byte));
-      if (q == 0) afr[buf][ni].s01 = v;
-      else if (q == 1) afr[buf][ni].s23 = v;
-      else if (q == 2) afr[buf][ni].s45 = v;
-      else afr[buf][ni].s67 = v;
-    };
-    if (idx < 4) {
-      read_a(0, idx);
-    } else if (idx < 4 + 2 * MT) {
-      const int mi = (idx - 4) / 2, half = (idx - 4) % 2, r = p_frag[mi];
-      const int chunk = 4 * s + 2 * (lane >> 5) + half;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(sp + r * PROW + swz_p<CH>(r, chunk) * 16);
-      const i32x4 vi = __builtin_bit_cast(i32x4, v);
-      if (half == 0) bfr[buf][mi].lo = vi; else bfr[buf][mi].hi = vi;
-    } else {
-      const int j = idx - 4 - 2 * MT;
-      read_a(1 + j / 4, j % 4);
-    }
+  // Both fragment sets are single-buffered: each fragment is reloaded for the
+  // next slice once its last MFMA of this slice has been issued.
+  i32x8 afr[NT];
+  i32x8 bfr[MT];
+  auto read_q = [&](int qst, int ni, int q) __attribute__((always_inline)) {
+    const uint8_t* sq = smem + Q_BASE + qst * Q_BYTES;
+    const i32x2 v = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+        (lds_i32x2*)(sq + q_addr[ni] + 8 * q * BN));
+    if (q == 0) afr[ni].s01 = v;
+    else if (q == 1) afr[ni].s23 = v;
+    else if (q == 2) afr[ni].s45 = v;
+    else afr[ni].s67 = v;
+  };
+  auto read_p = [&](int pst, int mi, int h) __attribute__((always_inline)) {
+    const uint8_t* sp = smem + pst * P_BYTES;
+    const int r = p_frag[mi];
+    const u32x4 v = *reinterpret_cast<const u32x4*>(
+        sp + r * PROW + swz_p<CH>(r, 2 * (lane >> 4) + h) * 16);
+    const i32x4 vi = __builtin_bit_cast(i32x4, v);
+    if (h == 0) bfr[mi].lo = vi; else bfr[mi].hi = vi;
   };
 
-  f32x16 acc[NT][MT];
+  f32x4 acc[NT][MT];
 #pragma unroll
   for (int ni = 0; ni < NT; ++ni)
 #pragma unroll
-    for (int mi = 0; mi < MT; ++mi)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[ni][mi][v] = 0.0f;
+    for (int mi = 0; mi < MT; ++mi) acc[ni][mi] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  constexpr int NMFMA = NT * MT;
-  auto kstep = [&](int cur, bool reads, int rkt, int rs, bool dma, const SliceDma& dd) {
+  constexpr int NMH = NH * MT;     // MFMAs per half k-step
+  constexpr int NRA = 4 * NH;      // Q-fragment reads per half
+  static_assert(NRA <= NMH && P_ROUNDS <= NMH && Q_ROUNDS <= NMH, "slots for reads and DMA");
+  // First half of slice kt: MFMAs of fragment columns ni < NH, ni-major; the
+  // reads of Q fragments ni >= NH of slice kt (stage rq), and the P part of
+  // slice dkt's DMA into P stage dst.
+  auto half0 = [&](int rq, int dkt, int dst) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < NMFMA; ++i) {
+    for (int i = 0; i < NMH; ++i) {
       const int ni = i / MT, mi = i % MT;
-      acc[ni][mi] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-          afr[cur][ni], bfr[cur][mi], acc[ni][mi], 0, 0, 0, 127, 0, 127);
-      if (reads) {
+      acc[ni][mi] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+          afr[ni], bfr[mi], acc[ni][mi], 0, 0, 0, 127, 0, 127);
 #pragma unroll
-        for (int j = 0; j < NREADS; ++j)
-          if ((NREADS <= NMFMA ? j : j * NMFMA / NREADS) == i) read_one(rkt, rs, cur ^ 1, j);
-      }
-      if (dma) {
+      for (int j = 0; j < NRA; ++j)
+        if (j * NMH / NRA == i) read_q(rq, NH + j / 4, j % 4);
 #pragma unroll
-        for (int j = 0; j < ROUNDS; ++j)
-          if ((ROUNDS <= NMFMA ? j : j * NMFMA / ROUNDS) == i) issue_one(dd, j);
+      for (int j = 0; j < P_ROUNDS; ++j)
+        if (j * NMH / P_ROUNDS == i) issue_p(dkt, dst, j);
+      SCHED_PIN();
+    }
+  };
+  // Second half: fragment columns ni >= NH, mi-major, so P fragment mi is
+  // dead after position mi·NH + NH − 1 and is reloaded there from the next
+  // slice (P stage rp); the Q fragments ni < NH of the next slice (stage rq)
+  // are read early in the half; the Q part of slice dkt's DMA goes into Q
+  // stage dst.
+  auto half1 = [&](int rp, int rq, int dkt, int dst) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NMH; ++i) {
+      const int mi = i / NH, ni = NH + i % NH;
+      acc[ni][mi] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+          afr[ni], bfr[mi], acc[ni][mi], 0, 0, 0, 127, 0, 127);
+      if (i % NH == NH - 1) {
+        read_p(rp, mi, 0);
+        read_p(rp, mi, 1);
       }
+#pragma unroll
+      for (int j = 0; j < NRA; ++j)
+        if (j * NMH / (2 * NRA) == i) read_q(rq, j / 4, j % 4);
+#pragma unroll
+      for (int j = 0; j < Q_ROUNDS; ++j)
+        if (j * NMH / Q_ROUNDS == i) issue_q(dkt, dst, j);
       SCHED_PIN();
     }
   };
 
-  const int pre = min(NS, ktiles);
-  for (int kt = 0; kt < pre; ++kt) issue_slice(kt);
-  wait_dma<ROUNDS, NS - 1>(pre - 1);
+  // Prologue: slices 0 and 1 (clamped to the last slice) into P stages 0, 1
+  // and Q stages 0, 1; wait for slice 0; read its P fragments and its
+  // first-half Q fragments.
+#pragma unroll
+  for (int j = 0; j < P_ROUNDS; ++j) issue_p(0, 0, j);
+#pragma unroll
+  for (int j = 0; j < Q_ROUNDS; ++j) issue_q(0, 0, j);
+#pragma unroll
+  for (int j = 0; j < P_ROUNDS; ++j) issue_p(min(1, last), 1, j);
+#pragma unroll
+  for (int j = 0; j < Q_ROUNDS; ++j) issue_q(min(1, last), 1, j);
+  waitcnt<ROUNDS, 0>();
   barrier();
-  if (k_tail && ktiles == 1) {
-    clear_tail(0);
-    waitcnt<0, 0>();
+  if (KTAIL && ktiles == 1) {
+    clear_tail();
+    waitcnt<63, 0>();
     barrier();
   }
 #pragma unroll
-  for (int i = 0; i < NREADS; ++i) read_one(0, 0, 0, i);
+  for (int mi = 0; mi < MT; ++mi) {
+    read_p(0, mi, 0);
+    read_p(0, mi, 1);
+  }
+#pragma unroll
+  for (int j = 0; j < NRA; ++j) read_q(0, j / 4, j % 4);
 
-  auto sync_next = [&](int kt) {
-    wait_dma<ROUNDS, NS - 2>(min(kt + NS, ktiles) - (kt + 2));
-    barrier();
-    if (k_tail && kt + 2 == ktiles) {
-      clear_tail(kt + 1);
-      waitcnt<0, 0>();
+  // Slice kt: Q stage kt & 1, P stage kt % 3.
+  for (int kt = 0; kt < ktiles; ++kt) {
+    const int qs = kt & 1;
+    const int ps1 = (kt + 1) % 3, ps2 = (kt + 2) % 3;
+    half0(qs, min(kt + 2, last), ps2);
+    waitcnt<P_ROUNDS, 0>();  // slice kt+1 has landed (only the P part of kt+2 may be in flight)
+    barrier();               // every wave is done reading the stages of slice kt
+    if (KTAIL && kt + 2 == ktiles) {
+      clear_tail();
+      waitcnt<63, 0>();
       barrier();
     }
-  };
-  const SliceDma none{};
-  const int steady_end = ktiles - NS - (k_tail ? 1 : 0);
-  int kt = 0;
-  for (; kt < steady_end; ++kt) {
-#pragma unroll
-    for (int s = 0; s + 1 < KS; ++s) kstep(s & 1, true, kt, s + 1, false, none);
-    sync_next(kt);
-    kstep((KS - 1) & 1, true, kt + 1, 0, true, slice_dma(kt + NS));
+    half1(ps1, qs ^ 1, min(kt + 2, last), qs);
   }
-  for (; kt < ktiles; ++kt) {
-#pragma unroll
-    for (int s = 0; s + 1 < KS; ++s) kstep(s & 1, true, kt, s + 1, false, none);
-    const bool more = kt + 1 < ktiles;
-    if (more) {
-      sync_next(kt);
-      if (kt + NS < ktiles) issue_slice(kt + NS);
-    }
-    kstep((KS - 1) & 1, more, kt + 1, 0, false, none);
-  }
+  waitcnt<0, 0>();  // no DMA may still write LDS when the workgroup ends
 
   // Epilogue: dequantise by 1/(sP·sQ); GeLU + bf16 + max|Z| (+ e4m3 with the
-  // given scale), or bf16.
-  constexpr bool GELU = OUT == (int)OutKind::GeluBf16 || OUT == (int)OutKind::GeluE4m3;
+  // given scale), or bf16. Lane holds, for 16x16 tile (ni, mi), C[m][n .. n+3]
+  // with m = mi·16 + (lane & 15), n = ni·16 + 4·(lane >> 4) (wave-tile relative).
   const float dq = 1.0f / (sP[0] * sQ[0]);
   const float sc = OUT == (int)OutKind::GeluE4m3 ? sC[0] : 1.0f;
   float zmax = 0.0f;
@@ -386,31 +414,28 @@ __global__ __launch_bounds__(kThreads) void gemm_e4m3_kernel(
   for (int ni = 0; ni < NT; ++ni) {
 #pragma unroll
     for (int mi = 0; mi < MT; ++mi) {
-      const int m = m0 + wm * TM + mi * 32 + (lane & 31);
-      if (m >= M) continue;
+      const int m = m0 + wm * TM + mi * 16 + (lane & 15);
+      const int n = n0 + wn * TN + ni * 16 + 4 * (lane >> 4);
+      if (m >= M || n >= N) continue;
+      f32x4 v = acc[ni][mi];
+      asm volatile("" : "+v"(v));
+      uint32_t bits[4];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int n = n0 + wn * TN + ni * 32 + 8 * g + 4 * (lane >> 5);
-        if (n >= N) continue;
-        uint32_t bits[4];
+      for (int e = 0; e < 4; ++e) {
+        const float x = v[e] * dq;
+        bits[e] = f32_to_bf16_rne(GELU ? gelu_exact(x) : x);
+        if (GELU) zmax = fmaxf(zmax, fabsf(bf16_bits_to_f32(bits[e])));
+      }
+      if constexpr (OUT == (int)OutKind::GeluE4m3) {
+        // the bf16 Z times the scale in fp32, clamped to ±448, one RNE rounding
+        float q[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float v = acc[ni][mi][4 * g + e] * dq;
-          const float z = GELU ? gelu_exact(v) : v;
-          bits[e] = f32_to_bf16_rne(z);
-          if (GELU) zmax = fmaxf(zmax, fabsf(bf16_bits_to_f32(bits[e])));
-        }
-        if constexpr (OUT == (int)OutKind::GeluE4m3) {
-          // the bf16 Z times the scale in fp32, clamped to ±448, one RNE rounding
-          float q[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) q[e] = clamp448(bf16_bits_to_f32(bits[e]) * sc);
-          const uint32_t o = cvt_e4m3x2(q[0], q[1]) | (cvt_e4m3x2(q[2], q[3]) << 16);
-          *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(C) + (int64_t)m * ldc + n) = o;
-        } else {
-          u32x2 o = {bits[0] | (bits[1] << 16), bits[2] | (bits[3] << 16)};
-          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(C) + (int64_t)m * ldc + n) = o;
-        }
+        for (int e = 0; e < 4; ++e) q[e] = clamp448(bf16_bits_to_f32(bits[e]) * sc);
+        const uint32_t o = cvt_e4m3x2(q[0], q[1]) | (cvt_e4m3x2(q[2], q[3]) << 16);
+        *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(C) + (int64_t)m * ldc + n) = o;
+      } else {
+        const u32x2 o = {bits[0] | (bits[1] << 16), bits[2] | (bits[3] << 16)};
+        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(C) + (int64_t)m * ldc + n) = o;
       }
     }
   }
@@ -422,25 +447,34 @@ __global__ __launch_bounds__(kThreads) void gemm_e4m3_kernel(
 
 }  // namespace e4
 
-template <int BM, int BN>
+template <int BM, int BN, bool KTAIL>
 hipError_t launch_cfg(const uint8_t* P, int64_t ldp, const float* sP, const uint8_t* Q,
                       int64_t ldq, const float* sQ, void* C, int64_t ldc, float* z_amax,
                       const float* sC, int M, int N, int K, OutKind out, hipStream_t stream) {
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   const int group_m = 4;
   if (out == OutKind::GeluBf16)
-    hipLaunchKernelGGL((e4::gemm_e4m3_kernel<BM, BN, (int)OutKind::GeluBf16>), dim3(tiles),
+    hipLaunchKernelGGL((e4::gemm_e4m3_kernel<BM, BN, (int)OutKind::GeluBf16, KTAIL>), dim3(tiles),
                        dim3(kThreads), 0, stream, P, ldp, sP, Q, ldq, sQ, C, ldc, z_amax, sC, M,
                        N, K, group_m);
   else if (out == OutKind::GeluE4m3)
-    hipLaunchKernelGGL((e4::gemm_e4m3_kernel<BM, BN, (int)OutKind::GeluE4m3>), dim3(tiles),
+    hipLaunchKernelGGL((e4::gemm_e4m3_kernel<BM, BN, (int)OutKind::GeluE4m3, KTAIL>), dim3(tiles),
                        dim3(kThreads), 0, stream, P, ldp, sP, Q, ldq, sQ, C, ldc, z_amax, sC, M,
                        N, K, group_m);
   else
-    hipLaunchKernelGGL((e4::gemm_e4m3_kernel<BM, BN, (int)OutKind::Bf16>), dim3(tiles),
+    hipLaunchKernelGGL((e4::gemm_e4m3_kernel<BM, BN, (int)OutKind::Bf16, KTAIL>), dim3(tiles),
                        dim3(kThreads), 0, stream, P, ldp, sP, Q, ldq, sQ, C, ldc, z_amax, sC, M,
                        N, K, group_m);
   return hipGetLastError();
+}
+
+template <int BM, int BN>
+hipError_t launch_tile(const uint8_t* P, int64_t ldp, const float* sP, const uint8_t* Q,
+                       int64_t ldq, const float* sQ, void* C, int64_t ldc, float* z_amax,
+                       const float* sC, int M, int N, int K, OutKind out, hipStream_t stream) {
+  if (K % e4::BK == 0)
+    return launch_cfg<BM, BN, false>(P, ldp, sP, Q, ldq, sQ, C, ldc, z_amax, sC, M, N, K, out, stream);
+  return launch_cfg<BM, BN, true>(P, ldp, sP, Q, ldq, sQ, C, ldc, z_amax, sC, M, N, K, out, stream);
 }
 
 int64_t grid_for(int64_t nvec) {
@@ -488,19 +522,22 @@ hipError_t launch_gemm_e4m3(const uint8_t* P, int64_t ldp, const float* sP, cons
   }
   if (M == 0 || N == 0) return hipSuccess;
   // Tile shape with the best estimated time: waves of 256 CUs times a
-  // per-tile cost that grows for smaller tiles. (A 256x256 e4m3 tile would
-  // need more than the 512 registers a lane has.)
-  static const struct { int bm, bn; double cost; } cands[] = {{256, 192, 1.00}, {128, 128, 0.38}};
+  // per-tile time relative to a 256x256 tile (smaller tiles reuse each LDS
+  // byte less, so their cost falls slower than their area).
+  static const struct { int bm, bn; double cost; } cands[] = {
+      {256, 256, 1.00}, {256, 192, 0.85}, {128, 128, 0.30}};
   double best = 1e300;
   int pick = 0;
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < 3; ++i) {
     const long tiles = (long)((M + cands[i].bm - 1) / cands[i].bm) * ((N + cands[i].bn - 1) / cands[i].bn);
     const double est = (double)((tiles + 255) / 256) * cands[i].cost;
     if (est < best - 1e-9) { best = est; pick = i; }
   }
   if (pick == 0)
-    return launch_cfg<256, 192>(P, ldp, sP, Q, ldq, sQ, C, ldc, z_amax, sC, M, N, K, out, stream);
-  return launch_cfg<128, 128>(P, ldp, sP, Q, ldq, sQ, C, ldc, z_amax, sC, M, N, K, out, stream);
+    return launch_tile<256, 256>(P, ldp, sP, Q, ldq, sQ, C, ldc, z_amax, sC, M, N, K, out, stream);
+  if (pick == 1)
+    return launch_tile<256, 192>(P, ldp, sP, Q, ldq, sQ, C, ldc, z_amax, sC, M, N, K, out, stream);
+  return launch_tile<128, 128>(P, ldp, sP, Q, ldq, sQ, C, ldc, z_amax, sC, M, N, K, out, stream);
 }
 
 }  // namespace tpmlp
