@@ -11,7 +11,9 @@ events on the stream it runs on.
 Default workload: 7b_tp8 - d = 4096, TP N = 8, X[8192x4096] (4 x 2048 tokens),
 A_i[4096x2048], B_i[2048x4096]; all 8 ranks then the sum. Other workloads:
 gpt2s_n1, 175b_tp8, 175b_tp8_e4m3 (fp8: col GEMM + GeLU + amax, requantise Z,
-row GEMM; inputs quantised once, outside the timed region).
+row GEMM; inputs quantised once, outside the timed region) and
+175b_tp8_e4m3_delayed (fp8 with delayed scaling of Z: col GEMM + GeLU + e4m3
+with the predicted scale + amax, row GEMM, amax history push).
 
 Prints one JSON line. `value` is TFLOP/s over the whole step (FLOPs =
 4·M·d·F per rank shard; GeLU, scaling and the sum are not counted).
@@ -81,7 +83,8 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="7b_tp8",
-                   help="7b_tp8 (default), gpt2s_n1, 175b_tp8, 175b_tp8_e4m3, or copy (a "
+                   help="7b_tp8 (default), gpt2s_n1, 175b_tp8, 175b_tp8_e4m3, 175b_tp8_e4m3_delayed, "
+                        "or copy (a "
                         "1-part tp_partial_sum over 256 MiB of fp32: the known-size copy that "
                         "calibrates rocprofv3's FETCH_SIZE / WRITE_SIZE)")
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the timed oracle leg")
@@ -171,6 +174,31 @@ def build_e4m3_step(tpm, wl):
     za = torch.empty(1, dtype=torch.float32, device="cuda")
     sZ = torch.empty(1, dtype=torch.float32, device="cuda")
     Y = torch.empty((M, d), dtype=torch.bfloat16, device="cuda")
+    kern_flops = {"col_gelu_e4m3": 2 * M * d * F, "row_partial_e4m3": 2 * M * d * F}
+    kern_bytes = {"col_gelu_e4m3": M * d + d * F + M * F * 2,
+                  "row_partial_e4m3": M * F + F * d + M * d * 2}
+
+    if "delayed" in wl.tags:
+        # delayed scaling of Z: the column GEMM quantises Z with the scale
+        # predicted from the amax history; the step ends by recording its amax
+        hist = tpm.AmaxHistory(1024, initial_scale=1.0)
+
+        def step(timer=None):
+            calls = [("col_gelu_e4m3_delayed",
+                      lambda: tpm.tp_mlp_col_gelu_e4m3_delayed(Xq, sX, Aq, sA, hist.scale, Zq, za)),
+                     ("row_partial_e4m3",
+                      lambda: tpm.tp_mlp_row_partial_e4m3(Zq, hist.scale, Bq, sB, Y)),
+                     ("amax_history_push", lambda: hist.push(za))]
+            for name, fn in calls:
+                if timer is None:
+                    fn()
+                else:
+                    timer.around(name, fn)
+
+        kern_flops = {"col_gelu_e4m3_delayed": 2 * M * d * F, "row_partial_e4m3": 2 * M * d * F}
+        kern_bytes = {"col_gelu_e4m3_delayed": M * d + d * F + M * F,
+                      "row_partial_e4m3": M * F + F * d + M * d * 2}
+        return step, kern_flops, kern_bytes, 0, (X, A, B), Y
 
     def step(timer=None):
         calls = [("col_gelu_e4m3", lambda: tpm.tp_mlp_col_gelu_e4m3(Xq, sX, Aq, sA, Z, za)),
@@ -182,9 +210,6 @@ def build_e4m3_step(tpm, wl):
             else:
                 timer.around(name, fn)
 
-    kern_flops = {"col_gelu_e4m3": 2 * M * d * F, "row_partial_e4m3": 2 * M * d * F}
-    kern_bytes = {"col_gelu_e4m3": M * d + d * F + M * F * 2,
-                  "row_partial_e4m3": M * F + F * d + M * d * 2}
     return step, kern_flops, kern_bytes, 0, (X, A, B), Y
 
 
@@ -202,7 +227,9 @@ def cpu_baseline(wl, inputs, budget_s):
     while done < wl.M and t_total < budget_s:
         rows = slice(done, min(wl.M, done + chunk))
         t0 = time.perf_counter()
-        if wl.fp8:
+        if wl.fp8 and "delayed" in wl.tags:
+            oracle.mlp_shard_e4m3_delayed(Xq[rows], sX, Aq, sA, Bq, sB, np.float32(1.0))
+        elif wl.fp8:
             oracle.mlp_shard_e4m3(Xq[rows], sX, Aq, sA, Bq, sB)
         else:
             parts = [oracle.mlp_shard(X[rows], A, B, wl.N, r) for r in range(wl.N)]

@@ -73,6 +73,12 @@ WORKLOADS = {
                               seed=3, fp8=True,
                               description="175b_tp8 shard quantised to e4m3, per-tensor "
                                           "scale 448/amax, bf16 output"),
+    # The same fp8 shard with delayed scaling of Z: Z quantised in the column
+    # GEMM's epilogue with the scale predicted from the recorded amaxes.
+    "175b_tp8_e4m3_delayed": Workload("175b_tp8_e4m3_delayed", M=2048, d=12288, H=6144, N=1,
+                                      sigma=0.006, seed=3, fp8=True, tags=("delayed",),
+                                      description="175b_tp8_e4m3 with delayed scaling of Z "
+                                                  "(amax history of 1024 steps)"),
 }
 
 
