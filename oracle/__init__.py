@@ -24,6 +24,10 @@ What it computes, and where the pages define it:
   ("Megatron-LM deep architecture", FP8 hybrid precision section), with the
   current scale (the tensor's own amax) or the delayed one (448 over the
   moving average of the amaxes recorded in earlier steps).
+* Backward of the shard: the chain rule through the forward as computed,
+  dZ = dY·B_iᵀ, dS = bf16(dZ ⊙ GeLU'(S)), dX_i = dS·A_iᵀ, dA_i = Xᵀ·dS,
+  dB_i = Z_iᵀ·dY; the ranks' dX_i sum to the input gradient (the backward
+  AllReduce).
 
 Everything is float64, on bfloat16 (or e4m3) inputs decoded exactly.  Z is
 rounded to bfloat16 once, after GeLU, which models the GPU's stored Z.
@@ -38,7 +42,8 @@ from .mlp import (shard_columns, gelu, col_gelu, row_partial, mlp_shard, partial
                   sp_rows, partial_sum_rows, reduce_scatter_share, mlp_unsharded, amax,
                   quant_scale, quant_e4m3, col_gelu_e4m3, requant_z, row_partial_e4m3,
                   mlp_shard_e4m3, quantize_inputs_e4m3, delayed_scale, amax_history_push,
-                  col_gelu_e4m3_delayed, mlp_shard_e4m3_delayed)
+                  col_gelu_e4m3_delayed, mlp_shard_e4m3_delayed, gelu_grad,
+                  mlp_shard_backward)
 
 __all__ = [
     "bf16_decode", "bf16_encode", "e4m3_decode", "e4m3_encode", "E4M3_MAX",
@@ -46,5 +51,5 @@ __all__ = [
     "sp_rows", "partial_sum_rows", "reduce_scatter_share", "mlp_unsharded", "amax",
     "quant_scale", "quant_e4m3", "col_gelu_e4m3", "requant_z", "row_partial_e4m3",
     "mlp_shard_e4m3", "quantize_inputs_e4m3", "delayed_scale", "amax_history_push",
-    "col_gelu_e4m3_delayed", "mlp_shard_e4m3_delayed",
+    "col_gelu_e4m3_delayed", "mlp_shard_e4m3_delayed", "gelu_grad", "mlp_shard_backward",
 ]

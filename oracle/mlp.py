@@ -264,3 +264,58 @@ def mlp_shard_e4m3_delayed(Xq, sX, Aq, sA, Bq, sB, sZ, N: int = 1, rank: int = 0
     Zq, za = col_gelu_e4m3_delayed(Xq, sX, Aq[:, lo:hi], sA, sZ)
     Y = row_partial_e4m3(Zq, sZ, Bq[lo:hi, :], sB)
     return Y, Zq, za
+
+
+# ----------------------------------------------------------------------------
+# Backward of one rank's shard.  The pages give only its communication: two
+# AllReduces in the backward pass ("Megatron-LM" glossary and "Megatron
+# architecture and 6D parallel guide", tensor-parallel communication): the
+# backward of the row-parallel sum hands every rank the same dY, and the
+# backward of the column-parallel (replicated) input sums the ranks' dX_i.
+# The formulas are the chain rule through the forward as computed: S_i = X·A_i,
+# Z_i = bf16(GeLU(S_i)), Y_i = Z_i·B_i.  S is recomputed (activation
+# recomputation); dS is rounded to bf16 once, because the next GEMMs take bf16
+# operands; dZ is never stored.
+# ----------------------------------------------------------------------------
+
+_INV_SQRT_2PI = 0.3989422804014327  # 1/√(2π)
+
+
+def gelu_grad(s: np.ndarray) -> np.ndarray:
+    """GeLU'(s) = Φ(s) + s·φ(s), φ(s) = e^(−s²/2)/√(2π), the derivative of s·Φ(s)."""
+    s = np.asarray(s, dtype=np.float64)
+    return 0.5 * erfc(-s * _INV_SQRT2) + s * _INV_SQRT_2PI * np.exp(-0.5 * s * s)
+
+
+def mlp_shard_backward(X_bits, A_bits, B_bits, dY_bits, N: int, rank: int, rounding: bool = True):
+    """Gradients of rank `rank`'s shard, given the block's output gradient dY.
+
+    Returns a dict of float64 arrays (dS and Z as bf16 bits when `rounding`):
+      S  = X·A_i                       [M, F]  (recomputed)
+      Z  = bf16(GeLU(S))               [M, F]  (the forward's stored Z)
+      dZ = dY·B_iᵀ                     [M, F]
+      dS = bf16(dZ ⊙ GeLU'(S))         [M, F]
+      dX = dS·A_iᵀ                     [M, d]  (this rank's part of the input gradient)
+      dA = Xᵀ·dS                       [d, F]  (the gradient of A_i, a column block of A's)
+      dB = Zᵀ·dY                       [F, d]  (the gradient of B_i, a row block of B's)
+    With rounding=False, Z and dS stay in float64 (the exact chain rule of the
+    unrounded forward, for checking the formulas against finite differences).
+    """
+    H = A_bits.shape[1]
+    lo, hi = shard_columns(H, N, rank)
+    X = bf16_decode(X_bits)
+    A_i = bf16_decode(A_bits)[:, lo:hi]
+    B_i = bf16_decode(B_bits)[lo:hi, :]
+    dY = bf16_decode(dY_bits)
+    S = X @ A_i
+    G = gelu(S)
+    dZ = dY @ B_i.T
+    dS = dZ * gelu_grad(S)
+    if rounding:
+        Z_bits, dS_bits = bf16_encode(G), bf16_encode(dS)
+        Z, dSv = bf16_decode(Z_bits), bf16_decode(dS_bits)
+    else:
+        Z_bits = dS_bits = None
+        Z, dSv = G, dS
+    return {"S": S, "Z": Z, "Z_bits": Z_bits, "dZ": dZ, "dS": dSv, "dS_bits": dS_bits,
+            "dX": dSv @ A_i.T, "dA": X.T @ dSv, "dB": Z.T @ dY}

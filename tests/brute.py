@@ -115,3 +115,30 @@ def fp8_shard_exact(Xq, sX, Aq, sA, Bq, sB, sZ_given=None):
     den2 = Fraction(float(sZ)) * Fraction(float(sB))
     Y = [[y / den2 for y in row] for row in Y]
     return Z, Zq, sZ, Y
+
+
+def gelu_grad_float(x: float) -> float:
+    """GeLU'(x) = Φ(x) + x·φ(x) with Python's math.erfc and math.exp."""
+    return 0.5 * math.erfc(-x / math.sqrt(2.0)) + x * math.exp(-0.5 * x * x) / math.sqrt(2.0 * math.pi)
+
+
+def shard_backward_exact(X_bits, A_bits, B_bits, dY_bits, N, rank):
+    """Exact backward of one rank's shard: (Z, dS on the bf16 grid, dX, dA, dB)
+    with every GEMM an exact rational sum."""
+    H = A_bits.shape[1]
+    F = H // N
+    lo = rank * F
+    X = [[bf16_value(v) for v in row] for row in X_bits.tolist()]
+    A = [[bf16_value(v) for v in row[lo:lo + F]] for row in A_bits.tolist()]
+    B = [[bf16_value(v) for v in row] for row in B_bits.tolist()[lo:lo + F]]
+    dY = [[bf16_value(v) for v in row] for row in dY_bits.tolist()]
+    S = matmul_exact(X, A)
+    Bt = [list(col) for col in zip(*B)]
+    dZ = matmul_exact(dY, Bt)
+    Z = [[bf16_round(Fraction(gelu_float(float(s)))) for s in row] for row in S]
+    dS = [[bf16_round(Fraction(float(dz) * gelu_grad_float(float(s)))) for dz, s in zip(rz, rs)]
+          for rz, rs in zip(dZ, S)]
+    At = [list(col) for col in zip(*A)]
+    Xt = [list(col) for col in zip(*X)]
+    Zt = [list(col) for col in zip(*Z)]
+    return Z, dS, matmul_exact(dS, At), matmul_exact(Xt, dS), matmul_exact(Zt, dY)

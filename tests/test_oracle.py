@@ -345,6 +345,80 @@ def test_delayed_path_matches_brute_force_with_a_predicted_scale(factor):
         assert np.max(np.abs(oracle.e4m3_decode(Zq))) == 448.0
 
 
+# ------------------------------------------------------------- backward ----
+
+def test_gelu_grad_identities_and_numerical_derivative():
+    assert oracle.gelu_grad(np.array([0.0]))[0] == 0.5
+    x = np.linspace(-8, 8, 4001)
+    g = oracle.gelu_grad(x)
+    # GeLU(x) − GeLU(−x) = x, so GeLU'(x) + GeLU'(−x) = 1
+    assert np.max(np.abs(g + oracle.gelu_grad(-x) - 1.0)) <= 2e-15
+    h = 1e-5
+    num = (omlp.gelu(x + h) - omlp.gelu(x - h)) / (2 * h)
+    assert np.max(np.abs(num - g)) <= 1e-9
+    assert abs(oracle.gelu_grad(np.array([10.0]))[0] - 1.0) < 1e-20
+    assert -1e-20 < oracle.gelu_grad(np.array([-10.0]))[0] < 0
+
+
+def _dy(M, d, seed):
+    rng = np.random.default_rng(seed)
+    return bf16_bits_from_f32(rng.standard_normal((M, d)).astype(np.float32))
+
+
+@pytest.mark.parametrize("N,rank", [(1, 0), (2, 1), (4, 2)])
+def test_backward_formulas_match_finite_differences(N, rank):
+    # the exact chain rule of the unrounded forward against central finite
+    # differences of L = Σ Y ⊙ dY, Y = GeLU(X·A_i)·B_i, in float64
+    M, d, H = 3, 4, 16
+    X, A, B = make_random(M, d, H, 60 + N, sigma=0.5)
+    dY = _dy(M, d, 61)
+    g = oracle.mlp_shard_backward(X, A, B, dY, N, rank, rounding=False)
+    lo, hi = omlp.shard_columns(H, N, rank)
+    Xv, Av, Bv, dYv = (oracle.bf16_decode(t) for t in (X, A[:, lo:hi], B[lo:hi, :], dY))
+
+    def loss(x, a, b):
+        return float(np.sum((omlp.gelu(x @ a) @ b) * dYv))
+    h = 1e-6
+    for name, base, grad in (("X", Xv, g["dX"]), ("A", Av, g["dA"]), ("B", Bv, g["dB"])):
+        num = np.zeros_like(base)
+        for idx in np.ndindex(base.shape):
+            p, m = base.copy(), base.copy()
+            p[idx] += h
+            m[idx] -= h
+            args_p = {"X": (p, Av, Bv), "A": (Xv, p, Bv), "B": (Xv, Av, p)}[name]
+            args_m = {"X": (m, Av, Bv), "A": (Xv, m, Bv), "B": (Xv, Av, m)}[name]
+            num[idx] = (loss(*args_p) - loss(*args_m)) / (2 * h)
+        assert grad.shape == base.shape
+        assert _rel_maxdiff(grad, num) <= 1e-6, name
+
+
+@pytest.mark.parametrize("M,d,H,N,rank,seed", [(4, 8, 16, 2, 0, 62), (3, 16, 32, 4, 3, 63)])
+def test_backward_matches_brute_force(M, d, H, N, rank, seed):
+    X, A, B = make_random(M, d, H, seed, sigma=0.3)
+    dY = _dy(M, d, seed + 1)
+    g = oracle.mlp_shard_backward(X, A, B, dY, N, rank)
+    Z, dS, dX, dA, dB = brute.shard_backward_exact(X, A, B, dY, N, rank)
+    as_f = lambda T: np.array([[float(v) for v in r] for r in T])
+    assert np.array_equal(g["Z"], as_f(Z))
+    assert np.array_equal(g["dS"], as_f(dS))
+    assert _rel_maxdiff(g["dX"], as_f(dX)) <= 1e-13
+    assert _rel_maxdiff(g["dA"], as_f(dA)) <= 1e-13
+    assert _rel_maxdiff(g["dB"], as_f(dB)) <= 1e-13
+
+
+def test_backward_shards_compose_to_the_unsharded_gradients():
+    # the ranks' dX_i sum to the unsharded dX (the backward AllReduce); the
+    # weight gradients are the column blocks of dA and the row blocks of dB
+    M, d, H, N = 24, 32, 128, 4
+    X, A, B = make_random(M, d, H, 64, sigma=0.1)
+    dY = _dy(M, d, 65)
+    full = oracle.mlp_shard_backward(X, A, B, dY, 1, 0)
+    parts = [oracle.mlp_shard_backward(X, A, B, dY, N, r) for r in range(N)]
+    assert _rel_maxdiff(oracle.partial_sum([p["dX"] for p in parts]), full["dX"]) <= 1e-12
+    assert _rel_maxdiff(np.concatenate([p["dA"] for p in parts], axis=1), full["dA"]) <= 1e-12
+    assert _rel_maxdiff(np.concatenate([p["dB"] for p in parts], axis=0), full["dB"]) <= 1e-12
+
+
 def test_workload_table_shapes():
     wl = WORKLOADS["7b_tp8"]
     assert (wl.M, wl.d, wl.F) == (8192, 4096, 2048) and wl.H == 4 * wl.d

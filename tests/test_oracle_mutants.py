@@ -185,3 +185,69 @@ def test_delayed_quantising_unrounded_z_is_caught(monkeypatch):
         return ocodecs.e4m3_encode(v.astype(np.float64)), float(np.max(np.abs(Zf)))
     monkeypatch.setattr(omlp, "col_gelu_e4m3_delayed", col)
     assert _pins_fail(DELAYED_PINS)
+
+
+BACKWARD_PINS = [
+    pins.test_gelu_grad_identities_and_numerical_derivative,
+    lambda: pins.test_backward_formulas_match_finite_differences(2, 1),
+    lambda: pins.test_backward_matches_brute_force(4, 8, 16, 2, 0, 62),
+    pins.test_backward_shards_compose_to_the_unsharded_gradients,
+]
+
+
+def test_gelu_grad_without_the_density_term_is_caught(monkeypatch):
+    monkeypatch.setattr(omlp, "gelu_grad", lambda s: 0.5 * erfc(-np.asarray(s, np.float64) * omlp._INV_SQRT2))
+    monkeypatch.setattr(oracle, "gelu_grad", omlp.gelu_grad)
+    assert _pins_fail(BACKWARD_PINS)
+
+
+def test_gelu_grad_sign_flip_is_caught(monkeypatch):
+    def g(s):
+        s = np.asarray(s, np.float64)
+        return 0.5 * erfc(-s * omlp._INV_SQRT2) - s * omlp._INV_SQRT_2PI * np.exp(-0.5 * s * s)
+    monkeypatch.setattr(omlp, "gelu_grad", g)
+    monkeypatch.setattr(oracle, "gelu_grad", g)
+    assert _pins_fail(BACKWARD_PINS)
+
+
+def _backward_variant(change):
+    real = omlp.mlp_shard_backward
+
+    def bw(X, A, B, dY, N, rank, rounding=True):
+        out = dict(real(X, A, B, dY, N, rank, rounding))
+        change(out, X, A, B, dY, N, rank)
+        return out
+    return bw
+
+
+def test_backward_weight_gradient_from_unrounded_gelu_is_caught(monkeypatch):
+    def change(out, X, A, B, dY, N, rank):
+        out["dB"] = omlp.gelu(out["S"]).T @ ocodecs.bf16_decode(dY)
+    bw = _backward_variant(change)
+    monkeypatch.setattr(omlp, "mlp_shard_backward", bw)
+    monkeypatch.setattr(oracle, "mlp_shard_backward", bw)
+    assert _pins_fail(BACKWARD_PINS)
+
+
+def test_backward_input_gradient_from_dz_instead_of_ds_is_caught(monkeypatch):
+    def change(out, X, A, B, dY, N, rank):
+        lo, hi = omlp.shard_columns(A.shape[1], N, rank)
+        out["dX"] = out["dZ"] @ ocodecs.bf16_decode(A)[:, lo:hi].T
+    bw = _backward_variant(change)
+    monkeypatch.setattr(omlp, "mlp_shard_backward", bw)
+    monkeypatch.setattr(oracle, "mlp_shard_backward", bw)
+    assert _pins_fail(BACKWARD_PINS)
+
+
+def test_backward_untransposed_weight_is_caught(monkeypatch):
+    def change(out, X, A, B, dY, N, rank):
+        lo, hi = omlp.shard_columns(A.shape[1], N, rank)
+        Bi = ocodecs.bf16_decode(B)[lo:hi, :]
+        if Bi.shape[0] == Bi.shape[1]:
+            dZ = ocodecs.bf16_decode(dY) @ Bi
+            out["dS"] = ocodecs.bf16_decode(ocodecs.bf16_encode(dZ * omlp.gelu_grad(out["S"])))
+            out["dX"] = out["dS"] @ ocodecs.bf16_decode(A)[:, lo:hi].T
+    bw = _backward_variant(change)
+    monkeypatch.setattr(omlp, "mlp_shard_backward", bw)
+    monkeypatch.setattr(oracle, "mlp_shard_backward", bw)
+    assert _pins_fail(BACKWARD_PINS)
