@@ -13,10 +13,14 @@ A_i[4096x2048], B_i[2048x4096]; all 8 ranks then the sum. Other workloads:
 gpt2s_n1, 175b_tp8, 175b_tp8_e4m3 (fp8: col GEMM + GeLU + amax, requantise Z,
 row GEMM; inputs quantised once, outside the timed region) and
 175b_tp8_e4m3_delayed (fp8 with delayed scaling of Z: col GEMM + GeLU + e4m3
-with the predicted scale + amax, row GEMM, amax history push).
+with the predicted scale + amax, row GEMM, amax history push) and 7b_tp8_bwd
+(the backward of every rank's 7b_tp8 shard for an output gradient dY: one
+tp_mlp_shard_backward call per rank, five GEMMs, then the sum of the ranks'
+input gradients dX_i).
 
 Prints one JSON line. `value` is TFLOP/s over the whole step (FLOPs =
-4·M·d·F per rank shard; GeLU, scaling and the sum are not counted).
+4·M·d·F per rank shard forward, 10·M·d·F backward; GeLU, GeLU', scaling and
+the sum are not counted).
 """
 import argparse
 import hashlib
@@ -84,6 +88,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="7b_tp8",
                    help="7b_tp8 (default), gpt2s_n1, 175b_tp8, 175b_tp8_e4m3, 175b_tp8_e4m3_delayed, "
+                        "7b_tp8_bwd, "
                         "or copy (a "
                         "1-part tp_partial_sum over 256 MiB of fp32: the known-size copy that "
                         "calibrates rocprofv3's FETCH_SIZE / WRITE_SIZE)")
@@ -158,6 +163,45 @@ def build_bf16_step(tpm, wl, partial_dtype):
     return step, kern_flops, kern_bytes, psum_bytes, (X, A, B), out
 
 
+def build_bwd_step(tpm, wl):
+    """Backward of every rank's shard: one tp_mlp_shard_backward call per rank
+    (S recomputed, dS with GeLU', dX_i, dB_i, dA_i), then Σ_i dX_i."""
+    import torch
+    from workloads import make_inputs, make_output_grad
+    X, A, B = make_inputs(wl)
+    dY = make_output_grad(wl.M, wl.d, wl.seed, wl.grad_sigma)
+    Xd, Ad, Bd, dYd = dev_bf16(X), dev_bf16(A), dev_bf16(B), dev_bf16(dY)
+    M, d, H, N, F = wl.M, wl.d, wl.H, wl.N, wl.F
+    ws = torch.empty(tpm.tp_mlp_shard_backward_workspace_size(M, d, H, N), dtype=torch.uint8,
+                     device="cuda")
+    dXs = [torch.empty((M, d), dtype=torch.float32, device="cuda") for _ in range(N)]
+    dA = torch.empty((d, F), dtype=torch.float32, device="cuda")
+    dB = torch.empty((F, d), dtype=torch.float32, device="cuda")
+    dX = torch.empty((M, d), dtype=torch.float32, device="cuda")
+
+    def step(timer=None):
+        for r in range(N):
+            def call(r=r):
+                tpm.tp_mlp_shard_backward(Xd, Ad, Bd, dYd, N, r, dX_i=dXs[r], dA_i=dA, dB_i=dB,
+                                          workspace=ws)
+            if timer is None:
+                call()
+            else:
+                timer.around("shard_backward", call)
+        if N > 1:
+            if timer is None:
+                tpm.tp_partial_sum(dXs, Y=dX)
+            else:
+                timer.around("partial_sum", lambda: tpm.tp_partial_sum(dXs, Y=dX))
+
+    kern_flops = {"shard_backward": 10 * M * d * F}
+    # algorithmic bytes of one call: X, dY, A_i, B_i read once; dX_i, dA_i,
+    # dB_i written once (the S, dS, Z intermediates are not counted)
+    kern_bytes = {"shard_backward": (2 * M * d + 2 * d * F) * 2 + (M * d + 2 * d * F) * 4}
+    psum_bytes = (N + 1) * 4 * M * d
+    return step, kern_flops, kern_bytes, psum_bytes, (X, A, B, dY), (dX if N > 1 else dXs[0])
+
+
 def build_e4m3_step(tpm, wl):
     import torch
     X, A, B = __import__("workloads").make_inputs(wl)
@@ -216,7 +260,7 @@ def build_e4m3_step(tpm, wl):
 def cpu_baseline(wl, inputs, budget_s):
     """Time the oracle as it stands on row chunks of the same step until the budget is spent."""
     import oracle
-    X, A, B = inputs
+    X, A, B = inputs[:3]
     chunk = max(1, min(wl.M, 1024))
     if wl.fp8:   # input quantisation is preparation (outside the GPU's timed step too)
         Xq, sX = oracle.quantize_inputs_e4m3(X)
@@ -227,7 +271,12 @@ def cpu_baseline(wl, inputs, budget_s):
     while done < wl.M and t_total < budget_s:
         rows = slice(done, min(wl.M, done + chunk))
         t0 = time.perf_counter()
-        if wl.fp8 and "delayed" in wl.tags:
+        if wl.backward:   # every row costs the five GEMMs' 10·d·F flops per rank
+            parts = [oracle.mlp_shard_backward(X[rows], A, B, inputs[3][rows], wl.N, r)["dX"]
+                     for r in range(wl.N)]
+            if wl.N > 1:
+                oracle.partial_sum(parts)
+        elif wl.fp8 and "delayed" in wl.tags:
             oracle.mlp_shard_e4m3_delayed(Xq[rows], sX, Aq, sA, Bq, sB, np.float32(1.0))
         elif wl.fp8:
             oracle.mlp_shard_e4m3(Xq[rows], sX, Aq, sA, Bq, sB)
@@ -237,7 +286,7 @@ def cpu_baseline(wl, inputs, budget_s):
                 oracle.partial_sum(parts)
         t_total += time.perf_counter() - t0
         done = rows.stop
-    flops = wl.N * 4 * done * wl.d * wl.F
+    flops = wl.N * (10 if wl.backward else 4) * done * wl.d * wl.F
     what = (f"rows [0, {done}) of {wl.M} of the {wl.name} step"
             + (f" (all {wl.N} ranks + partial sum)" if wl.N > 1 else "")
             + f", float64 numpy/OpenBLAS oracle, {t_total:.2f} s")
@@ -249,12 +298,14 @@ def sampled_check(wl, inputs, out, nrows=8):
     import torch
     import oracle
     from workloads import sample_rows
-    X, A, B = inputs
+    X, A, B = inputs[:3]
     rows = sample_rows(wl.M, nrows)
     got = out[torch.from_numpy(rows).cuda()].double().cpu().numpy()
     if wl.fp8:
         return None
-    if wl.N > 1:
+    if wl.backward:   # Σ_i dX_i is the unsharded block's input gradient
+        ref = oracle.mlp_shard_backward(X[rows], A, B, inputs[3][rows], 1, 0)["dX"]
+    elif wl.N > 1:
         ref = oracle.mlp_unsharded(X[rows], A, B)
     else:
         ref = oracle.mlp_shard(X[rows], A, B, 1, 0)
@@ -302,6 +353,8 @@ def main():
     log(f"bench: workload {wl.name}: {wl.description}")
     if wl.fp8:
         step, kern_flops, kern_bytes, psum_bytes, inputs, out = build_e4m3_step(tpm, wl)
+    elif wl.backward:
+        step, kern_flops, kern_bytes, psum_bytes, inputs, out = build_bwd_step(tpm, wl)
     else:
         step, kern_flops, kern_bytes, psum_bytes, inputs, out = build_bf16_step(
             tpm, wl, args.partial_dtype)
@@ -359,7 +412,8 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
         "data": "synthetic: seeded X~N(0,1), weights~N(0,sigma^2), bf16 (no trained weights)",
         "config": {"workload": wl.name, "M": wl.M, "d": wl.d, "F": wl.F, "tp_ranks": wl.N,
-                   "partial_dtype": "bf16" if wl.fp8 else args.partial_dtype,
+                   "partial_dtype": "bf16" if wl.fp8 else ("f32" if wl.backward
+                                                            else args.partial_dtype),
                    "parallelism": f"tp{wl.N} ranks sequentially on 1 GPU" if wl.N > 1 else "none"},
         "pct_of_peak": round(100 * value / peak, 2),
         "roofline": roofline,

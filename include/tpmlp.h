@@ -280,6 +280,42 @@ int tp_mlp_shard_e4m3_delayed(const void* Xq, const float* sX, const void* Aq, c
                               float* z_amax, int64_t M, int64_t d, int64_t H, int N, int rank,
                               void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Bytes of device workspace tp_mlp_shard_backward needs: S (fp32 [M, F]),
+ * dS and Z (bf16 [M, F] each), each 256-byte aligned. 0 for invalid sizes.
+ */
+size_t tp_mlp_shard_backward_workspace_size(int64_t M, int64_t d, int64_t H, int N);
+
+/*
+ * Backward of one rank's shard: the chain rule through Y_i = GeLU(X·A_i)·B_i
+ * for the output gradient dY. The pages give the backward's communication
+ * only ("Megatron-LM" glossary and "Megatron architecture and 6D parallel
+ * guide", tensor-parallel communication: AllReduces in the backward pass):
+ * every rank receives the same dY because the forward ends in a sum, and the
+ * ranks' input gradients dX_i are summed because X is replicated. The
+ * arithmetic is the chain rule through the forward as computed. With
+ * F = H / N and the shard views of tp_mlp_shard:
+ *   S    = X·A_i                     recomputed in fp32 (the forward keeps only Z)
+ *   dS   = bf16((dY·B_iᵀ) ⊙ GeLU'(S)), GeLU'(x) = Φ(x) + x·φ(x)
+ *   Z    = bf16(GeLU(S))             (bit-identical to the forward's Z_i)
+ *   dX_i = dS·A_iᵀ                   this rank's part of the input gradient
+ *   dA_i = Xᵀ·dS                     gradient of the column block A_i
+ *   dB_i = Z ᵀ·dY                    gradient of the row block B_i
+ * all accumulated in fp32. The input gradient is Σ_i dX_i (tp_partial_sum).
+ * X, dY : device, bf16 [M, d]. A : device, bf16 [d, H]. B : device, bf16 [H, d].
+ * dX_i : device, fp32 [M, d]. dA_i : device, fp32 [d, F]. dB_i : device, fp32 [F, d].
+ *   All dense; overwritten; no output may overlap an input, another output
+ *   or the workspace.
+ * M must be a multiple of 8 (it is the contraction length of dA_i and dB_i).
+ * workspace : device, at least tp_mlp_shard_backward_workspace_size(M, d, H, N)
+ *   bytes, 16-byte aligned; on return it holds S, dS, Z in that order, each
+ *   at a 256-byte-rounded offset.
+ */
+int tp_mlp_shard_backward(const void* X, const void* A, const void* B, const void* dY,
+                          float* dX_i, float* dA_i, float* dB_i, int64_t M, int64_t d,
+                          int64_t H, int N, int rank, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
 #ifdef __cplusplus
 }
 #endif

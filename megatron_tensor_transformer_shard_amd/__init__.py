@@ -26,6 +26,7 @@ __all__ = [
     "tp_mlp_row_partial_e4m3", "tp_mlp_shard_e4m3", "tp_mlp_shard_e4m3_workspace_size",
     "tp_amax_history_push", "tp_mlp_col_gelu_e4m3_delayed", "tp_mlp_shard_e4m3_delayed",
     "tp_mlp_shard_e4m3_delayed_workspace_size", "AmaxHistory",
+    "tp_mlp_shard_backward", "tp_mlp_shard_backward_workspace_size", "backward_workspace_views",
     "TPM_BF16", "TPM_F32", "TPM_E4M3", "EXPORTED_SYMBOLS",
 ]
 
@@ -61,6 +62,9 @@ _SIGNATURES = {
     "tp_mlp_shard_e4m3_delayed_workspace_size": (_sz, [_i64, _i64, _i64, _int]),
     "tp_mlp_shard_e4m3_delayed": (_int, [_vp, _fp, _vp, _fp, _vp, _fp, _fp, _vp, _fp, _i64, _i64,
                                          _i64, _int, _int, _vp, _sz, _vp]),
+    "tp_mlp_shard_backward_workspace_size": (_sz, [_i64, _i64, _i64, _int]),
+    "tp_mlp_shard_backward": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int,
+                                     _int, _vp, _sz, _vp]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGNATURES)
 
@@ -440,3 +444,64 @@ def tp_mlp_shard_e4m3_delayed(Xq, sX, Aq, sA, Bq, sB, sZ, N: int, rank: int, Y_i
                                          workspace.numel() * workspace.element_size(),
                                          _stream(stream)), "tp_mlp_shard_e4m3_delayed")
     return Y_i, z_amax
+
+
+def tp_mlp_shard_backward_workspace_size(M: int, d: int, H: int, N: int) -> int:
+    return int(lib.tp_mlp_shard_backward_workspace_size(M, d, H, N))
+
+
+def tp_mlp_shard_backward(X, A, B, dY, N: int, rank: int, dX_i=None, dA_i=None, dB_i=None,
+                          workspace=None, stream=None):
+    """Gradients of rank `rank`'s shard for the output gradient dY.
+
+    Returns (dX_i, dA_i, dB_i, workspace): fp32 [M, d], [d, F], [F, d]; the
+    workspace (uint8) holds S (fp32), dS and Z (bf16), [M, F] each, at the
+    offsets `backward_workspace_views` gives.
+    """
+    _need(X, "X", torch.bfloat16, 2)
+    _need(A, "A", torch.bfloat16, 2)
+    _need(B, "B", torch.bfloat16, 2)
+    _need(dY, "dY", torch.bfloat16, 2)
+    M, d = X.shape
+    dA, H = A.shape
+    if dA != d or tuple(B.shape) != (H, d) or tuple(dY.shape) != (M, d):
+        raise ValueError(f"shape mismatch: X {tuple(X.shape)}, A {tuple(A.shape)}, "
+                         f"B {tuple(B.shape)}, dY {tuple(dY.shape)}")
+    if N < 1 or H % N != 0:
+        raise ValueError("H must be divisible by N")
+    F = H // N
+    dev = X.device
+    if dX_i is None:
+        dX_i = torch.empty((M, d), dtype=torch.float32, device=dev)
+    if dA_i is None:
+        dA_i = torch.empty((d, F), dtype=torch.float32, device=dev)
+    if dB_i is None:
+        dB_i = torch.empty((F, d), dtype=torch.float32, device=dev)
+    for t, name, shp in ((dX_i, "dX_i", (M, d)), (dA_i, "dA_i", (d, F)), (dB_i, "dB_i", (F, d))):
+        _need(t, name, torch.float32, 2)
+        if tuple(t.shape) != shp:
+            raise ValueError(f"{name} has the wrong shape")
+    need = tp_mlp_shard_backward_workspace_size(M, d, H, N)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", None)
+    _check(lib.tp_mlp_shard_backward(X.data_ptr(), A.data_ptr(), B.data_ptr(), dY.data_ptr(),
+                                     dX_i.data_ptr(), dA_i.data_ptr(), dB_i.data_ptr(), M, d, H,
+                                     N, rank, workspace.data_ptr(),
+                                     workspace.numel() * workspace.element_size(),
+                                     _stream(stream)),
+           "tp_mlp_shard_backward")
+    return dX_i, dA_i, dB_i, workspace
+
+
+def backward_workspace_views(workspace, M: int, F: int):
+    """(S fp32, dS bf16, Z bf16) views, [M, F] each, of a backward workspace."""
+    def r256(b):
+        return (b + 255) // 256 * 256
+    mf = M * F
+    o1 = r256(4 * mf)
+    o2 = o1 + r256(2 * mf)
+    S = workspace[: 4 * mf].view(torch.float32).view(M, F)
+    dS = workspace[o1: o1 + 2 * mf].view(torch.bfloat16).view(M, F)
+    Z = workspace[o2: o2 + 2 * mf].view(torch.bfloat16).view(M, F)
+    return S, dS, Z

@@ -430,4 +430,78 @@ int tp_mlp_shard_e4m3_delayed(const void* Xq, const float* sX, const void* Aq, c
   return status_of(e);
 }
 
+size_t tp_mlp_shard_backward_workspace_size(int64_t M, int64_t d, int64_t H, int N) {
+  if (M < 0 || d <= 0 || H <= 0 || N < 1 || H % N != 0) return 0;
+  if (M > kMaxDim || H > kMaxDim) return 0;
+  const size_t mf = (size_t)M * (size_t)(H / N);
+  return round256(mf * 4) + 2 * round256(mf * 2);
+}
+
+int tp_mlp_shard_backward(const void* X, const void* A, const void* B, const void* dY,
+                          float* dX_i, float* dA_i, float* dB_i, int64_t M, int64_t d, int64_t H,
+                          int N, int rank, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  if (N < 1 || rank < 0 || rank >= N) return TPM_ERR_ARG;
+  if (H <= 0 || H % N != 0) return TPM_ERR_SHAPE;
+  const int64_t F = H / N;
+  int st = check_dims(M, d, F, 8);
+  if (st != TPM_OK) return st;
+  // M is the contraction length of the weight gradients.
+  if (M % 8 != 0 || M > kMaxLd) return TPM_ERR_SHAPE;
+  if (H > kMaxLd || H * d > (int64_t(1) << 46)) return TPM_ERR_SHAPE;
+  if (M == 0) return TPM_OK;
+  if (!X || !A || !B || !dY || !dX_i || !dA_i || !dB_i) return TPM_ERR_NULL;
+  const size_t need = tp_mlp_shard_backward_workspace_size(M, d, H, N);
+  if (!workspace || workspace_bytes < need) return TPM_ERR_WORKSPACE;
+  if (!aligned16(X) || !aligned16(A) || !aligned16(B) || !aligned16(dY) || !aligned16(dX_i) ||
+      !aligned16(dA_i) || !aligned16(dB_i) || !aligned16(workspace))
+    return TPM_ERR_ALIGN;
+  const Span ins[4] = {mat_span(X, M, d, d, 2), mat_span(A, d, H, H, 2), mat_span(B, H, d, d, 2),
+                       mat_span(dY, M, d, d, 2)};
+  const Span outs[4] = {mat_span(dX_i, M, d, d, 4), mat_span(dA_i, d, F, F, 4),
+                        mat_span(dB_i, F, d, d, 4),
+                        {reinterpret_cast<uintptr_t>(workspace),
+                         reinterpret_cast<uintptr_t>(workspace) + need}};
+  for (int o = 0; o < 4; ++o) {
+    for (int i = 0; i < 4; ++i)
+      if (overlap(outs[o], ins[i])) return TPM_ERR_ALIAS;
+    for (int p = o + 1; p < 4; ++p)
+      if (overlap(outs[o], outs[p])) return TPM_ERR_ALIAS;
+  }
+
+  // Shard views as in the forward; A_i is [d, F] with row stride H, B_i [F, d] dense.
+  const uint16_t* x = static_cast<const uint16_t*>(X);
+  const uint16_t* dy = static_cast<const uint16_t*>(dY);
+  const uint16_t* A_i = static_cast<const uint16_t*>(A) + (int64_t)rank * F;
+  const uint16_t* B_i = static_cast<const uint16_t*>(B) + (int64_t)rank * F * d;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  const size_t mf = (size_t)M * (size_t)F;
+  float* S = reinterpret_cast<float*>(ws);
+  uint16_t* dS = reinterpret_cast<uint16_t*>(ws + round256(mf * 4));
+  uint16_t* Z = reinterpret_cast<uint16_t*>(ws + round256(mf * 4) + round256(mf * 2));
+  hipStream_t s = as_stream(stream);
+  using tpmlp::Layout;
+  const int m = (int)M, dd = (int)d, f = (int)F;
+  // S = X·A_i (the forward's pre-activation, recomputed)
+  hipError_t e = tpmlp::launch_gemm_bf16_ex(x, d, A_i, H, S, F, m, f, dd, OutKind::F32,
+                                            Layout::NN, nullptr, 0, nullptr, s);
+  // dS = bf16((dY·B_iᵀ) ⊙ GeLU'(S)), Z = bf16(GeLU(S)); B_iᵀ is B_i read K-contiguous
+  if (e == hipSuccess)
+    e = tpmlp::launch_gemm_bf16_ex(dy, d, B_i, d, dS, F, m, f, dd, OutKind::GeluGradBf16,
+                                   Layout::QT, S, F, Z, s);
+  // dX_i = dS·A_iᵀ
+  if (e == hipSuccess)
+    e = tpmlp::launch_gemm_bf16_ex(dS, F, A_i, H, dX_i, d, m, dd, f, OutKind::F32, Layout::QT,
+                                   nullptr, 0, nullptr, s);
+  // dB_i = Zᵀ·dY ([F, d], contraction over the M tokens)
+  if (e == hipSuccess)
+    e = tpmlp::launch_gemm_bf16_ex(Z, F, dy, d, dB_i, d, f, dd, m, OutKind::F32, Layout::PT,
+                                   nullptr, 0, nullptr, s);
+  // dA_i = Xᵀ·dS ([d, F])
+  if (e == hipSuccess)
+    e = tpmlp::launch_gemm_bf16_ex(x, d, dS, F, dA_i, F, dd, f, m, OutKind::F32, Layout::PT,
+                                   nullptr, 0, nullptr, s);
+  return status_of(e);
+}
+
 }  // extern "C"

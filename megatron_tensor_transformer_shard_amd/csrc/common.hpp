@@ -59,6 +59,24 @@ __device__ __forceinline__ float gelu_exact(float x) {
   return fmaf(-ax, h, fmaxf(x, 0.0f));
 }
 
+// GeLU(x) and GeLU'(x) = Φ(x) + x·φ(x) together, φ(x) = e^(−x²/2)/√(2π), with
+// the same erfc evaluation as gelu_exact: h = Φ(−|x|), Φ(x) = 1 − h for x >= 0
+// and h for x < 0. The GeLU'(x) error is that of Φ (below 1e-7) plus fp32
+// rounding.
+__device__ __forceinline__ void gelu_and_grad(float x, float& g, float& dg) {
+  const float ax = fabsf(x);
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f * 0.70710678118654752f, ax, 1.0f));
+  float p = fmaf(t, 0.5f * 1.061405429f, 0.5f * -1.453152027f);
+  p = fmaf(t, p, 0.5f * 1.421413741f);
+  p = fmaf(t, p, 0.5f * -0.284496736f);
+  p = fmaf(t, p, 0.5f * 0.254829592f);
+  const float e = __builtin_amdgcn_exp2f((x * -0.72134752044448170f) * x);  // e^(−x²/2)
+  const float h = (t * p) * e;                                              // Φ(−|x|)
+  g = fmaf(-ax, h, fmaxf(x, 0.0f));
+  const float phi = x >= 0.0f ? 1.0f - h : h;
+  dg = fmaf(x, e * 0.39894228040143268f, phi);
+}
+
 // Consecutive workgroup ids are dispatched round-robin over the 8 XCDs of
 // an MI355X, each of which has its own L2. Renumber so that a run of
 // nblocks/8 consecutive logical ids executes on one XCD; tiles that share

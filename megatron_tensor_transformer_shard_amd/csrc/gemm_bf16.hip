@@ -45,6 +45,17 @@
 //    part of its LDS stage is cleared after it lands.
 //  - Workgroup ids are remapped so the tiles of one XCD share P and Q panels
 //    in that XCD's L2.
+//
+// The backward of the shard needs the other two operand layouts: Q stored
+// K-contiguous ([N, K], QT: the transposed weights of dZ = dY·B_iᵀ and
+// dX_i = dS·A_iᵀ) and P stored M-contiguous ([K, M], PT: the transposed
+// activations of dB_i = Z_iᵀ·dY and dA_i = Xᵀ·dS). Each operand is either
+// "K-major" (LDS rows are its m or n index, 128-byte K-contiguous rows,
+// fragments by one ds_read_b128, as P above) or "MN-major" (LDS rows are k,
+// fragments by two ds_read_b64_tr_b16, as Q above); an MFMA operand fragment
+// has the same register layout either way (index lane & 15, k group lane >> 4).
+// The GeluGradBf16 epilogue of the backward reads the recomputed S (fp32) and
+// writes dS = bf16(acc·GeLU'(S)) and Z = bf16(GeLU(S)).
 #include "common.hpp"
 #include "kernels.hpp"
 #include "tile_engine.hpp"
@@ -75,25 +86,122 @@ __device__ __forceinline__ int q_rot(int row) {
   else return 2 * ((row >> 1) & 1) + 4 * ((row >> 3) & 1);
 }
 
-template <int BM, int BN, int OUT, bool KTAIL>
+// One operand's slice in LDS and its DMA, tail clearing and fragment reads.
+// W = tile width of the operand (BM for P, BN for Q); KMAJ: LDS rows are the
+// operand's m/n index (128-byte K-contiguous rows), else rows are k (W
+// elements each). A stage is W·128 bytes either way.
+template <int W, bool KMAJ, bool KTAIL>
+struct Operand {
+  static constexpr int BK = kBK;
+  static constexpr int CH = BK / 8;         // 16-byte chunks per K-major row
+  static constexpr int GR = W / 8;          // granules per MN-major row
+  static constexpr int G = W * CH;          // granules in a slice
+  static constexpr int ROUNDS = G / kThreads;
+  static constexpr int BYTES = G * 16;
+  static constexpr int READS = KMAJ ? 1 : 2;  // LDS instructions per fragment
+  static_assert(G % kThreads == 0, "slices must split over 256 lanes");
+  static_assert(KMAJ || GR % 8 == 0, "MN-major rows must hold a multiple of 8 granules");
+
+  const uint16_t* base;
+  int64_t ld;
+  uint32_t off[ROUNDS];
+  uint32_t off_t[KTAIL ? ROUNDS : 1];
+
+  // x0: first m/n of the tile, X: extent of that index; K, k_last: as in the kernel.
+  __device__ __forceinline__ void init(const uint16_t* ptr, int64_t ld_, int x0, int X, int K,
+                                       int k_last, int wave, int lane) {
+    ld = ld_;
+    base = KMAJ ? ptr + (int64_t)x0 * ld : ptr + x0;
+#pragma unroll
+    for (int j = 0; j < ROUNDS; ++j) {
+      const int pos = (j * 4 + wave) * 64 + lane;
+      if constexpr (KMAJ) {
+        const int r = pos / CH, c = swz_p<CH>(r, pos % CH);
+        off[j] = (uint32_t)(((int64_t)(min(x0 + r, X - 1) - x0) * ld + c * 8) * 2);
+        if constexpr (KTAIL) {
+          const int keep = min(c * 8, K - 8 - k_last);
+          off_t[j] = off[j] - 2u * (uint32_t)(c * 8 - keep);
+        }
+      } else {
+        const int r = pos / GR, gp = pos % GR;
+        const int g = (gp + GR - q_rot<GR>(r)) % GR;  // granule stored at position gp
+        off[j] = (uint32_t)(((int64_t)r * ld + min(x0 + g * 8, X - 8) - x0) * 2);
+        if constexpr (KTAIL) {
+          const int keep = min(r, K - 1 - k_last);
+          off_t[j] = off[j] - 2u * (uint32_t)(r - keep) * (uint32_t)ld;
+        }
+      }
+    }
+  }
+  // DMA instruction j of slice kt into the stage at LDS byte address `stage`
+  // (+ the wave's 1 KB lane block, already in `stage`).
+  __device__ __forceinline__ void issue(int kt, int last, uint32_t stage, int j) const {
+    uint32_t o = off[j];
+    if constexpr (KTAIL) o = kt == last ? off_t[j] : o;
+    const uint16_t* b = KMAJ ? base + (int64_t)kt * BK : base + (int64_t)kt * BK * ld;
+    dma16(b, o, stage + j * 4096);
+  }
+  // Zero the k >= kvalid part of a stage.
+  __device__ __forceinline__ void clear(uint8_t* sp, int kvalid, int t) const {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    for (int i = t; i < G; i += kThreads) {
+      if constexpr (KMAJ) {
+        const int r = i / CH, c = i % CH;
+        if (c * 8 >= kvalid) *reinterpret_cast<u32x4*>(sp + r * (BK * 2) + swz_p<CH>(r, c) * 16) = z;
+      } else {
+        if (i / GR >= kvalid) *reinterpret_cast<u32x4*>(sp + i * 16) = z;
+      }
+    }
+  }
+};
+
+// Lane-dependent part of a fragment's LDS address for fragment rows/columns
+// fb .. fb+15 (wave-tile relative): K-major, the LDS row this lane reads;
+// MN-major, the byte offset of its first 8-byte piece at k-step 0.
+template <int W, bool KMAJ>
+__device__ __forceinline__ int frag_addr(int fb, int lane) {
+  if constexpr (KMAJ) {
+    return fb + (lane & 15);
+  } else {
+    constexpr int GR = W / 8;
+    // every k-row a lane reads is 32s + 4h + rsub, whose rotation (bits 0, 1
+    // and 3 of the row) equals that of rsub
+    const int rsub = 8 * (lane >> 4) + ((lane & 15) >> 2);
+    return rsub * (2 * W) + ((((fb + 4 * (lane & 3)) >> 3) + q_rot<GR>(rsub)) % GR) * 16 +
+           8 * (lane & 1);
+  }
+}
+
+// Piece h (of Operand::READS) of the fragment at `fa` (from frag_addr) for
+// k-step s of stage sp: K-major, one ds_read_b128 of chunk 4s + (lane >> 4);
+// MN-major, k-rows 32s + 4h + rsub by a transposing read.
+template <int W, bool KMAJ>
+__device__ __forceinline__ void read_frag(const uint8_t* sp, int fa, int s, int h, int lane,
+                                          s16x8& f) {
+  if constexpr (KMAJ) {
+    f = *reinterpret_cast<const s16x8*>(sp + fa * (kBK * 2) +
+                                        swz_p<kBK / 8>(fa, 4 * s + (lane >> 4)) * 16);
+  } else {
+    const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_s16x4*)(sp + fa + (32 * s + 4 * h) * (2 * W)));
+    if (h == 0) f.lo = v; else f.hi = v;
+  }
+}
+
+template <int BM, int BN, int OUT, bool KTAIL, bool PT, bool QT>
 __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
     const uint16_t* __restrict__ P, int64_t ldp, const uint16_t* __restrict__ Q, int64_t ldq,
-    void* __restrict__ C, int64_t ldc, int M, int N, int K, int group_m) {
+    void* __restrict__ C, int64_t ldc, const float* __restrict__ aux, int64_t ldaux,
+    void* __restrict__ C2, int M, int N, int K, int group_m) {
   constexpr int BK = kBK, NSP = kNSP, NSQ = kNSQ;
   constexpr int TM = BM / 2, TN = BN / 2;      // wave tile (2 x 2 waves)
   constexpr int MT = TM / 16, NT = TN / 16;    // 16x16 MFMA tiles per wave
-  constexpr int CH = BK / 8;                   // 16-byte chunks per P row
-  constexpr int PROW = BK * 2;                 // bytes per P row
-  constexpr int PG = BM * CH;                  // granules in a P slice
-  constexpr int QGR = BN / 8;                  // granules per Q row
-  constexpr int QG = BK * QGR;                 // granules in a Q slice
-  constexpr int P_ROUNDS = PG / kThreads, Q_ROUNDS = QG / kThreads;
+  using OpP = Operand<BM, !PT, KTAIL>;
+  using OpQ = Operand<BN, QT, KTAIL>;
+  constexpr int P_ROUNDS = OpP::ROUNDS, Q_ROUNDS = OpQ::ROUNDS;
   constexpr int ROUNDS = P_ROUNDS + Q_ROUNDS;  // DMA instructions per wave per slice
-  constexpr int P_BYTES = PG * 16, Q_BYTES = QG * 16;  // one stage of each operand
-  constexpr int Q_BASE = NSP * P_BYTES;                // Q stages follow the P stages
-  static_assert(CH == 8, "P rows are 128 bytes");
-  static_assert(PG % kThreads == 0 && QG % kThreads == 0, "slices must split over 256 lanes");
-  static_assert(QGR % 8 == 0, "Q rows must hold a multiple of 8 granules");
+  constexpr int P_BYTES = OpP::BYTES, Q_BYTES = OpQ::BYTES;  // one stage of each operand
+  constexpr int Q_BASE = NSP * P_BYTES;                      // Q stages follow the P stages
   static_assert(NSP * P_BYTES + NSQ * Q_BYTES <= 163840, "LDS stages");
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NSP * P_BYTES + NSQ * Q_BYTES];
@@ -112,101 +220,53 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
   const int last = ktiles - 1;
   const int k_last = last * BK;  // first k of the last slice
 
-  // Per-lane byte offsets (from the slice's wave-uniform base) of the
-  // granules this lane copies; rows of P beyond M and columns of Q beyond N
-  // are clamped. With KTAIL the last slice uses offsets clamped into
-  // [k_last, K); they only ever move down, so they stay non-negative.
-  const uint16_t* p_base = P + (int64_t)m0 * ldp;
-  const uint16_t* q_base = Q + n0;
-  uint32_t p_off[P_ROUNDS], q_off[Q_ROUNDS];
-  uint32_t p_off_t[KTAIL ? P_ROUNDS : 1], q_off_t[KTAIL ? Q_ROUNDS : 1];
-#pragma unroll
-  for (int j = 0; j < P_ROUNDS; ++j) {
-    const int pos = (j * 4 + wave) * 64 + lane;
-    const int r = pos / CH, c = swz_p<CH>(r, pos % CH);
-    p_off[j] = (uint32_t)(((int64_t)(min(m0 + r, M - 1) - m0) * ldp + c * 8) * 2);
-    if constexpr (KTAIL) {
-      const int keep = min(c * 8, K - 8 - k_last);
-      p_off_t[j] = p_off[j] - 2u * (uint32_t)(c * 8 - keep);
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < Q_ROUNDS; ++j) {
-    const int pos = (j * 4 + wave) * 64 + lane;
-    const int r = pos / QGR, gp = pos % QGR;
-    const int g = (gp + QGR - q_rot<QGR>(r)) % QGR;  // granule stored at position gp
-    q_off[j] = (uint32_t)(((int64_t)r * ldq + min(n0 + g * 8, N - 8) - n0) * 2);
-    if constexpr (KTAIL) {
-      const int keep = min(r, K - 1 - k_last);
-      q_off_t[j] = q_off[j] - 2u * (uint32_t)(r - keep) * (uint32_t)ldq;
-    }
-  }
+  // Per-lane byte offsets of the granules this lane copies; rows/columns
+  // beyond M or N are clamped, and with KTAIL the last slice's k is clamped
+  // into [k_last, K) (the offsets only move down, so they stay non-negative).
+  OpP op_p;
+  OpQ op_q;
+  op_p.init(P, ldp, m0, M, K, k_last, wave, lane);
+  op_q.init(Q, ldq, n0, N, K, k_last, wave, lane);
   const uint32_t lds0 = lds_addr(smem) + wave * 1024;
 
-  // DMA instruction j of the P (Q) part of slice kt into P stage pst (Q stage qst).
   auto issue_p = [&](int kt, int pst, int j) __attribute__((always_inline)) {
-    uint32_t off = p_off[j];
-    if constexpr (KTAIL) off = kt == last ? p_off_t[j] : off;
-    dma16(p_base + kt * BK, off, lds0 + pst * P_BYTES + j * 4096);
+    op_p.issue(kt, last, lds0 + pst * P_BYTES, j);
   };
   auto issue_q = [&](int kt, int qst, int j) __attribute__((always_inline)) {
-    uint32_t off = q_off[j];
-    if constexpr (KTAIL) off = kt == last ? q_off_t[j] : off;
-    dma16(q_base + (int64_t)(kt * BK) * ldq, off, lds0 + Q_BASE + qst * Q_BYTES + j * 4096);
+    op_q.issue(kt, last, lds0 + Q_BASE + qst * Q_BYTES, j);
   };
-
   // Clear the k >= K part of the last slice's stages (after its DMA landed).
   auto clear_tail = [&]() {
-    uint8_t* sp = smem + (last % NSP) * P_BYTES;
-    uint8_t* sq = smem + Q_BASE + (last % NSQ) * Q_BYTES;
-    const int kvalid = K - k_last;  // multiple of 8, in (0, BK)
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    for (int i = t; i < PG; i += kThreads) {
-      const int r = i / CH, c = i % CH;
-      if (c * 8 >= kvalid) *reinterpret_cast<u32x4*>(sp + r * PROW + swz_p<CH>(r, c) * 16) = z;
-    }
-    for (int i = t; i < QG; i += kThreads) {
-      if (i / QGR >= kvalid) *reinterpret_cast<u32x4*>(sq + i * 16) = z;
-    }
+    op_p.clear(smem + (last % NSP) * P_BYTES, K - k_last, t);
+    op_q.clear(smem + Q_BASE + (last % NSQ) * Q_BYTES, K - k_last, t);
   };
 
   // Fragment addressing (k-step s covers k 32s .. 32s+31 of the slice; lane
   // group g = lane >> 4 holds k 8g .. 8g+7 of its row or column).
-  int p_frag[MT];
+  int p_addr[MT], q_addr[NT];
 #pragma unroll
-  for (int mi = 0; mi < MT; ++mi) p_frag[mi] = wm * TM + mi * 16 + (lane & 15);
-  // Every k-row a lane reads is 32s + 4h + q_rsub, whose rotation (bits 0,
-  // 1 and 3 of the row) equals that of q_rsub.
-  const int q_rsub = 8 * (lane >> 4) + ((lane & 15) >> 2);
-  int q_pos[NT];
+  for (int mi = 0; mi < MT; ++mi) p_addr[mi] = frag_addr<BM, !PT>(wm * TM + mi * 16, lane);
 #pragma unroll
-  for (int ni = 0; ni < NT; ++ni)
-    q_pos[ni] = ((((wn * TN + ni * 16 + 4 * (lane & 3)) >> 3) + q_rot<QGR>(q_rsub)) % QGR) * 16 +
-                8 * (lane & 1);
+  for (int ni = 0; ni < NT; ++ni) q_addr[ni] = frag_addr<BN, QT>(wn * TN + ni * 16, lane);
 
-  s16x8 afr[2][NT];
-  bf16x8 bfr[2][MT];
-  constexpr int NREADS = MT + 2 * NT;
-  // idx-th fragment read of k-step s of the slice in `stage` into buffer
-  // buf; ordered so that the next k-step's first MFMAs (A fragment 0 with
-  // every B fragment) find their operands first.
+  s16x8 afr[2][NT];  // Q fragments (MFMA A operand)
+  s16x8 bfr[2][MT];  // P fragments (MFMA B operand)
+  constexpr int RQ = OpQ::READS, RP = OpP::READS;
+  constexpr int NREADS = NT * RQ + MT * RP;
+  // idx-th fragment read of k-step s of the slice in stages (pst, qst) into
+  // buffer buf; ordered so that the next k-step's first MFMAs (Q fragment 0
+  // with every P fragment) find their operands first.
   auto read_one = [&](int pst, int qst, int s, int buf, int idx) __attribute__((always_inline)) {
     const uint8_t* sp = smem + pst * P_BYTES;
     const uint8_t* sq = smem + Q_BASE + qst * Q_BYTES;
-    const int r0 = 32 * s + q_rsub;
-    if (idx < 2) {
-      const uint8_t* a = sq + (r0 + 4 * idx) * (2 * BN) + q_pos[0];
-      const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)a);
-      if (idx == 0) afr[buf][0].lo = v; else afr[buf][0].hi = v;
-    } else if (idx < 2 + MT) {
-      const int mi = idx - 2, r = p_frag[mi];
-      bfr[buf][mi] = *reinterpret_cast<const bf16x8*>(
-          sp + r * PROW + swz_p<CH>(r, 4 * s + (lane >> 4)) * 16);
+    if (idx < RQ) {
+      read_frag<BN, QT>(sq, q_addr[0], s, idx, lane, afr[buf][0]);
+    } else if (idx < RQ + MT * RP) {
+      const int j = idx - RQ, mi = j / RP;
+      read_frag<BM, !PT>(sp, p_addr[mi], s, j % RP, lane, bfr[buf][mi]);
     } else {
-      const int ni = 1 + (idx - 2 - MT) / 2, h = (idx - 2 - MT) % 2;
-      const uint8_t* a = sq + (r0 + 4 * h) * (2 * BN) + q_pos[ni];
-      const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)a);
-      if (h == 0) afr[buf][ni].lo = v; else afr[buf][ni].hi = v;
+      const int j = idx - RQ - MT * RP, ni = 1 + j / RQ;
+      read_frag<BN, QT>(sq, q_addr[ni], s, j % RQ, lane, afr[buf][ni]);
     }
   };
 
@@ -219,30 +279,30 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
   // One k-step: the NT x MT MFMAs on buffer `cur`, each followed by its
   // share of the fragment reads for the next k-step (P stage rp, Q stage rq,
   // k-step rs, into cur ^ 1) and of the DMA instructions of one operand of
-  // slice dkt (the P part into P stage dst when DQ is false, else the Q
+  // slice dkt (the P part into P stage dst when dq is false, else the Q
   // part into Q stage dst).
   constexpr int NMFMA = NT * MT;
   static_assert(NREADS <= NMFMA && P_ROUNDS <= NMFMA && Q_ROUNDS <= NMFMA,
                 "one MFMA slot per read and DMA");
   auto kstep = [&](int cur, int rp, int rq, int rs, bool dq, int dkt, int dst)
                    __attribute__((always_inline)) {
-    constexpr int NDMA_P = P_ROUNDS, NDMA_Q = Q_ROUNDS;
 #pragma unroll
     for (int i = 0; i < NMFMA; ++i) {
       const int ni = i / MT, mi = i % MT;
       acc[ni][mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-          __builtin_bit_cast(bf16x8, afr[cur][ni]), bfr[cur][mi], acc[ni][mi], 0, 0, 0);
+          __builtin_bit_cast(bf16x8, afr[cur][ni]), __builtin_bit_cast(bf16x8, bfr[cur][mi]),
+          acc[ni][mi], 0, 0, 0);
 #pragma unroll
       for (int j = 0; j < NREADS; ++j)
         if (j * NMFMA / NREADS == i) read_one(rp, rq, rs, cur ^ 1, j);
       if (!dq) {
 #pragma unroll
-        for (int j = 0; j < NDMA_P; ++j)
-          if (j * NMFMA / NDMA_P == i) issue_p(dkt, dst, j);
+        for (int j = 0; j < P_ROUNDS; ++j)
+          if (j * NMFMA / P_ROUNDS == i) issue_p(dkt, dst, j);
       } else {
 #pragma unroll
-        for (int j = 0; j < NDMA_Q; ++j)
-          if (j * NMFMA / NDMA_Q == i) issue_q(dkt, dst, j);
+        for (int j = 0; j < Q_ROUNDS; ++j)
+          if (j * NMFMA / Q_ROUNDS == i) issue_q(dkt, dst, j);
       }
       SCHED_PIN();
     }
@@ -312,6 +372,17 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
         const u32x2 o = {pack_bf16x2(gelu_exact(v[0]), gelu_exact(v[1])),
                          pack_bf16x2(gelu_exact(v[2]), gelu_exact(v[3]))};
         *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(C) + (int64_t)m * ldc + n) = o;
+      } else if constexpr (OUT == (int)OutKind::GeluGradBf16) {
+        // dS = bf16(dZ·GeLU'(S)) into C, Z = bf16(GeLU(S)) into C2
+        const f32x4 sv = *reinterpret_cast<const f32x4*>(aux + (int64_t)m * ldaux + n);
+        float g[4], dg[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) gelu_and_grad(sv[e], g[e], dg[e]);
+        const u32x2 o = {pack_bf16x2(v[0] * dg[0], v[1] * dg[1]),
+                         pack_bf16x2(v[2] * dg[2], v[3] * dg[3])};
+        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(C) + (int64_t)m * ldc + n) = o;
+        const u32x2 z = {pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3])};
+        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(C2) + (int64_t)m * ldc + n) = z;
       } else {
         const u32x2 o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
         *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(C) + (int64_t)m * ldc + n) = o;
@@ -320,33 +391,49 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
   }
 }
 
-template <int BM, int BN, bool KTAIL>
-hipError_t launch_cfg(const uint16_t* P, int64_t ldp, const uint16_t* Q, int64_t ldq, void* C,
-                      int64_t ldc, int M, int N, int K, OutKind out, hipStream_t stream) {
-  const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+struct GemmArgs {
+  const uint16_t* P; int64_t ldp; const uint16_t* Q; int64_t ldq; void* C; int64_t ldc;
+  const float* aux; int64_t ldaux; void* C2; int M, N, K;
+};
+
+template <int BM, int BN, int OUT, bool KTAIL, bool PT, bool QT>
+hipError_t launch_one(const GemmArgs& a, hipStream_t stream) {
+  const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   const int group_m = 4;
-  switch (out) {
-    case OutKind::GeluBf16:
-      hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, (int)OutKind::GeluBf16, KTAIL>), dim3(tiles),
-                         dim3(kThreads), 0, stream, P, ldp, Q, ldq, C, ldc, M, N, K, group_m);
-      break;
-    case OutKind::F32:
-      hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, (int)OutKind::F32, KTAIL>), dim3(tiles),
-                         dim3(kThreads), 0, stream, P, ldp, Q, ldq, C, ldc, M, N, K, group_m);
-      break;
-    case OutKind::Bf16:
-      hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, (int)OutKind::Bf16, KTAIL>), dim3(tiles),
-                         dim3(kThreads), 0, stream, P, ldp, Q, ldq, C, ldc, M, N, K, group_m);
-      break;
-  }
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, OUT, KTAIL, PT, QT>), dim3(tiles), dim3(kThreads), 0,
+                     stream, a.P, a.ldp, a.Q, a.ldq, a.C, a.ldc, a.aux, a.ldaux, a.C2, a.M, a.N,
+                     a.K, group_m);
   return hipGetLastError();
 }
 
+// The (layout, epilogue) combinations the path uses: the forward's
+// K-major P / N-major Q with GeLU, fp32 or bf16 output; K-major Q with the
+// GeLU-gradient or fp32 epilogue; M-major P with fp32 output.
+template <int BM, int BN, bool KTAIL>
+hipError_t launch_cfg(const GemmArgs& a, OutKind out, Layout lay, hipStream_t stream) {
+  if (lay == Layout::NN) {
+    switch (out) {
+      case OutKind::GeluBf16: return launch_one<BM, BN, (int)OutKind::GeluBf16, KTAIL, false, false>(a, stream);
+      case OutKind::F32: return launch_one<BM, BN, (int)OutKind::F32, KTAIL, false, false>(a, stream);
+      case OutKind::Bf16: return launch_one<BM, BN, (int)OutKind::Bf16, KTAIL, false, false>(a, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  if (lay == Layout::QT) {
+    switch (out) {
+      case OutKind::GeluGradBf16: return launch_one<BM, BN, (int)OutKind::GeluGradBf16, KTAIL, false, true>(a, stream);
+      case OutKind::F32: return launch_one<BM, BN, (int)OutKind::F32, KTAIL, false, true>(a, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  if (out == OutKind::F32) return launch_one<BM, BN, (int)OutKind::F32, KTAIL, true, false>(a, stream);
+  return hipErrorInvalidValue;
+}
+
 template <int BM, int BN>
-hipError_t launch_tile(const uint16_t* P, int64_t ldp, const uint16_t* Q, int64_t ldq, void* C,
-                       int64_t ldc, int M, int N, int K, OutKind out, hipStream_t stream) {
-  if (K % kBK == 0) return launch_cfg<BM, BN, false>(P, ldp, Q, ldq, C, ldc, M, N, K, out, stream);
-  return launch_cfg<BM, BN, true>(P, ldp, Q, ldq, C, ldc, M, N, K, out, stream);
+hipError_t launch_tile(const GemmArgs& a, OutKind out, Layout lay, hipStream_t stream) {
+  if (a.K % kBK == 0) return launch_cfg<BM, BN, false>(a, out, lay, stream);
+  return launch_cfg<BM, BN, true>(a, out, lay, stream);
 }
 
 struct TileChoice { int bm, bn; };
@@ -372,15 +459,23 @@ TileChoice choose_tile(int M, int N) {
 
 }  // namespace
 
+hipError_t launch_gemm_bf16_ex(const uint16_t* P, int64_t ldp, const uint16_t* Q, int64_t ldq,
+                               void* C, int64_t ldc, int M, int N, int K, OutKind out, Layout lay,
+                               const float* aux, int64_t ldaux, void* C2, hipStream_t stream) {
+  if (M == 0 || N == 0) return hipSuccess;
+  const GemmArgs a{P, ldp, Q, ldq, C, ldc, aux, ldaux, C2, M, N, K};
+  const TileChoice tc = choose_tile(M, N);
+  if (tc.bm == 256 && tc.bn == 256) return launch_tile<256, 256>(a, out, lay, stream);
+  if (tc.bm == 256 && tc.bn == 192) return launch_tile<256, 192>(a, out, lay, stream);
+  if (tc.bm == 256 && tc.bn == 128) return launch_tile<256, 128>(a, out, lay, stream);
+  return launch_tile<128, 128>(a, out, lay, stream);
+}
+
 hipError_t launch_gemm_bf16(const uint16_t* P, int64_t ldp, const uint16_t* Q, int64_t ldq,
                             void* C, int64_t ldc, int M, int N, int K, OutKind out,
                             hipStream_t stream) {
-  if (M == 0 || N == 0) return hipSuccess;
-  const TileChoice tc = choose_tile(M, N);
-  if (tc.bm == 256 && tc.bn == 256) return launch_tile<256, 256>(P, ldp, Q, ldq, C, ldc, M, N, K, out, stream);
-  if (tc.bm == 256 && tc.bn == 192) return launch_tile<256, 192>(P, ldp, Q, ldq, C, ldc, M, N, K, out, stream);
-  if (tc.bm == 256 && tc.bn == 128) return launch_tile<256, 128>(P, ldp, Q, ldq, C, ldc, M, N, K, out, stream);
-  return launch_tile<128, 128>(P, ldp, Q, ldq, C, ldc, M, N, K, out, stream);
+  return launch_gemm_bf16_ex(P, ldp, Q, ldq, C, ldc, M, N, K, out, Layout::NN, nullptr, 0,
+                             nullptr, stream);
 }
 
 }  // namespace tpmlp

@@ -11,13 +11,27 @@ namespace tpmlp {
 
 // GeluE4m3 (e4m3 GEMM only): Z = bf16(GeLU(.)) quantised to e4m3 with a
 // given scale, one byte per element.
-enum class OutKind : int { GeluBf16 = 0, F32 = 1, Bf16 = 2, GeluE4m3 = 3 };
+// GeluGradBf16 (bf16 GEMM, backward): C = bf16(acc·GeLU'(S)), C2 = bf16(GeLU(S))
+// with S read from an fp32 [M, N] matrix.
+enum class OutKind : int { GeluBf16 = 0, F32 = 1, Bf16 = 2, GeluE4m3 = 3, GeluGradBf16 = 4 };
+
+// Operand layouts of the bf16 GEMM C = P·Q: NN = P [M, K] K-contiguous and
+// Q [K, N] N-contiguous (the forward); QT = Q stored [N, K] K-contiguous;
+// PT = P stored [K, M] M-contiguous.
+enum class Layout : int { NN = 0, QT = 1, PT = 2 };
 
 // C[M, N] = epilogue(P[M, K] · Q[K, N]); P rows K-contiguous (stride ldp),
 // Q rows N-contiguous (stride ldq), C dense with stride ldc, all bf16 inputs.
 hipError_t launch_gemm_bf16(const uint16_t* P, int64_t ldp, const uint16_t* Q, int64_t ldq,
                             void* C, int64_t ldc, int M, int N, int K, OutKind out,
                             hipStream_t stream);
+
+// The same GEMM with another operand layout and the backward's epilogue;
+// ldp / ldq are the row strides of P and Q as stored; aux/ldaux (fp32 S) and
+// C2 (bf16 Z, row stride ldc) are used by GeluGradBf16 only.
+hipError_t launch_gemm_bf16_ex(const uint16_t* P, int64_t ldp, const uint16_t* Q, int64_t ldq,
+                               void* C, int64_t ldc, int M, int N, int K, OutKind out, Layout lay,
+                               const float* aux, int64_t ldaux, void* C2, hipStream_t stream);
 
 // Y = Σ_i parts[i] in rank order, fp32 accumulation, then + bias[e % d] when
 // bias_kind is 1 (fp32 bias) or 2 (bf16 bias); bias_kind 0 adds nothing.

@@ -227,6 +227,40 @@ def test_fp8_delayed_validation():
     assert sh(Y=BASE + 4 * GB) == EALIAS
 
 
+def test_backward_validation():
+    M, d, H, N = 32, 64, 256, 2
+    F = H // N
+    ws = L.tp_mlp_shard_backward_workspace_size(M, d, H, N)
+    assert ws == 4 * M * F + 2 * (2 * M * F)          # S fp32, dS and Z bf16 (256-multiples here)
+    assert L.tp_mlp_shard_backward_workspace_size(M, d, H, 3) == 0
+    assert L.tp_mlp_shard_backward_workspace_size(M, d, 0, 1) == 0
+    a = dict(X=BASE, A=BASE + GB, B=BASE + 2 * GB, dY=BASE + 3 * GB, dX=BASE + 4 * GB,
+             dA=BASE + 5 * GB, dB=BASE + 6 * GB, M=M, d=d, H=H, N=N, rank=1, ws=BASE + 7 * GB,
+             wsb=ws)
+
+    def bw(**kw):
+        b = dict(a, **kw)
+        return L.tp_mlp_shard_backward(b["X"], b["A"], b["B"], b["dY"], b["dX"], b["dA"], b["dB"],
+                                       b["M"], b["d"], b["H"], b["N"], b["rank"], b["ws"],
+                                       b["wsb"], None)
+    assert bw(M=0) == OK
+    assert bw(rank=2) == EARG
+    assert bw(N=0) == EARG
+    assert bw(N=3) == ESHAPE                  # H not divisible by N
+    assert bw(M=36) == ESHAPE                 # M is a contraction length: multiple of 8
+    assert bw(d=60) == ESHAPE
+    assert bw(N=64) == ESHAPE                 # F = 4
+    assert bw(dY=None) == ENULL
+    assert bw(dB=None) == ENULL
+    assert bw(ws=None) == EWS
+    assert bw(wsb=ws - 1) == EWS
+    assert bw(dA=BASE + 5 * GB + 8) == EALIGN
+    assert bw(dX=BASE + 3 * GB + 64) == EALIAS     # dX_i overlaps dY
+    assert bw(dA=BASE + 4 * GB + 64) == EALIAS     # dA_i overlaps dX_i
+    assert bw(ws=BASE + 6 * GB) == EALIAS          # workspace is dB_i
+    assert bw(dB=BASE + GB + 1024) == EALIAS       # dB_i inside A
+
+
 def test_python_wrapper_rejects_cpu_tensors():
     import torch
     X = torch.zeros(4, 8, dtype=torch.bfloat16)

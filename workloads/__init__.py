@@ -17,6 +17,11 @@ Recipe (the same for every workload):
 each then rounded float64 -> float32 (IEEE, round to nearest even) and
 float32 -> bfloat16 (round to nearest even).  H is 4d for a full weight, or
 the shard width F when a workload draws one rank's shard directly.
+
+The backward's output gradient comes from a generator of its own, so that
+the forward inputs of a workload stay the same bits:
+  dY = grad_sigma * default_rng([seed, 1]).standard_normal((M, d))
+rounded the same way.
 """
 from __future__ import annotations
 
@@ -24,8 +29,8 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-__all__ = ["Workload", "WORKLOADS", "make_inputs", "make_random", "bf16_bits_from_f32",
-           "bf16_bits_to_f32"]
+__all__ = ["Workload", "WORKLOADS", "make_inputs", "make_random", "make_output_grad",
+           "bf16_bits_from_f32", "bf16_bits_to_f32"]
 
 
 @dataclass(frozen=True)
@@ -40,15 +45,21 @@ class Workload:
     seed: int
     description: str = ""
     fp8: bool = False  # the workload runs the e4m3 variant of the path
+    grad_sigma: float = 1.0  # std-dev of the output gradient dY (backward workloads)
     tags: tuple = field(default_factory=tuple)
 
     @property
     def F(self) -> int:
         return self.H // self.N
 
+    @property
+    def backward(self) -> bool:
+        return "backward" in self.tags
+
     def flops_per_shard(self) -> int:
-        """Two GEMMs of 2·M·d·F flops each."""
-        return 4 * self.M * self.d * self.F
+        """Forward: two GEMMs of 2·M·d·F flops each. Backward: five (S
+        recomputed, dZ, dX_i, dA_i, dB_i)."""
+        return (10 if self.backward else 4) * self.M * self.d * self.F
 
 
 WORKLOADS = {
@@ -79,6 +90,12 @@ WORKLOADS = {
                                       sigma=0.006, seed=3, fp8=True, tags=("delayed",),
                                       description="175b_tp8_e4m3 with delayed scaling of Z "
                                                   "(amax history of 1024 steps)"),
+    # Backward of every rank's shard of 7b_tp8 for an output gradient dY, and
+    # the sum of the ranks' input gradients.
+    "7b_tp8_bwd": Workload("7b_tp8_bwd", M=8192, d=4096, H=16384, N=8, sigma=0.02, seed=2,
+                           tags=("backward",),
+                           description="backward of 7b_tp8: dY[8192x4096]; per rank S, dS, "
+                                       "dX_i, dA_i[4096x2048], dB_i[2048x4096]; sum of dX_i"),
 }
 
 
@@ -109,6 +126,11 @@ def make_random(M: int, d: int, H: int, seed: int, sigma: float = 0.02,
     A = _draw_bf16(rng, (d, H), sigma)
     B = _draw_bf16(rng, (H, d), sigma)
     return X, A, B
+
+
+def make_output_grad(M: int, d: int, seed: int, sigma: float = 1.0) -> np.ndarray:
+    """dY [M, d] as bfloat16 bits, from its own generator default_rng([seed, 1])."""
+    return _draw_bf16(np.random.default_rng([seed, 1]), (M, d), sigma)
 
 
 def make_inputs(name_or_wl) -> tuple:
