@@ -493,14 +493,11 @@ int tp_mlp_shard_backward(const void* X, const void* A, const void* B, const voi
   if (e == hipSuccess)
     e = tpmlp::launch_gemm_bf16_ex(dS, F, A_i, H, dX_i, d, m, dd, f, OutKind::F32, Layout::QT,
                                    nullptr, 0, nullptr, s);
-  // dB_i = Zᵀ·dY ([F, d], contraction over the M tokens)
+  // dB_i = Zᵀ·dY ([F, d]) and dA_i = Xᵀ·dS ([d, F]), contractions over the M
+  // tokens, in one launch: each alone has too few output tiles to fill the chip
   if (e == hipSuccess)
-    e = tpmlp::launch_gemm_bf16_ex(Z, F, dy, d, dB_i, d, f, dd, m, OutKind::F32, Layout::PT,
-                                   nullptr, 0, nullptr, s);
-  // dA_i = Xᵀ·dS ([d, F])
-  if (e == hipSuccess)
-    e = tpmlp::launch_gemm_bf16_ex(x, d, dS, F, dA_i, F, dd, f, m, OutKind::F32, Layout::PT,
-                                   nullptr, 0, nullptr, s);
+    e = tpmlp::launch_gemm_bf16_pair({Z, F, dy, d, dB_i, d, f, dd, m},
+                                     {x, d, dS, F, dA_i, F, dd, f, m}, OutKind::F32, Layout::PT, s);
   return status_of(e);
 }
 

@@ -155,13 +155,16 @@ struct Operand {
   }
 };
 
-// Lane-dependent part of a fragment's LDS address for fragment rows/columns
-// fb .. fb+15 (wave-tile relative): K-major, the LDS row this lane reads;
-// MN-major, the byte offset of its first 8-byte piece at k-step 0.
+// Fragment addressing. K-major: `fa` is the fragment's first row fb (a
+// multiple of 16), and the lane reads row fb + (lane & 15) at chunk
+// 4s + (lane >> 4); as fb is a multiple of 16 the chunk swizzle of that row
+// depends on the lane only, so the lane's byte offset is one value per k-step
+// plus fb·128 (an immediate once the wave's base is folded in). MN-major:
+// `fa` is the byte offset of the lane's first 8-byte piece at k-step 0.
 template <int W, bool KMAJ>
 __device__ __forceinline__ int frag_addr(int fb, int lane) {
   if constexpr (KMAJ) {
-    return fb + (lane & 15);
+    return fb;
   } else {
     constexpr int GR = W / 8;
     // every k-row a lane reads is 32s + 4h + rsub, whose rotation (bits 0, 1
@@ -172,15 +175,20 @@ __device__ __forceinline__ int frag_addr(int fb, int lane) {
   }
 }
 
+// Lane part of a K-major fragment address for k-step s: row lane & 15 of the
+// fragment, chunk swz_p(row, 4s + (lane >> 4)).
+__device__ __forceinline__ int kmaj_lane_off(int lane, int s) {
+  return (lane & 15) * (kBK * 2) + swz_p<kBK / 8>(lane & 15, 4 * s + (lane >> 4)) * 16;
+}
+
 // Piece h (of Operand::READS) of the fragment at `fa` (from frag_addr) for
-// k-step s of stage sp: K-major, one ds_read_b128 of chunk 4s + (lane >> 4);
-// MN-major, k-rows 32s + 4h + rsub by a transposing read.
+// k-step s of stage sp: K-major, one ds_read_b128; MN-major, k-rows
+// 32s + 4h + rsub by a transposing read.
 template <int W, bool KMAJ>
 __device__ __forceinline__ void read_frag(const uint8_t* sp, int fa, int s, int h, int lane,
                                           s16x8& f) {
   if constexpr (KMAJ) {
-    f = *reinterpret_cast<const s16x8*>(sp + fa * (kBK * 2) +
-                                        swz_p<kBK / 8>(fa, 4 * s + (lane >> 4)) * 16);
+    f = *reinterpret_cast<const s16x8*>(sp + fa * (kBK * 2) + kmaj_lane_off(lane, s));
   } else {
     const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (lds_s16x4*)(sp + fa + (32 * s + 4 * h) * (2 * W)));
@@ -188,11 +196,19 @@ __device__ __forceinline__ void read_frag(const uint8_t* sp, int fa, int s, int 
   }
 }
 
+// One GEMM problem: C = P·Q with the operands as stored (row strides ldp,
+// ldq), C [M, N] with row stride ldc; aux/ldaux and C2 for GeluGradBf16.
+struct GemmArgs {
+  const uint16_t* P; int64_t ldp; const uint16_t* Q; int64_t ldq; void* C; int64_t ldc;
+  const float* aux; int64_t ldaux; void* C2; int M, N, K;
+};
+
+// Workgroups [0, tiles0) compute problem g0, the rest problem g1 (a launch
+// of one problem passes tiles0 = its tile count). Both share the template
+// arguments (tile, epilogue, layouts, KTAIL).
 template <int BM, int BN, int OUT, bool KTAIL, bool PT, bool QT>
-__global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
-    const uint16_t* __restrict__ P, int64_t ldp, const uint16_t* __restrict__ Q, int64_t ldq,
-    void* __restrict__ C, int64_t ldc, const float* __restrict__ aux, int64_t ldaux,
-    void* __restrict__ C2, int M, int N, int K, int group_m) {
+__global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs g0, GemmArgs g1,
+                                                             int tiles0, int group_m) {
   constexpr int BK = kBK, NSP = kNSP, NSQ = kNSQ;
   constexpr int TM = BM / 2, TN = BN / 2;      // wave tile (2 x 2 waves)
   constexpr int MT = TM / 16, NT = TN / 16;    // 16x16 MFMA tiles per wave
@@ -206,9 +222,21 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NSP * P_BYTES + NSQ * Q_BYTES];
 
+  int id = xcd_remap(blockIdx.x, gridDim.x);
+  const bool second = id >= tiles0;
+  const GemmArgs& g = second ? g1 : g0;
+  if (second) id -= tiles0;
+  const uint16_t* const P = g.P;
+  const uint16_t* const Q = g.Q;
+  void* const C = g.C;
+  void* const C2 = g.C2;
+  const float* const aux = g.aux;
+  const int64_t ldp = g.ldp, ldq = g.ldq, ldc = g.ldc, ldaux = g.ldaux;
+  const int M = g.M, N = g.N, K = g.K;
+
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   int tm, tn;
-  grouped_tile(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n, group_m, tm, tn);
+  grouped_tile(id, tiles_m, tiles_n, group_m, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
 
   const int t = threadIdx.x;
@@ -354,6 +382,43 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
 
   // Epilogue. Lane holds, for 16x16 tile (ni, mi), C[m][n .. n+3] with
   // m = mi·16 + (lane & 15), n = ni·16 + 4·(lane >> 4) (wave-tile relative).
+  if constexpr (OUT == (int)OutKind::GeluGradBf16) {
+    // dS = bf16(dZ·GeLU'(S)) into C, Z = bf16(GeLU(S)) into C2. The S loads
+    // of EB tiles are issued together (from clamped addresses, so they need
+    // no branch) and their latency is paid once per batch.
+    constexpr int EB = 8;
+    static_assert((NT * MT) % EB == 0, "epilogue batches");
+#pragma unroll
+    for (int b0 = 0; b0 < NT * MT; b0 += EB) {
+      f32x4 sv[EB];
+#pragma unroll
+      for (int e = 0; e < EB; ++e) {
+        const int ni = (b0 + e) / MT, mi = (b0 + e) % MT;
+        const int m = min(m0 + wm * TM + mi * 16 + (lane & 15), M - 1);
+        const int n = min(n0 + wn * TN + ni * 16 + 4 * (lane >> 4), N - 4);
+        sv[e] = *reinterpret_cast<const f32x4*>(aux + (int64_t)m * ldaux + n);
+      }
+#pragma unroll
+      for (int e = 0; e < EB; ++e) {
+        const int ni = (b0 + e) / MT, mi = (b0 + e) % MT;
+        const int m = m0 + wm * TM + mi * 16 + (lane & 15);
+        const int n = n0 + wn * TN + ni * 16 + 4 * (lane >> 4);
+        f32x4 v = acc[ni][mi];
+        asm volatile("" : "+v"(v));
+        float gl[4], dg[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) gelu_and_grad(sv[e][q], gl[q], dg[q]);
+        if (m < M && n < N) {
+          const u32x2 o = {pack_bf16x2(v[0] * dg[0], v[1] * dg[1]),
+                           pack_bf16x2(v[2] * dg[2], v[3] * dg[3])};
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(C) + (int64_t)m * ldc + n) = o;
+          const u32x2 z = {pack_bf16x2(gl[0], gl[1]), pack_bf16x2(gl[2], gl[3])};
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(C2) + (int64_t)m * ldc + n) = z;
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int ni = 0; ni < NT; ++ni) {
 #pragma unroll
@@ -372,17 +437,6 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
         const u32x2 o = {pack_bf16x2(gelu_exact(v[0]), gelu_exact(v[1])),
                          pack_bf16x2(gelu_exact(v[2]), gelu_exact(v[3]))};
         *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(C) + (int64_t)m * ldc + n) = o;
-      } else if constexpr (OUT == (int)OutKind::GeluGradBf16) {
-        // dS = bf16(dZ·GeLU'(S)) into C, Z = bf16(GeLU(S)) into C2
-        const f32x4 sv = *reinterpret_cast<const f32x4*>(aux + (int64_t)m * ldaux + n);
-        float g[4], dg[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) gelu_and_grad(sv[e], g[e], dg[e]);
-        const u32x2 o = {pack_bf16x2(v[0] * dg[0], v[1] * dg[1]),
-                         pack_bf16x2(v[2] * dg[2], v[3] * dg[3])};
-        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(C) + (int64_t)m * ldc + n) = o;
-        const u32x2 z = {pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3])};
-        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(C2) + (int64_t)m * ldc + n) = z;
       } else {
         const u32x2 o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
         *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(C) + (int64_t)m * ldc + n) = o;
@@ -391,18 +445,19 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(
   }
 }
 
-struct GemmArgs {
-  const uint16_t* P; int64_t ldp; const uint16_t* Q; int64_t ldq; void* C; int64_t ldc;
-  const float* aux; int64_t ldaux; void* C2; int M, N, K;
-};
+template <int BM, int BN>
+int tile_count(const GemmArgs& a) {
+  return ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+}
 
+// One launch over problems a[0 .. n) (n = 1 or 2).
 template <int BM, int BN, int OUT, bool KTAIL, bool PT, bool QT>
-hipError_t launch_one(const GemmArgs& a, hipStream_t stream) {
-  const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+hipError_t launch_one(const GemmArgs* a, int n, hipStream_t stream) {
+  const int t0 = tile_count<BM, BN>(a[0]);
+  const int tiles = t0 + (n > 1 ? tile_count<BM, BN>(a[1]) : 0);
   const int group_m = 4;
   hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, OUT, KTAIL, PT, QT>), dim3(tiles), dim3(kThreads), 0,
-                     stream, a.P, a.ldp, a.Q, a.ldq, a.C, a.ldc, a.aux, a.ldaux, a.C2, a.M, a.N,
-                     a.K, group_m);
+                     stream, a[0], n > 1 ? a[1] : a[0], t0, group_m);
   return hipGetLastError();
 }
 
@@ -410,30 +465,32 @@ hipError_t launch_one(const GemmArgs& a, hipStream_t stream) {
 // K-major P / N-major Q with GeLU, fp32 or bf16 output; K-major Q with the
 // GeLU-gradient or fp32 epilogue; M-major P with fp32 output.
 template <int BM, int BN, bool KTAIL>
-hipError_t launch_cfg(const GemmArgs& a, OutKind out, Layout lay, hipStream_t stream) {
+hipError_t launch_cfg(const GemmArgs* a, int n, OutKind out, Layout lay, hipStream_t stream) {
   if (lay == Layout::NN) {
     switch (out) {
-      case OutKind::GeluBf16: return launch_one<BM, BN, (int)OutKind::GeluBf16, KTAIL, false, false>(a, stream);
-      case OutKind::F32: return launch_one<BM, BN, (int)OutKind::F32, KTAIL, false, false>(a, stream);
-      case OutKind::Bf16: return launch_one<BM, BN, (int)OutKind::Bf16, KTAIL, false, false>(a, stream);
+      case OutKind::GeluBf16: return launch_one<BM, BN, (int)OutKind::GeluBf16, KTAIL, false, false>(a, n, stream);
+      case OutKind::F32: return launch_one<BM, BN, (int)OutKind::F32, KTAIL, false, false>(a, n, stream);
+      case OutKind::Bf16: return launch_one<BM, BN, (int)OutKind::Bf16, KTAIL, false, false>(a, n, stream);
       default: return hipErrorInvalidValue;
     }
   }
   if (lay == Layout::QT) {
     switch (out) {
-      case OutKind::GeluGradBf16: return launch_one<BM, BN, (int)OutKind::GeluGradBf16, KTAIL, false, true>(a, stream);
-      case OutKind::F32: return launch_one<BM, BN, (int)OutKind::F32, KTAIL, false, true>(a, stream);
+      case OutKind::GeluGradBf16: return launch_one<BM, BN, (int)OutKind::GeluGradBf16, KTAIL, false, true>(a, n, stream);
+      case OutKind::F32: return launch_one<BM, BN, (int)OutKind::F32, KTAIL, false, true>(a, n, stream);
       default: return hipErrorInvalidValue;
     }
   }
-  if (out == OutKind::F32) return launch_one<BM, BN, (int)OutKind::F32, KTAIL, true, false>(a, stream);
+  if (out == OutKind::F32) return launch_one<BM, BN, (int)OutKind::F32, KTAIL, true, false>(a, n, stream);
   return hipErrorInvalidValue;
 }
 
 template <int BM, int BN>
-hipError_t launch_tile(const GemmArgs& a, OutKind out, Layout lay, hipStream_t stream) {
-  if (a.K % kBK == 0) return launch_cfg<BM, BN, false>(a, out, lay, stream);
-  return launch_cfg<BM, BN, true>(a, out, lay, stream);
+hipError_t launch_tile(const GemmArgs* a, int n, OutKind out, Layout lay, hipStream_t stream) {
+  bool tail = false;
+  for (int i = 0; i < n; ++i) tail = tail || a[i].K % kBK != 0;
+  if (!tail) return launch_cfg<BM, BN, false>(a, n, out, lay, stream);
+  return launch_cfg<BM, BN, true>(a, n, out, lay, stream);
 }
 
 struct TileChoice { int bm, bn; };
@@ -441,7 +498,7 @@ struct TileChoice { int bm, bn; };
 // Pick the tile shape with the best estimated time: waves of 256 CUs times a
 // per-tile time relative to a 256x256 tile, measured on MI355X (smaller
 // tiles reuse each LDS byte less, so their cost falls slower than their area).
-TileChoice choose_tile(int M, int N) {
+TileChoice choose_tile(const GemmArgs* a, int n) {
   static const struct { int bm, bn; double cost; } cands[] = {
       {256, 256, 1.00}, {256, 192, 0.85}, {256, 128, 0.62}, {128, 128, 0.30},
   };
@@ -449,12 +506,22 @@ TileChoice choose_tile(int M, int N) {
   double best = 1e300;
   TileChoice choice{256, 256};
   for (const auto& c : cands) {
-    const long tiles = (long)((M + c.bm - 1) / c.bm) * ((N + c.bn - 1) / c.bn);
+    long tiles = 0;
+    for (int i = 0; i < n; ++i)
+      tiles += (long)((a[i].M + c.bm - 1) / c.bm) * ((a[i].N + c.bn - 1) / c.bn);
     const long waves = (tiles + kCus - 1) / kCus;
     const double est = waves * c.cost;
     if (est < best - 1e-9) { best = est; choice = {c.bm, c.bn}; }
   }
   return choice;
+}
+
+hipError_t launch_group(const GemmArgs* a, int n, OutKind out, Layout lay, hipStream_t stream) {
+  const TileChoice tc = choose_tile(a, n);
+  if (tc.bm == 256 && tc.bn == 256) return launch_tile<256, 256>(a, n, out, lay, stream);
+  if (tc.bm == 256 && tc.bn == 192) return launch_tile<256, 192>(a, n, out, lay, stream);
+  if (tc.bm == 256 && tc.bn == 128) return launch_tile<256, 128>(a, n, out, lay, stream);
+  return launch_tile<128, 128>(a, n, out, lay, stream);
 }
 
 }  // namespace
@@ -464,11 +531,19 @@ hipError_t launch_gemm_bf16_ex(const uint16_t* P, int64_t ldp, const uint16_t* Q
                                const float* aux, int64_t ldaux, void* C2, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
   const GemmArgs a{P, ldp, Q, ldq, C, ldc, aux, ldaux, C2, M, N, K};
-  const TileChoice tc = choose_tile(M, N);
-  if (tc.bm == 256 && tc.bn == 256) return launch_tile<256, 256>(a, out, lay, stream);
-  if (tc.bm == 256 && tc.bn == 192) return launch_tile<256, 192>(a, out, lay, stream);
-  if (tc.bm == 256 && tc.bn == 128) return launch_tile<256, 128>(a, out, lay, stream);
-  return launch_tile<128, 128>(a, out, lay, stream);
+  return launch_group(&a, 1, out, lay, stream);
+}
+
+hipError_t launch_gemm_bf16_pair(const BfGemm& x, const BfGemm& y, OutKind out, Layout lay,
+                                 hipStream_t stream) {
+  GemmArgs a[2];
+  int n = 0;
+  for (const BfGemm* g : {&x, &y})
+    if (g->M > 0 && g->N > 0)
+      a[n++] = GemmArgs{g->P, g->ldp, g->Q, g->ldq, g->C, g->ldc, nullptr, 0, nullptr, g->M, g->N,
+                        g->K};
+  if (n == 0) return hipSuccess;
+  return launch_group(a, n, out, lay, stream);
 }
 
 hipError_t launch_gemm_bf16(const uint16_t* P, int64_t ldp, const uint16_t* Q, int64_t ldq,

@@ -33,6 +33,15 @@ hipError_t launch_gemm_bf16_ex(const uint16_t* P, int64_t ldp, const uint16_t* Q
                                void* C, int64_t ldc, int M, int N, int K, OutKind out, Layout lay,
                                const float* aux, int64_t ldaux, void* C2, hipStream_t stream);
 
+// Two independent GEMMs of one layout and epilogue (fp32 or bf16 output) in
+// one launch, so that two problems of few tiles each fill the chip together.
+struct BfGemm {
+  const uint16_t* P; int64_t ldp; const uint16_t* Q; int64_t ldq; void* C; int64_t ldc;
+  int M, N, K;
+};
+hipError_t launch_gemm_bf16_pair(const BfGemm& x, const BfGemm& y, OutKind out, Layout lay,
+                                 hipStream_t stream);
+
 // Y = Σ_i parts[i] in rank order, fp32 accumulation, then + bias[e % d] when
 // bias_kind is 1 (fp32 bias) or 2 (bf16 bias); bias_kind 0 adds nothing.
 hipError_t launch_partial_sum(const void* const* parts, int nparts, bool parts_bf16, void* Y,
