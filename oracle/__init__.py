@@ -24,6 +24,10 @@ What it computes, and where the pages define it:
   ("Megatron-LM deep architecture", FP8 hybrid precision section), with the
   current scale (the tensor's own amax) or the delayed one (448 over the
   moving average of the amaxes recorded in earlier steps).
+* Attention shard (module `attention`; "Megatron-LM" glossary and
+  "Megatron architecture and 6D parallel guide", §3.2): the heads split over
+  the ranks, column-parallel QKV projection, per-head softmax attention, and
+  the row-parallel output projection whose partials sum to the block output.
 * Backward of the shard: the chain rule through the forward as computed,
   dZ = dY·B_iᵀ, dS = bf16(dZ ⊙ GeLU'(S)), dX_i = dS·A_iᵀ, dA_i = Xᵀ·dS,
   dB_i = Z_iᵀ·dY; the ranks' dX_i sum to the input gradient (the backward
@@ -37,6 +41,7 @@ the closed form Σ_i Y_i = Y, N=1 = unsharded, structured inputs that reduce
 the path to an elementwise GeLU, textbook values of the normal CDF, and
 exhaustive codec checks against torch's CPU conversions.
 """
+from . import attention
 from .codecs import (bf16_decode, bf16_encode, e4m3_decode, e4m3_encode, E4M3_MAX)
 from .mlp import (shard_columns, gelu, col_gelu, row_partial, mlp_shard, partial_sum,
                   sp_rows, partial_sum_rows, reduce_scatter_share, mlp_unsharded, amax,
@@ -52,4 +57,5 @@ __all__ = [
     "quant_scale", "quant_e4m3", "col_gelu_e4m3", "requant_z", "row_partial_e4m3",
     "mlp_shard_e4m3", "quantize_inputs_e4m3", "delayed_scale", "amax_history_push",
     "col_gelu_e4m3_delayed", "mlp_shard_e4m3_delayed", "gelu_grad", "mlp_shard_backward",
+    "attention",
 ]

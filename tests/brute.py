@@ -142,3 +142,31 @@ def shard_backward_exact(X_bits, A_bits, B_bits, dY_bits, N, rank):
     Xt = [list(col) for col in zip(*X)]
     Zt = [list(col) for col in zip(*Z)]
     return Z, dS, matmul_exact(dS, At), matmul_exact(Xt, dS), matmul_exact(Zt, dY)
+
+
+def attention_exact(qkv_bits, B, S, heads, dh, causal=True):
+    """Per-head scaled dot-product attention with pure-Python loops: exact
+    rational scores q·k, each weight exp(score/√dh − max) by math.exp, the
+    weighted sums with math.fsum.  qkv_bits: list of rows of bfloat16 bits in
+    the head-major layout ([Q_h | K_h | V_h] per head).  Returns a list of
+    float rows [B·S][heads·dh] (unrounded)."""
+    val = [[float(bf16_value(b)) for b in row] for row in qkv_bits]
+    inv = 1.0 / math.sqrt(dh)
+    out = [[0.0] * (heads * dh) for _ in range(B * S)]
+    for b in range(B):
+        for h in range(heads):
+            c = 3 * h * dh
+            for t in range(S):
+                q = [Fraction(x) for x in val[b * S + t][c:c + dh]]
+                keys = range(t + 1) if causal else range(S)
+                sc = []
+                for j in keys:
+                    k = val[b * S + j][c + dh:c + 2 * dh]
+                    sc.append(float(sum(qi * Fraction(kj) for qi, kj in zip(q, k))) * inv)
+                mx = max(sc)
+                w = [math.exp(x - mx) for x in sc]
+                den = math.fsum(w)
+                for e in range(dh):
+                    vs = [val[b * S + j][c + 2 * dh + e] for j in keys]
+                    out[b * S + t][h * dh + e] = math.fsum(wi * vi for wi, vi in zip(w, vs)) / den
+    return out

@@ -251,3 +251,85 @@ def test_backward_untransposed_weight_is_caught(monkeypatch):
     monkeypatch.setattr(omlp, "mlp_shard_backward", bw)
     monkeypatch.setattr(oracle, "mlp_shard_backward", bw)
     assert _pins_fail(BACKWARD_PINS)
+
+
+# ------------------------------------------------------------- attention --
+
+import test_oracle_attention as apins  # noqa: E402
+from oracle import attention as oat  # noqa: E402
+
+ATTN_PINS = [
+    lambda: apins.test_matches_torch_sdpa_in_float64(2, 37, 3, 16, True),
+    lambda: apins.test_matches_torch_sdpa_in_float64(3, 19, 4, 8, False),
+    lambda: apins.test_matches_loop_brute_force(True),
+    apins.test_zero_queries_give_prefix_means,
+    apins.test_first_query_copies_first_value_and_dominant_key_is_selected,
+    apins.test_sequences_are_independent,
+    lambda: apins.test_shards_sum_to_the_unsharded_block(4),
+    apins.test_qkv_block_follows_the_glossary_listing,
+]
+
+
+def _attention_variant(monkeypatch, fn):
+    monkeypatch.setattr(oat, "attention_heads", fn)
+
+
+def _heads_variant(scale_fn=None, mask_shift=1, swap_kv=False, softmax_axis=-1, per_batch=True):
+    def attn(QKV_bits, B, S, heads, dh, causal=True, rounding=True):
+        M, F = B * S, heads * dh
+        qkv = oracle.bf16_decode(QKV_bits)
+        out = np.empty((M, F))
+        scale = scale_fn(dh) if scale_fn else 1.0 / np.sqrt(dh)
+        for b in range(B):
+            rows = slice(b * S, (b + 1) * S) if per_batch else slice(0, S)
+            for h in range(heads):
+                c = 3 * h * dh
+                q = qkv[rows, c:c + dh]
+                k = qkv[rows, c + dh:c + 2 * dh]
+                v = qkv[rows, c + 2 * dh:c + 3 * dh]
+                if swap_kv:
+                    k, v = v, k
+                s = (q @ k.T) * scale
+                if causal:
+                    s = np.where(np.triu(np.ones((S, S), bool), k=mask_shift), -np.inf, s)
+                m = np.max(s, axis=softmax_axis, keepdims=True)
+                e = np.exp(s - m)
+                p = e / np.sum(e, axis=softmax_axis, keepdims=True)
+                out[b * S:(b + 1) * S, h * dh:(h + 1) * dh] = p @ v
+        return oracle.bf16_encode(out) if rounding else out
+    return attn
+
+
+@pytest.mark.parametrize("mutant", [
+    dict(scale_fn=lambda dh: 1.0),                 # no 1/√dh
+    dict(scale_fn=lambda dh: 1.0 / dh),            # 1/dh
+    dict(mask_shift=0),                            # mask hides the diagonal too
+    dict(mask_shift=2),                            # one future key visible
+    dict(swap_kv=True),                            # K and V columns swapped
+    dict(softmax_axis=0),                          # normalised over queries
+    dict(per_batch=False),                         # every sequence reads sequence 0
+])
+def test_attention_mutants_are_caught(monkeypatch, mutant):
+    _attention_variant(monkeypatch, _heads_variant(**mutant))
+    assert _pins_fail(ATTN_PINS)
+
+
+def test_attention_wrong_head_block_is_caught(monkeypatch):
+    real = oat.qkv_block
+
+    def blk(W, N, rank):   # rank-major [Q_i | K_i | V_i] instead of head-major groups
+        d = W.shape[0]
+        F = d // N
+        return np.concatenate([W[:, j * d + rank * F:j * d + (rank + 1) * F] for j in range(3)], 1)
+    monkeypatch.setattr(oat, "qkv_block", blk)
+    assert _pins_fail(ATTN_PINS)
+    monkeypatch.setattr(oat, "qkv_block", real)
+
+
+def test_attention_output_rows_of_the_wrong_rank_are_caught(monkeypatch):
+    real = oat.out_partial
+
+    def op(O_bits, Wo_bits, N, rank):
+        return real(O_bits, Wo_bits, N, (rank + 1) % N)
+    monkeypatch.setattr(oat, "out_partial", op)
+    assert _pins_fail(ATTN_PINS)

@@ -30,6 +30,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "make_inputs", "make_random", "make_output_grad",
+           "AttnWorkload", "ATTN_WORKLOADS", "make_attn_inputs",
            "bf16_bits_from_f32", "bf16_bits_to_f32"]
 
 
@@ -97,6 +98,73 @@ WORKLOADS = {
                            description="backward of 7b_tp8: dY[8192x4096]; per rank S, dS, "
                                        "dX_i, dA_i[4096x2048], dB_i[2048x4096]; sum of dX_i"),
 }
+
+
+@dataclass(frozen=True)
+class AttnWorkload:
+    """One attention-block shape: B sequences of S tokens, width d, `heads`
+    heads of width d/heads split over N ranks."""
+    name: str
+    B: int
+    S: int
+    d: int
+    heads: int
+    N: int
+    sigma: float      # std-dev of W_qkv and W_o entries
+    seed: int
+    causal: bool = True
+    description: str = ""
+
+    @property
+    def M(self) -> int:
+        return self.B * self.S
+
+    @property
+    def dh(self) -> int:
+        return self.d // self.heads
+
+    @property
+    def F(self) -> int:
+        return self.d // self.N
+
+    def flops_per_shard(self) -> int:
+        """QKV projection 2·M·d·3F, output projection 2·M·F·d, and per head
+        QKᵀ and P·V, 4·S²·dh per sequence (half of it with the causal mask)."""
+        hr = self.heads // self.N
+        att = 4 * self.S * self.S * self.dh * hr * self.B
+        if self.causal:
+            att //= 2
+        return 2 * self.M * self.d * 3 * self.F + 2 * self.M * self.F * self.d + att
+
+
+ATTN_WORKLOADS = {
+    # Two sequences of 40 tokens (a ragged tail for 64-key blocks), d = 1024,
+    # 8 heads of 128 split over 2 ranks.
+    "attn_tiny": AttnWorkload("attn_tiny", B=2, S=40, d=1024, heads=8, N=2, sigma=0.03, seed=10,
+                              description="X[80x1024], W_qkv[1024x3072], W_o[1024x1024], "
+                                          "8 heads of 128, TP N=2, causal"),
+    # 7B-class attention block at TP=8: 32 heads of 128, 4 per rank
+    # ("Megatron architecture and 6D parallel guide", §3.2: 32 heads at TP=8),
+    # 4 sequences of 2048 tokens, causal.
+    "7b_tp8_attn": AttnWorkload("7b_tp8_attn", B=4, S=2048, d=4096, heads=32, N=8, sigma=0.02,
+                                seed=4,
+                                description="X[8192x4096] (4 x 2048 tokens), W_qkv[4096x12288], "
+                                            "W_o[4096x4096], 32 heads of 128, TP N=8 (4 heads "
+                                            "per rank), causal, all ranks + sum"),
+}
+
+
+def make_attn_inputs(name_or_wl) -> tuple:
+    """(X, W_qkv, W_o) bfloat16 bits: rng = default_rng(seed); X = N(0,1)
+    [B·S, d], then W_qkv = σ·N(0,1) [d, 3d] (head-major: columns
+    [h·3dh, (h+1)·3dh) are head h's query, key and value columns), then
+    W_o = σ·N(0,1) [d, d]; rounded as the MLP inputs are."""
+    wl = ATTN_WORKLOADS[name_or_wl] if isinstance(name_or_wl, str) else name_or_wl
+    rng = np.random.default_rng(wl.seed)
+    X = _draw_bf16(rng, (wl.M, wl.d), 1.0)
+    Wqkv = _draw_bf16(rng, (wl.d, 3 * wl.d), wl.sigma)
+    Wo = _draw_bf16(rng, (wl.d, wl.d), wl.sigma)
+    return X, Wqkv, Wo
 
 
 def bf16_bits_from_f32(x32: np.ndarray) -> np.ndarray:
