@@ -316,6 +316,70 @@ int tp_mlp_shard_backward(const void* X, const void* A, const void* B, const voi
                           int64_t H, int N, int rank, void* workspace, size_t workspace_bytes,
                           void* stream);
 
+/*
+ * ---------------------------------------------------------------------------
+ * Attention shard. With h heads of width dh = d/h and N ranks, rank i owns
+ * heads [i·h/N, (i+1)·h/N) and computes their attention with no exchange
+ * ("Megatron-LM" glossary, tensor-parallel section: QKV projection column
+ * parallel, attention head parallel, output projection row parallel with an
+ * AllReduce; "Megatron architecture and 6D parallel guide", §3.2: 32 heads
+ * at TP=8 give 4 per GPU). The fused projection weight W_qkv [d, 3d] is
+ * stored head-major: columns [h·3dh, (h+1)·3dh) are head h's query, key and
+ * value columns, so a rank's heads are one contiguous column block
+ * [i·3F, (i+1)·3F), F = d/N. W_o [d, d]: rank i holds rows [i·F, (i+1)·F).
+ * Tokens are batch-major: row b·S + t is token t of sequence b. The
+ * attention kernels take dh = TPM_ATTN_HEAD_DIM only.
+ * ---------------------------------------------------------------------------
+ */
+#define TPM_ATTN_HEAD_DIM 128
+
+/*
+ * Column-parallel QKV projection of one rank: QKV_i = bf16(X · W_i), fp32
+ * accumulation, one rounding.
+ * X : device, bf16 [M, d], dense. W_i : device, bf16 [d, F3] with row stride
+ * ldw >= F3 (ldw = 3d for a column block of W_qkv). QKV_i : device, bf16
+ * [M, F3], dense; written.
+ */
+int tp_attn_qkv(const void* X, const void* W_i, int64_t ldw, void* QKV_i, int64_t M,
+                int64_t d, int64_t F3, void* stream);
+
+/*
+ * Attention of `heads` heads (dh = TPM_ATTN_HEAD_DIM) over B sequences of S
+ * tokens: for sequence b and head j,
+ *   O_bj = softmax(Q_bj·K_bjᵀ / √dh + mask)·V_bj,
+ * mask = −inf where key > query when `causal` is non-zero, else none. Scores
+ * and the softmax are fp32 (exp2 of scaled scores); the probabilities are
+ * rounded to bf16 for the P·V product, whose fp32 sum is divided by the
+ * fp32 sum of the unrounded probabilities; O is rounded to bf16 once.
+ * QKV : device, bf16 [B·S, ld], head j's Q, K, V at columns 3j·dh, 3j·dh + dh,
+ *   3j·dh + 2dh (ld >= 3·heads·dh, a multiple of 8; (S·ld·2) < 2^32).
+ * O : device, bf16 [B·S, ldo], head j at columns [j·dh, (j+1)·dh) (ldo >=
+ *   heads·dh, a multiple of 8); written; must not overlap QKV.
+ */
+int tp_attn_heads(const void* QKV, int64_t ld, void* O, int64_t ldo, int64_t B, int64_t S,
+                  int64_t heads, int causal, void* stream);
+
+/*
+ * Bytes of device workspace tp_attn_shard needs (QKV_i, bf16 [M, 3F], then
+ * O_i, bf16 [M, F], each 256-byte aligned). 0 for invalid sizes.
+ */
+size_t tp_attn_shard_workspace_size(int64_t M, int64_t d, int N);
+
+/*
+ * One rank's partial output of the N-way split attention block:
+ *   QKV_i = bf16(X·W_qkv[:, i·3F:(i+1)·3F]), O_i = attention of its h/N heads,
+ *   Y_i = O_i·W_o[i·F:(i+1)·F, :] (fp32 accumulation);
+ * the block's output is Σ_i Y_i (tp_partial_sum), the AllReduce's sum.
+ * X : device, bf16 [B·S, d]. W_qkv : device, bf16 [d, 3d] (head-major).
+ * W_o : device, bf16 [d, d]. Y_i : device, [B·S, d], y_dtype TPM_F32 or TPM_BF16.
+ * d / heads must equal TPM_ATTN_HEAD_DIM and N must divide heads.
+ * workspace : device, at least tp_attn_shard_workspace_size(B·S, d, N) bytes,
+ *   16-byte aligned; on return it holds QKV_i and O_i.
+ */
+int tp_attn_shard(const void* X, const void* Wqkv, const void* Wo, void* Y_i, int y_dtype,
+                  int64_t B, int64_t S, int64_t d, int64_t heads, int N, int rank, int causal,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -27,12 +27,15 @@ __all__ = [
     "tp_amax_history_push", "tp_mlp_col_gelu_e4m3_delayed", "tp_mlp_shard_e4m3_delayed",
     "tp_mlp_shard_e4m3_delayed_workspace_size", "AmaxHistory",
     "tp_mlp_shard_backward", "tp_mlp_shard_backward_workspace_size", "backward_workspace_views",
+    "tp_attn_qkv", "tp_attn_heads", "tp_attn_shard", "tp_attn_shard_workspace_size",
+    "attn_workspace_views", "ATTN_HEAD_DIM",
     "TPM_BF16", "TPM_F32", "TPM_E4M3", "EXPORTED_SYMBOLS",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtpmlp.so")
 
 TPM_BF16, TPM_F32, TPM_E4M3 = 0, 1, 2
+ATTN_HEAD_DIM = 128  # TPM_ATTN_HEAD_DIM
 TPM_MAX_PARTS = 64
 
 _i64, _int, _vp, _sz = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
@@ -65,6 +68,11 @@ _SIGNATURES = {
     "tp_mlp_shard_backward_workspace_size": (_sz, [_i64, _i64, _i64, _int]),
     "tp_mlp_shard_backward": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int,
                                      _int, _vp, _sz, _vp]),
+    "tp_attn_qkv": (_int, [_vp, _vp, _i64, _vp, _i64, _i64, _i64, _vp]),
+    "tp_attn_heads": (_int, [_vp, _i64, _vp, _i64, _i64, _i64, _i64, _int, _vp]),
+    "tp_attn_shard_workspace_size": (_sz, [_i64, _i64, _int]),
+    "tp_attn_shard": (_int, [_vp, _vp, _vp, _vp, _int, _i64, _i64, _i64, _i64, _int, _int, _int,
+                             _vp, _sz, _vp]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGNATURES)
 
@@ -505,3 +513,75 @@ def backward_workspace_views(workspace, M: int, F: int):
     dS = workspace[o1: o1 + 2 * mf].view(torch.bfloat16).view(M, F)
     Z = workspace[o2: o2 + 2 * mf].view(torch.bfloat16).view(M, F)
     return S, dS, Z
+
+
+def tp_attn_qkv(X, W_i, QKV_i=None, stream=None):
+    """Column-parallel QKV projection QKV_i = bf16(X·W_i); W_i may be a column view (row stride)."""
+    _need(X, "X", torch.bfloat16, 2)
+    _need(W_i, "W_i", torch.bfloat16, 2, contiguous=False)
+    M, d = X.shape
+    if W_i.shape[0] != d or W_i.stride(1) != 1:
+        raise ValueError("W_i must be [d, F3] with unit column stride")
+    F3 = W_i.shape[1]
+    if QKV_i is None:
+        QKV_i = torch.empty((M, F3), dtype=torch.bfloat16, device=X.device)
+    _need(QKV_i, "QKV_i", torch.bfloat16, 2)
+    if tuple(QKV_i.shape) != (M, F3):
+        raise ValueError("QKV_i has the wrong shape")
+    _check(lib.tp_attn_qkv(X.data_ptr(), W_i.data_ptr(), W_i.stride(0), QKV_i.data_ptr(), M, d, F3,
+                           _stream(stream)), "tp_attn_qkv")
+    return QKV_i
+
+
+def tp_attn_heads(QKV, B: int, S: int, heads: int, causal: bool = True, O=None, stream=None):
+    """Per-head softmax attention: QKV [B·S, ≥3·heads·128] (head-major groups) -> O [B·S, heads·128]."""
+    _need(QKV, "QKV", torch.bfloat16, 2, contiguous=False)
+    if QKV.shape[0] != B * S or QKV.stride(1) != 1:
+        raise ValueError("QKV must be [B·S, ld] with unit column stride")
+    F = heads * ATTN_HEAD_DIM
+    if O is None:
+        O = torch.empty((B * S, F), dtype=torch.bfloat16, device=QKV.device)
+    _need(O, "O", torch.bfloat16, 2, contiguous=False)
+    if O.shape[0] != B * S or O.shape[1] < F or O.stride(1) != 1:
+        raise ValueError("O has the wrong shape")
+    _check(lib.tp_attn_heads(QKV.data_ptr(), QKV.stride(0), O.data_ptr(), O.stride(0), B, S, heads,
+                             int(bool(causal)), _stream(stream)), "tp_attn_heads")
+    return O
+
+
+def tp_attn_shard_workspace_size(M: int, d: int, N: int) -> int:
+    return int(lib.tp_attn_shard_workspace_size(M, d, N))
+
+
+def tp_attn_shard(X, Wqkv, Wo, B: int, S: int, heads: int, N: int, rank: int, causal: bool = True,
+                  Y_i=None, out_dtype=torch.float32, workspace=None, stream=None):
+    """Rank `rank`'s partial output of the N-way split attention block (W_qkv head-major [d, 3d])."""
+    _need(X, "X", torch.bfloat16, 2)
+    _need(Wqkv, "Wqkv", torch.bfloat16, 2)
+    _need(Wo, "Wo", torch.bfloat16, 2)
+    M, d = X.shape
+    if tuple(Wqkv.shape) != (d, 3 * d) or tuple(Wo.shape) != (d, d) or M != B * S:
+        raise ValueError(f"shape mismatch: X {tuple(X.shape)}, Wqkv {tuple(Wqkv.shape)}, "
+                         f"Wo {tuple(Wo.shape)}, B·S = {B * S}")
+    if Y_i is None:
+        Y_i = torch.empty((M, d), dtype=out_dtype, device=X.device)
+    _need(Y_i, "Y_i", None, 2)
+    if tuple(Y_i.shape) != (M, d):
+        raise ValueError("Y_i has the wrong shape")
+    need = tp_attn_shard_workspace_size(M, d, N) if N >= 1 else 0
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=X.device)
+    _need(workspace, "workspace", None)
+    _check(lib.tp_attn_shard(X.data_ptr(), Wqkv.data_ptr(), Wo.data_ptr(), Y_i.data_ptr(),
+                             _dtype_code(Y_i.dtype), B, S, d, heads, N, rank, int(bool(causal)),
+                             workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                             _stream(stream)), "tp_attn_shard")
+    return Y_i
+
+
+def attn_workspace_views(workspace, M: int, F: int):
+    """(QKV_i bf16 [M, 3F], O_i bf16 [M, F]) views of an attention-shard workspace."""
+    o1 = (6 * M * F + 255) // 256 * 256
+    QKV = workspace[: 6 * M * F].view(torch.bfloat16).view(M, 3 * F)
+    O = workspace[o1: o1 + 2 * M * F].view(torch.bfloat16).view(M, F)
+    return QKV, O

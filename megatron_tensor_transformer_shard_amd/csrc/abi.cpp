@@ -501,4 +501,93 @@ int tp_mlp_shard_backward(const void* X, const void* A, const void* B, const voi
   return status_of(e);
 }
 
+int tp_attn_qkv(const void* X, const void* W_i, int64_t ldw, void* QKV_i, int64_t M, int64_t d,
+                int64_t F3, void* stream) {
+  int st = check_dims(M, d, F3, 8);
+  if (st != TPM_OK) return st;
+  if (ldw < F3 || ldw > kMaxLd) return TPM_ERR_SHAPE;
+  if (M == 0) return TPM_OK;
+  if (!X || !W_i || !QKV_i) return TPM_ERR_NULL;
+  if (!aligned16(X) || !aligned16(W_i) || !aligned16(QKV_i) || ldw % 8 != 0) return TPM_ERR_ALIGN;
+  const Span q = mat_span(QKV_i, M, F3, F3, 2);
+  if (overlap(q, mat_span(X, M, d, d, 2)) || overlap(q, mat_span(W_i, d, F3, ldw, 2)))
+    return TPM_ERR_ALIAS;
+  return status_of(tpmlp::launch_gemm_bf16(static_cast<const uint16_t*>(X), d,
+                                           static_cast<const uint16_t*>(W_i), ldw, QKV_i, F3,
+                                           (int)M, (int)F3, (int)d, OutKind::Bf16,
+                                           as_stream(stream)));
+}
+
+int tp_attn_heads(const void* QKV, int64_t ld, void* O, int64_t ldo, int64_t B, int64_t S,
+                  int64_t heads, int causal, void* stream) {
+  if (B < 0 || S < 0 || heads < 1 || heads > 65536) return TPM_ERR_SHAPE;
+  if (ld < 3 * heads * TPM_ATTN_HEAD_DIM || ldo < heads * TPM_ATTN_HEAD_DIM) return TPM_ERR_SHAPE;
+  if (ld > kMaxLd || ldo > kMaxLd) return TPM_ERR_SHAPE;
+  // per-sequence byte offsets of the key/value loads are 32-bit
+  if (S > 0 && ((S - 1) * ld + ld) * 2 >= (int64_t(1) << 32)) return TPM_ERR_SHAPE;
+  const int64_t M = B * S;
+  if (M > kMaxDim || (M > 0 && ((M + 127) / 128) * heads > kMaxDim)) return TPM_ERR_SHAPE;
+  if (M == 0) return TPM_OK;
+  if (!QKV || !O) return TPM_ERR_NULL;
+  if (!aligned16(QKV) || !aligned16(O) || ld % 8 != 0 || ldo % 8 != 0) return TPM_ERR_ALIGN;
+  if (overlap(mat_span(O, M, heads * TPM_ATTN_HEAD_DIM, ldo, 2),
+              mat_span(QKV, M, 3 * heads * TPM_ATTN_HEAD_DIM, ld, 2)))
+    return TPM_ERR_ALIAS;
+  return status_of(tpmlp::launch_attention(static_cast<const uint16_t*>(QKV), ld,
+                                           static_cast<uint16_t*>(O), ldo, (int)B, (int)S,
+                                           (int)heads, causal != 0, as_stream(stream)));
+}
+
+size_t tp_attn_shard_workspace_size(int64_t M, int64_t d, int N) {
+  if (M < 0 || d <= 0 || N < 1 || d % N != 0 || M > kMaxDim) return 0;
+  const size_t mf = (size_t)M * (size_t)(d / N);
+  return round256(mf * 6) + round256(mf * 2);
+}
+
+int tp_attn_shard(const void* X, const void* Wqkv, const void* Wo, void* Y_i, int y_dtype,
+                  int64_t B, int64_t S, int64_t d, int64_t heads, int N, int rank, int causal,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+  if (y_dtype != TPM_F32 && y_dtype != TPM_BF16) return TPM_ERR_DTYPE;
+  if (N < 1 || rank < 0 || rank >= N) return TPM_ERR_ARG;
+  if (B < 0 || S < 0 || d <= 0 || heads < 1) return TPM_ERR_SHAPE;
+  if (d % heads != 0 || d / heads != TPM_ATTN_HEAD_DIM || heads % N != 0) return TPM_ERR_SHAPE;
+  const int64_t F = d / N, hr = heads / N, M = B * S;
+  int st = check_dims(M, d, 3 * F, 8);
+  if (st != TPM_OK) return st;
+  if (3 * d > kMaxLd || 3 * d * d > (int64_t(1) << 46)) return TPM_ERR_SHAPE;
+  if (S > 0 && S * 3 * F * 2 >= (int64_t(1) << 32)) return TPM_ERR_SHAPE;
+  if (M == 0) return TPM_OK;
+  if (!X || !Wqkv || !Wo || !Y_i) return TPM_ERR_NULL;
+  const size_t need = tp_attn_shard_workspace_size(M, d, N);
+  if (!workspace || workspace_bytes < need) return TPM_ERR_WORKSPACE;
+  if (!aligned16(X) || !aligned16(Wqkv) || !aligned16(Wo) || !aligned16(Y_i) ||
+      !aligned16(workspace))
+    return TPM_ERR_ALIGN;
+  const Span sy = mat_span(Y_i, M, d, d, y_dtype == TPM_F32 ? 4 : 2);
+  const Span sw = {reinterpret_cast<uintptr_t>(workspace),
+                   reinterpret_cast<uintptr_t>(workspace) + need};
+  const Span ins[3] = {mat_span(X, M, d, d, 2), mat_span(Wqkv, d, 3 * d, 3 * d, 2),
+                       mat_span(Wo, d, d, d, 2)};
+  for (const Span& in : ins)
+    if (overlap(sy, in) || overlap(sw, in)) return TPM_ERR_ALIAS;
+  if (overlap(sy, sw)) return TPM_ERR_ALIAS;
+
+  // Rank i's heads [i·hr, (i+1)·hr): columns [i·3F, (i+1)·3F) of the
+  // head-major W_qkv and rows [i·F, (i+1)·F) of W_o.
+  const uint16_t* W_i = static_cast<const uint16_t*>(Wqkv) + (int64_t)rank * 3 * F;
+  const uint16_t* Wo_i = static_cast<const uint16_t*>(Wo) + (int64_t)rank * F * d;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  uint16_t* QKV = reinterpret_cast<uint16_t*>(ws);
+  uint16_t* O = reinterpret_cast<uint16_t*>(ws + round256((size_t)M * F * 6));
+  hipStream_t s = as_stream(stream);
+  hipError_t e = tpmlp::launch_gemm_bf16(static_cast<const uint16_t*>(X), d, W_i, 3 * d, QKV,
+                                         3 * F, (int)M, (int)(3 * F), (int)d, OutKind::Bf16, s);
+  if (e == hipSuccess)
+    e = tpmlp::launch_attention(QKV, 3 * F, O, F, (int)B, (int)S, (int)hr, causal != 0, s);
+  if (e == hipSuccess)
+    e = tpmlp::launch_gemm_bf16(O, F, Wo_i, d, Y_i, d, (int)M, (int)d, (int)F,
+                                y_dtype == TPM_F32 ? OutKind::F32 : OutKind::Bf16, s);
+  return status_of(e);
+}
+
 }  // extern "C"

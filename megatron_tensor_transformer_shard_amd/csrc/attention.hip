@@ -1,0 +1,285 @@
+// Per-head attention of one tensor-parallel rank on gfx950 (flash-attention
+// style forward: scores, online softmax and the weighted sum of values per
+// block of keys, with nothing but the output written to HBM).
+//
+// Each rank owns whole heads and computes their attention with no exchange
+// ("Megatron-LM" glossary, tensor-parallel section; "Megatron architecture
+// and 6D parallel guide", §3.2: 32 heads at TP=8 give 4 per GPU). For
+// sequence b and head j: O = softmax(Q·Kᵀ/√dh, causal mask)·V.
+//
+// Layout. QKV [B·S, ld] bf16 (row b·S + t = token t of sequence b); local
+// head j's query, key and value columns are [3j·dh, 3j·dh + dh),
+// [.. + dh, .. + 2dh), [.. + 2dh, .. + 3dh). O [B·S, ldo] bf16, head j at
+// columns [j·dh, (j+1)·dh). dh = 128.
+//
+// Workgroup = 4 waves = one head of one sequence and a block of 128 queries;
+// wave w owns queries 32w .. 32w+31 of the block (two 16-row MFMA tiles).
+// Keys are taken in blocks of 64, double-buffered in LDS by
+// global_load_lds_dwordx4 (K 16 KB + V 16 KB per stage).
+//
+//  - Scores: D = K·Qᵀ with v_mfma_f32_16x16x32_bf16 (A = 16 keys x 32 dh of
+//    K, B = 32 dh x 16 queries of Q, the Q fragments held in registers for
+//    the whole kernel). A lane then holds, for its query (lane & 15), 4 keys
+//    of each 16-key tile. The K fragment rows are permuted: row i of key
+//    tile nt is key 32·(nt/2) + 8·(i/4) + 4·(nt%2) + i%4, so that across the
+//    tile pair (2c, 2c+1) lane group g = lane >> 4 holds keys
+//    32c + 8g .. 32c + 8g + 7, exactly the k slots of an MFMA B operand.
+//  - Softmax in the exp2 domain on the fp32 scores, online over key blocks
+//    (running max per query row reduced over the 4 lane groups with lane
+//    shuffles; the running sum kept per lane and reduced once at the end).
+//  - P·V: D = V'·P' with A = 16 dh x 32 keys of V (two transposing
+//    ds_read_b64_tr_b16 per lane from V rows stored as in HBM, granules
+//    rotated per row as in the GEMM engine's N-major operand) and B = the
+//    bf16-rounded probabilities straight from the score registers.
+//  - K rows (256 bytes, 16 chunks) store chunk c of key row r at position
+//    c ^ f(r), f(r) = (r & 3) | ((r >> 3) & 1) << 2 | ((r >> 4) & 1) << 3;
+//    for the permuted rows a 16-lane group reads, f(row) = lane & 15, so the
+//    16 reads of a group fall on 16 distinct 16-byte bank groups.
+#include "common.hpp"
+#include "kernels.hpp"
+#include "tile_engine.hpp"
+
+namespace tpmlp {
+namespace {
+
+using namespace engine;
+
+constexpr int kDh = 128;       // head width
+constexpr int kBQ = 128;       // queries per workgroup
+constexpr int kBKV = 64;       // keys per block
+constexpr int kThreads = 256;
+constexpr int kRowBytes = kDh * 2;                 // one K or V row in LDS
+constexpr int kStageBytes = kBKV * kRowBytes;      // 16 KB
+constexpr int kGranules = kStageBytes / 16;        // 1024 per K or V stage
+constexpr int kRounds = kGranules / kThreads;      // 4 DMA instructions per wave
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+__device__ __forceinline__ int k_swz(int r) {
+  return (r & 3) | (((r >> 3) & 1) << 2) | (((r >> 4) & 1) << 3);
+}
+
+// Granule rotation of V row r (16 granules per row), as the GEMM engine's
+// N-major operand with 256-byte rows.
+__device__ __forceinline__ int v_rot(int r) { return 2 * (r & 3) + 8 * ((r >> 3) & 1); }
+
+__device__ __forceinline__ float wave_max4(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  return fmaxf(v, __shfl_xor(v, 32));
+}
+
+__device__ __forceinline__ float wave_sum4(float v) {
+  v += __shfl_xor(v, 16);
+  return v + __shfl_xor(v, 32);
+}
+
+template <bool CAUSAL>
+__global__ __launch_bounds__(kThreads) void attn_fwd_kernel(const uint16_t* __restrict__ QKV,
+                                                            int64_t ld, uint16_t* __restrict__ O,
+                                                            int64_t ldo, int B, int S, int heads,
+                                                            float scale_log2) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * kStageBytes];  // K0 K1 V0 V1
+
+  const int nqb = (S + kBQ - 1) / kBQ;
+  const int bh_count = B * heads;
+  const int bid = blockIdx.x;
+  // longest query blocks first (with the causal mask later blocks see more keys)
+  const int qb = CAUSAL ? nqb - 1 - bid / bh_count : bid / bh_count;
+  const int bh = bid % bh_count;
+  const int b = bh / heads, j = bh % heads;
+
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int g = lane >> 4, L = lane & 15;
+
+  const uint16_t* seq = QKV + (int64_t)b * S * ld;   // row 0 of the sequence
+  const int qcol = 3 * j * kDh, kcol = qcol + kDh, vcol = qcol + 2 * kDh;
+  const int q0w = qb * kBQ + 32 * wave;              // first query of this wave
+
+  // Q fragments: query q0w + 16mi + L, dh 32s + 8g .. +7 (clamped rows beyond S).
+  s16x8 qf[2][4];
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi) {
+    const int q = min(q0w + 16 * mi + L, S - 1);
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      qf[mi][s] = *reinterpret_cast<const s16x8*>(seq + (int64_t)q * ld + qcol + 32 * s + 8 * g);
+  }
+
+  const int last_key = CAUSAL ? min(S - 1, qb * kBQ + kBQ - 1) : S - 1;
+  const int nkb = last_key / kBKV + 1;
+
+  // DMA of key block kb into stage st: granule pos = (round·4 + wave)·64 + lane.
+  const uint32_t lds0 = lds_addr(smem) + wave * 1024;
+  auto issue = [&](int kb, int st) {
+    const int kv0 = kb * kBKV;
+#pragma unroll
+    for (int r = 0; r < kRounds; ++r) {
+      const int pos = (r * 4 + wave) * 64 + lane;
+      const int row = pos >> 4, p = pos & 15;
+      const int key = min(kv0 + row, S - 1);
+      const uint32_t kc = (uint32_t)(((int64_t)key * ld + kcol + (p ^ k_swz(row)) * 8) * 2);
+      const uint32_t vc =
+          (uint32_t)(((int64_t)key * ld + vcol + ((p + 16 - v_rot(row)) & 15) * 8) * 2);
+      dma16(seq, kc, lds0 + st * kStageBytes + r * 4096);
+      dma16(seq, vc, lds0 + (2 + st) * kStageBytes + r * 4096);
+    }
+  };
+
+  // Fragment addressing (lane parts).
+  // K: row 8·(L>>2) + (L&3) (+ 32c + 4e per tile), chunk (4s + g) ^ L.
+  const int k_row = 8 * (L >> 2) + (L & 3);
+  // V: as the GEMM engine's A operand from an N-major stage of 128 columns.
+  const int rsub = 8 * g + (L >> 2);
+  int v_addr[8];
+#pragma unroll
+  for (int nd = 0; nd < 8; ++nd)
+    v_addr[nd] = rsub * kRowBytes + ((((16 * nd + 4 * (lane & 3)) >> 3) + v_rot(rsub)) & 15) * 16 +
+                 8 * (lane & 1);
+
+  f32x4 o[8][2];
+#pragma unroll
+  for (int nd = 0; nd < 8; ++nd)
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi) o[nd][mi] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[2] = {-INFINITY, -INFINITY};  // running max (log2 domain) of the lane's rows
+  float l_run[2] = {0.f, 0.f};              // running sum of this lane's probabilities
+
+  issue(0, 0);
+  for (int kb = 0; kb < nkb; ++kb) {
+    const int st = kb & 1;
+    waitcnt<0, 0>();
+    barrier();  // block kb is in LDS; every wave is done with block kb-1
+    if (kb + 1 < nkb) issue(kb + 1, st ^ 1);
+    const int kv0 = kb * kBKV;
+    // with the causal mask a wave whose queries all precede the block skips it
+    if (CAUSAL && kv0 > q0w + 31) continue;
+
+    const uint8_t* sk = smem + st * kStageBytes;
+    const uint8_t* sv = smem + (2 + st) * kStageBytes;
+
+    // scores
+    f32x4 sc[4][2];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int mi = 0; mi < 2; ++mi) sc[nt][mi] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const int row = k_row + 32 * (nt >> 1) + 4 * (nt & 1);
+        const s16x8 kf =
+            *reinterpret_cast<const s16x8*>(sk + row * kRowBytes + (((4 * s + g) ^ L) * 16));
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+          sc[nt][mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, kf), __builtin_bit_cast(bf16x8, qf[mi][s]), sc[nt][mi],
+              0, 0, 0);
+      }
+    }
+
+    // online softmax; element (nt, r) of row mi is key kv0 + 32(nt/2) + 8g + 4(nt%2) + r
+    const bool need_mask = (CAUSAL && kv0 + kBKV - 1 > q0w) || kv0 + kBKV > S;
+    s16x8 pf[2][2];
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi) {
+      const int q = q0w + 16 * mi + L;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float v = sc[nt][mi][r] * scale_log2;
+          if (need_mask) {
+            const int key = kv0 + 32 * (nt >> 1) + 8 * g + 4 * (nt & 1) + r;
+            if (key >= S || (CAUSAL && key > q)) v = -INFINITY;
+          }
+          sc[nt][mi][r] = v;
+          mx = fmaxf(mx, v);
+        }
+      mx = wave_max4(mx);
+      const float m_new = fmaxf(m_run[mi], mx);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run[mi] - m_use);
+      m_run[mi] = m_new;
+      float ls = 0.f;
+      uint32_t pk[4][2];
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        float pv[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          pv[r] = __builtin_amdgcn_exp2f(sc[nt][mi][r] - m_use);
+          ls += pv[r];
+        }
+        pk[nt][0] = pack_bf16x2(pv[0], pv[1]);
+        pk[nt][1] = pack_bf16x2(pv[2], pv[3]);
+      }
+      l_run[mi] = l_run[mi] * alpha + ls;
+#pragma unroll
+      for (int nd = 0; nd < 8; ++nd) o[nd][mi] *= alpha;
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const u32x4 w = {pk[2 * c][0], pk[2 * c][1], pk[2 * c + 1][0], pk[2 * c + 1][1]};
+        pf[mi][c] = __builtin_bit_cast(s16x8, w);
+      }
+    }
+
+    // O += P·V
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+#pragma unroll
+      for (int nd = 0; nd < 8; ++nd) {
+        s16x8 vf;
+        vf.lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4*)(sv + v_addr[nd] + (32 * c) * kRowBytes));
+        vf.hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_s16x4*)(sv + v_addr[nd] + (32 * c + 4) * kRowBytes));
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+          o[nd][mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, vf), __builtin_bit_cast(bf16x8, pf[mi][c]), o[nd][mi],
+              0, 0, 0);
+      }
+    }
+  }
+  waitcnt<0, 0>();
+
+  // O = acc / l; lane holds O[query q][dh 16nd + 4g .. +3]
+#pragma unroll
+  for (int mi = 0; mi < 2; ++mi) {
+    const int q = q0w + 16 * mi + L;
+    const float inv = 1.0f / wave_sum4(l_run[mi]);
+    if (q >= S) continue;
+    uint16_t* orow = O + ((int64_t)b * S + q) * ldo + j * kDh;
+#pragma unroll
+    for (int nd = 0; nd < 8; ++nd) {
+      const f32x4 v = o[nd][mi] * inv;
+      const u32x2 w = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+      *reinterpret_cast<u32x2*>(orow + 16 * nd + 4 * g) = w;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attention(const uint16_t* QKV, int64_t ld, uint16_t* O, int64_t ldo, int B,
+                            int S, int heads, bool causal, hipStream_t stream) {
+  if (B == 0 || S == 0 || heads == 0) return hipSuccess;
+  const int nqb = (S + kBQ - 1) / kBQ;
+  const dim3 grid(nqb * B * heads);
+  const float scale_log2 = 1.4426950408889634f / sqrtf((float)kDh);
+  if (causal)
+    hipLaunchKernelGGL(attn_fwd_kernel<true>, grid, dim3(kThreads), 0, stream, QKV, ld, O, ldo, B,
+                       S, heads, scale_log2);
+  else
+    hipLaunchKernelGGL(attn_fwd_kernel<false>, grid, dim3(kThreads), 0, stream, QKV, ld, O, ldo,
+                       B, S, heads, scale_log2);
+  return hipGetLastError();
+}
+
+}  // namespace tpmlp

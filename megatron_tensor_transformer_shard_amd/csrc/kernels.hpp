@@ -42,6 +42,12 @@ struct BfGemm {
 hipError_t launch_gemm_bf16_pair(const BfGemm& x, const BfGemm& y, OutKind out, Layout lay,
                                  hipStream_t stream);
 
+// Per-head causal (or full) softmax attention of one rank, head width 128:
+// QKV [B·S, ld] bf16 with head j's Q, K, V at columns 3j·128 + {0, 128, 256};
+// O [B·S, ldo] bf16 with head j at columns j·128.
+hipError_t launch_attention(const uint16_t* QKV, int64_t ld, uint16_t* O, int64_t ldo, int B,
+                            int S, int heads, bool causal, hipStream_t stream);
+
 // Y = Σ_i parts[i] in rank order, fp32 accumulation, then + bias[e % d] when
 // bias_kind is 1 (fp32 bias) or 2 (bf16 bias); bias_kind 0 adds nothing.
 hipError_t launch_partial_sum(const void* const* parts, int nparts, bool parts_bf16, void* Y,

@@ -261,6 +261,42 @@ def test_backward_validation():
     assert bw(dB=BASE + GB + 1024) == EALIAS       # dB_i inside A
 
 
+def test_attention_validation():
+    # tp_attn_heads
+    def heads(QKV=BASE, ld=3 * 256, O=BASE + GB, ldo=256, B=2, S=40, h=2, causal=1):
+        return L.tp_attn_heads(QKV, ld, O, ldo, B, S, h, causal, None)
+    assert heads(B=0) == OK
+    assert heads(S=0) == OK
+    assert heads(h=0) == ESHAPE
+    assert heads(ld=3 * 256 - 8) == ESHAPE           # too narrow for 2 heads' Q, K, V
+    assert heads(ldo=128) == ESHAPE
+    assert heads(ld=3 * 256 + 4) == EALIGN
+    assert heads(QKV=None) == ENULL
+    assert heads(O=BASE + 8) == EALIGN
+    assert heads(O=BASE + 1024) == EALIAS             # O inside QKV
+    assert heads(S=1 << 20, ld=3 << 12) == ESHAPE     # 32-bit per-sequence offsets
+    # tp_attn_qkv
+    assert L.tp_attn_qkv(BASE, BASE + GB, 1000, BASE + 2 * GB, 80, 1024, 1536, None) == ESHAPE
+    assert L.tp_attn_qkv(BASE, BASE + GB, 1536, BASE + 16, 80, 1024, 1536, None) == EALIAS
+    # tp_attn_shard
+    ws = L.tp_attn_shard_workspace_size(80, 1024, 2)
+    assert ws == 80 * 512 * 6 + 80 * 512 * 2
+    assert L.tp_attn_shard_workspace_size(80, 1024, 3) == 0
+
+    def sh(yd=F32, B=2, S=40, d=1024, h=8, N=2, rank=1, wsp=BASE + 4 * GB, wsb=ws, Y=BASE + 3 * GB):
+        return L.tp_attn_shard(BASE, BASE + GB, BASE + 2 * GB, Y, yd, B, S, d, h, N, rank, 1,
+                               wsp, wsb, None)
+    assert sh(B=0) == OK
+    assert sh(yd=E4M3) == EDTYPE
+    assert sh(rank=2) == EARG
+    assert sh(h=16) == ESHAPE                         # head width 64
+    assert sh(h=8, N=16, rank=0) == ESHAPE            # N does not divide the heads
+    assert sh(wsp=None) == EWS
+    assert sh(wsb=ws - 1) == EWS
+    assert sh(Y=BASE + GB + 64) == EALIAS             # Y inside W_qkv
+    assert sh(wsp=BASE + 3 * GB) == EALIAS            # workspace is Y
+
+
 def test_python_wrapper_rejects_cpu_tensors():
     import torch
     X = torch.zeros(4, 8, dtype=torch.bfloat16)
