@@ -16,7 +16,9 @@ row GEMM; inputs quantised once, outside the timed region) and
 with the predicted scale + amax, row GEMM, amax history push) and 7b_tp8_bwd
 (the backward of every rank's 7b_tp8 shard for an output gradient dY: one
 tp_mlp_shard_backward call per rank, five GEMMs, then the sum of the ranks'
-input gradients dX_i).
+input gradients dX_i) and 7b_tp8_attn (the attention block: every rank's
+QKV projection, causal attention of its 4 heads and output projection, then
+the sum of the partials).
 
 Prints one JSON line. `value` is TFLOP/s over the whole step (FLOPs =
 4·M·d·F per rank shard forward, 10·M·d·F backward; GeLU, GeLU', scaling and
@@ -48,6 +50,9 @@ os.environ.setdefault("OPENBLAS_NUM_THREADS", str(HOST_CORES))
 import numpy as np  # noqa: E402
 
 METRIC = "TFLOP/s and % of MFMA peak per TP-rank MLP shard (GeLU(X·A_i)·B_i), 1 GPU"
+METRIC_BWD = "TFLOP/s and % of MFMA peak per TP-rank MLP shard backward (dX_i, dA_i, dB_i), 1 GPU"
+METRIC_ATTN = ("TFLOP/s and % of MFMA peak per TP-rank attention shard (QKV projection, causal "
+               "attention, output projection), 1 GPU")
 PEAK_TFLOPS = {"bf16": 2516.6, "e4m3": 5033.2}   # MI355X dense MFMA (256 CU x 2.4 GHz)
 HBM_PEAK_GBS = 8000.0
 
@@ -88,7 +93,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="7b_tp8",
                    help="7b_tp8 (default), gpt2s_n1, 175b_tp8, 175b_tp8_e4m3, 175b_tp8_e4m3_delayed, "
-                        "7b_tp8_bwd, "
+                        "7b_tp8_bwd, 7b_tp8_attn, "
                         "or copy (a "
                         "1-part tp_partial_sum over 256 MiB of fp32: the known-size copy that "
                         "calibrates rocprofv3's FETCH_SIZE / WRITE_SIZE)")
@@ -202,6 +207,47 @@ def build_bwd_step(tpm, wl):
     return step, kern_flops, kern_bytes, psum_bytes, (X, A, B, dY), (dX if N > 1 else dXs[0])
 
 
+def build_attn_step(tpm, wl):
+    """Attention block of every rank: QKV projection, per-head attention,
+    output projection (the three launches tp_attn_shard makes), then Σ_i Y_i."""
+    import torch
+    from workloads import make_attn_inputs
+    X, Wqkv, Wo = make_attn_inputs(wl)
+    Xd, Wd, Wod = dev_bf16(X), dev_bf16(Wqkv), dev_bf16(Wo)
+    M, d, N, F, B, S = wl.M, wl.d, wl.N, wl.F, wl.B, wl.S
+    hr = wl.heads // N
+    QKV = torch.empty((M, 3 * F), dtype=torch.bfloat16, device="cuda")
+    O = torch.empty((M, F), dtype=torch.bfloat16, device="cuda")
+    parts = [torch.empty((M, d), dtype=torch.float32, device="cuda") for _ in range(N)]
+    Y = torch.empty((M, d), dtype=torch.float32, device="cuda")
+    views = [(Wd[:, r * 3 * F:(r + 1) * 3 * F], Wod[r * F:(r + 1) * F, :]) for r in range(N)]
+
+    def step(timer=None):
+        for r in range(N):
+            W_i, Wo_i = views[r]
+            calls = [("qkv_proj", lambda: tpm.tp_attn_qkv(Xd, W_i, QKV)),
+                     ("attention", lambda: tpm.tp_attn_heads(QKV, B, S, hr, wl.causal, O)),
+                     ("out_proj", lambda: tpm.tp_mlp_row_partial(O, Wo_i, parts[r]))]
+            for name, fn in calls:
+                if timer is None:
+                    fn()
+                else:
+                    timer.around(name, fn)
+        if N > 1:
+            if timer is None:
+                tpm.tp_partial_sum(parts, Y=Y)
+            else:
+                timer.around("partial_sum", lambda: tpm.tp_partial_sum(parts, Y=Y))
+
+    att = 4 * S * S * wl.dh * hr * B // (2 if wl.causal else 1)
+    kern_flops = {"qkv_proj": 2 * M * d * 3 * F, "attention": att, "out_proj": 2 * M * F * d}
+    kern_bytes = {"qkv_proj": (M * d + d * 3 * F) * 2 + M * 3 * F * 2,
+                  "attention": M * 3 * F * 2 + M * F * 2,
+                  "out_proj": (M * F + F * d) * 2 + M * d * 4}
+    psum_bytes = (N + 1) * 4 * M * d
+    return step, kern_flops, kern_bytes, psum_bytes, (X, Wqkv, Wo), (Y if N > 1 else parts[0])
+
+
 def build_e4m3_step(tpm, wl):
     import torch
     X, A, B = __import__("workloads").make_inputs(wl)
@@ -257,9 +303,35 @@ def build_e4m3_step(tpm, wl):
     return step, kern_flops, kern_bytes, 0, (X, A, B), Y
 
 
+def cpu_baseline_attn(wl, inputs, budget_s):
+    """Time the oracle's attention shard on whole sequences (all ranks + sum)
+    until the budget is spent; FLOPs counted as the GPU's are."""
+    import oracle
+    from oracle import attention as oat
+    X, Wqkv, Wo = inputs
+    done = 0
+    t_total = 0.0
+    while done < wl.B and t_total < budget_s:
+        rows = slice(done * wl.S, (done + 1) * wl.S)
+        t0 = time.perf_counter()
+        parts = [oat.attn_shard(X[rows], Wqkv, Wo, wl.N, r, 1, wl.S, wl.heads, wl.causal)
+                 for r in range(wl.N)]
+        if wl.N > 1:
+            oracle.partial_sum(parts)
+        t_total += time.perf_counter() - t0
+        done += 1
+    flops = wl.N * wl.flops_per_shard() * done // wl.B
+    what = (f"sequences [0, {done}) of {wl.B} of the {wl.name} step (all {wl.N} ranks + sum), "
+            f"float64 numpy/OpenBLAS oracle, {t_total:.2f} s")
+    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": HOST_CORES,
+            "kind": "oracle", "sample": what, "seconds": t_total}
+
+
 def cpu_baseline(wl, inputs, budget_s):
     """Time the oracle as it stands on row chunks of the same step until the budget is spent."""
     import oracle
+    if hasattr(wl, "heads"):
+        return cpu_baseline_attn(wl, inputs, budget_s)
     X, A, B = inputs[:3]
     chunk = max(1, min(wl.M, 1024))
     if wl.fp8:   # input quantisation is preparation (outside the GPU's timed step too)
@@ -298,6 +370,16 @@ def sampled_check(wl, inputs, out, nrows=8):
     import torch
     import oracle
     from workloads import sample_rows
+    if hasattr(wl, "heads"):   # causal: a prefix of sequence 0 depends on nothing after it
+        from oracle import attention as oat
+        X, Wqkv, Wo = inputs
+        T = min(wl.S, 256)
+        rows = sample_rows(T, nrows)
+        got = out[torch.from_numpy(rows).cuda()].double().cpu().numpy()
+        ref = oat.attn_unsharded(X[:T], Wqkv, Wo, 1, T, wl.heads, wl.causal)[rows]
+        if not wl.causal:
+            return None
+        return float(np.max(np.abs(got - ref)) / np.max(np.abs(ref)))
     X, A, B = inputs[:3]
     rows = sample_rows(wl.M, nrows)
     got = out[torch.from_numpy(rows).cuda()].double().cpu().numpy()
@@ -348,10 +430,14 @@ def main():
     if args.workload == "copy":
         copy_calibration(tpm, args)
         return
-    wl = WORKLOADS[args.workload]
-    dtype = "e4m3" if wl.fp8 else "bf16"
+    from workloads import ATTN_WORKLOADS
+    wl = WORKLOADS[args.workload] if args.workload in WORKLOADS else ATTN_WORKLOADS[args.workload]
+    attn = args.workload in ATTN_WORKLOADS
+    dtype = "e4m3" if getattr(wl, "fp8", False) else "bf16"
     log(f"bench: workload {wl.name}: {wl.description}")
-    if wl.fp8:
+    if attn:
+        step, kern_flops, kern_bytes, psum_bytes, inputs, out = build_attn_step(tpm, wl)
+    elif wl.fp8:
         step, kern_flops, kern_bytes, psum_bytes, inputs, out = build_e4m3_step(tpm, wl)
     elif wl.backward:
         step, kern_flops, kern_bytes, psum_bytes, inputs, out = build_bwd_step(tpm, wl)
@@ -386,8 +472,12 @@ def main():
     for name, fl in kern_flops.items():
         kstats[name]["tflops"] = fl / (kstats[name]["avg_us"] * 1e-6) / 1e12
         kstats[name]["frac_of_peak"] = kstats[name]["tflops"] / peak
+        kstats[name]["algorithmic_bytes"] = kern_bytes[name]
+        kstats[name]["traffic"] = measured_traffic(wl.name, name)
     if "partial_sum" in kstats:
         kstats["partial_sum"]["GBps"] = psum_bytes / (kstats["partial_sum"]["avg_us"] * 1e-6) / 1e9
+        kstats["partial_sum"]["algorithmic_bytes"] = psum_bytes
+        kstats["partial_sum"]["traffic"] = measured_traffic(wl.name, "partial_sum")
     dom = max(kern_flops, key=lambda k: kstats[k]["total_ms"])
     ach = kstats[dom]["tflops"]
     roofline = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2), "peak": peak,
@@ -407,14 +497,20 @@ def main():
             4096 if dtype == "bf16" else 8192) / 1e12
 
     result = {
-        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "metric": (METRIC_ATTN if attn else METRIC_BWD if getattr(wl, "backward", False)
+                   else METRIC),
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
         "data": "synthetic: seeded X~N(0,1), weights~N(0,sigma^2), bf16 (no trained weights)",
-        "config": {"workload": wl.name, "M": wl.M, "d": wl.d, "F": wl.F, "tp_ranks": wl.N,
-                   "partial_dtype": "bf16" if wl.fp8 else ("f32" if wl.backward
-                                                            else args.partial_dtype),
-                   "parallelism": f"tp{wl.N} ranks sequentially on 1 GPU" if wl.N > 1 else "none"},
+        "config": ({"workload": wl.name, "B": wl.B, "S": wl.S, "d": wl.d, "heads": wl.heads,
+                    "head_dim": wl.dh, "causal": wl.causal, "tp_ranks": wl.N,
+                    "partial_dtype": "f32",
+                    "parallelism": f"tp{wl.N} ranks sequentially on 1 GPU"} if attn else
+                   {"workload": wl.name, "M": wl.M, "d": wl.d, "F": wl.F, "tp_ranks": wl.N,
+                    "partial_dtype": "bf16" if wl.fp8 else ("f32" if wl.backward
+                                                             else args.partial_dtype),
+                    "parallelism": f"tp{wl.N} ranks sequentially on 1 GPU" if wl.N > 1 else "none"}),
         "pct_of_peak": round(100 * value / peak, 2),
         "roofline": roofline,
         "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()}

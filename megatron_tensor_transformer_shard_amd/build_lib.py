@@ -36,6 +36,12 @@ CFLAGS = [
     "-mllvm", "-pragma-unroll-threshold=1000000",
 ]
 
+# Per-source flags. The attention kernel rescales its fp32 output accumulators
+# with VALU multiplies after every key block; MFMAs in the VGPR form keep them
+# in VGPRs, where the accumulator-register form would copy all of them out of
+# and back into AGPRs each time.
+SOURCE_FLAGS = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
 
 def _hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
@@ -66,7 +72,8 @@ def build(verbose: bool = False, extra_flags=None, jobs: int = 4) -> str:
         obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
         lang = ["-x", "hip"]
-        cmds.append([hipcc, *lang, *flags, "-I", CSRC, "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([hipcc, *lang, *flags, *SOURCE_FLAGS.get(src, []), "-I", CSRC, "-c",
+                     os.path.join(CSRC, src), "-o", obj])
     with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
     tmp = LIB_PATH + ".tmp"
