@@ -199,7 +199,6 @@ __global__ __launch_bounds__(64 * SPLIT * kBQ / (16 * MT)) void attn_fwd_kernel(
 
     const uint8_t* sk = smem + (kst0 + st) * kStageBytes;
     const uint8_t* sv = smem + (vst0 + st) * kStageBytes;
-
     // scores
     f32x4 sc[4][MT];
 #pragma unroll
@@ -221,25 +220,29 @@ __global__ __launch_bounds__(64 * SPLIT * kBQ / (16 * MT)) void attn_fwd_kernel(
       }
     }
 
-    // online softmax; element (nt, r) of row mi is key kv0 + 32(nt/2) + 8g + 4(nt%2) + r.
-    // The running max m (log2 domain) is raised lazily: only when some row's
-    // block max exceeds it by more than kLazy are O and the sums rescaled, so
-    // the probabilities exp2(s·c − m) stay below 2^kLazy and most blocks cost
-    // one FMA, one exp2 and one add per score.
-    const bool need_mask = (CAUSAL && kv0 + kBKV - 1 > q0w) || kv0 + kBKV > S;
-    s16x8 pf[MT][2];
+    // Mask (diagonal blocks and the ragged tail only; a wave-uniform branch):
+    // element (nt, r) of row mi is key kv0 + 8g + 32(nt/2) + 4(nt%2) + r, and
+    // visible keys are <= min(query, S - 1).
+    if ((CAUSAL && kv0 + kBKV - 1 > q0w) || kv0 + kBKV > S) {
 #pragma unroll
-    for (int mi = 0; mi < MT; ++mi) {
-      if (need_mask) {
+      for (int mi = 0; mi < MT; ++mi) {
         const int q = q0w + 16 * mi + L;
+        const int lim = (CAUSAL ? min(q, S - 1) : S - 1) - kv0 - 8 * g;
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int key = kv0 + 32 * (nt >> 1) + 8 * g + 4 * (nt & 1) + r;
-            if (key >= S || (CAUSAL && key > q)) sc[nt][mi][r] = -INFINITY;
-          }
+          for (int r = 0; r < 4; ++r)
+            if (32 * (nt >> 1) + 4 * (nt & 1) + r > lim) sc[nt][mi][r] = -INFINITY;
       }
+    }
+
+    // online softmax. The running max m (log2 domain) is raised lazily: only
+    // when some row's block max exceeds it by more than kLazy are O and the
+    // sums rescaled, so the probabilities exp2(s·c − m) stay below 2^kLazy
+    // and most blocks cost one FMA, one exp2 and one add per score.
+    s16x8 pf[MT][2];
+#pragma unroll
+    for (int mi = 0; mi < MT; ++mi) {
       float mx = -INFINITY;  // the scale is positive: take the max of the raw scores
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt)
