@@ -93,7 +93,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="7b_tp8",
                    help="7b_tp8 (default), gpt2s_n1, 175b_tp8, 175b_tp8_e4m3, 175b_tp8_e4m3_delayed, "
-                        "7b_tp8_bwd, 7b_tp8_attn, "
+                        "7b_tp8_bwd, 7b_tp8_attn, library_compare (the 7B-class column GEMM "
+                        "against torch.matmul on the same data), "
                         "or copy (a "
                         "1-part tp_partial_sum over 256 MiB of fp32: the known-size copy that "
                         "calibrates rocprofv3's FETCH_SIZE / WRITE_SIZE)")
@@ -394,6 +395,38 @@ def sampled_check(wl, inputs, out, nrows=8):
     return float(np.max(np.abs(got - ref)) / np.max(np.abs(ref)))
 
 
+def library_compare(tpm, args):
+    """The 7B-class column GEMM (X[8192x4096] · A_i[4096x2048], bf16) three ways on the same
+    data: tp_mlp_col_gelu (fused GeLU), and the vendor library through torch.matmul with
+    B N-contiguous (NN, the math layout) and K-contiguous (NT, B stored transposed), neither
+    with an activation. Prints one JSON line of HIP-event averages; a counter profile of this
+    run compares the kernels' instruction mixes."""
+    import torch
+    M, K, N = 8192, 4096, 2048
+    g = torch.Generator(device="cuda").manual_seed(0)
+    a = torch.randn(M, K, device="cuda", dtype=torch.bfloat16, generator=g)
+    b = (torch.randn(K, N, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+    bt = b.t().contiguous().t()
+    z = torch.empty(M, N, device="cuda", dtype=torch.bfloat16)
+    calls = {"library_nt": lambda: a @ bt, "library_nn": lambda: a @ b,
+             "col_gelu": lambda: tpm.tp_mlp_col_gelu(a, b, z)}
+    for _ in range(args.warmup):
+        for fn in calls.values():
+            fn()
+    torch.cuda.synchronize()
+    timer = KernelTimer()
+    for _ in range(args.steps):
+        for name, fn in calls.items():
+            timer.around(name, fn)
+    torch.cuda.synchronize()
+    st = timer.summary()
+    fl = 2 * M * N * K
+    print(json.dumps({"workload": "library_compare", "shape": [M, K, N],
+                      "kernels": {k: {"avg_us": round(v["avg_us"], 2),
+                                      "tflops": round(fl / (v["avg_us"] * 1e-6) / 1e12, 1)}
+                                  for k, v in st.items()}}), flush=True)
+
+
 def copy_calibration(tpm, args):
     """Y = parts[0] over 64 Mi fp32 elements: 256 MiB read, 256 MiB written per launch."""
     import torch
@@ -429,6 +462,9 @@ def main():
         sys.exit(1)
     if args.workload == "copy":
         copy_calibration(tpm, args)
+        return
+    if args.workload == "library_compare":
+        library_compare(tpm, args)
         return
     from workloads import ATTN_WORKLOADS
     wl = WORKLOADS[args.workload] if args.workload in WORKLOADS else ATTN_WORKLOADS[args.workload]
