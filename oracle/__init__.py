@@ -28,6 +28,9 @@ What it computes, and where the pages define it:
   "Megatron architecture and 6D parallel guide", §3.2): the heads split over
   the ranks, column-parallel QKV projection, per-head softmax attention, and
   the row-parallel output projection whose partials sum to the block output.
+* fp8 backward in the hybrid formats ("Megatron-LM deep architecture", FP8
+  hybrid precision section): E4M3 for activations and weights, E5M2 for the
+  gradients, each with its own amax scale.
 * Backward of the shard: the chain rule through the forward as computed,
   dZ = dY·B_iᵀ, dS = bf16(dZ ⊙ GeLU'(S)), dX_i = dS·A_iᵀ, dA_i = Xᵀ·dS,
   dB_i = Z_iᵀ·dY; the ranks' dX_i sum to the input gradient (the backward
@@ -42,16 +45,20 @@ the path to an elementwise GeLU, textbook values of the normal CDF, and
 exhaustive codec checks against torch's CPU conversions.
 """
 from . import attention
-from .codecs import (bf16_decode, bf16_encode, e4m3_decode, e4m3_encode, E4M3_MAX)
+from .codecs import (bf16_decode, bf16_encode, e4m3_decode, e4m3_encode, e5m2_decode,
+                     e5m2_encode, E4M3_MAX, E5M2_MAX)
 from .mlp import (shard_columns, gelu, col_gelu, row_partial, mlp_shard, partial_sum,
                   sp_rows, partial_sum_rows, reduce_scatter_share, mlp_unsharded, amax,
                   quant_scale, quant_e4m3, col_gelu_e4m3, requant_z, row_partial_e4m3,
                   mlp_shard_e4m3, quantize_inputs_e4m3, delayed_scale, amax_history_push,
                   col_gelu_e4m3_delayed, mlp_shard_e4m3_delayed, gelu_grad,
-                  mlp_shard_backward)
+                  mlp_shard_backward, quant_scale_e5m2, quant_e5m2, quantize_e5m2,
+                  mlp_shard_backward_fp8)
 
 __all__ = [
     "bf16_decode", "bf16_encode", "e4m3_decode", "e4m3_encode", "E4M3_MAX",
+    "e5m2_decode", "e5m2_encode", "E5M2_MAX", "quant_scale_e5m2", "quant_e5m2", "quantize_e5m2",
+    "mlp_shard_backward_fp8",
     "shard_columns", "gelu", "col_gelu", "row_partial", "mlp_shard", "partial_sum",
     "sp_rows", "partial_sum_rows", "reduce_scatter_share", "mlp_unsharded", "amax",
     "quant_scale", "quant_e4m3", "col_gelu_e4m3", "requant_z", "row_partial_e4m3",

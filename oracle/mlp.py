@@ -15,7 +15,8 @@ from __future__ import annotations
 import numpy as np
 from scipy.special import erfc
 
-from .codecs import bf16_decode, bf16_encode, e4m3_decode, e4m3_encode, E4M3_MAX
+from .codecs import (bf16_decode, bf16_encode, e4m3_decode, e4m3_encode, e5m2_decode,
+                     e5m2_encode, E4M3_MAX, E5M2_MAX)
 
 _INV_SQRT2 = 0.7071067811865476  # 1/√2 rounded to float64
 
@@ -319,3 +320,70 @@ def mlp_shard_backward(X_bits, A_bits, B_bits, dY_bits, N: int, rank: int, round
         Z, dSv = G, dS
     return {"S": S, "Z": Z, "Z_bits": Z_bits, "dZ": dZ, "dS": dSv, "dS_bits": dS_bits,
             "dX": dSv @ A_i.T, "dA": X.T @ dSv, "dB": Z.T @ dY}
+
+
+# ----------------------------------------------------------------------------
+# fp8 backward, hybrid formats ("Megatron-LM deep architecture", FP8 hybrid
+# precision section: E4M3 for the forward's activations and weights, E5M2,
+# with its wider range, for the gradients of the backward pass).  Every
+# tensor is quantised with its own current amax scale (448/amax for e4m3,
+# 57344/amax for e5m2, fp32 divisions): X, A and B over the whole tensor as
+# in the fp8 forward, dY, and the two tensors the backward produces on the
+# way, dS (e5m2) and Z (e4m3, the bf16 Z of the recomputed forward).  Each
+# GEMM of two quantised operands is divided by the product of their scales.
+# ----------------------------------------------------------------------------
+
+def quant_scale_e5m2(a: float) -> np.float32:
+    """Per-tensor scale s = 57344/amax, an fp32 division (1 if amax = 0)."""
+    if a == 0.0:
+        return np.float32(1.0)
+    return np.float32(np.float32(E5M2_MAX) / np.float32(a))
+
+
+def quant_e5m2(T_bits: np.ndarray, s: np.float32) -> np.ndarray:
+    """e5m2 codes of T·s: the product in fp32 (RNE), clamped to ±57344, then
+    rounded once to e5m2 (RNE)."""
+    t32 = bf16_decode(T_bits).astype(np.float32)
+    v = (t32 * np.float32(s)).astype(np.float32)
+    v = np.clip(v, -E5M2_MAX, E5M2_MAX)
+    return e5m2_encode(v.astype(np.float64))
+
+
+def quantize_e5m2(T_bits: np.ndarray):
+    """(codes, s) of a bfloat16 tensor under its own amax scale, in e5m2."""
+    s = quant_scale_e5m2(amax(T_bits))
+    return quant_e5m2(T_bits, s), s
+
+
+def mlp_shard_backward_fp8(X_bits, A_bits, B_bits, dY_bits, N: int, rank: int):
+    """Gradients of rank `rank`'s shard with fp8 GEMMs in the hybrid formats.
+
+    Returns a dict: the scales sX, sA, sB, sdY, sdS, sZ (float32), the codes
+    Xq, Aq_i, Bq_i, dYq (e4m3 / e5m2), S and dZ (float64), dS and Z (bf16
+    bits), dSq (e5m2), Zq (e4m3), and the gradients dX, dA, dB (float64):
+      S  = (Xq·Aq_i)/(sX·sA)               the recomputed pre-activation
+      dZ = (dYq·Bq_iᵀ)/(sdY·sB)
+      dS = bf16(dZ ⊙ GeLU'(S)),  Z = bf16(GeLU(S))
+      dX = (dSq·Aq_iᵀ)/(sdS·sA),  dA = (Xqᵀ·dSq)/(sX·sdS),  dB = (Zqᵀ·dYq)/(sZ·sdY)
+    """
+    H = A_bits.shape[1]
+    lo, hi = shard_columns(H, N, rank)
+    Xq, sX = quantize_inputs_e4m3(X_bits)
+    Aq, sA = quantize_inputs_e4m3(A_bits)
+    Bq, sB = quantize_inputs_e4m3(B_bits)
+    dYq, sdY = quantize_e5m2(dY_bits)
+    Xv, Av, Bv = e4m3_decode(Xq), e4m3_decode(Aq)[:, lo:hi], e4m3_decode(Bq)[lo:hi, :]
+    dYv = e5m2_decode(dYq)
+    S = (Xv @ Av) / (float(sX) * float(sA))
+    dZ = (dYv @ Bv.T) / (float(sdY) * float(sB))
+    dS_bits = bf16_encode(dZ * gelu_grad(S))
+    Z_bits = bf16_encode(gelu(S))
+    dSq, sdS = quantize_e5m2(dS_bits)
+    Zq, sZ = quantize_inputs_e4m3(Z_bits)
+    dSv, Zv = e5m2_decode(dSq), e4m3_decode(Zq)
+    return {"sX": sX, "sA": sA, "sB": sB, "sdY": sdY, "sdS": sdS, "sZ": sZ,
+            "Xq": Xq, "Aq_i": Aq[:, lo:hi], "Bq_i": Bq[lo:hi, :], "dYq": dYq,
+            "S": S, "dZ": dZ, "dS_bits": dS_bits, "Z_bits": Z_bits, "dSq": dSq, "Zq": Zq,
+            "dX": (dSv @ Av.T) / (float(sdS) * float(sA)),
+            "dA": (Xv.T @ dSv) / (float(sX) * float(sdS)),
+            "dB": (Zv.T @ dYv) / (float(sZ) * float(sdY))}

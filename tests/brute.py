@@ -170,3 +170,73 @@ def attention_exact(qkv_bits, B, S, heads, dh, causal=True):
                     vs = [val[b * S + j][c + 2 * dh + e] for j in keys]
                     out[b * S + t][h * dh + e] = math.fsum(wi * vi for wi, vi in zip(w, vs)) / den
     return out
+
+
+def e5m2_value(code: int) -> Fraction:
+    """Exact value of a finite OCP e5m2 code (infinities and NaNs are rejected)."""
+    code = int(code) & 0xFF
+    sign = -1 if code & 0x80 else 1
+    E = (code >> 2) & 0x1F
+    m = code & 3
+    if E == 31:
+        raise ValueError("non-finite code")
+    if E == 0:
+        return sign * Fraction(m, 2 ** 16)
+    return sign * (1 + Fraction(m, 4)) * Fraction(2) ** (E - 15)
+
+
+def _quant_exact(vals, fmt):
+    """Codes (as exact values) and scale of a list of rows under the tensor's own amax:
+    s = MAX/amax as an fp32 division, the product in fp32, clamp, one RNE rounding."""
+    import numpy as np
+    top, frac_bits, emin = (448.0, 3, -6) if fmt == "e4m3" else (57344.0, 2, -14)
+    amax = max(abs(v) for row in vals for v in row)
+    s = np.float32(1.0) if amax == 0 else np.float32(np.float32(top) / np.float32(float(amax)))
+    out = []
+    for row in vals:
+        q = []
+        for v in row:
+            p = Fraction(float(np.float32(np.float32(float(v)) * s)))
+            p = max(min(p, Fraction(top)), Fraction(-top))
+            q.append(round_half_even(p, frac_bits, emin))
+        out.append(q)
+    return out, s
+
+
+def shard_backward_fp8_exact(X_bits, A_bits, B_bits, dY_bits, N, rank):
+    """Exact fp8 backward in the hybrid formats: every tensor quantised with its
+    own amax scale (e4m3 for X, A, B, Z; e5m2 for dY, dS), every GEMM an exact
+    rational sum divided by its scales. Returns a dict of exact values."""
+    H = A_bits.shape[1]
+    F = H // N
+    lo = rank * F
+    X = [[bf16_value(v) for v in row] for row in X_bits.tolist()]
+    A = [[bf16_value(v) for v in row] for row in A_bits.tolist()]
+    B = [[bf16_value(v) for v in row] for row in B_bits.tolist()]
+    dY = [[bf16_value(v) for v in row] for row in dY_bits.tolist()]
+    Xq, sX = _quant_exact(X, "e4m3")
+    Aq, sA = _quant_exact(A, "e4m3")
+    Bq, sB = _quant_exact(B, "e4m3")
+    dYq, sdY = _quant_exact(dY, "e5m2")
+    Aq_i = [row[lo:lo + F] for row in Aq]
+    Bq_i = Bq[lo:lo + F]
+    S = [[v / (Fraction(float(sX)) * Fraction(float(sA))) for v in row] for row in matmul_exact(Xq, Aq_i)]
+    Bt = [list(col) for col in zip(*Bq_i)]
+    dZ = [[v / (Fraction(float(sdY)) * Fraction(float(sB))) for v in row] for row in matmul_exact(dYq, Bt)]
+    Z = [[bf16_round(Fraction(gelu_float(float(s)))) for s in row] for row in S]
+    dS = [[bf16_round(Fraction(float(dz) * gelu_grad_float(float(s)))) for dz, s in zip(rz, rs)]
+          for rz, rs in zip(dZ, S)]
+    dSq, sdS = _quant_exact(dS, "e5m2")
+    Zq, sZ = _quant_exact(Z, "e4m3")
+    At = [list(col) for col in zip(*Aq_i)]
+    Xt = [list(col) for col in zip(*Xq)]
+    Zt = [list(col) for col in zip(*Zq)]
+    def scaled(M, a, b):
+        den = Fraction(float(a)) * Fraction(float(b))
+        return [[v / den for v in row] for row in M]
+    return {"sX": sX, "sA": sA, "sB": sB, "sdY": sdY, "sdS": sdS, "sZ": sZ,
+            "Xq": Xq, "Aq_i": Aq_i, "Bq_i": Bq_i, "dYq": dYq, "S": S, "dZ": dZ, "Z": Z, "dS": dS,
+            "dSq": dSq, "Zq": Zq,
+            "dX": scaled(matmul_exact(dSq, At), sdS, sA),
+            "dA": scaled(matmul_exact(Xt, dSq), sX, sdS),
+            "dB": scaled(matmul_exact(Zt, dYq), sZ, sdY)}

@@ -10,7 +10,8 @@ import numpy as np
 import pytest
 import torch
 
-from oracle.codecs import bf16_decode, bf16_encode, e4m3_decode, e4m3_encode, E4M3_MAX
+from oracle.codecs import (bf16_decode, bf16_encode, e4m3_decode, e4m3_encode, E4M3_MAX,
+                           e5m2_decode, e5m2_encode, E5M2_MAX)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -130,3 +131,38 @@ def test_e4m3_matches_torch_in_range():
     x = (rng.uniform(-448, 448, 500_000) * np.exp(rng.uniform(-12, 0, 500_000))).astype(np.float32)
     ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
     assert np.array_equal(e4m3_encode(x.astype(np.float64)), ref)
+
+
+def test_e5m2_all_codes():
+    """Every code decodes to its format-definition value (torch's float8_e5m2 as a
+    second reading), and every finite value encodes back to its code."""
+    codes = np.arange(256, dtype=np.uint8)
+    vals = e5m2_decode(codes)
+    fin = np.isfinite(vals)
+    assert fin.sum() == 248 and np.isinf(vals).sum() == 2 and np.isnan(vals).sum() == 6
+    assert np.array_equal(e5m2_encode(vals[fin]), codes[fin])
+    t = torch.from_numpy(codes).view(torch.float8_e5m2).to(torch.float64).numpy()
+    assert np.array_equal(vals[fin], t[fin])
+    assert vals[0x7B] == E5M2_MAX == 1.75 * 2.0 ** 15
+    assert vals[0x01] == 2.0 ** -16 and vals[0x04] == 2.0 ** -14      # min subnormal, min normal
+    assert vals[0x3C] == 1.0 and vals[0x3D] == 1.25 and vals[0xBE] == -1.5
+
+
+def test_e5m2_midpoints_and_saturation():
+    pos = e5m2_decode(np.arange(0x7C, dtype=np.uint8))
+    mid = (pos[:-1] + pos[1:]) / 2
+    got = e5m2_encode(mid)
+    # ties go to the even code (the code with an even mantissa field)
+    want = np.where(np.arange(0x7B) % 2 == 0, np.arange(0x7B), np.arange(1, 0x7C)).astype(np.uint8)
+    assert np.array_equal(got, want)
+    assert e5m2_encode(np.array([57345.0, 61440.0, 1e9, -1e9])).tolist() == [0x7B, 0x7B, 0x7B, 0xFB]
+    assert e5m2_encode(np.array([2.0 ** -17]))[0] == 0x00          # tie below min subnormal -> 0
+    assert e5m2_encode(np.array([2.0 ** -17 * 1.0001]))[0] == 0x01
+
+
+def test_e5m2_matches_torch_in_range():
+    rng = np.random.default_rng(11)
+    x = (rng.standard_normal(200000) * np.exp(rng.uniform(-12, 10, 200000))).astype(np.float32)
+    x = np.clip(x, -E5M2_MAX, E5M2_MAX)
+    ref = torch.from_numpy(x).to(torch.float8_e5m2).view(torch.uint8).numpy()
+    assert np.array_equal(e5m2_encode(x.astype(np.float64)), ref)

@@ -425,3 +425,52 @@ def test_workload_table_shapes():
     wl = WORKLOADS["175b_tp8"]
     assert (wl.M, wl.d, wl.F) == (2048, 12288, 6144)
     assert WORKLOADS["tiny_tp2"].flops_per_shard() == 4 * 32 * 64 * 128
+
+
+# ------------------------------------------------------ fp8 backward (hybrid) --
+
+@pytest.mark.parametrize("M,d,H,N,rank,seed", [(4, 16, 32, 2, 1, 70), (5, 32, 64, 4, 2, 71)])
+def test_fp8_backward_matches_brute_force(M, d, H, N, rank, seed):
+    """Every code, scale and gradient of the hybrid fp8 backward against the
+    exact rational evaluation (own decoders and rounding in tests/brute.py)."""
+    X, A, B = make_random(M, d, H, seed, sigma=0.3)
+    dY = _dy(M, d, seed + 1)
+    g = oracle.mlp_shard_backward_fp8(X, A, B, dY, N, rank)
+    ex = brute.shard_backward_fp8_exact(X, A, B, dY, N, rank)
+    as_f = lambda T: np.array([[float(v) for v in r] for r in T])
+    for k in ("sX", "sA", "sB", "sdY", "sdS", "sZ"):
+        assert np.float32(g[k]) == np.float32(ex[k]), k
+    assert np.array_equal(oracle.e4m3_decode(g["Xq"]), as_f(ex["Xq"]))
+    assert np.array_equal(oracle.e4m3_decode(g["Aq_i"]), as_f(ex["Aq_i"]))
+    assert np.array_equal(oracle.e4m3_decode(g["Bq_i"]), as_f(ex["Bq_i"]))
+    assert np.array_equal(oracle.e5m2_decode(g["dYq"]), as_f(ex["dYq"]))
+    assert np.array_equal(oracle.bf16_decode(g["Z_bits"]), as_f(ex["Z"]))
+    assert np.array_equal(oracle.bf16_decode(g["dS_bits"]), as_f(ex["dS"]))
+    assert np.array_equal(oracle.e5m2_decode(g["dSq"]), as_f(ex["dSq"]))
+    assert np.array_equal(oracle.e4m3_decode(g["Zq"]), as_f(ex["Zq"]))
+    for k in ("dX", "dA", "dB"):
+        assert _rel_maxdiff(g[k], as_f(ex[k])) <= 1e-13, k
+
+
+def _int_bits(rng, shape, top=7):
+    """Small integers in [-top, top] with ±top present, as bfloat16 bits."""
+    v = rng.integers(-top, top + 1, size=shape).astype(np.float32)
+    v.flat[0] = top
+    return bf16_bits_from_f32(v)
+
+
+def test_fp8_backward_on_exact_inputs_reduces_to_the_bf16_backward():
+    """With integers in [-7, 7] (amax 7), the scales are 448/7 = 2^6 (e4m3) and
+    57344/7 = 2^13 (e5m2): X, A, B and dY quantise exactly, so S, dZ, and the
+    rounded dS and Z equal the bf16 backward's (a separate code path)."""
+    rng = np.random.default_rng(5)
+    M, d, H, N, rank = 6, 16, 64, 4, 1
+    X, A, B, dY = (_int_bits(rng, s) for s in ((M, d), (d, H), (H, d), (M, d)))
+    g = oracle.mlp_shard_backward_fp8(X, A, B, dY, N, rank)
+    ref = oracle.mlp_shard_backward(X, A, B, dY, N, rank)
+    assert float(g["sX"]) == 64.0 and float(g["sdY"]) == 8192.0
+    assert np.array_equal(g["S"], ref["S"]) and np.array_equal(g["dZ"], ref["dZ"])
+    assert np.array_equal(g["dS_bits"], ref["dS_bits"]) and np.array_equal(g["Z_bits"], ref["Z_bits"])
+    # and the gradients agree with the bf16 ones up to the quantisation of dS and Z
+    for k in ("dX", "dA", "dB"):
+        assert _rel_maxdiff(g[k], ref[k]) <= 0.13, k

@@ -333,3 +333,47 @@ def test_attention_output_rows_of_the_wrong_rank_are_caught(monkeypatch):
         return real(O_bits, Wo_bits, N, (rank + 1) % N)
     monkeypatch.setattr(oat, "out_partial", op)
     assert _pins_fail(ATTN_PINS)
+
+
+# ------------------------------------------------------- fp8 backward -----
+
+FP8_BWD_PINS = [
+    lambda: pins.test_fp8_backward_matches_brute_force(4, 16, 32, 2, 1, 70),
+    pins.test_fp8_backward_on_exact_inputs_reduces_to_the_bf16_backward,
+]
+
+
+def _fp8_bwd_variant(monkeypatch, change):
+    real = omlp.mlp_shard_backward_fp8
+
+    def bw(X, A, B, dY, N, rank):
+        return change(dict(real(X, A, B, dY, N, rank)), X, A, B, dY, N, rank)
+    monkeypatch.setattr(omlp, "mlp_shard_backward_fp8", bw)
+    monkeypatch.setattr(oracle, "mlp_shard_backward_fp8", bw)
+
+
+def test_fp8_backward_gradient_in_e4m3_is_caught(monkeypatch):
+    def change(g, X, A, B, dY, N, rank):
+        dSq, sdS = omlp.quantize_inputs_e4m3(g["dS_bits"])    # e4m3 instead of e5m2
+        g["dSq"], g["sdS"] = dSq, sdS
+        return g
+    _fp8_bwd_variant(monkeypatch, change)
+    assert _pins_fail(FP8_BWD_PINS)
+
+
+def test_fp8_backward_swapped_scales_are_caught(monkeypatch):
+    def change(g, X, A, B, dY, N, rank):
+        g["dB"] = g["dB"] * (float(g["sdY"]) / float(g["sdS"]))   # divided by sZ·sdS
+        return g
+    _fp8_bwd_variant(monkeypatch, change)
+    assert _pins_fail(FP8_BWD_PINS)
+
+
+def test_fp8_backward_unquantised_dy_is_caught(monkeypatch):
+    real_q = omlp.quantize_e5m2
+
+    def q(T):
+        codes, s = real_q(T)
+        return omlp.e5m2_encode(oracle.bf16_decode(T) * 1.0), np.float32(1.0)  # no scale
+    monkeypatch.setattr(omlp, "quantize_e5m2", q)
+    assert _pins_fail(FP8_BWD_PINS)
