@@ -93,7 +93,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="7b_tp8",
                    help="7b_tp8 (default), gpt2s_n1, 175b_tp8, 175b_tp8_e4m3, 175b_tp8_e4m3_delayed, "
-                        "7b_tp8_bwd, 7b_tp8_attn, library_compare (the 7B-class column GEMM "
+                        "7b_tp8_bwd, 7b_tp8_bwd_fp8, 7b_tp8_attn, library_compare (the 7B-class column GEMM "
                         "against torch.matmul on the same data), "
                         "or copy (a "
                         "1-part tp_partial_sum over 256 MiB of fp32: the known-size copy that "
@@ -171,15 +171,18 @@ def build_bf16_step(tpm, wl, partial_dtype):
 
 def build_bwd_step(tpm, wl):
     """Backward of every rank's shard: one tp_mlp_shard_backward call per rank
-    (S recomputed, dS with GeLU', dX_i, dB_i, dA_i), then Σ_i dX_i."""
+    (S recomputed, dS with GeLU', dX_i, dB_i, dA_i), or its fp8 form (the
+    operands quantised inside the call), then Σ_i dX_i."""
     import torch
     from workloads import make_inputs, make_output_grad
     X, A, B = make_inputs(wl)
     dY = make_output_grad(wl.M, wl.d, wl.seed, wl.grad_sigma)
     Xd, Ad, Bd, dYd = dev_bf16(X), dev_bf16(A), dev_bf16(B), dev_bf16(dY)
     M, d, H, N, F = wl.M, wl.d, wl.H, wl.N, wl.F
-    ws = torch.empty(tpm.tp_mlp_shard_backward_workspace_size(M, d, H, N), dtype=torch.uint8,
-                     device="cuda")
+    fn = tpm.tp_mlp_shard_backward_fp8 if wl.fp8 else tpm.tp_mlp_shard_backward
+    size = (tpm.tp_mlp_shard_backward_fp8_workspace_size if wl.fp8
+            else tpm.tp_mlp_shard_backward_workspace_size)
+    ws = torch.empty(size(M, d, H, N), dtype=torch.uint8, device="cuda")
     dXs = [torch.empty((M, d), dtype=torch.float32, device="cuda") for _ in range(N)]
     dA = torch.empty((d, F), dtype=torch.float32, device="cuda")
     dB = torch.empty((F, d), dtype=torch.float32, device="cuda")
@@ -188,8 +191,7 @@ def build_bwd_step(tpm, wl):
     def step(timer=None):
         for r in range(N):
             def call(r=r):
-                tpm.tp_mlp_shard_backward(Xd, Ad, Bd, dYd, N, r, dX_i=dXs[r], dA_i=dA, dB_i=dB,
-                                          workspace=ws)
+                fn(Xd, Ad, Bd, dYd, N, r, dX_i=dXs[r], dA_i=dA, dB_i=dB, workspace=ws)
             if timer is None:
                 call()
             else:
@@ -202,7 +204,8 @@ def build_bwd_step(tpm, wl):
 
     kern_flops = {"shard_backward": 10 * M * d * F}
     # algorithmic bytes of one call: X, dY, A_i, B_i read once; dX_i, dA_i,
-    # dB_i written once (the S, dS, Z intermediates are not counted)
+    # dB_i written once (the S, dS, Z intermediates and, for fp8, the
+    # quantised copies and the whole-tensor amaxes of A and B are not counted)
     kern_bytes = {"shard_backward": (2 * M * d + 2 * d * F) * 2 + (M * d + 2 * d * F) * 4}
     psum_bytes = (N + 1) * 4 * M * d
     return step, kern_flops, kern_bytes, psum_bytes, (X, A, B, dY), (dX if N > 1 else dXs[0])
@@ -335,6 +338,15 @@ def cpu_baseline(wl, inputs, budget_s):
         return cpu_baseline_attn(wl, inputs, budget_s)
     X, A, B = inputs[:3]
     chunk = max(1, min(wl.M, 1024))
+    if wl.fp8 and wl.backward:   # one rank's whole fp8 backward (quantisation included)
+        t0 = time.perf_counter()
+        oracle.mlp_shard_backward_fp8(X, A, B, inputs[3], wl.N, 0)
+        t = time.perf_counter() - t0
+        return {"value": wl.flops_per_shard() / t / 1e12, "unit": "TFLOP/s", "cores": HOST_CORES,
+                "kind": "oracle",
+                "sample": f"rank 0 of {wl.N}: the whole fp8 backward of {wl.name} (all {wl.M} "
+                          f"rows, quantisation included), float64 numpy/OpenBLAS oracle, {t:.2f} s",
+                "seconds": t}
     if wl.fp8:   # input quantisation is preparation (outside the GPU's timed step too)
         Xq, sX = oracle.quantize_inputs_e4m3(X)
         Aq, sA = oracle.quantize_inputs_e4m3(A)
@@ -384,9 +396,11 @@ def sampled_check(wl, inputs, out, nrows=8):
     X, A, B = inputs[:3]
     rows = sample_rows(wl.M, nrows)
     got = out[torch.from_numpy(rows).cuda()].double().cpu().numpy()
-    if wl.fp8:
+    if wl.fp8 and not wl.backward:
         return None
-    if wl.backward:   # Σ_i dX_i is the unsharded block's input gradient
+    if wl.fp8:        # Σ_i dX_i against the unsharded bf16 input gradient: the fp8 error
+        ref = oracle.mlp_shard_backward(X[rows], A, B, inputs[3][rows], 1, 0)["dX"]
+    elif wl.backward:   # Σ_i dX_i is the unsharded block's input gradient
         ref = oracle.mlp_shard_backward(X[rows], A, B, inputs[3][rows], 1, 0)["dX"]
     elif wl.N > 1:
         ref = oracle.mlp_unsharded(X[rows], A, B)
@@ -473,10 +487,10 @@ def main():
     log(f"bench: workload {wl.name}: {wl.description}")
     if attn:
         step, kern_flops, kern_bytes, psum_bytes, inputs, out = build_attn_step(tpm, wl)
-    elif wl.fp8:
-        step, kern_flops, kern_bytes, psum_bytes, inputs, out = build_e4m3_step(tpm, wl)
     elif wl.backward:
         step, kern_flops, kern_bytes, psum_bytes, inputs, out = build_bwd_step(tpm, wl)
+    elif wl.fp8:
+        step, kern_flops, kern_bytes, psum_bytes, inputs, out = build_e4m3_step(tpm, wl)
     else:
         step, kern_flops, kern_bytes, psum_bytes, inputs, out = build_bf16_step(
             tpm, wl, args.partial_dtype)
@@ -544,8 +558,8 @@ def main():
                     "partial_dtype": "f32",
                     "parallelism": f"tp{wl.N} ranks sequentially on 1 GPU"} if attn else
                    {"workload": wl.name, "M": wl.M, "d": wl.d, "F": wl.F, "tp_ranks": wl.N,
-                    "partial_dtype": "bf16" if wl.fp8 else ("f32" if wl.backward
-                                                             else args.partial_dtype),
+                    "partial_dtype": "f32" if wl.backward else ("bf16" if wl.fp8
+                                                                else args.partial_dtype),
                     "parallelism": f"tp{wl.N} ranks sequentially on 1 GPU" if wl.N > 1 else "none"}),
         "pct_of_peak": round(100 * value / peak, 2),
         "roofline": roofline,

@@ -317,6 +317,35 @@ int tp_mlp_shard_backward(const void* X, const void* A, const void* B, const voi
                           void* stream);
 
 /*
+ * Bytes of device workspace tp_mlp_shard_backward_fp8 needs; 0 for invalid sizes.
+ */
+size_t tp_mlp_shard_backward_fp8_workspace_size(int64_t M, int64_t d, int64_t H, int N);
+
+/*
+ * The backward of tp_mlp_shard_backward with fp8 GEMMs in the hybrid formats
+ * ("Megatron-LM deep architecture", FP8 hybrid precision section: E4M3 for
+ * activations and weights, E5M2, with its wider range, for the backward's
+ * gradients). Each tensor is quantised with its own current amax scale,
+ * s = 448/amax (e4m3) or 57344/amax (e5m2), values clamped to the format's
+ * range, RNE: X, the whole of A and B (as in the fp8 forward) and Z in e4m3;
+ * dY and dS in e5m2. With q(T) the codes and s_T the scale:
+ *   S    = (q(X)·q(A)_i) / (s_X·s_A)                   (fp32)
+ *   dS   = bf16(((q(dY)·q(B)_iᵀ) / (s_dY·s_B)) ⊙ GeLU'(S)),  Z = bf16(GeLU(S))
+ *   dX_i = (q(dS)·q(A)_iᵀ) / (s_dS·s_A)
+ *   dA_i = (q(X)ᵀ·q(dS)) / (s_X·s_dS),  dB_i = (q(Z)ᵀ·q(dY)) / (s_Z·s_dY)
+ * all accumulated in fp32; the transposed operands are quantised straight
+ * into their transposed layout. Arguments, layouts and outputs as for
+ * tp_mlp_shard_backward; M, d and F = H/N must be multiples of 16.
+ * workspace : device, at least tp_mlp_shard_backward_fp8_workspace_size(M, d, H, N)
+ *   bytes, 16-byte aligned; the first 64 bytes hold the amaxes of X, A, B, dY,
+ *   dS, Z (floats 0-5) and their scales (floats 8-13).
+ */
+int tp_mlp_shard_backward_fp8(const void* X, const void* A, const void* B, const void* dY,
+                              float* dX_i, float* dA_i, float* dB_i, int64_t M, int64_t d,
+                              int64_t H, int N, int rank, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/*
  * ---------------------------------------------------------------------------
  * Attention shard. With h heads of width dh = d/h and N ranks, rank i owns
  * heads [i·h/N, (i+1)·h/N) and computes their attention with no exchange

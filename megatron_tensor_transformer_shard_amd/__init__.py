@@ -27,8 +27,9 @@ __all__ = [
     "tp_amax_history_push", "tp_mlp_col_gelu_e4m3_delayed", "tp_mlp_shard_e4m3_delayed",
     "tp_mlp_shard_e4m3_delayed_workspace_size", "AmaxHistory",
     "tp_mlp_shard_backward", "tp_mlp_shard_backward_workspace_size", "backward_workspace_views",
+    "tp_mlp_shard_backward_fp8", "tp_mlp_shard_backward_fp8_workspace_size",
     "tp_attn_qkv", "tp_attn_heads", "tp_attn_shard", "tp_attn_shard_workspace_size",
-    "attn_workspace_views", "ATTN_HEAD_DIM",
+    "attn_workspace_views", "ATTN_HEAD_DIM", "fp8_backward_workspace_views",
     "TPM_BF16", "TPM_F32", "TPM_E4M3", "EXPORTED_SYMBOLS",
 ]
 
@@ -73,6 +74,9 @@ _SIGNATURES = {
     "tp_attn_shard_workspace_size": (_sz, [_i64, _i64, _int]),
     "tp_attn_shard": (_int, [_vp, _vp, _vp, _vp, _int, _i64, _i64, _i64, _i64, _int, _int, _int,
                              _vp, _sz, _vp]),
+    "tp_mlp_shard_backward_fp8_workspace_size": (_sz, [_i64, _i64, _i64, _int]),
+    "tp_mlp_shard_backward_fp8": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64,
+                                         _int, _int, _vp, _sz, _vp]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGNATURES)
 
@@ -585,3 +589,69 @@ def attn_workspace_views(workspace, M: int, F: int):
     QKV = workspace[: 6 * M * F].view(torch.bfloat16).view(M, 3 * F)
     O = workspace[o1: o1 + 2 * M * F].view(torch.bfloat16).view(M, F)
     return QKV, O
+
+
+def tp_mlp_shard_backward_fp8_workspace_size(M: int, d: int, H: int, N: int) -> int:
+    return int(lib.tp_mlp_shard_backward_fp8_workspace_size(M, d, H, N))
+
+
+def tp_mlp_shard_backward_fp8(X, A, B, dY, N: int, rank: int, dX_i=None, dA_i=None, dB_i=None,
+                              workspace=None, stream=None):
+    """Gradients of rank `rank`'s shard with hybrid fp8 GEMMs (E4M3 activations and
+    weights, E5M2 gradients). Returns (dX_i, dA_i, dB_i, workspace)."""
+    for t, name in ((X, "X"), (A, "A"), (B, "B"), (dY, "dY")):
+        _need(t, name, torch.bfloat16, 2)
+    M, d = X.shape
+    H = A.shape[1]
+    if tuple(A.shape) != (d, H) or tuple(B.shape) != (H, d) or tuple(dY.shape) != (M, d):
+        raise ValueError("shape mismatch")
+    if N < 1 or H % N != 0:
+        raise ValueError("H must be divisible by N")
+    F = H // N
+    dev = X.device
+    dX_i = torch.empty((M, d), dtype=torch.float32, device=dev) if dX_i is None else dX_i
+    dA_i = torch.empty((d, F), dtype=torch.float32, device=dev) if dA_i is None else dA_i
+    dB_i = torch.empty((F, d), dtype=torch.float32, device=dev) if dB_i is None else dB_i
+    for t, name, shp in ((dX_i, "dX_i", (M, d)), (dA_i, "dA_i", (d, F)), (dB_i, "dB_i", (F, d))):
+        _need(t, name, torch.float32, 2)
+        if tuple(t.shape) != shp:
+            raise ValueError(f"{name} has the wrong shape")
+    need = tp_mlp_shard_backward_fp8_workspace_size(M, d, H, N)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", None)
+    _check(lib.tp_mlp_shard_backward_fp8(X.data_ptr(), A.data_ptr(), B.data_ptr(), dY.data_ptr(),
+                                         dX_i.data_ptr(), dA_i.data_ptr(), dB_i.data_ptr(), M, d,
+                                         H, N, rank, workspace.data_ptr(),
+                                         workspace.numel() * workspace.element_size(),
+                                         _stream(stream)),
+           "tp_mlp_shard_backward_fp8")
+    return dX_i, dA_i, dB_i, workspace
+
+
+def fp8_backward_workspace_views(workspace, M: int, d: int, F: int):
+    """Named views of a tp_mlp_shard_backward_fp8 workspace: amax/scale floats
+    and the codes and intermediates, in the layout the library uses."""
+    def r256(b):
+        return (b + 255) // 256 * 256
+    o = 256
+    views = {}
+    for name, nbytes in (("Xq", M * d), ("XqT", M * d), ("Aq", d * F), ("AqT", d * F),
+                         ("BqT", d * F), ("dYq", M * d), ("S", M * F * 4), ("dS", M * F * 2),
+                         ("Z", M * F * 2), ("dSq", M * F), ("ZqT", M * F)):
+        views[name] = workspace[o:o + nbytes]
+        o += r256(nbytes)
+    fl = workspace[:64].view(torch.float32)
+    views["amax"], views["scale"] = fl[:6], fl[8:14]
+    views["Xq"] = views["Xq"].view(M, d)
+    views["XqT"] = views["XqT"].view(d, M)
+    views["Aq"] = views["Aq"].view(d, F)
+    views["AqT"] = views["AqT"].view(F, d)
+    views["BqT"] = views["BqT"].view(d, F)
+    views["dYq"] = views["dYq"].view(M, d)
+    views["S"] = views["S"].view(torch.float32).view(M, F)
+    views["dS"] = views["dS"].view(torch.bfloat16).view(M, F)
+    views["Z"] = views["Z"].view(torch.bfloat16).view(M, F)
+    views["dSq"] = views["dSq"].view(M, F)
+    views["ZqT"] = views["ZqT"].view(F, M)
+    return views

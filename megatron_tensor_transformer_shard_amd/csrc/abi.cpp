@@ -501,6 +501,120 @@ int tp_mlp_shard_backward(const void* X, const void* A, const void* B, const voi
   return status_of(e);
 }
 
+namespace {
+// Byte offsets of the fp8 backward's workspace parts (each 256-byte aligned).
+struct Fp8BwdLayout {
+  size_t xq, xqt, aq, aqt, bqt, dyq, s, ds, z, dsq, zqt, total;
+};
+Fp8BwdLayout fp8_bwd_layout(int64_t M, int64_t d, int64_t F) {
+  Fp8BwdLayout L{};
+  size_t o = 256;  // amaxes and scales
+  auto take = [&](size_t bytes) { const size_t at = o; o += round256(bytes); return at; };
+  const size_t md = (size_t)M * d, df = (size_t)d * F, mf = (size_t)M * F;
+  L.xq = take(md); L.xqt = take(md); L.aq = take(df); L.aqt = take(df); L.bqt = take(df);
+  L.dyq = take(md); L.s = take(mf * 4); L.ds = take(mf * 2); L.z = take(mf * 2);
+  L.dsq = take(mf); L.zqt = take(mf);
+  L.total = o;
+  return L;
+}
+}  // namespace
+
+size_t tp_mlp_shard_backward_fp8_workspace_size(int64_t M, int64_t d, int64_t H, int N) {
+  if (M < 0 || d <= 0 || H <= 0 || N < 1 || H % N != 0) return 0;
+  if (M > kMaxDim || H > kMaxDim) return 0;
+  return fp8_bwd_layout(M, d, H / N).total;
+}
+
+int tp_mlp_shard_backward_fp8(const void* X, const void* A, const void* B, const void* dY,
+                              float* dX_i, float* dA_i, float* dB_i, int64_t M, int64_t d,
+                              int64_t H, int N, int rank, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  if (N < 1 || rank < 0 || rank >= N) return TPM_ERR_ARG;
+  if (H <= 0 || H % N != 0) return TPM_ERR_SHAPE;
+  const int64_t F = H / N;
+  int st = check_dims(M, d, F, 16);
+  if (st != TPM_OK) return st;
+  // M is the row length of the transposed fp8 copies and the contraction
+  // length of the weight gradients
+  if (M % 16 != 0 || M > kMaxLd) return TPM_ERR_SHAPE;
+  if (H > kMaxLd || H * d > (int64_t(1) << 46)) return TPM_ERR_SHAPE;
+  // the quantise-and-transpose grid has one 64-row tile per y index
+  constexpr int64_t kMaxTileRows = int64_t(65535) * 64;
+  if (M > kMaxTileRows || d > kMaxTileRows || F > kMaxTileRows) return TPM_ERR_SHAPE;
+  if (M == 0) return TPM_OK;
+  if (!X || !A || !B || !dY || !dX_i || !dA_i || !dB_i) return TPM_ERR_NULL;
+  const Fp8BwdLayout L = fp8_bwd_layout(M, d, F);
+  if (!workspace || workspace_bytes < L.total) return TPM_ERR_WORKSPACE;
+  if (!aligned16(X) || !aligned16(A) || !aligned16(B) || !aligned16(dY) || !aligned16(dX_i) ||
+      !aligned16(dA_i) || !aligned16(dB_i) || !aligned16(workspace))
+    return TPM_ERR_ALIGN;
+  const Span ins[4] = {mat_span(X, M, d, d, 2), mat_span(A, d, H, H, 2), mat_span(B, H, d, d, 2),
+                       mat_span(dY, M, d, d, 2)};
+  const Span outs[4] = {mat_span(dX_i, M, d, d, 4), mat_span(dA_i, d, F, F, 4),
+                        mat_span(dB_i, F, d, d, 4),
+                        {reinterpret_cast<uintptr_t>(workspace),
+                         reinterpret_cast<uintptr_t>(workspace) + L.total}};
+  for (int o = 0; o < 4; ++o) {
+    for (int i = 0; i < 4; ++i)
+      if (overlap(outs[o], ins[i])) return TPM_ERR_ALIAS;
+    for (int p = o + 1; p < 4; ++p)
+      if (overlap(outs[o], outs[p])) return TPM_ERR_ALIAS;
+  }
+
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  float* am = reinterpret_cast<float*>(ws);       // amax: X, A, B, dY, dS, Z
+  float* sc = am + 8;                             // scales in the same order
+  uint8_t *Xq = ws + L.xq, *XqT = ws + L.xqt, *Aq = ws + L.aq, *AqT = ws + L.aqt;
+  uint8_t *BqT = ws + L.bqt, *dYq = ws + L.dyq, *dSq = ws + L.dsq, *ZqT = ws + L.zqt;
+  float* S = reinterpret_cast<float*>(ws + L.s);
+  uint16_t* dS = reinterpret_cast<uint16_t*>(ws + L.ds);
+  uint16_t* Z = reinterpret_cast<uint16_t*>(ws + L.z);
+  const uint16_t* x = static_cast<const uint16_t*>(X);
+  const uint16_t* dy = static_cast<const uint16_t*>(dY);
+  const uint16_t* A_i = static_cast<const uint16_t*>(A) + (int64_t)rank * F;
+  const uint16_t* B_i = static_cast<const uint16_t*>(B) + (int64_t)rank * F * d;
+  hipStream_t s = as_stream(stream);
+  const int m = (int)M, dd = (int)d, f = (int)F;
+  using tpmlp::Fp8GemmArgs;
+  constexpr int E4 = 0, E5 = 1;
+  hipError_t e = hipSuccess;
+  auto run = [&](hipError_t r) { if (e == hipSuccess) e = r; };
+  // per-tensor amax scales: X, the whole of A and B (as in the fp8 forward), dY
+  run(tpmlp::launch_amax_bf16(x, M * d, am + 0, s));
+  run(tpmlp::launch_amax_bf16(static_cast<const uint16_t*>(A), d * H, am + 1, s));
+  run(tpmlp::launch_amax_bf16(static_cast<const uint16_t*>(B), H * d, am + 2, s));
+  run(tpmlp::launch_amax_bf16(dy, M * d, am + 3, s));
+  // quantised operands, in the orientation each GEMM reads them
+  run(tpmlp::launch_quant_fp8(E4, x, M * d, am + 0, Xq, sc + 0, s));
+  run(tpmlp::launch_quant_fp8_tile(E4, true, x, d, m, dd, am + 0, XqT, M, sc + 0, s));
+  run(tpmlp::launch_quant_fp8_tile(E4, false, A_i, H, dd, f, am + 1, Aq, F, sc + 1, s));
+  run(tpmlp::launch_quant_fp8_tile(E4, true, A_i, H, dd, f, am + 1, AqT, d, sc + 1, s));
+  run(tpmlp::launch_quant_fp8_tile(E4, true, B_i, d, f, dd, am + 2, BqT, F, sc + 2, s));
+  run(tpmlp::launch_quant_fp8(E5, dy, M * d, am + 3, dYq, sc + 3, s));
+  // S = (Xq·Aq_i)/(sX·sA)
+  run(tpmlp::launch_gemm_fp8(Fp8GemmArgs{Xq, d, sc + 0, Aq, F, sc + 1, S, F, nullptr, nullptr,
+                                         nullptr, 0, nullptr, nullptr, m, f, dd},
+                             OutKind::F32, E4, E4, s));
+  // dS = bf16(((dYq·Bq_iᵀ)/(sdY·sB)) ⊙ GeLU'(S)), Z = bf16(GeLU(S)), their amaxes
+  run(tpmlp::launch_gemm_fp8(Fp8GemmArgs{dYq, d, sc + 3, BqT, F, sc + 2, dS, F, am + 4, nullptr,
+                                         S, F, Z, am + 5, m, f, dd},
+                             OutKind::GeluGradBf16, E5, E4, s));
+  run(tpmlp::launch_quant_fp8(E5, dS, M * F, am + 4, dSq, sc + 4, s));
+  run(tpmlp::launch_quant_fp8_tile(E4, true, Z, F, m, f, am + 5, ZqT, M, sc + 5, s));
+  // dX_i = (dSq·Aq_iᵀ)/(sdS·sA)
+  run(tpmlp::launch_gemm_fp8(Fp8GemmArgs{dSq, F, sc + 4, AqT, d, sc + 1, dX_i, d, nullptr,
+                                         nullptr, nullptr, 0, nullptr, nullptr, m, dd, f},
+                             OutKind::F32, E5, E4, s));
+  // dB_i = (Zqᵀ·dYq)/(sZ·sdY), dA_i = (Xqᵀ·dSq)/(sX·sdS)
+  run(tpmlp::launch_gemm_fp8(Fp8GemmArgs{ZqT, M, sc + 5, dYq, d, sc + 3, dB_i, d, nullptr,
+                                         nullptr, nullptr, 0, nullptr, nullptr, f, dd, m},
+                             OutKind::F32, E4, E5, s));
+  run(tpmlp::launch_gemm_fp8(Fp8GemmArgs{XqT, M, sc + 0, dSq, F, sc + 4, dA_i, F, nullptr,
+                                         nullptr, nullptr, 0, nullptr, nullptr, dd, f, m},
+                             OutKind::F32, E4, E5, s));
+  return status_of(e);
+}
+
 int tp_attn_qkv(const void* X, const void* W_i, int64_t ldw, void* QKV_i, int64_t M, int64_t d,
                 int64_t F3, void* stream) {
   int st = check_dims(M, d, F3, 8);

@@ -15,6 +15,14 @@
 //                as the bf16 GEMM with BK = 128 bytes, and either a GeLU +
 //                bf16 + amax(|Z|) epilogue, the same with Z quantised to e4m3
 //                by a given (delayed) scale, or a plain bf16 store.
+//  - quant_fp8_tile: the same quantisation for a strided block, optionally
+//                written transposed (through LDS), in e4m3 or e5m2; the fp8
+//                backward needs X, A_i, B_i and Z in the other orientation.
+//  - The backward's gradients are e5m2 ("Megatron-LM deep architecture", FP8
+//                hybrid precision section: E5M2, with its wider range, for the
+//                backward's gradients): s = 57344/amax, v_cvt_pk_bf8_f32, and
+//                the GEMM takes the format of each operand as a template
+//                argument (the MFMA's A and B format fields).
 //  - amax_history_push: delayed scaling ("Megatron-LM deep architecture",
 //                FP8 section: the scale a step applies is predicted from the
 //                moving average of the amaxes of earlier steps, so it is known
@@ -30,6 +38,11 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr float kE4m3Max = 448.0f;
+constexpr float kE5m2Max = 57344.0f;
+
+// fp8 formats (the MFMA's format codes): 0 = e4m3, 1 = e5m2.
+template <int FMT>
+constexpr float fp8_max() { return FMT == 0 ? kE4m3Max : kE5m2Max; }
 
 __global__ void fill_f32_kernel(float* p, float v) { *p = v; }
 
@@ -43,28 +56,51 @@ __device__ __forceinline__ void atomic_max_nonneg(float* addr, float v) {
   atomicMax(reinterpret_cast<unsigned int*>(addr), __builtin_bit_cast(unsigned int, v));
 }
 
-__global__ __launch_bounds__(kThreads) void amax_bf16_kernel(const uint16_t* __restrict__ T,
-                                                             int64_t numel, float* amax) {
-  float m = 0.0f;
-  const int64_t nvec = numel / 8;
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  for (int64_t v = (int64_t)blockIdx.x * kThreads + threadIdx.x; v < nvec; v += stride) {
-    const u32x4 w = reinterpret_cast<const u32x4*>(T)[v];
+// max |x| of the 8 bf16 values in w: |x| of a bf16 is its bit pattern with
+// the sign cleared, and non-negative floats order like their bit patterns.
+__device__ __forceinline__ uint32_t absmax_bits8(const u32x4& w) {
+  uint32_t m = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      m = fmaxf(m, fabsf(bf16_bits_to_f32(w[j] & 0xFFFFu)));
-      m = fmaxf(m, fabsf(bf16_bits_to_f32(w[j] >> 16)));
-    }
-  }
-  if (blockIdx.x == 0)
-    for (int64_t e = nvec * 8 + threadIdx.x; e < numel; e += kThreads)
-      m = fmaxf(m, fabsf(bf16_bits_to_f32(T[e])));
-  m = wave_max(m);
-  if ((threadIdx.x & 63) == 0) atomic_max_nonneg(amax, m);
+  for (int j = 0; j < 4; ++j) m = max(m, max(w[j] & 0x7FFFu, (w[j] >> 16) & 0x7FFFu));
+  return m;
 }
 
+// Grid-stride over 16-byte vectors, four loads in flight per thread; the
+// workgroup's four waves combine through LDS and issue one atomic, since
+// atomics on the single result address serialise.
+__global__ __launch_bounds__(kThreads) void amax_bf16_kernel(const uint16_t* __restrict__ T,
+                                                             int64_t numel, float* amax) {
+  __shared__ uint32_t part[kThreads / 64];
+  uint32_t mb = 0;
+  const int64_t nvec = numel / 8;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  const u32x4* src = reinterpret_cast<const u32x4*>(T);
+  int64_t v = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  for (; v + 3 * stride < nvec; v += 4 * stride) {
+    const u32x4 w0 = __builtin_nontemporal_load(src + v);
+    const u32x4 w1 = __builtin_nontemporal_load(src + v + stride);
+    const u32x4 w2 = __builtin_nontemporal_load(src + v + 2 * stride);
+    const u32x4 w3 = __builtin_nontemporal_load(src + v + 3 * stride);
+    mb = max(mb, max(max(absmax_bits8(w0), absmax_bits8(w1)), max(absmax_bits8(w2), absmax_bits8(w3))));
+  }
+  for (; v < nvec; v += stride) mb = max(mb, absmax_bits8(__builtin_nontemporal_load(src + v)));
+  if (blockIdx.x == 0)
+    for (int64_t e = nvec * 8 + threadIdx.x; e < numel; e += kThreads) mb = max(mb, T[e] & 0x7FFFu);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mb = max(mb, (uint32_t)__shfl_xor((int)mb, off, 64));
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = mb;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t b = part[0];
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w) b = max(b, part[w]);
+    atomic_max_nonneg(amax, bf16_bits_to_f32(b));
+  }
+}
+
+template <int FMT = 0>
 __device__ __forceinline__ float quant_scale_of(float amax) {
-  return amax == 0.0f ? 1.0f : kE4m3Max / amax;
+  return amax == 0.0f ? 1.0f : fp8_max<FMT>() / amax;
 }
 
 // Two floats -> two e4m3 codes in the low 16 bits (RNE; inputs within ±448).
@@ -74,6 +110,17 @@ __device__ __forceinline__ uint32_t cvt_e4m3x2(float a, float b) {
 
 __device__ __forceinline__ float clamp448(float x) {
   return fminf(fmaxf(x, -kE4m3Max), kE4m3Max);
+}
+
+// Two floats -> two codes of format FMT in the low 16 bits, after the clamp
+// to the format's largest finite value (RNE).
+template <int FMT>
+__device__ __forceinline__ uint32_t cvt_fp8x2(float a, float b) {
+  constexpr float top = fp8_max<FMT>();
+  a = fminf(fmaxf(a, -top), top);
+  b = fminf(fmaxf(b, -top), top);
+  if constexpr (FMT == 0) return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xFFFFu;
+  else return (uint32_t)__builtin_amdgcn_cvt_pk_bf8_f32(a, b, 0, false) & 0xFFFFu;
 }
 
 // One wave: lane l sums ring slots l, l+64, ... (the new amax in place of
@@ -101,12 +148,13 @@ __global__ __launch_bounds__(64) void amax_history_push_kernel(float* __restrict
 }
 
 // 16 elements per thread per step: 2 x 16-byte bf16 loads, one 16-byte store.
-__global__ __launch_bounds__(kThreads) void quant_e4m3_kernel(const uint16_t* __restrict__ T,
-                                                              int64_t numel,
-                                                              const float* __restrict__ amax,
-                                                              uint8_t* __restrict__ Tq,
-                                                              float* __restrict__ scale) {
-  const float s = quant_scale_of(amax[0]);
+template <int FMT>
+__global__ __launch_bounds__(kThreads) void quant_fp8_kernel(const uint16_t* __restrict__ T,
+                                                             int64_t numel,
+                                                             const float* __restrict__ amax,
+                                                             uint8_t* __restrict__ Tq,
+                                                             float* __restrict__ scale) {
+  const float s = quant_scale_of<FMT>(amax[0]);
   if (blockIdx.x == 0 && threadIdx.x == 0) scale[0] = s;
   const int64_t nvec = numel / 16;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
@@ -118,13 +166,58 @@ __global__ __launch_bounds__(kThreads) void quant_e4m3_kernel(const uint16_t* __
     for (int j = 0; j < 4; ++j) {
       const u32x4& w = (j < 2) ? w0 : w1;
       const uint32_t x0 = w[(j & 1) * 2], x1 = w[(j & 1) * 2 + 1];
-      const float f0 = clamp448(bf16_bits_to_f32(x0 & 0xFFFFu) * s);
-      const float f1 = clamp448(bf16_bits_to_f32(x0 >> 16) * s);
-      const float f2 = clamp448(bf16_bits_to_f32(x1 & 0xFFFFu) * s);
-      const float f3 = clamp448(bf16_bits_to_f32(x1 >> 16) * s);
-      o[j] = cvt_e4m3x2(f0, f1) | (cvt_e4m3x2(f2, f3) << 16);
+      const float f0 = bf16_bits_to_f32(x0 & 0xFFFFu) * s;
+      const float f1 = bf16_bits_to_f32(x0 >> 16) * s;
+      const float f2 = bf16_bits_to_f32(x1 & 0xFFFFu) * s;
+      const float f3 = bf16_bits_to_f32(x1 >> 16) * s;
+      o[j] = cvt_fp8x2<FMT>(f0, f1) | (cvt_fp8x2<FMT>(f2, f3) << 16);
     }
     reinterpret_cast<u32x4*>(Tq)[v] = o;
+  }
+}
+
+// Quantise the block T [R, C] (row stride ldt) with the scale of `amax`
+// into Tq [R, C] or, with TRANS, Tq [C, R] (row stride ldq). One workgroup
+// per 64 x 64 tile: thread t loads 16 consecutive elements of row t / 4 and
+// converts them; with TRANS the codes go through LDS ([column][row], rows of
+// 80 bytes) and thread t stores 16 consecutive codes of output row t / 4.
+// R and C are multiples of 16, so a 16-element chunk is either wholly inside
+// or wholly outside the block.
+template <int FMT, bool TRANS>
+__global__ __launch_bounds__(kThreads) void quant_fp8_tile_kernel(
+    const uint16_t* __restrict__ T, int64_t ldt, int R, int C, const float* __restrict__ amax,
+    uint8_t* __restrict__ Tq, int64_t ldq, float* __restrict__ scale) {
+  constexpr int kTile = 64, kStride = 80;
+  __shared__ __attribute__((aligned(16))) uint8_t tile[kTile * kStride];
+  const float s = quant_scale_of<FMT>(amax[0]);
+  if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) scale[0] = s;
+  const int t = threadIdx.x;
+  const int r = t >> 2, cc = (t & 3) * 16;
+  const int row = blockIdx.y * kTile + r, col = blockIdx.x * kTile + cc;
+  u32x4 o = {0u, 0u, 0u, 0u};
+  if (row < R && col < C) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(T + (int64_t)row * ldt + col);
+    const u32x4 w0 = src[0], w1 = src[1];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const u32x4& w = (j < 2) ? w0 : w1;
+      const uint32_t x0 = w[(j & 1) * 2], x1 = w[(j & 1) * 2 + 1];
+      o[j] = cvt_fp8x2<FMT>(bf16_bits_to_f32(x0 & 0xFFFFu) * s, bf16_bits_to_f32(x0 >> 16) * s) |
+             (cvt_fp8x2<FMT>(bf16_bits_to_f32(x1 & 0xFFFFu) * s, bf16_bits_to_f32(x1 >> 16) * s)
+              << 16);
+    }
+  }
+  if constexpr (!TRANS) {
+    if (row < R && col < C) *reinterpret_cast<u32x4*>(Tq + (int64_t)row * ldq + col) = o;
+  } else {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) tile[(cc + j) * kStride + r] = (uint8_t)(o[j >> 2] >> (8 * (j & 3)));
+    __syncthreads();
+    const int orow = blockIdx.x * kTile + r;   // a column of T
+    const int ocol = blockIdx.y * kTile + cc;  // rows of T
+    if (orow < C && ocol < R)
+      *reinterpret_cast<u32x4*>(Tq + (int64_t)orow * ldq + ocol) =
+          *reinterpret_cast<const u32x4*>(tile + r * kStride + cc);
   }
 }
 
@@ -179,12 +272,14 @@ __device__ __forceinline__ int q8_rot(int r) {
   else return ((r >> 1) & 1) + 2 * ((r >> 2) & 1) + 4 * ((r >> 5) & 1);
 }
 
-template <int BM, int BN, int OUT, bool KTAIL>
+// FP, FQ: fp8 formats of P and Q (0 = e4m3, 1 = e5m2).
+template <int BM, int BN, int OUT, bool KTAIL, int FP, int FQ>
 __global__ __launch_bounds__(kThreads) void gemm_e4m3_kernel(
     const uint8_t* __restrict__ P, int64_t ldp, const float* __restrict__ sP,
     const uint8_t* __restrict__ Q, int64_t ldq, const float* __restrict__ sQ,
     void* __restrict__ C, int64_t ldc, float* __restrict__ z_amax, const float* __restrict__ sC,
-    int M, int N, int K, int group_m) {
+    const float* __restrict__ aux, int64_t ldaux, void* __restrict__ C2,
+    float* __restrict__ z_amax2, int M, int N, int K, int group_m) {
   constexpr int TM = BM / 2, TN = BN / 2;      // wave tile (2 x 2 waves)
   constexpr int MT = TM / 16, NT = TN / 16;    // 16x16 MFMA tiles per wave
   constexpr int NH = NT / 2;                   // fragment columns of the first half k-step
@@ -327,7 +422,7 @@ __global__ __launch_bounds__(kThreads) void gemm_e4m3_kernel(
     for (int i = 0; i < NMH; ++i) {
       const int ni = i / MT, mi = i % MT;
       acc[ni][mi] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-          afr[ni], bfr[mi], acc[ni][mi], 0, 0, 0, 127, 0, 127);
+          afr[ni], bfr[mi], acc[ni][mi], FQ, FP, 0, 127, 0, 127);
 #pragma unroll
       for (int j = 0; j < NRA; ++j)
         if (j * NMH / NRA == i) read_q(rq, NH + j / 4, j % 4);
@@ -347,7 +442,7 @@ __global__ __launch_bounds__(kThreads) void gemm_e4m3_kernel(
     for (int i = 0; i < NMH; ++i) {
       const int mi = i / NH, ni = NH + i % NH;
       acc[ni][mi] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-          afr[ni], bfr[mi], acc[ni][mi], 0, 0, 0, 127, 0, 127);
+          afr[ni], bfr[mi], acc[ni][mi], FQ, FP, 0, 127, 0, 127);
       if (i % NH == NH - 1) {
         read_p(rp, mi, 0);
         read_p(rp, mi, 1);
@@ -405,9 +500,77 @@ __global__ __launch_bounds__(kThreads) void gemm_e4m3_kernel(
   waitcnt<0, 0>();  // no DMA may still write LDS when the workgroup ends
 
   // Epilogue: dequantise by 1/(sP·sQ); GeLU + bf16 + max|Z| (+ e4m3 with the
-  // given scale), or bf16. Lane holds, for 16x16 tile (ni, mi), C[m][n .. n+3]
-  // with m = mi·16 + (lane & 15), n = ni·16 + 4·(lane >> 4) (wave-tile relative).
+  // given scale), bf16, fp32, or (backward) dS = bf16(acc·GeLU'(S)) and
+  // Z = bf16(GeLU(S)) with max|dS| and max|Z|. Lane holds, for 16x16 tile
+  // (ni, mi), C[m][n .. n+3] with m = mi·16 + (lane & 15),
+  // n = ni·16 + 4·(lane >> 4) (wave-tile relative).
   const float dq = 1.0f / (sP[0] * sQ[0]);
+  if constexpr (OUT == (int)OutKind::F32) {
+#pragma unroll
+    for (int ni = 0; ni < NT; ++ni) {
+#pragma unroll
+      for (int mi = 0; mi < MT; ++mi) {
+        const int m = m0 + wm * TM + mi * 16 + (lane & 15);
+        const int n = n0 + wn * TN + ni * 16 + 4 * (lane >> 4);
+        if (m >= M || n >= N) continue;
+        f32x4 v = acc[ni][mi];
+        asm volatile("" : "+v"(v));
+        *reinterpret_cast<f32x4*>(static_cast<float*>(C) + (int64_t)m * ldc + n) = v * dq;
+      }
+    }
+    return;
+  }
+  if constexpr (OUT == (int)OutKind::GeluGradBf16) {
+    // The S loads of EB tiles are issued together (from clamped addresses, so
+    // they need no branch) and their latency is paid once per batch.
+    constexpr int EB = 8;
+    static_assert((NT * MT) % EB == 0, "epilogue batches");
+    float dsmax = 0.0f, gmax = 0.0f;
+#pragma unroll
+    for (int b0 = 0; b0 < NT * MT; b0 += EB) {
+      f32x4 svb[EB];
+#pragma unroll
+      for (int e = 0; e < EB; ++e) {
+        const int ni = (b0 + e) / MT, mi = (b0 + e) % MT;
+        const int m = min(m0 + wm * TM + mi * 16 + (lane & 15), M - 1);
+        const int n = min(n0 + wn * TN + ni * 16 + 4 * (lane >> 4), N - 4);
+        svb[e] = *reinterpret_cast<const f32x4*>(aux + (int64_t)m * ldaux + n);
+      }
+#pragma unroll
+      for (int e = 0; e < EB; ++e) {
+        const int ni = (b0 + e) / MT, mi = (b0 + e) % MT;
+        const int m = m0 + wm * TM + mi * 16 + (lane & 15);
+        const int n = n0 + wn * TN + ni * 16 + 4 * (lane >> 4);
+        f32x4 v = acc[ni][mi];
+        asm volatile("" : "+v"(v));
+        v *= dq;
+        if (m < M && n < N) {
+          const f32x4 sv = svb[e];
+          uint32_t db[4], zb[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            float g, dg;
+            gelu_and_grad(sv[e], g, dg);
+            db[e] = f32_to_bf16_rne(v[e] * dg);
+            zb[e] = f32_to_bf16_rne(g);
+            dsmax = fmaxf(dsmax, fabsf(bf16_bits_to_f32(db[e])));
+            gmax = fmaxf(gmax, fabsf(bf16_bits_to_f32(zb[e])));
+          }
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(C) + (int64_t)m * ldc + n) =
+              u32x2{db[0] | (db[1] << 16), db[2] | (db[3] << 16)};
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(C2) + (int64_t)m * ldc + n) =
+              u32x2{zb[0] | (zb[1] << 16), zb[2] | (zb[3] << 16)};
+        }
+      }
+    }
+    dsmax = wave_max(dsmax);
+    gmax = wave_max(gmax);
+    if (lane == 0) {
+      atomic_max_nonneg(z_amax, dsmax);
+      atomic_max_nonneg(z_amax2, gmax);
+    }
+    return;
+  }
   const float sc = OUT == (int)OutKind::GeluE4m3 ? sC[0] : 1.0f;
   float zmax = 0.0f;
 #pragma unroll
@@ -447,34 +610,47 @@ __global__ __launch_bounds__(kThreads) void gemm_e4m3_kernel(
 
 }  // namespace e4
 
-template <int BM, int BN, bool KTAIL>
-hipError_t launch_cfg(const uint8_t* P, int64_t ldp, const float* sP, const uint8_t* Q,
-                      int64_t ldq, const float* sQ, void* C, int64_t ldc, float* z_amax,
-                      const float* sC, int M, int N, int K, OutKind out, hipStream_t stream) {
-  const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+template <int BM, int BN, int OUT, bool KTAIL, int FP, int FQ>
+hipError_t launch_one(const Fp8GemmArgs& a, hipStream_t stream) {
+  const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   const int group_m = 4;
-  if (out == OutKind::GeluBf16)
-    hipLaunchKernelGGL((e4::gemm_e4m3_kernel<BM, BN, (int)OutKind::GeluBf16, KTAIL>), dim3(tiles),
-                       dim3(kThreads), 0, stream, P, ldp, sP, Q, ldq, sQ, C, ldc, z_amax, sC, M,
-                       N, K, group_m);
-  else if (out == OutKind::GeluE4m3)
-    hipLaunchKernelGGL((e4::gemm_e4m3_kernel<BM, BN, (int)OutKind::GeluE4m3, KTAIL>), dim3(tiles),
-                       dim3(kThreads), 0, stream, P, ldp, sP, Q, ldq, sQ, C, ldc, z_amax, sC, M,
-                       N, K, group_m);
-  else
-    hipLaunchKernelGGL((e4::gemm_e4m3_kernel<BM, BN, (int)OutKind::Bf16, KTAIL>), dim3(tiles),
-                       dim3(kThreads), 0, stream, P, ldp, sP, Q, ldq, sQ, C, ldc, z_amax, sC, M,
-                       N, K, group_m);
+  hipLaunchKernelGGL((e4::gemm_e4m3_kernel<BM, BN, OUT, KTAIL, FP, FQ>), dim3(tiles),
+                     dim3(kThreads), 0, stream, a.P, a.ldp, a.sP, a.Q, a.ldq, a.sQ, a.C, a.ldc,
+                     a.z_amax, a.sC, a.aux, a.ldaux, a.C2, a.z_amax2, a.M, a.N, a.K, group_m);
   return hipGetLastError();
 }
 
+// The (formats, epilogue) combinations the path uses: e4m3 x e4m3 for the
+// forward (GeLU, GeLU + e4m3, bf16) and the backward's recomputed S (fp32);
+// e5m2 P x e4m3 Q for dS (GeLU') and dX_i (fp32); e4m3 P x e5m2 Q for the
+// weight gradients (fp32).
+template <int BM, int BN, bool KTAIL>
+hipError_t launch_cfg(const Fp8GemmArgs& a, OutKind out, int fp, int fq, hipStream_t stream) {
+  if (fp == 0 && fq == 0) {
+    switch (out) {
+      case OutKind::GeluBf16: return launch_one<BM, BN, (int)OutKind::GeluBf16, KTAIL, 0, 0>(a, stream);
+      case OutKind::GeluE4m3: return launch_one<BM, BN, (int)OutKind::GeluE4m3, KTAIL, 0, 0>(a, stream);
+      case OutKind::Bf16: return launch_one<BM, BN, (int)OutKind::Bf16, KTAIL, 0, 0>(a, stream);
+      case OutKind::F32: return launch_one<BM, BN, (int)OutKind::F32, KTAIL, 0, 0>(a, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  if (fp == 1 && fq == 0) {
+    switch (out) {
+      case OutKind::GeluGradBf16: return launch_one<BM, BN, (int)OutKind::GeluGradBf16, KTAIL, 1, 0>(a, stream);
+      case OutKind::F32: return launch_one<BM, BN, (int)OutKind::F32, KTAIL, 1, 0>(a, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  if (fp == 0 && fq == 1 && out == OutKind::F32)
+    return launch_one<BM, BN, (int)OutKind::F32, KTAIL, 0, 1>(a, stream);
+  return hipErrorInvalidValue;
+}
+
 template <int BM, int BN>
-hipError_t launch_tile(const uint8_t* P, int64_t ldp, const float* sP, const uint8_t* Q,
-                       int64_t ldq, const float* sQ, void* C, int64_t ldc, float* z_amax,
-                       const float* sC, int M, int N, int K, OutKind out, hipStream_t stream) {
-  if (K % e4::BK == 0)
-    return launch_cfg<BM, BN, false>(P, ldp, sP, Q, ldq, sQ, C, ldc, z_amax, sC, M, N, K, out, stream);
-  return launch_cfg<BM, BN, true>(P, ldp, sP, Q, ldq, sQ, C, ldc, z_amax, sC, M, N, K, out, stream);
+hipError_t launch_tile(const Fp8GemmArgs& a, OutKind out, int fp, int fq, hipStream_t stream) {
+  if (a.K % e4::BK == 0) return launch_cfg<BM, BN, false>(a, out, fp, fq, stream);
+  return launch_cfg<BM, BN, true>(a, out, fp, fq, stream);
 }
 
 int64_t grid_for(int64_t nvec) {
@@ -493,15 +669,42 @@ hipError_t launch_fill_f32(float* p, float v, hipStream_t stream) {
 hipError_t launch_amax_bf16(const uint16_t* T, int64_t numel, float* amax, hipStream_t stream) {
   hipError_t e = launch_fill_f32(amax, 0.0f, stream);
   if (e != hipSuccess || numel == 0) return e;
-  hipLaunchKernelGGL(amax_bf16_kernel, dim3((unsigned)grid_for(numel / 8)), dim3(kThreads), 0,
-                     stream, T, numel, amax);
+  // four vectors per thread per step; up to 4 workgroups per CU (one atomic each)
+  int64_t blocks = (numel / 8 + 4 * kThreads - 1) / (4 * kThreads);
+  blocks = blocks < 1 ? 1 : (blocks > 256 * 4 ? 256 * 4 : blocks);
+  hipLaunchKernelGGL(amax_bf16_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, T,
+                     numel, amax);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_fp8(int fmt, const uint16_t* T, int64_t numel, const float* amax,
+                            uint8_t* Tq, float* scale, hipStream_t stream) {
+  const dim3 grid((unsigned)grid_for(numel / 16));
+  if (fmt == 0)
+    hipLaunchKernelGGL(quant_fp8_kernel<0>, grid, dim3(kThreads), 0, stream, T, numel, amax, Tq, scale);
+  else
+    hipLaunchKernelGGL(quant_fp8_kernel<1>, grid, dim3(kThreads), 0, stream, T, numel, amax, Tq, scale);
   return hipGetLastError();
 }
 
 hipError_t launch_quant_e4m3(const uint16_t* T, int64_t numel, const float* amax, uint8_t* Tq,
                              float* scale, hipStream_t stream) {
-  hipLaunchKernelGGL(quant_e4m3_kernel, dim3((unsigned)grid_for(numel / 16)), dim3(kThreads), 0,
-                     stream, T, numel, amax, Tq, scale);
+  return launch_quant_fp8(0, T, numel, amax, Tq, scale, stream);
+}
+
+hipError_t launch_quant_fp8_tile(int fmt, bool trans, const uint16_t* T, int64_t ldt, int R, int C,
+                                 const float* amax, uint8_t* Tq, int64_t ldq, float* scale,
+                                 hipStream_t stream) {
+  if (R == 0 || C == 0) return hipSuccess;
+  const dim3 grid((unsigned)((C + 63) / 64), (unsigned)((R + 63) / 64));
+  if (fmt == 0 && trans)
+    hipLaunchKernelGGL((quant_fp8_tile_kernel<0, true>), grid, dim3(kThreads), 0, stream, T, ldt, R, C, amax, Tq, ldq, scale);
+  else if (fmt == 0)
+    hipLaunchKernelGGL((quant_fp8_tile_kernel<0, false>), grid, dim3(kThreads), 0, stream, T, ldt, R, C, amax, Tq, ldq, scale);
+  else if (trans)
+    hipLaunchKernelGGL((quant_fp8_tile_kernel<1, true>), grid, dim3(kThreads), 0, stream, T, ldt, R, C, amax, Tq, ldq, scale);
+  else
+    hipLaunchKernelGGL((quant_fp8_tile_kernel<1, false>), grid, dim3(kThreads), 0, stream, T, ldt, R, C, amax, Tq, ldq, scale);
   return hipGetLastError();
 }
 
@@ -512,15 +715,15 @@ hipError_t launch_amax_history_push(float* history, uint32_t* count, int L, cons
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_e4m3(const uint8_t* P, int64_t ldp, const float* sP, const uint8_t* Q,
-                            int64_t ldq, const float* sQ, void* C, int64_t ldc, float* z_amax,
-                            const float* sC, int M, int N, int K, OutKind out,
-                            hipStream_t stream) {
-  if (z_amax != nullptr) {
-    hipError_t e = launch_fill_f32(z_amax, 0.0f, stream);
-    if (e != hipSuccess) return e;
+hipError_t launch_gemm_fp8(const Fp8GemmArgs& a, OutKind out, int fp, int fq,
+                           hipStream_t stream) {
+  for (float* am : {a.z_amax, a.z_amax2}) {
+    if (am != nullptr) {
+      hipError_t e = launch_fill_f32(am, 0.0f, stream);
+      if (e != hipSuccess) return e;
+    }
   }
-  if (M == 0 || N == 0) return hipSuccess;
+  if (a.M == 0 || a.N == 0) return hipSuccess;
   // Tile shape with the best estimated time: waves of 256 CUs times a
   // per-tile time relative to a 256x256 tile (smaller tiles reuse each LDS
   // byte less, so their cost falls slower than their area).
@@ -529,15 +732,22 @@ hipError_t launch_gemm_e4m3(const uint8_t* P, int64_t ldp, const float* sP, cons
   double best = 1e300;
   int pick = 0;
   for (int i = 0; i < 3; ++i) {
-    const long tiles = (long)((M + cands[i].bm - 1) / cands[i].bm) * ((N + cands[i].bn - 1) / cands[i].bn);
+    const long tiles = (long)((a.M + cands[i].bm - 1) / cands[i].bm) * ((a.N + cands[i].bn - 1) / cands[i].bn);
     const double est = (double)((tiles + 255) / 256) * cands[i].cost;
     if (est < best - 1e-9) { best = est; pick = i; }
   }
-  if (pick == 0)
-    return launch_tile<256, 256>(P, ldp, sP, Q, ldq, sQ, C, ldc, z_amax, sC, M, N, K, out, stream);
-  if (pick == 1)
-    return launch_tile<256, 192>(P, ldp, sP, Q, ldq, sQ, C, ldc, z_amax, sC, M, N, K, out, stream);
-  return launch_tile<128, 128>(P, ldp, sP, Q, ldq, sQ, C, ldc, z_amax, sC, M, N, K, out, stream);
+  if (pick == 0) return launch_tile<256, 256>(a, out, fp, fq, stream);
+  if (pick == 1) return launch_tile<256, 192>(a, out, fp, fq, stream);
+  return launch_tile<128, 128>(a, out, fp, fq, stream);
+}
+
+hipError_t launch_gemm_e4m3(const uint8_t* P, int64_t ldp, const float* sP, const uint8_t* Q,
+                            int64_t ldq, const float* sQ, void* C, int64_t ldc, float* z_amax,
+                            const float* sC, int M, int N, int K, OutKind out,
+                            hipStream_t stream) {
+  const Fp8GemmArgs a{P, ldp, sP, Q, ldq, sQ, C, ldc, z_amax, sC, nullptr, 0, nullptr, nullptr,
+                      M, N, K};
+  return launch_gemm_fp8(a, out, 0, 0, stream);
 }
 
 }  // namespace tpmlp

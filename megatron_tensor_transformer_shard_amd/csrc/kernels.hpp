@@ -62,6 +62,34 @@ hipError_t launch_quant_e4m3(const uint16_t* T, int64_t numel, const float* amax
 // C = epilogue((P·Q) / (sP·sQ)); GeluBf16 also folds max|Z| into z_amax when
 // z_amax is not NULL; Bf16 stores bf16; GeluE4m3 stores e4m3(bf16(GeLU)·sC[0])
 // bytes (ldc in bytes) and folds max|bf16(GeLU)| into z_amax.
+// fp8 GEMM C = epilogue((P·Q)/(sP·sQ)) with P [M, K] (row stride ldp) and Q
+// [K, N] (row stride ldq) as fp8 codes of formats fp and fq (0 = e4m3, 1 =
+// e5m2). z_amax (and z_amax2) are zeroed on the stream first when given.
+// Epilogues: GeluBf16 / GeluE4m3 / Bf16 (e4m3 x e4m3, z_amax = max|Z|, sC the
+// e4m3 scale of Z), F32 (any of the format pairs used), GeluGradBf16 (e5m2 P x
+// e4m3 Q: C = bf16(acc·GeLU'(S)) with S from aux [M, N] fp32, C2 = bf16(GeLU(S)),
+// z_amax = max|C|, z_amax2 = max|C2|).
+struct Fp8GemmArgs {
+  const uint8_t* P; int64_t ldp; const float* sP;
+  const uint8_t* Q; int64_t ldq; const float* sQ;
+  void* C; int64_t ldc; float* z_amax; const float* sC;
+  const float* aux; int64_t ldaux; void* C2; float* z_amax2;
+  int M, N, K;
+};
+hipError_t launch_gemm_fp8(const Fp8GemmArgs& a, OutKind out, int fp, int fq,
+                           hipStream_t stream);
+
+// Tq = fp8 codes (format fmt) of T·s, s = MAX/amax (448 for e4m3, 57344 for
+// e5m2; 1 if amax = 0), clamped to ±MAX, RNE; scale[0] = s. numel % 16 == 0
+// handled in vector steps (the caller guarantees it).
+hipError_t launch_quant_fp8(int fmt, const uint16_t* T, int64_t numel, const float* amax,
+                            uint8_t* Tq, float* scale, hipStream_t stream);
+// The same for the block T [R, C] (row stride ldt), written to Tq [R, C] or,
+// with trans, Tq [C, R] (row stride ldq). R and C multiples of 16.
+hipError_t launch_quant_fp8_tile(int fmt, bool trans, const uint16_t* T, int64_t ldt, int R, int C,
+                                 const float* amax, uint8_t* Tq, int64_t ldq, float* scale,
+                                 hipStream_t stream);
+
 hipError_t launch_gemm_e4m3(const uint8_t* P, int64_t ldp, const float* sP, const uint8_t* Q,
                             int64_t ldq, const float* sQ, void* C, int64_t ldc, float* z_amax,
                             const float* sC, int M, int N, int K, OutKind out,

@@ -261,6 +261,30 @@ def test_backward_validation():
     assert bw(dB=BASE + GB + 1024) == EALIAS       # dB_i inside A
 
 
+def test_backward_fp8_validation():
+    M, d, H, N = 32, 64, 256, 2
+    ws = L.tp_mlp_shard_backward_fp8_workspace_size(M, d, H, N)
+    assert ws > 0 and L.tp_mlp_shard_backward_fp8_workspace_size(M, d, H, 3) == 0
+
+    def bw(**kw):
+        a = dict(X=BASE, A=BASE + GB, B=BASE + 2 * GB, dY=BASE + 3 * GB, dX=BASE + 4 * GB,
+                 dA=BASE + 5 * GB, dB=BASE + 6 * GB, M=M, d=d, H=H, N=N, rank=0,
+                 ws=BASE + 7 * GB, wsb=ws)
+        a.update(kw)
+        return L.tp_mlp_shard_backward_fp8(a["X"], a["A"], a["B"], a["dY"], a["dX"], a["dA"],
+                                           a["dB"], a["M"], a["d"], a["H"], a["N"], a["rank"],
+                                           a["ws"], a["wsb"], None)
+    assert bw(M=0) == OK
+    assert bw(rank=2) == EARG
+    assert bw(M=24) == ESHAPE             # fp8 rows of the transposed copies: multiple of 16
+    assert bw(d=72) == ESHAPE
+    assert bw(N=32) == ESHAPE             # F = 8
+    assert bw(dX=None) == ENULL
+    assert bw(wsb=ws - 1) == EWS
+    assert bw(dB=BASE + 2 * GB + 32) == EALIAS
+    assert bw(ws=BASE + 4 * GB) == EALIAS
+
+
 def test_attention_validation():
     # tp_attn_heads
     def heads(QKV=BASE, ld=3 * 256, O=BASE + GB, ldo=256, B=2, S=40, h=2, causal=1):

@@ -97,6 +97,12 @@ WORKLOADS = {
                            tags=("backward",),
                            description="backward of 7b_tp8: dY[8192x4096]; per rank S, dS, "
                                        "dX_i, dA_i[4096x2048], dB_i[2048x4096]; sum of dX_i"),
+    # The same backward with fp8 GEMMs in the hybrid formats (E4M3 activations
+    # and weights, E5M2 gradients, current amax scales).
+    "7b_tp8_bwd_fp8": Workload("7b_tp8_bwd_fp8", M=8192, d=4096, H=16384, N=8, sigma=0.02,
+                               seed=2, fp8=True, tags=("backward",),
+                               description="7b_tp8_bwd with fp8 GEMMs: X, A_i, B_i, Z in e4m3, "
+                                           "dY, dS in e5m2; sum of dX_i"),
 }
 
 
