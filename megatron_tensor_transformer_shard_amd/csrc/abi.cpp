@@ -605,13 +605,14 @@ int tp_mlp_shard_backward_fp8(const void* X, const void* A, const void* B, const
   run(tpmlp::launch_gemm_fp8(Fp8GemmArgs{dSq, F, sc + 4, AqT, d, sc + 1, dX_i, d, nullptr,
                                          nullptr, nullptr, 0, nullptr, nullptr, m, dd, f},
                              OutKind::F32, E5, E4, s));
-  // dB_i = (Zqᵀ·dYq)/(sZ·sdY), dA_i = (Xqᵀ·dSq)/(sX·sdS)
-  run(tpmlp::launch_gemm_fp8(Fp8GemmArgs{ZqT, M, sc + 5, dYq, d, sc + 3, dB_i, d, nullptr,
-                                         nullptr, nullptr, 0, nullptr, nullptr, f, dd, m},
-                             OutKind::F32, E4, E5, s));
-  run(tpmlp::launch_gemm_fp8(Fp8GemmArgs{XqT, M, sc + 0, dSq, F, sc + 4, dA_i, F, nullptr,
-                                         nullptr, nullptr, 0, nullptr, nullptr, dd, f, m},
-                             OutKind::F32, E4, E5, s));
+  // dB_i = (Zqᵀ·dYq)/(sZ·sdY) and dA_i = (Xqᵀ·dSq)/(sX·sdS) in one launch: each
+  // alone has too few output tiles to fill the chip
+  run(tpmlp::launch_gemm_fp8_pair(
+      Fp8GemmArgs{ZqT, M, sc + 5, dYq, d, sc + 3, dB_i, d, nullptr, nullptr, nullptr, 0, nullptr,
+                  nullptr, f, dd, m},
+      Fp8GemmArgs{XqT, M, sc + 0, dSq, F, sc + 4, dA_i, F, nullptr, nullptr, nullptr, 0, nullptr,
+                  nullptr, dd, f, m},
+      OutKind::F32, E4, E5, s));
   return status_of(e);
 }
 

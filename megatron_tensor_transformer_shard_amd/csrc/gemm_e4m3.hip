@@ -272,14 +272,12 @@ __device__ __forceinline__ int q8_rot(int r) {
   else return ((r >> 1) & 1) + 2 * ((r >> 2) & 1) + 4 * ((r >> 5) & 1);
 }
 
-// FP, FQ: fp8 formats of P and Q (0 = e4m3, 1 = e5m2).
+// FP, FQ: fp8 formats of P and Q (0 = e4m3, 1 = e5m2). Workgroups [0, tiles0)
+// compute problem g0, the rest problem g1 (a launch of one problem passes
+// tiles0 = its tile count).
 template <int BM, int BN, int OUT, bool KTAIL, int FP, int FQ>
-__global__ __launch_bounds__(kThreads) void gemm_e4m3_kernel(
-    const uint8_t* __restrict__ P, int64_t ldp, const float* __restrict__ sP,
-    const uint8_t* __restrict__ Q, int64_t ldq, const float* __restrict__ sQ,
-    void* __restrict__ C, int64_t ldc, float* __restrict__ z_amax, const float* __restrict__ sC,
-    const float* __restrict__ aux, int64_t ldaux, void* __restrict__ C2,
-    float* __restrict__ z_amax2, int M, int N, int K, int group_m) {
+__global__ __launch_bounds__(kThreads) void gemm_e4m3_kernel(Fp8GemmArgs g0, Fp8GemmArgs g1,
+                                                             int tiles0, int group_m) {
   constexpr int TM = BM / 2, TN = BN / 2;      // wave tile (2 x 2 waves)
   constexpr int MT = TM / 16, NT = TN / 16;    // 16x16 MFMA tiles per wave
   constexpr int NH = NT / 2;                   // fragment columns of the first half k-step
@@ -299,9 +297,26 @@ __global__ __launch_bounds__(kThreads) void gemm_e4m3_kernel(
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[NSP * P_BYTES + NSQ * Q_BYTES];
 
+  int id = xcd_remap(blockIdx.x, gridDim.x);
+  const bool second = id >= tiles0;
+  const Fp8GemmArgs& g = second ? g1 : g0;
+  if (second) id -= tiles0;
+  const uint8_t* const P = g.P;
+  const uint8_t* const Q = g.Q;
+  const float* const sP = g.sP;
+  const float* const sQ = g.sQ;
+  void* const C = g.C;
+  void* const C2 = g.C2;
+  float* const z_amax = g.z_amax;
+  float* const z_amax2 = g.z_amax2;
+  const float* const sC = g.sC;
+  const float* const aux = g.aux;
+  const int64_t ldp = g.ldp, ldq = g.ldq, ldc = g.ldc, ldaux = g.ldaux;
+  const int M = g.M, N = g.N, K = g.K;
+
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   int tm, tn;
-  grouped_tile(xcd_remap(blockIdx.x, gridDim.x), tiles_m, tiles_n, group_m, tm, tn);
+  grouped_tile(id, tiles_m, tiles_n, group_m, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
 
   const int t = threadIdx.x;
@@ -610,13 +625,19 @@ __global__ __launch_bounds__(kThreads) void gemm_e4m3_kernel(
 
 }  // namespace e4
 
+template <int BM, int BN>
+int tile_count(const Fp8GemmArgs& a) {
+  return ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+}
+
+// One launch over problems a[0 .. n) (n = 1 or 2).
 template <int BM, int BN, int OUT, bool KTAIL, int FP, int FQ>
-hipError_t launch_one(const Fp8GemmArgs& a, hipStream_t stream) {
-  const int tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+hipError_t launch_one(const Fp8GemmArgs* a, int n, hipStream_t stream) {
+  const int t0 = tile_count<BM, BN>(a[0]);
+  const int tiles = t0 + (n > 1 ? tile_count<BM, BN>(a[1]) : 0);
   const int group_m = 4;
   hipLaunchKernelGGL((e4::gemm_e4m3_kernel<BM, BN, OUT, KTAIL, FP, FQ>), dim3(tiles),
-                     dim3(kThreads), 0, stream, a.P, a.ldp, a.sP, a.Q, a.ldq, a.sQ, a.C, a.ldc,
-                     a.z_amax, a.sC, a.aux, a.ldaux, a.C2, a.z_amax2, a.M, a.N, a.K, group_m);
+                     dim3(kThreads), 0, stream, a[0], n > 1 ? a[1] : a[0], t0, group_m);
   return hipGetLastError();
 }
 
@@ -625,32 +646,35 @@ hipError_t launch_one(const Fp8GemmArgs& a, hipStream_t stream) {
 // e5m2 P x e4m3 Q for dS (GeLU') and dX_i (fp32); e4m3 P x e5m2 Q for the
 // weight gradients (fp32).
 template <int BM, int BN, bool KTAIL>
-hipError_t launch_cfg(const Fp8GemmArgs& a, OutKind out, int fp, int fq, hipStream_t stream) {
+hipError_t launch_cfg(const Fp8GemmArgs* a, int n, OutKind out, int fp, int fq, hipStream_t stream) {
   if (fp == 0 && fq == 0) {
     switch (out) {
-      case OutKind::GeluBf16: return launch_one<BM, BN, (int)OutKind::GeluBf16, KTAIL, 0, 0>(a, stream);
-      case OutKind::GeluE4m3: return launch_one<BM, BN, (int)OutKind::GeluE4m3, KTAIL, 0, 0>(a, stream);
-      case OutKind::Bf16: return launch_one<BM, BN, (int)OutKind::Bf16, KTAIL, 0, 0>(a, stream);
-      case OutKind::F32: return launch_one<BM, BN, (int)OutKind::F32, KTAIL, 0, 0>(a, stream);
+      case OutKind::GeluBf16: return launch_one<BM, BN, (int)OutKind::GeluBf16, KTAIL, 0, 0>(a, n, stream);
+      case OutKind::GeluE4m3: return launch_one<BM, BN, (int)OutKind::GeluE4m3, KTAIL, 0, 0>(a, n, stream);
+      case OutKind::Bf16: return launch_one<BM, BN, (int)OutKind::Bf16, KTAIL, 0, 0>(a, n, stream);
+      case OutKind::F32: return launch_one<BM, BN, (int)OutKind::F32, KTAIL, 0, 0>(a, n, stream);
       default: return hipErrorInvalidValue;
     }
   }
   if (fp == 1 && fq == 0) {
     switch (out) {
-      case OutKind::GeluGradBf16: return launch_one<BM, BN, (int)OutKind::GeluGradBf16, KTAIL, 1, 0>(a, stream);
-      case OutKind::F32: return launch_one<BM, BN, (int)OutKind::F32, KTAIL, 1, 0>(a, stream);
+      case OutKind::GeluGradBf16: return launch_one<BM, BN, (int)OutKind::GeluGradBf16, KTAIL, 1, 0>(a, n, stream);
+      case OutKind::F32: return launch_one<BM, BN, (int)OutKind::F32, KTAIL, 1, 0>(a, n, stream);
       default: return hipErrorInvalidValue;
     }
   }
   if (fp == 0 && fq == 1 && out == OutKind::F32)
-    return launch_one<BM, BN, (int)OutKind::F32, KTAIL, 0, 1>(a, stream);
+    return launch_one<BM, BN, (int)OutKind::F32, KTAIL, 0, 1>(a, n, stream);
   return hipErrorInvalidValue;
 }
 
 template <int BM, int BN>
-hipError_t launch_tile(const Fp8GemmArgs& a, OutKind out, int fp, int fq, hipStream_t stream) {
-  if (a.K % e4::BK == 0) return launch_cfg<BM, BN, false>(a, out, fp, fq, stream);
-  return launch_cfg<BM, BN, true>(a, out, fp, fq, stream);
+hipError_t launch_tile(const Fp8GemmArgs* a, int n, OutKind out, int fp, int fq,
+                       hipStream_t stream) {
+  bool tail = false;
+  for (int i = 0; i < n; ++i) tail = tail || a[i].K % e4::BK != 0;
+  if (!tail) return launch_cfg<BM, BN, false>(a, n, out, fp, fq, stream);
+  return launch_cfg<BM, BN, true>(a, n, out, fp, fq, stream);
 }
 
 int64_t grid_for(int64_t nvec) {
@@ -715,30 +739,57 @@ hipError_t launch_amax_history_push(float* history, uint32_t* count, int L, cons
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_fp8(const Fp8GemmArgs& a, OutKind out, int fp, int fq,
-                           hipStream_t stream) {
-  for (float* am : {a.z_amax, a.z_amax2}) {
-    if (am != nullptr) {
-      hipError_t e = launch_fill_f32(am, 0.0f, stream);
-      if (e != hipSuccess) return e;
-    }
-  }
-  if (a.M == 0 || a.N == 0) return hipSuccess;
-  // Tile shape with the best estimated time: waves of 256 CUs times a
-  // per-tile time relative to a 256x256 tile (smaller tiles reuse each LDS
-  // byte less, so their cost falls slower than their area).
+namespace {
+// Zero the amax outputs, then launch problems a[0 .. n) with the tile shape of
+// the best estimated time: waves of 256 CUs times a per-tile time relative to
+// a 256x256 tile (smaller tiles reuse each LDS byte less, so their cost falls
+// slower than their area).
+hipError_t launch_group(const Fp8GemmArgs* a, int n, OutKind out, int fp, int fq,
+                        hipStream_t stream) {
+  for (int i = 0; i < n; ++i)
+    for (float* am : {a[i].z_amax, a[i].z_amax2})
+      if (am != nullptr) {
+        hipError_t e = launch_fill_f32(am, 0.0f, stream);
+        if (e != hipSuccess) return e;
+      }
   static const struct { int bm, bn; double cost; } cands[] = {
       {256, 256, 1.00}, {256, 192, 0.85}, {128, 128, 0.30}};
   double best = 1e300;
   int pick = 0;
-  for (int i = 0; i < 3; ++i) {
-    const long tiles = (long)((a.M + cands[i].bm - 1) / cands[i].bm) * ((a.N + cands[i].bn - 1) / cands[i].bn);
-    const double est = (double)((tiles + 255) / 256) * cands[i].cost;
-    if (est < best - 1e-9) { best = est; pick = i; }
+  for (int c = 0; c < 3; ++c) {
+    long tiles = 0;
+    for (int i = 0; i < n; ++i)
+      tiles += (long)((a[i].M + cands[c].bm - 1) / cands[c].bm) * ((a[i].N + cands[c].bn - 1) / cands[c].bn);
+    const double est = (double)((tiles + 255) / 256) * cands[c].cost;
+    if (est < best - 1e-9) { best = est; pick = c; }
   }
-  if (pick == 0) return launch_tile<256, 256>(a, out, fp, fq, stream);
-  if (pick == 1) return launch_tile<256, 192>(a, out, fp, fq, stream);
-  return launch_tile<128, 128>(a, out, fp, fq, stream);
+  if (pick == 0) return launch_tile<256, 256>(a, n, out, fp, fq, stream);
+  if (pick == 1) return launch_tile<256, 192>(a, n, out, fp, fq, stream);
+  return launch_tile<128, 128>(a, n, out, fp, fq, stream);
+}
+}  // namespace
+
+hipError_t launch_gemm_fp8(const Fp8GemmArgs& a, OutKind out, int fp, int fq,
+                           hipStream_t stream) {
+  if (a.M == 0 || a.N == 0) {
+    for (float* am : {a.z_amax, a.z_amax2})
+      if (am != nullptr) {
+        hipError_t e = launch_fill_f32(am, 0.0f, stream);
+        if (e != hipSuccess) return e;
+      }
+    return hipSuccess;
+  }
+  return launch_group(&a, 1, out, fp, fq, stream);
+}
+
+hipError_t launch_gemm_fp8_pair(const Fp8GemmArgs& x, const Fp8GemmArgs& y, OutKind out, int fp,
+                                int fq, hipStream_t stream) {
+  Fp8GemmArgs a[2];
+  int n = 0;
+  for (const Fp8GemmArgs* g : {&x, &y})
+    if (g->M > 0 && g->N > 0) a[n++] = *g;
+  if (n == 0) return hipSuccess;
+  return launch_group(a, n, out, fp, fq, stream);
 }
 
 hipError_t launch_gemm_e4m3(const uint8_t* P, int64_t ldp, const float* sP, const uint8_t* Q,

@@ -78,6 +78,9 @@ struct Fp8GemmArgs {
 };
 hipError_t launch_gemm_fp8(const Fp8GemmArgs& a, OutKind out, int fp, int fq,
                            hipStream_t stream);
+// Two independent fp8 GEMMs of one format pair and epilogue in one launch.
+hipError_t launch_gemm_fp8_pair(const Fp8GemmArgs& x, const Fp8GemmArgs& y, OutKind out, int fp,
+                                int fq, hipStream_t stream);
 
 // Tq = fp8 codes (format fmt) of T·s, s = MAX/amax (448 for e4m3, 57344 for
 // e5m2; 1 if amax = 0), clamped to ±MAX, RNE; scale[0] = s. numel % 16 == 0
