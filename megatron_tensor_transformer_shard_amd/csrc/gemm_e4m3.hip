@@ -275,6 +275,30 @@ __device__ __forceinline__ int q8_rot(int r) {
 // FP, FQ: fp8 formats of P and Q (0 = e4m3, 1 = e5m2). Workgroups [0, tiles0)
 // compute problem g0, the rest problem g1 (a launch of one problem passes
 // tiles0 = its tile count).
+// Combine the workgroup's per-lane maxima a (and b) and add them to *pa (and
+// *pb) with one atomic each: atomics on one address serialise, so one per
+// workgroup rather than one per wave. Called by every wave after the
+// epilogue; the first barrier also ensures that no wave still reads the LDS
+// stages and that every wave's DMA has landed (each waited for it after its
+// main loop), so the stage memory can hold the partial maxima.
+__device__ __forceinline__ void block_max_to(uint8_t* smem, int wave, int lane, float a, float b,
+                                             float* pa, float* pb) {
+  a = wave_max(a);
+  b = wave_max(b);
+  float* red = reinterpret_cast<float*>(smem);
+  barrier();
+  if (lane == 0) {
+    red[wave] = a;
+    red[4 + wave] = b;
+  }
+  waitcnt<0, 0>();
+  barrier();
+  if (wave == 0 && lane == 0) {
+    atomic_max_nonneg(pa, fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
+    if (pb != nullptr) atomic_max_nonneg(pb, fmaxf(fmaxf(red[4], red[5]), fmaxf(red[6], red[7])));
+  }
+}
+
 template <int BM, int BN, int OUT, bool KTAIL, int FP, int FQ>
 __global__ __launch_bounds__(kThreads) void gemm_e4m3_kernel(Fp8GemmArgs g0, Fp8GemmArgs g1,
                                                              int tiles0, int group_m) {
@@ -578,12 +602,7 @@ __global__ __launch_bounds__(kThreads) void gemm_e4m3_kernel(Fp8GemmArgs g0, Fp8
         }
       }
     }
-    dsmax = wave_max(dsmax);
-    gmax = wave_max(gmax);
-    if (lane == 0) {
-      atomic_max_nonneg(z_amax, dsmax);
-      atomic_max_nonneg(z_amax2, gmax);
-    }
+    block_max_to(smem, wave, lane, dsmax, gmax, z_amax, z_amax2);
     return;
   }
   const float sc = OUT == (int)OutKind::GeluE4m3 ? sC[0] : 1.0f;
@@ -617,10 +636,7 @@ __global__ __launch_bounds__(kThreads) void gemm_e4m3_kernel(Fp8GemmArgs g0, Fp8
       }
     }
   }
-  if (GELU && z_amax != nullptr) {
-    zmax = wave_max(zmax);
-    if (lane == 0) atomic_max_nonneg(z_amax, zmax);
-  }
+  if (GELU && z_amax != nullptr) block_max_to(smem, wave, lane, zmax, 0.0f, z_amax, nullptr);
 }
 
 }  // namespace e4
