@@ -1,0 +1,87 @@
+"""The C-ABI entry points under HIP graph capture: every call only enqueues
+kernels on the caller's stream (amax outputs are cleared by a fill kernel,
+never by a memset), so a captured step replays to the same bits as the eager
+one. Each replay is preceded by eager work on the outputs and followed by a
+synchronisation, and every replay is compared with the eager result."""
+import numpy as np
+import pytest
+
+from helpers import dev_bf16, log
+from workloads import make_output_grad, make_random
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def tpm():
+    import torch
+    import megatron_tensor_transformer_shard_amd as m
+    assert torch.cuda.is_available()
+    return m
+
+
+def _replay_and_compare(step, outputs, reps=3):
+    import torch
+    # eager reference
+    step()
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in outputs]
+    # capture (after a warm-up on the capture's side stream)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(reps):
+        for o in outputs:
+            o.fill_(float("nan"))           # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (o, r) in enumerate(zip(outputs, ref)):
+            assert torch.equal(o, r), f"replay {rep}: output {i} differs from the eager result"
+        log(f"replay {rep}: {len(outputs)} outputs equal to eager")
+
+
+def test_forward_step_in_a_graph(tpm):
+    import torch
+    M, d, H, N = 300, 136, 544, 2
+    X, A, B = make_random(M, d, H, seed=31, sigma=0.05)
+    Xd, Ad, Bd = dev_bf16(X), dev_bf16(A), dev_bf16(B)
+    parts = [torch.empty((M, d), dtype=torch.float32, device="cuda") for _ in range(N)]
+    ws = [torch.empty(tpm.tp_mlp_shard_workspace_size(M, d, H, N), dtype=torch.uint8,
+                      device="cuda") for _ in range(N)]
+    Y = torch.empty((M, d), dtype=torch.float32, device="cuda")
+
+    def step():
+        for r in range(N):
+            tpm.tp_mlp_shard(Xd, Ad, Bd, N, r, Y_i=parts[r], workspace=ws[r])
+        tpm.tp_partial_sum(parts, Y=Y)
+    _replay_and_compare(step, parts + [Y])
+
+
+def test_backward_bf16_and_fp8_in_a_graph(tpm):
+    import torch
+    M, d, H, N = 272, 144, 576, 2
+    F = H // N
+    X, A, B = make_random(M, d, H, seed=32, sigma=0.05)
+    dY = make_output_grad(M, d, seed=33)
+    Xd, Ad, Bd, dYd = dev_bf16(X), dev_bf16(A), dev_bf16(B), dev_bf16(dY)
+    outs = [torch.empty(shp, dtype=torch.float32, device="cuda")
+            for _ in range(2) for shp in ((M, d), (d, F), (F, d))]
+    ws16 = torch.empty(tpm.tp_mlp_shard_backward_workspace_size(M, d, H, N), dtype=torch.uint8,
+                       device="cuda")
+    ws8 = torch.empty(tpm.tp_mlp_shard_backward_fp8_workspace_size(M, d, H, N), dtype=torch.uint8,
+                      device="cuda")
+
+    def step():
+        tpm.tp_mlp_shard_backward(Xd, Ad, Bd, dYd, N, 1, dX_i=outs[0], dA_i=outs[1], dB_i=outs[2],
+                                  workspace=ws16)
+        tpm.tp_mlp_shard_backward_fp8(Xd, Ad, Bd, dYd, N, 1, dX_i=outs[3], dA_i=outs[4],
+                                      dB_i=outs[5], workspace=ws8)
+    _replay_and_compare(step, outs)
