@@ -579,11 +579,13 @@ int tp_mlp_shard_backward_fp8(const void* X, const void* A, const void* B, const
   constexpr int E4 = 0, E5 = 1;
   hipError_t e = hipSuccess;
   auto run = [&](hipError_t r) { if (e == hipSuccess) e = r; };
-  // per-tensor amax scales: X, the whole of A and B (as in the fp8 forward), dY
-  run(tpmlp::launch_amax_bf16(x, M * d, am + 0, s));
-  run(tpmlp::launch_amax_bf16(static_cast<const uint16_t*>(A), d * H, am + 1, s));
-  run(tpmlp::launch_amax_bf16(static_cast<const uint16_t*>(B), H * d, am + 2, s));
-  run(tpmlp::launch_amax_bf16(dy, M * d, am + 3, s));
+  // per-tensor amax scales: X, the whole of A and B (as in the fp8 forward), dY;
+  // the six amax slots (these four, then dS and Z) are cleared by one kernel
+  run(tpmlp::launch_fill_f32(am, 0.0f, s, 6));
+  run(tpmlp::launch_amax_bf16(x, M * d, am + 0, s, false));
+  run(tpmlp::launch_amax_bf16(static_cast<const uint16_t*>(A), d * H, am + 1, s, false));
+  run(tpmlp::launch_amax_bf16(static_cast<const uint16_t*>(B), H * d, am + 2, s, false));
+  run(tpmlp::launch_amax_bf16(dy, M * d, am + 3, s, false));
   // quantised operands, in the orientation each GEMM reads them
   run(tpmlp::launch_quant_fp8(E4, x, M * d, am + 0, Xq, sc + 0, s));
   run(tpmlp::launch_quant_fp8_tile(E4, true, x, d, m, dd, am + 0, XqT, M, sc + 0, s));
@@ -598,7 +600,7 @@ int tp_mlp_shard_backward_fp8(const void* X, const void* A, const void* B, const
   // dS = bf16(((dYq·Bq_iᵀ)/(sdY·sB)) ⊙ GeLU'(S)), Z = bf16(GeLU(S)), their amaxes
   run(tpmlp::launch_gemm_fp8(Fp8GemmArgs{dYq, d, sc + 3, BqT, F, sc + 2, dS, F, am + 4, nullptr,
                                          S, F, Z, am + 5, m, f, dd},
-                             OutKind::GeluGradBf16, E5, E4, s));
+                             OutKind::GeluGradBf16, E5, E4, s, false));
   run(tpmlp::launch_quant_fp8(E5, dS, M * F, am + 4, dSq, sc + 4, s));
   run(tpmlp::launch_quant_fp8_tile(E4, true, Z, F, m, f, am + 5, ZqT, M, sc + 5, s));
   // dX_i = (dSq·Aq_iᵀ)/(sdS·sA)

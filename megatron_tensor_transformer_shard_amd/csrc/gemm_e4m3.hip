@@ -44,7 +44,9 @@ constexpr float kE5m2Max = 57344.0f;
 template <int FMT>
 constexpr float fp8_max() { return FMT == 0 ? kE4m3Max : kE5m2Max; }
 
-__global__ void fill_f32_kernel(float* p, float v) { *p = v; }
+__global__ void fill_f32_kernel(float* p, int n, float v) {
+  if ((int)threadIdx.x < n) p[threadIdx.x] = v;
+}
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -701,13 +703,14 @@ int64_t grid_for(int64_t nvec) {
 
 }  // namespace
 
-hipError_t launch_fill_f32(float* p, float v, hipStream_t stream) {
-  hipLaunchKernelGGL(fill_f32_kernel, dim3(1), dim3(1), 0, stream, p, v);
+hipError_t launch_fill_f32(float* p, float v, hipStream_t stream, int n) {
+  hipLaunchKernelGGL(fill_f32_kernel, dim3(1), dim3(64), 0, stream, p, n, v);
   return hipGetLastError();
 }
 
-hipError_t launch_amax_bf16(const uint16_t* T, int64_t numel, float* amax, hipStream_t stream) {
-  hipError_t e = launch_fill_f32(amax, 0.0f, stream);
+hipError_t launch_amax_bf16(const uint16_t* T, int64_t numel, float* amax, hipStream_t stream,
+                            bool zero) {
+  hipError_t e = zero ? launch_fill_f32(amax, 0.0f, stream) : hipSuccess;
   if (e != hipSuccess || numel == 0) return e;
   // four vectors per thread per step; up to 4 workgroups per CU (one atomic each)
   int64_t blocks = (numel / 8 + 4 * kThreads - 1) / (4 * kThreads);
@@ -761,8 +764,8 @@ namespace {
 // a 256x256 tile (smaller tiles reuse each LDS byte less, so their cost falls
 // slower than their area).
 hipError_t launch_group(const Fp8GemmArgs* a, int n, OutKind out, int fp, int fq,
-                        hipStream_t stream) {
-  for (int i = 0; i < n; ++i)
+                        hipStream_t stream, bool zero_amax) {
+  for (int i = 0; i < n && zero_amax; ++i)
     for (float* am : {a[i].z_amax, a[i].z_amax2})
       if (am != nullptr) {
         hipError_t e = launch_fill_f32(am, 0.0f, stream);
@@ -786,16 +789,16 @@ hipError_t launch_group(const Fp8GemmArgs* a, int n, OutKind out, int fp, int fq
 }  // namespace
 
 hipError_t launch_gemm_fp8(const Fp8GemmArgs& a, OutKind out, int fp, int fq,
-                           hipStream_t stream) {
+                           hipStream_t stream, bool zero_amax) {
   if (a.M == 0 || a.N == 0) {
     for (float* am : {a.z_amax, a.z_amax2})
-      if (am != nullptr) {
+      if (am != nullptr && zero_amax) {
         hipError_t e = launch_fill_f32(am, 0.0f, stream);
         if (e != hipSuccess) return e;
       }
     return hipSuccess;
   }
-  return launch_group(&a, 1, out, fp, fq, stream);
+  return launch_group(&a, 1, out, fp, fq, stream, zero_amax);
 }
 
 hipError_t launch_gemm_fp8_pair(const Fp8GemmArgs& x, const Fp8GemmArgs& y, OutKind out, int fp,
@@ -805,7 +808,7 @@ hipError_t launch_gemm_fp8_pair(const Fp8GemmArgs& x, const Fp8GemmArgs& y, OutK
   for (const Fp8GemmArgs* g : {&x, &y})
     if (g->M > 0 && g->N > 0) a[n++] = *g;
   if (n == 0) return hipSuccess;
-  return launch_group(a, n, out, fp, fq, stream);
+  return launch_group(a, n, out, fp, fq, stream, true);
 }
 
 hipError_t launch_gemm_e4m3(const uint8_t* P, int64_t ldp, const float* sP, const uint8_t* Q,
@@ -814,7 +817,7 @@ hipError_t launch_gemm_e4m3(const uint8_t* P, int64_t ldp, const float* sP, cons
                             hipStream_t stream) {
   const Fp8GemmArgs a{P, ldp, sP, Q, ldq, sQ, C, ldc, z_amax, sC, nullptr, 0, nullptr, nullptr,
                       M, N, K};
-  return launch_gemm_fp8(a, out, 0, 0, stream);
+  return launch_gemm_fp8(a, out, 0, 0, stream, true);
 }
 
 }  // namespace tpmlp

@@ -55,8 +55,11 @@ hipError_t launch_partial_sum(const void* const* parts, int nparts, bool parts_b
                               int64_t d, hipStream_t stream);
 
 // fp8 (OCP e4m3) path.
-hipError_t launch_fill_f32(float* p, float v, hipStream_t stream);
-hipError_t launch_amax_bf16(const uint16_t* T, int64_t numel, float* amax, hipStream_t stream);
+// p[0 .. n) = v (n <= 64), one small kernel (no memset: safe under graph capture).
+hipError_t launch_fill_f32(float* p, float v, hipStream_t stream, int n = 1);
+// *amax = max |T| (zeroed first unless zero is false: then it is max'ed into).
+hipError_t launch_amax_bf16(const uint16_t* T, int64_t numel, float* amax, hipStream_t stream,
+                            bool zero = true);
 hipError_t launch_quant_e4m3(const uint16_t* T, int64_t numel, const float* amax, uint8_t* Tq,
                              float* scale, hipStream_t stream);
 // C = epilogue((P·Q) / (sP·sQ)); GeluBf16 also folds max|Z| into z_amax when
@@ -77,7 +80,7 @@ struct Fp8GemmArgs {
   int M, N, K;
 };
 hipError_t launch_gemm_fp8(const Fp8GemmArgs& a, OutKind out, int fp, int fq,
-                           hipStream_t stream);
+                           hipStream_t stream, bool zero_amax = true);
 // Two independent fp8 GEMMs of one format pair and epilogue in one launch.
 hipError_t launch_gemm_fp8_pair(const Fp8GemmArgs& x, const Fp8GemmArgs& y, OutKind out, int fp,
                                 int fq, hipStream_t stream);
