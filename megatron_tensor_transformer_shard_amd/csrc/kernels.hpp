@@ -9,10 +9,11 @@
 
 namespace tpmlp {
 
-// GeluE4m3 (e4m3 GEMM only): Z = bf16(GeLU(.)) quantised to e4m3 with a
-// given scale, one byte per element.
-// GeluGradBf16 (bf16 GEMM, backward): C = bf16(acc·GeLU'(S)), C2 = bf16(GeLU(S))
-// with S read from an fp32 [M, N] matrix.
+// Epilogues: GeluBf16 = bf16(GeLU(acc)); F32 = acc; Bf16 = bf16(acc);
+// GeluE4m3 (fp8 GEMM only): bf16(GeLU(acc)) quantised to e4m3 with a given
+// scale, one byte per element; GeluGradBf16 (backward, both engines):
+// C = bf16(acc·GeLU'(S)), C2 = bf16(GeLU(S)) with S read from an fp32 [M, N]
+// matrix. In the fp8 engine acc is first divided by sP·sQ.
 enum class OutKind : int { GeluBf16 = 0, F32 = 1, Bf16 = 2, GeluE4m3 = 3, GeluGradBf16 = 4 };
 
 // Operand layouts of the bf16 GEMM C = P·Q: NN = P [M, K] K-contiguous and
@@ -54,7 +55,7 @@ hipError_t launch_partial_sum(const void* const* parts, int nparts, bool parts_b
                               bool y_bf16, int64_t numel, const void* bias, int bias_kind,
                               int64_t d, hipStream_t stream);
 
-// fp8 (OCP e4m3) path.
+// fp8 paths (OCP e4m3 forward, e4m3 / e5m2 backward).
 // p[0 .. n) = v (n <= 64), one small kernel (no memset: safe under graph capture).
 hipError_t launch_fill_f32(float* p, float v, hipStream_t stream, int n = 1);
 // *amax = max |T| (zeroed first unless zero is false: then it is max'ed into).
