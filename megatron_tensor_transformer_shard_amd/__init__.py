@@ -84,8 +84,8 @@ EXPORTED_SYMBOLS = tuple(_SIGNATURES)
 def _load_library():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is not built; run `python -m megatron_tensor_transformer_shard_amd.build_lib` "
-            "(there is no CPU fallback)")
+            f"{LIB_PATH} is not built; run `python megatron_tensor_transformer_shard_amd/build_lib.py` "
+            "from the repository root (there is no CPU fallback)")
     lib = ctypes.CDLL(LIB_PATH)
     for name, (res, args) in _SIGNATURES.items():
         fn = getattr(lib, name)

@@ -326,3 +326,18 @@ def test_python_wrapper_rejects_cpu_tensors():
     X = torch.zeros(4, 8, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         tpm.tp_mlp_col_gelu(X, torch.zeros(8, 8, dtype=torch.bfloat16))
+
+
+def test_import_fails_loudly_without_the_library(tmp_path):
+    """The package has no CPU fallback: with libtpmlp.so absent, importing it
+    raises instead of silently computing elsewhere."""
+    import shutil
+    import subprocess
+    import sys
+    pkg = os.path.join(ROOT, "megatron_tensor_transformer_shard_amd")
+    dst = tmp_path / "megatron_tensor_transformer_shard_amd"
+    shutil.copytree(pkg, dst, ignore=shutil.ignore_patterns("*.so", "_build", "__pycache__"))
+    r = subprocess.run([sys.executable, "-c", "import megatron_tensor_transformer_shard_amd"],
+                       cwd=tmp_path, capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0
+    assert "libtpmlp.so" in (r.stderr + r.stdout)

@@ -109,6 +109,21 @@ def test_backward_fp8_vs_oracle(tpm, M, d, H, N):
             assert r <= TOL_FP8, f"{what}: {name} err ratio {r:.3e}"
 
 
+def test_backward_fp8_zero_gradient(tpm):
+    """dY = 0: its scale is 1 (amax 0), dS = 0 (scale 1), and every gradient is exactly 0."""
+    import torch
+    M, d, H, N = 48, 64, 256, 2
+    X, A, B = make_random(M, d, H, seed=41, sigma=0.05)
+    Xd, Ad, Bd = dev_bf16(X), dev_bf16(A), dev_bf16(B)
+    dY0 = torch.zeros((M, d), dtype=torch.bfloat16, device="cuda")
+    dX, dA, dB, ws = tpm.tp_mlp_shard_backward_fp8(Xd, Ad, Bd, dY0, N, 0)
+    _sync()
+    sc = tpm.fp8_backward_workspace_views(ws, M, d, H // N)["scale"].cpu().numpy()
+    assert sc[3] == 1.0 and sc[4] == 1.0
+    for name, t in (("dX", dX), ("dA", dA), ("dB", dB)):
+        assert torch.count_nonzero(t).item() == 0, f"{name} nonzero for dY = 0"
+
+
 def test_backward_fp8_close_to_bf16_backward(tpm):
     """The fp8 gradients against the bf16 backward of the same inputs: the
     difference is the quantisation, a few percent of the largest gradient."""
