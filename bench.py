@@ -188,10 +188,24 @@ def build_bwd_step(tpm, wl):
     dB = torch.empty((F, d), dtype=torch.float32, device="cuda")
     dX = torch.empty((M, d), dtype=torch.float32, device="cuda")
 
+    # fp8: the weights' whole-tensor amaxes, once per step for every rank (as
+    # a real rank would all-reduce the amax of its own shard), inside the step
+    wam = torch.empty(2, dtype=torch.float32, device="cuda")
+    extra = {"w_amax": wam} if wl.fp8 else {}
+
+    def weight_amax():
+        tpm.tp_amax_bf16(Ad, amax=wam[0:1])
+        tpm.tp_amax_bf16(Bd, amax=wam[1:2])
+
     def step(timer=None):
+        if wl.fp8:
+            if timer is None:
+                weight_amax()
+            else:
+                timer.around("weight_amax", weight_amax)
         for r in range(N):
             def call(r=r):
-                fn(Xd, Ad, Bd, dYd, N, r, dX_i=dXs[r], dA_i=dA, dB_i=dB, workspace=ws)
+                fn(Xd, Ad, Bd, dYd, N, r, dX_i=dXs[r], dA_i=dA, dB_i=dB, workspace=ws, **extra)
             if timer is None:
                 call()
             else:
@@ -205,7 +219,7 @@ def build_bwd_step(tpm, wl):
     kern_flops = {"shard_backward": 10 * M * d * F}
     # algorithmic bytes of one call: X, dY, A_i, B_i read once; dX_i, dA_i,
     # dB_i written once (the S, dS, Z intermediates and, for fp8, the
-    # quantised copies and the whole-tensor amaxes of A and B are not counted)
+    # quantised copies are not counted)
     kern_bytes = {"shard_backward": (2 * M * d + 2 * d * F) * 2 + (M * d + 2 * d * F) * 4}
     psum_bytes = (N + 1) * 4 * M * d
     return step, kern_flops, kern_bytes, psum_bytes, (X, A, B, dY), (dX if N > 1 else dXs[0])
@@ -524,6 +538,10 @@ def main():
         kstats[name]["frac_of_peak"] = kstats[name]["tflops"] / peak
         kstats[name]["algorithmic_bytes"] = kern_bytes[name]
         kstats[name]["traffic"] = measured_traffic(wl.name, name)
+    if "weight_amax" in kstats:   # reads the whole of A and B once per step
+        wbytes = 2 * 2 * wl.d * wl.H
+        kstats["weight_amax"]["GBps"] = wbytes / (kstats["weight_amax"]["avg_us"] * 1e-6) / 1e9
+        kstats["weight_amax"]["algorithmic_bytes"] = wbytes
     if "partial_sum" in kstats:
         kstats["partial_sum"]["GBps"] = psum_bytes / (kstats["partial_sum"]["avg_us"] * 1e-6) / 1e9
         kstats["partial_sum"]["algorithmic_bytes"] = psum_bytes
@@ -537,6 +555,15 @@ def main():
                 "avg_launch_us": round(kstats[dom]["avg_us"], 2)}
 
     check = sampled_check(wl, inputs, out)
+    if hasattr(wl, "heads"):
+        check_ref = "unsharded attention block, float64 oracle, sampled rows of a causal prefix"
+    elif wl.fp8 and wl.backward:
+        check_ref = ("unsharded bf16 input gradient, float64 oracle: the fp8 quantisation error "
+                     "itself (parity with the fp8 oracle is a GPU test)")
+    elif wl.backward:
+        check_ref = "unsharded input gradient, float64 oracle"
+    else:
+        check_ref = "unsharded GeLU(X·A)·B, float64 oracle"
     props = torch.cuda.get_device_properties(0)
     device = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
               "cus": props.multi_processor_count}
@@ -566,6 +593,7 @@ def main():
         "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in kstats.items()},
         "check_max_err_ratio_8rows": check,
+        "check_against": None if check is None else check_ref,
         "device": device,
     }
     if not args.no_cpu_baseline:

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define TPM_ABI_VERSION 1
+#define TPM_ABI_VERSION 2
 
 /* Element types. */
 typedef enum {
@@ -336,14 +336,20 @@ size_t tp_mlp_shard_backward_fp8_workspace_size(int64_t M, int64_t d, int64_t H,
  * all accumulated in fp32; the transposed operands are quantised straight
  * into their transposed layout. Arguments, layouts and outputs as for
  * tp_mlp_shard_backward; M, d and F = H/N must be multiples of 16.
+ * w_amax : NULL, or device fp32 [2] = {max|A|, max|B|} over the whole weights
+ *   (e.g. from tp_amax_bf16): the weights' amaxes do not change between the
+ *   forward and the backward of a step, so a caller that already has them (or
+ *   runs every rank's backward against the same weights) passes them instead
+ *   of having every call read all of A and B again. NULL: computed here.
  * workspace : device, at least tp_mlp_shard_backward_fp8_workspace_size(M, d, H, N)
  *   bytes, 16-byte aligned; the first 64 bytes hold the amaxes of X, A, B, dY,
- *   dS, Z (floats 0-5) and their scales (floats 8-13).
+ *   dS, Z (floats 0-5; those of A and B only when computed here) and the
+ *   scales of the six (floats 8-13).
  */
 int tp_mlp_shard_backward_fp8(const void* X, const void* A, const void* B, const void* dY,
                               float* dX_i, float* dA_i, float* dB_i, int64_t M, int64_t d,
-                              int64_t H, int N, int rank, void* workspace, size_t workspace_bytes,
-                              void* stream);
+                              int64_t H, int N, int rank, const float* w_amax, void* workspace,
+                              size_t workspace_bytes, void* stream);
 
 /*
  * ---------------------------------------------------------------------------

@@ -20,7 +20,7 @@ import os
 import torch  # loads the HIP runtime that libtpmlp.so then binds to
 
 __all__ = [
-    "LIB_PATH", "TpmError", "abi_version", "status_string",
+    "LIB_PATH", "ABI_VERSION", "TpmError", "abi_version", "status_string",
     "tp_mlp_col_gelu", "tp_mlp_row_partial", "tp_mlp_shard", "tp_mlp_shard_workspace_size",
     "tp_partial_sum", "tp_partial_sum_rows", "tp_reduce_scatter_share", "tp_amax_bf16", "tp_quant_e4m3", "tp_mlp_col_gelu_e4m3",
     "tp_mlp_row_partial_e4m3", "tp_mlp_shard_e4m3", "tp_mlp_shard_e4m3_workspace_size",
@@ -76,9 +76,13 @@ _SIGNATURES = {
                              _vp, _sz, _vp]),
     "tp_mlp_shard_backward_fp8_workspace_size": (_sz, [_i64, _i64, _i64, _int]),
     "tp_mlp_shard_backward_fp8": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64,
-                                         _int, _int, _vp, _sz, _vp]),
+                                         _int, _int, _vp, _vp, _sz, _vp]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGNATURES)
+
+
+# The entry-point signatures below are those of this ABI version of include/tpmlp.h.
+ABI_VERSION = 2
 
 
 def _load_library():
@@ -91,6 +95,10 @@ def _load_library():
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
+    if lib.tp_abi_version() != ABI_VERSION:
+        raise ImportError(
+            f"{LIB_PATH} has ABI version {lib.tp_abi_version()}, these bindings expect "
+            f"{ABI_VERSION}: rebuild it with `python megatron_tensor_transformer_shard_amd/build_lib.py`")
     return lib
 
 
@@ -596,9 +604,11 @@ def tp_mlp_shard_backward_fp8_workspace_size(M: int, d: int, H: int, N: int) -> 
 
 
 def tp_mlp_shard_backward_fp8(X, A, B, dY, N: int, rank: int, dX_i=None, dA_i=None, dB_i=None,
-                              workspace=None, stream=None):
+                              workspace=None, stream=None, w_amax=None):
     """Gradients of rank `rank`'s shard with hybrid fp8 GEMMs (E4M3 activations and
-    weights, E5M2 gradients). Returns (dX_i, dA_i, dB_i, workspace)."""
+    weights, E5M2 gradients). w_amax: None, or a device float32 tensor of two
+    values, max|A| and max|B| over the whole weights (then they are not
+    recomputed). Returns (dX_i, dA_i, dB_i, workspace)."""
     for t, name in ((X, "X"), (A, "A"), (B, "B"), (dY, "dY")):
         _need(t, name, torch.bfloat16, 2)
     M, d = X.shape
@@ -620,9 +630,14 @@ def tp_mlp_shard_backward_fp8(X, A, B, dY, N: int, rank: int, dX_i=None, dA_i=No
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     _need(workspace, "workspace", None)
+    if w_amax is not None:
+        _need(w_amax, "w_amax", torch.float32)
+        if w_amax.numel() != 2:
+            raise ValueError("w_amax holds two values: max|A| and max|B|")
     _check(lib.tp_mlp_shard_backward_fp8(X.data_ptr(), A.data_ptr(), B.data_ptr(), dY.data_ptr(),
                                          dX_i.data_ptr(), dA_i.data_ptr(), dB_i.data_ptr(), M, d,
-                                         H, N, rank, workspace.data_ptr(),
+                                         H, N, rank, 0 if w_amax is None else w_amax.data_ptr(),
+                                         workspace.data_ptr(),
                                          workspace.numel() * workspace.element_size(),
                                          _stream(stream)),
            "tp_mlp_shard_backward_fp8")

@@ -527,8 +527,8 @@ size_t tp_mlp_shard_backward_fp8_workspace_size(int64_t M, int64_t d, int64_t H,
 
 int tp_mlp_shard_backward_fp8(const void* X, const void* A, const void* B, const void* dY,
                               float* dX_i, float* dA_i, float* dB_i, int64_t M, int64_t d,
-                              int64_t H, int N, int rank, void* workspace, size_t workspace_bytes,
-                              void* stream) {
+                              int64_t H, int N, int rank, const float* w_amax, void* workspace,
+                              size_t workspace_bytes, void* stream) {
   if (N < 1 || rank < 0 || rank >= N) return TPM_ERR_ARG;
   if (H <= 0 || H % N != 0) return TPM_ERR_SHAPE;
   const int64_t F = H / N;
@@ -546,16 +546,17 @@ int tp_mlp_shard_backward_fp8(const void* X, const void* A, const void* B, const
   const Fp8BwdLayout L = fp8_bwd_layout(M, d, F);
   if (!workspace || workspace_bytes < L.total) return TPM_ERR_WORKSPACE;
   if (!aligned16(X) || !aligned16(A) || !aligned16(B) || !aligned16(dY) || !aligned16(dX_i) ||
-      !aligned16(dA_i) || !aligned16(dB_i) || !aligned16(workspace))
+      !aligned16(dA_i) || !aligned16(dB_i) || !aligned16(workspace) ||
+      (reinterpret_cast<uintptr_t>(w_amax) & 3u))
     return TPM_ERR_ALIGN;
-  const Span ins[4] = {mat_span(X, M, d, d, 2), mat_span(A, d, H, H, 2), mat_span(B, H, d, d, 2),
-                       mat_span(dY, M, d, d, 2)};
+  const Span ins[5] = {mat_span(X, M, d, d, 2), mat_span(A, d, H, H, 2), mat_span(B, H, d, d, 2),
+                       mat_span(dY, M, d, d, 2), mat_span(w_amax, w_amax ? 1 : 0, 2, 2, 4)};
   const Span outs[4] = {mat_span(dX_i, M, d, d, 4), mat_span(dA_i, d, F, F, 4),
                         mat_span(dB_i, F, d, d, 4),
                         {reinterpret_cast<uintptr_t>(workspace),
                          reinterpret_cast<uintptr_t>(workspace) + L.total}};
   for (int o = 0; o < 4; ++o) {
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 5; ++i)
       if (overlap(outs[o], ins[i])) return TPM_ERR_ALIAS;
     for (int p = o + 1; p < 4; ++p)
       if (overlap(outs[o], outs[p])) return TPM_ERR_ALIAS;
@@ -579,19 +580,23 @@ int tp_mlp_shard_backward_fp8(const void* X, const void* A, const void* B, const
   constexpr int E4 = 0, E5 = 1;
   hipError_t e = hipSuccess;
   auto run = [&](hipError_t r) { if (e == hipSuccess) e = r; };
-  // per-tensor amax scales: X, the whole of A and B (as in the fp8 forward), dY;
-  // the six amax slots (these four, then dS and Z) are cleared by one kernel
+  // per-tensor amax scales: X, the whole of A and B (as in the fp8 forward;
+  // given by the caller when w_amax is not NULL), dY; the six amax slots
+  // (these four, then dS and Z) are cleared by one kernel
+  const float* amA = w_amax ? w_amax : am + 1;
+  const float* amB = w_amax ? w_amax + 1 : am + 2;
   run(tpmlp::launch_fill_f32(am, 0.0f, s, 6));
-  run(tpmlp::launch_amax_bf16(x, M * d, am + 0, s, false));
-  run(tpmlp::launch_amax_bf16(static_cast<const uint16_t*>(A), d * H, am + 1, s, false));
-  run(tpmlp::launch_amax_bf16(static_cast<const uint16_t*>(B), H * d, am + 2, s, false));
-  run(tpmlp::launch_amax_bf16(dy, M * d, am + 3, s, false));
-  // quantised operands, in the orientation each GEMM reads them
-  run(tpmlp::launch_quant_fp8(E4, x, M * d, am + 0, Xq, sc + 0, s));
-  run(tpmlp::launch_quant_fp8_tile(E4, true, x, d, m, dd, am + 0, XqT, M, sc + 0, s));
-  run(tpmlp::launch_quant_fp8_tile(E4, false, A_i, H, dd, f, am + 1, Aq, F, sc + 1, s));
-  run(tpmlp::launch_quant_fp8_tile(E4, true, A_i, H, dd, f, am + 1, AqT, d, sc + 1, s));
-  run(tpmlp::launch_quant_fp8_tile(E4, true, B_i, d, f, dd, am + 2, BqT, F, sc + 2, s));
+  {
+    const uint16_t* ts[4] = {x, dy, static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B)};
+    const int64_t ns[4] = {M * d, M * d, d * H, H * d};
+    float* const outs4[4] = {am + 0, am + 3, am + 1, am + 2};
+    run(tpmlp::launch_amax_bf16_multi(ts, ns, outs4, w_amax ? 2 : 4, s));
+  }
+  // quantised operands, in the orientation each GEMM reads them (X and A_i
+  // in both, each from one read)
+  run(tpmlp::launch_quant_fp8_tile(E4, x, d, m, dd, am + 0, Xq, d, XqT, M, sc + 0, s));
+  run(tpmlp::launch_quant_fp8_tile(E4, A_i, H, dd, f, amA, Aq, F, AqT, d, sc + 1, s));
+  run(tpmlp::launch_quant_fp8_tile(E4, B_i, d, f, dd, amB, nullptr, 0, BqT, F, sc + 2, s));
   run(tpmlp::launch_quant_fp8(E5, dy, M * d, am + 3, dYq, sc + 3, s));
   // S = (Xq·Aq_i)/(sX·sA)
   run(tpmlp::launch_gemm_fp8(Fp8GemmArgs{Xq, d, sc + 0, Aq, F, sc + 1, S, F, nullptr, nullptr,
@@ -602,7 +607,7 @@ int tp_mlp_shard_backward_fp8(const void* X, const void* A, const void* B, const
                                          S, F, Z, am + 5, m, f, dd},
                              OutKind::GeluGradBf16, E5, E4, s, false));
   run(tpmlp::launch_quant_fp8(E5, dS, M * F, am + 4, dSq, sc + 4, s));
-  run(tpmlp::launch_quant_fp8_tile(E4, true, Z, F, m, f, am + 5, ZqT, M, sc + 5, s));
+  run(tpmlp::launch_quant_fp8_tile(E4, Z, F, m, f, am + 5, nullptr, 0, ZqT, M, sc + 5, s));
   // dX_i = (dSq·Aq_iᵀ)/(sdS·sA)
   run(tpmlp::launch_gemm_fp8(Fp8GemmArgs{dSq, F, sc + 4, AqT, d, sc + 1, dX_i, d, nullptr,
                                          nullptr, nullptr, 0, nullptr, nullptr, m, dd, f},

@@ -383,31 +383,37 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs g0, GemmAr
   // Epilogue. Lane holds, for 16x16 tile (ni, mi), C[m][n .. n+3] with
   // m = mi·16 + (lane & 15), n = ni·16 + 4·(lane >> 4) (wave-tile relative).
   if constexpr (OUT == (int)OutKind::GeluGradBf16) {
-    // dS = bf16(dZ·GeLU'(S)) into C, Z = bf16(GeLU(S)) into C2. The S loads
-    // of EB tiles are issued together (from clamped addresses, so they need
-    // no branch) and their latency is paid once per batch.
-    constexpr int EB = 8;
+    // dS = bf16(dZ·GeLU'(S)) into C, Z = bf16(GeLU(S)) into C2. The S values
+    // of EB tiles are loaded together (from clamped addresses, so they need
+    // no branch), one batch ahead: batch b+1 is in flight while batch b is
+    // computed, so its latency hides under the GeLU work of one wave per SIMD.
+    constexpr int EB = 8, NB = NT * MT / EB;
     static_assert((NT * MT) % EB == 0, "epilogue batches");
-#pragma unroll
-    for (int b0 = 0; b0 < NT * MT; b0 += EB) {
-      f32x4 sv[EB];
+    f32x4 sv[2][EB];
+    auto load_batch = [&](int b, int buf) __attribute__((always_inline)) {
 #pragma unroll
       for (int e = 0; e < EB; ++e) {
-        const int ni = (b0 + e) / MT, mi = (b0 + e) % MT;
+        const int ni = (b * EB + e) / MT, mi = (b * EB + e) % MT;
         const int m = min(m0 + wm * TM + mi * 16 + (lane & 15), M - 1);
         const int n = min(n0 + wn * TN + ni * 16 + 4 * (lane >> 4), N - 4);
-        sv[e] = *reinterpret_cast<const f32x4*>(aux + (int64_t)m * ldaux + n);
+        sv[buf][e] = *reinterpret_cast<const f32x4*>(aux + (int64_t)m * ldaux + n);
       }
+    };
+    load_batch(0, 0);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      if (b + 1 < NB) load_batch(b + 1, (b + 1) & 1);
 #pragma unroll
       for (int e = 0; e < EB; ++e) {
-        const int ni = (b0 + e) / MT, mi = (b0 + e) % MT;
+        const int ni = (b * EB + e) / MT, mi = (b * EB + e) % MT;
         const int m = m0 + wm * TM + mi * 16 + (lane & 15);
         const int n = n0 + wn * TN + ni * 16 + 4 * (lane >> 4);
         f32x4 v = acc[ni][mi];
         asm volatile("" : "+v"(v));
+        const f32x4 x = sv[b & 1][e];
         float gl[4], dg[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) gelu_and_grad(sv[e][q], gl[q], dg[q]);
+        for (int q = 0; q < 4; ++q) gelu_and_grad(x[q], gl[q], dg[q]);
         if (m < M && n < N) {
           const u32x2 o = {pack_bf16x2(v[0] * dg[0], v[1] * dg[1]),
                            pack_bf16x2(v[2] * dg[2], v[3] * dg[3])};

@@ -67,36 +67,54 @@ __device__ __forceinline__ uint32_t absmax_bits8(const u32x4& w) {
   return m;
 }
 
-// Grid-stride over 16-byte vectors, four loads in flight per thread; the
-// workgroup's four waves combine through LDS and issue one atomic, since
-// atomics on the single result address serialise.
-__global__ __launch_bounds__(kThreads) void amax_bf16_kernel(const uint16_t* __restrict__ T,
-                                                             int64_t numel, float* amax) {
-  __shared__ uint32_t part[kThreads / 64];
-  uint32_t mb = 0;
-  const int64_t nvec = numel / 8;
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  const u32x4* src = reinterpret_cast<const u32x4*>(T);
-  int64_t v = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  for (; v + 3 * stride < nvec; v += 4 * stride) {
-    const u32x4 w0 = __builtin_nontemporal_load(src + v);
-    const u32x4 w1 = __builtin_nontemporal_load(src + v + stride);
-    const u32x4 w2 = __builtin_nontemporal_load(src + v + 2 * stride);
-    const u32x4 w3 = __builtin_nontemporal_load(src + v + 3 * stride);
-    mb = max(mb, max(max(absmax_bits8(w0), absmax_bits8(w1)), max(absmax_bits8(w2), absmax_bits8(w3))));
-  }
-  for (; v < nvec; v += stride) mb = max(mb, absmax_bits8(__builtin_nontemporal_load(src + v)));
-  if (blockIdx.x == 0)
-    for (int64_t e = nvec * 8 + threadIdx.x; e < numel; e += kThreads) mb = max(mb, T[e] & 0x7FFFu);
+// max |T_i| of up to four bf16 tensors in one launch, max'ed into *amax[i].
+// A workgroup reads contiguous chunks of kAmaxUnroll x 1024 vectors (128 KB;
+// each thread's eight 16-byte loads in flight together), chunk-strided over
+// the grid, one tensor after the other; per tensor, the workgroup's waves
+// combine through LDS and issue one atomic, since atomics on one address
+// serialise.
+constexpr int kAmaxThreads = 1024, kAmaxUnroll = 8, kAmaxMaxTensors = 4;
+struct AmaxSet {
+  const uint16_t* t[kAmaxMaxTensors];
+  int64_t numel[kAmaxMaxTensors];
+  float* out[kAmaxMaxTensors];
+  int n;
+};
+
+__global__ __launch_bounds__(kAmaxThreads) void amax_bf16_kernel(AmaxSet set) {
+  __shared__ uint32_t part[kAmaxThreads / 64];
+  constexpr int64_t kChunk = (int64_t)kAmaxUnroll * kAmaxThreads;
+  for (int i = 0; i < set.n; ++i) {
+    const uint16_t* T = set.t[i];
+    const int64_t numel = set.numel[i], nvec = numel / 8, nchunk = nvec / kChunk;
+    const u32x4* src = reinterpret_cast<const u32x4*>(T);
+    uint32_t mb = 0;
+    for (int64_t c = blockIdx.x; c < nchunk; c += gridDim.x) {
+      const u32x4* p = src + c * kChunk + threadIdx.x;
+      u32x4 w[kAmaxUnroll];
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) mb = max(mb, (uint32_t)__shfl_xor((int)mb, off, 64));
-  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = mb;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t b = part[0];
+      for (int j = 0; j < kAmaxUnroll; ++j) w[j] = p[j * kAmaxThreads];
 #pragma unroll
-    for (int w = 1; w < kThreads / 64; ++w) b = max(b, part[w]);
-    atomic_max_nonneg(amax, bf16_bits_to_f32(b));
+      for (int j = 0; j < kAmaxUnroll; ++j) mb = max(mb, absmax_bits8(w[j]));
+    }
+    // the vectors after the last whole chunk, then the elements after the last vector
+    for (int64_t v = nchunk * kChunk + (int64_t)blockIdx.x * kAmaxThreads + threadIdx.x; v < nvec;
+         v += (int64_t)gridDim.x * kAmaxThreads)
+      mb = max(mb, absmax_bits8(src[v]));
+    if (blockIdx.x == 0)
+      for (int64_t e = nvec * 8 + threadIdx.x; e < numel; e += kAmaxThreads)
+        mb = max(mb, T[e] & 0x7FFFu);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mb = max(mb, (uint32_t)__shfl_xor((int)mb, off, 64));
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = mb;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      uint32_t b = part[0];
+#pragma unroll
+      for (int w = 1; w < kAmaxThreads / 64; ++w) b = max(b, part[w]);
+      atomic_max_nonneg(set.out[i], bf16_bits_to_f32(b));
+    }
+    __syncthreads();  // part is rewritten for the next tensor
   }
 }
 
@@ -149,46 +167,63 @@ __global__ __launch_bounds__(64) void amax_history_push_kernel(float* __restrict
   }
 }
 
-// 16 elements per thread per step: 2 x 16-byte bf16 loads, one 16-byte store.
+// 16 bf16 values (two 16-byte vectors) -> 16 codes of format FMT.
+template <int FMT>
+__device__ __forceinline__ u32x4 quant16(const u32x4& w0, const u32x4& w1, float s) {
+  u32x4 o;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const u32x4& w = (j < 2) ? w0 : w1;
+    const uint32_t x0 = w[(j & 1) * 2], x1 = w[(j & 1) * 2 + 1];
+    o[j] = cvt_fp8x2<FMT>(bf16_bits_to_f32(x0 & 0xFFFFu) * s, bf16_bits_to_f32(x0 >> 16) * s) |
+           (cvt_fp8x2<FMT>(bf16_bits_to_f32(x1 & 0xFFFFu) * s, bf16_bits_to_f32(x1 >> 16) * s)
+            << 16);
+  }
+  return o;
+}
+
+// 16 elements per thread per step (two 16-byte loads, one 16-byte store),
+// the loads of four grid-stride steps issued together.
 template <int FMT>
 __global__ __launch_bounds__(kThreads) void quant_fp8_kernel(const uint16_t* __restrict__ T,
                                                              int64_t numel,
                                                              const float* __restrict__ amax,
                                                              uint8_t* __restrict__ Tq,
                                                              float* __restrict__ scale) {
+  constexpr int U = 4;
   const float s = quant_scale_of<FMT>(amax[0]);
   if (blockIdx.x == 0 && threadIdx.x == 0) scale[0] = s;
   const int64_t nvec = numel / 16;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
-  for (int64_t v = (int64_t)blockIdx.x * kThreads + threadIdx.x; v < nvec; v += stride) {
-    const u32x4 w0 = reinterpret_cast<const u32x4*>(T)[2 * v];
-    const u32x4 w1 = reinterpret_cast<const u32x4*>(T)[2 * v + 1];
-    u32x4 o;
+  const u32x4* src = reinterpret_cast<const u32x4*>(T);
+  u32x4* dst = reinterpret_cast<u32x4*>(Tq);
+  int64_t v = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  for (; v + (U - 1) * stride < nvec; v += U * stride) {
+    u32x4 w[2 * U];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const u32x4& w = (j < 2) ? w0 : w1;
-      const uint32_t x0 = w[(j & 1) * 2], x1 = w[(j & 1) * 2 + 1];
-      const float f0 = bf16_bits_to_f32(x0 & 0xFFFFu) * s;
-      const float f1 = bf16_bits_to_f32(x0 >> 16) * s;
-      const float f2 = bf16_bits_to_f32(x1 & 0xFFFFu) * s;
-      const float f3 = bf16_bits_to_f32(x1 >> 16) * s;
-      o[j] = cvt_fp8x2<FMT>(f0, f1) | (cvt_fp8x2<FMT>(f2, f3) << 16);
+    for (int j = 0; j < U; ++j) {
+      w[2 * j] = src[2 * (v + j * stride)];
+      w[2 * j + 1] = src[2 * (v + j * stride) + 1];
     }
-    reinterpret_cast<u32x4*>(Tq)[v] = o;
+#pragma unroll
+    for (int j = 0; j < U; ++j) dst[v + j * stride] = quant16<FMT>(w[2 * j], w[2 * j + 1], s);
   }
+  for (; v < nvec; v += stride) dst[v] = quant16<FMT>(src[2 * v], src[2 * v + 1], s);
 }
 
-// Quantise the block T [R, C] (row stride ldt) with the scale of `amax`
-// into Tq [R, C] or, with TRANS, Tq [C, R] (row stride ldq). One workgroup
-// per 64 x 64 tile: thread t loads 16 consecutive elements of row t / 4 and
-// converts them; with TRANS the codes go through LDS ([column][row], rows of
-// 80 bytes) and thread t stores 16 consecutive codes of output row t / 4.
-// R and C are multiples of 16, so a 16-element chunk is either wholly inside
-// or wholly outside the block.
-template <int FMT, bool TRANS>
+// Quantise the block T [R, C] (row stride ldt) with the scale of `amax` into
+// Tq [R, C] (row stride ldq; MODE bit 0) and/or TqT [C, R] (row stride ldqt;
+// MODE bit 1), so a tensor needed in both orientations is read once. One
+// workgroup per 64 x 64 tile: thread t loads 16 consecutive elements of row
+// t / 4 and converts them; the transposed codes go through LDS ([column][row],
+// rows of 80 bytes) and thread t stores 16 consecutive codes of output row
+// t / 4. R and C are multiples of 16, so a 16-element chunk is either wholly
+// inside or wholly outside the block.
+template <int FMT, int MODE>
 __global__ __launch_bounds__(kThreads) void quant_fp8_tile_kernel(
     const uint16_t* __restrict__ T, int64_t ldt, int R, int C, const float* __restrict__ amax,
-    uint8_t* __restrict__ Tq, int64_t ldq, float* __restrict__ scale) {
+    uint8_t* __restrict__ Tq, int64_t ldq, uint8_t* __restrict__ TqT, int64_t ldqt,
+    float* __restrict__ scale) {
   constexpr int kTile = 64, kStride = 80;
   __shared__ __attribute__((aligned(16))) uint8_t tile[kTile * kStride];
   const float s = quant_scale_of<FMT>(amax[0]);
@@ -199,26 +234,17 @@ __global__ __launch_bounds__(kThreads) void quant_fp8_tile_kernel(
   u32x4 o = {0u, 0u, 0u, 0u};
   if (row < R && col < C) {
     const u32x4* src = reinterpret_cast<const u32x4*>(T + (int64_t)row * ldt + col);
-    const u32x4 w0 = src[0], w1 = src[1];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const u32x4& w = (j < 2) ? w0 : w1;
-      const uint32_t x0 = w[(j & 1) * 2], x1 = w[(j & 1) * 2 + 1];
-      o[j] = cvt_fp8x2<FMT>(bf16_bits_to_f32(x0 & 0xFFFFu) * s, bf16_bits_to_f32(x0 >> 16) * s) |
-             (cvt_fp8x2<FMT>(bf16_bits_to_f32(x1 & 0xFFFFu) * s, bf16_bits_to_f32(x1 >> 16) * s)
-              << 16);
-    }
+    o = quant16<FMT>(src[0], src[1], s);
+    if constexpr ((MODE & 1) != 0) *reinterpret_cast<u32x4*>(Tq + (int64_t)row * ldq + col) = o;
   }
-  if constexpr (!TRANS) {
-    if (row < R && col < C) *reinterpret_cast<u32x4*>(Tq + (int64_t)row * ldq + col) = o;
-  } else {
+  if constexpr ((MODE & 2) != 0) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) tile[(cc + j) * kStride + r] = (uint8_t)(o[j >> 2] >> (8 * (j & 3)));
     __syncthreads();
     const int orow = blockIdx.x * kTile + r;   // a column of T
     const int ocol = blockIdx.y * kTile + cc;  // rows of T
     if (orow < C && ocol < R)
-      *reinterpret_cast<u32x4*>(Tq + (int64_t)orow * ldq + ocol) =
+      *reinterpret_cast<u32x4*>(TqT + (int64_t)orow * ldqt + ocol) =
           *reinterpret_cast<const u32x4*>(tile + r * kStride + cc);
   }
 }
@@ -562,45 +588,52 @@ __global__ __launch_bounds__(kThreads) void gemm_e4m3_kernel(Fp8GemmArgs g0, Fp8
     return;
   }
   if constexpr (OUT == (int)OutKind::GeluGradBf16) {
-    // The S loads of EB tiles are issued together (from clamped addresses, so
-    // they need no branch) and their latency is paid once per batch.
-    constexpr int EB = 8;
+    // The S values of EB tiles are loaded together (from clamped addresses,
+    // so they need no branch), one batch ahead: batch b+1 is in flight while
+    // batch b is computed.
+    constexpr int EB = 8, NB = NT * MT / EB;
     static_assert((NT * MT) % EB == 0, "epilogue batches");
     float dsmax = 0.0f, gmax = 0.0f;
-#pragma unroll
-    for (int b0 = 0; b0 < NT * MT; b0 += EB) {
-      f32x4 svb[EB];
+    f32x4 svb[2][EB];
+    auto load_batch = [&](int b, int buf) __attribute__((always_inline)) {
 #pragma unroll
       for (int e = 0; e < EB; ++e) {
-        const int ni = (b0 + e) / MT, mi = (b0 + e) % MT;
+        const int ni = (b * EB + e) / MT, mi = (b * EB + e) % MT;
         const int m = min(m0 + wm * TM + mi * 16 + (lane & 15), M - 1);
         const int n = min(n0 + wn * TN + ni * 16 + 4 * (lane >> 4), N - 4);
-        svb[e] = *reinterpret_cast<const f32x4*>(aux + (int64_t)m * ldaux + n);
+        svb[buf][e] = *reinterpret_cast<const f32x4*>(aux + (int64_t)m * ldaux + n);
       }
+    };
+    load_batch(0, 0);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      if (b + 1 < NB) load_batch(b + 1, (b + 1) & 1);
 #pragma unroll
       for (int e = 0; e < EB; ++e) {
-        const int ni = (b0 + e) / MT, mi = (b0 + e) % MT;
+        const int ni = (b * EB + e) / MT, mi = (b * EB + e) % MT;
         const int m = m0 + wm * TM + mi * 16 + (lane & 15);
         const int n = n0 + wn * TN + ni * 16 + 4 * (lane >> 4);
         f32x4 v = acc[ni][mi];
         asm volatile("" : "+v"(v));
         v *= dq;
         if (m < M && n < N) {
-          const f32x4 sv = svb[e];
-          uint32_t db[4], zb[4];
+          const f32x4 sv = svb[b & 1][e];
+          float gl[4], dg[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float g, dg;
-            gelu_and_grad(sv[e], g, dg);
-            db[e] = f32_to_bf16_rne(v[e] * dg);
-            zb[e] = f32_to_bf16_rne(g);
-            dsmax = fmaxf(dsmax, fabsf(bf16_bits_to_f32(db[e])));
-            gmax = fmaxf(gmax, fabsf(bf16_bits_to_f32(zb[e])));
-          }
-          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(C) + (int64_t)m * ldc + n) =
-              u32x2{db[0] | (db[1] << 16), db[2] | (db[3] << 16)};
-          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(C2) + (int64_t)m * ldc + n) =
-              u32x2{zb[0] | (zb[1] << 16), zb[2] | (zb[3] << 16)};
+          for (int q = 0; q < 4; ++q) gelu_and_grad(sv[q], gl[q], dg[q]);
+          const u32x2 o = {pack_bf16x2(v[0] * dg[0], v[1] * dg[1]),
+                           pack_bf16x2(v[2] * dg[2], v[3] * dg[3])};
+          const u32x2 z = {pack_bf16x2(gl[0], gl[1]), pack_bf16x2(gl[2], gl[3])};
+          // |x| of a bf16 pair: clear both sign bits; the larger half is the
+          // pair's max (non-negative floats order like their bit patterns)
+          const uint32_t od = max(max(o[0] & 0x7FFFu, (o[0] >> 16) & 0x7FFFu),
+                                  max(o[1] & 0x7FFFu, (o[1] >> 16) & 0x7FFFu));
+          const uint32_t oz = max(max(z[0] & 0x7FFFu, (z[0] >> 16) & 0x7FFFu),
+                                  max(z[1] & 0x7FFFu, (z[1] >> 16) & 0x7FFFu));
+          dsmax = fmaxf(dsmax, bf16_bits_to_f32(od));
+          gmax = fmaxf(gmax, bf16_bits_to_f32(oz));
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(C) + (int64_t)m * ldc + n) = o;
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(C2) + (int64_t)m * ldc + n) = z;
         }
       }
     }
@@ -708,16 +741,33 @@ hipError_t launch_fill_f32(float* p, float v, hipStream_t stream, int n) {
   return hipGetLastError();
 }
 
+hipError_t launch_amax_bf16_multi(const uint16_t* const* T, const int64_t* numel,
+                                  float* const* amax, int n, hipStream_t stream) {
+  if (n < 1 || n > kAmaxMaxTensors) return hipErrorInvalidValue;
+  AmaxSet set{};
+  int64_t most = 0;
+  set.n = 0;
+  for (int i = 0; i < n; ++i) {
+    if (numel[i] == 0) continue;
+    set.t[set.n] = T[i];
+    set.numel[set.n] = numel[i];
+    set.out[set.n] = amax[i];
+    ++set.n;
+    most = numel[i] > most ? numel[i] : most;
+  }
+  if (set.n == 0) return hipSuccess;
+  // one 1024-thread workgroup per CU, or one per chunk of the largest tensor
+  int64_t blocks = (most / 8 + kAmaxUnroll * kAmaxThreads - 1) / (kAmaxUnroll * kAmaxThreads);
+  blocks = blocks < 1 ? 1 : (blocks > 256 ? 256 : blocks);
+  hipLaunchKernelGGL(amax_bf16_kernel, dim3((unsigned)blocks), dim3(kAmaxThreads), 0, stream, set);
+  return hipGetLastError();
+}
+
 hipError_t launch_amax_bf16(const uint16_t* T, int64_t numel, float* amax, hipStream_t stream,
                             bool zero) {
   hipError_t e = zero ? launch_fill_f32(amax, 0.0f, stream) : hipSuccess;
   if (e != hipSuccess || numel == 0) return e;
-  // four vectors per thread per step; up to 4 workgroups per CU (one atomic each)
-  int64_t blocks = (numel / 8 + 4 * kThreads - 1) / (4 * kThreads);
-  blocks = blocks < 1 ? 1 : (blocks > 256 * 4 ? 256 * 4 : blocks);
-  hipLaunchKernelGGL(amax_bf16_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, T,
-                     numel, amax);
-  return hipGetLastError();
+  return launch_amax_bf16_multi(&T, &numel, &amax, 1, stream);
 }
 
 hipError_t launch_quant_fp8(int fmt, const uint16_t* T, int64_t numel, const float* amax,
@@ -735,19 +785,33 @@ hipError_t launch_quant_e4m3(const uint16_t* T, int64_t numel, const float* amax
   return launch_quant_fp8(0, T, numel, amax, Tq, scale, stream);
 }
 
-hipError_t launch_quant_fp8_tile(int fmt, bool trans, const uint16_t* T, int64_t ldt, int R, int C,
-                                 const float* amax, uint8_t* Tq, int64_t ldq, float* scale,
-                                 hipStream_t stream) {
+namespace {
+template <int FMT, int MODE>
+void launch_tile_mode(dim3 grid, const uint16_t* T, int64_t ldt, int R, int C, const float* amax,
+                      uint8_t* Tq, int64_t ldq, uint8_t* TqT, int64_t ldqt, float* scale,
+                      hipStream_t stream) {
+  hipLaunchKernelGGL((quant_fp8_tile_kernel<FMT, MODE>), grid, dim3(kThreads), 0, stream, T, ldt,
+                     R, C, amax, Tq, ldq, TqT, ldqt, scale);
+}
+template <int FMT>
+void launch_tile_fmt(int mode, dim3 grid, const uint16_t* T, int64_t ldt, int R, int C,
+                     const float* amax, uint8_t* Tq, int64_t ldq, uint8_t* TqT, int64_t ldqt,
+                     float* scale, hipStream_t stream) {
+  if (mode == 1) launch_tile_mode<FMT, 1>(grid, T, ldt, R, C, amax, Tq, ldq, TqT, ldqt, scale, stream);
+  else if (mode == 2) launch_tile_mode<FMT, 2>(grid, T, ldt, R, C, amax, Tq, ldq, TqT, ldqt, scale, stream);
+  else launch_tile_mode<FMT, 3>(grid, T, ldt, R, C, amax, Tq, ldq, TqT, ldqt, scale, stream);
+}
+}  // namespace
+
+hipError_t launch_quant_fp8_tile(int fmt, const uint16_t* T, int64_t ldt, int R, int C,
+                                 const float* amax, uint8_t* Tq, int64_t ldq, uint8_t* TqT,
+                                 int64_t ldqt, float* scale, hipStream_t stream) {
+  const int mode = (Tq != nullptr ? 1 : 0) | (TqT != nullptr ? 2 : 0);
+  if (mode == 0) return hipErrorInvalidValue;
   if (R == 0 || C == 0) return hipSuccess;
   const dim3 grid((unsigned)((C + 63) / 64), (unsigned)((R + 63) / 64));
-  if (fmt == 0 && trans)
-    hipLaunchKernelGGL((quant_fp8_tile_kernel<0, true>), grid, dim3(kThreads), 0, stream, T, ldt, R, C, amax, Tq, ldq, scale);
-  else if (fmt == 0)
-    hipLaunchKernelGGL((quant_fp8_tile_kernel<0, false>), grid, dim3(kThreads), 0, stream, T, ldt, R, C, amax, Tq, ldq, scale);
-  else if (trans)
-    hipLaunchKernelGGL((quant_fp8_tile_kernel<1, true>), grid, dim3(kThreads), 0, stream, T, ldt, R, C, amax, Tq, ldq, scale);
-  else
-    hipLaunchKernelGGL((quant_fp8_tile_kernel<1, false>), grid, dim3(kThreads), 0, stream, T, ldt, R, C, amax, Tq, ldq, scale);
+  if (fmt == 0) launch_tile_fmt<0>(mode, grid, T, ldt, R, C, amax, Tq, ldq, TqT, ldqt, scale, stream);
+  else launch_tile_fmt<1>(mode, grid, T, ldt, R, C, amax, Tq, ldq, TqT, ldqt, scale, stream);
   return hipGetLastError();
 }
 

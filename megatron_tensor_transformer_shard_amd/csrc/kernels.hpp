@@ -61,6 +61,10 @@ hipError_t launch_fill_f32(float* p, float v, hipStream_t stream, int n = 1);
 // *amax = max |T| (zeroed first unless zero is false: then it is max'ed into).
 hipError_t launch_amax_bf16(const uint16_t* T, int64_t numel, float* amax, hipStream_t stream,
                             bool zero = true);
+// *amax[i] = max(*amax[i], max |T[i]|) for up to four tensors in one launch
+// (the slots are not cleared).
+hipError_t launch_amax_bf16_multi(const uint16_t* const* T, const int64_t* numel,
+                                  float* const* amax, int n, hipStream_t stream);
 hipError_t launch_quant_e4m3(const uint16_t* T, int64_t numel, const float* amax, uint8_t* Tq,
                              float* scale, hipStream_t stream);
 // C = epilogue((P·Q) / (sP·sQ)); GeluBf16 also folds max|Z| into z_amax when
@@ -91,11 +95,12 @@ hipError_t launch_gemm_fp8_pair(const Fp8GemmArgs& x, const Fp8GemmArgs& y, OutK
 // handled in vector steps (the caller guarantees it).
 hipError_t launch_quant_fp8(int fmt, const uint16_t* T, int64_t numel, const float* amax,
                             uint8_t* Tq, float* scale, hipStream_t stream);
-// The same for the block T [R, C] (row stride ldt), written to Tq [R, C] or,
-// with trans, Tq [C, R] (row stride ldq). R and C multiples of 16.
-hipError_t launch_quant_fp8_tile(int fmt, bool trans, const uint16_t* T, int64_t ldt, int R, int C,
-                                 const float* amax, uint8_t* Tq, int64_t ldq, float* scale,
-                                 hipStream_t stream);
+// The same for the block T [R, C] (row stride ldt), written to Tq [R, C]
+// (row stride ldq) and/or its transpose TqT [C, R] (row stride ldqt) from one
+// read of T; either output may be NULL, not both. R and C multiples of 16.
+hipError_t launch_quant_fp8_tile(int fmt, const uint16_t* T, int64_t ldt, int R, int C,
+                                 const float* amax, uint8_t* Tq, int64_t ldq, uint8_t* TqT,
+                                 int64_t ldqt, float* scale, hipStream_t stream);
 
 hipError_t launch_gemm_e4m3(const uint8_t* P, int64_t ldp, const float* sP, const uint8_t* Q,
                             int64_t ldq, const float* sQ, void* C, int64_t ldc, float* z_amax,

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert tpm.abi_version() == 1
+    assert tpm.abi_version() == tpm.ABI_VERSION == 2
     for code in (OK, ENULL, EARG, ESHAPE, EDTYPE, EALIGN, EWS, EALIAS, EHIP):
         s = tpm.status_string(code)
         assert s.startswith("TPM_")
@@ -269,11 +269,11 @@ def test_backward_fp8_validation():
     def bw(**kw):
         a = dict(X=BASE, A=BASE + GB, B=BASE + 2 * GB, dY=BASE + 3 * GB, dX=BASE + 4 * GB,
                  dA=BASE + 5 * GB, dB=BASE + 6 * GB, M=M, d=d, H=H, N=N, rank=0,
-                 ws=BASE + 7 * GB, wsb=ws)
+                 wam=None, ws=BASE + 7 * GB, wsb=ws)
         a.update(kw)
         return L.tp_mlp_shard_backward_fp8(a["X"], a["A"], a["B"], a["dY"], a["dX"], a["dA"],
                                            a["dB"], a["M"], a["d"], a["H"], a["N"], a["rank"],
-                                           a["ws"], a["wsb"], None)
+                                           a["wam"], a["ws"], a["wsb"], None)
     assert bw(M=0) == OK
     assert bw(rank=2) == EARG
     assert bw(M=24) == ESHAPE             # fp8 rows of the transposed copies: multiple of 16
@@ -283,6 +283,9 @@ def test_backward_fp8_validation():
     assert bw(wsb=ws - 1) == EWS
     assert bw(dB=BASE + 2 * GB + 32) == EALIAS
     assert bw(ws=BASE + 4 * GB) == EALIAS
+    assert bw(wam=BASE + 8 * GB + 2) == EALIGN      # the weight amaxes are floats
+    assert bw(wam=BASE + 7 * GB + 32) == EALIAS     # inside the workspace the call writes
+    assert bw(wam=BASE + 4 * GB) == EALIAS          # dX_i
 
 
 def test_attention_validation():

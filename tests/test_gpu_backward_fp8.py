@@ -124,6 +124,33 @@ def test_backward_fp8_zero_gradient(tpm):
         assert torch.count_nonzero(t).item() == 0, f"{name} nonzero for dY = 0"
 
 
+@pytest.mark.parametrize("M,d,H,N", [(272, 144, 576, 2), (528, 272, 1088, 4)])
+def test_backward_fp8_given_weight_amaxes(tpm, M, d, H, N):
+    """max|A| and max|B| passed in (from tp_amax_bf16) give the same bits as
+    computing them inside the call, for every rank."""
+    import torch
+    log(f"case fp8 backward, given weight amaxes, M={M} d={d} H={H} N={N}")
+    X, A, B = make_random(M, d, H, seed=5 * M + N, sigma=0.05)
+    dY = make_output_grad(M, d, seed=M + 3, sigma=1.0)
+    Xd, Ad, Bd, dYd = dev_bf16(X), dev_bf16(A), dev_bf16(B), dev_bf16(dY)
+    wam = torch.full((2,), float("nan"), dtype=torch.float32, device="cuda")
+    tpm.tp_amax_bf16(Ad, amax=wam[0:1])
+    tpm.tp_amax_bf16(Bd, amax=wam[1:2])
+    _sync()
+    assert float(wam[0]) == float(np.max(np.abs(oracle.bf16_decode(A))))
+    assert float(wam[1]) == float(np.max(np.abs(oracle.bf16_decode(B))))
+    for rank in range(N):
+        ref = tpm.tp_mlp_shard_backward_fp8(Xd, Ad, Bd, dYd, N, rank)
+        got = tpm.tp_mlp_shard_backward_fp8(Xd, Ad, Bd, dYd, N, rank, w_amax=wam)
+        _sync()
+        F = H // N
+        sr = tpm.fp8_backward_workspace_views(ref[3], M, d, F)["scale"].cpu().numpy()
+        sg = tpm.fp8_backward_workspace_views(got[3], M, d, F)["scale"].cpu().numpy()
+        assert np.array_equal(sr[:6], sg[:6]), f"rank {rank}: scales"
+        for name, a, b in zip(("dX", "dA", "dB"), ref[:3], got[:3]):
+            assert torch.equal(a, b), f"rank {rank}: {name} differs with given weight amaxes"
+
+
 def test_backward_fp8_close_to_bf16_backward(tpm):
     """The fp8 gradients against the bf16 backward of the same inputs: the
     difference is the quantisation, a few percent of the largest gradient."""
