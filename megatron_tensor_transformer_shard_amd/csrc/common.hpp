@@ -18,6 +18,7 @@ typedef __attribute__((ext_vector_type(4))) int i32x4;
 
 typedef __attribute__((ext_vector_type(2))) float f32x2;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(2))) unsigned short u16x2;
 
 // Two floats -> two bfloat16 (low half = lo), round to nearest even; a single
 // v_cvt_pk_bf16_f32 on gfx950.
@@ -32,6 +33,12 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
   return __builtin_bit_cast(float, b << 16);
+}
+
+// max(x, 0) for finite x as one v_med3_f32 (fmaxf would first quiet a
+// signalling NaN in x with a second instruction).
+__device__ __forceinline__ float relu(float x) {
+  return __builtin_amdgcn_fmed3f(x, 0.0f, __builtin_huge_valf());
 }
 
 // GeLU(x) = x·Φ(x), the exact (Gaussian CDF) form.
@@ -56,7 +63,7 @@ __device__ __forceinline__ float gelu_exact(float x) {
   p = fmaf(t, p, 0.5f * 0.254829592f);
   const float e = __builtin_amdgcn_exp2f((x * -0.72134752044448170f) * x);  // e^(−x²/2)
   const float h = (t * p) * e;                                              // Φ(−|x|)
-  return fmaf(-ax, h, fmaxf(x, 0.0f));
+  return fmaf(-ax, h, relu(x));
 }
 
 // GeLU(x) and GeLU'(x) = Φ(x) + x·φ(x) together, φ(x) = e^(−x²/2)/√(2π), with
@@ -72,7 +79,7 @@ __device__ __forceinline__ void gelu_and_grad(float x, float& g, float& dg) {
   p = fmaf(t, p, 0.5f * 0.254829592f);
   const float e = __builtin_amdgcn_exp2f((x * -0.72134752044448170f) * x);  // e^(−x²/2)
   const float h = (t * p) * e;                                              // Φ(−|x|)
-  g = fmaf(-ax, h, fmaxf(x, 0.0f));
+  g = fmaf(-ax, h, relu(x));
   const float phi = x >= 0.0f ? 1.0f - h : h;
   dg = fmaf(x, e * 0.39894228040143268f, phi);
 }

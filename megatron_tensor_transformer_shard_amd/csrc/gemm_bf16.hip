@@ -382,44 +382,57 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs g0, GemmAr
 
   // Epilogue. Lane holds, for 16x16 tile (ni, mi), C[m][n .. n+3] with
   // m = mi·16 + (lane & 15), n = ni·16 + 4·(lane >> 4) (wave-tile relative).
+  // Element offsets are a per-lane base (tile (0, 0)) plus the wave-uniform
+  // 16·mi rows and 16·ni columns (row strides are below 2^23, so the latter
+  // fits 32 bits); a tile is stored where its row and column are inside.
+  const int mrow = m0 + wm * TM + (lane & 15), ncol = n0 + wn * TN + 4 * (lane >> 4);
+  const int rows_left = M - mrow, cols_left = N - ncol;
+  const int64_t c_lane = (int64_t)mrow * ldc + ncol;
+  auto c_off = [&](int mi, int ni) __attribute__((always_inline)) {
+    return c_lane + (int)(16 * mi * ldc + 16 * ni);
+  };
+  auto inside = [&](int mi, int ni) __attribute__((always_inline)) {
+    return 16 * mi < rows_left && 16 * ni < cols_left;
+  };
   if constexpr (OUT == (int)OutKind::GeluGradBf16) {
     // dS = bf16(dZ·GeLU'(S)) into C, Z = bf16(GeLU(S)) into C2. The S values
-    // of EB tiles are loaded together (from clamped addresses, so they need
-    // no branch), one batch ahead: batch b+1 is in flight while batch b is
-    // computed, so its latency hides under the GeLU work of one wave per SIMD.
-    constexpr int EB = 8, NB = NT * MT / EB;
+    // of EB tiles are loaded together, LA batches ahead of the batch being
+    // computed, so their latency hides under the GeLU work of one wave per
+    // SIMD. Loads are clamped to the last row and column group (no branch).
+    constexpr int EB = 8, NB = NT * MT / EB, LA = 2;
     static_assert((NT * MT) % EB == 0, "epilogue batches");
-    f32x4 sv[2][EB];
+    const int row_max = M - 1 - mrow, col_max = N - 4 - ncol;
+    const float* aux_lane = aux + (int64_t)mrow * ldaux + ncol;
+    f32x4 sv[LA + 1][EB];
     auto load_batch = [&](int b, int buf) __attribute__((always_inline)) {
 #pragma unroll
       for (int e = 0; e < EB; ++e) {
         const int ni = (b * EB + e) / MT, mi = (b * EB + e) % MT;
-        const int m = min(m0 + wm * TM + mi * 16 + (lane & 15), M - 1);
-        const int n = min(n0 + wn * TN + ni * 16 + 4 * (lane >> 4), N - 4);
-        sv[buf][e] = *reinterpret_cast<const f32x4*>(aux + (int64_t)m * ldaux + n);
+        const int r = min(16 * mi, row_max), c = min(16 * ni, col_max);
+        sv[buf][e] = *reinterpret_cast<const f32x4*>(aux_lane + ((int64_t)r * (int)ldaux + c));
       }
     };
-    load_batch(0, 0);
+#pragma unroll
+    for (int b = 0; b < LA && b < NB; ++b) load_batch(b, b);
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      if (b + 1 < NB) load_batch(b + 1, (b + 1) & 1);
+      if (b + LA < NB) load_batch(b + LA, (b + LA) % (LA + 1));
 #pragma unroll
       for (int e = 0; e < EB; ++e) {
         const int ni = (b * EB + e) / MT, mi = (b * EB + e) % MT;
-        const int m = m0 + wm * TM + mi * 16 + (lane & 15);
-        const int n = n0 + wn * TN + ni * 16 + 4 * (lane >> 4);
         f32x4 v = acc[ni][mi];
         asm volatile("" : "+v"(v));
-        const f32x4 x = sv[b & 1][e];
+        const f32x4 x = sv[b % (LA + 1)][e];
         float gl[4], dg[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) gelu_and_grad(x[q], gl[q], dg[q]);
-        if (m < M && n < N) {
-          const u32x2 o = {pack_bf16x2(v[0] * dg[0], v[1] * dg[1]),
-                           pack_bf16x2(v[2] * dg[2], v[3] * dg[3])};
-          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(C) + (int64_t)m * ldc + n) = o;
+        if (inside(mi, ni)) {
+          const int64_t o = c_off(mi, ni);
+          const u32x2 d2 = {pack_bf16x2(v[0] * dg[0], v[1] * dg[1]),
+                            pack_bf16x2(v[2] * dg[2], v[3] * dg[3])};
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(C) + o) = d2;
           const u32x2 z = {pack_bf16x2(gl[0], gl[1]), pack_bf16x2(gl[2], gl[3])};
-          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(C2) + (int64_t)m * ldc + n) = z;
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(C2) + o) = z;
         }
       }
     }
@@ -429,23 +442,22 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs g0, GemmAr
   for (int ni = 0; ni < NT; ++ni) {
 #pragma unroll
     for (int mi = 0; mi < MT; ++mi) {
-      const int m = m0 + wm * TM + mi * 16 + (lane & 15);
-      const int n = n0 + wn * TN + ni * 16 + 4 * (lane >> 4);
-      if (m >= M || n >= N) continue;
+      if (!inside(mi, ni)) continue;
+      const int64_t o = c_off(mi, ni);
       f32x4 v = acc[ni][mi];
       // Read the accumulator into VGPRs here, as the GeLU epilogue does; a
       // store straight from AGPRs lets the register allocator split the
       // accumulators between the two files and copy them inside the loop.
       asm volatile("" : "+v"(v));
       if constexpr (OUT == (int)OutKind::F32) {
-        *reinterpret_cast<f32x4*>(static_cast<float*>(C) + (int64_t)m * ldc + n) = v;
+        *reinterpret_cast<f32x4*>(static_cast<float*>(C) + o) = v;
       } else if constexpr (OUT == (int)OutKind::GeluBf16) {
-        const u32x2 o = {pack_bf16x2(gelu_exact(v[0]), gelu_exact(v[1])),
+        const u32x2 g = {pack_bf16x2(gelu_exact(v[0]), gelu_exact(v[1])),
                          pack_bf16x2(gelu_exact(v[2]), gelu_exact(v[3]))};
-        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(C) + (int64_t)m * ldc + n) = o;
+        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(C) + o) = g;
       } else {
-        const u32x2 o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(C) + (int64_t)m * ldc + n) = o;
+        const u32x2 g = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(C) + o) = g;
       }
     }
   }

@@ -570,108 +570,118 @@ __global__ __launch_bounds__(kThreads) void gemm_e4m3_kernel(Fp8GemmArgs g0, Fp8
   // given scale), bf16, fp32, or (backward) dS = bf16(acc·GeLU'(S)) and
   // Z = bf16(GeLU(S)) with max|dS| and max|Z|. Lane holds, for 16x16 tile
   // (ni, mi), C[m][n .. n+3] with m = mi·16 + (lane & 15),
-  // n = ni·16 + 4·(lane >> 4) (wave-tile relative).
+  // n = ni·16 + 4·(lane >> 4) (wave-tile relative). Element offsets are a
+  // per-lane base (tile (0, 0)) plus the wave-uniform 16·mi rows and 16·ni
+  // columns (row strides are below 2^23, so the latter fits 32 bits); a tile
+  // is stored where its row and column are inside. The maxima of bf16 values
+  // are taken on their bit patterns with the sign cleared, two at a time
+  // (v_pk_max_u16): non-negative floats order like their bit patterns.
   const float dq = 1.0f / (sP[0] * sQ[0]);
+  const int mrow = m0 + wm * TM + (lane & 15), ncol = n0 + wn * TN + 4 * (lane >> 4);
+  const int rows_left = M - mrow, cols_left = N - ncol;
+  const int64_t c_lane = (int64_t)mrow * ldc + ncol;
+  auto c_off = [&](int mi, int ni) __attribute__((always_inline)) {
+    return c_lane + (int)(16 * mi * ldc + 16 * ni);
+  };
+  auto inside = [&](int mi, int ni) __attribute__((always_inline)) {
+    return 16 * mi < rows_left && 16 * ni < cols_left;
+  };
+  auto absmax16x2 = [](u16x2 m, uint32_t w) __attribute__((always_inline)) {
+    return __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w & 0x7FFF7FFFu));
+  };
+  auto max_of = [](u16x2 m) __attribute__((always_inline)) {
+    return bf16_bits_to_f32(max((uint32_t)m[0], (uint32_t)m[1]));
+  };
   if constexpr (OUT == (int)OutKind::F32) {
 #pragma unroll
     for (int ni = 0; ni < NT; ++ni) {
 #pragma unroll
       for (int mi = 0; mi < MT; ++mi) {
-        const int m = m0 + wm * TM + mi * 16 + (lane & 15);
-        const int n = n0 + wn * TN + ni * 16 + 4 * (lane >> 4);
-        if (m >= M || n >= N) continue;
+        if (!inside(mi, ni)) continue;
         f32x4 v = acc[ni][mi];
         asm volatile("" : "+v"(v));
-        *reinterpret_cast<f32x4*>(static_cast<float*>(C) + (int64_t)m * ldc + n) = v * dq;
+        *reinterpret_cast<f32x4*>(static_cast<float*>(C) + c_off(mi, ni)) = v * dq;
       }
     }
     return;
   }
   if constexpr (OUT == (int)OutKind::GeluGradBf16) {
-    // The S values of EB tiles are loaded together (from clamped addresses,
-    // so they need no branch), one batch ahead: batch b+1 is in flight while
-    // batch b is computed.
-    constexpr int EB = 8, NB = NT * MT / EB;
+    // The S values of EB tiles are loaded together, LA batches ahead of the
+    // batch being computed; loads are clamped to the last row and column
+    // group (no branch).
+    constexpr int EB = 8, NB = NT * MT / EB, LA = 2;
     static_assert((NT * MT) % EB == 0, "epilogue batches");
-    float dsmax = 0.0f, gmax = 0.0f;
-    f32x4 svb[2][EB];
+    const int row_max = M - 1 - mrow, col_max = N - 4 - ncol;
+    const float* aux_lane = aux + (int64_t)mrow * ldaux + ncol;
+    u16x2 dsm = {0, 0}, zm = {0, 0};
+    f32x4 svb[LA + 1][EB];
     auto load_batch = [&](int b, int buf) __attribute__((always_inline)) {
 #pragma unroll
       for (int e = 0; e < EB; ++e) {
         const int ni = (b * EB + e) / MT, mi = (b * EB + e) % MT;
-        const int m = min(m0 + wm * TM + mi * 16 + (lane & 15), M - 1);
-        const int n = min(n0 + wn * TN + ni * 16 + 4 * (lane >> 4), N - 4);
-        svb[buf][e] = *reinterpret_cast<const f32x4*>(aux + (int64_t)m * ldaux + n);
+        const int r = min(16 * mi, row_max), c = min(16 * ni, col_max);
+        svb[buf][e] = *reinterpret_cast<const f32x4*>(aux_lane + ((int64_t)r * (int)ldaux + c));
       }
     };
-    load_batch(0, 0);
+#pragma unroll
+    for (int b = 0; b < LA && b < NB; ++b) load_batch(b, b);
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      if (b + 1 < NB) load_batch(b + 1, (b + 1) & 1);
+      if (b + LA < NB) load_batch(b + LA, (b + LA) % (LA + 1));
 #pragma unroll
       for (int e = 0; e < EB; ++e) {
         const int ni = (b * EB + e) / MT, mi = (b * EB + e) % MT;
-        const int m = m0 + wm * TM + mi * 16 + (lane & 15);
-        const int n = n0 + wn * TN + ni * 16 + 4 * (lane >> 4);
         f32x4 v = acc[ni][mi];
         asm volatile("" : "+v"(v));
         v *= dq;
-        if (m < M && n < N) {
-          const f32x4 sv = svb[b & 1][e];
+        if (inside(mi, ni)) {
+          const f32x4 sv = svb[b % (LA + 1)][e];
           float gl[4], dg[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) gelu_and_grad(sv[q], gl[q], dg[q]);
           const u32x2 o = {pack_bf16x2(v[0] * dg[0], v[1] * dg[1]),
                            pack_bf16x2(v[2] * dg[2], v[3] * dg[3])};
           const u32x2 z = {pack_bf16x2(gl[0], gl[1]), pack_bf16x2(gl[2], gl[3])};
-          // |x| of a bf16 pair: clear both sign bits; the larger half is the
-          // pair's max (non-negative floats order like their bit patterns)
-          const uint32_t od = max(max(o[0] & 0x7FFFu, (o[0] >> 16) & 0x7FFFu),
-                                  max(o[1] & 0x7FFFu, (o[1] >> 16) & 0x7FFFu));
-          const uint32_t oz = max(max(z[0] & 0x7FFFu, (z[0] >> 16) & 0x7FFFu),
-                                  max(z[1] & 0x7FFFu, (z[1] >> 16) & 0x7FFFu));
-          dsmax = fmaxf(dsmax, bf16_bits_to_f32(od));
-          gmax = fmaxf(gmax, bf16_bits_to_f32(oz));
-          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(C) + (int64_t)m * ldc + n) = o;
-          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(C2) + (int64_t)m * ldc + n) = z;
+          dsm = absmax16x2(absmax16x2(dsm, o[0]), o[1]);
+          zm = absmax16x2(absmax16x2(zm, z[0]), z[1]);
+          const int64_t off = c_off(mi, ni);
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(C) + off) = o;
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(C2) + off) = z;
         }
       }
     }
-    block_max_to(smem, wave, lane, dsmax, gmax, z_amax, z_amax2);
+    block_max_to(smem, wave, lane, max_of(dsm), max_of(zm), z_amax, z_amax2);
     return;
   }
   const float sc = OUT == (int)OutKind::GeluE4m3 ? sC[0] : 1.0f;
-  float zmax = 0.0f;
+  u16x2 zm = {0, 0};
 #pragma unroll
   for (int ni = 0; ni < NT; ++ni) {
 #pragma unroll
     for (int mi = 0; mi < MT; ++mi) {
-      const int m = m0 + wm * TM + mi * 16 + (lane & 15);
-      const int n = n0 + wn * TN + ni * 16 + 4 * (lane >> 4);
-      if (m >= M || n >= N) continue;
+      if (!inside(mi, ni)) continue;
       f32x4 v = acc[ni][mi];
       asm volatile("" : "+v"(v));
-      uint32_t bits[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float x = v[e] * dq;
-        bits[e] = f32_to_bf16_rne(GELU ? gelu_exact(x) : x);
-        if (GELU) zmax = fmaxf(zmax, fabsf(bf16_bits_to_f32(bits[e])));
-      }
+      v *= dq;
+      const u32x2 o = GELU ? u32x2{pack_bf16x2(gelu_exact(v[0]), gelu_exact(v[1])),
+                                   pack_bf16x2(gelu_exact(v[2]), gelu_exact(v[3]))}
+                           : u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+      if (GELU) zm = absmax16x2(absmax16x2(zm, o[0]), o[1]);
+      const int64_t off = c_off(mi, ni);
       if constexpr (OUT == (int)OutKind::GeluE4m3) {
         // the bf16 Z times the scale in fp32, clamped to ±448, one RNE rounding
         float q[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) q[e] = clamp448(bf16_bits_to_f32(bits[e]) * sc);
-        const uint32_t o = cvt_e4m3x2(q[0], q[1]) | (cvt_e4m3x2(q[2], q[3]) << 16);
-        *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(C) + (int64_t)m * ldc + n) = o;
+        for (int e = 0; e < 4; ++e)
+          q[e] = clamp448(bf16_bits_to_f32((o[e >> 1] >> (16 * (e & 1))) & 0xFFFFu) * sc);
+        const uint32_t qb = cvt_e4m3x2(q[0], q[1]) | (cvt_e4m3x2(q[2], q[3]) << 16);
+        *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(C) + off) = qb;
       } else {
-        const u32x2 o = {bits[0] | (bits[1] << 16), bits[2] | (bits[3] << 16)};
-        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(C) + (int64_t)m * ldc + n) = o;
+        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(C) + off) = o;
       }
     }
   }
-  if (GELU && z_amax != nullptr) block_max_to(smem, wave, lane, zmax, 0.0f, z_amax, nullptr);
+  if (GELU && z_amax != nullptr) block_max_to(smem, wave, lane, max_of(zm), 0.0f, z_amax, nullptr);
 }
 
 }  // namespace e4
