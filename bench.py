@@ -424,35 +424,52 @@ def sampled_check(wl, inputs, out, nrows=8):
 
 
 def library_compare(tpm, args):
-    """The 7B-class column GEMM (X[8192x4096] · A_i[4096x2048], bf16) three ways on the same
-    data: tp_mlp_col_gelu (fused GeLU), and the vendor library through torch.matmul with
-    B N-contiguous (NN, the math layout) and K-contiguous (NT, B stored transposed), neither
-    with an activation. Prints one JSON line of HIP-event averages; a counter profile of this
-    run compares the kernels' instruction mixes."""
+    """The 7B-class column GEMM (X[8192x4096] · A_i[4096x2048], bf16) and row GEMM
+    (Z[8192x2048] · B_i[2048x4096]) against the vendor library on the same data:
+    tp_mlp_col_gelu (fused GeLU) and tp_mlp_row_partial (fp32 and bf16 partials) beside
+    torch's GEMM with the weight N-contiguous (NN, the math layout) and K-contiguous (NT,
+    stored transposed), bf16 output, and for the row GEMM also fp32 output where torch
+    offers it (torch.mm with out_dtype). No library call has an activation. Prints one
+    JSON line of HIP-event averages; a counter profile of this run compares the kernels'
+    instruction mixes."""
     import torch
-    M, K, N = 8192, 4096, 2048
     g = torch.Generator(device="cuda").manual_seed(0)
-    a = torch.randn(M, K, device="cuda", dtype=torch.bfloat16, generator=g)
-    b = (torch.randn(K, N, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
-    bt = b.t().contiguous().t()
-    z = torch.empty(M, N, device="cuda", dtype=torch.bfloat16)
-    calls = {"library_nt": lambda: a @ bt, "library_nn": lambda: a @ b,
-             "col_gelu": lambda: tpm.tp_mlp_col_gelu(a, b, z)}
-    for _ in range(args.warmup):
-        for fn in calls.values():
-            fn()
-    torch.cuda.synchronize()
-    timer = KernelTimer()
-    for _ in range(args.steps):
-        for name, fn in calls.items():
-            timer.around(name, fn)
-    torch.cuda.synchronize()
-    st = timer.summary()
-    fl = 2 * M * N * K
-    print(json.dumps({"workload": "library_compare", "shape": [M, K, N],
-                      "kernels": {k: {"avg_us": round(v["avg_us"], 2),
-                                      "tflops": round(fl / (v["avg_us"] * 1e-6) / 1e12, 1)}
-                                  for k, v in st.items()}}), flush=True)
+    out = {}
+    for label, (M, K, N) in (("col", (8192, 4096, 2048)), ("row", (8192, 2048, 4096))):
+        a = torch.randn(M, K, device="cuda", dtype=torch.bfloat16, generator=g)
+        b = (torch.randn(K, N, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+        bt = b.t().contiguous().t()
+        calls = {f"{label}_library_nt": lambda a=a, bt=bt: a @ bt,
+                 f"{label}_library_nn": lambda a=a, b=b: a @ b}
+        if label == "col":
+            z = torch.empty(M, N, device="cuda", dtype=torch.bfloat16)
+            calls["col_gelu"] = lambda a=a, b=b, z=z: tpm.tp_mlp_col_gelu(a, b, z)
+        else:
+            y32 = torch.empty(M, N, device="cuda", dtype=torch.float32)
+            y16 = torch.empty(M, N, device="cuda", dtype=torch.bfloat16)
+            calls["row_partial_f32"] = lambda a=a, b=b, y=y32: tpm.tp_mlp_row_partial(a, b, y)
+            calls["row_partial_bf16"] = lambda a=a, b=b, y=y16: tpm.tp_mlp_row_partial(
+                a, b, y, out_dtype=torch.bfloat16)
+            try:
+                torch.mm(a, b, out_dtype=torch.float32)
+                calls["row_library_nn_f32"] = lambda a=a, b=b: torch.mm(a, b, out_dtype=torch.float32)
+                calls["row_library_nt_f32"] = lambda a=a, bt=bt: torch.mm(a, bt, out_dtype=torch.float32)
+            except (RuntimeError, NotImplementedError, TypeError) as e:
+                log(f"library_compare: no fp32-output library GEMM ({type(e).__name__})")
+        for _ in range(args.warmup):
+            for fn in calls.values():
+                fn()
+        torch.cuda.synchronize()
+        timer = KernelTimer()
+        for _ in range(args.steps):
+            for name, fn in calls.items():
+                timer.around(name, fn)
+        torch.cuda.synchronize()
+        fl = 2 * M * N * K
+        for k, v in timer.summary().items():
+            out[k] = {"shape": [M, K, N], "avg_us": round(v["avg_us"], 2),
+                      "tflops": round(fl / (v["avg_us"] * 1e-6) / 1e12, 1)}
+    print(json.dumps({"workload": "library_compare", "kernels": out}), flush=True)
 
 
 def copy_calibration(tpm, args):
