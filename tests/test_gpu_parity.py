@@ -10,7 +10,8 @@ import pytest
 import oracle
 from helpers import (bf16_ulp, dev_bf16, dev_f32, dev_u8, host_bf16_bits, host_f64, log,
                      max_err_ratio)
-from workloads import WORKLOADS, make_inputs, make_integer_valued, make_random, sample_rows
+from workloads import (WORKLOADS, bf16_bits_from_f32, make_inputs, make_integer_valued, make_random,
+                       sample_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -437,6 +438,41 @@ def test_amax_and_quant_codes_bit_exact(tpm, shape, sigma):
     assert float(amax.item()) == a_ref
     assert np.float32(s.item()) == s_ref
     assert np.array_equal(Tq.cpu().numpy(), q_ref)
+
+
+# sizes that reach each part of the amax kernel: the scalar tail alone, vectors
+# after the last whole chunk (a chunk is 8 x 1024 vectors of 8 values), several
+# chunks, and more chunks than workgroups (grid-stride over chunks)
+AMAX_SIZES = [1, 7, 8, 9, 1000, 65536, 65536 + 8 * 33 + 5, 3 * 65536 + 17, 300 * 65536 + 8 * 1024 + 3]
+
+
+@pytest.mark.parametrize("numel", AMAX_SIZES)
+def test_amax_bf16_sizes_and_positions(tpm, numel):
+    """max|T| wherever the largest magnitude sits: first element, inside the
+    first chunk, among the vectors after the last whole chunk, in the scalar
+    tail, last element; negative values count by magnitude."""
+    import torch
+    log(f"case amax numel={numel}")
+    rng = np.random.default_rng(numel)
+    base = bf16_bits_from_f32((0.5 * rng.standard_normal(numel)).astype(np.float32))
+    nvec = numel // 8
+    last_chunk_end = (nvec // 8192) * 8192 * 8
+    spots = sorted({0, min(numel - 1, 4099), numel - 1, min(numel - 1, last_chunk_end + 3),
+                    min(numel - 1, nvec * 8)})
+    for pos in spots:
+        bits = base.copy()
+        bits[pos] = bf16_bits_from_f32(np.array([-7.75], dtype=np.float32))[0]
+        a = tpm.tp_amax_bf16(dev_bf16(bits))
+        _sync()
+        ref = float(np.max(np.abs(oracle.bf16_decode(bits))))
+        assert ref == 7.75
+        assert float(a.item()) == ref, f"numel {numel}: max at {pos} not found"
+    # all zeros (and negative zeros) give 0
+    z = np.zeros(numel, dtype=np.uint16)
+    z[::3] = 0x8000
+    a = tpm.tp_amax_bf16(dev_bf16(z))
+    _sync()
+    assert float(a.item()) == 0.0
 
 
 def test_quant_zero_tensor_scale_one(tpm):
