@@ -12,15 +12,17 @@
 // [.. + dh, .. + 2dh), [.. + 2dh, .. + 3dh). O [B·S, ldo] bf16, head j at
 // columns [j·dh, (j+1)·dh). dh = 128.
 //
-// Workgroup = one head of one sequence and a block of 128 queries, as SPLIT
+// Workgroup = one head of one sequence and 128 queries, as SPLIT
 // groups of 128/(16·MT) waves; a wave owns 16·MT queries. The groups split the
 // key blocks (64 keys each) round-robin, each double-buffering its own blocks
 // in LDS by global_load_lds_dwordx4 (K 16 KB + V 16 KB per stage), and merge
 // their partial results through LDS at the end. The shipped configuration is
 // MT = 1, SPLIT = 2 (16 waves, 4 per SIMD): the softmax is VALU work that only
 // other waves' MFMAs and LDS reads can hide, and splitting the keys halves
-// the longest workgroup's chain under the causal mask (query block q needs
-// q+1 pairs of key blocks; the blocks run longest first).
+// the longest workgroup's chain. Under the causal mask a workgroup holds two
+// blocks of 64 queries, an early and a late one (block p and block n-1-p of
+// the n in the sequence), so all workgroups have the same number of query-key
+// block pairs.
 //
 //  - Scores: D = K·Qᵀ with v_mfma_f32_16x16x32_bf16 (A = 16 keys x 32 dh of
 //    K, B = 32 dh x 16 queries of Q, the Q fragments held in registers for
@@ -114,11 +116,8 @@ __global__ __launch_bounds__(64 * SPLIT * kBQ / (16 * MT)) void attn_fwd_kernel(
   // K stages (group h, buffer st) at (2h + st)·16 KB, V stages after all K stages
   __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * SPLIT * kStageBytes];
 
-  const int nqb = (S + kBQ - 1) / kBQ;
   const int bh_count = B * heads;
   const int bid = blockIdx.x;
-  // longest query blocks first (with the causal mask later blocks see more keys)
-  const int qb = CAUSAL ? nqb - 1 - bid / bh_count : bid / bh_count;
   const int bh = bid % bh_count;
   const int b = bh / heads, j = bh % heads;
 
@@ -130,7 +129,28 @@ __global__ __launch_bounds__(64 * SPLIT * kBQ / (16 * MT)) void attn_fwd_kernel(
 
   const uint16_t* seq = QKV + (int64_t)b * S * ld;   // row 0 of the sequence
   const int qcol = 3 * j * kDh, kcol = qcol + kDh, vcol = qcol + 2 * kDh;
-  const int q0w = qb * kBQ + kRows * wave;           // first query of this wave
+  // q0w: first query of this wave (S for a wave with no queries); last_q: the
+  // workgroup's last query. Without the mask a workgroup is kBQ consecutive
+  // queries. With it, query block h (of kBQ/2) needs h+1 key blocks, so
+  // workgroup p pairs block p (first half of each group's waves) with block
+  // nhb-1-p (second half): every workgroup then has about the same work, and
+  // the kernel no longer waits on the one that holds the last queries.
+  int q0w, last_q;
+  if constexpr (CAUSAL) {
+    constexpr int kHalf = kBQ / 2;
+    static_assert(kRows * (kWaves / 2) == kHalf, "half of a group's waves hold one block");
+    const int nhb = (S + kHalf - 1) / kHalf, p = bid / bh_count;
+    const int hb = nhb - 1 - p;                      // the later block; hb == p: none
+    const bool first = wave < kWaves / 2;
+    const int q0 = (first ? p : hb) * kHalf + kRows * (wave % (kWaves / 2));
+    q0w = (first || hb > p) ? q0 : S;
+    last_q = min(S - 1, max(p, hb) * kHalf + kHalf - 1);
+  } else {
+    const int qb = bid / bh_count;
+    q0w = qb * kBQ + kRows * wave;
+    last_q = min(S - 1, qb * kBQ + kBQ - 1);
+  }
+  const bool idle = q0w >= S;
 
   // Q fragments: query q0w + 16mi + L, dh 32s + 8g .. +7 (clamped rows beyond S).
   s16x8 qf[MT][4];
@@ -142,7 +162,7 @@ __global__ __launch_bounds__(64 * SPLIT * kBQ / (16 * MT)) void attn_fwd_kernel(
       qf[mi][s] = *reinterpret_cast<const s16x8*>(seq + (int64_t)q * ld + qcol + 32 * s + 8 * g);
   }
 
-  const int last_key = CAUSAL ? min(S - 1, qb * kBQ + kBQ - 1) : S - 1;
+  const int last_key = CAUSAL ? last_q : S - 1;
   const int nkb = last_key / kBKV + 1;
 
   // DMA of key block kb into the group's buffer st: granule
@@ -194,8 +214,9 @@ __global__ __launch_bounds__(64 * SPLIT * kBQ / (16 * MT)) void attn_fwd_kernel(
     barrier();  // block kb is in LDS; every wave is done with the group's previous block
     if (kb + SPLIT < nkb) issue(kb + SPLIT, st ^ 1);
     const int kv0 = kb * kBKV;
-    // past the last block, or (causal) every query of the wave precedes the block
-    if (kb >= nkb || (CAUSAL && kv0 > q0w + kRows - 1)) continue;
+    // no queries, past the last block, or (causal) every query of the wave
+    // precedes the block
+    if (idle || kb >= nkb || (CAUSAL && kv0 > q0w + kRows - 1)) continue;
 
     const uint8_t* sk = smem + (kst0 + st) * kStageBytes;
     const uint8_t* sv = smem + (vst0 + st) * kStageBytes;
