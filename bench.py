@@ -99,6 +99,8 @@ def parse():
                         "1-part tp_partial_sum over 256 MiB of fp32: the known-size copy that "
                         "calibrates rocprofv3's FETCH_SIZE / WRITE_SIZE)")
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the timed oracle leg")
+    p.add_argument("--no-cold", action="store_true",
+                   help="skip the cold pass (for counter runs, whose per-dispatch averages it would mix)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="stop adding oracle row chunks once this much CPU time is spent")
     p.add_argument("--partial-dtype", choices=["f32", "bf16"], default="f32")
@@ -130,8 +132,47 @@ class KernelTimer:
         for name, pairs in self.marks.items():
             ms = [a.elapsed_time(b) for a, b in pairs]
             out[name] = {"launches": len(ms), "avg_us": 1e3 * float(np.mean(ms)),
+                         "median_us": 1e3 * float(np.median(ms)),
                          "min_us": 1e3 * float(np.min(ms)), "total_ms": float(np.sum(ms))}
         return out
+
+
+class ColdTimer(KernelTimer):
+    """KernelTimer with a 512 MiB write before every timed launch (outside the
+    events), which evicts L2 and the 256 MB Infinity Cache: each launch then
+    starts from HBM."""
+
+    def __init__(self):
+        import torch
+        super().__init__()
+        self.scratch = torch.empty(128 << 20, dtype=torch.float32, device="cuda")
+
+    def around(self, name, fn):
+        self.scratch.fill_(1.0)
+        super().around(name, fn)
+
+
+def device_peak(tpm_peak_key):
+    """The dense MFMA peak recomputed from the device's own figures: CUs and
+    peak engine clock from hipDeviceGetAttribute (the clock torch does not
+    expose on ROCm), times 4096 (bf16) or 8192 (fp8) flops per CU per clock."""
+    import ctypes
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        dev = ctypes.c_int()
+        if hip.hipGetDevice(ctypes.byref(dev)) != 0:
+            return None
+        vals = {}
+        for name, attr in (("clock_khz", 5), ("cus", 63)):   # hipDeviceAttributeClockRate, ...MultiprocessorCount
+            v = ctypes.c_int()
+            if hip.hipDeviceGetAttribute(ctypes.byref(v), attr, dev) != 0:
+                return None
+            vals[name] = v.value
+    except OSError:
+        return None
+    per_clk = 8192 if tpm_peak_key == "e4m3" else 4096
+    vals["peak_tflops"] = vals["cus"] * vals["clock_khz"] * 1e3 * per_clk / 1e12
+    return vals
 
 
 def build_bf16_step(tpm, wl, partial_dtype):
@@ -569,7 +610,24 @@ def main():
                 "unit": "TFLOP/s", "frac": round(ach / peak, 4),
                 "traffic": measured_traffic(wl.name, dom),
                 "flops_per_launch": kern_flops[dom], "algorithmic_bytes": kern_bytes[dom],
-                "avg_launch_us": round(kstats[dom]["avg_us"], 2)}
+                "avg_launch_us": round(kstats[dom]["avg_us"], 2),
+                "median_launch_us": round(kstats[dom]["median_us"], 2)}
+
+    # cold mode: the same launches, each after a 512 MiB write that evicts L2
+    # and the Infinity Cache (a separate, shorter pass; context beside the
+    # warm figures above, which are the primary ones)
+    cold = None if args.no_cold else {}
+    cold_timer = None if args.no_cold else ColdTimer()
+    for _ in range(0 if args.no_cold else min(args.steps, 5)):
+        step(cold_timer)
+    torch.cuda.synchronize()
+    for name, st in ({} if args.no_cold else cold_timer.summary()).items():
+        c = {"launches": st["launches"], "avg_us": round(st["avg_us"], 2),
+             "median_us": round(st["median_us"], 2), "min_us": round(st["min_us"], 2)}
+        if name in kern_flops:
+            c["tflops"] = round(kern_flops[name] / (st["median_us"] * 1e-6) / 1e12, 1)
+        cold[name] = c
+    del cold_timer
 
     check = sampled_check(wl, inputs, out)
     if hasattr(wl, "heads"):
@@ -584,11 +642,10 @@ def main():
     props = torch.cuda.get_device_properties(0)
     device = {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
               "cus": props.multi_processor_count}
-    clk = getattr(props, "clock_rate", None)
-    if clk:
-        device["clock_khz"] = clk
-        device["peak_from_props_tflops"] = props.multi_processor_count * clk * 1e3 * (
-            4096 if dtype == "bf16" else 8192) / 1e12
+    dp = device_peak(dtype)
+    if dp is not None:
+        device["clock_khz"] = dp["clock_khz"]
+        device["peak_from_props_tflops"] = round(dp["peak_tflops"], 1)
 
     result = {
         "metric": (METRIC_ATTN if attn else METRIC_BWD if getattr(wl, "backward", False)
@@ -609,6 +666,7 @@ def main():
         "roofline": roofline,
         "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in kstats.items()},
+        "cold": cold,
         "check_max_err_ratio_8rows": check,
         "check_against": None if check is None else check_ref,
         "device": device,
