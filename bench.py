@@ -152,6 +152,59 @@ class ColdTimer(KernelTimer):
         super().around(name, fn)
 
 
+class ClockSampler:
+    """Samples the engine clock the driver reports as current (the line it
+    marks in pp_dpm_sclk) every few milliseconds from a thread while a pass
+    runs. Only when the box shows exactly one such GPU (else no samples)."""
+
+    def __init__(self, period_s=0.003):
+        import glob
+        paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.path = paths[0] if len(paths) == 1 else None
+        self.period = period_s
+        self.samples = []
+        self._stop = None
+        self._thread = None
+
+    def _read(self):
+        try:
+            with open(self.path) as f:
+                for line in f:
+                    if line.rstrip().endswith("*"):
+                        return float(line.split(":")[1].strip().split("M")[0])
+        except (OSError, ValueError, IndexError):
+            return None
+        return None
+
+    def __enter__(self):
+        import threading
+        if self.path is None:
+            return self
+        self._stop = threading.Event()
+
+        def run():
+            while not self._stop.wait(self.period):
+                v = self._read()
+                if v is not None:
+                    self.samples.append(v)
+        self._thread = threading.Thread(target=run, daemon=True)
+        self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join()
+        return False
+
+    def summary(self):
+        if not self.samples:
+            return None
+        v = np.array(self.samples)
+        return {"samples": int(v.size), "median_mhz": float(np.median(v)), "mean_mhz": round(float(v.mean()), 1),
+                "min_mhz": float(v.min()), "max_mhz": float(v.max())}
+
+
 def device_peak(tpm_peak_key):
     """The dense MFMA peak recomputed from the device's own figures: CUs and
     peak engine clock from hipDeviceGetAttribute (the clock torch does not
@@ -584,11 +637,13 @@ def main():
     value = flops_step / (ms_per_step * 1e-3) / 1e12
     log(f"bench: {args.steps} steps, {ms_per_step:.3f} ms/step, {value:.1f} TFLOP/s")
 
-    # per-kernel timing with events on the launch stream (separate pass)
+    # per-kernel timing with events on the launch stream (separate pass), with
+    # the engine clock sampled meanwhile
     timer = KernelTimer()
-    for _ in range(args.steps):
-        step(timer)
-    torch.cuda.synchronize()
+    with ClockSampler() as clock:
+        for _ in range(args.steps):
+            step(timer)
+        torch.cuda.synchronize()
     kstats = timer.summary()
     peak = PEAK_TFLOPS[dtype]
     for name, fl in kern_flops.items():
@@ -646,6 +701,9 @@ def main():
     if dp is not None:
         device["clock_khz"] = dp["clock_khz"]
         device["peak_from_props_tflops"] = round(dp["peak_tflops"], 1)
+    sclk = clock.summary()
+    if sclk is not None:   # the driver's figure, not the shader clock itself (it reads lower)
+        device["driver_reported_sclk_during_kernel_pass"] = sclk
 
     result = {
         "metric": (METRIC_ATTN if attn else METRIC_BWD if getattr(wl, "backward", False)
