@@ -68,12 +68,17 @@ def kernel_source_sha256() -> str:
     return h.hexdigest()
 
 
-def measured_traffic(workload: str, kernel: str):
+# The partial dtype the committed traffic profiles were taken with.
+PROFILED_PARTIAL_DTYPE = "f32"
+
+
+def measured_traffic(workload: str, kernel: str, partial_dtype: str = PROFILED_PARTIAL_DTYPE):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 FETCH_SIZE /
     WRITE_SIZE passes (scaled by the copy calibration), or None when there are
-    none for this workload or the kernels have changed since they were taken."""
+    none for this workload, the kernels have changed since they were taken, or
+    the run's partials differ in dtype from the profiled run's."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
-    if not os.path.exists(path):
+    if not os.path.exists(path) or partial_dtype != PROFILED_PARTIAL_DTYPE:
         return None
     with open(path) as fh:
         t = json.load(fh)
@@ -619,6 +624,8 @@ def main():
     else:
         step, kern_flops, kern_bytes, psum_bytes, inputs, out = build_bf16_step(
             tpm, wl, args.partial_dtype)
+    # only the bf16 forward takes --partial-dtype; every other step's partials are fixed
+    pdt = args.partial_dtype if not (attn or wl.backward or wl.fp8) else PROFILED_PARTIAL_DTYPE
     torch.cuda.synchronize()
 
     for _ in range(args.warmup):
@@ -650,7 +657,7 @@ def main():
         kstats[name]["tflops"] = fl / (kstats[name]["avg_us"] * 1e-6) / 1e12
         kstats[name]["frac_of_peak"] = kstats[name]["tflops"] / peak
         kstats[name]["algorithmic_bytes"] = kern_bytes[name]
-        kstats[name]["traffic"] = measured_traffic(wl.name, name)
+        kstats[name]["traffic"] = measured_traffic(wl.name, name, pdt)
     if "weight_amax" in kstats:   # reads the whole of A and B once per step
         wbytes = 2 * 2 * wl.d * wl.H
         kstats["weight_amax"]["GBps"] = wbytes / (kstats["weight_amax"]["avg_us"] * 1e-6) / 1e9
@@ -658,12 +665,12 @@ def main():
     if "partial_sum" in kstats:
         kstats["partial_sum"]["GBps"] = psum_bytes / (kstats["partial_sum"]["avg_us"] * 1e-6) / 1e9
         kstats["partial_sum"]["algorithmic_bytes"] = psum_bytes
-        kstats["partial_sum"]["traffic"] = measured_traffic(wl.name, "partial_sum")
+        kstats["partial_sum"]["traffic"] = measured_traffic(wl.name, "partial_sum", pdt)
     dom = max(kern_flops, key=lambda k: kstats[k]["total_ms"])
     ach = kstats[dom]["tflops"]
     roofline = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(ach / peak, 4),
-                "traffic": measured_traffic(wl.name, dom),
+                "traffic": measured_traffic(wl.name, dom, pdt),
                 "flops_per_launch": kern_flops[dom], "algorithmic_bytes": kern_bytes[dom],
                 "avg_launch_us": round(kstats[dom]["avg_us"], 2),
                 "median_launch_us": round(kstats[dom]["median_us"], 2)}
