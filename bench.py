@@ -728,6 +728,10 @@ def main():
                                                                 else args.partial_dtype),
                     "parallelism": f"tp{wl.N} ranks sequentially on 1 GPU" if wl.N > 1 else "none"}),
         "pct_of_peak": round(100 * value / peak, 2),
+        # one rank's shard (the event-timed averages of its flop-bearing launches
+        # added) and the sum of the partials, once per step
+        "per_rank_us": round(sum(kstats[k]["avg_us"] for k in kern_flops), 2),
+        "partial_sum_us": round(kstats["partial_sum"]["avg_us"], 2) if "partial_sum" in kstats else None,
         "roofline": roofline,
         "kernels": {k: {kk: (round(vv, 3) if isinstance(vv, float) else vv) for kk, vv in v.items()}
                     for k, v in kstats.items()},
