@@ -21,7 +21,8 @@ GB = 1 << 30
 
 
 def _declared_functions():
-    text = open(HEADER).read()
+    with open(HEADER) as fh:
+        text = fh.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(tp_\w+)\s*\(", text, flags=re.M)))
 

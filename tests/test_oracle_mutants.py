@@ -293,7 +293,8 @@ def _heads_variant(scale_fn=None, mask_shift=1, swap_kv=False, softmax_axis=-1, 
                 if causal:
                     s = np.where(np.triu(np.ones((S, S), bool), k=mask_shift), -np.inf, s)
                 m = np.max(s, axis=softmax_axis, keepdims=True)
-                e = np.exp(s - m)
+                with np.errstate(invalid="ignore"):   # a mutant's wrong axis meets a fully masked row
+                    e = np.exp(s - m)
                 p = e / np.sum(e, axis=softmax_axis, keepdims=True)
                 out[b * S:(b + 1) * S, h * dh:(h + 1) * dh] = p @ v
         return oracle.bf16_encode(out) if rounding else out
