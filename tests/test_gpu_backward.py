@@ -101,6 +101,7 @@ CASES = [
     (264, 8, 64, 8),
     (1032, 520, 4160, 8),
     (200, 1032, 2064, 1),
+    (264, 200, 2400, 3),            # N = 3: F = 800
 ]
 
 

@@ -47,6 +47,7 @@ CASES = [
     (272, 144, 576, 2),
     (528, 272, 1088, 4),
     (1040, 528, 4224, 8),
+    (272, 208, 2496, 3),            # N = 3: F = 832
 ]
 
 

@@ -103,6 +103,8 @@ RAGGED = [
     (1, 64, 256, 1, "f32"),
     (257, 8, 64, 8, "f32"),
     (1030, 520, 4160, 8, "bf16"),
+    (333, 200, 2400, 3, "f32"),     # N = 3: F = 800, not a power of two
+    (130, 96, 1152, 6, "bf16"),     # N = 6: F = 192
 ]
 
 
