@@ -109,6 +109,9 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="stop adding oracle row chunks once this much CPU time is spent")
     p.add_argument("--partial-dtype", choices=["f32", "bf16"], default="f32")
+    p.add_argument("--weight-layout", choices=["math", "linear"], default="math",
+                   help="bf16 forward only: weights as A [d, H], B [H, d] (math), or as the "
+                        "linear layers store them, W1 [H, d], W2 [d, H] (linear)")
     return p.parse_args()
 
 
@@ -233,7 +236,11 @@ def device_peak(tpm_peak_key):
     return vals
 
 
-def build_bf16_step(tpm, wl, partial_dtype):
+def build_bf16_step(tpm, wl, partial_dtype, weight_layout="math"):
+    """The forward of every rank's shard, then the sum of the partials. With
+    the linear layout the weights are stored [out, in] (W1 = Aᵀ, W2 = Bᵀ,
+    transposed once outside the timed region) and the rank's shards are a row
+    block of W1 and a column block of W2."""
     import torch
     X, A, B = __import__("workloads").make_inputs(wl)
     Xd, Ad, Bd = dev_bf16(X), dev_bf16(A), dev_bf16(B)
@@ -242,27 +249,34 @@ def build_bf16_step(tpm, wl, partial_dtype):
     Z = torch.empty((M, F), dtype=torch.bfloat16, device="cuda")
     parts = [torch.empty((M, d), dtype=pdt, device="cuda") for _ in range(N)]
     Y = torch.empty((M, d), dtype=torch.float32, device="cuda")
-    views = [(Ad[:, r * F:(r + 1) * F], Bd[r * F:(r + 1) * F, :]) for r in range(N)]
+    if weight_layout == "linear":
+        W1, W2 = Ad.t().contiguous(), Bd.t().contiguous()
+        del Ad, Bd
+        views = [(W1[r * F:(r + 1) * F], W2[:, r * F:(r + 1) * F]) for r in range(N)]
+        col, row, kc, kr = tpm.tp_mlp_col_gelu_wt, tpm.tp_mlp_row_partial_wt, "col_gelu_wt", "row_partial_wt"
+    else:
+        views = [(Ad[:, r * F:(r + 1) * F], Bd[r * F:(r + 1) * F, :]) for r in range(N)]
+        col, row, kc, kr = tpm.tp_mlp_col_gelu, tpm.tp_mlp_row_partial, "col_gelu", "row_partial"
 
     def step(timer=None):
         for r in range(N):
             A_i, B_i = views[r]
             if timer is None:
-                tpm.tp_mlp_col_gelu(Xd, A_i, Z)
-                tpm.tp_mlp_row_partial(Z, B_i, parts[r])
+                col(Xd, A_i, Z)
+                row(Z, B_i, parts[r])
             else:
-                timer.around("col_gelu", lambda: tpm.tp_mlp_col_gelu(Xd, A_i, Z))
-                timer.around("row_partial", lambda: tpm.tp_mlp_row_partial(Z, B_i, parts[r]))
+                timer.around(kc, lambda: col(Xd, A_i, Z))
+                timer.around(kr, lambda: row(Z, B_i, parts[r]))
         if N > 1:
             if timer is None:
                 tpm.tp_partial_sum(parts, Y=Y)
             else:
                 timer.around("partial_sum", lambda: tpm.tp_partial_sum(parts, Y=Y))
 
-    kern_flops = {"col_gelu": 2 * M * d * F, "row_partial": 2 * M * d * F}
+    kern_flops = {kc: 2 * M * d * F, kr: 2 * M * d * F}
     # algorithmic bytes: each operand read once, each output written once
-    kern_bytes = {"col_gelu": (M * d + d * F) * 2 + M * F * 2,
-                  "row_partial": (M * F + F * d) * 2 + M * d * parts[0].element_size()}
+    kern_bytes = {kc: (M * d + d * F) * 2 + M * F * 2,
+                  kr: (M * F + F * d) * 2 + M * d * parts[0].element_size()}
     psum_bytes = (N * parts[0].element_size() + Y.element_size()) * M * d
     out = Y if N > 1 else parts[0]
     return step, kern_flops, kern_bytes, psum_bytes, (X, A, B), out
@@ -623,7 +637,7 @@ def main():
         step, kern_flops, kern_bytes, psum_bytes, inputs, out = build_e4m3_step(tpm, wl)
     else:
         step, kern_flops, kern_bytes, psum_bytes, inputs, out = build_bf16_step(
-            tpm, wl, args.partial_dtype)
+            tpm, wl, args.partial_dtype, args.weight_layout)
     # only the bf16 forward takes --partial-dtype; every other step's partials are fixed
     pdt = args.partial_dtype if not (attn or wl.backward or wl.fp8) else PROFILED_PARTIAL_DTYPE
     torch.cuda.synchronize()
@@ -726,6 +740,8 @@ def main():
                    {"workload": wl.name, "M": wl.M, "d": wl.d, "F": wl.F, "tp_ranks": wl.N,
                     "partial_dtype": "f32" if wl.backward else ("bf16" if wl.fp8
                                                                 else args.partial_dtype),
+                    "weight_layout": ("linear [out, in]" if args.weight_layout == "linear"
+                                      and not (wl.backward or wl.fp8) else "math [in, out]"),
                     "parallelism": f"tp{wl.N} ranks sequentially on 1 GPU" if wl.N > 1 else "none"}),
         "pct_of_peak": round(100 * value / peak, 2),
         # one rank's shard (the event-timed averages of its flop-bearing launches

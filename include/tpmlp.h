@@ -125,6 +125,43 @@ int tp_mlp_shard(const void* X, const void* A, const void* B, void* Y_i, int y_d
                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * ---------------------------------------------------------------------------
+ * The same forward with the weights stored as their transposes, the
+ * [out_features, in_features] layout of the linear layers in the pages'
+ * column- and row-parallel code pattern ("Megatron-LM deep architecture",
+ * code-pattern section): W1 = Aᵀ [H, d] and W2 = Bᵀ [d, H]. Rank i's
+ * shards are W1_i = W1[i·F : (i+1)·F, :] (a block of rows) and
+ * W2_i = W2[:, i·F : (i+1)·F] (a block of columns); the products and the
+ * outputs are those of the math-layout calls above, to the bit.
+ * ---------------------------------------------------------------------------
+ */
+
+/*
+ * Z_i = bf16(GeLU(X · W1_iᵀ)). X : device, bf16 [M, d], dense.
+ * W1_i : device, bf16 [F, d], row stride ldw >= d (a row block of W1).
+ * Z_i : device, bf16 [M, F], dense. Errors as for tp_mlp_col_gelu.
+ */
+int tp_mlp_col_gelu_wt(const void* X, const void* W1_i, int64_t ldw, void* Z_i, int64_t M,
+                       int64_t d, int64_t F, void* stream);
+
+/*
+ * Y_i = Z_i · W2_iᵀ, accumulated in fp32. Z_i : device, bf16 [M, F], dense.
+ * W2_i : device, bf16 [d, F], row stride ldw >= F (a column block of W2 has
+ * ldw = H). Y_i : device, [M, d], dense, y_dtype TPM_F32 or TPM_BF16.
+ */
+int tp_mlp_row_partial_wt(const void* Z_i, const void* W2_i, int64_t ldw, void* Y_i,
+                          int y_dtype, int64_t M, int64_t F, int64_t d, void* stream);
+
+/*
+ * tp_mlp_shard with W1 = Aᵀ : device, bf16 [H, d] and W2 = Bᵀ : device,
+ * bf16 [d, H], both dense; the workspace is sized by
+ * tp_mlp_shard_workspace_size and holds Z_i on return.
+ */
+int tp_mlp_shard_wt(const void* X, const void* W1, const void* W2, void* Y_i, int y_dtype,
+                    int64_t M, int64_t d, int64_t H, int N, int rank, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/*
  * Sum of the partial outputs, the arithmetic of the AllReduce(sum) that ends
  * the block ("Megatron-LM deep architecture", eq. for Output:
  * Output = Σ_i Y_i):

@@ -22,6 +22,7 @@ import torch  # loads the HIP runtime that libtpmlp.so then binds to
 __all__ = [
     "LIB_PATH", "ABI_VERSION", "TpmError", "abi_version", "status_string",
     "tp_mlp_col_gelu", "tp_mlp_row_partial", "tp_mlp_shard", "tp_mlp_shard_workspace_size",
+    "tp_mlp_col_gelu_wt", "tp_mlp_row_partial_wt", "tp_mlp_shard_wt",
     "tp_partial_sum", "tp_partial_sum_rows", "tp_reduce_scatter_share", "tp_amax_bf16", "tp_quant_e4m3", "tp_mlp_col_gelu_e4m3",
     "tp_mlp_row_partial_e4m3", "tp_mlp_shard_e4m3", "tp_mlp_shard_e4m3_workspace_size",
     "tp_amax_history_push", "tp_mlp_col_gelu_e4m3_delayed", "tp_mlp_shard_e4m3_delayed",
@@ -50,6 +51,9 @@ _SIGNATURES = {
     "tp_mlp_row_partial": (_int, [_vp, _vp, _vp, _int, _i64, _i64, _i64, _vp]),
     "tp_mlp_shard_workspace_size": (_sz, [_i64, _i64, _i64, _int]),
     "tp_mlp_shard": (_int, [_vp, _vp, _vp, _vp, _int, _i64, _i64, _i64, _int, _int, _vp, _sz, _vp]),
+    "tp_mlp_col_gelu_wt": (_int, [_vp, _vp, _i64, _vp, _i64, _i64, _i64, _vp]),
+    "tp_mlp_row_partial_wt": (_int, [_vp, _vp, _i64, _vp, _int, _i64, _i64, _i64, _vp]),
+    "tp_mlp_shard_wt": (_int, [_vp, _vp, _vp, _vp, _int, _i64, _i64, _i64, _int, _int, _vp, _sz, _vp]),
     "tp_partial_sum": (_int, [ctypes.POINTER(_vp), _int, _int, _vp, _int, _i64, _vp]),
     "tp_partial_sum_rows": (_int, [ctypes.POINTER(_vp), _int, _int, _i64, _i64, _i64, _i64, _vp,
                                    _int, _vp, _int, _vp]),
@@ -228,6 +232,81 @@ def tp_mlp_shard(X: torch.Tensor, A: torch.Tensor, B: torch.Tensor, N: int, rank
                             _dtype_code(Y_i.dtype), M, d, H, N, rank, workspace.data_ptr(),
                             workspace.numel() * workspace.element_size(), _stream(stream)),
            "tp_mlp_shard")
+    return Y_i
+
+
+# The forward with the weights stored transposed, as the pages' column- and
+# row-parallel linear layers keep them ([out_features, in_features]).
+
+def tp_mlp_col_gelu_wt(X: torch.Tensor, W1_i: torch.Tensor, Z_i: torch.Tensor | None = None,
+                       stream=None) -> torch.Tensor:
+    """Z_i = bf16(GeLU(X·W1_iᵀ)). X [M, d] bf16; W1_i [F, d] bf16 (the column-parallel
+    layer's weight: unit column stride, any row stride)."""
+    _need(X, "X", torch.bfloat16, 2)
+    _need(W1_i, "W1_i", torch.bfloat16, 2, contiguous=False)
+    if W1_i.stride(1) != 1:
+        raise ValueError("W1_i must have unit column stride")
+    M, d = X.shape
+    F, d2 = W1_i.shape
+    if d2 != d:
+        raise ValueError(f"inner dimensions differ: X {tuple(X.shape)}, W1_i {tuple(W1_i.shape)}")
+    if Z_i is None:
+        Z_i = torch.empty((M, F), dtype=torch.bfloat16, device=X.device)
+    _need(Z_i, "Z_i", torch.bfloat16, 2)
+    if tuple(Z_i.shape) != (M, F):
+        raise ValueError("Z_i has the wrong shape")
+    _check(lib.tp_mlp_col_gelu_wt(X.data_ptr(), W1_i.data_ptr(), W1_i.stride(0), Z_i.data_ptr(),
+                                  M, d, F, _stream(stream)), "tp_mlp_col_gelu_wt")
+    return Z_i
+
+
+def tp_mlp_row_partial_wt(Z_i: torch.Tensor, W2_i: torch.Tensor, Y_i: torch.Tensor | None = None,
+                          out_dtype=torch.float32, stream=None) -> torch.Tensor:
+    """Y_i = Z_i·W2_iᵀ (fp32 or bf16). Z_i [M, F] bf16; W2_i [d, F] bf16 (the row-parallel
+    layer's weight, e.g. a column block of a full [d, H] weight: unit column stride)."""
+    _need(Z_i, "Z_i", torch.bfloat16, 2)
+    _need(W2_i, "W2_i", torch.bfloat16, 2, contiguous=False)
+    if W2_i.stride(1) != 1:
+        raise ValueError("W2_i must have unit column stride")
+    M, F = Z_i.shape
+    d, F2 = W2_i.shape
+    if F2 != F:
+        raise ValueError(f"inner dimensions differ: Z_i {tuple(Z_i.shape)}, W2_i {tuple(W2_i.shape)}")
+    if Y_i is None:
+        Y_i = torch.empty((M, d), dtype=out_dtype, device=Z_i.device)
+    _need(Y_i, "Y_i", None, 2)
+    if tuple(Y_i.shape) != (M, d):
+        raise ValueError("Y_i has the wrong shape")
+    _check(lib.tp_mlp_row_partial_wt(Z_i.data_ptr(), W2_i.data_ptr(), W2_i.stride(0),
+                                     Y_i.data_ptr(), _dtype_code(Y_i.dtype), M, F, d,
+                                     _stream(stream)), "tp_mlp_row_partial_wt")
+    return Y_i
+
+
+def tp_mlp_shard_wt(X: torch.Tensor, W1: torch.Tensor, W2: torch.Tensor, N: int, rank: int,
+                    Y_i: torch.Tensor | None = None, out_dtype=torch.float32,
+                    workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """tp_mlp_shard with the weights stored transposed: W1 = Aᵀ [H, d], W2 = Bᵀ [d, H]."""
+    _need(X, "X", torch.bfloat16, 2)
+    _need(W1, "W1", torch.bfloat16, 2)
+    _need(W2, "W2", torch.bfloat16, 2)
+    M, d = X.shape
+    H, d1 = W1.shape
+    if d1 != d or tuple(W2.shape) != (d, H):
+        raise ValueError(f"shape mismatch: X {tuple(X.shape)}, W1 {tuple(W1.shape)}, W2 {tuple(W2.shape)}")
+    if Y_i is None:
+        Y_i = torch.empty((M, d), dtype=out_dtype, device=X.device)
+    _need(Y_i, "Y_i", None, 2)
+    if tuple(Y_i.shape) != (M, d):
+        raise ValueError("Y_i has the wrong shape")
+    need = tp_mlp_shard_workspace_size(M, d, H, N) if N >= 1 else 0
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=X.device)
+    _need(workspace, "workspace", None)
+    _check(lib.tp_mlp_shard_wt(X.data_ptr(), W1.data_ptr(), W2.data_ptr(), Y_i.data_ptr(),
+                               _dtype_code(Y_i.dtype), M, d, H, N, rank, workspace.data_ptr(),
+                               workspace.numel() * workspace.element_size(), _stream(stream)),
+           "tp_mlp_shard_wt")
     return Y_i
 
 

@@ -152,6 +152,87 @@ int tp_mlp_shard(const void* X, const void* A, const void* B, void* Y_i, int y_d
   return status_of(e);
 }
 
+// ------------------------------------------------ transposed weights --
+// The weights stored as nn.Linear keeps them ([out, in]): the GEMMs read them
+// K-contiguous (the engine's K-major Q operand) instead of N-contiguous.
+
+int tp_mlp_col_gelu_wt(const void* X, const void* W1_i, int64_t ldw, void* Z_i, int64_t M,
+                       int64_t d, int64_t F, void* stream) {
+  int st = check_dims(M, d, F, 8);
+  if (st != TPM_OK) return st;
+  if (ldw < d || ldw > kMaxLd) return TPM_ERR_SHAPE;
+  if (M == 0) return TPM_OK;
+  if (!X || !W1_i || !Z_i) return TPM_ERR_NULL;
+  if (!aligned16(X) || !aligned16(W1_i) || !aligned16(Z_i) || ldw % 8 != 0) return TPM_ERR_ALIGN;
+  const Span z = mat_span(Z_i, M, F, F, 2);
+  if (overlap(z, mat_span(X, M, d, d, 2)) || overlap(z, mat_span(W1_i, F, d, ldw, 2)))
+    return TPM_ERR_ALIAS;
+  return status_of(tpmlp::launch_gemm_bf16_ex(
+      static_cast<const uint16_t*>(X), d, static_cast<const uint16_t*>(W1_i), ldw, Z_i, F,
+      (int)M, (int)F, (int)d, OutKind::GeluBf16, tpmlp::Layout::QT, nullptr, 0, nullptr,
+      as_stream(stream)));
+}
+
+int tp_mlp_row_partial_wt(const void* Z_i, const void* W2_i, int64_t ldw, void* Y_i,
+                          int y_dtype, int64_t M, int64_t F, int64_t d, void* stream) {
+  if (y_dtype != TPM_F32 && y_dtype != TPM_BF16) return TPM_ERR_DTYPE;
+  int st = check_dims(M, F, d, 8);
+  if (st != TPM_OK) return st;
+  if (ldw < F || ldw > kMaxLd) return TPM_ERR_SHAPE;
+  if (M == 0) return TPM_OK;
+  if (!Z_i || !W2_i || !Y_i) return TPM_ERR_NULL;
+  if (!aligned16(Z_i) || !aligned16(W2_i) || !aligned16(Y_i) || ldw % 8 != 0) return TPM_ERR_ALIGN;
+  const Span y = mat_span(Y_i, M, d, d, y_dtype == TPM_F32 ? 4 : 2);
+  if (overlap(y, mat_span(Z_i, M, F, F, 2)) || overlap(y, mat_span(W2_i, d, F, ldw, 2)))
+    return TPM_ERR_ALIAS;
+  return status_of(tpmlp::launch_gemm_bf16_ex(
+      static_cast<const uint16_t*>(Z_i), F, static_cast<const uint16_t*>(W2_i), ldw, Y_i, d,
+      (int)M, (int)d, (int)F, y_dtype == TPM_F32 ? OutKind::F32 : OutKind::Bf16,
+      tpmlp::Layout::QT, nullptr, 0, nullptr, as_stream(stream)));
+}
+
+int tp_mlp_shard_wt(const void* X, const void* W1, const void* W2, void* Y_i, int y_dtype,
+                    int64_t M, int64_t d, int64_t H, int N, int rank, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  if (y_dtype != TPM_F32 && y_dtype != TPM_BF16) return TPM_ERR_DTYPE;
+  if (N < 1 || rank < 0 || rank >= N) return TPM_ERR_ARG;
+  if (H <= 0 || H % N != 0) return TPM_ERR_SHAPE;
+  const int64_t F = H / N;
+  int st = check_dims(M, d, F, 8);
+  if (st != TPM_OK) return st;
+  if (H > kMaxLd || d > kMaxLd || H * d > (int64_t(1) << 46)) return TPM_ERR_SHAPE;
+  if (M == 0) return TPM_OK;
+  if (!X || !W1 || !W2 || !Y_i) return TPM_ERR_NULL;
+  if (!workspace || workspace_bytes < tp_mlp_shard_workspace_size(M, d, H, N))
+    return TPM_ERR_WORKSPACE;
+  if (!aligned16(X) || !aligned16(W1) || !aligned16(W2) || !aligned16(Y_i) ||
+      !aligned16(workspace))
+    return TPM_ERR_ALIGN;
+  const Span sx = mat_span(X, M, d, d, 2), s1 = mat_span(W1, H, d, d, 2);
+  const Span s2 = mat_span(W2, d, H, H, 2);
+  const Span sy = mat_span(Y_i, M, d, d, y_dtype == TPM_F32 ? 4 : 2);
+  const Span sw = {reinterpret_cast<uintptr_t>(workspace),
+                   reinterpret_cast<uintptr_t>(workspace) + (uintptr_t)(M * F * 2)};
+  if (overlap(sy, sx) || overlap(sy, s1) || overlap(sy, s2) || overlap(sy, sw) ||
+      overlap(sw, sx) || overlap(sw, s1) || overlap(sw, s2))
+    return TPM_ERR_ALIAS;
+
+  // The shards of the transposed weights: W1_i = W1[rank·F : (rank+1)·F, :]
+  // (dense rows), W2_i = W2[:, rank·F : (rank+1)·F] (row stride H).
+  const uint16_t* W1_i = static_cast<const uint16_t*>(W1) + (int64_t)rank * F * d;
+  const uint16_t* W2_i = static_cast<const uint16_t*>(W2) + (int64_t)rank * F;
+  uint16_t* Z = static_cast<uint16_t*>(workspace);
+  hipStream_t s = as_stream(stream);
+  hipError_t e = tpmlp::launch_gemm_bf16_ex(static_cast<const uint16_t*>(X), d, W1_i, d, Z, F,
+                                            (int)M, (int)F, (int)d, OutKind::GeluBf16,
+                                            tpmlp::Layout::QT, nullptr, 0, nullptr, s);
+  if (e != hipSuccess) return TPM_ERR_HIP;
+  e = tpmlp::launch_gemm_bf16_ex(Z, F, W2_i, H, Y_i, d, (int)M, (int)d, (int)F,
+                                 y_dtype == TPM_F32 ? OutKind::F32 : OutKind::Bf16,
+                                 tpmlp::Layout::QT, nullptr, 0, nullptr, s);
+  return status_of(e);
+}
+
 int tp_partial_sum(const void* const* parts, int N, int part_dtype, void* Y, int y_dtype,
                    int64_t numel, void* stream) {
   if ((part_dtype != TPM_F32 && part_dtype != TPM_BF16) ||

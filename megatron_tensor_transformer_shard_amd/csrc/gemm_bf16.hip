@@ -481,7 +481,8 @@ hipError_t launch_one(const GemmArgs* a, int n, hipStream_t stream) {
 
 // The (layout, epilogue) combinations the path uses: the forward's
 // K-major P / N-major Q with GeLU, fp32 or bf16 output; K-major Q with the
-// GeLU-gradient or fp32 epilogue; M-major P with fp32 output.
+// same three (the forward with weights stored transposed) or the
+// GeLU-gradient epilogue; M-major P with fp32 output.
 template <int BM, int BN, bool KTAIL>
 hipError_t launch_cfg(const GemmArgs* a, int n, OutKind out, Layout lay, hipStream_t stream) {
   if (lay == Layout::NN) {
@@ -496,6 +497,8 @@ hipError_t launch_cfg(const GemmArgs* a, int n, OutKind out, Layout lay, hipStre
     switch (out) {
       case OutKind::GeluGradBf16: return launch_one<BM, BN, (int)OutKind::GeluGradBf16, KTAIL, false, true>(a, n, stream);
       case OutKind::F32: return launch_one<BM, BN, (int)OutKind::F32, KTAIL, false, true>(a, n, stream);
+      case OutKind::GeluBf16: return launch_one<BM, BN, (int)OutKind::GeluBf16, KTAIL, false, true>(a, n, stream);
+      case OutKind::Bf16: return launch_one<BM, BN, (int)OutKind::Bf16, KTAIL, false, true>(a, n, stream);
       default: return hipErrorInvalidValue;
     }
   }

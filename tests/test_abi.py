@@ -109,6 +109,54 @@ def test_shard_validation():
     assert shard(Y=BASE + 4 * GB) == EALIAS            # Y overlaps workspace
 
 
+def col_gelu_wt(X=BASE, W=BASE + GB, ldw=64, Z=BASE + 2 * GB, M=32, d=64, F=256):
+    return L.tp_mlp_col_gelu_wt(X, W, ldw, Z, M, d, F, None)
+
+
+def test_col_gelu_wt_validation():
+    assert col_gelu_wt(M=0) == OK
+    assert col_gelu_wt(W=None) == ENULL
+    assert col_gelu_wt(d=60) == ESHAPE
+    assert col_gelu_wt(ldw=56) == ESHAPE              # ldw < d
+    assert col_gelu_wt(ldw=68) == EALIGN              # row stride not 16-byte multiple
+    assert col_gelu_wt(W=BASE + GB + 8) == EALIGN
+    assert col_gelu_wt(Z=BASE + GB + 4096) == EALIAS  # Z overlaps W1_i [F, d]
+    assert col_gelu_wt(Z=BASE + 64) == EALIAS         # Z overlaps X
+
+
+def row_partial_wt(Z=BASE, W=BASE + GB, ldw=128, Y=BASE + 2 * GB, yd=F32, M=32, F=128, d=64):
+    return L.tp_mlp_row_partial_wt(Z, W, ldw, Y, yd, M, F, d, None)
+
+
+def test_row_partial_wt_validation():
+    assert row_partial_wt(M=0) == OK
+    assert row_partial_wt(yd=E4M3) == EDTYPE
+    assert row_partial_wt(Z=None) == ENULL
+    assert row_partial_wt(ldw=120) == ESHAPE          # ldw < F
+    assert row_partial_wt(ldw=132) == EALIGN
+    assert row_partial_wt(F=12) == ESHAPE
+    assert row_partial_wt(Y=BASE + GB + 1024) == EALIAS   # Y overlaps W2_i [d, F], stride ldw
+
+
+def shard_wt(X=BASE, W1=BASE + GB, W2=BASE + 2 * GB, Y=BASE + 3 * GB, yd=F32, M=32, d=64, H=256,
+             N=2, rank=0, ws=BASE + 4 * GB, wsb=None):
+    if wsb is None:
+        wsb = L.tp_mlp_shard_workspace_size(M, d, H, N)
+    return L.tp_mlp_shard_wt(X, W1, W2, Y, yd, M, d, H, N, rank, ws, wsb, None)
+
+
+def test_shard_wt_validation():
+    assert shard_wt(M=0) == OK
+    assert shard_wt(rank=2) == EARG
+    assert shard_wt(N=3) == ESHAPE
+    assert shard_wt(yd=9) == EDTYPE
+    assert shard_wt(W2=None) == ENULL
+    assert shard_wt(wsb=100) == EWS
+    assert shard_wt(W1=BASE + GB + 2) == EALIGN
+    assert shard_wt(Y=BASE + 2 * GB + 256) == EALIAS   # Y overlaps W2
+    assert shard_wt(ws=BASE + GB + 1024) == EALIAS     # workspace overlaps W1
+
+
 def psum(parts, N=None, pd=F32, Y=BASE + 10 * GB, yd=F32, numel=4096):
     arr = (ctypes.c_void_p * max(1, len(parts)))(*parts)
     return L.tp_partial_sum(arr, len(parts) if N is None else N, pd, Y, yd, numel, None)
