@@ -85,3 +85,19 @@ def test_backward_bf16_and_fp8_in_a_graph(tpm):
         tpm.tp_mlp_shard_backward_fp8(Xd, Ad, Bd, dYd, N, 1, dX_i=outs[3], dA_i=outs[4],
                                       dB_i=outs[5], workspace=ws8)
     _replay_and_compare(step, outs)
+
+
+def test_transposed_weight_forward_in_a_graph(tpm):
+    import torch
+    M, d, H, N = 300, 136, 544, 2
+    X, A, B = make_random(M, d, H, seed=34, sigma=0.05)
+    Xd = dev_bf16(X)
+    W1, W2 = dev_bf16(A).t().contiguous(), dev_bf16(B).t().contiguous()
+    parts = [torch.empty((M, d), dtype=torch.float32, device="cuda") for _ in range(N)]
+    ws = [torch.empty(tpm.tp_mlp_shard_workspace_size(M, d, H, N), dtype=torch.uint8,
+                      device="cuda") for _ in range(N)]
+
+    def step():
+        for r in range(N):
+            tpm.tp_mlp_shard_wt(Xd, W1, W2, N, r, Y_i=parts[r], workspace=ws[r])
+    _replay_and_compare(step, parts)

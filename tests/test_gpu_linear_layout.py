@@ -74,6 +74,31 @@ def test_transposed_weights_vs_oracle_and_math_layout(tpm, M, d, H, N, odt):
         assert same, f"rank {rank}: the transposed-weight path differs from the math-layout path"
 
 
+def test_padded_weight_rows(tpm):
+    """W1 and W2 held in buffers with padded rows (row strides d + 24 and
+    H + 40): the calls read through the strides and give the contiguous
+    weights' bits."""
+    import torch
+    M, d, H, N = 200, 136, 1088, 4
+    F = H // N
+    X, A, B = make_random(M, d, H, seed=23, sigma=0.05)
+    Xd, Ad, Bd = dev_bf16(X), dev_bf16(A), dev_bf16(B)
+    W1, W2 = Ad.t().contiguous(), Bd.t().contiguous()
+    W1p = torch.full((H, d + 24), float("nan"), dtype=torch.bfloat16, device="cuda")[:, :d]
+    W2p = torch.full((d, H + 40), float("nan"), dtype=torch.bfloat16, device="cuda")[:, :H]
+    W1p.copy_(W1)
+    W2p.copy_(W2)
+    for rank in range(N):
+        Z = tpm.tp_mlp_col_gelu_wt(Xd, W1[rank * F:(rank + 1) * F])
+        Zp = tpm.tp_mlp_col_gelu_wt(Xd, W1p[rank * F:(rank + 1) * F])
+        Y = tpm.tp_mlp_row_partial_wt(Z, W2[:, rank * F:(rank + 1) * F])
+        Yp = tpm.tp_mlp_row_partial_wt(Zp, W2p[:, rank * F:(rank + 1) * F])
+        _sync()
+        assert torch.equal(Z, Zp) and torch.equal(Y, Yp), f"rank {rank}: padded rows change the result"
+        r = max_err_ratio(host_f64(Yp), oracle.mlp_shard(X, A, B, N, rank))
+        assert r <= TOL, f"rank {rank}: err ratio {r:.3e}"
+
+
 def test_shard_width_not_a_multiple_of_8_is_refused_by_both_layouts(tpm):
     """F = H/N = 258: both layouts refuse it with the same status, writing nothing."""
     import torch
