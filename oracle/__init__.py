@@ -16,6 +16,9 @@ What it computes, and where the pages define it:
   section): Y_i = Z_i·B_i.
 * Closed form of the output (same section, eq. for Output):
   Y = Z·B = Σ_i Z_i·B_i = Σ_i Y_i.
+* Bias of the column-parallel linear ("Megatron-LM deep architecture", code
+  pattern): rank i's block b1_i of the first bias is added to X·A_i inside
+  the linear, before GeLU: Z_i = GeLU(X·A_i + b1_i).
 * Sequence-parallel share of the sum and the bias ("Megatron-LM deep
   architecture", sequence-parallel section and the row-parallel code
   pattern): rank j keeps rows [j·M/N, (j+1)·M/N) of Σ_i Y_i, and the bias
@@ -53,7 +56,7 @@ from .mlp import (shard_columns, gelu, col_gelu, row_partial, mlp_shard, partial
                   mlp_shard_e4m3, quantize_inputs_e4m3, delayed_scale, amax_history_push,
                   col_gelu_e4m3_delayed, mlp_shard_e4m3_delayed, gelu_grad,
                   mlp_shard_backward, quant_scale_e5m2, quant_e5m2, quantize_e5m2,
-                  mlp_shard_backward_fp8)
+                  mlp_shard_backward_fp8, col_gelu_bias, mlp_shard_bias, mlp_unsharded_bias)
 
 __all__ = [
     "bf16_decode", "bf16_encode", "e4m3_decode", "e4m3_encode", "E4M3_MAX",
@@ -64,5 +67,5 @@ __all__ = [
     "quant_scale", "quant_e4m3", "col_gelu_e4m3", "requant_z", "row_partial_e4m3",
     "mlp_shard_e4m3", "quantize_inputs_e4m3", "delayed_scale", "amax_history_push",
     "col_gelu_e4m3_delayed", "mlp_shard_e4m3_delayed", "gelu_grad", "mlp_shard_backward",
-    "attention",
+    "col_gelu_bias", "mlp_shard_bias", "mlp_unsharded_bias", "attention",
 ]

@@ -59,6 +59,19 @@ def col_gelu(X_bits: np.ndarray, A_i_bits: np.ndarray) -> np.ndarray:
     return bf16_encode(gelu(S))
 
 
+def col_gelu_bias(X_bits: np.ndarray, A_i_bits: np.ndarray, b_i_bits: np.ndarray) -> np.ndarray:
+    """Column-parallel step with the layer's bias: Z_i = bf16(GeLU(X·A_i + b_i)).
+
+    "Megatron-LM deep architecture", code pattern: the column-parallel
+    linear holds a bias of its own output width (the rank's block of the
+    first bias) and adds it inside the linear, so before the activation that
+    the column/row-parallel section applies to the layer's output.  b_i is
+    bf16 bits of length F; the sum is taken in float64.
+    """
+    S = bf16_decode(X_bits) @ bf16_decode(A_i_bits)
+    return bf16_encode(gelu(S + bf16_decode(b_i_bits)[None, :]))
+
+
 def row_partial(Z_bits: np.ndarray, B_i_bits: np.ndarray) -> np.ndarray:
     """Row-parallel step: the partial output Y_i = Z_i·B_i (float64).
 
@@ -150,6 +163,24 @@ def reduce_scatter_share(parts, rank: int, bias=None) -> np.ndarray:
 def mlp_unsharded(X_bits, A_bits, B_bits) -> np.ndarray:
     """The unsharded block Y = bf16(GeLU(X·A))·B (Z rounded as in a shard)."""
     return row_partial(col_gelu(X_bits, A_bits), B_bits)
+
+
+def mlp_shard_bias(X_bits, A_bits, b1_bits, B_bits, N: int, rank: int) -> np.ndarray:
+    """Rank `rank`'s partial output with the first layer's bias:
+    Y_i = bf16(GeLU(X·A_i + b1_i))·B_i, b1_i the rank's block of b1 (the
+    column-parallel layer's bias shard).  The second layer's bias is not in
+    any partial: it is added once after the sum (`partial_sum_rows`)."""
+    H = A_bits.shape[1]
+    if b1_bits.shape != (H,):
+        raise ValueError("b1 must have the hidden width")
+    lo, hi = shard_columns(H, N, rank)
+    return row_partial(col_gelu_bias(X_bits, A_bits[:, lo:hi], b1_bits[lo:hi]), B_bits[lo:hi, :])
+
+
+def mlp_unsharded_bias(X_bits, A_bits, b1_bits, B_bits, b2_bits) -> np.ndarray:
+    """The unsharded block with both biases: bf16(GeLU(X·A + b1))·B + b2."""
+    return (row_partial(col_gelu_bias(X_bits, A_bits, b1_bits), B_bits)
+            + bf16_decode(b2_bits)[None, :])
 
 
 # ----------------------------------------------------------------------------

@@ -87,6 +87,22 @@ def shard_exact(X_bits, A_bits, B_bits, N, rank):
     return Z, Y
 
 
+def shard_bias_exact(X_bits, A_bits, b1_bits, B_bits, N, rank):
+    """(Z_i, Y_i) with the first layer's bias: Z_i = bf16(GeLU(S + b1_i)) with
+    S + b1_i exact, Y_i = Z_i·B_i exact."""
+    X = [[bf16_value(b) for b in row] for row in X_bits.tolist()]
+    A = [[bf16_value(b) for b in row] for row in A_bits.tolist()]
+    B = [[bf16_value(b) for b in row] for row in B_bits.tolist()]
+    b1 = [bf16_value(b) for b in b1_bits.tolist()]
+    H = len(A[0])
+    F = H // N
+    lo, hi = rank * F, (rank + 1) * F
+    S = matmul_exact(X, [row[lo:hi] for row in A])
+    Z = [[bf16_round(Fraction(gelu_float(float(s + b1[lo + j])))) for j, s in enumerate(row)]
+         for row in S]
+    return Z, matmul_exact(Z, B[lo:hi])
+
+
 def fp8_shard_exact(Xq, sX, Aq, sA, Bq, sB, sZ_given=None):
     """Exact fp8 path on codes: returns (Z on the bf16 grid, Z codes, sZ, Y).
     sZ is Z's own amax scale unless sZ_given (a predicted scale) is passed."""

@@ -1,0 +1,120 @@
+"""Pins of the oracle's column-parallel bias (Z_i = bf16(GeLU(X·A_i + b1_i))),
+on the CPU: a zero bias is the unbiased step, a zero input reduces the step
+to the elementwise GeLU of the bias, an exact rational brute force on tiny
+shapes, and the biased shards summing (plus the second bias, once) to the
+unsharded block."""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import brute
+import oracle
+from workloads import bf16_bits_from_f32, make_bias, make_random
+
+
+def _rel_maxdiff(a, b):
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-300))
+
+
+def test_zero_bias_is_the_unbiased_step():
+    X, A, _ = make_random(24, 32, 64, seed=51, sigma=0.3)
+    zero = np.zeros(64, dtype=np.uint16)
+    assert np.array_equal(oracle.col_gelu_bias(X, A, zero), oracle.col_gelu(X, A))
+    # -0.0 is a zero too
+    nzero = np.full(64, 0x8000, dtype=np.uint16)
+    assert np.array_equal(oracle.col_gelu_bias(X, A, nzero), oracle.col_gelu(X, A))
+
+
+def test_zero_input_gives_the_gelu_of_the_bias():
+    """X = 0: every row of Z_i is bf16(GeLU(b1_i)), each value against
+    math.erfc and an exact round to the bf16 grid."""
+    F = 48
+    b = make_bias(F, seed=52, sigma=2.0)
+    X = np.zeros((5, 16), dtype=np.uint16)
+    _, A, _ = make_random(5, 16, F, seed=53, sigma=0.3)
+    Z = oracle.bf16_decode(oracle.col_gelu_bias(X, A, b))
+    for j in range(F):
+        want = float(brute.bf16_round(Fraction(brute.gelu_float(float(brute.bf16_value(int(b[j])))))))
+        assert np.all(Z[:, j] == want), f"column {j}: {Z[0, j]} != GeLU(b) = {want}"
+
+
+@pytest.mark.parametrize("M,d,H,N,seed", [
+    (3, 4, 16, 1, 60), (5, 8, 16, 2, 61), (7, 16, 16, 4, 62), (9, 5, 12, 3, 63), (1, 16, 16, 4, 64),
+])
+def test_biased_step_matches_brute_force(M, d, H, N, seed):
+    X, A, B = make_random(M, d, H, seed, sigma=0.5)
+    b1 = make_bias(H, seed, sigma=1.0)
+    for rank in range(N):
+        Zb, Yb = brute.shard_bias_exact(X, A, b1, B, N, rank)
+        lo, hi = rank * (H // N), (rank + 1) * (H // N)
+        Z = oracle.bf16_decode(oracle.col_gelu_bias(X, A[:, lo:hi], b1[lo:hi]))
+        Zb_f = np.array([[float(v) for v in row] for row in Zb])
+        assert np.array_equal(Z, Zb_f), f"rank {rank}: Z differs from the brute force"
+        Y = oracle.mlp_shard_bias(X, A, b1, B, N, rank)
+        Yb_f = np.array([[float(v) for v in row] for row in Yb])
+        assert _rel_maxdiff(Y, Yb_f) <= 1e-13, f"rank {rank}: Y differs from the brute force"
+
+
+@pytest.mark.parametrize("M,d,N,seed", [(32, 64, 2, 70), (17, 32, 8, 71), (5, 24, 3, 72)])
+def test_biased_shards_sum_to_the_unsharded_block(M, d, N, seed):
+    """Σ_i Z_i·B_i + b2 = bf16(GeLU(X·A + b1))·B + b2: each rank adds its own
+    block of b1 before GeLU, and b2 is added once, after the sum."""
+    X, A, B = make_random(M, d, 4 * d, seed, sigma=0.1)
+    b1 = make_bias(4 * d, seed, sigma=0.5)
+    b2 = make_bias(d, seed + 1000, sigma=0.5)
+    parts = [oracle.mlp_shard_bias(X, A, b1, B, N, r) for r in range(N)]
+    Y = oracle.partial_sum_rows(parts, 0, M, oracle.bf16_decode(b2))
+    Yfull = oracle.mlp_unsharded_bias(X, A, b1, B, b2)
+    assert _rel_maxdiff(Y, Yfull) <= 1e-12
+    # the bias moves the result: the unbiased block is far from it
+    assert _rel_maxdiff(oracle.mlp_unsharded(X, A, B), Yfull) > 1e-2
+
+
+def test_bias_shape_is_checked():
+    X, A, B = make_random(4, 8, 32, seed=73)
+    with pytest.raises(ValueError):
+        oracle.mlp_shard_bias(X, A, make_bias(31, 73), B, 2, 0)
+
+
+# plausible mistakes, each planted in the oracle, fail at least one pin above
+def _pins_fail():
+    for fn in (test_zero_bias_is_the_unbiased_step, test_zero_input_gives_the_gelu_of_the_bias,
+               lambda: test_biased_step_matches_brute_force(7, 16, 16, 4, 62),
+               lambda: test_biased_shards_sum_to_the_unsharded_block(17, 32, 8, 71)):
+        try:
+            fn()
+        except AssertionError:
+            return True
+    return False
+
+
+def _after_gelu(X, A, b):
+    Z = oracle.gelu(oracle.bf16_decode(X) @ oracle.bf16_decode(A)) + oracle.bf16_decode(b)[None, :]
+    return oracle.bf16_encode(Z)
+
+
+def _bias_subtracted(X, A, b):
+    S = oracle.bf16_decode(X) @ oracle.bf16_decode(A) - oracle.bf16_decode(b)[None, :]
+    return oracle.bf16_encode(oracle.gelu(S))
+
+
+def _bias_dropped(X, A, b):
+    return oracle.col_gelu(X, A)
+
+
+def _whole_bias_first_block(X, A, b):
+    # a rank taking the first block of the bias whatever its columns: here the
+    # reversed block stands in, so a shard gets columns of the wrong positions
+    S = oracle.bf16_decode(X) @ oracle.bf16_decode(A)
+    return oracle.bf16_encode(oracle.gelu(S + oracle.bf16_decode(b[::-1])[None, :]))
+
+
+@pytest.mark.parametrize("mutant", [_after_gelu, _bias_subtracted, _bias_dropped,
+                                    _whole_bias_first_block])
+def test_bias_mutant_is_caught(mutant, monkeypatch):
+    from oracle import mlp as omlp
+    monkeypatch.setattr(omlp, "col_gelu_bias", mutant)
+    monkeypatch.setattr(oracle, "col_gelu_bias", mutant)
+    assert _pins_fail(), f"{mutant.__name__} passed every pin"

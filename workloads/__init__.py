@@ -207,6 +207,11 @@ def make_output_grad(M: int, d: int, seed: int, sigma: float = 1.0) -> np.ndarra
     return _draw_bf16(np.random.default_rng([seed, 1]), (M, d), sigma)
 
 
+def make_bias(n: int, seed: int, sigma: float = 0.5) -> np.ndarray:
+    """A bias vector [n] as bfloat16 bits, from its own generator default_rng([seed, 2])."""
+    return _draw_bf16(np.random.default_rng([seed, 2]), (n,), sigma)
+
+
 def make_inputs(name_or_wl) -> tuple:
     """Inputs of a named workload: (X, A, B) bfloat16 bit arrays (uint16)."""
     wl = WORKLOADS[name_or_wl] if isinstance(name_or_wl, str) else name_or_wl
