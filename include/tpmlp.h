@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define TPM_ABI_VERSION 2
+#define TPM_ABI_VERSION 3
 
 /* Element types. */
 typedef enum {
@@ -160,6 +160,37 @@ int tp_mlp_row_partial_wt(const void* Z_i, const void* W2_i, int64_t ldw, void* 
 int tp_mlp_shard_wt(const void* X, const void* W1, const void* W2, void* Y_i, int y_dtype,
                     int64_t M, int64_t d, int64_t H, int N, int rank, void* workspace,
                     size_t workspace_bytes, void* stream);
+
+/*
+ * ---------------------------------------------------------------------------
+ * The column-parallel linear with its bias ("Megatron-LM deep architecture",
+ * code-pattern section: the column-parallel layer holds a bias of its own
+ * output width, H/N values per rank, and adds it inside the linear, so
+ * before the GeLU that the column/row-parallel section applies to its
+ * output):
+ *   Z_i = bf16(GeLU(X·A_i + b1_i)), b1_i = b1[i·F : (i+1)·F].
+ * The sum is taken in fp32 (the fp32 accumulator plus the bias, one
+ * rounding), then GeLU, then one RNE rounding to bf16. The second layer's
+ * bias is added once, after the sum of the partials (tp_partial_sum_rows).
+ * ---------------------------------------------------------------------------
+ */
+
+/*
+ * X : device, bf16 [M, d], dense. A_i : device, bf16 [d, F], row stride
+ * lda >= F (the math layout, as tp_mlp_col_gelu). b_i : device, bf16 [F],
+ * 16-byte aligned (a block of b1 at an offset of i·F elements, F a multiple
+ * of 8). Z_i : device, bf16 [M, F], dense; must not overlap X, A_i or b_i.
+ * Errors as for tp_mlp_col_gelu, and TPM_ERR_NULL when b_i is NULL.
+ */
+int tp_mlp_col_gelu_bias(const void* X, const void* A_i, int64_t lda, const void* b_i, void* Z_i,
+                         int64_t M, int64_t d, int64_t F, void* stream);
+
+/*
+ * The same with W1_i : device, bf16 [F, d], row stride ldw >= d (the
+ * [out, in] layout of tp_mlp_col_gelu_wt).
+ */
+int tp_mlp_col_gelu_bias_wt(const void* X, const void* W1_i, int64_t ldw, const void* b_i,
+                            void* Z_i, int64_t M, int64_t d, int64_t F, void* stream);
 
 /*
  * Sum of the partial outputs, the arithmetic of the AllReduce(sum) that ends

@@ -23,6 +23,7 @@ __all__ = [
     "LIB_PATH", "ABI_VERSION", "TpmError", "abi_version", "status_string",
     "tp_mlp_col_gelu", "tp_mlp_row_partial", "tp_mlp_shard", "tp_mlp_shard_workspace_size",
     "tp_mlp_col_gelu_wt", "tp_mlp_row_partial_wt", "tp_mlp_shard_wt",
+    "tp_mlp_col_gelu_bias", "tp_mlp_col_gelu_bias_wt",
     "tp_partial_sum", "tp_partial_sum_rows", "tp_reduce_scatter_share", "tp_amax_bf16", "tp_quant_e4m3", "tp_mlp_col_gelu_e4m3",
     "tp_mlp_row_partial_e4m3", "tp_mlp_shard_e4m3", "tp_mlp_shard_e4m3_workspace_size",
     "tp_amax_history_push", "tp_mlp_col_gelu_e4m3_delayed", "tp_mlp_shard_e4m3_delayed",
@@ -52,6 +53,8 @@ _SIGNATURES = {
     "tp_mlp_shard_workspace_size": (_sz, [_i64, _i64, _i64, _int]),
     "tp_mlp_shard": (_int, [_vp, _vp, _vp, _vp, _int, _i64, _i64, _i64, _int, _int, _vp, _sz, _vp]),
     "tp_mlp_col_gelu_wt": (_int, [_vp, _vp, _i64, _vp, _i64, _i64, _i64, _vp]),
+    "tp_mlp_col_gelu_bias": (_int, [_vp, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _vp]),
+    "tp_mlp_col_gelu_bias_wt": (_int, [_vp, _vp, _i64, _vp, _vp, _i64, _i64, _i64, _vp]),
     "tp_mlp_row_partial_wt": (_int, [_vp, _vp, _i64, _vp, _int, _i64, _i64, _i64, _vp]),
     "tp_mlp_shard_wt": (_int, [_vp, _vp, _vp, _vp, _int, _i64, _i64, _i64, _int, _int, _vp, _sz, _vp]),
     "tp_partial_sum": (_int, [ctypes.POINTER(_vp), _int, _int, _vp, _int, _i64, _vp]),
@@ -86,7 +89,7 @@ EXPORTED_SYMBOLS = tuple(_SIGNATURES)
 
 
 # The entry-point signatures below are those of this ABI version of include/tpmlp.h.
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 
 def _load_library():
@@ -181,6 +184,45 @@ def tp_mlp_col_gelu(X: torch.Tensor, A_i: torch.Tensor, Z_i: torch.Tensor | None
         raise ValueError("Z_i has the wrong shape")
     _check(lib.tp_mlp_col_gelu(X.data_ptr(), A_i.data_ptr(), A_i.stride(0), Z_i.data_ptr(),
                                M, d, F, _stream(stream)), "tp_mlp_col_gelu")
+    return Z_i
+
+
+def tp_mlp_col_gelu_bias(X: torch.Tensor, A_i: torch.Tensor, b_i: torch.Tensor,
+                         Z_i: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Z_i = bf16(GeLU(X·A_i + b_i)), the column-parallel linear with its bias.
+    X [M, d] bf16; A_i [d, F] bf16 (unit column stride, any row stride);
+    b_i [F] bf16, dense."""
+    return _col_gelu_bias(X, A_i, b_i, Z_i, False, stream)
+
+
+def tp_mlp_col_gelu_bias_wt(X: torch.Tensor, W1_i: torch.Tensor, b_i: torch.Tensor,
+                            Z_i: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """tp_mlp_col_gelu_bias with W1_i [F, d] bf16, the [out, in] layout (unit
+    column stride, any row stride)."""
+    return _col_gelu_bias(X, W1_i, b_i, Z_i, True, stream)
+
+
+def _col_gelu_bias(X, A_i, b_i, Z_i, transposed, stream):
+    _need(X, "X", torch.bfloat16, 2)
+    _need(A_i, "W1_i" if transposed else "A_i", torch.bfloat16, 2, contiguous=False)
+    if A_i.stride(1) != 1:
+        raise ValueError("the weight must have unit column stride")
+    M, d = X.shape
+    F, d2 = A_i.shape if transposed else A_i.shape[::-1]
+    if d2 != d:
+        raise ValueError(f"inner dimensions differ: X {tuple(X.shape)}, weight {tuple(A_i.shape)}")
+    _need(b_i, "b_i", torch.bfloat16, 1)
+    if b_i.numel() != F:
+        raise ValueError(f"b_i has {b_i.numel()} values, the shard is {F} wide")
+    if Z_i is None:
+        Z_i = torch.empty((M, F), dtype=torch.bfloat16, device=X.device)
+    _need(Z_i, "Z_i", torch.bfloat16, 2)
+    if tuple(Z_i.shape) != (M, F):
+        raise ValueError("Z_i has the wrong shape")
+    fn = lib.tp_mlp_col_gelu_bias_wt if transposed else lib.tp_mlp_col_gelu_bias
+    _check(fn(X.data_ptr(), A_i.data_ptr(), A_i.stride(0), b_i.data_ptr(), Z_i.data_ptr(),
+              M, d, F, _stream(stream)),
+           "tp_mlp_col_gelu_bias_wt" if transposed else "tp_mlp_col_gelu_bias")
     return Z_i
 
 

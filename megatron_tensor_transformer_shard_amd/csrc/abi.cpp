@@ -173,6 +173,41 @@ int tp_mlp_col_gelu_wt(const void* X, const void* W1_i, int64_t ldw, void* Z_i, 
       as_stream(stream)));
 }
 
+// ------------------------------------------------ column-layer bias --
+
+namespace {
+// The biased column step in either weight layout: W is A_i [d, F] (row
+// stride ldw >= F) or W1_i [F, d] (row stride ldw >= d).
+int col_gelu_bias(const void* X, const void* W, int64_t ldw, bool transposed, const void* b_i,
+                  void* Z_i, int64_t M, int64_t d, int64_t F, void* stream) {
+  int st = check_dims(M, d, F, 8);
+  if (st != TPM_OK) return st;
+  if (ldw < (transposed ? d : F) || ldw > kMaxLd) return TPM_ERR_SHAPE;
+  if (M == 0) return TPM_OK;
+  if (!X || !W || !b_i || !Z_i) return TPM_ERR_NULL;
+  if (!aligned16(X) || !aligned16(W) || !aligned16(b_i) || !aligned16(Z_i) || ldw % 8 != 0)
+    return TPM_ERR_ALIGN;
+  const Span z = mat_span(Z_i, M, F, F, 2);
+  const Span w = transposed ? mat_span(W, F, d, ldw, 2) : mat_span(W, d, F, ldw, 2);
+  if (overlap(z, mat_span(X, M, d, d, 2)) || overlap(z, w) || overlap(z, mat_span(b_i, 1, F, F, 2)))
+    return TPM_ERR_ALIAS;
+  return status_of(tpmlp::launch_gemm_bf16_bias(
+      static_cast<const uint16_t*>(X), d, static_cast<const uint16_t*>(W), ldw,
+      static_cast<const uint16_t*>(b_i), Z_i, F, (int)M, (int)F, (int)d,
+      transposed ? tpmlp::Layout::QT : tpmlp::Layout::NN, as_stream(stream)));
+}
+}  // namespace
+
+int tp_mlp_col_gelu_bias(const void* X, const void* A_i, int64_t lda, const void* b_i, void* Z_i,
+                         int64_t M, int64_t d, int64_t F, void* stream) {
+  return col_gelu_bias(X, A_i, lda, false, b_i, Z_i, M, d, F, stream);
+}
+
+int tp_mlp_col_gelu_bias_wt(const void* X, const void* W1_i, int64_t ldw, const void* b_i,
+                            void* Z_i, int64_t M, int64_t d, int64_t F, void* stream) {
+  return col_gelu_bias(X, W1_i, ldw, true, b_i, Z_i, M, d, F, stream);
+}
+
 int tp_mlp_row_partial_wt(const void* Z_i, const void* W2_i, int64_t ldw, void* Y_i,
                           int y_dtype, int64_t M, int64_t F, int64_t d, void* stream) {
   if (y_dtype != TPM_F32 && y_dtype != TPM_BF16) return TPM_ERR_DTYPE;

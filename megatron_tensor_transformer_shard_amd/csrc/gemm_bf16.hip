@@ -1,6 +1,7 @@
 // bf16 MFMA GEMMs of the tensor-parallel MLP shard on gfx950.
 //
 //   column-parallel step:  Z_i = bf16(GeLU(X·A_i))      (GeLU fused in the epilogue)
+//                          or bf16(GeLU(X·A_i + b1_i)) with the layer's bias
 //   row-parallel step:     Y_i = Z_i·B_i                 (fp32 or bf16 partial)
 //
 // ("Megatron-LM deep architecture", column/row-parallel section.) Both are
@@ -201,6 +202,7 @@ __device__ __forceinline__ void read_frag(const uint8_t* sp, int fa, int s, int 
 struct GemmArgs {
   const uint16_t* P; int64_t ldp; const uint16_t* Q; int64_t ldq; void* C; int64_t ldc;
   const float* aux; int64_t ldaux; void* C2; int M, N, K;
+  const uint16_t* bias;  // GeluBiasBf16: bf16 [N], added to every row before GeLU
 };
 
 // Workgroups [0, tiles0) compute problem g0, the rest problem g1 (a launch
@@ -438,6 +440,18 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs g0, GemmAr
     }
     return;
   }
+  // GeluBiasBf16: the bias of the lane's four columns in each 16-column
+  // group, loaded once per tile from a column clamped into [0, N - 4] (N is
+  // a multiple of 8 and ncol of 4, so the load is whole and 8-byte aligned;
+  // a clamped group is never stored).
+  // Kept as packed bf16 pairs and widened where used.
+  [[maybe_unused]] u32x2 bias2[NT];
+  if constexpr (OUT == (int)OutKind::GeluBiasBf16) {
+    const int col_max = N - 4 - ncol;
+#pragma unroll
+    for (int ni = 0; ni < NT; ++ni)
+      bias2[ni] = *reinterpret_cast<const u32x2*>(g.bias + ncol + min(16 * ni, col_max));
+  }
 #pragma unroll
   for (int ni = 0; ni < NT; ++ni) {
 #pragma unroll
@@ -454,6 +468,13 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs g0, GemmAr
       } else if constexpr (OUT == (int)OutKind::GeluBf16) {
         const u32x2 g = {pack_bf16x2(gelu_exact(v[0]), gelu_exact(v[1])),
                          pack_bf16x2(gelu_exact(v[2]), gelu_exact(v[3]))};
+        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(C) + o) = g;
+      } else if constexpr (OUT == (int)OutKind::GeluBiasBf16) {
+        const u32x2 w = bias2[ni];
+        const f32x4 b = {__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xFFFF0000u),
+                         __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xFFFF0000u)};
+        const u32x2 g = {pack_bf16x2(gelu_exact(v[0] + b[0]), gelu_exact(v[1] + b[1])),
+                         pack_bf16x2(gelu_exact(v[2] + b[2]), gelu_exact(v[3] + b[3]))};
         *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(C) + o) = g;
       } else {
         const u32x2 g = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
@@ -480,9 +501,9 @@ hipError_t launch_one(const GemmArgs* a, int n, hipStream_t stream) {
 }
 
 // The (layout, epilogue) combinations the path uses: the forward's
-// K-major P / N-major Q with GeLU, fp32 or bf16 output; K-major Q with the
-// same three (the forward with weights stored transposed) or the
-// GeLU-gradient epilogue; M-major P with fp32 output.
+// K-major P / N-major Q with GeLU (with or without a bias), fp32 or bf16
+// output; K-major Q with the same four (the forward with weights stored
+// transposed) or the GeLU-gradient epilogue; M-major P with fp32 output.
 template <int BM, int BN, bool KTAIL>
 hipError_t launch_cfg(const GemmArgs* a, int n, OutKind out, Layout lay, hipStream_t stream) {
   if (lay == Layout::NN) {
@@ -490,6 +511,7 @@ hipError_t launch_cfg(const GemmArgs* a, int n, OutKind out, Layout lay, hipStre
       case OutKind::GeluBf16: return launch_one<BM, BN, (int)OutKind::GeluBf16, KTAIL, false, false>(a, n, stream);
       case OutKind::F32: return launch_one<BM, BN, (int)OutKind::F32, KTAIL, false, false>(a, n, stream);
       case OutKind::Bf16: return launch_one<BM, BN, (int)OutKind::Bf16, KTAIL, false, false>(a, n, stream);
+      case OutKind::GeluBiasBf16: return launch_one<BM, BN, (int)OutKind::GeluBiasBf16, KTAIL, false, false>(a, n, stream);
       default: return hipErrorInvalidValue;
     }
   }
@@ -499,6 +521,7 @@ hipError_t launch_cfg(const GemmArgs* a, int n, OutKind out, Layout lay, hipStre
       case OutKind::F32: return launch_one<BM, BN, (int)OutKind::F32, KTAIL, false, true>(a, n, stream);
       case OutKind::GeluBf16: return launch_one<BM, BN, (int)OutKind::GeluBf16, KTAIL, false, true>(a, n, stream);
       case OutKind::Bf16: return launch_one<BM, BN, (int)OutKind::Bf16, KTAIL, false, true>(a, n, stream);
+      case OutKind::GeluBiasBf16: return launch_one<BM, BN, (int)OutKind::GeluBiasBf16, KTAIL, false, true>(a, n, stream);
       default: return hipErrorInvalidValue;
     }
   }
@@ -553,6 +576,16 @@ hipError_t launch_gemm_bf16_ex(const uint16_t* P, int64_t ldp, const uint16_t* Q
   if (M == 0 || N == 0) return hipSuccess;
   const GemmArgs a{P, ldp, Q, ldq, C, ldc, aux, ldaux, C2, M, N, K};
   return launch_group(&a, 1, out, lay, stream);
+}
+
+hipError_t launch_gemm_bf16_bias(const uint16_t* P, int64_t ldp, const uint16_t* Q, int64_t ldq,
+                                 const uint16_t* bias, void* C, int64_t ldc, int M, int N, int K,
+                                 Layout lay, hipStream_t stream) {
+  if (M == 0 || N == 0) return hipSuccess;
+  if (lay != Layout::NN && lay != Layout::QT) return hipErrorInvalidValue;
+  GemmArgs a{P, ldp, Q, ldq, C, ldc, nullptr, 0, nullptr, M, N, K};
+  a.bias = bias;
+  return launch_group(&a, 1, OutKind::GeluBiasBf16, lay, stream);
 }
 
 hipError_t launch_gemm_bf16_pair(const BfGemm& x, const BfGemm& y, OutKind out, Layout lay,

@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert tpm.abi_version() == tpm.ABI_VERSION == 2
+    assert tpm.abi_version() == tpm.ABI_VERSION == 3
     for code in (OK, ENULL, EARG, ESHAPE, EDTYPE, EALIGN, EWS, EALIAS, EHIP):
         s = tpm.status_string(code)
         assert s.startswith("TPM_")
@@ -122,6 +122,27 @@ def test_col_gelu_wt_validation():
     assert col_gelu_wt(W=BASE + GB + 8) == EALIGN
     assert col_gelu_wt(Z=BASE + GB + 4096) == EALIAS  # Z overlaps W1_i [F, d]
     assert col_gelu_wt(Z=BASE + 64) == EALIAS         # Z overlaps X
+
+
+def col_gelu_bias(X=BASE, W=BASE + GB, ld=128, b=BASE + 2 * GB, Z=BASE + 3 * GB, M=32, d=64,
+                  F=128, wt=False):
+    fn = L.tp_mlp_col_gelu_bias_wt if wt else L.tp_mlp_col_gelu_bias
+    return fn(X, W, ld, b, Z, M, d, F, None)
+
+
+def test_col_gelu_bias_validation():
+    for wt in (False, True):
+        assert col_gelu_bias(M=0, wt=wt) == OK
+        assert col_gelu_bias(b=None, wt=wt) == ENULL
+        assert col_gelu_bias(W=None, wt=wt) == ENULL
+        assert col_gelu_bias(F=12, wt=wt) == ESHAPE
+        assert col_gelu_bias(b=BASE + 2 * GB + 8, wt=wt) == EALIGN
+        assert col_gelu_bias(Z=BASE + 2 * GB + 128, wt=wt) == EALIAS   # Z overlaps b_i
+        assert col_gelu_bias(Z=BASE + 64, wt=wt) == EALIAS             # Z overlaps X
+        assert col_gelu_bias(ld=132, wt=wt) == EALIGN
+    assert col_gelu_bias(ld=120) == ESHAPE              # math layout: ld < F
+    assert col_gelu_bias(ld=56, wt=True) == ESHAPE      # [out, in] layout: ld < d
+    assert col_gelu_bias(ld=64, wt=True, M=0) == OK     # ld = d is valid (no launch at M = 0)
 
 
 def row_partial_wt(Z=BASE, W=BASE + GB, ldw=128, Y=BASE + 2 * GB, yd=F32, M=32, F=128, d=64):

@@ -1,0 +1,149 @@
+"""The column-parallel linear with its bias, Z_i = bf16(GeLU(X·A_i + b1_i)),
+on the GPU against the oracle, in both weight layouts; and the whole block
+with both biases (the second added once, after the sum)."""
+import numpy as np
+import pytest
+
+import oracle
+from helpers import bf16_ulp, dev_bf16, host_bf16_bits, host_f64, log, max_err_ratio
+from workloads import WORKLOADS, make_bias, make_inputs, make_random, sample_rows
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-2
+U = 2.0 ** -24
+GELU_APPROX_REL = 3e-7   # fp32 GeLU with |Δerf| <= 1.5e-7
+
+
+@pytest.fixture(scope="module")
+def tpm():
+    import torch
+    import megatron_tensor_transformer_shard_amd as m
+    assert torch.cuda.is_available()
+    return m
+
+
+def _sync():
+    import torch
+    torch.cuda.synchronize()
+
+
+def _check_z_bias(zg_bits, zr_bits, absdot, b, K, what, min_exact=0.95):
+    """Within one bf16 ulp plus the fp32 errors of S (K·2^-24·Σ|x·a|) and of
+    the add S + b (one rounding), carried through GeLU (|GeLU'| <= 1.13), plus
+    the GeLU approximation on |S + b|; at least `min_exact` bit-identical."""
+    zg, zr = oracle.bf16_decode(zg_bits), oracle.bf16_decode(zr_bits)
+    mag = absdot + np.abs(oracle.bf16_decode(b))[None, :]
+    tol = bf16_ulp(zr) + 1.13 * (K * U * absdot + U * mag) + GELU_APPROX_REL * mag
+    bad = np.abs(zg - zr) > tol
+    exact = float(np.mean(zg == zr))
+    log(f"{what}: Z bit-identical fraction {exact:.6f}")
+    assert not np.any(bad), f"{what}: {int(bad.sum())} Z elements beyond the bound"
+    assert exact >= min_exact, f"{what}: only {exact:.4f} bit-identical"
+
+
+CASES = [
+    # M, d, H, N
+    (300, 136, 544, 2),
+    (1, 64, 256, 1),
+    (333, 200, 2400, 3),
+    (513, 264, 1056, 4),
+    (257, 1032, 2112, 8),
+]
+
+
+@pytest.mark.parametrize("M,d,H,N", CASES)
+def test_col_gelu_bias_vs_oracle_both_layouts(tpm, M, d, H, N):
+    import torch
+    log(f"case column bias M={M} d={d} H={H} N={N}")
+    X, A, _ = make_random(M, d, H, seed=11 * M + N, sigma=0.05)
+    b1 = make_bias(H, seed=M + N, sigma=0.5)
+    Xd, Ad, bd = dev_bf16(X), dev_bf16(A), dev_bf16(b1)
+    W1 = Ad.t().contiguous()
+    F = H // N
+    for rank in range(N):
+        lo, hi = rank * F, (rank + 1) * F
+        Z = torch.full((M, F), float("nan"), dtype=torch.bfloat16, device="cuda")
+        tpm.tp_mlp_col_gelu_bias(Xd, Ad[:, lo:hi], bd[lo:hi], Z)
+        Zt = tpm.tp_mlp_col_gelu_bias_wt(Xd, W1[lo:hi], bd[lo:hi])
+        _sync()
+        ref = oracle.col_gelu_bias(X, A[:, lo:hi], b1[lo:hi])
+        absdot = np.abs(oracle.bf16_decode(X)) @ np.abs(oracle.bf16_decode(A[:, lo:hi]))
+        _check_z_bias(host_bf16_bits(Z), ref, absdot, b1[lo:hi], d, f"rank {rank}")
+        assert torch.equal(Z, Zt), f"rank {rank}: the two weight layouts differ"
+
+
+def test_zero_bias_gives_the_unbiased_bits(tpm):
+    import torch
+    M, d, H = 300, 136, 544
+    X, A, _ = make_random(M, d, H, seed=3, sigma=0.05)
+    Xd, Ad = dev_bf16(X), dev_bf16(A)
+    zero = torch.zeros(H, dtype=torch.bfloat16, device="cuda")
+    Z = tpm.tp_mlp_col_gelu_bias(Xd, Ad, zero)
+    Z0 = tpm.tp_mlp_col_gelu(Xd, Ad)
+    _sync()
+    assert torch.equal(Z, Z0)
+
+
+def test_zero_input_gives_the_gelu_of_the_bias(tpm):
+    """X = 0: every row is bf16(GeLU(b)); a large spread of b reaches GeLU's
+    tails (GeLU(b) -> b and -> -0). Below about s = -3 the fp32 GeLU's error
+    (absolute, at most 3e-7·|s|) exceeds a bf16 ulp of the tiny result, so
+    there only the bound holds, not the bits (about 12% of this draw)."""
+    import torch
+    M, d, F = 40, 64, 256
+    b = make_bias(F, seed=9, sigma=4.0)
+    _, A, _ = make_random(M, d, F, seed=9, sigma=0.05)
+    Z = tpm.tp_mlp_col_gelu_bias(torch.zeros((M, d), dtype=torch.bfloat16, device="cuda"),
+                                 dev_bf16(A), dev_bf16(b))
+    _sync()
+    ref = oracle.col_gelu_bias(np.zeros((M, d), np.uint16), A, b)
+    _check_z_bias(host_bf16_bits(Z), ref, np.zeros((M, F)), b, d, "X = 0", min_exact=0.8)
+    far = oracle.bf16_decode(b) < -3.0
+    assert far.any()   # the draw does reach the tail
+
+
+@pytest.mark.parametrize("M,d,H,N", [(300, 136, 544, 2), (333, 200, 2400, 3)])
+def test_block_with_both_biases(tpm, M, d, H, N):
+    """Σ_i bf16(GeLU(X·A_i + b1_i))·B_i + b2 against the unsharded block with
+    both biases; b2 is added once, by the sum."""
+    import torch
+    log(f"case block with both biases M={M} d={d} H={H} N={N}")
+    X, A, B = make_random(M, d, H, seed=5 * M + N, sigma=0.05)
+    b1, b2 = make_bias(H, seed=M, sigma=0.5), make_bias(d, seed=M + 1, sigma=0.5)
+    Xd, Ad, Bd, b1d, b2d = dev_bf16(X), dev_bf16(A), dev_bf16(B), dev_bf16(b1), dev_bf16(b2)
+    F = H // N
+    parts = []
+    for rank in range(N):
+        lo, hi = rank * F, (rank + 1) * F
+        Z = tpm.tp_mlp_col_gelu_bias(Xd, Ad[:, lo:hi], b1d[lo:hi])
+        parts.append(tpm.tp_mlp_row_partial(Z, Bd[lo:hi]))
+    Y = tpm.tp_partial_sum_rows(parts, 0, M, bias=b2d)
+    _sync()
+    r = max_err_ratio(host_f64(Y), oracle.mlp_unsharded_bias(X, A, b1, B, b2))
+    log(f"block with both biases: err ratio {r:.3e}")
+    assert r <= TOL
+
+
+def test_full_7b_tp8_column_bias_sampled_rows(tpm):
+    """The 7B-class TP=8 column step with a bias at full size (ranks 0 and 7,
+    both layouts): sampled rows of Z_i against the oracle on those rows."""
+    import torch
+    wl = WORKLOADS["7b_tp8"]
+    log(f"case {wl.name} column bias")
+    X, A, _ = make_inputs(wl)
+    b1 = make_bias(wl.H, seed=wl.seed, sigma=0.5)
+    Xd, Ad, bd = dev_bf16(X), dev_bf16(A), dev_bf16(b1)
+    W1 = Ad.t().contiguous()
+    rows = sample_rows(wl.M, 64)
+    F = wl.F
+    for rank in (0, wl.N - 1):
+        lo, hi = rank * F, (rank + 1) * F
+        Z = tpm.tp_mlp_col_gelu_bias(Xd, Ad[:, lo:hi], bd[lo:hi])
+        Zt = tpm.tp_mlp_col_gelu_bias_wt(Xd, W1[lo:hi], bd[lo:hi])
+        _sync()
+        assert torch.equal(Z, Zt), f"rank {rank}: the two weight layouts differ"
+        ref = oracle.col_gelu_bias(X[rows], A[:, lo:hi], b1[lo:hi])
+        absdot = np.abs(oracle.bf16_decode(X[rows])) @ np.abs(oracle.bf16_decode(A[:, lo:hi]))
+        _check_z_bias(host_bf16_bits(Z[torch.from_numpy(rows).cuda()]), ref, absdot, b1[lo:hi],
+                      wl.d, f"rank {rank}")
