@@ -319,7 +319,8 @@ def gelu_grad(s: np.ndarray) -> np.ndarray:
     return 0.5 * erfc(-s * _INV_SQRT2) + s * _INV_SQRT_2PI * np.exp(-0.5 * s * s)
 
 
-def mlp_shard_backward(X_bits, A_bits, B_bits, dY_bits, N: int, rank: int, rounding: bool = True):
+def mlp_shard_backward(X_bits, A_bits, B_bits, dY_bits, N: int, rank: int, rounding: bool = True,
+                       b1_bits=None):
     """Gradients of rank `rank`'s shard, given the block's output gradient dY.
 
     Returns a dict of float64 arrays (dS and Z as bf16 bits when `rounding`):
@@ -332,6 +333,12 @@ def mlp_shard_backward(X_bits, A_bits, B_bits, dY_bits, N: int, rank: int, round
       dB = Zᵀ·dY                       [F, d]  (the gradient of B_i, a row block of B's)
     With rounding=False, Z and dS stay in float64 (the exact chain rule of the
     unrounded forward, for checking the formulas against finite differences).
+
+    With b1_bits (bf16 [H], the column-parallel layer's bias, added before
+    GeLU as in the pages' code pattern) S = X·A_i + b1_i, and the dict also
+    holds the bias gradients: db1 = Σ_m dS[m, :] ([F], this rank's block of
+    b1's gradient) and db2 = Σ_m dY[m, :] ([d], the gradient of the row
+    layer's bias, added once after the sum, so the same on every rank).
     """
     H = A_bits.shape[1]
     lo, hi = shard_columns(H, N, rank)
@@ -340,6 +347,10 @@ def mlp_shard_backward(X_bits, A_bits, B_bits, dY_bits, N: int, rank: int, round
     B_i = bf16_decode(B_bits)[lo:hi, :]
     dY = bf16_decode(dY_bits)
     S = X @ A_i
+    if b1_bits is not None:
+        if np.shape(b1_bits) != (H,):
+            raise ValueError("b1 must have the hidden width")
+        S = S + bf16_decode(b1_bits)[lo:hi][None, :]
     G = gelu(S)
     dZ = dY @ B_i.T
     dS = dZ * gelu_grad(S)
@@ -349,8 +360,12 @@ def mlp_shard_backward(X_bits, A_bits, B_bits, dY_bits, N: int, rank: int, round
     else:
         Z_bits = dS_bits = None
         Z, dSv = G, dS
-    return {"S": S, "Z": Z, "Z_bits": Z_bits, "dZ": dZ, "dS": dSv, "dS_bits": dS_bits,
-            "dX": dSv @ A_i.T, "dA": X.T @ dSv, "dB": Z.T @ dY}
+    g = {"S": S, "Z": Z, "Z_bits": Z_bits, "dZ": dZ, "dS": dSv, "dS_bits": dS_bits,
+         "dX": dSv @ A_i.T, "dA": X.T @ dSv, "dB": Z.T @ dY}
+    if b1_bits is not None:
+        g["db1"] = dSv.sum(axis=0)
+        g["db2"] = dY.sum(axis=0)
+    return g
 
 
 # ----------------------------------------------------------------------------

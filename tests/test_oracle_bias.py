@@ -78,6 +78,54 @@ def test_bias_shape_is_checked():
         oracle.mlp_shard_bias(X, A, make_bias(31, 73), B, 2, 0)
 
 
+# ------------------------------------------------------------- backward --
+
+def _dy(M, d, seed):
+    return bf16_bits_from_f32(np.random.default_rng(seed).standard_normal((M, d)).astype(np.float32))
+
+
+def test_backward_with_a_zero_bias_is_the_unbiased_backward():
+    X, A, B = make_random(6, 16, 32, seed=80, sigma=0.3)
+    dY = _dy(6, 16, 81)
+    g0 = oracle.mlp_shard_backward(X, A, B, dY, 2, 1)
+    gb = oracle.mlp_shard_backward(X, A, B, dY, 2, 1, b1_bits=np.zeros(32, np.uint16))
+    for k in ("S", "Z_bits", "dS_bits", "dX", "dA", "dB"):
+        assert np.array_equal(g0[k], gb[k]), k
+    assert np.array_equal(gb["db1"], oracle.bf16_decode(gb["dS_bits"]).sum(axis=0))
+
+
+@pytest.mark.parametrize("N,rank", [(1, 0), (2, 1), (4, 2)])
+def test_backward_bias_gradients_match_finite_differences(N, rank):
+    """The unrounded chain rule against central finite differences of
+    L = Σ (Y ⊙ dY) with Y = GeLU(X·A_i + b1_i)·B_i + b2, with respect to every
+    entry of b1_i, b2, X and A_i."""
+    M, d, H = 3, 4, 16
+    X, A, B = make_random(M, d, H, 82 + N, sigma=0.5)
+    b1 = make_bias(H, 82 + N, sigma=0.7)
+    dY = _dy(M, d, 83)
+    g = oracle.mlp_shard_backward(X, A, B, dY, N, rank, rounding=False, b1_bits=b1)
+    lo, hi = oracle.shard_columns(H, N, rank)
+    Xv, Av, Bv, dYv = (oracle.bf16_decode(t) for t in (X, A[:, lo:hi], B[lo:hi, :], dY))
+    b1v, b2v = oracle.bf16_decode(b1)[lo:hi], np.linspace(-1, 1, d)
+
+    def loss(x, a, c1, c2):
+        return float(np.sum((oracle.gelu(x @ a + c1[None, :]) @ Bv + c2[None, :]) * dYv))
+    h = 1e-6
+    base = {"X": Xv, "A": Av, "b1": b1v, "b2": b2v}
+    grads = {"X": g["dX"], "A": g["dA"], "b1": g["db1"], "b2": g["db2"]}
+    for name, v in base.items():
+        num = np.zeros_like(v)
+        for idx in np.ndindex(v.shape):
+            p, m = dict(base), dict(base)
+            p[name], m[name] = v.copy(), v.copy()
+            p[name][idx] += h
+            m[name][idx] -= h
+            num[idx] = (loss(p["X"], p["A"], p["b1"], p["b2"])
+                        - loss(m["X"], m["A"], m["b1"], m["b2"])) / (2 * h)
+        assert grads[name].shape == v.shape
+        assert _rel_maxdiff(grads[name], num) <= 1e-6, name
+
+
 # plausible mistakes, each planted in the oracle, fail at least one pin above
 def _pins_fail():
     for fn in (test_zero_bias_is_the_unbiased_step, test_zero_input_gives_the_gelu_of_the_bias,
