@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define TPM_ABI_VERSION 3
+#define TPM_ABI_VERSION 4
 
 /* Element types. */
 typedef enum {
@@ -191,6 +191,44 @@ int tp_mlp_col_gelu_bias(const void* X, const void* A_i, int64_t lda, const void
  */
 int tp_mlp_col_gelu_bias_wt(const void* X, const void* W1_i, int64_t ldw, const void* b_i,
                             void* Z_i, int64_t M, int64_t d, int64_t F, void* stream);
+
+/*
+ * Backward of one rank's shard when the forward had the column layer's bias
+ * (tp_mlp_col_gelu_bias): as tp_mlp_shard_backward, with S = X·A_i + b1_i
+ * recomputed, and also
+ *   db1_i = Σ_m dS[m, :]   (the gradient of this rank's block of b1)
+ * ("Megatron-LM deep architecture", code pattern: the column layer's bias
+ * is added to every token's output, so its gradient sums the gradient at
+ * that output over the tokens; dS is the gradient at GeLU's input, summed
+ * as the bf16 values the other gradients use, in fp32).
+ * b1 : device, bf16 [H], the whole first bias (the rank's block is taken at
+ *   rank·F). db1_i : device, fp32 [F], written. The second layer's bias
+ *   gradient, the same on every rank, is tp_bias_grad_bf16 of dY.
+ * workspace : tp_mlp_shard_backward_bias_workspace_size bytes. M = 0 writes
+ * db1_i = 0 and nothing else. Errors as tp_mlp_shard_backward, and
+ * TPM_ERR_NULL when b1 or db1_i is NULL.
+ */
+size_t tp_mlp_shard_backward_bias_workspace_size(int64_t M, int64_t d, int64_t H, int N);
+int tp_mlp_shard_backward_bias(const void* X, const void* A, const void* b1, const void* B,
+                               const void* dY, float* dX_i, float* dA_i, float* dB_i,
+                               float* db1_i, int64_t M, int64_t d, int64_t H, int N, int rank,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Gradient of a bias added to every row of a layer's output:
+ *   db[c] = Σ_r G[r, c], summed in fp32 (two passes, no atomics: the result
+ *   does not depend on timing).
+ * G : device, bf16 [rows, cols], row stride ld >= cols (a multiple of 8);
+ *   cols a multiple of 8. db : device, fp32 [cols], written (0 when rows is
+ *   0). workspace : tp_bias_grad_workspace_size(rows, cols) bytes of
+ *   scratch (none needed when rows is 0); must not overlap G or db.
+ * Used for the row layer's bias with G = dY. Errors: TPM_ERR_SHAPE,
+ * TPM_ERR_NULL, TPM_ERR_WORKSPACE, TPM_ERR_ALIGN (16-byte pointers),
+ * TPM_ERR_ALIAS.
+ */
+size_t tp_bias_grad_workspace_size(int64_t rows, int64_t cols);
+int tp_bias_grad_bf16(const void* G, int64_t ld, int64_t rows, int64_t cols, float* db,
+                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Sum of the partial outputs, the arithmetic of the AllReduce(sum) that ends

@@ -29,6 +29,8 @@ __all__ = [
     "tp_amax_history_push", "tp_mlp_col_gelu_e4m3_delayed", "tp_mlp_shard_e4m3_delayed",
     "tp_mlp_shard_e4m3_delayed_workspace_size", "AmaxHistory",
     "tp_mlp_shard_backward", "tp_mlp_shard_backward_workspace_size", "backward_workspace_views",
+    "tp_mlp_shard_backward_bias", "tp_mlp_shard_backward_bias_workspace_size",
+    "tp_bias_grad_bf16", "tp_bias_grad_workspace_size",
     "tp_mlp_shard_backward_fp8", "tp_mlp_shard_backward_fp8_workspace_size",
     "tp_attn_qkv", "tp_attn_heads", "tp_attn_shard", "tp_attn_shard_workspace_size",
     "attn_workspace_views", "ATTN_HEAD_DIM", "fp8_backward_workspace_views",
@@ -76,6 +78,11 @@ _SIGNATURES = {
     "tp_mlp_shard_backward_workspace_size": (_sz, [_i64, _i64, _i64, _int]),
     "tp_mlp_shard_backward": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _int,
                                      _int, _vp, _sz, _vp]),
+    "tp_mlp_shard_backward_bias_workspace_size": (_sz, [_i64, _i64, _i64, _int]),
+    "tp_mlp_shard_backward_bias": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64,
+                                          _i64, _int, _int, _vp, _sz, _vp]),
+    "tp_bias_grad_workspace_size": (_sz, [_i64, _i64]),
+    "tp_bias_grad_bf16": (_int, [_vp, _i64, _i64, _i64, _vp, _vp, _sz, _vp]),
     "tp_attn_qkv": (_int, [_vp, _vp, _i64, _vp, _i64, _i64, _i64, _vp]),
     "tp_attn_heads": (_int, [_vp, _i64, _vp, _i64, _i64, _i64, _i64, _int, _vp]),
     "tp_attn_shard_workspace_size": (_sz, [_i64, _i64, _int]),
@@ -89,7 +96,7 @@ EXPORTED_SYMBOLS = tuple(_SIGNATURES)
 
 
 # The entry-point signatures below are those of this ABI version of include/tpmlp.h.
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 
 def _load_library():
@@ -592,7 +599,7 @@ def tp_mlp_shard_backward_workspace_size(M: int, d: int, H: int, N: int) -> int:
 
 
 def tp_mlp_shard_backward(X, A, B, dY, N: int, rank: int, dX_i=None, dA_i=None, dB_i=None,
-                          workspace=None, stream=None):
+                          workspace=None, stream=None, b1=None, db1_i=None):
     """Gradients of rank `rank`'s shard for the output gradient dY.
 
     Returns (dX_i, dA_i, dB_i, workspace): fp32 [M, d], [d, F], [F, d]; the
@@ -622,17 +629,80 @@ def tp_mlp_shard_backward(X, A, B, dY, N: int, rank: int, dX_i=None, dA_i=None, 
         _need(t, name, torch.float32, 2)
         if tuple(t.shape) != shp:
             raise ValueError(f"{name} has the wrong shape")
-    need = tp_mlp_shard_backward_workspace_size(M, d, H, N)
+    if b1 is not None:
+        _need(b1, "b1", torch.bfloat16, 1)
+        if b1.numel() != H:
+            raise ValueError(f"b1 has {b1.numel()} values, the hidden width is {H}")
+        if db1_i is None:
+            db1_i = torch.empty(F, dtype=torch.float32, device=dev)
+        _need(db1_i, "db1_i", torch.float32, 1)
+        if db1_i.numel() != F:
+            raise ValueError("db1_i has the wrong shape")
+        need = tp_mlp_shard_backward_bias_workspace_size(M, d, H, N)
+    else:
+        need = tp_mlp_shard_backward_workspace_size(M, d, H, N)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     _need(workspace, "workspace", None)
-    _check(lib.tp_mlp_shard_backward(X.data_ptr(), A.data_ptr(), B.data_ptr(), dY.data_ptr(),
-                                     dX_i.data_ptr(), dA_i.data_ptr(), dB_i.data_ptr(), M, d, H,
-                                     N, rank, workspace.data_ptr(),
-                                     workspace.numel() * workspace.element_size(),
-                                     _stream(stream)),
-           "tp_mlp_shard_backward")
-    return dX_i, dA_i, dB_i, workspace
+    wsb = workspace.numel() * workspace.element_size()
+    if b1 is None:
+        _check(lib.tp_mlp_shard_backward(X.data_ptr(), A.data_ptr(), B.data_ptr(), dY.data_ptr(),
+                                         dX_i.data_ptr(), dA_i.data_ptr(), dB_i.data_ptr(), M, d,
+                                         H, N, rank, workspace.data_ptr(), wsb, _stream(stream)),
+               "tp_mlp_shard_backward")
+        return dX_i, dA_i, dB_i, workspace
+    _check(lib.tp_mlp_shard_backward_bias(X.data_ptr(), A.data_ptr(), b1.data_ptr(), B.data_ptr(),
+                                          dY.data_ptr(), dX_i.data_ptr(), dA_i.data_ptr(),
+                                          dB_i.data_ptr(), db1_i.data_ptr(), M, d, H, N, rank,
+                                          workspace.data_ptr(), wsb, _stream(stream)),
+           "tp_mlp_shard_backward_bias")
+    return dX_i, dA_i, dB_i, db1_i, workspace
+
+
+def tp_mlp_shard_backward_bias_workspace_size(M: int, d: int, H: int, N: int) -> int:
+    return int(lib.tp_mlp_shard_backward_bias_workspace_size(M, d, H, N))
+
+
+def tp_mlp_shard_backward_bias(X, A, b1, B, dY, N: int, rank: int, dX_i=None, dA_i=None,
+                               dB_i=None, db1_i=None, workspace=None, stream=None):
+    """tp_mlp_shard_backward when the forward added the column layer's bias
+    b1 [H] (bf16) before GeLU: S is recomputed with the rank's block of b1,
+    and db1_i = Σ_m dS[m, :] (fp32 [F]) is returned as well.
+
+    Returns (dX_i, dA_i, dB_i, db1_i, workspace); the workspace's first three
+    parts are those `backward_workspace_views` gives.
+    """
+    if b1 is None:
+        raise ValueError("b1 is required")
+    return tp_mlp_shard_backward(X, A, B, dY, N, rank, dX_i, dA_i, dB_i, workspace, stream,
+                                 b1=b1, db1_i=db1_i)
+
+
+def tp_bias_grad_workspace_size(rows: int, cols: int) -> int:
+    return int(lib.tp_bias_grad_workspace_size(rows, cols))
+
+
+def tp_bias_grad_bf16(G, db=None, workspace=None, stream=None):
+    """db = Σ_r G[r, :] in fp32: the gradient of a bias added to every row of a
+    layer's output whose gradient is G (bf16 [rows, cols], unit column
+    stride, any row stride). For the row layer's bias, G = dY."""
+    _need(G, "G", torch.bfloat16, 2, contiguous=False)
+    if G.stride(1) != 1:
+        raise ValueError("G must have unit column stride")
+    rows, cols = G.shape
+    if db is None:
+        db = torch.empty(cols, dtype=torch.float32, device=G.device)
+    _need(db, "db", torch.float32, 1)
+    if db.numel() != cols:
+        raise ValueError("db has the wrong shape")
+    need = tp_bias_grad_workspace_size(rows, cols)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=G.device)
+    _need(workspace, "workspace", None)
+    _check(lib.tp_bias_grad_bf16(G.data_ptr(), G.stride(0), rows, cols, db.data_ptr(),
+                                 workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                 _stream(stream)), "tp_bias_grad_bf16")
+    return db
 
 
 def backward_workspace_views(workspace, M: int, F: int):

@@ -21,7 +21,8 @@ BUILD_DIR = os.path.join(PKG_DIR, "_build")
 LIB_NAME = "libtpmlp.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
-SOURCES = ["gemm_bf16.hip", "gemm_e4m3.hip", "partial_sum.hip", "attention.hip", "abi.cpp"]
+SOURCES = ["gemm_bf16.hip", "gemm_e4m3.hip", "partial_sum.hip", "attention.hip", "bias_grad.hip",
+           "abi.cpp"]
 ARCH = "gfx950"
 
 # Packed-fp32 VALU instructions are disabled for the device code; hipcc's host

@@ -193,7 +193,7 @@ int col_gelu_bias(const void* X, const void* W, int64_t ldw, bool transposed, co
     return TPM_ERR_ALIAS;
   return status_of(tpmlp::launch_gemm_bf16_bias(
       static_cast<const uint16_t*>(X), d, static_cast<const uint16_t*>(W), ldw,
-      static_cast<const uint16_t*>(b_i), Z_i, F, (int)M, (int)F, (int)d,
+      static_cast<const uint16_t*>(b_i), Z_i, F, (int)M, (int)F, (int)d, OutKind::GeluBiasBf16,
       transposed ? tpmlp::Layout::QT : tpmlp::Layout::NN, as_stream(stream)));
 }
 }  // namespace
@@ -553,10 +553,14 @@ size_t tp_mlp_shard_backward_workspace_size(int64_t M, int64_t d, int64_t H, int
   return round256(mf * 4) + 2 * round256(mf * 2);
 }
 
-int tp_mlp_shard_backward(const void* X, const void* A, const void* B, const void* dY,
-                          float* dX_i, float* dA_i, float* dB_i, int64_t M, int64_t d, int64_t H,
-                          int N, int rank, void* workspace, size_t workspace_bytes,
-                          void* stream) {
+namespace {
+// The bf16 backward of one rank's shard; with b1 (the column layer's whole
+// bias [H]) S is recomputed with the rank's block b1_i and db1_i = Σ_m dS is
+// written (bias-gradient scratch after the three workspace parts).
+int shard_backward_bf16(const void* X, const void* A, const void* B, const void* dY,
+                        const void* b1, float* dX_i, float* dA_i, float* dB_i, float* db1_i,
+                        int64_t M, int64_t d, int64_t H, int N, int rank, void* workspace,
+                        size_t workspace_bytes, void* stream) {
   if (N < 1 || rank < 0 || rank >= N) return TPM_ERR_ARG;
   if (H <= 0 || H % N != 0) return TPM_ERR_SHAPE;
   const int64_t F = H / N;
@@ -565,25 +569,37 @@ int tp_mlp_shard_backward(const void* X, const void* A, const void* B, const voi
   // M is the contraction length of the weight gradients.
   if (M % 8 != 0 || M > kMaxLd) return TPM_ERR_SHAPE;
   if (H > kMaxLd || H * d > (int64_t(1) << 46)) return TPM_ERR_SHAPE;
-  if (M == 0) return TPM_OK;
+  const bool bias = b1 != nullptr || db1_i != nullptr;
+  if (bias && (!b1 || !db1_i)) return TPM_ERR_NULL;
+  if (M == 0) {  // no tokens: nothing to do, and a zero bias gradient
+    if (!bias) return TPM_OK;
+    if (!aligned16(db1_i)) return TPM_ERR_ALIGN;
+    if (overlap(mat_span(db1_i, 1, F, F, 4), mat_span(b1, 1, H, H, 2))) return TPM_ERR_ALIAS;
+    // the column sum of zero rows writes 0 to every column and reads no scratch
+    return status_of(tpmlp::launch_colsum_bf16(nullptr, F, 0, (int)F, db1_i, nullptr,
+                                               as_stream(stream)));
+  }
   if (!X || !A || !B || !dY || !dX_i || !dA_i || !dB_i) return TPM_ERR_NULL;
-  const size_t need = tp_mlp_shard_backward_workspace_size(M, d, H, N);
+  const size_t need = bias ? tp_mlp_shard_backward_bias_workspace_size(M, d, H, N)
+                           : tp_mlp_shard_backward_workspace_size(M, d, H, N);
   if (!workspace || workspace_bytes < need) return TPM_ERR_WORKSPACE;
   if (!aligned16(X) || !aligned16(A) || !aligned16(B) || !aligned16(dY) || !aligned16(dX_i) ||
-      !aligned16(dA_i) || !aligned16(dB_i) || !aligned16(workspace))
+      !aligned16(dA_i) || !aligned16(dB_i) || !aligned16(workspace) ||
+      (bias && (!aligned16(b1) || !aligned16(db1_i))))
     return TPM_ERR_ALIGN;
-  const Span ins[4] = {mat_span(X, M, d, d, 2), mat_span(A, d, H, H, 2), mat_span(B, H, d, d, 2),
-                       mat_span(dY, M, d, d, 2)};
-  const Span outs[4] = {mat_span(dX_i, M, d, d, 4), mat_span(dA_i, d, F, F, 4),
-                        mat_span(dB_i, F, d, d, 4),
+  const Span ins[5] = {mat_span(X, M, d, d, 2), mat_span(A, d, H, H, 2), mat_span(B, H, d, d, 2),
+                       mat_span(dY, M, d, d, 2), mat_span(b1, bias ? 1 : 0, H, H, 2)};
+  const Span outs[5] = {mat_span(dX_i, M, d, d, 4), mat_span(dA_i, d, F, F, 4),
+                        mat_span(dB_i, F, d, d, 4), mat_span(db1_i, bias ? 1 : 0, F, F, 4),
                         {reinterpret_cast<uintptr_t>(workspace),
                          reinterpret_cast<uintptr_t>(workspace) + need}};
-  for (int o = 0; o < 4; ++o) {
-    for (int i = 0; i < 4; ++i)
+  for (int o = 0; o < 5; ++o) {
+    for (int i = 0; i < 5; ++i)
       if (overlap(outs[o], ins[i])) return TPM_ERR_ALIAS;
-    for (int p = o + 1; p < 4; ++p)
+    for (int p = o + 1; p < 5; ++p)
       if (overlap(outs[o], outs[p])) return TPM_ERR_ALIAS;
   }
+  hipStream_t s = as_stream(stream);
 
   // Shard views as in the forward; A_i is [d, F] with row stride H, B_i [F, d] dense.
   const uint16_t* x = static_cast<const uint16_t*>(X);
@@ -595,16 +611,23 @@ int tp_mlp_shard_backward(const void* X, const void* A, const void* B, const voi
   float* S = reinterpret_cast<float*>(ws);
   uint16_t* dS = reinterpret_cast<uint16_t*>(ws + round256(mf * 4));
   uint16_t* Z = reinterpret_cast<uint16_t*>(ws + round256(mf * 4) + round256(mf * 2));
-  hipStream_t s = as_stream(stream);
   using tpmlp::Layout;
   const int m = (int)M, dd = (int)d, f = (int)F;
-  // S = X·A_i (the forward's pre-activation, recomputed)
-  hipError_t e = tpmlp::launch_gemm_bf16_ex(x, d, A_i, H, S, F, m, f, dd, OutKind::F32,
-                                            Layout::NN, nullptr, 0, nullptr, s);
+  // S = X·A_i (+ b1_i), the forward's pre-activation, recomputed
+  hipError_t e =
+      bias ? tpmlp::launch_gemm_bf16_bias(x, d, A_i, H, static_cast<const uint16_t*>(b1) + rank * F,
+                                          S, F, m, f, dd, OutKind::F32Bias, Layout::NN, s)
+           : tpmlp::launch_gemm_bf16_ex(x, d, A_i, H, S, F, m, f, dd, OutKind::F32, Layout::NN,
+                                        nullptr, 0, nullptr, s);
   // dS = bf16((dY·B_iᵀ) ⊙ GeLU'(S)), Z = bf16(GeLU(S)); B_iᵀ is B_i read K-contiguous
   if (e == hipSuccess)
     e = tpmlp::launch_gemm_bf16_ex(dy, d, B_i, d, dS, F, m, f, dd, OutKind::GeluGradBf16,
                                    Layout::QT, S, F, Z, s);
+  // db1_i = Σ_m dS[m, :], the bias gradient, from the stored bf16 dS
+  if (e == hipSuccess && bias)
+    e = tpmlp::launch_colsum_bf16(dS, F, m, f, db1_i,
+                                  reinterpret_cast<float*>(ws + round256(mf * 4) + 2 * round256(mf * 2)),
+                                  s);
   // dX_i = dS·A_iᵀ
   if (e == hipSuccess)
     e = tpmlp::launch_gemm_bf16_ex(dS, F, A_i, H, dX_i, d, m, dd, f, OutKind::F32, Layout::QT,
@@ -615,6 +638,57 @@ int tp_mlp_shard_backward(const void* X, const void* A, const void* B, const voi
     e = tpmlp::launch_gemm_bf16_pair({Z, F, dy, d, dB_i, d, f, dd, m},
                                      {x, d, dS, F, dA_i, F, dd, f, m}, OutKind::F32, Layout::PT, s);
   return status_of(e);
+}
+}  // namespace
+
+size_t tp_mlp_shard_backward_bias_workspace_size(int64_t M, int64_t d, int64_t H, int N) {
+  const size_t base = tp_mlp_shard_backward_workspace_size(M, d, H, N);
+  if (base == 0) return 0;
+  return base + round256((size_t)tpmlp::colsum_row_blocks(M) * (size_t)(H / N) * 4);
+}
+
+int tp_mlp_shard_backward(const void* X, const void* A, const void* B, const void* dY,
+                          float* dX_i, float* dA_i, float* dB_i, int64_t M, int64_t d, int64_t H,
+                          int N, int rank, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  return shard_backward_bf16(X, A, B, dY, nullptr, dX_i, dA_i, dB_i, nullptr, M, d, H, N, rank,
+                             workspace, workspace_bytes, stream);
+}
+
+int tp_mlp_shard_backward_bias(const void* X, const void* A, const void* b1, const void* B,
+                               const void* dY, float* dX_i, float* dA_i, float* dB_i,
+                               float* db1_i, int64_t M, int64_t d, int64_t H, int N, int rank,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  return shard_backward_bf16(X, A, B, dY, b1, dX_i, dA_i, dB_i, db1_i, M, d, H, N, rank,
+                             workspace, workspace_bytes, stream);
+}
+
+size_t tp_bias_grad_workspace_size(int64_t rows, int64_t cols) {
+  if (rows < 0 || cols <= 0 || rows > kMaxDim || cols > kMaxLd) return 0;
+  return round256((size_t)tpmlp::colsum_row_blocks(rows) * (size_t)cols * 4);
+}
+
+int tp_bias_grad_bf16(const void* G, int64_t ld, int64_t rows, int64_t cols, float* db,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  if (rows < 0 || cols <= 0 || cols % 8 != 0 || cols > kMaxLd || rows > kMaxDim) return TPM_ERR_SHAPE;
+  if (ld < cols || ld > kMaxLd) return TPM_ERR_SHAPE;
+  // the partial pass has one 128-row block per grid row
+  if (tpmlp::colsum_row_blocks(rows) > 65535) return TPM_ERR_SHAPE;
+  if (!db || (rows > 0 && !G)) return TPM_ERR_NULL;
+  const size_t need = tp_bias_grad_workspace_size(rows, cols);
+  if (rows > 0 && (!workspace || workspace_bytes < need)) return TPM_ERR_WORKSPACE;
+  if ((rows > 0 && (!aligned16(G) || !aligned16(workspace))) || !aligned16(db) || ld % 8 != 0)
+    return TPM_ERR_ALIGN;
+  const Span out = mat_span(db, 1, cols, cols, 4);
+  if (rows > 0) {
+    const Span ws{reinterpret_cast<uintptr_t>(workspace), reinterpret_cast<uintptr_t>(workspace) + need};
+    if (overlap(out, mat_span(G, rows, cols, ld, 2)) || overlap(out, ws) ||
+        overlap(ws, mat_span(G, rows, cols, ld, 2)))
+      return TPM_ERR_ALIAS;
+  }
+  return status_of(tpmlp::launch_colsum_bf16(static_cast<const uint16_t*>(G), ld, (int)rows,
+                                             (int)cols, db, static_cast<float*>(workspace),
+                                             as_stream(stream)));
 }
 
 namespace {

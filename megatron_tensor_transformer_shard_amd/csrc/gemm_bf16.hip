@@ -446,7 +446,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs g0, GemmAr
   // a clamped group is never stored).
   // Kept as packed bf16 pairs and widened where used.
   [[maybe_unused]] u32x2 bias2[NT];
-  if constexpr (OUT == (int)OutKind::GeluBiasBf16) {
+  if constexpr (OUT == (int)OutKind::GeluBiasBf16 || OUT == (int)OutKind::F32Bias) {
     const int col_max = N - 4 - ncol;
 #pragma unroll
     for (int ni = 0; ni < NT; ++ni)
@@ -465,6 +465,11 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs g0, GemmAr
       asm volatile("" : "+v"(v));
       if constexpr (OUT == (int)OutKind::F32) {
         *reinterpret_cast<f32x4*>(static_cast<float*>(C) + o) = v;
+      } else if constexpr (OUT == (int)OutKind::F32Bias) {
+        const u32x2 w = bias2[ni];
+        const f32x4 b = {__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xFFFF0000u),
+                         __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xFFFF0000u)};
+        *reinterpret_cast<f32x4*>(static_cast<float*>(C) + o) = v + b;
       } else if constexpr (OUT == (int)OutKind::GeluBf16) {
         const u32x2 g = {pack_bf16x2(gelu_exact(v[0]), gelu_exact(v[1])),
                          pack_bf16x2(gelu_exact(v[2]), gelu_exact(v[3]))};
@@ -501,8 +506,8 @@ hipError_t launch_one(const GemmArgs* a, int n, hipStream_t stream) {
 }
 
 // The (layout, epilogue) combinations the path uses: the forward's
-// K-major P / N-major Q with GeLU (with or without a bias), fp32 or bf16
-// output; K-major Q with the same four (the forward with weights stored
+// K-major P / N-major Q with GeLU (with or without a bias), fp32 (with or
+// without a bias: the backward's recomputed S) or bf16 output; K-major Q with the same four (the forward with weights stored
 // transposed) or the GeLU-gradient epilogue; M-major P with fp32 output.
 template <int BM, int BN, bool KTAIL>
 hipError_t launch_cfg(const GemmArgs* a, int n, OutKind out, Layout lay, hipStream_t stream) {
@@ -512,6 +517,7 @@ hipError_t launch_cfg(const GemmArgs* a, int n, OutKind out, Layout lay, hipStre
       case OutKind::F32: return launch_one<BM, BN, (int)OutKind::F32, KTAIL, false, false>(a, n, stream);
       case OutKind::Bf16: return launch_one<BM, BN, (int)OutKind::Bf16, KTAIL, false, false>(a, n, stream);
       case OutKind::GeluBiasBf16: return launch_one<BM, BN, (int)OutKind::GeluBiasBf16, KTAIL, false, false>(a, n, stream);
+      case OutKind::F32Bias: return launch_one<BM, BN, (int)OutKind::F32Bias, KTAIL, false, false>(a, n, stream);
       default: return hipErrorInvalidValue;
     }
   }
@@ -580,12 +586,14 @@ hipError_t launch_gemm_bf16_ex(const uint16_t* P, int64_t ldp, const uint16_t* Q
 
 hipError_t launch_gemm_bf16_bias(const uint16_t* P, int64_t ldp, const uint16_t* Q, int64_t ldq,
                                  const uint16_t* bias, void* C, int64_t ldc, int M, int N, int K,
-                                 Layout lay, hipStream_t stream) {
+                                 OutKind out, Layout lay, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
-  if (lay != Layout::NN && lay != Layout::QT) return hipErrorInvalidValue;
+  const bool ok = (out == OutKind::GeluBiasBf16 && (lay == Layout::NN || lay == Layout::QT)) ||
+                  (out == OutKind::F32Bias && lay == Layout::NN);
+  if (!ok) return hipErrorInvalidValue;
   GemmArgs a{P, ldp, Q, ldq, C, ldc, nullptr, 0, nullptr, M, N, K};
   a.bias = bias;
-  return launch_group(&a, 1, OutKind::GeluBiasBf16, lay, stream);
+  return launch_group(&a, 1, out, lay, stream);
 }
 
 hipError_t launch_gemm_bf16_pair(const BfGemm& x, const BfGemm& y, OutKind out, Layout lay,

@@ -14,7 +14,8 @@ namespace tpmlp {
 // scale, one byte per element; GeluGradBf16 (backward, both engines):
 // C = bf16(acc·GeLU'(S)), C2 = bf16(GeLU(S)) with S read from an fp32 [M, N]
 // matrix. In the fp8 engine acc is first divided by sP·sQ.
-enum class OutKind : int { GeluBf16 = 0, F32 = 1, Bf16 = 2, GeluE4m3 = 3, GeluGradBf16 = 4, GeluBiasBf16 = 5 };
+enum class OutKind : int { GeluBf16 = 0, F32 = 1, Bf16 = 2, GeluE4m3 = 3, GeluGradBf16 = 4, GeluBiasBf16 = 5,
+                            F32Bias = 6 };
 
 // Operand layouts of the bf16 GEMM C = P·Q: NN = P [M, K] K-contiguous and
 // Q [K, N] N-contiguous (the forward); QT = Q stored [N, K] K-contiguous;
@@ -34,11 +35,18 @@ hipError_t launch_gemm_bf16_ex(const uint16_t* P, int64_t ldp, const uint16_t* Q
                                void* C, int64_t ldc, int M, int N, int K, OutKind out, Layout lay,
                                const float* aux, int64_t ldaux, void* C2, hipStream_t stream);
 
-// C = bf16(GeLU(P·Q + bias)) with bias bf16 [N] added to every row before
-// GeLU; layout NN or QT.
+// C = bf16(GeLU(P·Q + bias)) (out GeluBiasBf16, layout NN or QT) or the fp32
+// C = P·Q + bias (out F32Bias, layout NN), with bias bf16 [N] added to every row.
 hipError_t launch_gemm_bf16_bias(const uint16_t* P, int64_t ldp, const uint16_t* Q, int64_t ldq,
                                  const uint16_t* bias, void* C, int64_t ldc, int M, int N, int K,
-                                 Layout lay, hipStream_t stream);
+                                 OutKind out, Layout lay, hipStream_t stream);
+
+// out[c] = Σ_r G[r, c] in fp32 (bias gradient), G bf16 [rows, cols] with row
+// stride ld, cols a multiple of 8; partial holds colsum_row_blocks(rows)·cols
+// floats of scratch. Deterministic (no atomics).
+int64_t colsum_row_blocks(int64_t rows);
+hipError_t launch_colsum_bf16(const uint16_t* G, int64_t ld, int rows, int cols, float* out,
+                              float* partial, hipStream_t stream);
 
 // Two independent GEMMs of one layout and epilogue (fp32 or bf16 output) in
 // one launch, so that two problems of few tiles each fill the chip together.

@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert tpm.abi_version() == tpm.ABI_VERSION == 3
+    assert tpm.abi_version() == tpm.ABI_VERSION == 4
     for code in (OK, ENULL, EARG, ESHAPE, EDTYPE, EALIGN, EWS, EALIAS, EHIP):
         s = tpm.status_string(code)
         assert s.startswith("TPM_")
@@ -143,6 +143,51 @@ def test_col_gelu_bias_validation():
     assert col_gelu_bias(ld=120) == ESHAPE              # math layout: ld < F
     assert col_gelu_bias(ld=56, wt=True) == ESHAPE      # [out, in] layout: ld < d
     assert col_gelu_bias(ld=64, wt=True, M=0) == OK     # ld = d is valid (no launch at M = 0)
+
+
+def bwd_bias(X=BASE, A=BASE + GB, b1=BASE + 2 * GB, B=BASE + 3 * GB, dY=BASE + 4 * GB,
+             dX=BASE + 5 * GB, dA=BASE + 6 * GB, dB=BASE + 7 * GB, db1=BASE + 8 * GB, M=32, d=64,
+             H=256, N=2, rank=0, ws=BASE + 9 * GB, wsb=None):
+    if wsb is None:
+        wsb = L.tp_mlp_shard_backward_bias_workspace_size(M, d, H, N)
+    return L.tp_mlp_shard_backward_bias(X, A, b1, B, dY, dX, dA, dB, db1, M, d, H, N, rank, ws,
+                                        wsb, None)
+
+
+def test_backward_bias_validation():
+    plain = L.tp_mlp_shard_backward_workspace_size(32, 64, 256, 2)
+    assert L.tp_mlp_shard_backward_bias_workspace_size(32, 64, 256, 2) == plain + 512  # 1 block x 128 x 4
+    assert bwd_bias(b1=None) == ENULL
+    assert bwd_bias(db1=None) == ENULL
+    assert bwd_bias(b1=None, M=0) == ENULL
+    assert bwd_bias(db1=BASE + 8 * GB + 4) == EALIGN
+    assert bwd_bias(db1=BASE + 2 * GB + 64) == EALIAS     # db1_i overlaps b1
+    assert bwd_bias(db1=BASE + 9 * GB + 256) == EALIAS    # db1_i inside the workspace
+    assert bwd_bias(wsb=L.tp_mlp_shard_backward_workspace_size(32, 64, 256, 2)) == EWS
+    assert bwd_bias(rank=2) == EARG
+    assert bwd_bias(M=12) == ESHAPE
+
+
+def bias_grad(G=BASE, ld=64, rows=300, cols=64, db=BASE + GB, ws=BASE + 2 * GB, wsb=None):
+    if wsb is None:
+        wsb = L.tp_bias_grad_workspace_size(rows, cols)
+    return L.tp_bias_grad_bf16(G, ld, rows, cols, db, ws, wsb, None)
+
+
+def test_bias_grad_validation():
+    assert L.tp_bias_grad_workspace_size(300, 64) == 3 * 64 * 4     # 3 row blocks x 64 columns, fp32
+    assert L.tp_bias_grad_workspace_size(0, 64) == 0
+    assert L.tp_bias_grad_workspace_size(10, 0) == 0
+    assert bias_grad(cols=60, ld=64) == ESHAPE
+    assert bias_grad(ld=56) == ESHAPE
+    assert bias_grad(ld=72 + 4) == EALIGN
+    assert bias_grad(db=None) == ENULL
+    assert bias_grad(G=None) == ENULL
+    assert bias_grad(wsb=16) == EWS
+    assert bias_grad(G=BASE + 8) == EALIGN
+    assert bias_grad(db=BASE + 1024) == EALIAS            # db inside G
+    assert bias_grad(ws=BASE + 4096) == EALIAS            # workspace inside G
+    assert bias_grad(rows=128 * 65536) == ESHAPE          # more row blocks than the grid holds
 
 
 def row_partial_wt(Z=BASE, W=BASE + GB, ldw=128, Y=BASE + 2 * GB, yd=F32, M=32, F=128, d=64):

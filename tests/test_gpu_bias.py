@@ -147,3 +147,90 @@ def test_full_7b_tp8_column_bias_sampled_rows(tpm):
         absdot = np.abs(oracle.bf16_decode(X[rows])) @ np.abs(oracle.bf16_decode(A[:, lo:hi]))
         _check_z_bias(host_bf16_bits(Z[torch.from_numpy(rows).cuda()]), ref, absdot, b1[lo:hi],
                       wl.d, f"rank {rank}")
+
+
+# ------------------------------------------------------------- backward --
+
+def _dy(M, d, seed):
+    from workloads import make_output_grad
+    return make_output_grad(M, d, seed=seed, sigma=1.0)
+
+
+@pytest.mark.parametrize("M,d,H,N", [(264, 200, 2400, 3), (520, 136, 1088, 4), (8, 64, 256, 1)])
+def test_backward_with_bias_vs_oracle(tpm, M, d, H, N):
+    """S recomputed with b1_i within the fp32 bound; db1_i against an exact
+    sum of the GPU's own dS (the fp32 column-sum bound) and against the
+    oracle's; dX_i, dA_i, dB_i within 1e-2·max|ref|."""
+    import torch
+    log(f"case backward with bias M={M} d={d} H={H} N={N}")
+    X, A, B = make_random(M, d, H, seed=7 * M + N, sigma=0.05)
+    b1 = make_bias(H, seed=M + 3, sigma=0.5)
+    dY = _dy(M, d, M + 4)
+    Xd, Ad, Bd, dYd, b1d = dev_bf16(X), dev_bf16(A), dev_bf16(B), dev_bf16(dY), dev_bf16(b1)
+    F = H // N
+    for rank in sorted({0, N - 1}):
+        dX, dA, dB, db1, ws = tpm.tp_mlp_shard_backward_bias(Xd, Ad, b1d, Bd, dYd, N, rank)
+        _sync()
+        g = oracle.mlp_shard_backward(X, A, B, dY, N, rank, b1_bits=b1)
+        S, dS, _ = tpm.backward_workspace_views(ws, M, F)
+        lo, hi = rank * F, (rank + 1) * F
+        absdot = np.abs(oracle.bf16_decode(X)) @ np.abs(oracle.bf16_decode(A[:, lo:hi]))
+        Sg = host_f64(S)
+        bound = d * U * absdot + U * np.abs(g["S"]) + 1e-30
+        assert np.all(np.abs(Sg - g["S"]) <= bound * 1.01), f"rank {rank}: S with the bias"
+        dSg = host_f64(dS)
+        exact = dSg.sum(axis=0)
+        dbg = host_f64(db1)
+        assert np.all(np.abs(dbg - exact) <= M * U * np.abs(dSg).sum(axis=0) + 1e-30), \
+            f"rank {rank}: db1_i is not the column sum of dS"
+        for name, t, ref in (("db1", db1, g["db1"]), ("dX", dX, g["dX"]), ("dA", dA, g["dA"]),
+                             ("dB", dB, g["dB"])):
+            r = max_err_ratio(host_f64(t), ref)
+            log(f"rank {rank}: {name} err ratio {r:.3e}")
+            assert r <= TOL, f"rank {rank}: {name}"
+
+
+def test_backward_with_a_zero_bias_equals_the_unbiased_backward(tpm):
+    import torch
+    M, d, H, N = 264, 136, 544, 2
+    X, A, B = make_random(M, d, H, seed=90, sigma=0.05)
+    dY = _dy(M, d, 91)
+    Xd, Ad, Bd, dYd = dev_bf16(X), dev_bf16(A), dev_bf16(B), dev_bf16(dY)
+    zero = torch.zeros(H, dtype=torch.bfloat16, device="cuda")
+    got = tpm.tp_mlp_shard_backward_bias(Xd, Ad, zero, Bd, dYd, N, 1)
+    ref = tpm.tp_mlp_shard_backward(Xd, Ad, Bd, dYd, N, 1)
+    _sync()
+    for name, a, b in zip(("dX", "dA", "dB"), got[:3], ref[:3]):
+        assert torch.equal(a, b), f"{name} differs with a zero bias"
+
+
+@pytest.mark.parametrize("rows,cols,pad", [(0, 64, 0), (1, 8, 0), (127, 520, 8), (129, 4096, 0),
+                                           (1000, 2048, 24), (8192, 4096, 0)])
+def test_bias_grad_integer_values_exact(tpm, rows, cols, pad):
+    """Small integers sum exactly in fp32, so db equals the exact column sum
+    bit for bit: every element of G is counted once, none twice, whatever the
+    row blocks and the ragged last column block."""
+    import torch
+    log(f"case bias gradient rows={rows} cols={cols} pad={pad}")
+    rng = np.random.default_rng(rows + cols)
+    vals = rng.integers(-8, 9, size=(rows, cols)).astype(np.float32)
+    G = torch.zeros((rows, cols + pad), dtype=torch.bfloat16, device="cuda")
+    G[:, :cols] = torch.from_numpy(vals).to("cuda").to(torch.bfloat16)
+    if pad:
+        G[:, cols:] = float("nan")   # the padding is never read
+    db = tpm.tp_bias_grad_bf16(G[:, :cols])
+    _sync()
+    assert np.array_equal(host_f64(db), vals.astype(np.float64).sum(axis=0))
+
+
+def test_bias_grad_of_dy_vs_oracle(tpm):
+    """db2 = Σ_m dY[m, :] against the oracle's, within the fp32 summation bound."""
+    M, d, H = 520, 136, 544
+    X, A, B = make_random(M, d, H, seed=92, sigma=0.05)
+    dY = _dy(M, d, 93)
+    b1 = make_bias(H, seed=94)
+    db2 = tpm.tp_bias_grad_bf16(dev_bf16(dY))
+    _sync()
+    ref = oracle.mlp_shard_backward(X, A, B, dY, 2, 0, b1_bits=b1)["db2"]
+    mag = np.abs(oracle.bf16_decode(dY)).sum(axis=0)
+    assert np.all(np.abs(host_f64(db2) - ref) <= M * U * mag)
