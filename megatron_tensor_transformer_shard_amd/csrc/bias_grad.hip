@@ -14,7 +14,9 @@
 //     8 adjacent columns (one 16-byte load per row), the 4 waves take every
 //     4th row, and their sums are added in wave order through LDS into one
 //     fp32 partial per column and row block.
-//  2. One thread per column adds the row blocks' partials in block order.
+//  2. One thread per column adds the row blocks' partials in block order,
+//     loading kBatch of them at a time so that their latencies overlap (a
+//     loop of dependent single loads left this pass latency-bound).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -25,6 +27,7 @@ constexpr int kThreads = 256;
 constexpr int kRows = 128;              // rows per workgroup of pass 1
 constexpr int kCols = 512;              // columns per workgroup of pass 1 (64 lanes x 8)
 constexpr int kRowsPerWave = kRows / 4;
+constexpr int kBatch = 16;              // partials loaded together in pass 2
 
 __global__ __launch_bounds__(kThreads) void colsum_partial_kernel(const uint16_t* __restrict__ G,
                                                                   int64_t ld, int rows, int cols,
@@ -36,7 +39,7 @@ __global__ __launch_bounds__(kThreads) void colsum_partial_kernel(const uint16_t
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   if (c0 < cols) {  // cols is a multiple of 8, so a lane's 8 columns are all inside or all out
     const uint16_t* p = G + (int64_t)r0 * ld + c0;
-#pragma unroll 8
+#pragma unroll 16
     for (int j = 0; j < kRowsPerWave; ++j) {
       if (r0 + 4 * j < rows) {
         const u32x4 w = *reinterpret_cast<const u32x4*>(p + (int64_t)(4 * j) * ld);
@@ -66,7 +69,14 @@ __global__ __launch_bounds__(kThreads) void colsum_finish_kernel(const float* __
   const int c = blockIdx.x * kThreads + threadIdx.x;
   if (c >= cols) return;
   float s = 0.0f;
-  for (int b = 0; b < blocks; ++b) s += partial[(int64_t)b * cols + c];
+  for (int b0 = 0; b0 < blocks; b0 += kBatch) {
+    float v[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j)
+      v[j] = b0 + j < blocks ? partial[(int64_t)(b0 + j) * cols + c] : 0.0f;
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) s += v[j];  // block order; a missing block adds +0
+  }
   out[c] = s;
 }
 
