@@ -101,3 +101,28 @@ def test_transposed_weight_forward_in_a_graph(tpm):
         for r in range(N):
             tpm.tp_mlp_shard_wt(Xd, W1, W2, N, r, Y_i=parts[r], workspace=ws[r])
     _replay_and_compare(step, parts)
+
+
+def test_bias_forward_backward_and_bias_gradient_in_a_graph(tpm):
+    import torch
+    from workloads import make_bias
+    M, d, H, N = 272, 144, 576, 2
+    F = H // N
+    X, A, B = make_random(M, d, H, seed=35, sigma=0.05)
+    dY = make_output_grad(M, d, seed=36)
+    Xd, Ad, Bd, dYd = dev_bf16(X), dev_bf16(A), dev_bf16(B), dev_bf16(dY)
+    b1 = dev_bf16(make_bias(H, seed=37))
+    Z = torch.empty((M, F), dtype=torch.bfloat16, device="cuda")
+    outs = [torch.empty(shp, dtype=torch.float32, device="cuda")
+            for shp in ((M, d), (d, F), (F, d), (F,), (d,))]
+    ws = torch.empty(tpm.tp_mlp_shard_backward_bias_workspace_size(M, d, H, N), dtype=torch.uint8,
+                     device="cuda")
+    wsg = torch.empty(max(tpm.tp_bias_grad_workspace_size(M, d), 256), dtype=torch.uint8,
+                      device="cuda")
+
+    def step():
+        tpm.tp_mlp_col_gelu_bias(Xd, Ad[:, F:], b1[F:], Z)
+        tpm.tp_mlp_shard_backward_bias(Xd, Ad, b1, Bd, dYd, N, 1, dX_i=outs[0], dA_i=outs[1],
+                                       dB_i=outs[2], db1_i=outs[3], workspace=ws)
+        tpm.tp_bias_grad_bf16(dYd, db=outs[4], workspace=wsg)
+    _replay_and_compare(step, [Z] + outs)
