@@ -401,7 +401,7 @@ def quantize_e5m2(T_bits: np.ndarray):
     return quant_e5m2(T_bits, s), s
 
 
-def mlp_shard_backward_fp8(X_bits, A_bits, B_bits, dY_bits, N: int, rank: int):
+def mlp_shard_backward_fp8(X_bits, A_bits, B_bits, dY_bits, N: int, rank: int, b1_bits=None):
     """Gradients of rank `rank`'s shard with fp8 GEMMs in the hybrid formats.
 
     Returns a dict: the scales sX, sA, sB, sdY, sdS, sZ (float32), the codes
@@ -411,6 +411,9 @@ def mlp_shard_backward_fp8(X_bits, A_bits, B_bits, dY_bits, N: int, rank: int):
       dZ = (dYq·Bq_iᵀ)/(sdY·sB)
       dS = bf16(dZ ⊙ GeLU'(S)),  Z = bf16(GeLU(S))
       dX = (dSq·Aq_iᵀ)/(sdS·sA),  dA = (Xqᵀ·dSq)/(sX·sdS),  dB = (Zqᵀ·dYq)/(sZ·sdY)
+    With b1_bits (bf16 [H], the column layer's bias, not quantised) the rank's
+    block is added to the dequantised S, and db1 = Σ_m dS (the bf16 dS, before
+    its e5m2 quantisation) and db2 = Σ_m dY (bf16 dY) are returned as well.
     """
     H = A_bits.shape[1]
     lo, hi = shard_columns(H, N, rank)
@@ -421,15 +424,23 @@ def mlp_shard_backward_fp8(X_bits, A_bits, B_bits, dY_bits, N: int, rank: int):
     Xv, Av, Bv = e4m3_decode(Xq), e4m3_decode(Aq)[:, lo:hi], e4m3_decode(Bq)[lo:hi, :]
     dYv = e5m2_decode(dYq)
     S = (Xv @ Av) / (float(sX) * float(sA))
+    if b1_bits is not None:
+        if np.shape(b1_bits) != (H,):
+            raise ValueError("b1 must have the hidden width")
+        S = S + bf16_decode(b1_bits)[lo:hi][None, :]
     dZ = (dYv @ Bv.T) / (float(sdY) * float(sB))
     dS_bits = bf16_encode(dZ * gelu_grad(S))
     Z_bits = bf16_encode(gelu(S))
     dSq, sdS = quantize_e5m2(dS_bits)
     Zq, sZ = quantize_inputs_e4m3(Z_bits)
     dSv, Zv = e5m2_decode(dSq), e4m3_decode(Zq)
-    return {"sX": sX, "sA": sA, "sB": sB, "sdY": sdY, "sdS": sdS, "sZ": sZ,
-            "Xq": Xq, "Aq_i": Aq[:, lo:hi], "Bq_i": Bq[lo:hi, :], "dYq": dYq,
-            "S": S, "dZ": dZ, "dS_bits": dS_bits, "Z_bits": Z_bits, "dSq": dSq, "Zq": Zq,
-            "dX": (dSv @ Av.T) / (float(sdS) * float(sA)),
-            "dA": (Xv.T @ dSv) / (float(sX) * float(sdS)),
-            "dB": (Zv.T @ dYv) / (float(sZ) * float(sdY))}
+    g = {"sX": sX, "sA": sA, "sB": sB, "sdY": sdY, "sdS": sdS, "sZ": sZ,
+         "Xq": Xq, "Aq_i": Aq[:, lo:hi], "Bq_i": Bq[lo:hi, :], "dYq": dYq,
+         "S": S, "dZ": dZ, "dS_bits": dS_bits, "Z_bits": Z_bits, "dSq": dSq, "Zq": Zq,
+         "dX": (dSv @ Av.T) / (float(sdS) * float(sA)),
+         "dA": (Xv.T @ dSv) / (float(sX) * float(sdS)),
+         "dB": (Zv.T @ dYv) / (float(sZ) * float(sdY))}
+    if b1_bits is not None:
+        g["db1"] = bf16_decode(dS_bits).sum(axis=0)
+        g["db2"] = bf16_decode(dY_bits).sum(axis=0)
+    return g

@@ -126,6 +126,37 @@ def test_backward_bias_gradients_match_finite_differences(N, rank):
         assert _rel_maxdiff(grads[name], num) <= 1e-6, name
 
 
+def test_fp8_backward_with_a_zero_bias_is_the_unbiased_fp8_backward():
+    X, A, B = make_random(32, 64, 256, seed=84, sigma=0.05)
+    dY = _dy(32, 64, 85)
+    g0 = oracle.mlp_shard_backward_fp8(X, A, B, dY, 2, 1)
+    gb = oracle.mlp_shard_backward_fp8(X, A, B, dY, 2, 1, b1_bits=np.zeros(256, np.uint16))
+    for k in ("S", "dS_bits", "Z_bits", "dSq", "Zq", "dX", "dA", "dB"):
+        assert np.array_equal(g0[k], gb[k]), k
+
+
+def test_fp8_backward_bias_enters_s_and_sums_ds():
+    """The bias moves the dequantised S by exactly its block (float64 sums of
+    exactly representable values), and db1 / db2 are the column sums of the
+    bf16 dS and dY; against the bf16 oracle's bias gradients the fp8 ones
+    differ by the quantisation only."""
+    M, d, H, N, rank = 32, 64, 256, 4, 2
+    X, A, B = make_random(M, d, H, seed=86, sigma=0.05)
+    dY = _dy(M, d, 87)
+    b1 = make_bias(H, seed=88, sigma=0.5)
+    g0 = oracle.mlp_shard_backward_fp8(X, A, B, dY, N, rank)
+    gb = oracle.mlp_shard_backward_fp8(X, A, B, dY, N, rank, b1_bits=b1)
+    lo, hi = oracle.shard_columns(H, N, rank)
+    assert np.array_equal(gb["S"] - g0["S"],
+                          np.broadcast_to(oracle.bf16_decode(b1)[lo:hi], (M, hi - lo))) or \
+        np.max(np.abs(gb["S"] - g0["S"] - oracle.bf16_decode(b1)[lo:hi][None, :])) <= 1e-15
+    assert np.array_equal(gb["db1"], oracle.bf16_decode(gb["dS_bits"]).sum(axis=0))
+    assert np.array_equal(gb["db2"], oracle.bf16_decode(dY).sum(axis=0))
+    g16 = oracle.mlp_shard_backward(X, A, B, dY, N, rank, b1_bits=b1)
+    assert np.array_equal(gb["db2"], g16["db2"])
+    assert _rel_maxdiff(gb["db1"], g16["db1"]) <= 0.1
+
+
 # plausible mistakes, each planted in the oracle, fail at least one pin above
 def _pins_fail():
     for fn in (test_zero_bias_is_the_unbiased_step, test_zero_input_gives_the_gelu_of_the_bias,
