@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define TPM_ABI_VERSION 4
+#define TPM_ABI_VERSION 5
 
 /* Element types. */
 typedef enum {
@@ -213,6 +213,24 @@ int tp_mlp_shard_backward_bias(const void* X, const void* A, const void* b1, con
                                const void* dY, float* dX_i, float* dA_i, float* dB_i,
                                float* db1_i, int64_t M, int64_t d, int64_t H, int N, int rank,
                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The fp8 backward (tp_mlp_shard_backward_fp8) when the forward had the
+ * column layer's bias: the rank's block of b1 (bf16, not quantised) is added
+ * to the dequantised S, and db1_i = Σ_m dS[m, :] is taken over the bf16 dS
+ * before its e5m2 quantisation (the higher-precision gradient), in fp32.
+ * Arguments as tp_mlp_shard_backward_fp8 plus b1 (device, bf16 [H]) and
+ * db1_i (device, fp32 [F], written); workspace:
+ * tp_mlp_shard_backward_fp8_bias_workspace_size bytes, laid out as the fp8
+ * backward's with the bias-gradient scratch after it. M = 0 writes
+ * db1_i = 0 and nothing else.
+ */
+size_t tp_mlp_shard_backward_fp8_bias_workspace_size(int64_t M, int64_t d, int64_t H, int N);
+int tp_mlp_shard_backward_fp8_bias(const void* X, const void* A, const void* b1, const void* B,
+                                   const void* dY, float* dX_i, float* dA_i, float* dB_i,
+                                   float* db1_i, int64_t M, int64_t d, int64_t H, int N, int rank,
+                                   const float* w_amax, void* workspace, size_t workspace_bytes,
+                                   void* stream);
 
 /*
  * Gradient of a bias added to every row of a layer's output:

@@ -31,6 +31,7 @@ __all__ = [
     "tp_mlp_shard_backward", "tp_mlp_shard_backward_workspace_size", "backward_workspace_views",
     "tp_mlp_shard_backward_bias", "tp_mlp_shard_backward_bias_workspace_size",
     "tp_bias_grad_bf16", "tp_bias_grad_workspace_size",
+    "tp_mlp_shard_backward_fp8_bias", "tp_mlp_shard_backward_fp8_bias_workspace_size",
     "tp_mlp_shard_backward_fp8", "tp_mlp_shard_backward_fp8_workspace_size",
     "tp_attn_qkv", "tp_attn_heads", "tp_attn_shard", "tp_attn_shard_workspace_size",
     "attn_workspace_views", "ATTN_HEAD_DIM", "fp8_backward_workspace_views",
@@ -82,6 +83,9 @@ _SIGNATURES = {
     "tp_mlp_shard_backward_bias": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64,
                                           _i64, _int, _int, _vp, _sz, _vp]),
     "tp_bias_grad_workspace_size": (_sz, [_i64, _i64]),
+    "tp_mlp_shard_backward_fp8_bias_workspace_size": (_sz, [_i64, _i64, _i64, _int]),
+    "tp_mlp_shard_backward_fp8_bias": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64,
+                                              _i64, _i64, _int, _int, _vp, _vp, _sz, _vp]),
     "tp_bias_grad_bf16": (_int, [_vp, _i64, _i64, _i64, _vp, _vp, _sz, _vp]),
     "tp_attn_qkv": (_int, [_vp, _vp, _i64, _vp, _i64, _i64, _i64, _vp]),
     "tp_attn_heads": (_int, [_vp, _i64, _vp, _i64, _i64, _i64, _i64, _int, _vp]),
@@ -96,7 +100,7 @@ EXPORTED_SYMBOLS = tuple(_SIGNATURES)
 
 
 # The entry-point signatures below are those of this ABI version of include/tpmlp.h.
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 
 def _load_library():
@@ -795,7 +799,7 @@ def tp_mlp_shard_backward_fp8_workspace_size(M: int, d: int, H: int, N: int) -> 
 
 
 def tp_mlp_shard_backward_fp8(X, A, B, dY, N: int, rank: int, dX_i=None, dA_i=None, dB_i=None,
-                              workspace=None, stream=None, w_amax=None):
+                              workspace=None, stream=None, w_amax=None, b1=None, db1_i=None):
     """Gradients of rank `rank`'s shard with hybrid fp8 GEMMs (E4M3 activations and
     weights, E5M2 gradients). w_amax: None, or a device float32 tensor of two
     values, max|A| and max|B| over the whole weights (then they are not
@@ -817,7 +821,18 @@ def tp_mlp_shard_backward_fp8(X, A, B, dY, N: int, rank: int, dX_i=None, dA_i=No
         _need(t, name, torch.float32, 2)
         if tuple(t.shape) != shp:
             raise ValueError(f"{name} has the wrong shape")
-    need = tp_mlp_shard_backward_fp8_workspace_size(M, d, H, N)
+    if b1 is not None:
+        _need(b1, "b1", torch.bfloat16, 1)
+        if b1.numel() != H:
+            raise ValueError(f"b1 has {b1.numel()} values, the hidden width is {H}")
+        if db1_i is None:
+            db1_i = torch.empty(F, dtype=torch.float32, device=dev)
+        _need(db1_i, "db1_i", torch.float32, 1)
+        if db1_i.numel() != F:
+            raise ValueError("db1_i has the wrong shape")
+        need = tp_mlp_shard_backward_fp8_bias_workspace_size(M, d, H, N)
+    else:
+        need = tp_mlp_shard_backward_fp8_workspace_size(M, d, H, N)
     if workspace is None:
         workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
     _need(workspace, "workspace", None)
@@ -825,14 +840,38 @@ def tp_mlp_shard_backward_fp8(X, A, B, dY, N: int, rank: int, dX_i=None, dA_i=No
         _need(w_amax, "w_amax", torch.float32)
         if w_amax.numel() != 2:
             raise ValueError("w_amax holds two values: max|A| and max|B|")
-    _check(lib.tp_mlp_shard_backward_fp8(X.data_ptr(), A.data_ptr(), B.data_ptr(), dY.data_ptr(),
-                                         dX_i.data_ptr(), dA_i.data_ptr(), dB_i.data_ptr(), M, d,
-                                         H, N, rank, 0 if w_amax is None else w_amax.data_ptr(),
-                                         workspace.data_ptr(),
-                                         workspace.numel() * workspace.element_size(),
-                                         _stream(stream)),
-           "tp_mlp_shard_backward_fp8")
-    return dX_i, dA_i, dB_i, workspace
+    wam = 0 if w_amax is None else w_amax.data_ptr()
+    wsb = workspace.numel() * workspace.element_size()
+    if b1 is None:
+        _check(lib.tp_mlp_shard_backward_fp8(X.data_ptr(), A.data_ptr(), B.data_ptr(),
+                                             dY.data_ptr(), dX_i.data_ptr(), dA_i.data_ptr(),
+                                             dB_i.data_ptr(), M, d, H, N, rank, wam,
+                                             workspace.data_ptr(), wsb, _stream(stream)),
+               "tp_mlp_shard_backward_fp8")
+        return dX_i, dA_i, dB_i, workspace
+    _check(lib.tp_mlp_shard_backward_fp8_bias(X.data_ptr(), A.data_ptr(), b1.data_ptr(),
+                                              B.data_ptr(), dY.data_ptr(), dX_i.data_ptr(),
+                                              dA_i.data_ptr(), dB_i.data_ptr(), db1_i.data_ptr(),
+                                              M, d, H, N, rank, wam, workspace.data_ptr(), wsb,
+                                              _stream(stream)),
+           "tp_mlp_shard_backward_fp8_bias")
+    return dX_i, dA_i, dB_i, db1_i, workspace
+
+
+def tp_mlp_shard_backward_fp8_bias_workspace_size(M: int, d: int, H: int, N: int) -> int:
+    return int(lib.tp_mlp_shard_backward_fp8_bias_workspace_size(M, d, H, N))
+
+
+def tp_mlp_shard_backward_fp8_bias(X, A, b1, B, dY, N: int, rank: int, dX_i=None, dA_i=None,
+                                   dB_i=None, db1_i=None, workspace=None, stream=None,
+                                   w_amax=None):
+    """tp_mlp_shard_backward_fp8 when the forward added the column layer's bias
+    b1 [H] (bf16) before GeLU. Returns (dX_i, dA_i, dB_i, db1_i, workspace);
+    the workspace's views are those of `fp8_backward_workspace_views`."""
+    if b1 is None:
+        raise ValueError("b1 is required")
+    return tp_mlp_shard_backward_fp8(X, A, B, dY, N, rank, dX_i, dA_i, dB_i, workspace, stream,
+                                     w_amax, b1=b1, db1_i=db1_i)
 
 
 def fp8_backward_workspace_views(workspace, M: int, d: int, F: int):

@@ -715,10 +715,15 @@ size_t tp_mlp_shard_backward_fp8_workspace_size(int64_t M, int64_t d, int64_t H,
   return fp8_bwd_layout(M, d, H / N).total;
 }
 
-int tp_mlp_shard_backward_fp8(const void* X, const void* A, const void* B, const void* dY,
-                              float* dX_i, float* dA_i, float* dB_i, int64_t M, int64_t d,
-                              int64_t H, int N, int rank, const float* w_amax, void* workspace,
-                              size_t workspace_bytes, void* stream) {
+namespace {
+// The fp8 backward of one rank's shard; with b1 (the column layer's whole
+// bf16 bias [H]) the rank's block is added to the dequantised S, and
+// db1_i = Σ_m dS (the bf16 dS) is written, with its scratch after the
+// workspace's other parts.
+int shard_backward_fp8(const void* X, const void* A, const void* B, const void* dY,
+                       const void* b1, float* dX_i, float* dA_i, float* dB_i, float* db1_i,
+                       int64_t M, int64_t d, int64_t H, int N, int rank, const float* w_amax,
+                       void* workspace, size_t workspace_bytes, void* stream) {
   if (N < 1 || rank < 0 || rank >= N) return TPM_ERR_ARG;
   if (H <= 0 || H % N != 0) return TPM_ERR_SHAPE;
   const int64_t F = H / N;
@@ -731,24 +736,34 @@ int tp_mlp_shard_backward_fp8(const void* X, const void* A, const void* B, const
   // the quantise-and-transpose grid has one 64-row tile per y index
   constexpr int64_t kMaxTileRows = int64_t(65535) * 64;
   if (M > kMaxTileRows || d > kMaxTileRows || F > kMaxTileRows) return TPM_ERR_SHAPE;
-  if (M == 0) return TPM_OK;
+  const bool bias = b1 != nullptr || db1_i != nullptr;
+  if (bias && (!b1 || !db1_i)) return TPM_ERR_NULL;
+  if (M == 0) {  // no tokens: nothing to do, and a zero bias gradient
+    if (!bias) return TPM_OK;
+    if (!aligned16(db1_i)) return TPM_ERR_ALIGN;
+    if (overlap(mat_span(db1_i, 1, F, F, 4), mat_span(b1, 1, H, H, 2))) return TPM_ERR_ALIAS;
+    return status_of(tpmlp::launch_colsum_bf16(nullptr, F, 0, (int)F, db1_i, nullptr,
+                                               as_stream(stream)));
+  }
   if (!X || !A || !B || !dY || !dX_i || !dA_i || !dB_i) return TPM_ERR_NULL;
   const Fp8BwdLayout L = fp8_bwd_layout(M, d, F);
-  if (!workspace || workspace_bytes < L.total) return TPM_ERR_WORKSPACE;
+  const size_t need = L.total + (bias ? round256((size_t)tpmlp::colsum_row_blocks(M) * F * 4) : 0);
+  if (!workspace || workspace_bytes < need) return TPM_ERR_WORKSPACE;
   if (!aligned16(X) || !aligned16(A) || !aligned16(B) || !aligned16(dY) || !aligned16(dX_i) ||
       !aligned16(dA_i) || !aligned16(dB_i) || !aligned16(workspace) ||
-      (reinterpret_cast<uintptr_t>(w_amax) & 3u))
+      (reinterpret_cast<uintptr_t>(w_amax) & 3u) || (bias && (!aligned16(b1) || !aligned16(db1_i))))
     return TPM_ERR_ALIGN;
-  const Span ins[5] = {mat_span(X, M, d, d, 2), mat_span(A, d, H, H, 2), mat_span(B, H, d, d, 2),
-                       mat_span(dY, M, d, d, 2), mat_span(w_amax, w_amax ? 1 : 0, 2, 2, 4)};
-  const Span outs[4] = {mat_span(dX_i, M, d, d, 4), mat_span(dA_i, d, F, F, 4),
-                        mat_span(dB_i, F, d, d, 4),
+  const Span ins[6] = {mat_span(X, M, d, d, 2), mat_span(A, d, H, H, 2), mat_span(B, H, d, d, 2),
+                       mat_span(dY, M, d, d, 2), mat_span(w_amax, w_amax ? 1 : 0, 2, 2, 4),
+                       mat_span(b1, bias ? 1 : 0, H, H, 2)};
+  const Span outs[5] = {mat_span(dX_i, M, d, d, 4), mat_span(dA_i, d, F, F, 4),
+                        mat_span(dB_i, F, d, d, 4), mat_span(db1_i, bias ? 1 : 0, F, F, 4),
                         {reinterpret_cast<uintptr_t>(workspace),
-                         reinterpret_cast<uintptr_t>(workspace) + L.total}};
-  for (int o = 0; o < 4; ++o) {
-    for (int i = 0; i < 5; ++i)
+                         reinterpret_cast<uintptr_t>(workspace) + need}};
+  for (int o = 0; o < 5; ++o) {
+    for (int i = 0; i < 6; ++i)
       if (overlap(outs[o], ins[i])) return TPM_ERR_ALIAS;
-    for (int p = o + 1; p < 4; ++p)
+    for (int p = o + 1; p < 5; ++p)
       if (overlap(outs[o], outs[p])) return TPM_ERR_ALIAS;
   }
 
@@ -788,14 +803,20 @@ int tp_mlp_shard_backward_fp8(const void* X, const void* A, const void* B, const
   run(tpmlp::launch_quant_fp8_tile(E4, A_i, H, dd, f, amA, Aq, F, AqT, d, sc + 1, s));
   run(tpmlp::launch_quant_fp8_tile(E4, B_i, d, f, dd, amB, nullptr, 0, BqT, F, sc + 2, s));
   run(tpmlp::launch_quant_fp8(E5, dy, M * d, am + 3, dYq, sc + 3, s));
-  // S = (Xq·Aq_i)/(sX·sA)
-  run(tpmlp::launch_gemm_fp8(Fp8GemmArgs{Xq, d, sc + 0, Aq, F, sc + 1, S, F, nullptr, nullptr,
-                                         nullptr, 0, nullptr, nullptr, m, f, dd},
-                             OutKind::F32, E4, E4, s));
+  // S = (Xq·Aq_i)/(sX·sA) (+ b1_i)
+  {
+    Fp8GemmArgs a{Xq, d, sc + 0, Aq, F, sc + 1, S, F, nullptr, nullptr,
+                  nullptr, 0, nullptr, nullptr, m, f, dd};
+    if (bias) a.bias = static_cast<const uint16_t*>(b1) + (int64_t)rank * F;
+    run(tpmlp::launch_gemm_fp8(a, bias ? OutKind::F32Bias : OutKind::F32, E4, E4, s));
+  }
   // dS = bf16(((dYq·Bq_iᵀ)/(sdY·sB)) ⊙ GeLU'(S)), Z = bf16(GeLU(S)), their amaxes
   run(tpmlp::launch_gemm_fp8(Fp8GemmArgs{dYq, d, sc + 3, BqT, F, sc + 2, dS, F, am + 4, nullptr,
                                          S, F, Z, am + 5, m, f, dd},
                              OutKind::GeluGradBf16, E5, E4, s, false));
+  // db1_i = Σ_m dS[m, :] from the bf16 dS, before its e5m2 quantisation
+  if (bias)
+    run(tpmlp::launch_colsum_bf16(dS, F, m, f, db1_i, reinterpret_cast<float*>(ws + L.total), s));
   run(tpmlp::launch_quant_fp8(E5, dS, M * F, am + 4, dSq, sc + 4, s));
   run(tpmlp::launch_quant_fp8_tile(E4, Z, F, m, f, am + 5, nullptr, 0, ZqT, M, sc + 5, s));
   // dX_i = (dSq·Aq_iᵀ)/(sdS·sA)
@@ -811,6 +832,30 @@ int tp_mlp_shard_backward_fp8(const void* X, const void* A, const void* B, const
                   nullptr, dd, f, m},
       OutKind::F32, E4, E5, s));
   return status_of(e);
+}
+}  // namespace
+
+int tp_mlp_shard_backward_fp8(const void* X, const void* A, const void* B, const void* dY,
+                              float* dX_i, float* dA_i, float* dB_i, int64_t M, int64_t d,
+                              int64_t H, int N, int rank, const float* w_amax, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  return shard_backward_fp8(X, A, B, dY, nullptr, dX_i, dA_i, dB_i, nullptr, M, d, H, N, rank,
+                            w_amax, workspace, workspace_bytes, stream);
+}
+
+size_t tp_mlp_shard_backward_fp8_bias_workspace_size(int64_t M, int64_t d, int64_t H, int N) {
+  const size_t base = tp_mlp_shard_backward_fp8_workspace_size(M, d, H, N);
+  if (base == 0) return 0;
+  return base + round256((size_t)tpmlp::colsum_row_blocks(M) * (size_t)(H / N) * 4);
+}
+
+int tp_mlp_shard_backward_fp8_bias(const void* X, const void* A, const void* b1, const void* B,
+                                   const void* dY, float* dX_i, float* dA_i, float* dB_i,
+                                   float* db1_i, int64_t M, int64_t d, int64_t H, int N, int rank,
+                                   const float* w_amax, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  return shard_backward_fp8(X, A, B, dY, b1, dX_i, dA_i, dB_i, db1_i, M, d, H, N, rank, w_amax,
+                            workspace, workspace_bytes, stream);
 }
 
 int tp_attn_qkv(const void* X, const void* W_i, int64_t ldw, void* QKV_i, int64_t M, int64_t d,

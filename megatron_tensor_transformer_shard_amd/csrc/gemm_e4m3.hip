@@ -592,7 +592,17 @@ __global__ __launch_bounds__(kThreads) void gemm_e4m3_kernel(Fp8GemmArgs g0, Fp8
   auto max_of = [](u16x2 m) __attribute__((always_inline)) {
     return bf16_bits_to_f32(max((uint32_t)m[0], (uint32_t)m[1]));
   };
-  if constexpr (OUT == (int)OutKind::F32) {
+  if constexpr (OUT == (int)OutKind::F32 || OUT == (int)OutKind::F32Bias) {
+    // F32Bias: the lane's four bias values per 16-column group, loaded once
+    // from a column clamped into [0, N - 4] (N a multiple of 16, ncol of 4)
+    // and kept as packed bf16 pairs; a clamped group is never stored.
+    [[maybe_unused]] u32x2 bias2[NT];
+    if constexpr (OUT == (int)OutKind::F32Bias) {
+      const int col_max = N - 4 - ncol;
+#pragma unroll
+      for (int ni = 0; ni < NT; ++ni)
+        bias2[ni] = *reinterpret_cast<const u32x2*>(g.bias + ncol + min(16 * ni, col_max));
+    }
 #pragma unroll
     for (int ni = 0; ni < NT; ++ni) {
 #pragma unroll
@@ -600,7 +610,14 @@ __global__ __launch_bounds__(kThreads) void gemm_e4m3_kernel(Fp8GemmArgs g0, Fp8
         if (!inside(mi, ni)) continue;
         f32x4 v = acc[ni][mi];
         asm volatile("" : "+v"(v));
-        *reinterpret_cast<f32x4*>(static_cast<float*>(C) + c_off(mi, ni)) = v * dq;
+        if constexpr (OUT == (int)OutKind::F32Bias) {
+          const u32x2 w = bias2[ni];
+          const f32x4 b = {__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xFFFF0000u),
+                           __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xFFFF0000u)};
+          *reinterpret_cast<f32x4*>(static_cast<float*>(C) + c_off(mi, ni)) = v * dq + b;
+        } else {
+          *reinterpret_cast<f32x4*>(static_cast<float*>(C) + c_off(mi, ni)) = v * dq;
+        }
       }
     }
     return;
@@ -703,7 +720,8 @@ hipError_t launch_one(const Fp8GemmArgs* a, int n, hipStream_t stream) {
 }
 
 // The (formats, epilogue) combinations the path uses: e4m3 x e4m3 for the
-// forward (GeLU, GeLU + e4m3, bf16) and the backward's recomputed S (fp32);
+// forward (GeLU, GeLU + e4m3, bf16) and the backward's recomputed S (fp32,
+// with or without the column layer's bias);
 // e5m2 P x e4m3 Q for dS (GeLU') and dX_i (fp32); e4m3 P x e5m2 Q for the
 // weight gradients (fp32).
 template <int BM, int BN, bool KTAIL>
@@ -714,6 +732,7 @@ hipError_t launch_cfg(const Fp8GemmArgs* a, int n, OutKind out, int fp, int fq, 
       case OutKind::GeluE4m3: return launch_one<BM, BN, (int)OutKind::GeluE4m3, KTAIL, 0, 0>(a, n, stream);
       case OutKind::Bf16: return launch_one<BM, BN, (int)OutKind::Bf16, KTAIL, 0, 0>(a, n, stream);
       case OutKind::F32: return launch_one<BM, BN, (int)OutKind::F32, KTAIL, 0, 0>(a, n, stream);
+      case OutKind::F32Bias: return launch_one<BM, BN, (int)OutKind::F32Bias, KTAIL, 0, 0>(a, n, stream);
       default: return hipErrorInvalidValue;
     }
   }

@@ -97,6 +97,7 @@ struct Fp8GemmArgs {
   void* C; int64_t ldc; float* z_amax; const float* sC;
   const float* aux; int64_t ldaux; void* C2; float* z_amax2;
   int M, N, K;
+  const uint16_t* bias = nullptr;  // F32Bias: bf16 [N], added to every row after dequantising
 };
 hipError_t launch_gemm_fp8(const Fp8GemmArgs& a, OutKind out, int fp, int fq,
                            hipStream_t stream, bool zero_amax = true);

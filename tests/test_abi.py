@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert tpm.abi_version() == tpm.ABI_VERSION == 4
+    assert tpm.abi_version() == tpm.ABI_VERSION == 5
     for code in (OK, ENULL, EARG, ESHAPE, EDTYPE, EALIGN, EWS, EALIAS, EHIP):
         s = tpm.status_string(code)
         assert s.startswith("TPM_")
@@ -166,6 +166,25 @@ def test_backward_bias_validation():
     assert bwd_bias(wsb=L.tp_mlp_shard_backward_workspace_size(32, 64, 256, 2)) == EWS
     assert bwd_bias(rank=2) == EARG
     assert bwd_bias(M=12) == ESHAPE
+
+
+def bwd8_bias(b1=BASE + 2 * GB, db1=BASE + 8 * GB, M=32, d=64, H=256, N=2, rank=0, wsb=None):
+    if wsb is None:
+        wsb = L.tp_mlp_shard_backward_fp8_bias_workspace_size(M, d, H, N)
+    return L.tp_mlp_shard_backward_fp8_bias(BASE, BASE + GB, b1, BASE + 3 * GB, BASE + 4 * GB,
+                                            BASE + 5 * GB, BASE + 6 * GB, BASE + 7 * GB, db1,
+                                            M, d, H, N, rank, None, BASE + 9 * GB, wsb, None)
+
+
+def test_backward_fp8_bias_validation():
+    plain = L.tp_mlp_shard_backward_fp8_workspace_size(32, 64, 256, 2)
+    assert L.tp_mlp_shard_backward_fp8_bias_workspace_size(32, 64, 256, 2) == plain + 512
+    assert bwd8_bias(b1=None) == ENULL
+    assert bwd8_bias(db1=None) == ENULL
+    assert bwd8_bias(db1=BASE + 8 * GB + 4) == EALIGN
+    assert bwd8_bias(db1=BASE + 2 * GB + 64) == EALIAS    # db1_i overlaps b1
+    assert bwd8_bias(wsb=L.tp_mlp_shard_backward_fp8_workspace_size(32, 64, 256, 2)) == EWS
+    assert bwd8_bias(M=8) == ESHAPE                       # M a multiple of 16 for fp8
 
 
 def bias_grad(G=BASE, ld=64, rows=300, cols=64, db=BASE + GB, ws=BASE + 2 * GB, wsb=None):

@@ -234,3 +234,49 @@ def test_bias_grad_of_dy_vs_oracle(tpm):
     ref = oracle.mlp_shard_backward(X, A, B, dY, 2, 0, b1_bits=b1)["db2"]
     mag = np.abs(oracle.bf16_decode(dY)).sum(axis=0)
     assert np.all(np.abs(host_f64(db2) - ref) <= M * U * mag)
+
+
+@pytest.mark.parametrize("M,d,H,N", [(272, 208, 2496, 3), (528, 272, 1088, 4)])
+def test_fp8_backward_with_bias_vs_oracle(tpm, M, d, H, N):
+    """The fp8 backward with the column bias: the scales as without it, db1_i
+    equal to the column sum of the GPU's own bf16 dS within the fp32
+    summation bound, and db1_i and the gradients within the fp8 bar of the
+    oracle."""
+    import torch
+    log(f"case fp8 backward with bias M={M} d={d} H={H} N={N}")
+    X, A, B = make_random(M, d, H, seed=13 * M + N, sigma=0.05)
+    b1 = make_bias(H, seed=M + 5, sigma=0.5)
+    dY = _dy(M, d, M + 6)
+    Xd, Ad, Bd, dYd, b1d = dev_bf16(X), dev_bf16(A), dev_bf16(B), dev_bf16(dY), dev_bf16(b1)
+    F = H // N
+    for rank in sorted({0, N - 1}):
+        dX, dA, dB, db1, ws = tpm.tp_mlp_shard_backward_fp8_bias(Xd, Ad, b1d, Bd, dYd, N, rank)
+        _sync()
+        g = oracle.mlp_shard_backward_fp8(X, A, B, dY, N, rank, b1_bits=b1)
+        v = tpm.fp8_backward_workspace_views(ws, M, d, F)
+        sc = v["scale"].cpu().numpy()
+        for i, k in enumerate(("sX", "sA", "sB", "sdY")):
+            assert np.float32(sc[i]) == np.float32(g[k]), f"rank {rank}: scale {k}"
+        dSg = host_f64(v["dS"])
+        dbg = host_f64(db1)
+        assert np.all(np.abs(dbg - dSg.sum(axis=0)) <= M * U * np.abs(dSg).sum(axis=0) + 1e-30), \
+            f"rank {rank}: db1_i is not the column sum of dS"
+        for name, t, ref in (("db1", db1, g["db1"]), ("dX", dX, g["dX"]), ("dA", dA, g["dA"]),
+                             ("dB", dB, g["dB"])):
+            r = max_err_ratio(host_f64(t), ref)
+            log(f"rank {rank}: {name} err ratio {r:.3e}")
+            assert r <= 6e-2, f"rank {rank}: {name}"
+
+
+def test_fp8_backward_with_a_zero_bias_equals_the_unbiased_one(tpm):
+    import torch
+    M, d, H, N = 272, 144, 576, 2
+    X, A, B = make_random(M, d, H, seed=95, sigma=0.05)
+    dY = _dy(M, d, 96)
+    Xd, Ad, Bd, dYd = dev_bf16(X), dev_bf16(A), dev_bf16(B), dev_bf16(dY)
+    zero = torch.zeros(H, dtype=torch.bfloat16, device="cuda")
+    got = tpm.tp_mlp_shard_backward_fp8_bias(Xd, Ad, zero, Bd, dYd, N, 1)
+    ref = tpm.tp_mlp_shard_backward_fp8(Xd, Ad, Bd, dYd, N, 1)
+    _sync()
+    for name, a, b in zip(("dX", "dA", "dB"), got[:3], ref[:3]):
+        assert torch.equal(a, b), f"{name} differs with a zero bias"
