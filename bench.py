@@ -109,6 +109,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="stop adding oracle row chunks once this much CPU time is spent")
     p.add_argument("--partial-dtype", choices=["f32", "bf16"], default="f32")
+    p.add_argument("--no-clock", action="store_true",
+                   help="skip the pass that reads the shader clock inside the stamped kernels")
     p.add_argument("--weight-layout", choices=["math", "linear"], default="math",
                    help="bf16 forward only: weights as A [d, H], B [H, d] (math), or as the "
                         "linear layers store them, W1 [H, d], W2 [d, H] (linear)")
@@ -236,6 +238,58 @@ def device_peak(tpm_peak_key):
     return vals
 
 
+def wall_clock_hz():
+    """Rate of the constant counter the kernels' clock stamps read
+    (hipDeviceAttributeWallClockRate, kHz), or None."""
+    import ctypes
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        dev, v = ctypes.c_int(), ctypes.c_int()
+        if hip.hipGetDevice(ctypes.byref(dev)) != 0:
+            return None
+        if hip.hipDeviceGetAttribute(ctypes.byref(v), 10017, dev) != 0 or v.value <= 0:
+            return None
+        return v.value * 1e3
+    except OSError:
+        return None
+
+
+def clock_pass(tpm, stamped, reps=5):
+    """The shader clock inside each stamped kernel: the launch repeated `reps`
+    times (warm, back to back, as in the kernel pass), each workgroup's
+    shader-clock cycles over its constant-counter time. Per kernel: the median
+    of the workgroups' clocks over all launches, the span from the first
+    workgroup's start to the last one's end (the in-kernel duration, without
+    the launch overhead that HIP events include), and the cycles of that span
+    at the median clock."""
+    import torch
+    hz = wall_clock_hz()
+    if hz is None:
+        return None
+    out = {}
+    for name, ((m, n), fn) in stamped.items():
+        count = tpm.tp_clock_stamp_count(m, n)
+        clocks, spans = [], []
+        for _ in range(reps):
+            st = torch.zeros(count, dtype=torch.int64, device="cuda")
+            fn(st)
+            torch.cuda.synchronize()
+            q = st.cpu().numpy().view(np.uint64).reshape(-1, 4)
+            q = q[np.any(q != 0, axis=1)].astype(np.float64)
+            if len(q) == 0:
+                return None
+            clocks.append((q[:, 2] - q[:, 0]) / ((q[:, 3] - q[:, 1]) / hz))
+            spans.append((q[:, 3].max() - q[:, 1].min()) / hz)
+        c = np.concatenate(clocks)
+        out[name] = {"workgroups": int(len(clocks[0])), "launches": reps,
+                     "clock_ghz_median": round(float(np.median(c)) / 1e9, 4),
+                     "clock_ghz_min": round(float(c.min()) / 1e9, 4),
+                     "clock_ghz_max": round(float(c.max()) / 1e9, 4),
+                     "span_us_median": round(1e6 * float(np.median(spans)), 2),
+                     "wall_clock_hz": hz}
+    return out
+
+
 def build_bf16_step(tpm, wl, partial_dtype, weight_layout="math"):
     """The forward of every rank's shard, then the sum of the partials. With
     the linear layout the weights are stored [out, in] (W1 = Aᵀ, W2 = Bᵀ,
@@ -273,6 +327,13 @@ def build_bf16_step(tpm, wl, partial_dtype, weight_layout="math"):
             else:
                 timer.around("partial_sum", lambda: tpm.tp_partial_sum(parts, Y=Y))
 
+    if weight_layout != "linear":
+        # the same launches with per-workgroup clock stamps (rank 0's shard views)
+        A0, B0 = views[0]
+        step.stamped = {
+            kc: ((M, F), lambda st: tpm.tp_mlp_col_gelu_stamped(Xd, A0, st, Z)),
+            kr: ((M, d), lambda st: tpm.tp_mlp_row_partial_stamped(Z, B0, st, parts[0])),
+        }
     kern_flops = {kc: 2 * M * d * F, kr: 2 * M * d * F}
     # algorithmic bytes: each operand read once, each output written once
     kern_bytes = {kc: (M * d + d * F) * 2 + M * F * 2,
@@ -416,6 +477,8 @@ def build_e4m3_step(tpm, wl):
                 else:
                     timer.around(name, fn)
 
+        step.stamped = {"row_partial_e4m3": (
+            (M, d), lambda st: tpm.tp_mlp_row_partial_e4m3_stamped(Zq, hist.scale, Bq, sB, st, Y))}
         kern_flops = {"col_gelu_e4m3_delayed": 2 * M * d * F, "row_partial_e4m3": 2 * M * d * F}
         kern_bytes = {"col_gelu_e4m3_delayed": M * d + d * F + M * F,
                       "row_partial_e4m3": M * F + F * d + M * d * 2}
@@ -431,6 +494,8 @@ def build_e4m3_step(tpm, wl):
             else:
                 timer.around(name, fn)
 
+    step.stamped = {"row_partial_e4m3": (
+        (M, d), lambda st: tpm.tp_mlp_row_partial_e4m3_stamped(Zq, sZ, Bq, sB, st, Y))}
     return step, kern_flops, kern_bytes, 0, (X, A, B), Y
 
 
@@ -687,7 +752,26 @@ def main():
                 "traffic": measured_traffic(wl.name, dom, pdt),
                 "flops_per_launch": kern_flops[dom], "algorithmic_bytes": kern_bytes[dom],
                 "avg_launch_us": round(kstats[dom]["avg_us"], 2),
-                "median_launch_us": round(kstats[dom]["median_us"], 2)}
+                "median_launch_us": round(kstats[dom]["median_us"], 2),
+                "clock_ghz_in_kernel": None, "frac_at_measured_clock": None}
+
+    # the shader clock inside the kernels, from the same kernels with clock
+    # stamps (a separate pass, outside every timed region): the MFMA peak
+    # scales with it, 4096 (bf16) or 8192 (fp8) flops per CU per clock
+    clocks = None if args.no_clock else clock_pass(tpm, getattr(step, "stamped", {}))
+    per_clk = 8192 if dtype == "e4m3" else 4096
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    for name, c in (clocks or {}).items():
+        peak_at = cus * per_clk * c["clock_ghz_median"] * 1e9 / 1e12
+        c["peak_at_clock_tflops"] = round(peak_at, 1)
+        if name in kstats:
+            kstats[name]["clock_ghz_in_kernel"] = c["clock_ghz_median"]
+            kstats[name]["frac_at_measured_clock"] = round(kstats[name]["tflops"] / peak_at, 4)
+            kstats[name]["tflops_over_in_kernel_span"] = round(
+                kern_flops[name] / (c["span_us_median"] * 1e-6) / 1e12, 1)
+    if clocks and dom in clocks:
+        roofline["clock_ghz_in_kernel"] = clocks[dom]["clock_ghz_median"]
+        roofline["frac_at_measured_clock"] = kstats[dom]["frac_at_measured_clock"]
 
     # cold mode: the same launches, each after a 512 MiB write that evicts L2
     # and the Infinity Cache (a separate, shorter pass; context beside the
@@ -755,6 +839,7 @@ def main():
         "check_max_err_ratio_8rows": check,
         "check_against": None if check is None else check_ref,
         "device": device,
+        "clock_in_kernels": clocks,
     }
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle")

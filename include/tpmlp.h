@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define TPM_ABI_VERSION 5
+#define TPM_ABI_VERSION 6
 
 /* Element types. */
 typedef enum {
@@ -123,6 +123,34 @@ size_t tp_mlp_shard_workspace_size(int64_t M, int64_t d, int64_t H, int N);
 int tp_mlp_shard(const void* X, const void* A, const void* B, void* Y_i, int y_dtype,
                  int64_t M, int64_t d, int64_t H, int N, int rank,
                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * ---------------------------------------------------------------------------
+ * Measurement calls: the forward's GEMM steps with per-workgroup clock stamps,
+ * so the shader clock the kernel actually ran at can be reported beside its
+ * throughput (the MFMA peak scales with that clock). Each is the production
+ * kernel of tp_mlp_col_gelu / tp_mlp_row_partial / tp_mlp_row_partial_e4m3
+ * (same tile choice, same results), given a stamps array: workgroup w writes
+ * stamps[4w .. 4w+3] = {shader-clock counter at its start, constant 100 MHz
+ * counter at its start, shader-clock counter once its stores have completed,
+ * 100 MHz counter then}. Entries of workgroups the launch does not have are
+ * left as they were (zero them first to count the workgroups).
+ * stamps : device, 16-byte aligned, stamp_count >= tp_clock_stamp_count(M, N)
+ *   values (M, N: rows and columns of the step's output), else
+ *   TPM_ERR_WORKSPACE; it must not overlap any other argument.
+ * ---------------------------------------------------------------------------
+ */
+int64_t tp_clock_stamp_count(int64_t M, int64_t N);
+int tp_mlp_col_gelu_stamped(const void* X, const void* A_i, int64_t lda, void* Z_i,
+                            int64_t M, int64_t d, int64_t F, uint64_t* stamps,
+                            int64_t stamp_count, void* stream);
+int tp_mlp_row_partial_stamped(const void* Z_i, const void* B_i, void* Y_i, int y_dtype,
+                               int64_t M, int64_t F, int64_t d, uint64_t* stamps,
+                               int64_t stamp_count, void* stream);
+int tp_mlp_row_partial_e4m3_stamped(const void* Zq, const float* sZ, const void* Bq_i,
+                                    const float* sB, void* Y_i, int64_t M, int64_t F,
+                                    int64_t d, uint64_t* stamps, int64_t stamp_count,
+                                    void* stream);
 
 /*
  * ---------------------------------------------------------------------------
@@ -286,6 +314,20 @@ int tp_partial_sum(const void* const* parts, int N, int part_dtype, void* Y, int
 int tp_partial_sum_rows(const void* const* parts, int N, int part_dtype, int64_t M, int64_t d,
                         int64_t row_begin, int64_t row_end, const void* bias, int bias_dtype,
                         void* Y, int y_dtype, void* stream);
+
+/*
+ * Rank `rank`'s share of the sequence-parallel reduce-scatter of the N
+ * partial outputs ("Megatron-LM deep architecture", sequence-parallel
+ * section: the AllReduce ending the block becomes a ReduceScatter, and each
+ * GPU keeps the sum over its 1/N of the sequence): tp_partial_sum_rows over
+ * rows [rank·M/N, (rank+1)·M/N), bias added once. Tokens are stored
+ * sequence-major ([S, B, H]), so that share is one contiguous row block.
+ * Arguments as tp_partial_sum_rows; Y is [M/N, d]. rank not in [0, N):
+ * TPM_ERR_ARG; M not divisible by N: TPM_ERR_SHAPE.
+ */
+int tp_reduce_scatter_share(const void* const* parts, int N, int part_dtype, int64_t M,
+                            int64_t d, int rank, const void* bias, int bias_dtype, void* Y,
+                            int y_dtype, void* stream);
 
 /* ------------------------------------------------------------------------
  * fp8 e4m3 variant ("Megatron-LM deep architecture", FP8 hybrid precision:

@@ -36,6 +36,8 @@ __all__ = [
     "tp_attn_qkv", "tp_attn_heads", "tp_attn_shard", "tp_attn_shard_workspace_size",
     "attn_workspace_views", "ATTN_HEAD_DIM", "fp8_backward_workspace_views",
     "TPM_BF16", "TPM_F32", "TPM_E4M3", "EXPORTED_SYMBOLS",
+    "tp_clock_stamp_count",
+    "tp_mlp_col_gelu_stamped", "tp_mlp_row_partial_stamped", "tp_mlp_row_partial_e4m3_stamped",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtpmlp.so")
@@ -95,12 +97,19 @@ _SIGNATURES = {
     "tp_mlp_shard_backward_fp8_workspace_size": (_sz, [_i64, _i64, _i64, _int]),
     "tp_mlp_shard_backward_fp8": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _i64,
                                          _int, _int, _vp, _vp, _sz, _vp]),
+    "tp_reduce_scatter_share": (_int, [ctypes.POINTER(_vp), _int, _int, _i64, _i64, _int, _vp, _int,
+                                       _vp, _int, _vp]),
+    "tp_clock_stamp_count": (_i64, [_i64, _i64]),
+    "tp_mlp_col_gelu_stamped": (_int, [_vp, _vp, _i64, _vp, _i64, _i64, _i64, _vp, _i64, _vp]),
+    "tp_mlp_row_partial_stamped": (_int, [_vp, _vp, _vp, _int, _i64, _i64, _i64, _vp, _i64, _vp]),
+    "tp_mlp_row_partial_e4m3_stamped": (_int, [_vp, _fp, _vp, _fp, _vp, _i64, _i64, _i64, _vp, _i64,
+                                               _vp]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGNATURES)
 
 
 # The entry-point signatures below are those of this ABI version of include/tpmlp.h.
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 
 def _load_library():
@@ -177,7 +186,7 @@ def _fptr(t: torch.Tensor) -> int:
 # --------------------------------------------------------------- bf16 path
 
 def tp_mlp_col_gelu(X: torch.Tensor, A_i: torch.Tensor, Z_i: torch.Tensor | None = None,
-                    stream=None) -> torch.Tensor:
+                    stream=None, stamps: torch.Tensor | None = None) -> torch.Tensor:
     """Z_i = bf16(GeLU(X·A_i)). X [M, d] bf16; A_i [d, F] bf16 (may be a column
     slice of a full A: unit column stride, any row stride)."""
     _need(X, "X", torch.bfloat16, 2)
@@ -193,9 +202,28 @@ def tp_mlp_col_gelu(X: torch.Tensor, A_i: torch.Tensor, Z_i: torch.Tensor | None
     _need(Z_i, "Z_i", torch.bfloat16, 2)
     if tuple(Z_i.shape) != (M, F):
         raise ValueError("Z_i has the wrong shape")
-    _check(lib.tp_mlp_col_gelu(X.data_ptr(), A_i.data_ptr(), A_i.stride(0), Z_i.data_ptr(),
-                               M, d, F, _stream(stream)), "tp_mlp_col_gelu")
+    if stamps is None:
+        _check(lib.tp_mlp_col_gelu(X.data_ptr(), A_i.data_ptr(), A_i.stride(0), Z_i.data_ptr(),
+                                   M, d, F, _stream(stream)), "tp_mlp_col_gelu")
+    else:
+        _need(stamps, "stamps", torch.int64, 1)
+        _check(lib.tp_mlp_col_gelu_stamped(X.data_ptr(), A_i.data_ptr(), A_i.stride(0),
+                                           Z_i.data_ptr(), M, d, F, stamps.data_ptr(),
+                                           stamps.numel(), _stream(stream)),
+               "tp_mlp_col_gelu_stamped")
     return Z_i
+
+
+def tp_clock_stamp_count(M: int, N: int) -> int:
+    """Length of the stamps array the clock-stamped calls need for an [M, N] output."""
+    return int(lib.tp_clock_stamp_count(M, N))
+
+
+def tp_mlp_col_gelu_stamped(X, A_i, stamps, Z_i=None, stream=None):
+    """tp_mlp_col_gelu with per-workgroup clock stamps in `stamps` (int64
+    [tp_clock_stamp_count(M, F)], device; 4 per workgroup: shader-clock and
+    100 MHz counters at the start and after the stores)."""
+    return tp_mlp_col_gelu(X, A_i, Z_i, stream, stamps=stamps)
 
 
 def tp_mlp_col_gelu_bias(X: torch.Tensor, A_i: torch.Tensor, b_i: torch.Tensor,
@@ -238,7 +266,8 @@ def _col_gelu_bias(X, A_i, b_i, Z_i, transposed, stream):
 
 
 def tp_mlp_row_partial(Z_i: torch.Tensor, B_i: torch.Tensor, Y_i: torch.Tensor | None = None,
-                       out_dtype=torch.float32, stream=None) -> torch.Tensor:
+                       out_dtype=torch.float32, stream=None,
+                       stamps: torch.Tensor | None = None) -> torch.Tensor:
     """Y_i = Z_i·B_i (fp32 or bf16). Z_i [M, F] bf16; B_i [F, d] bf16."""
     _need(Z_i, "Z_i", torch.bfloat16, 2)
     _need(B_i, "B_i", torch.bfloat16, 2)
@@ -251,10 +280,22 @@ def tp_mlp_row_partial(Z_i: torch.Tensor, B_i: torch.Tensor, Y_i: torch.Tensor |
     _need(Y_i, "Y_i", None, 2)
     if tuple(Y_i.shape) != (M, d):
         raise ValueError("Y_i has the wrong shape")
-    _check(lib.tp_mlp_row_partial(Z_i.data_ptr(), B_i.data_ptr(), Y_i.data_ptr(),
-                                  _dtype_code(Y_i.dtype), M, F, d, _stream(stream)),
-           "tp_mlp_row_partial")
+    if stamps is None:
+        _check(lib.tp_mlp_row_partial(Z_i.data_ptr(), B_i.data_ptr(), Y_i.data_ptr(),
+                                      _dtype_code(Y_i.dtype), M, F, d, _stream(stream)),
+               "tp_mlp_row_partial")
+    else:
+        _need(stamps, "stamps", torch.int64, 1)
+        _check(lib.tp_mlp_row_partial_stamped(Z_i.data_ptr(), B_i.data_ptr(), Y_i.data_ptr(),
+                                              _dtype_code(Y_i.dtype), M, F, d, stamps.data_ptr(),
+                                              stamps.numel(), _stream(stream)),
+               "tp_mlp_row_partial_stamped")
     return Y_i
+
+
+def tp_mlp_row_partial_stamped(Z_i, B_i, stamps, Y_i=None, out_dtype=torch.float32, stream=None):
+    """tp_mlp_row_partial with per-workgroup clock stamps (see tp_mlp_col_gelu_stamped)."""
+    return tp_mlp_row_partial(Z_i, B_i, Y_i, out_dtype, stream, stamps=stamps)
 
 
 def tp_mlp_shard_workspace_size(M: int, d: int, H: int, N: int) -> int:
@@ -422,16 +463,33 @@ def tp_reduce_scatter_share(parts, rank: int, bias: torch.Tensor | None = None,
                             Y: torch.Tensor | None = None, out_dtype=None,
                             stream=None) -> torch.Tensor:
     """Rank `rank`'s share of the sequence-parallel reduce-scatter: rows
-    [rank·M/N, (rank+1)·M/N) of Σ_i parts[i] (N = len(parts)), plus bias."""
+    [rank·M/N, (rank+1)·M/N) of Σ_i parts[i] (N = len(parts)), plus bias once."""
     parts = list(parts)
+    if not parts:
+        raise ValueError("no partials")
+    dt = parts[0].dtype
+    for i, p in enumerate(parts):
+        _need(p, f"parts[{i}]", dt, 2)
+        if p.shape != parts[0].shape:
+            raise ValueError("partials must be [M, d] tensors of one shape")
+    M, d = parts[0].shape
     N = len(parts)
-    if N < 1 or not (0 <= rank < N):
-        raise ValueError(f"rank {rank} not in [0, {N})")
-    M = parts[0].shape[0]
-    if M % N:
-        raise ValueError(f"{M} rows not divisible by N={N}")
-    R = M // N
-    return tp_partial_sum_rows(parts, rank * R, (rank + 1) * R, bias, Y, out_dtype, stream)
+    if Y is None:
+        Y = torch.empty((M // N if N else 0, d), dtype=out_dtype or dt, device=parts[0].device)
+    _need(Y, "Y", None)
+    bptr, bdt = None, TPM_F32
+    if bias is not None:
+        _need(bias, "bias", None)
+        if bias.numel() != d:
+            raise ValueError("bias must have d elements")
+        bptr, bdt = bias.data_ptr(), _dtype_code(bias.dtype)
+    if Y.numel() != (M // N) * d:
+        raise ValueError("Y has the wrong size")
+    arr = (_vp * N)(*[p.data_ptr() for p in parts])
+    _check(lib.tp_reduce_scatter_share(arr, N, _dtype_code(dt), M, d, rank, bptr, bdt, Y.data_ptr(),
+                                       _dtype_code(Y.dtype), _stream(stream)),
+           "tp_reduce_scatter_share")
+    return Y
 
 
 # ---------------------------------------------------------------- fp8 path
@@ -478,7 +536,7 @@ def tp_mlp_col_gelu_e4m3(Xq, sX, Aq_i, sA, Z_i=None, z_amax=None, stream=None):
     return Z_i
 
 
-def tp_mlp_row_partial_e4m3(Zq, sZ, Bq_i, sB, Y_i=None, stream=None):
+def tp_mlp_row_partial_e4m3(Zq, sZ, Bq_i, sB, Y_i=None, stream=None, stamps=None):
     _need(Zq, "Zq", torch.uint8, 2)
     _need(Bq_i, "Bq_i", torch.uint8, 2)
     M, F = Zq.shape
@@ -488,10 +546,23 @@ def tp_mlp_row_partial_e4m3(Zq, sZ, Bq_i, sB, Y_i=None, stream=None):
     if Y_i is None:
         Y_i = torch.empty((M, d), dtype=torch.bfloat16, device=Zq.device)
     _need(Y_i, "Y_i", torch.bfloat16, 2)
-    _check(lib.tp_mlp_row_partial_e4m3(Zq.data_ptr(), _fptr(sZ), Bq_i.data_ptr(), _fptr(sB),
-                                       Y_i.data_ptr(), M, F, d, _stream(stream)),
-           "tp_mlp_row_partial_e4m3")
+    if stamps is None:
+        _check(lib.tp_mlp_row_partial_e4m3(Zq.data_ptr(), _fptr(sZ), Bq_i.data_ptr(), _fptr(sB),
+                                           Y_i.data_ptr(), M, F, d, _stream(stream)),
+               "tp_mlp_row_partial_e4m3")
+    else:
+        _need(stamps, "stamps", torch.int64, 1)
+        _check(lib.tp_mlp_row_partial_e4m3_stamped(Zq.data_ptr(), _fptr(sZ), Bq_i.data_ptr(),
+                                                   _fptr(sB), Y_i.data_ptr(), M, F, d,
+                                                   stamps.data_ptr(), stamps.numel(),
+                                                   _stream(stream)),
+               "tp_mlp_row_partial_e4m3_stamped")
     return Y_i
+
+
+def tp_mlp_row_partial_e4m3_stamped(Zq, sZ, Bq_i, sB, stamps, Y_i=None, stream=None):
+    """tp_mlp_row_partial_e4m3 with per-workgroup clock stamps (see tp_mlp_col_gelu_stamped)."""
+    return tp_mlp_row_partial_e4m3(Zq, sZ, Bq_i, sB, Y_i, stream, stamps=stamps)
 
 
 def tp_mlp_shard_e4m3_workspace_size(M: int, d: int, H: int, N: int) -> int:

@@ -51,6 +51,25 @@ int check_dims(int64_t M, int64_t K, int64_t N, int64_t mult) {
 
 size_t round256(size_t b) { return (b + 255) & ~size_t(255); }
 
+// The clock-stamped measurement calls: the stamps array must hold
+// tp_clock_stamp_count(M, N) values (4 per workgroup of the largest grid any
+// tile choice makes for an [M, N] output).
+int check_stamps(const uint64_t* stamps, int64_t count, int64_t M, int64_t N) {
+  if (stamps == nullptr) return TPM_ERR_NULL;
+  if (!aligned16(stamps)) return TPM_ERR_ALIGN;
+  if (M < 0 || N < 0 || M > kMaxDim || N > kMaxDim) return TPM_ERR_SHAPE;
+  if (count < 4 * ((M + 127) / 128) * ((N + 127) / 128)) return TPM_ERR_WORKSPACE;
+  return TPM_OK;
+}
+
+int col_gelu_stamped(const void* X, const void* A_i, int64_t lda, void* Z_i, int64_t M,
+                     int64_t d, int64_t F, uint64_t* stamps, void* stream);
+int row_partial_stamped(const void* Z_i, const void* B_i, void* Y_i, int y_dtype, int64_t M,
+                        int64_t F, int64_t d, uint64_t* stamps, void* stream);
+int row_partial_e4m3_stamped(const void* Zq, const float* sZ, const void* Bq_i, const float* sB,
+                             void* Y_i, int64_t M, int64_t F, int64_t d, uint64_t* stamps,
+                             void* stream);
+
 }  // namespace
 
 extern "C" {
@@ -74,6 +93,49 @@ const char* tp_status_string(int status) {
 
 int tp_mlp_col_gelu(const void* X, const void* A_i, int64_t lda, void* Z_i, int64_t M,
                     int64_t d, int64_t F, void* stream) {
+  return col_gelu_stamped(X, A_i, lda, Z_i, M, d, F, nullptr, stream);
+}
+
+int tp_mlp_row_partial(const void* Z_i, const void* B_i, void* Y_i, int y_dtype, int64_t M,
+                       int64_t F, int64_t d, void* stream) {
+  return row_partial_stamped(Z_i, B_i, Y_i, y_dtype, M, F, d, nullptr, stream);
+}
+
+int64_t tp_clock_stamp_count(int64_t M, int64_t N) {
+  if (M < 0 || N < 0 || M > kMaxDim || N > kMaxDim) return 0;
+  return 4 * ((M + 127) / 128) * ((N + 127) / 128);
+}
+
+int tp_mlp_col_gelu_stamped(const void* X, const void* A_i, int64_t lda, void* Z_i, int64_t M,
+                            int64_t d, int64_t F, uint64_t* stamps, int64_t stamp_count,
+                            void* stream) {
+  int st = check_stamps(stamps, stamp_count, M, F);
+  if (st != TPM_OK) return st;
+  return col_gelu_stamped(X, A_i, lda, Z_i, M, d, F, stamps, stream);
+}
+
+int tp_mlp_row_partial_stamped(const void* Z_i, const void* B_i, void* Y_i, int y_dtype,
+                               int64_t M, int64_t F, int64_t d, uint64_t* stamps,
+                               int64_t stamp_count, void* stream) {
+  int st = check_stamps(stamps, stamp_count, M, d);
+  if (st != TPM_OK) return st;
+  return row_partial_stamped(Z_i, B_i, Y_i, y_dtype, M, F, d, stamps, stream);
+}
+
+int tp_mlp_row_partial_e4m3_stamped(const void* Zq, const float* sZ, const void* Bq_i,
+                                    const float* sB, void* Y_i, int64_t M, int64_t F, int64_t d,
+                                    uint64_t* stamps, int64_t stamp_count, void* stream) {
+  int st = check_stamps(stamps, stamp_count, M, d);
+  if (st != TPM_OK) return st;
+  return row_partial_e4m3_stamped(Zq, sZ, Bq_i, sB, Y_i, M, F, d, stamps, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+int col_gelu_stamped(const void* X, const void* A_i, int64_t lda, void* Z_i, int64_t M,
+                     int64_t d, int64_t F, uint64_t* stamps, void* stream) {
   int st = check_dims(M, d, F, 8);
   if (st != TPM_OK) return st;
   if (lda < F || lda > kMaxLd) return TPM_ERR_SHAPE;
@@ -86,11 +148,11 @@ int tp_mlp_col_gelu(const void* X, const void* A_i, int64_t lda, void* Z_i, int6
   return status_of(tpmlp::launch_gemm_bf16(static_cast<const uint16_t*>(X), d,
                                            static_cast<const uint16_t*>(A_i), lda, Z_i, F,
                                            (int)M, (int)F, (int)d, OutKind::GeluBf16,
-                                           as_stream(stream)));
+                                           as_stream(stream), stamps));
 }
 
-int tp_mlp_row_partial(const void* Z_i, const void* B_i, void* Y_i, int y_dtype, int64_t M,
-                       int64_t F, int64_t d, void* stream) {
+int row_partial_stamped(const void* Z_i, const void* B_i, void* Y_i, int y_dtype, int64_t M,
+                        int64_t F, int64_t d, uint64_t* stamps, void* stream) {
   if (y_dtype != TPM_F32 && y_dtype != TPM_BF16) return TPM_ERR_DTYPE;
   int st = check_dims(M, F, d, 8);
   if (st != TPM_OK) return st;
@@ -103,8 +165,12 @@ int tp_mlp_row_partial(const void* Z_i, const void* B_i, void* Y_i, int y_dtype,
   return status_of(tpmlp::launch_gemm_bf16(
       static_cast<const uint16_t*>(Z_i), F, static_cast<const uint16_t*>(B_i), d, Y_i, d,
       (int)M, (int)d, (int)F, y_dtype == TPM_F32 ? OutKind::F32 : OutKind::Bf16,
-      as_stream(stream)));
+      as_stream(stream), stamps));
 }
+
+}  // namespace
+
+extern "C" {
 
 size_t tp_mlp_shard_workspace_size(int64_t M, int64_t d, int64_t H, int N) {
   if (M < 0 || d <= 0 || H <= 0 || N < 1 || H % N != 0) return 0;
@@ -331,6 +397,18 @@ int tp_partial_sum_rows(const void* const* parts, int N, int part_dtype, int64_t
       bias ? (bias_dtype == TPM_F32 ? 1 : 2) : 0, d, as_stream(stream)));
 }
 
+int tp_reduce_scatter_share(const void* const* parts, int N, int part_dtype, int64_t M,
+                            int64_t d, int rank, const void* bias, int bias_dtype, void* Y,
+                            int y_dtype, void* stream) {
+  if (N < 1 || N > TPM_MAX_PARTS || rank < 0 || rank >= N) return TPM_ERR_ARG;
+  if (M < 0 || M % N != 0) return TPM_ERR_SHAPE;
+  // Rank j's share of the sequence-parallel reduce-scatter: with tokens stored
+  // sequence-major, its 1/N of the sequence is the row block [j·M/N, (j+1)·M/N).
+  const int64_t rows = M / N;
+  return tp_partial_sum_rows(parts, N, part_dtype, M, d, rank * rows, (rank + 1) * rows, bias,
+                             bias_dtype, Y, y_dtype, stream);
+}
+
 // ------------------------------------------------------------------ fp8 --
 
 int tp_amax_bf16(const void* T, int64_t numel, float* amax, void* stream) {
@@ -388,6 +466,16 @@ int tp_mlp_col_gelu_e4m3(const void* Xq, const float* sX, const void* Aq_i, int6
 
 int tp_mlp_row_partial_e4m3(const void* Zq, const float* sZ, const void* Bq_i, const float* sB,
                             void* Y_i, int64_t M, int64_t F, int64_t d, void* stream) {
+  return row_partial_e4m3_stamped(Zq, sZ, Bq_i, sB, Y_i, M, F, d, nullptr, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+int row_partial_e4m3_stamped(const void* Zq, const float* sZ, const void* Bq_i, const float* sB,
+                             void* Y_i, int64_t M, int64_t F, int64_t d, uint64_t* stamps,
+                             void* stream) {
   int st = check_dims(M, F, d, 16);
   if (st != TPM_OK) return st;
   if (M == 0) return TPM_OK;
@@ -400,8 +488,12 @@ int tp_mlp_row_partial_e4m3(const void* Zq, const float* sZ, const void* Bq_i, c
   return status_of(tpmlp::launch_gemm_e4m3(
       static_cast<const uint8_t*>(Zq), F, sZ, static_cast<const uint8_t*>(Bq_i), d, sB,
       static_cast<uint16_t*>(Y_i), d, nullptr, nullptr, (int)M, (int)d, (int)F, OutKind::Bf16,
-      as_stream(stream)));
+      as_stream(stream), stamps));
 }
+
+}  // namespace
+
+extern "C" {
 
 size_t tp_mlp_shard_e4m3_workspace_size(int64_t M, int64_t d, int64_t H, int N) {
   if (M < 0 || d <= 0 || H <= 0 || N < 1 || H % N != 0) return 0;

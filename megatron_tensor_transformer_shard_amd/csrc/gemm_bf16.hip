@@ -203,6 +203,7 @@ struct GemmArgs {
   const uint16_t* P; int64_t ldp; const uint16_t* Q; int64_t ldq; void* C; int64_t ldc;
   const float* aux; int64_t ldaux; void* C2; int M, N, K;
   const uint16_t* bias;  // GeluBiasBf16: bf16 [N], added to every row before GeLU
+  uint64_t* stamps;      // measurement only, else NULL: clock stamps per workgroup
 };
 
 // Workgroups [0, tiles0) compute problem g0, the rest problem g1 (a launch
@@ -228,6 +229,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs g0, GemmAr
   const bool second = id >= tiles0;
   const GemmArgs& g = second ? g1 : g0;
   if (second) id -= tiles0;
+  const ClockStamp stamp(g.stamps);
   const uint16_t* const P = g.P;
   const uint16_t* const Q = g.Q;
   void* const C = g.C;
@@ -438,6 +440,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs g0, GemmAr
         }
       }
     }
+    stamp.finish(g.stamps);
     return;
   }
   // GeluBiasBf16: the bias of the lane's four columns in each 16-column
@@ -487,6 +490,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs g0, GemmAr
       }
     }
   }
+  stamp.finish(g.stamps);
 }
 
 template <int BM, int BN>
@@ -553,6 +557,10 @@ TileChoice choose_tile(const GemmArgs* a, int n) {
       {256, 256, 1.00}, {256, 192, 0.85}, {256, 128, 0.62}, {128, 128, 0.30},
   };
   constexpr int kCus = 256;
+  int obm, obn;
+  if (tile_override(obm, obn))
+    for (const auto& c : cands)
+      if (c.bm == obm && c.bn == obn) return {obm, obn};
   double best = 1e300;
   TileChoice choice{256, 256};
   for (const auto& c : cands) {
@@ -610,9 +618,11 @@ hipError_t launch_gemm_bf16_pair(const BfGemm& x, const BfGemm& y, OutKind out, 
 
 hipError_t launch_gemm_bf16(const uint16_t* P, int64_t ldp, const uint16_t* Q, int64_t ldq,
                             void* C, int64_t ldc, int M, int N, int K, OutKind out,
-                            hipStream_t stream) {
-  return launch_gemm_bf16_ex(P, ldp, Q, ldq, C, ldc, M, N, K, out, Layout::NN, nullptr, 0,
-                             nullptr, stream);
+                            hipStream_t stream, uint64_t* stamps) {
+  if (M == 0 || N == 0) return hipSuccess;
+  GemmArgs a{P, ldp, Q, ldq, C, ldc, nullptr, 0, nullptr, M, N, K};
+  a.stamps = stamps;
+  return launch_group(&a, 1, out, Layout::NN, stream);
 }
 
 }  // namespace tpmlp

@@ -353,6 +353,7 @@ __global__ __launch_bounds__(kThreads) void gemm_e4m3_kernel(Fp8GemmArgs g0, Fp8
   const bool second = id >= tiles0;
   const Fp8GemmArgs& g = second ? g1 : g0;
   if (second) id -= tiles0;
+  const engine::ClockStamp stamp(g.stamps);
   const uint8_t* const P = g.P;
   const uint8_t* const Q = g.Q;
   const float* const sP = g.sP;
@@ -620,6 +621,7 @@ __global__ __launch_bounds__(kThreads) void gemm_e4m3_kernel(Fp8GemmArgs g0, Fp8
         }
       }
     }
+    stamp.finish(g.stamps);
     return;
   }
   if constexpr (OUT == (int)OutKind::GeluGradBf16) {
@@ -668,6 +670,7 @@ __global__ __launch_bounds__(kThreads) void gemm_e4m3_kernel(Fp8GemmArgs g0, Fp8
       }
     }
     block_max_to(smem, wave, lane, max_of(dsm), max_of(zm), z_amax, z_amax2);
+    stamp.finish(g.stamps);
     return;
   }
   const float sc = OUT == (int)OutKind::GeluE4m3 ? sC[0] : 1.0f;
@@ -699,6 +702,7 @@ __global__ __launch_bounds__(kThreads) void gemm_e4m3_kernel(Fp8GemmArgs g0, Fp8
     }
   }
   if (GELU && z_amax != nullptr) block_max_to(smem, wave, lane, max_of(zm), 0.0f, z_amax, nullptr);
+  stamp.finish(g.stamps);
 }
 
 }  // namespace e4
@@ -868,6 +872,10 @@ hipError_t launch_group(const Fp8GemmArgs* a, int n, OutKind out, int fp, int fq
       {256, 256, 1.00}, {256, 192, 0.85}, {128, 128, 0.30}};
   double best = 1e300;
   int pick = 0;
+  int forced = -1, obm, obn;
+  if (tile_override(obm, obn))
+    for (int c = 0; c < 3; ++c)
+      if (cands[c].bm == obm && cands[c].bn == obn) forced = c;
   for (int c = 0; c < 3; ++c) {
     long tiles = 0;
     for (int i = 0; i < n; ++i)
@@ -875,6 +883,7 @@ hipError_t launch_group(const Fp8GemmArgs* a, int n, OutKind out, int fp, int fq
     const double est = (double)((tiles + 255) / 256) * cands[c].cost;
     if (est < best - 1e-9) { best = est; pick = c; }
   }
+  if (forced >= 0) pick = forced;
   if (pick == 0) return launch_tile<256, 256>(a, n, out, fp, fq, stream);
   if (pick == 1) return launch_tile<256, 192>(a, n, out, fp, fq, stream);
   return launch_tile<128, 128>(a, n, out, fp, fq, stream);
@@ -907,9 +916,10 @@ hipError_t launch_gemm_fp8_pair(const Fp8GemmArgs& x, const Fp8GemmArgs& y, OutK
 hipError_t launch_gemm_e4m3(const uint8_t* P, int64_t ldp, const float* sP, const uint8_t* Q,
                             int64_t ldq, const float* sQ, void* C, int64_t ldc, float* z_amax,
                             const float* sC, int M, int N, int K, OutKind out,
-                            hipStream_t stream) {
-  const Fp8GemmArgs a{P, ldp, sP, Q, ldq, sQ, C, ldc, z_amax, sC, nullptr, 0, nullptr, nullptr,
-                      M, N, K};
+                            hipStream_t stream, uint64_t* stamps) {
+  Fp8GemmArgs a{P, ldp, sP, Q, ldq, sQ, C, ldc, z_amax, sC, nullptr, 0, nullptr, nullptr,
+                M, N, K};
+  a.stamps = stamps;
   return launch_gemm_fp8(a, out, 0, 0, stream, true);
 }
 

@@ -6,8 +6,26 @@
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
 
 namespace tpmlp {
+
+// Tile shape named by the environment variable TPMLP_TILE ("<BM>x<BN>", e.g.
+// "256x192"). The GEMM launchers take it instead of their own choice when it
+// names one of their instantiated shapes, so that tests can run every tile
+// shape on shapes small enough to check each output element against the
+// oracle. Unset or malformed: false, and the launchers choose as usual.
+inline bool tile_override(int& bm, int& bn) {
+  const char* s = getenv("TPMLP_TILE");
+  if (s == nullptr || *s == '\0') return false;
+  int a = 0, b = 0;
+  char tail = 0;
+  if (sscanf(s, "%dx%d%c", &a, &b, &tail) != 2) return false;
+  bm = a;
+  bn = b;
+  return true;
+}
 
 // Epilogues: GeluBf16 = bf16(GeLU(acc)); F32 = acc; Bf16 = bf16(acc);
 // GeluE4m3 (fp8 GEMM only): bf16(GeLU(acc)) quantised to e4m3 with a given
@@ -24,9 +42,11 @@ enum class Layout : int { NN = 0, QT = 1, PT = 2 };
 
 // C[M, N] = epilogue(P[M, K] · Q[K, N]); P rows K-contiguous (stride ldp),
 // Q rows N-contiguous (stride ldq), C dense with stride ldc, all bf16 inputs.
+// stamps (measurement only, else NULL): 4 clock stamps per workgroup, see
+// engine::ClockStamp; room for 4·⌈M/128⌉·⌈N/128⌉ values covers any tile.
 hipError_t launch_gemm_bf16(const uint16_t* P, int64_t ldp, const uint16_t* Q, int64_t ldq,
                             void* C, int64_t ldc, int M, int N, int K, OutKind out,
-                            hipStream_t stream);
+                            hipStream_t stream, uint64_t* stamps = nullptr);
 
 // The same GEMM with another operand layout and the backward's epilogue;
 // ldp / ldq are the row strides of P and Q as stored; aux/ldaux (fp32 S) and
@@ -98,6 +118,7 @@ struct Fp8GemmArgs {
   const float* aux; int64_t ldaux; void* C2; float* z_amax2;
   int M, N, K;
   const uint16_t* bias = nullptr;  // F32Bias: bf16 [N], added to every row after dequantising
+  uint64_t* stamps = nullptr;      // measurement only: clock stamps per workgroup (ClockStamp)
 };
 hipError_t launch_gemm_fp8(const Fp8GemmArgs& a, OutKind out, int fp, int fq,
                            hipStream_t stream, bool zero_amax = true);
@@ -120,7 +141,7 @@ hipError_t launch_quant_fp8_tile(int fmt, const uint16_t* T, int64_t ldt, int R,
 hipError_t launch_gemm_e4m3(const uint8_t* P, int64_t ldp, const float* sP, const uint8_t* Q,
                             int64_t ldq, const float* sQ, void* C, int64_t ldc, float* z_amax,
                             const float* sC, int M, int N, int K, OutKind out,
-                            hipStream_t stream);
+                            hipStream_t stream, uint64_t* stamps = nullptr);
 // Delayed scaling: record amax[0] in the ring history[L] at slot count % L,
 // advance count, and write next_scale[0] = 448 / mean of the recorded values
 // (the last min(count, L)), or 1 when that mean is 0.

@@ -71,5 +71,34 @@ __device__ __forceinline__ void barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Clock stamps of one workgroup, taken only when a measurement call passes a
+// stamps array (else the kernel is unchanged but for one uniform branch at
+// each end): the shader-clock counter (s_memtime) and the constant 100 MHz
+// counter (s_memrealtime) when the workgroup starts, and again once every
+// wave's stores have completed. Workgroup w writes
+// stamps[4w .. 4w+3] = {shader start, constant start, shader end, constant end},
+// so Δshader / Δconstant · 100 MHz is the shader clock the workgroup ran at.
+struct ClockStamp {
+  uint64_t shader0 = 0, wall0 = 0;
+  __device__ __forceinline__ explicit ClockStamp(const uint64_t* stamps) {
+    if (stamps != nullptr) {
+      shader0 = __builtin_amdgcn_s_memtime();
+      wall0 = __builtin_amdgcn_s_memrealtime();
+    }
+  }
+  __device__ __forceinline__ void finish(uint64_t* stamps) const {
+    if (stamps == nullptr) return;
+    waitcnt<0, 0>();
+    barrier();
+    if (threadIdx.x == 0) {
+      const uint64_t shader1 = __builtin_amdgcn_s_memtime();
+      const uint64_t wall1 = __builtin_amdgcn_s_memrealtime();
+      typedef __attribute__((ext_vector_type(4))) unsigned long long u64x4;
+      const u64x4 v = {shader0, wall0, shader1, wall1};
+      *reinterpret_cast<u64x4*>(stamps + 4 * (uint64_t)blockIdx.x) = v;
+    }
+  }
+};
+
 }  // namespace engine
 }  // namespace tpmlp

@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert tpm.abi_version() == tpm.ABI_VERSION == 5
+    assert tpm.abi_version() == tpm.ABI_VERSION == 6
     for code in (OK, ENULL, EARG, ESHAPE, EDTYPE, EALIGN, EWS, EALIAS, EHIP):
         s = tpm.status_string(code)
         assert s.startswith("TPM_")
@@ -291,6 +291,49 @@ def test_partial_sum_rows_validation():
     assert psum_rows(parts, Y=parts[1] + 128 * 4 * 8) == EALIAS   # inside parts[1]
     assert psum_rows(parts, rb=8, re=16, Y=parts[0]) == EALIAS     # not the block's first row
     assert psum_rows(parts, bias=BASE + 10 * GB + 64) == EALIAS    # bias overlaps Y
+
+
+def rs_share(parts, N=None, pd=F32, M=64, d=128, rank=1, bias=None, bd=F32, Y=BASE + 10 * GB,
+             yd=F32):
+    N = len(parts) if N is None else N
+    arr = (ctypes.c_void_p * max(1, len(parts)))(*parts)
+    return L.tp_reduce_scatter_share(arr, N, pd, M, d, rank, bias, bd, Y, yd, None)
+
+
+def test_reduce_scatter_share_validation():
+    parts = [BASE + i * GB for i in range(4)]
+    assert rs_share(parts, M=0) == OK                   # empty share: no-op
+    assert rs_share(parts, rank=4) == EARG
+    assert rs_share(parts, rank=-1) == EARG
+    assert rs_share(parts, N=0) == EARG
+    assert rs_share(parts, M=66) == ESHAPE              # 66 rows do not split over 4 ranks
+    assert rs_share(parts, d=100) == ESHAPE
+    assert rs_share(parts, pd=E4M3) == EDTYPE
+    assert rs_share(parts, Y=None) == ENULL
+    assert rs_share(parts, Y=BASE + 10 * GB + 8) == EALIGN
+    # rank 1's rows [16, 32) of parts[0] in place are allowed; rows of rank 0 are not
+    assert rs_share(parts, rank=0, Y=parts[0] + 16 * 128 * 4) == EALIAS
+
+
+def test_clock_stamp_validation():
+    assert L.tp_clock_stamp_count(8192, 4096) == 4 * 64 * 32
+    assert L.tp_clock_stamp_count(1, 1) == 4
+    assert L.tp_clock_stamp_count(-1, 4) == 0
+    st = BASE + 9 * GB
+    n = L.tp_clock_stamp_count(32, 256)
+    cg = lambda stamps=st, count=n, **kw: L.tp_mlp_col_gelu_stamped(
+        BASE, BASE + GB, 256, BASE + 2 * GB, 32, 64, 256, stamps, count, None)
+    assert cg(stamps=None) == ENULL
+    assert cg(count=n - 1) == EWS
+    assert cg(stamps=st + 8) == EALIGN
+    rp = lambda stamps=st, count=L.tp_clock_stamp_count(32, 64): L.tp_mlp_row_partial_stamped(
+        BASE, BASE + GB, BASE + 2 * GB, E4M3, 32, 128, 64, stamps, count, None)
+    assert rp() == EDTYPE                                 # the row step's own checks still apply
+    assert rp(count=3) == EWS
+    fp = lambda count=L.tp_clock_stamp_count(32, 64): L.tp_mlp_row_partial_e4m3_stamped(
+        BASE, BASE + 3 * GB, BASE + GB, BASE + 4 * GB, BASE + 2 * GB, 32, 128, 60, st, count, None)
+    assert fp() == ESHAPE                                 # d = 60 not a multiple of 16
+    assert fp(count=0) == EWS
 
 
 def test_fp8_validation():

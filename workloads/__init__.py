@@ -231,6 +231,20 @@ def make_integer_valued(M: int, d: int, H: int, seed: int, lo: int = -4, hi: int
     return bf16_bits_from_f32(X), bf16_bits_from_f32(A), bf16_bits_from_f32(B)
 
 
+def tile_rows(M: int, seed: int = 4321, tile: int = 256, per_tile: int = 4) -> np.ndarray:
+    """Sorted distinct row indices in [0, M) that hit every `tile`-row block of
+    the output: one row at a random offset inside each of its `per_tile` equal
+    parts (so every 256-, 128- and 64-row M-tile of the GEMM tilings is
+    sampled, at offsets that differ from block to block), plus rows 0 and M-1."""
+    rng = np.random.default_rng(seed)
+    part = tile // per_tile
+    rows = {0, M - 1}
+    for start in range(0, M, part):
+        n = min(part, M - start)
+        rows.add(start + int(rng.integers(0, n)))
+    return np.array(sorted(rows), dtype=np.int64)
+
+
 def sample_rows(M: int, count: int, seed: int = 1234) -> np.ndarray:
     """Sorted distinct row indices in [0, M), always including 0 and M-1."""
     rng = np.random.default_rng(seed)
