@@ -25,8 +25,10 @@
  *    are handled); M = 0 is a no-op that returns TPM_OK.
  *  - The caller owns every buffer and keeps it alive until the work on
  *    `stream` has finished. The library allocates nothing, keeps no pointers
- *    and has no global mutable state. Outputs are overwritten, never
- *    accumulated, and must not overlap any input (TPM_ERR_ALIAS).
+ *    and has no global mutable state, with one stated exception:
+ *    tp_mlp_shard_noalloc uses a static device array (and keeps its address
+ *    per device). Outputs are overwritten, never accumulated, and must not
+ *    overlap any input (TPM_ERR_ALIAS).
  *  - `stream` is a hipStream_t passed as void*; NULL means the default
  *    stream. Every call only enqueues work and returns; device faults surface
  *    at the caller's next synchronisation.
@@ -47,7 +49,7 @@
 extern "C" {
 #endif
 
-#define TPM_ABI_VERSION 6
+#define TPM_ABI_VERSION 7
 
 /* Element types. */
 typedef enum {
@@ -67,7 +69,8 @@ typedef enum {
   TPM_ERR_ALIGN = -5,     /* pointer not 16-byte aligned, row stride not 16-byte multiple */
   TPM_ERR_WORKSPACE = -6, /* workspace NULL or smaller than the size query returns */
   TPM_ERR_ALIAS = -7,     /* an output overlaps an input */
-  TPM_ERR_HIP = -8        /* a HIP launch failed */
+  TPM_ERR_HIP = -8,       /* a HIP launch failed */
+  TPM_ERR_SCRATCH = -9    /* tp_mlp_shard_noalloc: Z_i larger than its static scratch */
 } tpm_status;
 
 /* Largest number of partials tp_partial_sum accepts in one call. */
@@ -123,6 +126,24 @@ size_t tp_mlp_shard_workspace_size(int64_t M, int64_t d, int64_t H, int N);
 int tp_mlp_shard(const void* X, const void* A, const void* B, void* Y_i, int y_dtype,
                  int64_t M, int64_t d, int64_t H, int N, int rank,
                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Allocation-free form of tp_mlp_shard, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same arguments without the workspace, the same
+ * kernels and the same results, bit for bit. Z_i is kept in a static device
+ * array of TPM_NOALLOC_SCRATCH_BYTES that the library holds on each device it
+ * runs on until the process ends (its address is looked up on the first call
+ * on a device). The call allocates nothing. Z_i must fit:
+ * tp_mlp_shard_workspace_size(M, d, H, N) <= TPM_NOALLOC_SCRATCH_BYTES, else
+ * TPM_ERR_SCRATCH (checked on the host, nothing enqueued). Every call on one
+ * device shares that array: calls that overlap in time on one device (on
+ * different streams, or from several host threads without ordering) race on
+ * it and must not be issued. The array keeps the last call's Z_i.
+ */
+#define TPM_NOALLOC_SCRATCH_BYTES (64 * 1024 * 1024)
+int tp_mlp_shard_noalloc(const void* X, const void* A, const void* B, void* Y_i, int y_dtype,
+                         int64_t M, int64_t d, int64_t H, int N, int rank, void* stream);
 
 /*
  * ---------------------------------------------------------------------------

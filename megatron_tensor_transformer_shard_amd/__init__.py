@@ -36,7 +36,7 @@ __all__ = [
     "tp_attn_qkv", "tp_attn_heads", "tp_attn_shard", "tp_attn_shard_workspace_size",
     "attn_workspace_views", "ATTN_HEAD_DIM", "fp8_backward_workspace_views",
     "TPM_BF16", "TPM_F32", "TPM_E4M3", "EXPORTED_SYMBOLS",
-    "tp_clock_stamp_count",
+    "tp_mlp_shard_noalloc", "NOALLOC_SCRATCH_BYTES", "tp_clock_stamp_count",
     "tp_mlp_col_gelu_stamped", "tp_mlp_row_partial_stamped", "tp_mlp_row_partial_e4m3_stamped",
 ]
 
@@ -45,6 +45,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtpmlp.so
 TPM_BF16, TPM_F32, TPM_E4M3 = 0, 1, 2
 ATTN_HEAD_DIM = 128  # TPM_ATTN_HEAD_DIM
 TPM_MAX_PARTS = 64
+NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024  # TPM_NOALLOC_SCRATCH_BYTES
 
 _i64, _int, _vp, _sz = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
 _fp = ctypes.c_void_p  # float* (device)
@@ -99,6 +100,7 @@ _SIGNATURES = {
                                          _int, _int, _vp, _vp, _sz, _vp]),
     "tp_reduce_scatter_share": (_int, [ctypes.POINTER(_vp), _int, _int, _i64, _i64, _int, _vp, _int,
                                        _vp, _int, _vp]),
+    "tp_mlp_shard_noalloc": (_int, [_vp, _vp, _vp, _vp, _int, _i64, _i64, _i64, _int, _int, _vp]),
     "tp_clock_stamp_count": (_i64, [_i64, _i64]),
     "tp_mlp_col_gelu_stamped": (_int, [_vp, _vp, _i64, _vp, _i64, _i64, _i64, _vp, _i64, _vp]),
     "tp_mlp_row_partial_stamped": (_int, [_vp, _vp, _vp, _int, _i64, _i64, _i64, _vp, _i64, _vp]),
@@ -109,7 +111,7 @@ EXPORTED_SYMBOLS = tuple(_SIGNATURES)
 
 
 # The entry-point signatures below are those of this ABI version of include/tpmlp.h.
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 
 def _load_library():
@@ -326,6 +328,24 @@ def tp_mlp_shard(X: torch.Tensor, A: torch.Tensor, B: torch.Tensor, N: int, rank
                             _dtype_code(Y_i.dtype), M, d, H, N, rank, workspace.data_ptr(),
                             workspace.numel() * workspace.element_size(), _stream(stream)),
            "tp_mlp_shard")
+    return Y_i
+
+
+def tp_mlp_shard_noalloc(X: torch.Tensor, A: torch.Tensor, B: torch.Tensor, N: int, rank: int,
+                         Y_i: torch.Tensor, stream=None) -> torch.Tensor:
+    """tp_mlp_shard without a workspace: Z_i goes to the library's static
+    device scratch (NOALLOC_SCRATCH_BYTES per device), so the call allocates
+    nothing; the caller passes the output. Calls that overlap in time on one
+    device share that scratch and race."""
+    _need(X, "X", torch.bfloat16, 2)
+    _need(A, "A", torch.bfloat16, 2)
+    _need(B, "B", torch.bfloat16, 2)
+    _need(Y_i, "Y_i", None, 2)
+    M, d = X.shape
+    H = A.shape[1]
+    _check(lib.tp_mlp_shard_noalloc(X.data_ptr(), A.data_ptr(), B.data_ptr(), Y_i.data_ptr(),
+                                    _dtype_code(Y_i.dtype), M, d, H, N, rank, _stream(stream)),
+           "tp_mlp_shard_noalloc")
     return Y_i
 
 

@@ -8,6 +8,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <mutex>
 
 #include "kernels.hpp"
 
@@ -87,6 +88,9 @@ const char* tp_status_string(int status) {
     case TPM_ERR_WORKSPACE: return "TPM_ERR_WORKSPACE: workspace missing or too small";
     case TPM_ERR_ALIAS: return "TPM_ERR_ALIAS: an output overlaps an input";
     case TPM_ERR_HIP: return "TPM_ERR_HIP: a HIP launch failed";
+    case TPM_ERR_SCRATCH:
+      return "TPM_ERR_SCRATCH: Z_i would exceed the static scratch of tp_mlp_shard_noalloc "
+             "(TPM_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown tpmlp status";
   }
 }
@@ -407,6 +411,57 @@ int tp_reduce_scatter_share(const void* const* parts, int N, int part_dtype, int
   const int64_t rows = M / N;
   return tp_partial_sum_rows(parts, N, part_dtype, M, d, rank * rows, (rank + 1) * rows, bias,
                              bias_dtype, Y, y_dtype, stream);
+}
+
+}  // extern "C"
+
+// ------------------------------------------------- allocation-free shard --
+// Z_i of tp_mlp_shard_noalloc lives in this file-scope device array instead of
+// a caller's workspace. Each device holds its own copy (for the life of the
+// process); its address on a device is looked up once, with that device
+// current, and kept. Calls on one device share the array.
+namespace {
+
+static __device__ __align__(256) unsigned char scratch[TPM_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, or NULL on a HIP error.
+void* scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int tp_mlp_shard_noalloc(const void* X, const void* A, const void* B, void* Y_i, int y_dtype,
+                         int64_t M, int64_t d, int64_t H, int N, int rank, void* stream) {
+  // the same checks as tp_mlp_shard, before anything touches the device
+  if (y_dtype != TPM_F32 && y_dtype != TPM_BF16) return TPM_ERR_DTYPE;
+  if (N < 1 || rank < 0 || rank >= N) return TPM_ERR_ARG;
+  if (H <= 0 || H % N != 0) return TPM_ERR_SHAPE;
+  int st = check_dims(M, d, H / N, 8);
+  if (st != TPM_OK) return st;
+  if (H > kMaxLd || H * d > (int64_t(1) << 46)) return TPM_ERR_SHAPE;
+  if (M == 0) return TPM_OK;
+  if (!X || !A || !B || !Y_i) return TPM_ERR_NULL;
+  const size_t need = tp_mlp_shard_workspace_size(M, d, H, N);
+  if (need == 0 || need > (size_t)TPM_NOALLOC_SCRATCH_BYTES) return TPM_ERR_SCRATCH;
+  void* z = scratch_on_current_device();
+  if (z == nullptr) return TPM_ERR_HIP;
+  return tp_mlp_shard(X, A, B, Y_i, y_dtype, M, d, H, N, rank, z,
+                      (size_t)TPM_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 // ------------------------------------------------------------------ fp8 --

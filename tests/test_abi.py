@@ -12,7 +12,7 @@ import megatron_tensor_transformer_shard_amd as tpm
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "tpmlp.h")
 
-OK, ENULL, EARG, ESHAPE, EDTYPE, EALIGN, EWS, EALIAS, EHIP = 0, -1, -2, -3, -4, -5, -6, -7, -8
+OK, ENULL, EARG, ESHAPE, EDTYPE, EALIGN, EWS, EALIAS, EHIP, ESCRATCH = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
 BF16, F32, E4M3 = 0, 1, 2
 
 # Fake, never-dereferenced "device" addresses; validation only inspects them.
@@ -40,8 +40,8 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert tpm.abi_version() == tpm.ABI_VERSION == 6
-    for code in (OK, ENULL, EARG, ESHAPE, EDTYPE, EALIGN, EWS, EALIAS, EHIP):
+    assert tpm.abi_version() == tpm.ABI_VERSION == 7
+    for code in (OK, ENULL, EARG, ESHAPE, EDTYPE, EALIGN, EWS, EALIAS, EHIP, ESCRATCH):
         s = tpm.status_string(code)
         assert s.startswith("TPM_")
     assert "unknown" in tpm.status_string(12345)
@@ -313,6 +313,30 @@ def test_reduce_scatter_share_validation():
     assert rs_share(parts, Y=BASE + 10 * GB + 8) == EALIGN
     # rank 1's rows [16, 32) of parts[0] in place are allowed; rows of rank 0 are not
     assert rs_share(parts, rank=0, Y=parts[0] + 16 * 128 * 4) == EALIAS
+
+
+def noalloc(X=BASE, A=BASE + GB, B=BASE + 2 * GB, Y=BASE + 3 * GB, yd=F32, M=32, d=64, H=256,
+            N=2, rank=1):
+    return L.tp_mlp_shard_noalloc(X, A, B, Y, yd, M, d, H, N, rank, None)
+
+
+def test_noalloc_validation():
+    # every error below is found on the host before the device is touched
+    assert noalloc(M=0) == OK
+    assert noalloc(N=0) == EARG
+    assert noalloc(rank=2) == EARG
+    assert noalloc(N=3) == ESHAPE
+    assert noalloc(yd=E4M3) == EDTYPE
+    assert noalloc(X=None) == ENULL
+    assert noalloc(Y=None) == ENULL
+    # Z_i [M, F] bf16 must fit the 64 MiB scratch: 32768 x 1024 x 2 B = 64 MiB fits,
+    # one more row does not
+    assert tpm.NOALLOC_SCRATCH_BYTES == 64 << 20
+    big = dict(d=256, H=2048, N=2)
+    assert L.tp_mlp_shard_workspace_size(32768, 256, 2048, 2) == 64 << 20
+    assert noalloc(M=32769, **big) == ESCRATCH
+    assert noalloc(M=1 << 20, d=4096, H=16384, N=8) == ESCRATCH
+    assert "static scratch" in tpm.status_string(ESCRATCH)
 
 
 def test_clock_stamp_validation():
