@@ -226,7 +226,10 @@ def device_peak(tpm_peak_key):
         if hip.hipGetDevice(ctypes.byref(dev)) != 0:
             return None
         vals = {}
-        for name, attr in (("clock_khz", 5), ("cus", 63)):   # hipDeviceAttributeClockRate, ...MultiprocessorCount
+        # hipDeviceAttributeClockRate, ...MultiprocessorCount, ...ClockInstructionRate
+        # (the rate HIP states for the device-side clock counters), ...WallClockRate
+        for name, attr in (("clock_khz", 5), ("cus", 63), ("clock_instruction_rate_khz", 10000),
+                           ("wall_clock_rate_khz", 10017)):
             v = ctypes.c_int()
             if hip.hipDeviceGetAttribute(ctypes.byref(v), attr, dev) != 0:
                 return None
@@ -254,27 +257,31 @@ def wall_clock_hz():
         return None
 
 
-def clock_pass(tpm, stamped, reps=5):
-    """The shader clock inside each stamped kernel: the launch repeated `reps`
-    times (warm, back to back, as in the kernel pass), each workgroup's
-    shader-clock cycles over its constant-counter time. Per kernel: the median
-    of the workgroups' clocks over all launches, the span from the first
-    workgroup's start to the last one's end (the in-kernel duration, without
-    the launch overhead that HIP events include), and the cycles of that span
-    at the median clock."""
+def clock_pass(tpm, step, reps=5):
+    """The shader clock inside the stamped kernels under the benchmark's own
+    sustained load: `reps` ordinary steps back to back, with no
+    synchronisation between them, in which one rank's launches carry clock
+    stamps (the same kernels given a stamps array). For each workgroup, its
+    shader-clock cycles over its constant-counter time; per kernel, the median
+    over workgroups and launches, and the span from the first workgroup's start
+    to the last one's end (the in-kernel duration, without the launch overhead
+    that HIP events include)."""
     import torch
+    shapes = getattr(step, "stamp_shapes", None)
     hz = wall_clock_hz()
-    if hz is None:
+    if not shapes or hz is None:
         return None
+    bufs = [{k: torch.zeros(tpm.tp_clock_stamp_count(*mn), dtype=torch.int64, device="cuda")
+             for k, mn in shapes.items()} for _ in range(reps)]
+    torch.cuda.synchronize()
+    for b in bufs:
+        step(stamp=b)
+    torch.cuda.synchronize()
     out = {}
-    for name, ((m, n), fn) in stamped.items():
-        count = tpm.tp_clock_stamp_count(m, n)
+    for name in shapes:
         clocks, spans = [], []
-        for _ in range(reps):
-            st = torch.zeros(count, dtype=torch.int64, device="cuda")
-            fn(st)
-            torch.cuda.synchronize()
-            q = st.cpu().numpy().view(np.uint64).reshape(-1, 4)
+        for b in bufs:
+            q = b[name].cpu().numpy().view(np.uint64).reshape(-1, 4)
             q = q[np.any(q != 0, axis=1)].astype(np.float64)
             if len(q) == 0:
                 return None
@@ -312,10 +319,15 @@ def build_bf16_step(tpm, wl, partial_dtype, weight_layout="math"):
         views = [(Ad[:, r * F:(r + 1) * F], Bd[r * F:(r + 1) * F, :]) for r in range(N)]
         col, row, kc, kr = tpm.tp_mlp_col_gelu, tpm.tp_mlp_row_partial, "col_gelu", "row_partial"
 
-    def step(timer=None):
+    def step(timer=None, stamp=None):
         for r in range(N):
             A_i, B_i = views[r]
-            if timer is None:
+            # one middle rank's launches with clock stamps (rank 0's follow the
+            # previous step's partial sum and its 134 MB of fresh writes)
+            if stamp is not None and r == N // 2:
+                tpm.tp_mlp_col_gelu_stamped(Xd, A_i, stamp[kc], Z)
+                tpm.tp_mlp_row_partial_stamped(Z, B_i, stamp[kr], parts[r])
+            elif timer is None:
                 col(Xd, A_i, Z)
                 row(Z, B_i, parts[r])
             else:
@@ -328,12 +340,8 @@ def build_bf16_step(tpm, wl, partial_dtype, weight_layout="math"):
                 timer.around("partial_sum", lambda: tpm.tp_partial_sum(parts, Y=Y))
 
     if weight_layout != "linear":
-        # the same launches with per-workgroup clock stamps (rank 0's shard views)
-        A0, B0 = views[0]
-        step.stamped = {
-            kc: ((M, F), lambda st: tpm.tp_mlp_col_gelu_stamped(Xd, A0, st, Z)),
-            kr: ((M, d), lambda st: tpm.tp_mlp_row_partial_stamped(Z, B0, st, parts[0])),
-        }
+        # output shapes of the launches step(stamp=...) runs with clock stamps
+        step.stamp_shapes = {kc: (M, F), kr: (M, d)}
     kern_flops = {kc: 2 * M * d * F, kr: 2 * M * d * F}
     # algorithmic bytes: each operand read once, each output written once
     kern_bytes = {kc: (M * d + d * F) * 2 + M * F * 2,
@@ -465,11 +473,12 @@ def build_e4m3_step(tpm, wl):
         # predicted from the amax history; the step ends by recording its amax
         hist = tpm.AmaxHistory(1024, initial_scale=1.0)
 
-        def step(timer=None):
+        def step(timer=None, stamp=None):
+            st = None if stamp is None else stamp["row_partial_e4m3"]
             calls = [("col_gelu_e4m3_delayed",
                       lambda: tpm.tp_mlp_col_gelu_e4m3_delayed(Xq, sX, Aq, sA, hist.scale, Zq, za)),
                      ("row_partial_e4m3",
-                      lambda: tpm.tp_mlp_row_partial_e4m3(Zq, hist.scale, Bq, sB, Y)),
+                      lambda: tpm.tp_mlp_row_partial_e4m3(Zq, hist.scale, Bq, sB, Y, stamps=st)),
                      ("amax_history_push", lambda: hist.push(za))]
             for name, fn in calls:
                 if timer is None:
@@ -477,25 +486,25 @@ def build_e4m3_step(tpm, wl):
                 else:
                     timer.around(name, fn)
 
-        step.stamped = {"row_partial_e4m3": (
-            (M, d), lambda st: tpm.tp_mlp_row_partial_e4m3_stamped(Zq, hist.scale, Bq, sB, st, Y))}
+        step.stamp_shapes = {"row_partial_e4m3": (M, d)}
         kern_flops = {"col_gelu_e4m3_delayed": 2 * M * d * F, "row_partial_e4m3": 2 * M * d * F}
         kern_bytes = {"col_gelu_e4m3_delayed": M * d + d * F + M * F,
                       "row_partial_e4m3": M * F + F * d + M * d * 2}
         return step, kern_flops, kern_bytes, 0, (X, A, B), Y
 
-    def step(timer=None):
+    def step(timer=None, stamp=None):
+        st = None if stamp is None else stamp["row_partial_e4m3"]
         calls = [("col_gelu_e4m3", lambda: tpm.tp_mlp_col_gelu_e4m3(Xq, sX, Aq, sA, Z, za)),
                  ("quant_z", lambda: tpm.tp_quant_e4m3(Z, za, Zq, sZ)),
-                 ("row_partial_e4m3", lambda: tpm.tp_mlp_row_partial_e4m3(Zq, sZ, Bq, sB, Y))]
+                 ("row_partial_e4m3",
+                  lambda: tpm.tp_mlp_row_partial_e4m3(Zq, sZ, Bq, sB, Y, stamps=st))]
         for name, fn in calls:
             if timer is None:
                 fn()
             else:
                 timer.around(name, fn)
 
-    step.stamped = {"row_partial_e4m3": (
-        (M, d), lambda st: tpm.tp_mlp_row_partial_e4m3_stamped(Zq, sZ, Bq, sB, st, Y))}
+    step.stamp_shapes = {"row_partial_e4m3": (M, d)}
     return step, kern_flops, kern_bytes, 0, (X, A, B), Y
 
 
@@ -758,7 +767,7 @@ def main():
     # the shader clock inside the kernels, from the same kernels with clock
     # stamps (a separate pass, outside every timed region): the MFMA peak
     # scales with it, 4096 (bf16) or 8192 (fp8) flops per CU per clock
-    clocks = None if args.no_clock else clock_pass(tpm, getattr(step, "stamped", {}))
+    clocks = None if args.no_clock else clock_pass(tpm, step)
     per_clk = 8192 if dtype == "e4m3" else 4096
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     for name, c in (clocks or {}).items():
@@ -805,6 +814,8 @@ def main():
     dp = device_peak(dtype)
     if dp is not None:
         device["clock_khz"] = dp["clock_khz"]
+        device["clock_instruction_rate_khz"] = dp["clock_instruction_rate_khz"]
+        device["wall_clock_rate_khz"] = dp["wall_clock_rate_khz"]
         device["peak_from_props_tflops"] = round(dp["peak_tflops"], 1)
     sclk = clock.summary()
     if sclk is not None:   # the driver's figure, not the shader clock itself (it reads lower)
