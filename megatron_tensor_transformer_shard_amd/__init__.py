@@ -699,8 +699,12 @@ def tp_mlp_shard_backward(X, A, B, dY, N: int, rank: int, dX_i=None, dA_i=None, 
 
     Returns (dX_i, dA_i, dB_i, workspace): fp32 [M, d], [d, F], [F, d]; the
     workspace (uint8) holds S (fp32), dS and Z (bf16), [M, F] each, at the
-    offsets `backward_workspace_views` gives.
+    offsets `backward_workspace_views` gives. With the column layer's bias b1
+    the tuple has five entries, (dX_i, dA_i, dB_i, db1_i, workspace); db1_i
+    without b1 is an error (there is no bias gradient to write).
     """
+    if b1 is None and db1_i is not None:
+        raise ValueError("db1_i is given without b1")
     _need(X, "X", torch.bfloat16, 2)
     _need(A, "A", torch.bfloat16, 2)
     _need(B, "B", torch.bfloat16, 2)
@@ -894,7 +898,10 @@ def tp_mlp_shard_backward_fp8(X, A, B, dY, N: int, rank: int, dX_i=None, dA_i=No
     """Gradients of rank `rank`'s shard with hybrid fp8 GEMMs (E4M3 activations and
     weights, E5M2 gradients). w_amax: None, or a device float32 tensor of two
     values, max|A| and max|B| over the whole weights (then they are not
-    recomputed). Returns (dX_i, dA_i, dB_i, workspace)."""
+    recomputed). Returns (dX_i, dA_i, dB_i, workspace); with the column layer's
+    bias b1, (dX_i, dA_i, dB_i, db1_i, workspace). db1_i without b1 is an error."""
+    if b1 is None and db1_i is not None:
+        raise ValueError("db1_i is given without b1")
     for t, name in ((X, "X"), (A, "A"), (B, "B"), (dY, "dY")):
         _need(t, name, torch.bfloat16, 2)
     M, d = X.shape

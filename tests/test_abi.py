@@ -532,6 +532,16 @@ def test_python_wrapper_rejects_cpu_tensors():
         tpm.tp_mlp_col_gelu(X, torch.zeros(8, 8, dtype=torch.bfloat16))
 
 
+def test_backward_wrappers_refuse_a_bias_gradient_without_a_bias():
+    # db1_i with no b1 would never be written: refused before any tensor check
+    import torch
+    t = torch.zeros(4, 8, dtype=torch.bfloat16)
+    db = torch.zeros(8, dtype=torch.float32)
+    for fn in (tpm.tp_mlp_shard_backward, tpm.tp_mlp_shard_backward_fp8):
+        with pytest.raises(ValueError, match="db1_i is given without b1"):
+            fn(t, t, t, t, 1, 0, db1_i=db)
+
+
 def test_import_fails_loudly_without_the_library(tmp_path):
     """The package has no CPU fallback: with libtpmlp.so absent, importing it
     raises instead of silently computing elsewhere."""

@@ -236,36 +236,52 @@ def test_bias_grad_of_dy_vs_oracle(tpm):
     assert np.all(np.abs(host_f64(db2) - ref) <= M * U * mag)
 
 
-@pytest.mark.parametrize("M,d,H,N", [(272, 208, 2496, 3), (528, 272, 1088, 4)])
-def test_fp8_backward_with_bias_vs_oracle(tpm, M, d, H, N):
-    """The fp8 backward with the column bias: the scales as without it, db1_i
-    equal to the column sum of the GPU's own bf16 dS within the fp32
-    summation bound, and db1_i and the gradients within the fp8 bar of the
-    oracle."""
-    import torch
-    log(f"case fp8 backward with bias M={M} d={d} H={H} N={N}")
-    X, A, B = make_random(M, d, H, seed=13 * M + N, sigma=0.05)
-    b1 = make_bias(H, seed=M + 5, sigma=0.5)
-    dY = _dy(M, d, M + 6)
-    Xd, Ad, Bd, dYd, b1d = dev_bf16(X), dev_bf16(A), dev_bf16(B), dev_bf16(dY), dev_bf16(b1)
+def _fp8_bias_case(tpm, X, A, B, dY, b1, N, ranks, label):
+    """The fp8 backward with the column bias against the oracle: every check
+    of the unbiased fp8 backward (scales, codes, S with the bias add's
+    rounding, dS, Z, their codes, the gradients), db1_i equal to the column
+    sum of the GPU's own bf16 dS within the fp32 summation bound, and db1_i
+    within the fp8 bar of the oracle."""
+    from test_gpu_backward_fp8 import check_fp8_backward
+    M, d = X.shape
+    H = A.shape[1]
     F = H // N
-    for rank in sorted({0, N - 1}):
+    Xd, Ad, Bd, dYd, b1d = dev_bf16(X), dev_bf16(A), dev_bf16(B), dev_bf16(dY), dev_bf16(b1)
+    for rank in ranks:
         dX, dA, dB, db1, ws = tpm.tp_mlp_shard_backward_fp8_bias(Xd, Ad, b1d, Bd, dYd, N, rank)
         _sync()
         g = oracle.mlp_shard_backward_fp8(X, A, B, dY, N, rank, b1_bits=b1)
         v = tpm.fp8_backward_workspace_views(ws, M, d, F)
-        sc = v["scale"].cpu().numpy()
-        for i, k in enumerate(("sX", "sA", "sB", "sdY")):
-            assert np.float32(sc[i]) == np.float32(g[k]), f"rank {rank}: scale {k}"
+        lo, hi = oracle.shard_columns(H, N, rank)
+        what = f"{label} rank {rank}"
+        check_fp8_backward(what, v, g, dX, dA, dB, d, b1_block=oracle.bf16_decode(b1)[lo:hi])
         dSg = host_f64(v["dS"])
         dbg = host_f64(db1)
         assert np.all(np.abs(dbg - dSg.sum(axis=0)) <= M * U * np.abs(dSg).sum(axis=0) + 1e-30), \
-            f"rank {rank}: db1_i is not the column sum of dS"
-        for name, t, ref in (("db1", db1, g["db1"]), ("dX", dX, g["dX"]), ("dA", dA, g["dA"]),
-                             ("dB", dB, g["dB"])):
-            r = max_err_ratio(host_f64(t), ref)
-            log(f"rank {rank}: {name} err ratio {r:.3e}")
-            assert r <= 6e-2, f"rank {rank}: {name}"
+            f"{what}: db1_i is not the column sum of dS"
+        r = max_err_ratio(dbg, g["db1"])
+        log(f"{what}: db1 err ratio {r:.3e}")
+        assert r <= 6e-2, f"{what}: db1"
+
+
+@pytest.mark.parametrize("M,d,H,N", [(272, 208, 2496, 3), (528, 272, 1088, 4)])
+def test_fp8_backward_with_bias_vs_oracle(tpm, M, d, H, N):
+    log(f"case fp8 backward with bias M={M} d={d} H={H} N={N}")
+    X, A, B = make_random(M, d, H, seed=13 * M + N, sigma=0.05)
+    b1 = make_bias(H, seed=M + 5, sigma=0.5)
+    dY = _dy(M, d, M + 6)
+    _fp8_bias_case(tpm, X, A, B, dY, b1, N, sorted({0, N - 1}), "fp8 bias")
+
+
+def test_full_7b_tp8_fp8_backward_with_bias(tpm):
+    """One rank of the 7B-class shard (the 256x256 tiles) with the column bias."""
+    from workloads import make_output_grad
+    wl = WORKLOADS["7b_tp8_bwd"]
+    log(f"case {wl.name} fp8 with the column bias, rank 3")
+    X, A, B = make_inputs(wl)
+    dY = make_output_grad(wl.M, wl.d, wl.seed, wl.grad_sigma)
+    b1 = make_bias(wl.H, seed=wl.seed, sigma=0.5)
+    _fp8_bias_case(tpm, X, A, B, dY, b1, wl.N, (3,), wl.name)
 
 
 def test_fp8_backward_with_a_zero_bias_equals_the_unbiased_one(tpm):

@@ -197,3 +197,75 @@ def test_bias_mutant_is_caught(mutant, monkeypatch):
     monkeypatch.setattr(omlp, "col_gelu_bias", mutant)
     monkeypatch.setattr(oracle, "col_gelu_bias", mutant)
     assert _pins_fail(), f"{mutant.__name__} passed every pin"
+
+
+# -- the biased fp8 backward pinned to the biased bf16 backward ------------------
+# With integer inputs whose largest magnitude is 7, every scale is a power of
+# two (448/7 = 2^6 for e4m3, 57344/7 = 2^13 for e5m2) and every quantised code
+# is exact, so the fp8 backward computes the bf16 backward's S, dZ, dS and Z;
+# with the column bias (bf16, never quantised) it must then also match its
+# bias gradients. The bf16 biased backward is pinned by central differences
+# above, so this ties the fp8 bias path to the chain rule.
+
+def _sevens(M, d, H, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for shape in ((M, d), (d, H), (H, d), (M, d)):
+        v = rng.integers(-7, 8, size=shape).astype(np.float32)
+        v.flat[rng.integers(0, v.size)] = 7.0 * (1 if rng.integers(2) else -1)   # amax exactly 7
+        out.append(bf16_bits_from_f32(v))
+    return out
+
+
+def _fp8_bias_pin(M=24, d=32, H=128, N=4, rank=1, seed=90):
+    X, A, B, dY = _sevens(M, d, H, seed)
+    b1 = make_bias(H, seed=seed + 1, sigma=2.0)
+    g8 = oracle.mlp_shard_backward_fp8(X, A, B, dY, N, rank, b1_bits=b1)
+    assert (g8["sX"], g8["sA"], g8["sB"], g8["sdY"]) == (64.0, 64.0, 64.0, 8192.0)
+    g16 = oracle.mlp_shard_backward(X, A, B, dY, N, rank, b1_bits=b1)
+    for k8, k16 in (("S", "S"), ("dZ", "dZ")):
+        assert np.array_equal(g8[k8], g16[k16]), k8
+    assert np.array_equal(oracle.bf16_decode(g8["dS_bits"]), g16["dS"]), "dS"
+    assert np.array_equal(oracle.bf16_decode(g8["Z_bits"]), g16["Z"]), "Z"
+    assert np.array_equal(g8["db1"], g16["db1"]), "db1"
+    assert np.array_equal(g8["db2"], g16["db2"]), "db2"
+
+
+def test_fp8_backward_with_bias_equals_bf16_backward_on_exact_codes():
+    _fp8_bias_pin()
+    _fp8_bias_pin(M=40, d=48, H=96, N=3, rank=2, seed=91)
+
+
+_real_fp8_bwd = oracle.mlp_shard_backward_fp8
+
+
+def _db1_from_e5m2(X, A, B, dY, N, rank, b1_bits=None):
+    g = _real_fp8_bwd(X, A, B, dY, N, rank, b1_bits=b1_bits)
+    if b1_bits is not None:
+        g["db1"] = (oracle.e5m2_decode(g["dSq"]) / float(g["sdS"])).sum(axis=0)
+    return g
+
+
+def _bias_quantised(X, A, B, dY, N, rank, b1_bits=None):
+    if b1_bits is None:
+        return _real_fp8_bwd(X, A, B, dY, N, rank)
+    q, s = oracle.quantize_inputs_e4m3(b1_bits)
+    b1q = bf16_bits_from_f32((oracle.e4m3_decode(q) / float(s)).astype(np.float32))
+    return _real_fp8_bwd(X, A, B, dY, N, rank, b1_bits=b1q)
+
+
+def _bias_before_dequantising(X, A, B, dY, N, rank, b1_bits=None):
+    if b1_bits is None:
+        return _real_fp8_bwd(X, A, B, dY, N, rank)
+    # S = (Xq·Aq + b1)/(sX·sA): the bias divided by the scales' product
+    sX = oracle.quantize_inputs_e4m3(X)[1]
+    sA = oracle.quantize_inputs_e4m3(A)[1]
+    b = oracle.bf16_decode(b1_bits) / (float(sX) * float(sA))
+    return _real_fp8_bwd(X, A, B, dY, N, rank, b1_bits=bf16_bits_from_f32(b.astype(np.float32)))
+
+
+@pytest.mark.parametrize("mutant", [_db1_from_e5m2, _bias_quantised, _bias_before_dequantising])
+def test_fp8_bias_mutant_is_caught(mutant, monkeypatch):
+    monkeypatch.setattr(oracle, "mlp_shard_backward_fp8", mutant)
+    with pytest.raises(AssertionError):
+        _fp8_bias_pin()
