@@ -19,14 +19,21 @@
 //    registers): each wave instruction fills 1 KB of LDS contiguously, and
 //    each lane picks the 16-byte granule of HBM that belongs at its LDS
 //    position, which is how the LDS layouts below are realised.
+//  - The MFMA's k order: in k-step s (of 2 per slice) lane group
+//    g = lane >> 4 holds slice k-values 16g + 8s .. 16g + 8s + 7 of its row
+//    or column (any k order is valid when both operands use it). Taking
+//    16-byte chunk 2g + s rather than 4s + g keeps the two 16-lane groups of
+//    each 32-lane half of a ds_read_b128 on different chunks of rows four
+//    apart, which share banks: with chunk 4s + g the P reads stalled 4 cycles
+//    each on bank conflicts (SQ_LDS_BANK_CONFLICT on MI355X).
 //  - P slice: K-contiguous 128-byte rows, 16-byte chunk c of row r stored at
 //    c ^ ((r & 7) ^ ((r >> 3) & 1)). B-operand fragment (16 rows x 32 k):
-//    one ds_read_b128 per lane (row = lane & 15, chunk 4s + lane >> 4).
+//    one ds_read_b128 per lane (row = lane & 15, chunk 2(lane >> 4) + s).
 //  - Q slice: N-contiguous rows as in HBM; granule g of row r stored at
 //    (g + rot(r)) mod (BN/8), a row-dependent rotation that spreads the 8
 //    rows a 32-lane half of a transposing read touches over distinct banks.
 //    A-operand fragment (16 columns x 32 k): two ds_read_b64_tr_b16 per lane;
-//    in each 16-lane group lane L addresses k-row 8g + 4h + (L >> 2) at
+//    in each 16-lane group lane L addresses k-row 16g + 8s + 4h + (L >> 2) at
 //    columns 4(L & 3) .. +3 and receives column L of the 4 rows.
 //  - Three LDS stages for P and two for Q (3 x 32 + 2 x 32 KB = 160 KB for a
 //    256 x 256 tile), one barrier per slice. Slice kt: k-step 0 (reads the
@@ -77,14 +84,14 @@ typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 // Granule rotation of Q row `row` (GR granules of 16 bytes per row). A
 // 32-lane half of a ds_read_b64_tr_b16 reads 2 adjacent granules of rows
-// {0,1,2,3, 8,9,10,11} (+ a multiple of 4); with 512- or 256-byte rows
+// {0,1,2,3, 16,17,18,19} (+ a multiple of 4); with 512- or 256-byte rows
 // (GR = 32, 16) every row starts at bank 0, so those rows are spread by
 // 32 bytes each; with 384-byte rows (GR = 24) odd rows already start half a
 // bank row later, so rows are only spread by 32 bytes per row pair.
 template <int GR>
 __device__ __forceinline__ int q_rot(int row) {
-  if constexpr (GR % 16 == 0) return 2 * (row & 3) + 8 * ((row >> 3) & 1);
-  else return 2 * ((row >> 1) & 1) + 4 * ((row >> 3) & 1);
+  if constexpr (GR % 16 == 0) return 2 * (row & 3) + 8 * ((row >> 4) & 1);
+  else return 2 * ((row >> 1) & 1) + 4 * ((row >> 4) & 1);
 }
 
 // One operand's slice in LDS and its DMA, tail clearing and fragment reads.
@@ -168,23 +175,23 @@ __device__ __forceinline__ int frag_addr(int fb, int lane) {
     return fb;
   } else {
     constexpr int GR = W / 8;
-    // every k-row a lane reads is 32s + 4h + rsub, whose rotation (bits 0, 1
-    // and 3 of the row) equals that of rsub
-    const int rsub = 8 * (lane >> 4) + ((lane & 15) >> 2);
+    // every k-row a lane reads is 8s + 4h + rsub, whose rotation (bits 0, 1
+    // and 4 of the row) equals that of rsub
+    const int rsub = 16 * (lane >> 4) + ((lane & 15) >> 2);
     return rsub * (2 * W) + ((((fb + 4 * (lane & 3)) >> 3) + q_rot<GR>(rsub)) % GR) * 16 +
            8 * (lane & 1);
   }
 }
 
 // Lane part of a K-major fragment address for k-step s: row lane & 15 of the
-// fragment, chunk swz_p(row, 4s + (lane >> 4)).
+// fragment, chunk swz_p(row, 2(lane >> 4) + s).
 __device__ __forceinline__ int kmaj_lane_off(int lane, int s) {
-  return (lane & 15) * (kBK * 2) + swz_p<kBK / 8>(lane & 15, 4 * s + (lane >> 4)) * 16;
+  return (lane & 15) * (kBK * 2) + swz_p<kBK / 8>(lane & 15, 2 * (lane >> 4) + s) * 16;
 }
 
 // Piece h (of Operand::READS) of the fragment at `fa` (from frag_addr) for
 // k-step s of stage sp: K-major, one ds_read_b128; MN-major, k-rows
-// 32s + 4h + rsub by a transposing read.
+// 8s + 4h + rsub by a transposing read.
 template <int W, bool KMAJ>
 __device__ __forceinline__ void read_frag(const uint8_t* sp, int fa, int s, int h, int lane,
                                           s16x8& f) {
@@ -192,7 +199,7 @@ __device__ __forceinline__ void read_frag(const uint8_t* sp, int fa, int s, int 
     f = *reinterpret_cast<const s16x8*>(sp + fa * (kBK * 2) + kmaj_lane_off(lane, s));
   } else {
     const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_s16x4*)(sp + fa + (32 * s + 4 * h) * (2 * W)));
+        (lds_s16x4*)(sp + fa + (8 * s + 4 * h) * (2 * W)));
     if (h == 0) f.lo = v; else f.hi = v;
   }
 }
@@ -273,8 +280,8 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs g0, GemmAr
     op_q.clear(smem + Q_BASE + (last % NSQ) * Q_BYTES, K - k_last, t);
   };
 
-  // Fragment addressing (k-step s covers k 32s .. 32s+31 of the slice; lane
-  // group g = lane >> 4 holds k 8g .. 8g+7 of its row or column).
+  // Fragment addressing (in k-step s lane group g = lane >> 4 holds slice
+  // k-values 16g + 8s .. 16g + 8s + 7 of its row or column).
   int p_addr[MT], q_addr[NT];
 #pragma unroll
   for (int mi = 0; mi < MT; ++mi) p_addr[mi] = frag_addr<BM, !PT>(wm * TM + mi * 16, lane);
