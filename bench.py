@@ -122,6 +122,11 @@ def dev_bf16(bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
 
 
+# spin cycles (shader clock) queued before each step of an event-timed pass:
+# 2-5 ms at the clocks a loaded MI355X runs at
+LEAD_CYCLES = 6_000_000
+
+
 class KernelTimer:
     """HIP events recorded on the current stream around each launch."""
 
@@ -649,6 +654,7 @@ def library_compare(tpm, args):
         torch.cuda.synchronize()
         timer = KernelTimer()
         for _ in range(args.steps):
+            torch.cuda._sleep(LEAD_CYCLES)
             for name, fn in calls.items():
                 timer.around(name, fn)
         torch.cuda.synchronize()
@@ -670,6 +676,7 @@ def copy_calibration(tpm, args):
     torch.cuda.synchronize()
     timer = KernelTimer()
     for _ in range(args.steps):
+        torch.cuda._sleep(LEAD_CYCLES)
         timer.around("copy", lambda: tpm.tp_partial_sum([src], Y=dst))
     torch.cuda.synchronize()
     st = timer.summary()["copy"]
@@ -733,10 +740,14 @@ def main():
     log(f"bench: {args.steps} steps, {ms_per_step:.3f} ms/step, {value:.1f} TFLOP/s")
 
     # per-kernel timing with events on the launch stream (separate pass), with
-    # the engine clock sampled meanwhile
+    # the engine clock sampled meanwhile. Before each step a spin kernel of a
+    # few milliseconds (outside every event pair) lets the host queue the
+    # step's launches ahead of the GPU: an event pair around a launch that the
+    # host has not yet queued would also time the host's delay.
     timer = KernelTimer()
     with ClockSampler() as clock:
         for _ in range(args.steps):
+            torch.cuda._sleep(LEAD_CYCLES)
             step(timer)
         torch.cuda.synchronize()
     kstats = timer.summary()
@@ -788,6 +799,7 @@ def main():
     cold = None if args.no_cold else {}
     cold_timer = None if args.no_cold else ColdTimer()
     for _ in range(0 if args.no_cold else min(args.steps, 5)):
+        torch.cuda._sleep(LEAD_CYCLES)
         step(cold_timer)
     torch.cuda.synchronize()
     for name, st in ({} if args.no_cold else cold_timer.summary()).items():
