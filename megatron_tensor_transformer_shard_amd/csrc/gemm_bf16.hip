@@ -44,9 +44,15 @@
 //    interleaved one by one with the MFMAs. A DMA instruction whose address
 //    unit is busy stalls the wave's in-order issue, so splitting a slice's
 //    DMA over both k-steps halves the burst each k-step carries.
-//  - The main loop is uniform: past the last slice the DMA reloads the last
-//    slice into stages that are not read again, so every MFMA has exactly
-//    one call site and the accumulators stay in AGPRs without copies.
+//  - The main loop has no tail: past the last slice the DMA reloads the last
+//    slice into stages that are not read again. Its stage indices cost
+//    instructions on the loop's critical path: they come from a phase counter
+//    (kt mod 6, no division), the K-major reads add immediate offsets to one
+//    VGPR base per k-step, and where the compiler still keeps the
+//    accumulators in place with two slices per iteration (every tile but
+//    256 x 256) an even slice count takes that form, whose Q stages are
+//    constants. (Measured on MI355X: a loop whose stage indices were all
+//    constants took about 300 of its 2600 cycles per slice fewer.)
 //  - Rows of P beyond M and columns of Q beyond N are loaded from clamped
 //    addresses (their outputs are discarded). When K is not a multiple of 64
 //    (KTAIL), the last slice loads k clamped into [k_last, K) and the k >= K
@@ -216,7 +222,7 @@ struct GemmArgs {
 // Workgroups [0, tiles0) compute problem g0, the rest problem g1 (a launch
 // of one problem passes tiles0 = its tile count). Both share the template
 // arguments (tile, epilogue, layouts, KTAIL).
-template <int BM, int BN, int OUT, bool KTAIL, bool PT, bool QT>
+template <int BM, int BN, int OUT, bool KTAIL, bool PT, bool QT, bool PAIR>
 __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs g0, GemmArgs g1,
                                                              int tiles0, int group_m) {
   constexpr int BK = kBK, NSP = kNSP, NSQ = kNSQ;
@@ -295,18 +301,45 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs g0, GemmAr
   // idx-th fragment read of k-step s of the slice in stages (pst, qst) into
   // buffer buf; ordered so that the next k-step's first MFMAs (Q fragment 0
   // with every P fragment) find their operands first.
-  auto read_one = [&](int pst, int qst, int s, int buf, int idx) __attribute__((always_inline)) {
+  // A K-major operand's fragment reads share one VGPR base per k-step: the
+  // stage's LDS offset, the wave's first row and the lane's row and chunk;
+  // each fragment adds its rows as an immediate offset. (Formed opaquely, so
+  // that the compiler does not fold the wave's rows into a per-fragment
+  // scalar and re-add it with a VALU op before every read.)
+  auto kmaj_base = [&](uint32_t stage_off, int wrow0, int s) __attribute__((always_inline)) {
+    uint32_t o = stage_off + (uint32_t)(wrow0 * (kBK * 2) + kmaj_lane_off(lane, s));
+    asm("" : "+v"(o));
+    return smem + o;
+  };
+  auto read_one = [&](int pst, int qst, int s, int buf, int idx, const uint8_t* pk,
+                      const uint8_t* qk) __attribute__((always_inline)) {
     const uint8_t* sp = smem + pst * P_BYTES;
     const uint8_t* sq = smem + Q_BASE + qst * Q_BYTES;
+    auto read_q = [&](int ni, int h) __attribute__((always_inline)) {
+      if constexpr (QT) {
+        afr[buf][ni] = *reinterpret_cast<const s16x8*>(qk + ni * 16 * (kBK * 2));
+      } else {
+        read_frag<BN, false>(sq, q_addr[ni], s, h, lane, afr[buf][ni]);
+      }
+    };
     if (idx < RQ) {
-      read_frag<BN, QT>(sq, q_addr[0], s, idx, lane, afr[buf][0]);
+      read_q(0, idx);
     } else if (idx < RQ + MT * RP) {
       const int j = idx - RQ, mi = j / RP;
-      read_frag<BM, !PT>(sp, p_addr[mi], s, j % RP, lane, bfr[buf][mi]);
+      if constexpr (!PT) {
+        bfr[buf][mi] = *reinterpret_cast<const s16x8*>(pk + mi * 16 * (kBK * 2));
+      } else {
+        read_frag<BM, false>(sp, p_addr[mi], s, j % RP, lane, bfr[buf][mi]);
+      }
     } else {
       const int j = idx - RQ - MT * RP, ni = 1 + j / RQ;
-      read_frag<BN, QT>(sq, q_addr[ni], s, j % RQ, lane, afr[buf][ni]);
+      read_q(ni, j % RQ);
     }
+  };
+  auto read_bases = [&](int pst, int qst, int s, const uint8_t*& pk, const uint8_t*& qk)
+                        __attribute__((always_inline)) {
+    pk = PT ? nullptr : kmaj_base(pst * P_BYTES, wm * TM, s);
+    qk = QT ? kmaj_base(Q_BASE + qst * Q_BYTES, wn * TN, s) : nullptr;
   };
 
   f32x4 acc[NT][MT];
@@ -325,6 +358,8 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs g0, GemmAr
                 "one MFMA slot per read and DMA");
   auto kstep = [&](int cur, int rp, int rq, int rs, bool dq, int dkt, int dst)
                    __attribute__((always_inline)) {
+    const uint8_t *pk, *qk;
+    read_bases(rp, rq, rs, pk, qk);
 #pragma unroll
     for (int i = 0; i < NMFMA; ++i) {
       const int ni = i / MT, mi = i % MT;
@@ -333,7 +368,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs g0, GemmAr
           acc[ni][mi], 0, 0, 0);
 #pragma unroll
       for (int j = 0; j < NREADS; ++j)
-        if (j * NMFMA / NREADS == i) read_one(rp, rq, rs, cur ^ 1, j);
+        if (j * NMFMA / NREADS == i) read_one(rp, rq, rs, cur ^ 1, j, pk, qk);
       if (!dq) {
 #pragma unroll
         for (int j = 0; j < P_ROUNDS; ++j)
@@ -365,8 +400,12 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs g0, GemmAr
     waitcnt<63, 0>();
     barrier();
   }
+  {
+    const uint8_t *pk, *qk;
+    read_bases(0, 0, 0, pk, qk);
 #pragma unroll
-  for (int i = 0; i < NREADS; ++i) read_one(0, 0, 0, 0, i);
+    for (int i = 0; i < NREADS; ++i) read_one(0, 0, 0, 0, i, pk, qk);
+  }
 
   // Slice kt lives in P stage kt % 3 and Q stage kt % 2. Its fragments are
   // all read by the end of its first k-step. The P part of slice kt+2 is
@@ -376,9 +415,8 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs g0, GemmAr
   // has passed). So each k-step carries half of a slice's DMA instructions.
   // Near the end the DMA reloads the last slice into stages that are never
   // read again.
-  for (int kt = 0; kt < ktiles; ++kt) {
-    const int qs = kt & 1;
-    const int ps = kt % 3, ps1 = (kt + 1) % 3, ps2 = (kt + 2) % 3;
+  auto slice = [&](int kt, int ps, int qs) __attribute__((always_inline)) {
+    const int ps1 = ps == 2 ? 0 : ps + 1, ps2 = ps == 0 ? 2 : ps - 1;
     kstep(0, ps, qs, 1, false, min(kt + 2, last), ps2);
     waitcnt<P_ROUNDS, 0>();  // slice kt+1 has landed (only the P part of kt+2 may be in flight)
     barrier();               // every wave is done reading the stages of slice kt
@@ -388,6 +426,22 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs g0, GemmAr
       barrier();
     }
     kstep(1, ps1, qs ^ 1, 0, true, min(kt + 2, last), qs);
+  };
+  if constexpr (PAIR) {
+    // Two slices per iteration (ktiles is even), so that the Q stage of
+    // every read and DMA is a constant; ph = kt % 3.
+    int ph = 0;
+    for (int kt = 0; kt < ktiles; kt += 2) {
+      slice(kt, ph, 0);
+      slice(kt + 1, ph == 2 ? 0 : ph + 1, 1);
+      ph = ph == 0 ? 2 : ph - 1;
+    }
+  } else {
+    int ph = 0;  // kt % 6
+    for (int kt = 0; kt < ktiles; ++kt) {
+      slice(kt, ph >= 3 ? ph - 3 : ph, ph & 1);
+      ph = ph == 5 ? 0 : ph + 1;
+    }
   }
   waitcnt<0, 0>();  // no DMA may still write LDS when the workgroup ends
 
@@ -506,13 +560,28 @@ int tile_count(const GemmArgs& a) {
 }
 
 // One launch over problems a[0 .. n) (n = 1 or 2).
+// The main loop takes two slices per iteration when every problem of the
+// launch has an even number of slices, except at 256 x 256 (its 64
+// accumulator quadruples fill the 256 AGPRs, and with four MFMA call sites per
+// accumulator the compiler no longer keeps them in place: it moves them
+// through VGPRs inside the loop) and with the M-major P operand (the same
+// happens at 256 x 192).
 template <int BM, int BN, int OUT, bool KTAIL, bool PT, bool QT>
 hipError_t launch_one(const GemmArgs* a, int n, hipStream_t stream) {
   const int t0 = tile_count<BM, BN>(a[0]);
   const int tiles = t0 + (n > 1 ? tile_count<BM, BN>(a[1]) : 0);
   const int group_m = 4;
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, OUT, KTAIL, PT, QT>), dim3(tiles), dim3(kThreads), 0,
-                     stream, a[0], n > 1 ? a[1] : a[0], t0, group_m);
+  const GemmArgs& a1 = n > 1 ? a[1] : a[0];
+  const bool even = ((a[0].K + kBK - 1) / kBK) % 2 == 0 && ((a1.K + kBK - 1) / kBK) % 2 == 0;
+  if constexpr (!(BM == 256 && BN == 256) && !PT) {
+    if (even) {
+      hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, OUT, KTAIL, PT, QT, true>), dim3(tiles),
+                         dim3(kThreads), 0, stream, a[0], a1, t0, group_m);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, OUT, KTAIL, PT, QT, false>), dim3(tiles),
+                     dim3(kThreads), 0, stream, a[0], a1, t0, group_m);
   return hipGetLastError();
 }
 

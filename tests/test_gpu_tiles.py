@@ -46,11 +46,15 @@ def tile(request, monkeypatch):
 
 
 # M, d, H, N, out dtype; F = H/N. K1 is [M, d]·[d, F], K2 [M, F]·[F, d].
+# The main loop takes two 64-k slices per iteration when the slice count is
+# even (every tile but 256x256), one otherwise: the shapes cover both counts,
+# with and without a K tail.
 SHAPES = [
-    (600, 512, 1280, 2, "f32"),    # no K tail in either GEMM (d = 512, F = 640); M, N ragged
+    (600, 512, 1280, 2, "f32"),    # no K tail in either GEMM (d = 512, F = 640: 8 and 10 slices); M, N ragged
+    (600, 576, 2560, 4, "bf16"),   # no K tail, an odd slice count in K1 (d = 576: 9 slices)
     (520, 328, 912, 2, "bf16"),    # K tails in both (328 = 5·64 + 8, F = 456 = 7·64 + 8)
-    (1030, 520, 4160, 8, "bf16"),  # 8 ranks, K tails, ragged everywhere
-    (333, 200, 2400, 3, "f32"),    # F = 800
+    (1030, 520, 4160, 8, "bf16"),  # 8 ranks, K tails with 9 slices, ragged everywhere
+    (333, 200, 2400, 3, "f32"),    # F = 800 (13 slices with a tail)
 ]
 
 
