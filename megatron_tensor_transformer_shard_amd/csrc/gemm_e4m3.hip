@@ -327,7 +327,7 @@ __device__ __forceinline__ void block_max_to(uint8_t* smem, int wave, int lane, 
   }
 }
 
-template <int BM, int BN, int OUT, bool KTAIL, int FP, int FQ>
+template <int BM, int BN, int OUT, bool KTAIL, int FP, int FQ, bool PAIR>
 __global__ __launch_bounds__(kThreads) void gemm_e4m3_kernel(Fp8GemmArgs g0, Fp8GemmArgs g1,
                                                              int tiles0, int group_m) {
   constexpr int TM = BM / 2, TN = BN / 2;      // wave tile (2 x 2 waves)
@@ -551,10 +551,13 @@ __global__ __launch_bounds__(kThreads) void gemm_e4m3_kernel(Fp8GemmArgs g0, Fp8
 #pragma unroll
   for (int j = 0; j < NRA; ++j) read_q(0, j / 4, j % 4);
 
-  // Slice kt: Q stage kt & 1, P stage kt % 3.
-  for (int kt = 0; kt < ktiles; ++kt) {
-    const int qs = kt & 1;
-    const int ps1 = (kt + 1) % 3, ps2 = (kt + 2) % 3;
+  // Slice kt: Q stage qs = kt & 1, P stage ps = kt % 3. With PAIR (an even
+  // slice count) two slices per iteration make the Q stages constants and
+  // the P stages come from a phase counter (no division on the loop's
+  // critical path).
+  // (The first k-step reads no P fragments, so slice kt needs the P stages
+  // of slices kt+1 and kt+2 only.)
+  auto slice = [&](int kt, int ps1, int ps2, int qs) __attribute__((always_inline)) {
     half0(qs, min(kt + 2, last), ps2);
     waitcnt<P_ROUNDS, 0>();  // slice kt+1 has landed (only the P part of kt+2 may be in flight)
     barrier();               // every wave is done reading the stages of slice kt
@@ -564,6 +567,17 @@ __global__ __launch_bounds__(kThreads) void gemm_e4m3_kernel(Fp8GemmArgs g0, Fp8
       barrier();
     }
     half1(ps1, qs ^ 1, min(kt + 2, last), qs);
+  };
+  if constexpr (PAIR) {
+    int ph = 0;  // kt % 3
+    for (int kt = 0; kt < ktiles; kt += 2) {
+      const int p1 = ph == 2 ? 0 : ph + 1, p2 = ph == 0 ? 2 : ph - 1;  // (kt + 1) % 3, (kt + 2) % 3
+      slice(kt, p1, p2, 0);
+      slice(kt + 1, p2, ph, 1);
+      ph = p2;
+    }
+  } else {
+    for (int kt = 0; kt < ktiles; ++kt) slice(kt, (kt + 1) % 3, (kt + 2) % 3, kt & 1);
   }
   waitcnt<0, 0>();  // no DMA may still write LDS when the workgroup ends
 
@@ -713,13 +727,25 @@ int tile_count(const Fp8GemmArgs& a) {
 }
 
 // One launch over problems a[0 .. n) (n = 1 or 2).
+// Two slices per main-loop iteration when every problem has an even slice
+// count, except at 256 x 256 (there the compiler no longer keeps the
+// accumulators in place with four MFMA call sites each).
 template <int BM, int BN, int OUT, bool KTAIL, int FP, int FQ>
 hipError_t launch_one(const Fp8GemmArgs* a, int n, hipStream_t stream) {
   const int t0 = tile_count<BM, BN>(a[0]);
   const int tiles = t0 + (n > 1 ? tile_count<BM, BN>(a[1]) : 0);
   const int group_m = 4;
-  hipLaunchKernelGGL((e4::gemm_e4m3_kernel<BM, BN, OUT, KTAIL, FP, FQ>), dim3(tiles),
-                     dim3(kThreads), 0, stream, a[0], n > 1 ? a[1] : a[0], t0, group_m);
+  const Fp8GemmArgs& a1 = n > 1 ? a[1] : a[0];
+  const bool even = ((a[0].K + e4::BK - 1) / e4::BK) % 2 == 0 && ((a1.K + e4::BK - 1) / e4::BK) % 2 == 0;
+  if constexpr (!(BM == 256 && BN == 256)) {
+    if (even) {
+      hipLaunchKernelGGL((e4::gemm_e4m3_kernel<BM, BN, OUT, KTAIL, FP, FQ, true>), dim3(tiles),
+                         dim3(kThreads), 0, stream, a[0], a1, t0, group_m);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((e4::gemm_e4m3_kernel<BM, BN, OUT, KTAIL, FP, FQ, false>), dim3(tiles),
+                     dim3(kThreads), 0, stream, a[0], a1, t0, group_m);
   return hipGetLastError();
 }
 
