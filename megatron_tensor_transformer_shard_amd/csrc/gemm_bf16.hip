@@ -561,11 +561,11 @@ int tile_count(const GemmArgs& a) {
 
 // One launch over problems a[0 .. n) (n = 1 or 2).
 // The main loop takes two slices per iteration when every problem of the
-// launch has an even number of slices, except at 256 x 256 (its 64
-// accumulator quadruples fill the 256 AGPRs, and with four MFMA call sites per
-// accumulator the compiler no longer keeps them in place: it moves them
-// through VGPRs inside the loop) and with the M-major P operand (the same
-// happens at 256 x 192).
+// launch has an even number of slices, except with the M-major P operand
+// (there, at 256 x 192, the compiler no longer keeps the accumulators in place
+// with four MFMA call sites each: it moves them through VGPRs inside the
+// loop) and at 256 x 256 with a K tail (the tail clearing in both slices
+// makes it spill).
 template <int BM, int BN, int OUT, bool KTAIL, bool PT, bool QT>
 hipError_t launch_one(const GemmArgs* a, int n, hipStream_t stream) {
   const int t0 = tile_count<BM, BN>(a[0]);
@@ -573,7 +573,7 @@ hipError_t launch_one(const GemmArgs* a, int n, hipStream_t stream) {
   const int group_m = 4;
   const GemmArgs& a1 = n > 1 ? a[1] : a[0];
   const bool even = ((a[0].K + kBK - 1) / kBK) % 2 == 0 && ((a1.K + kBK - 1) / kBK) % 2 == 0;
-  if constexpr (!(BM == 256 && BN == 256) && !PT) {
+  if constexpr (!PT && !(KTAIL && BM == 256 && BN == 256)) {
     if (even) {
       hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, OUT, KTAIL, PT, QT, true>), dim3(tiles),
                          dim3(kThreads), 0, stream, a[0], a1, t0, group_m);

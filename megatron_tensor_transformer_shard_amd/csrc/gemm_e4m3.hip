@@ -728,8 +728,8 @@ int tile_count(const Fp8GemmArgs& a) {
 
 // One launch over problems a[0 .. n) (n = 1 or 2).
 // Two slices per main-loop iteration when every problem has an even slice
-// count, except at 256 x 256 (there the compiler no longer keeps the
-// accumulators in place with four MFMA call sites each).
+// count, except at 256 x 256 with a K tail (the tail clearing in both slices
+// makes it spill).
 template <int BM, int BN, int OUT, bool KTAIL, int FP, int FQ>
 hipError_t launch_one(const Fp8GemmArgs* a, int n, hipStream_t stream) {
   const int t0 = tile_count<BM, BN>(a[0]);
@@ -737,7 +737,7 @@ hipError_t launch_one(const Fp8GemmArgs* a, int n, hipStream_t stream) {
   const int group_m = 4;
   const Fp8GemmArgs& a1 = n > 1 ? a[1] : a[0];
   const bool even = ((a[0].K + e4::BK - 1) / e4::BK) % 2 == 0 && ((a1.K + e4::BK - 1) / e4::BK) % 2 == 0;
-  if constexpr (!(BM == 256 && BN == 256)) {
+  if constexpr (!(KTAIL && BM == 256 && BN == 256)) {
     if (even) {
       hipLaunchKernelGGL((e4::gemm_e4m3_kernel<BM, BN, OUT, KTAIL, FP, FQ, true>), dim3(tiles),
                          dim3(kThreads), 0, stream, a[0], a1, t0, group_m);
