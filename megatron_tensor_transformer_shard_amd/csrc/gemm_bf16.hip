@@ -222,7 +222,7 @@ struct GemmArgs {
 // Workgroups [0, tiles0) compute problem g0, the rest problem g1 (a launch
 // of one problem passes tiles0 = its tile count). Both share the template
 // arguments (tile, epilogue, layouts, KTAIL).
-template <int BM, int BN, int OUT, bool KTAIL, bool PT, bool QT, bool PAIR>
+template <int BM, int BN, int OUT, bool KTAIL, bool PT, bool QT, int UNR>
 __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs g0, GemmArgs g1,
                                                              int tiles0, int group_m) {
   constexpr int BK = kBK, NSP = kNSP, NSQ = kNSQ;
@@ -427,7 +427,14 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs g0, GemmAr
     }
     kstep(1, ps1, qs ^ 1, 0, true, min(kt + 2, last), qs);
   };
-  if constexpr (PAIR) {
+  if constexpr (UNR == 6) {
+    // Six slices per iteration (ktiles is a multiple of 6): every stage
+    // index of every read and DMA is a constant.
+    for (int kt = 0; kt < ktiles; kt += 6) {
+#pragma unroll
+      for (int u = 0; u < 6; ++u) slice(kt + u, u % 3, u & 1);
+    }
+  } else if constexpr (UNR == 2) {
     // Two slices per iteration (ktiles is even), so that the Q stage of
     // every read and DMA is a constant; ph = kt % 3.
     int ph = 0;
@@ -560,27 +567,35 @@ int tile_count(const GemmArgs& a) {
 }
 
 // One launch over problems a[0 .. n) (n = 1 or 2).
-// The main loop takes two slices per iteration when every problem of the
-// launch has an even number of slices, except with the M-major P operand
-// (there, at 256 x 192, the compiler no longer keeps the accumulators in place
-// with four MFMA call sites each: it moves them through VGPRs inside the
-// loop) and at 256 x 256 with a K tail (the tail clearing in both slices
-// makes it spill).
+// The main loop takes six slices per iteration when every problem of the
+// launch has a multiple of 6 slices, two when they are even, else one. Not
+// six at 256 x 256, nor two or six with the M-major P operand, nor at
+// 256 x 256 with a K tail: there the compiler no longer keeps the
+// accumulators in place (it moves them through VGPRs inside the loop, or
+// spills).
 template <int BM, int BN, int OUT, bool KTAIL, bool PT, bool QT>
 hipError_t launch_one(const GemmArgs* a, int n, hipStream_t stream) {
   const int t0 = tile_count<BM, BN>(a[0]);
   const int tiles = t0 + (n > 1 ? tile_count<BM, BN>(a[1]) : 0);
   const int group_m = 4;
   const GemmArgs& a1 = n > 1 ? a[1] : a[0];
-  const bool even = ((a[0].K + kBK - 1) / kBK) % 2 == 0 && ((a1.K + kBK - 1) / kBK) % 2 == 0;
-  if constexpr (!PT && !(KTAIL && BM == 256 && BN == 256)) {
-    if (even) {
-      hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, OUT, KTAIL, PT, QT, true>), dim3(tiles),
+  const int s0 = (a[0].K + kBK - 1) / kBK, s1 = (a1.K + kBK - 1) / kBK;
+  constexpr bool big = BM == 256 && BN == 256;
+  if constexpr (!PT && !big) {
+    if (s0 % 6 == 0 && s1 % 6 == 0) {
+      hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, OUT, KTAIL, PT, QT, 6>), dim3(tiles),
                          dim3(kThreads), 0, stream, a[0], a1, t0, group_m);
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, OUT, KTAIL, PT, QT, false>), dim3(tiles),
+  if constexpr (!PT && !(KTAIL && big)) {
+    if (s0 % 2 == 0 && s1 % 2 == 0) {
+      hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, OUT, KTAIL, PT, QT, 2>), dim3(tiles),
+                         dim3(kThreads), 0, stream, a[0], a1, t0, group_m);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, OUT, KTAIL, PT, QT, 1>), dim3(tiles),
                      dim3(kThreads), 0, stream, a[0], a1, t0, group_m);
   return hipGetLastError();
 }

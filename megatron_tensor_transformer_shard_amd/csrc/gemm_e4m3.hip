@@ -327,7 +327,7 @@ __device__ __forceinline__ void block_max_to(uint8_t* smem, int wave, int lane, 
   }
 }
 
-template <int BM, int BN, int OUT, bool KTAIL, int FP, int FQ, bool PAIR>
+template <int BM, int BN, int OUT, bool KTAIL, int FP, int FQ, int UNR>
 __global__ __launch_bounds__(kThreads) void gemm_e4m3_kernel(Fp8GemmArgs g0, Fp8GemmArgs g1,
                                                              int tiles0, int group_m) {
   constexpr int TM = BM / 2, TN = BN / 2;      // wave tile (2 x 2 waves)
@@ -551,8 +551,9 @@ __global__ __launch_bounds__(kThreads) void gemm_e4m3_kernel(Fp8GemmArgs g0, Fp8
 #pragma unroll
   for (int j = 0; j < NRA; ++j) read_q(0, j / 4, j % 4);
 
-  // Slice kt: Q stage qs = kt & 1, P stage ps = kt % 3. With PAIR (an even
-  // slice count) two slices per iteration make the Q stages constants and
+  // Slice kt: Q stage qs = kt & 1, P stage ps = kt % 3. With six slices per
+  // iteration (UNR = 6, a multiple of 6 slices) every stage index is a
+  // constant; with two (UNR = 2, an even slice count) the Q stages are, and
   // the P stages come from a phase counter (no division on the loop's
   // critical path).
   // (The first k-step reads no P fragments, so slice kt needs the P stages
@@ -568,7 +569,12 @@ __global__ __launch_bounds__(kThreads) void gemm_e4m3_kernel(Fp8GemmArgs g0, Fp8
     }
     half1(ps1, qs ^ 1, min(kt + 2, last), qs);
   };
-  if constexpr (PAIR) {
+  if constexpr (UNR == 6) {
+    for (int kt = 0; kt < ktiles; kt += 6) {
+#pragma unroll
+      for (int u = 0; u < 6; ++u) slice(kt + u, (u + 1) % 3, (u + 2) % 3, u & 1);
+    }
+  } else if constexpr (UNR == 2) {
     int ph = 0;  // kt % 3
     for (int kt = 0; kt < ktiles; kt += 2) {
       const int p1 = ph == 2 ? 0 : ph + 1, p2 = ph == 0 ? 2 : ph - 1;  // (kt + 1) % 3, (kt + 2) % 3
@@ -727,24 +733,33 @@ int tile_count(const Fp8GemmArgs& a) {
 }
 
 // One launch over problems a[0 .. n) (n = 1 or 2).
-// Two slices per main-loop iteration when every problem has an even slice
-// count, except at 256 x 256 with a K tail (the tail clearing in both slices
-// makes it spill).
+// Six slices per main-loop iteration when every problem has a multiple of 6
+// slices, two when they are even, else one; not six at 256 x 256 or with a K
+// tail, nor two at 256 x 256 with a K tail (the compiler would move or spill
+// accumulators).
 template <int BM, int BN, int OUT, bool KTAIL, int FP, int FQ>
 hipError_t launch_one(const Fp8GemmArgs* a, int n, hipStream_t stream) {
   const int t0 = tile_count<BM, BN>(a[0]);
   const int tiles = t0 + (n > 1 ? tile_count<BM, BN>(a[1]) : 0);
   const int group_m = 4;
   const Fp8GemmArgs& a1 = n > 1 ? a[1] : a[0];
-  const bool even = ((a[0].K + e4::BK - 1) / e4::BK) % 2 == 0 && ((a1.K + e4::BK - 1) / e4::BK) % 2 == 0;
-  if constexpr (!(KTAIL && BM == 256 && BN == 256)) {
-    if (even) {
-      hipLaunchKernelGGL((e4::gemm_e4m3_kernel<BM, BN, OUT, KTAIL, FP, FQ, true>), dim3(tiles),
+  const int s0 = (a[0].K + e4::BK - 1) / e4::BK, s1 = (a1.K + e4::BK - 1) / e4::BK;
+  constexpr bool big = BM == 256 && BN == 256;
+  if constexpr (!big && !KTAIL) {
+    if (s0 % 6 == 0 && s1 % 6 == 0) {
+      hipLaunchKernelGGL((e4::gemm_e4m3_kernel<BM, BN, OUT, KTAIL, FP, FQ, 6>), dim3(tiles),
                          dim3(kThreads), 0, stream, a[0], a1, t0, group_m);
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((e4::gemm_e4m3_kernel<BM, BN, OUT, KTAIL, FP, FQ, false>), dim3(tiles),
+  if constexpr (!(KTAIL && big)) {
+    if (s0 % 2 == 0 && s1 % 2 == 0) {
+      hipLaunchKernelGGL((e4::gemm_e4m3_kernel<BM, BN, OUT, KTAIL, FP, FQ, 2>), dim3(tiles),
+                         dim3(kThreads), 0, stream, a[0], a1, t0, group_m);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((e4::gemm_e4m3_kernel<BM, BN, OUT, KTAIL, FP, FQ, 1>), dim3(tiles),
                      dim3(kThreads), 0, stream, a[0], a1, t0, group_m);
   return hipGetLastError();
 }

@@ -46,12 +46,13 @@ def tile(request, monkeypatch):
 
 
 # M, d, H, N, out dtype; F = H/N. K1 is [M, d]·[d, F], K2 [M, F]·[F, d].
-# The main loop takes two 64-k slices per iteration when the slice count is
-# even (every tile but 256x256), one otherwise: the shapes cover both counts,
-# with and without a K tail.
+# The main loop takes six 64-k slices per iteration when the slice count is a
+# multiple of 6 (not at 256x256), two when it is even, one otherwise: the
+# shapes cover all three, with and without a K tail.
 SHAPES = [
     (600, 512, 1280, 2, "f32"),    # no K tail in either GEMM (d = 512, F = 640: 8 and 10 slices); M, N ragged
     (600, 576, 2560, 4, "bf16"),   # no K tail, an odd slice count in K1 (d = 576: 9 slices)
+    (600, 768, 1536, 2, "f32"),    # no K tail, 12 slices in both GEMMs
     (520, 328, 912, 2, "bf16"),    # K tails in both (328 = 5·64 + 8, F = 456 = 7·64 + 8)
     (1030, 520, 4160, 8, "bf16"),  # 8 ranks, K tails with 9 slices, ragged everywhere
     (333, 200, 2400, 3, "f32"),    # F = 800 (13 slices with a tail)
@@ -104,8 +105,9 @@ def test_transposed_weights_and_biases(tpm, tile):
 # fp8: d, F multiples of 16; k-slices of 128 bytes. (300, 272, 800, 1): K tails
 # in both GEMMs (272 = 2·128 + 16, 800 = 6·128 + 32); (520, 512, 2048, 4): none.
 @pytest.mark.parametrize("tile", FP8_TILES, indirect=True)
-@pytest.mark.parametrize("M,d,H,N", [(300, 272, 800, 1), (520, 512, 2048, 4)])
+@pytest.mark.parametrize("M,d,H,N", [(300, 272, 800, 1), (520, 512, 2048, 4), (384, 768, 1536, 2)])
 def test_fp8_forward_every_element(tpm, tile, M, d, H, N):
+    # 128-byte slices: 3 and 7 with K tails, 4, and 6 (six per iteration)
     par.test_fp8_shard_vs_oracle(tpm, M, d, H, N)
 
 
