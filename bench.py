@@ -109,6 +109,8 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="stop adding oracle row chunks once this much CPU time is spent")
     p.add_argument("--partial-dtype", choices=["f32", "bf16"], default="f32")
+    p.add_argument("--eager", action="store_true",
+                   help="time the steps' launches eagerly (default: replay of a HIP graph of one step)")
     p.add_argument("--no-clock", action="store_true",
                    help="skip the pass that reads the shader clock inside the stamped kernels")
     p.add_argument("--weight-layout", choices=["math", "linear"], default="math",
@@ -728,16 +730,45 @@ def main():
     torch.cuda.synchronize()
     log(f"bench: warmup {args.warmup} steps done")
 
-    # whole-step timing: exactly K steps between two synchronisations
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    wall_s = time.perf_counter() - t0
-    ms_per_step = 1e3 * wall_s / max(1, args.steps)
+    # whole-step timing: exactly K steps between two synchronisations. By
+    # default the launches of K steps are captured in one HIP graph, replayed
+    # once untimed and once timed, so that neither the host's launch calls nor
+    # a graph launch per step leaves gaps between kernels (every entry point
+    # only enqueues kernels on the caller's stream, and every step here
+    # replays to the eager bits: tests/test_gpu_graph.py); the same K steps
+    # launched eagerly are timed beside it.
+    graph = None
+    if not args.eager:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for _ in range(args.steps):
+                step()
+        graph.replay()
+        torch.cuda.synchronize()
+
+    def timed_steps(replay):
+        t0 = time.perf_counter()
+        if replay:
+            graph.replay()
+        else:
+            for _ in range(args.steps):
+                step()
+        torch.cuda.synchronize()
+        return 1e3 * (time.perf_counter() - t0) / max(1, args.steps)
+
+    ms_eager = timed_steps(False)
+    ms_per_step = timed_steps(True) if graph is not None else ms_eager
     flops_step = wl.N * wl.flops_per_shard()
     value = flops_step / (ms_per_step * 1e-3) / 1e12
-    log(f"bench: {args.steps} steps, {ms_per_step:.3f} ms/step, {value:.1f} TFLOP/s")
+    log(f"bench: {args.steps} steps, {ms_per_step:.3f} ms/step"
+        f"{' (graph replay)' if graph is not None else ''}, {value:.1f} TFLOP/s; "
+        f"eager launches {ms_eager:.3f} ms/step")
 
     # per-kernel timing with events on the launch stream (separate pass), with
     # the engine clock sampled meanwhile. Before each step a spin kernel of a
@@ -838,6 +869,9 @@ def main():
                    else METRIC),
         "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "step_timing": ("one HIP graph of all K steps, replayed" if graph is not None
+                        else "eager launches"),
+        "ms_per_step_eager_launches": round(ms_eager, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
         "data": "synthetic: seeded X~N(0,1), weights~N(0,sigma^2), bf16 (no trained weights)",
         "config": ({"workload": wl.name, "B": wl.B, "S": wl.S, "d": wl.d, "heads": wl.heads,

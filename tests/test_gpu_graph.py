@@ -38,8 +38,8 @@ def _replay_and_compare(step, outputs, reps=3):
         step()
     torch.cuda.synchronize()
     for rep in range(reps):
-        for o in outputs:
-            o.fill_(float("nan"))           # eager work between replays
+        for o in outputs:                   # eager work between replays
+            o.fill_(float("nan") if o.is_floating_point() else 123)
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
@@ -126,3 +126,104 @@ def test_bias_forward_backward_and_bias_gradient_in_a_graph(tpm):
                                        dB_i=outs[2], db1_i=outs[3], workspace=ws)
         tpm.tp_bias_grad_bf16(dYd, db=outs[4], workspace=wsg)
     _replay_and_compare(step, [Z] + outs)
+
+
+def test_e4m3_forward_step_in_a_graph(tpm):
+    # the fp8 forward as the benchmark runs it: Z = GeLU(X·A_i) with its amax,
+    # Z requantised with its own scale, then the fp8 row step
+    import torch
+    M, d, F = 264, 272, 384  # the fp8 calls take d and F in multiples of 16
+    X, A, B = make_random(M, d, F, seed=38, sigma=0.3)
+
+    def quant(bits):
+        T = dev_bf16(bits)
+        return tpm.tp_quant_e4m3(T, tpm.tp_amax_bf16(T))
+    (Xq, sX), (Aq, sA), (Bq, sB) = quant(X), quant(A), quant(B)
+    Z = torch.empty((M, F), dtype=torch.bfloat16, device="cuda")
+    Zq = torch.empty((M, F), dtype=torch.uint8, device="cuda")
+    za = torch.empty(1, dtype=torch.float32, device="cuda")
+    sZ = torch.empty(1, dtype=torch.float32, device="cuda")
+    Y = torch.empty((M, d), dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        tpm.tp_mlp_col_gelu_e4m3(Xq, sX, Aq, sA, Z, za)
+        tpm.tp_quant_e4m3(Z, za, Zq, sZ)
+        tpm.tp_mlp_row_partial_e4m3(Zq, sZ, Bq, sB, Y)
+    _replay_and_compare(step, [Z, za, Zq, sZ, Y])
+
+
+def test_e4m3_delayed_scaling_steps_in_a_graph(tpm):
+    # the delayed-scaling step changes its own state (amax history, scale) on
+    # every run: three replays from the initial state must give the three
+    # eager steps' outputs and states, in order
+    import torch
+    M, d, F = 264, 272, 384  # the fp8 calls take d and F in multiples of 16
+    X, A, B = make_random(M, d, F, seed=39, sigma=0.3)
+
+    def quant(bits):
+        T = dev_bf16(bits)
+        return tpm.tp_quant_e4m3(T, tpm.tp_amax_bf16(T))
+    (Xq, sX), (Aq, sA), (Bq, sB) = quant(X), quant(A), quant(B)
+    hist = tpm.AmaxHistory(4, initial_scale=1.0)
+    Zq = torch.empty((M, F), dtype=torch.uint8, device="cuda")
+    za = torch.empty(1, dtype=torch.float32, device="cuda")
+    Y = torch.empty((M, d), dtype=torch.bfloat16, device="cuda")
+
+    def reset():
+        hist.history.zero_()
+        hist.count.zero_()
+        hist.scale.fill_(1.0)
+        torch.cuda.synchronize()
+
+    def step():
+        tpm.tp_mlp_col_gelu_e4m3_delayed(Xq, sX, Aq, sA, hist.scale, Zq, za)
+        tpm.tp_mlp_row_partial_e4m3(Zq, hist.scale, Bq, sB, Y)
+        hist.push(za)
+
+    state = [Zq, za, Y, hist.history, hist.count, hist.scale]
+    reset()
+    ref = []
+    for _ in range(3):
+        step()
+        torch.cuda.synchronize()
+        ref.append([t.clone() for t in state])
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    reset()
+    for rep in range(3):
+        Y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (o, r) in enumerate(zip(state, ref[rep])):
+            assert torch.equal(o, r), f"replay {rep}: state {i} differs from eager step {rep}"
+        log(f"replay {rep}: outputs and delayed-scaling state equal to eager step {rep}")
+
+
+def test_attention_block_in_a_graph(tpm):
+    import torch
+    from workloads import AttnWorkload, make_attn_inputs
+    wl = AttnWorkload("graph_attn", B=2, S=192, d=512, heads=4, N=2, sigma=0.02, seed=40)
+    X, Wqkv, Wo = make_attn_inputs(wl)
+    Xd, Wd, Wod = dev_bf16(X), dev_bf16(Wqkv), dev_bf16(Wo)
+    M, F = wl.B * wl.S, wl.F
+    hr = wl.heads // wl.N
+    QKV = torch.empty((M, 3 * F), dtype=torch.bfloat16, device="cuda")
+    O = torch.empty((M, F), dtype=torch.bfloat16, device="cuda")
+    parts = [torch.empty((M, wl.d), dtype=torch.float32, device="cuda") for _ in range(wl.N)]
+    Y = torch.empty((M, wl.d), dtype=torch.float32, device="cuda")
+
+    def step():
+        for r in range(wl.N):
+            tpm.tp_attn_qkv(Xd, Wd[:, r * 3 * F:(r + 1) * 3 * F], QKV)
+            tpm.tp_attn_heads(QKV, wl.B, wl.S, hr, True, O)
+            tpm.tp_mlp_row_partial(O, Wod[r * F:(r + 1) * F, :], parts[r])
+        tpm.tp_partial_sum(parts, Y=Y)
+    _replay_and_compare(step, parts + [Y])
