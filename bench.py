@@ -110,7 +110,7 @@ def parse():
                    help="stop adding oracle row chunks once this much CPU time is spent")
     p.add_argument("--partial-dtype", choices=["f32", "bf16"], default="f32")
     p.add_argument("--eager", action="store_true",
-                   help="time the steps' launches eagerly (default: replay of a HIP graph of one step)")
+                   help="time the steps' launches eagerly (default: one HIP graph of all K steps, replayed)")
     p.add_argument("--no-clock", action="store_true",
                    help="skip the pass that reads the shader clock inside the stamped kernels")
     p.add_argument("--weight-layout", choices=["math", "linear"], default="math",
