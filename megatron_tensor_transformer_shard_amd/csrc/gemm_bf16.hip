@@ -643,9 +643,14 @@ struct TileChoice { int bm, bn; };
 // Pick the tile shape with the best estimated time: waves of 256 CUs times a
 // per-tile time relative to a 256x256 tile, measured on MI355X (smaller
 // tiles reuse each LDS byte less, so their cost falls slower than their area).
+// 128x192 is for GEMMs whose short N leaves the other shapes too few tiles
+// (GPT-2-small's row GEMM, 8192 x 768: 256 tiles, 40 us against 45 us with
+// 128x128); its entry sits between the bounds measured on MI355X, below the
+// 0.6 at which it would lose there and above the 0.43 at which it would
+// displace 256x192 on the 175B-class GEMMs, where it is 40-50% slower.
 TileChoice choose_tile(const GemmArgs* a, int n) {
   static const struct { int bm, bn; double cost; } cands[] = {
-      {256, 256, 1.00}, {256, 192, 0.85}, {256, 128, 0.62}, {128, 128, 0.30},
+      {256, 256, 1.00}, {256, 192, 0.85}, {256, 128, 0.62}, {128, 192, 0.55}, {128, 128, 0.30},
   };
   constexpr int kCus = 256;
   int obm, obn;
@@ -670,6 +675,7 @@ hipError_t launch_group(const GemmArgs* a, int n, OutKind out, Layout lay, hipSt
   if (tc.bm == 256 && tc.bn == 256) return launch_tile<256, 256>(a, n, out, lay, stream);
   if (tc.bm == 256 && tc.bn == 192) return launch_tile<256, 192>(a, n, out, lay, stream);
   if (tc.bm == 256 && tc.bn == 128) return launch_tile<256, 128>(a, n, out, lay, stream);
+  if (tc.bm == 128 && tc.bn == 192) return launch_tile<128, 192>(a, n, out, lay, stream);
   return launch_tile<128, 128>(a, n, out, lay, stream);
 }
 

@@ -545,7 +545,8 @@ def test_fp8_steps_individually(tpm):
 # ------------------------------------------------ full-size workloads ----
 # The workloads at their full sizes, in the launch configuration the benchmark
 # times (the tile shapes the launchers pick for them: 256x256 for the 7B-class
-# GEMMs, 256x192 for the GPT-2-small column GEMM and the 175B-class GEMMs).
+# GEMMs, 256x192 for the GPT-2-small column GEMM and the 175B-class GEMMs,
+# 128x192 for the GPT-2-small row GEMM).
 # Every element of every rank's Y_i is compared with the oracle, and Z_i of the
 # ranks in z_ranks element by element with the Z bound and its bit-identical
 # floor. The sum of the ranks is compared in full with the sum of the

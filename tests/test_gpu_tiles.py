@@ -2,10 +2,10 @@
 by element.
 
 The launchers pick a tile shape from the problem size, so the moderate shapes
-of the other parity tests all run the 128x128 tile, and the large tiles the
+of the other parity tests mostly run the 128x128 tile, and the large tiles the
 full-size workloads run (256x256 for the 7B-class GEMMs, 256x192 for the
-GPT-2-small column GEMM and the 175B-class ones) would otherwise only be
-checked there. Here the environment variable TPMLP_TILE forces each shape in
+GPT-2-small column GEMM and the 175B-class ones, 128x192 for the GPT-2-small
+row GEMM) would otherwise only be checked there. Here the environment variable TPMLP_TILE forces each shape in
 turn on shapes that span several tiles with ragged edges in M and N, with and
 without a K tail (K not a multiple of the 64-element bf16 or 128-byte fp8
 k-slice), and every output element is compared with the oracle by the same
@@ -26,7 +26,7 @@ from workloads import make_integer_valued
 
 pytestmark = pytest.mark.gpu
 
-BF16_TILES = ["256x256", "256x192", "256x128", "128x128"]
+BF16_TILES = ["256x256", "256x192", "256x128", "128x192", "128x128"]
 FP8_TILES = ["256x256", "256x192", "128x128"]
 
 
