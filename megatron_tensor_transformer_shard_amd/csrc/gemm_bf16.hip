@@ -46,13 +46,16 @@
 //    DMA over both k-steps halves the burst each k-step carries.
 //  - The main loop has no tail: past the last slice the DMA reloads the last
 //    slice into stages that are not read again. Its stage indices cost
-//    instructions on the loop's critical path: they come from a phase counter
-//    (kt mod 6, no division), the K-major reads add immediate offsets to one
-//    VGPR base per k-step, and where the compiler still keeps the
-//    accumulators in place with two slices per iteration (every tile but
-//    256 x 256) an even slice count takes that form, whose Q stages are
-//    constants. (Measured on MI355X: a loop whose stage indices were all
-//    constants took about 300 of its 2600 cycles per slice fewer.)
+//    instructions on the loop's critical path, so they are kept out of it
+//    where the slice count allows: six slices per iteration when it is a
+//    multiple of 6 (every stage index a constant), two when it is even (the
+//    Q stages constants, the P stages from a phase counter kept mod 3), else
+//    one (both from a counter kept mod 6, no division); the K-major reads add
+//    immediate offsets to one VGPR base per k-step. Six per iteration is not
+//    used at 256 x 256, where the compiler then stops keeping the
+//    accumulators in place (see launch_one). (Measured on MI355X: a loop
+//    whose stage indices were all constants took about 300 of its 2600
+//    cycles per slice fewer.)
 //  - Rows of P beyond M and columns of Q beyond N are loaded from clamped
 //    addresses (their outputs are discarded). When K is not a multiple of 64
 //    (KTAIL), the last slice loads k clamped into [k_last, K) and the k >= K
