@@ -460,6 +460,11 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs g0, GemmAr
   // Element offsets are a per-lane base (tile (0, 0)) plus the wave-uniform
   // 16·mi rows and 16·ni columns (row strides are below 2^23, so the latter
   // fits 32 bits); a tile is stored where its row and column are inside.
+  // Tiles go out row block by row block (mi outer, ni inner), so the pieces
+  // of each 128-byte line of C come from consecutive store instructions:
+  // with the column groups outer, lines reached HBM in parts (WRITE_SIZE
+  // 1.26-1.77 times the output bytes with 256x192 tiles, measured on MI355X;
+  // exactly the output bytes in this order, and the GEMMs 2-3% faster).
   const int mrow = m0 + wm * TM + (lane & 15), ncol = n0 + wn * TN + 4 * (lane >> 4);
   const int rows_left = M - mrow, cols_left = N - ncol;
   const int64_t c_lane = (int64_t)mrow * ldc + ncol;
@@ -482,7 +487,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs g0, GemmAr
     auto load_batch = [&](int b, int buf) __attribute__((always_inline)) {
 #pragma unroll
       for (int e = 0; e < EB; ++e) {
-        const int ni = (b * EB + e) / MT, mi = (b * EB + e) % MT;
+        const int mi = (b * EB + e) / NT, ni = (b * EB + e) % NT;
         const int r = min(16 * mi, row_max), c = min(16 * ni, col_max);
         sv[buf][e] = *reinterpret_cast<const f32x4*>(aux_lane + ((int64_t)r * (int)ldaux + c));
       }
@@ -494,7 +499,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs g0, GemmAr
       if (b + LA < NB) load_batch(b + LA, (b + LA) % (LA + 1));
 #pragma unroll
       for (int e = 0; e < EB; ++e) {
-        const int ni = (b * EB + e) / MT, mi = (b * EB + e) % MT;
+        const int mi = (b * EB + e) / NT, ni = (b * EB + e) % NT;
         f32x4 v = acc[ni][mi];
         asm volatile("" : "+v"(v));
         const f32x4 x = sv[b % (LA + 1)][e];
@@ -527,9 +532,9 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs g0, GemmAr
       bias2[ni] = *reinterpret_cast<const u32x2*>(g.bias + ncol + min(16 * ni, col_max));
   }
 #pragma unroll
-  for (int ni = 0; ni < NT; ++ni) {
+  for (int mi = 0; mi < MT; ++mi) {
 #pragma unroll
-    for (int mi = 0; mi < MT; ++mi) {
+    for (int ni = 0; ni < NT; ++ni) {
       if (!inside(mi, ni)) continue;
       const int64_t o = c_off(mi, ni);
       f32x4 v = acc[ni][mi];

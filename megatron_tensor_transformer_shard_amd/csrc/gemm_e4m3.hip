@@ -597,6 +597,8 @@ __global__ __launch_bounds__(kThreads) void gemm_e4m3_kernel(Fp8GemmArgs g0, Fp8
   // is stored where its row and column are inside. The maxima of bf16 values
   // are taken on their bit patterns with the sign cleared, two at a time
   // (v_pk_max_u16): non-negative floats order like their bit patterns.
+  // Tiles are stored row block by row block, as in the bf16 engine, so each
+  // 128-byte line of C is completed by consecutive store instructions.
   const float dq = 1.0f / (sP[0] * sQ[0]);
   const int mrow = m0 + wm * TM + (lane & 15), ncol = n0 + wn * TN + 4 * (lane >> 4);
   const int rows_left = M - mrow, cols_left = N - ncol;
@@ -625,9 +627,9 @@ __global__ __launch_bounds__(kThreads) void gemm_e4m3_kernel(Fp8GemmArgs g0, Fp8
         bias2[ni] = *reinterpret_cast<const u32x2*>(g.bias + ncol + min(16 * ni, col_max));
     }
 #pragma unroll
-    for (int ni = 0; ni < NT; ++ni) {
+    for (int mi = 0; mi < MT; ++mi) {
 #pragma unroll
-      for (int mi = 0; mi < MT; ++mi) {
+      for (int ni = 0; ni < NT; ++ni) {
         if (!inside(mi, ni)) continue;
         f32x4 v = acc[ni][mi];
         asm volatile("" : "+v"(v));
@@ -657,7 +659,7 @@ __global__ __launch_bounds__(kThreads) void gemm_e4m3_kernel(Fp8GemmArgs g0, Fp8
     auto load_batch = [&](int b, int buf) __attribute__((always_inline)) {
 #pragma unroll
       for (int e = 0; e < EB; ++e) {
-        const int ni = (b * EB + e) / MT, mi = (b * EB + e) % MT;
+        const int mi = (b * EB + e) / NT, ni = (b * EB + e) % NT;
         const int r = min(16 * mi, row_max), c = min(16 * ni, col_max);
         svb[buf][e] = *reinterpret_cast<const f32x4*>(aux_lane + ((int64_t)r * (int)ldaux + c));
       }
@@ -669,7 +671,7 @@ __global__ __launch_bounds__(kThreads) void gemm_e4m3_kernel(Fp8GemmArgs g0, Fp8
       if (b + LA < NB) load_batch(b + LA, (b + LA) % (LA + 1));
 #pragma unroll
       for (int e = 0; e < EB; ++e) {
-        const int ni = (b * EB + e) / MT, mi = (b * EB + e) % MT;
+        const int mi = (b * EB + e) / NT, ni = (b * EB + e) % NT;
         f32x4 v = acc[ni][mi];
         asm volatile("" : "+v"(v));
         v *= dq;
@@ -696,9 +698,9 @@ __global__ __launch_bounds__(kThreads) void gemm_e4m3_kernel(Fp8GemmArgs g0, Fp8
   const float sc = OUT == (int)OutKind::GeluE4m3 ? sC[0] : 1.0f;
   u16x2 zm = {0, 0};
 #pragma unroll
-  for (int ni = 0; ni < NT; ++ni) {
+  for (int mi = 0; mi < MT; ++mi) {
 #pragma unroll
-    for (int mi = 0; mi < MT; ++mi) {
+    for (int ni = 0; ni < NT; ++ni) {
       if (!inside(mi, ni)) continue;
       f32x4 v = acc[ni][mi];
       asm volatile("" : "+v"(v));
