@@ -36,9 +36,10 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
 }
 
 // max(x, 0) for finite x as one v_med3_f32 (fmaxf would first quiet a
-// signalling NaN in x with a second instruction).
-__device__ __forceinline__ float relu(float x) {
-  return __builtin_amdgcn_fmed3f(x, 0.0f, __builtin_huge_valf());
+// signalling NaN in x with a second instruction; with +inf as the upper
+// bound the compiler turns the median into exactly that fmaxf).
+__device__ __forceinline__ float relu(float x, float big = 3.40282347e38f) {
+  return __builtin_amdgcn_fmed3f(x, 0.0f, big);
 }
 
 // GeLU(x) = x·Φ(x), the exact (Gaussian CDF) form.
@@ -54,32 +55,56 @@ __device__ __forceinline__ float relu(float x) {
 // |x|·3e-7, far under half a bf16 ulp of GeLU(x) except where GeLU(x) itself
 // is below about 1e-4, i.e. in the far negative tail. 11 VALU operations and
 // 2 transcendentals.
-__device__ __forceinline__ float gelu_exact(float x) {
+//
+// The constants of gelu_exact. In an epilogue they are held in VGPRs
+// (gelu_regs), opaque to the compiler: a VOP3 instruction (every fma here
+// whose operands are not all plain registers) cannot encode a literal, and
+// the compiler would otherwise move a literal into a register on every call.
+struct GeluRegs {
+  float p, a5, a4, a3, a2, a1, big;
+};
+
+__device__ __forceinline__ GeluRegs gelu_consts() {
+  return GeluRegs{0.3275911f * 0.70710678118654752f, 0.5f * 1.061405429f,
+                  0.5f * -1.453152027f, 0.5f * 1.421413741f, 0.5f * -0.284496736f,
+                  0.5f * 0.254829592f, 3.40282347e38f};
+}
+
+__device__ __forceinline__ GeluRegs gelu_regs() {
+  GeluRegs k = gelu_consts();
+  asm("" : "+v"(k.p), "+v"(k.a5), "+v"(k.a4), "+v"(k.a3), "+v"(k.a2), "+v"(k.a1), "+v"(k.big));
+  return k;
+}
+
+__device__ __forceinline__ float gelu_exact(float x, const GeluRegs& k) {
   const float ax = fabsf(x);
-  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f * 0.70710678118654752f, ax, 1.0f));
-  float p = fmaf(t, 0.5f * 1.061405429f, 0.5f * -1.453152027f);
-  p = fmaf(t, p, 0.5f * 1.421413741f);
-  p = fmaf(t, p, 0.5f * -0.284496736f);
-  p = fmaf(t, p, 0.5f * 0.254829592f);
+  const float t = __builtin_amdgcn_rcpf(fmaf(k.p, ax, 1.0f));
+  float p = fmaf(t, k.a5, k.a4);
+  p = fmaf(t, p, k.a3);
+  p = fmaf(t, p, k.a2);
+  p = fmaf(t, p, k.a1);
   const float e = __builtin_amdgcn_exp2f((x * -0.72134752044448170f) * x);  // e^(−x²/2)
   const float h = (t * p) * e;                                              // Φ(−|x|)
-  return fmaf(-ax, h, relu(x));
+  return fmaf(-ax, h, relu(x, k.big));
 }
+
+__device__ __forceinline__ float gelu_exact(float x) { return gelu_exact(x, gelu_consts()); }
 
 // GeLU(x) and GeLU'(x) = Φ(x) + x·φ(x) together, φ(x) = e^(−x²/2)/√(2π), with
 // the same erfc evaluation as gelu_exact: h = Φ(−|x|), Φ(x) = 1 − h for x >= 0
 // and h for x < 0. The GeLU'(x) error is that of Φ (below 1e-7) plus fp32
 // rounding.
-__device__ __forceinline__ void gelu_and_grad(float x, float& g, float& dg) {
+__device__ __forceinline__ void gelu_and_grad(float x, float& g, float& dg,
+                                              const GeluRegs& k = gelu_consts()) {
   const float ax = fabsf(x);
-  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f * 0.70710678118654752f, ax, 1.0f));
-  float p = fmaf(t, 0.5f * 1.061405429f, 0.5f * -1.453152027f);
-  p = fmaf(t, p, 0.5f * 1.421413741f);
-  p = fmaf(t, p, 0.5f * -0.284496736f);
-  p = fmaf(t, p, 0.5f * 0.254829592f);
+  const float t = __builtin_amdgcn_rcpf(fmaf(k.p, ax, 1.0f));
+  float p = fmaf(t, k.a5, k.a4);
+  p = fmaf(t, p, k.a3);
+  p = fmaf(t, p, k.a2);
+  p = fmaf(t, p, k.a1);
   const float e = __builtin_amdgcn_exp2f((x * -0.72134752044448170f) * x);  // e^(−x²/2)
   const float h = (t * p) * e;                                              // Φ(−|x|)
-  g = fmaf(-ax, h, relu(x));
+  g = fmaf(-ax, h, relu(x, k.big));
   const float phi = x >= 0.0f ? 1.0f - h : h;
   dg = fmaf(x, e * 0.39894228040143268f, phi);
 }

@@ -484,6 +484,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs g0, GemmAr
     const int row_max = M - 1 - mrow, col_max = N - 4 - ncol;
     const float* aux_lane = aux + (int64_t)mrow * ldaux + ncol;
     f32x4 sv[LA + 1][EB];
+    const GeluRegs gk = gelu_regs();
     auto load_batch = [&](int b, int buf) __attribute__((always_inline)) {
 #pragma unroll
       for (int e = 0; e < EB; ++e) {
@@ -505,7 +506,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs g0, GemmAr
         const f32x4 x = sv[b % (LA + 1)][e];
         float gl[4], dg[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) gelu_and_grad(x[q], gl[q], dg[q]);
+        for (int q = 0; q < 4; ++q) gelu_and_grad(x[q], gl[q], dg[q], gk);
         if (inside(mi, ni)) {
           const int64_t o = c_off(mi, ni);
           const u32x2 d2 = {pack_bf16x2(v[0] * dg[0], v[1] * dg[1]),
@@ -531,6 +532,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs g0, GemmAr
     for (int ni = 0; ni < NT; ++ni)
       bias2[ni] = *reinterpret_cast<const u32x2*>(g.bias + ncol + min(16 * ni, col_max));
   }
+  [[maybe_unused]] const GeluRegs gk = gelu_regs();
 #pragma unroll
   for (int mi = 0; mi < MT; ++mi) {
 #pragma unroll
@@ -550,15 +552,15 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs g0, GemmAr
                          __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xFFFF0000u)};
         *reinterpret_cast<f32x4*>(static_cast<float*>(C) + o) = v + b;
       } else if constexpr (OUT == (int)OutKind::GeluBf16) {
-        const u32x2 g = {pack_bf16x2(gelu_exact(v[0]), gelu_exact(v[1])),
-                         pack_bf16x2(gelu_exact(v[2]), gelu_exact(v[3]))};
+        const u32x2 g = {pack_bf16x2(gelu_exact(v[0], gk), gelu_exact(v[1], gk)),
+                         pack_bf16x2(gelu_exact(v[2], gk), gelu_exact(v[3], gk))};
         *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(C) + o) = g;
       } else if constexpr (OUT == (int)OutKind::GeluBiasBf16) {
         const u32x2 w = bias2[ni];
         const f32x4 b = {__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xFFFF0000u),
                          __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xFFFF0000u)};
-        const u32x2 g = {pack_bf16x2(gelu_exact(v[0] + b[0]), gelu_exact(v[1] + b[1])),
-                         pack_bf16x2(gelu_exact(v[2] + b[2]), gelu_exact(v[3] + b[3]))};
+        const u32x2 g = {pack_bf16x2(gelu_exact(v[0] + b[0], gk), gelu_exact(v[1] + b[1], gk)),
+                         pack_bf16x2(gelu_exact(v[2] + b[2], gk), gelu_exact(v[3] + b[3], gk))};
         *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(C) + o) = g;
       } else {
         const u32x2 g = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};

@@ -656,6 +656,7 @@ __global__ __launch_bounds__(kThreads) void gemm_e4m3_kernel(Fp8GemmArgs g0, Fp8
     const float* aux_lane = aux + (int64_t)mrow * ldaux + ncol;
     u16x2 dsm = {0, 0}, zm = {0, 0};
     f32x4 svb[LA + 1][EB];
+    const GeluRegs gk = gelu_regs();
     auto load_batch = [&](int b, int buf) __attribute__((always_inline)) {
 #pragma unroll
       for (int e = 0; e < EB; ++e) {
@@ -679,7 +680,7 @@ __global__ __launch_bounds__(kThreads) void gemm_e4m3_kernel(Fp8GemmArgs g0, Fp8
           const f32x4 sv = svb[b % (LA + 1)][e];
           float gl[4], dg[4];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) gelu_and_grad(sv[q], gl[q], dg[q]);
+          for (int q = 0; q < 4; ++q) gelu_and_grad(sv[q], gl[q], dg[q], gk);
           const u32x2 o = {pack_bf16x2(v[0] * dg[0], v[1] * dg[1]),
                            pack_bf16x2(v[2] * dg[2], v[3] * dg[3])};
           const u32x2 z = {pack_bf16x2(gl[0], gl[1]), pack_bf16x2(gl[2], gl[3])};
@@ -696,6 +697,7 @@ __global__ __launch_bounds__(kThreads) void gemm_e4m3_kernel(Fp8GemmArgs g0, Fp8
     return;
   }
   const float sc = OUT == (int)OutKind::GeluE4m3 ? sC[0] : 1.0f;
+  [[maybe_unused]] const GeluRegs gk = gelu_regs();
   u16x2 zm = {0, 0};
 #pragma unroll
   for (int mi = 0; mi < MT; ++mi) {
@@ -705,8 +707,8 @@ __global__ __launch_bounds__(kThreads) void gemm_e4m3_kernel(Fp8GemmArgs g0, Fp8
       f32x4 v = acc[ni][mi];
       asm volatile("" : "+v"(v));
       v *= dq;
-      const u32x2 o = GELU ? u32x2{pack_bf16x2(gelu_exact(v[0]), gelu_exact(v[1])),
-                                   pack_bf16x2(gelu_exact(v[2]), gelu_exact(v[3]))}
+      const u32x2 o = GELU ? u32x2{pack_bf16x2(gelu_exact(v[0], gk), gelu_exact(v[1], gk)),
+                                   pack_bf16x2(gelu_exact(v[2], gk), gelu_exact(v[3], gk))}
                            : u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
       if (GELU) zm = absmax16x2(absmax16x2(zm, o[0]), o[1]);
       const int64_t off = c_off(mi, ni);
