@@ -73,6 +73,8 @@
 // has the same register layout either way (index lane & 15, k group lane >> 4).
 // The GeluGradBf16 epilogue of the backward reads the recomputed S (fp32) and
 // writes dS = bf16(acc·GeLU'(S)) and Z = bf16(GeLU(S)).
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 #include "tile_engine.hpp"
@@ -533,41 +535,48 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs g0, GemmAr
       bias2[ni] = *reinterpret_cast<const u32x2*>(g.bias + ncol + min(16 * ni, col_max));
   }
   [[maybe_unused]] const GeluRegs gk = gelu_regs();
+  // Every store of a tile wholly inside C takes the path without the
+  // per-tile row and column checks (the checks cost each 16x16 tile a few
+  // scalar instructions and two branches).
+  auto store_all = [&](auto checked) __attribute__((always_inline)) {
 #pragma unroll
-  for (int mi = 0; mi < MT; ++mi) {
+    for (int mi = 0; mi < MT; ++mi) {
 #pragma unroll
-    for (int ni = 0; ni < NT; ++ni) {
-      if (!inside(mi, ni)) continue;
-      const int64_t o = c_off(mi, ni);
-      f32x4 v = acc[ni][mi];
-      // Read the accumulator into VGPRs here, as the GeLU epilogue does; a
-      // store straight from AGPRs lets the register allocator split the
-      // accumulators between the two files and copy them inside the loop.
-      asm volatile("" : "+v"(v));
-      if constexpr (OUT == (int)OutKind::F32) {
-        *reinterpret_cast<f32x4*>(static_cast<float*>(C) + o) = v;
-      } else if constexpr (OUT == (int)OutKind::F32Bias) {
-        const u32x2 w = bias2[ni];
-        const f32x4 b = {__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xFFFF0000u),
-                         __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xFFFF0000u)};
-        *reinterpret_cast<f32x4*>(static_cast<float*>(C) + o) = v + b;
-      } else if constexpr (OUT == (int)OutKind::GeluBf16) {
-        const u32x2 g = {pack_bf16x2(gelu_exact(v[0], gk), gelu_exact(v[1], gk)),
-                         pack_bf16x2(gelu_exact(v[2], gk), gelu_exact(v[3], gk))};
-        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(C) + o) = g;
-      } else if constexpr (OUT == (int)OutKind::GeluBiasBf16) {
-        const u32x2 w = bias2[ni];
-        const f32x4 b = {__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xFFFF0000u),
-                         __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xFFFF0000u)};
-        const u32x2 g = {pack_bf16x2(gelu_exact(v[0] + b[0], gk), gelu_exact(v[1] + b[1], gk)),
-                         pack_bf16x2(gelu_exact(v[2] + b[2], gk), gelu_exact(v[3] + b[3], gk))};
-        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(C) + o) = g;
-      } else {
-        const u32x2 g = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(C) + o) = g;
+      for (int ni = 0; ni < NT; ++ni) {
+        if (decltype(checked)::value && !inside(mi, ni)) continue;
+        const int64_t o = c_off(mi, ni);
+        f32x4 v = acc[ni][mi];
+        // Read the accumulator into VGPRs here, as the GeLU epilogue does; a
+        // store straight from AGPRs lets the register allocator split the
+        // accumulators between the two files and copy them inside the loop.
+        asm volatile("" : "+v"(v));
+        if constexpr (OUT == (int)OutKind::F32) {
+          *reinterpret_cast<f32x4*>(static_cast<float*>(C) + o) = v;
+        } else if constexpr (OUT == (int)OutKind::F32Bias) {
+          const u32x2 w = bias2[ni];
+          const f32x4 b = {__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xFFFF0000u),
+                           __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xFFFF0000u)};
+          *reinterpret_cast<f32x4*>(static_cast<float*>(C) + o) = v + b;
+        } else if constexpr (OUT == (int)OutKind::GeluBf16) {
+          const u32x2 g = {pack_bf16x2(gelu_exact(v[0], gk), gelu_exact(v[1], gk)),
+                           pack_bf16x2(gelu_exact(v[2], gk), gelu_exact(v[3], gk))};
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(C) + o) = g;
+        } else if constexpr (OUT == (int)OutKind::GeluBiasBf16) {
+          const u32x2 w = bias2[ni];
+          const f32x4 b = {__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xFFFF0000u),
+                           __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xFFFF0000u)};
+          const u32x2 g = {pack_bf16x2(gelu_exact(v[0] + b[0], gk), gelu_exact(v[1] + b[1], gk)),
+                           pack_bf16x2(gelu_exact(v[2] + b[2], gk), gelu_exact(v[3] + b[3], gk))};
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(C) + o) = g;
+        } else {
+          const u32x2 g = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(C) + o) = g;
+        }
       }
     }
-  }
+  };
+  if (M - m0 >= BM && N - n0 >= BN) store_all(std::false_type{});
+  else store_all(std::true_type{});
   stamp.finish(g.stamps);
 }
 
