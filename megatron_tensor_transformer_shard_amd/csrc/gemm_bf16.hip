@@ -495,30 +495,35 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs g0, GemmAr
         sv[buf][e] = *reinterpret_cast<const f32x4*>(aux_lane + ((int64_t)r * (int)ldaux + c));
       }
     };
+    // tiles wholly inside C store without the per-tile row and column checks
+    auto run = [&](auto checked) __attribute__((always_inline)) {
 #pragma unroll
-    for (int b = 0; b < LA && b < NB; ++b) load_batch(b, b);
+      for (int b = 0; b < LA && b < NB; ++b) load_batch(b, b);
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      if (b + LA < NB) load_batch(b + LA, (b + LA) % (LA + 1));
+      for (int b = 0; b < NB; ++b) {
+        if (b + LA < NB) load_batch(b + LA, (b + LA) % (LA + 1));
 #pragma unroll
-      for (int e = 0; e < EB; ++e) {
-        const int mi = (b * EB + e) / NT, ni = (b * EB + e) % NT;
-        f32x4 v = acc[ni][mi];
-        asm volatile("" : "+v"(v));
-        const f32x4 x = sv[b % (LA + 1)][e];
-        float gl[4], dg[4];
+        for (int e = 0; e < EB; ++e) {
+          const int mi = (b * EB + e) / NT, ni = (b * EB + e) % NT;
+          f32x4 v = acc[ni][mi];
+          asm volatile("" : "+v"(v));
+          const f32x4 x = sv[b % (LA + 1)][e];
+          float gl[4], dg[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) gelu_and_grad(x[q], gl[q], dg[q], gk);
-        if (inside(mi, ni)) {
-          const int64_t o = c_off(mi, ni);
-          const u32x2 d2 = {pack_bf16x2(v[0] * dg[0], v[1] * dg[1]),
-                            pack_bf16x2(v[2] * dg[2], v[3] * dg[3])};
-          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(C) + o) = d2;
-          const u32x2 z = {pack_bf16x2(gl[0], gl[1]), pack_bf16x2(gl[2], gl[3])};
-          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(C2) + o) = z;
+          for (int q = 0; q < 4; ++q) gelu_and_grad(x[q], gl[q], dg[q], gk);
+          if (!decltype(checked)::value || inside(mi, ni)) {
+            const int64_t o = c_off(mi, ni);
+            const u32x2 d2 = {pack_bf16x2(v[0] * dg[0], v[1] * dg[1]),
+                              pack_bf16x2(v[2] * dg[2], v[3] * dg[3])};
+            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(C) + o) = d2;
+            const u32x2 z = {pack_bf16x2(gl[0], gl[1]), pack_bf16x2(gl[2], gl[3])};
+            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(C2) + o) = z;
+          }
         }
       }
-    }
+    };
+    if (M - m0 >= BM && N - n0 >= BN) run(std::false_type{});
+    else run(std::true_type{});
     stamp.finish(g.stamps);
     return;
   }

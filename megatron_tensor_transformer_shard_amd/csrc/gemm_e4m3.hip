@@ -29,6 +29,8 @@
 //                before the tensor exists and Z can be quantised inside the
 //                GEMM's epilogue). One wave records the step's amax in a ring
 //                of L values and derives the next scale from their mean.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 #include "tile_engine.hpp"
@@ -626,23 +628,27 @@ __global__ __launch_bounds__(kThreads) void gemm_e4m3_kernel(Fp8GemmArgs g0, Fp8
       for (int ni = 0; ni < NT; ++ni)
         bias2[ni] = *reinterpret_cast<const u32x2*>(g.bias + ncol + min(16 * ni, col_max));
     }
+    auto store_all = [&](auto checked) __attribute__((always_inline)) {
 #pragma unroll
-    for (int mi = 0; mi < MT; ++mi) {
+      for (int mi = 0; mi < MT; ++mi) {
 #pragma unroll
-      for (int ni = 0; ni < NT; ++ni) {
-        if (!inside(mi, ni)) continue;
-        f32x4 v = acc[ni][mi];
-        asm volatile("" : "+v"(v));
-        if constexpr (OUT == (int)OutKind::F32Bias) {
-          const u32x2 w = bias2[ni];
-          const f32x4 b = {__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xFFFF0000u),
-                           __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xFFFF0000u)};
-          *reinterpret_cast<f32x4*>(static_cast<float*>(C) + c_off(mi, ni)) = v * dq + b;
-        } else {
-          *reinterpret_cast<f32x4*>(static_cast<float*>(C) + c_off(mi, ni)) = v * dq;
+        for (int ni = 0; ni < NT; ++ni) {
+          if (decltype(checked)::value && !inside(mi, ni)) continue;
+          f32x4 v = acc[ni][mi];
+          asm volatile("" : "+v"(v));
+          if constexpr (OUT == (int)OutKind::F32Bias) {
+            const u32x2 w = bias2[ni];
+            const f32x4 b = {__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xFFFF0000u),
+                             __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xFFFF0000u)};
+            *reinterpret_cast<f32x4*>(static_cast<float*>(C) + c_off(mi, ni)) = v * dq + b;
+          } else {
+            *reinterpret_cast<f32x4*>(static_cast<float*>(C) + c_off(mi, ni)) = v * dq;
+          }
         }
       }
-    }
+    };
+    if (M - m0 >= BM && N - n0 >= BN) store_all(std::false_type{});
+    else store_all(std::true_type{});
     stamp.finish(g.stamps);
     return;
   }
@@ -665,33 +671,38 @@ __global__ __launch_bounds__(kThreads) void gemm_e4m3_kernel(Fp8GemmArgs g0, Fp8
         svb[buf][e] = *reinterpret_cast<const f32x4*>(aux_lane + ((int64_t)r * (int)ldaux + c));
       }
     };
+    // tiles wholly inside C store without the per-tile row and column checks
+    auto run = [&](auto checked) __attribute__((always_inline)) {
 #pragma unroll
-    for (int b = 0; b < LA && b < NB; ++b) load_batch(b, b);
+      for (int b = 0; b < LA && b < NB; ++b) load_batch(b, b);
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      if (b + LA < NB) load_batch(b + LA, (b + LA) % (LA + 1));
+      for (int b = 0; b < NB; ++b) {
+        if (b + LA < NB) load_batch(b + LA, (b + LA) % (LA + 1));
 #pragma unroll
-      for (int e = 0; e < EB; ++e) {
-        const int mi = (b * EB + e) / NT, ni = (b * EB + e) % NT;
-        f32x4 v = acc[ni][mi];
-        asm volatile("" : "+v"(v));
-        v *= dq;
-        if (inside(mi, ni)) {
-          const f32x4 sv = svb[b % (LA + 1)][e];
-          float gl[4], dg[4];
+        for (int e = 0; e < EB; ++e) {
+          const int mi = (b * EB + e) / NT, ni = (b * EB + e) % NT;
+          f32x4 v = acc[ni][mi];
+          asm volatile("" : "+v"(v));
+          v *= dq;
+          if (!decltype(checked)::value || inside(mi, ni)) {
+            const f32x4 sv = svb[b % (LA + 1)][e];
+            float gl[4], dg[4];
 #pragma unroll
-          for (int q = 0; q < 4; ++q) gelu_and_grad(sv[q], gl[q], dg[q], gk);
-          const u32x2 o = {pack_bf16x2(v[0] * dg[0], v[1] * dg[1]),
-                           pack_bf16x2(v[2] * dg[2], v[3] * dg[3])};
-          const u32x2 z = {pack_bf16x2(gl[0], gl[1]), pack_bf16x2(gl[2], gl[3])};
-          dsm = absmax16x2(absmax16x2(dsm, o[0]), o[1]);
-          zm = absmax16x2(absmax16x2(zm, z[0]), z[1]);
-          const int64_t off = c_off(mi, ni);
-          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(C) + off) = o;
-          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(C2) + off) = z;
+            for (int q = 0; q < 4; ++q) gelu_and_grad(sv[q], gl[q], dg[q], gk);
+            const u32x2 o = {pack_bf16x2(v[0] * dg[0], v[1] * dg[1]),
+                             pack_bf16x2(v[2] * dg[2], v[3] * dg[3])};
+            const u32x2 z = {pack_bf16x2(gl[0], gl[1]), pack_bf16x2(gl[2], gl[3])};
+            dsm = absmax16x2(absmax16x2(dsm, o[0]), o[1]);
+            zm = absmax16x2(absmax16x2(zm, z[0]), z[1]);
+            const int64_t off = c_off(mi, ni);
+            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(C) + off) = o;
+            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(C2) + off) = z;
+          }
         }
       }
-    }
+    };
+    if (M - m0 >= BM && N - n0 >= BN) run(std::false_type{});
+    else run(std::true_type{});
     block_max_to(smem, wave, lane, max_of(dsm), max_of(zm), z_amax, z_amax2);
     stamp.finish(g.stamps);
     return;
@@ -699,32 +710,37 @@ __global__ __launch_bounds__(kThreads) void gemm_e4m3_kernel(Fp8GemmArgs g0, Fp8
   const float sc = OUT == (int)OutKind::GeluE4m3 ? sC[0] : 1.0f;
   [[maybe_unused]] const GeluRegs gk = gelu_regs();
   u16x2 zm = {0, 0};
+  // tiles wholly inside C store without the per-tile row and column checks
+  auto store_all = [&](auto checked) __attribute__((always_inline)) {
 #pragma unroll
-  for (int mi = 0; mi < MT; ++mi) {
+    for (int mi = 0; mi < MT; ++mi) {
 #pragma unroll
-    for (int ni = 0; ni < NT; ++ni) {
-      if (!inside(mi, ni)) continue;
-      f32x4 v = acc[ni][mi];
-      asm volatile("" : "+v"(v));
-      v *= dq;
-      const u32x2 o = GELU ? u32x2{pack_bf16x2(gelu_exact(v[0], gk), gelu_exact(v[1], gk)),
-                                   pack_bf16x2(gelu_exact(v[2], gk), gelu_exact(v[3], gk))}
-                           : u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-      if (GELU) zm = absmax16x2(absmax16x2(zm, o[0]), o[1]);
-      const int64_t off = c_off(mi, ni);
-      if constexpr (OUT == (int)OutKind::GeluE4m3) {
-        // the bf16 Z times the scale in fp32, clamped to ±448, one RNE rounding
-        float q[4];
+      for (int ni = 0; ni < NT; ++ni) {
+        if (decltype(checked)::value && !inside(mi, ni)) continue;
+        f32x4 v = acc[ni][mi];
+        asm volatile("" : "+v"(v));
+        v *= dq;
+        const u32x2 o = GELU ? u32x2{pack_bf16x2(gelu_exact(v[0], gk), gelu_exact(v[1], gk)),
+                                     pack_bf16x2(gelu_exact(v[2], gk), gelu_exact(v[3], gk))}
+                             : u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        if (GELU) zm = absmax16x2(absmax16x2(zm, o[0]), o[1]);
+        const int64_t off = c_off(mi, ni);
+        if constexpr (OUT == (int)OutKind::GeluE4m3) {
+          // the bf16 Z times the scale in fp32, clamped to ±448, one RNE rounding
+          float q[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          q[e] = clamp448(bf16_bits_to_f32((o[e >> 1] >> (16 * (e & 1))) & 0xFFFFu) * sc);
-        const uint32_t qb = cvt_e4m3x2(q[0], q[1]) | (cvt_e4m3x2(q[2], q[3]) << 16);
-        *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(C) + off) = qb;
-      } else {
-        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(C) + off) = o;
+          for (int e = 0; e < 4; ++e)
+            q[e] = clamp448(bf16_bits_to_f32((o[e >> 1] >> (16 * (e & 1))) & 0xFFFFu) * sc);
+          const uint32_t qb = cvt_e4m3x2(q[0], q[1]) | (cvt_e4m3x2(q[2], q[3]) << 16);
+          *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(C) + off) = qb;
+        } else {
+          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(C) + off) = o;
+        }
       }
     }
-  }
+  };
+  if (M - m0 >= BM && N - n0 >= BN) store_all(std::false_type{});
+  else store_all(std::true_type{});
   if (GELU && z_amax != nullptr) block_max_to(smem, wave, lane, max_of(zm), 0.0f, z_amax, nullptr);
   stamp.finish(g.stamps);
 }
